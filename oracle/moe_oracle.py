@@ -1,0 +1,439 @@
+"""Plain CPU oracle of the DeepSeekMoE layer forward (sigmoid routing, aux-loss-free bias).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this module: only the
+test-suite, the smoke check in ``__graft_entry__`` and the ``cpu_baseline`` leg of
+``bench.py`` use it.  It shares no code with the HIP library; it is a slow, obviously
+correct NumPy restatement of what the layer computes, in float64 unless a step is
+defined in a lower precision (the fp8 codec, the fp32 bias add).
+
+Sources (the pages this follows; cited by page title and section):
+
+* [TR]  "DeepSeek-V3 Technical Report" (wiki summary, notes.yuuk.io), sections
+  "DeepSeekMoE と補助損失なしの負荷分散" (shared + routed experts, N_s = 1, N_r = 256,
+  K_r = 8, sigmoid gating, gates from the normalised selected affinities, per-expert bias
+  b_i used for routing only, the +/- gamma load rule, no token dropping, node limit M = 4)
+  and "FP8 混合精度訓練" (1x128 activation tiles, 128x128 weight blocks, online amax
+  scaling, E4M3 everywhere, promotion to FP32 every N_C = 128 elements, gating kept in
+  high precision).
+* [PFN] "Vol.25 DeepSeek-V3の技術とその影響" (preferred.jp), section
+  "MoEの歴史とDeepSeekMoE-V3の特徴": one always-on shared expert plus 8 of 256 routed
+  experts per token, whose results are combined.
+
+Readings taken where the pages are silent (each is listed again in the design doc):
+
+* affinity s = sigmoid(x . e_i) with e_i the i-th router row and no router bias vector;
+* selection on z = s + b, larger z first, equal z -> lower expert index;
+* gates g = s_S / sum(s_S) with no extra scaling (they sum to one);
+* expert FFN = SwiGLU: W2 (silu(W1 x) * (W3 x)); W13 rows [0, I) are W1, [I, 2I) are W3;
+* output = shared expert + sum_k g_k FFN_k(x), no residual;
+* group-limited routing (stand-in for the node limit): groups of N/n_group contiguous
+  experts, group score = sum of the two largest z, keep the topk_group best groups (equal
+  scores -> lower group index), then top-K inside them;
+* bias step b <- b + fl32(-gamma * sign(load - T K / N)), sign(0) = 0, compared in
+  integers as load * N vs T * K;
+* E4M3 = OCP E4M3FN (bias 7, max 448, no infinities); q = RNE(fl32(v / s)) with
+  s = fl32(amax / 448), saturating at +/-448, amax = 0 -> s = 1; the sign bit of q is the
+  sign bit of v (so a negative value that rounds to zero gives code 0x80).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+# --------------------------------------------------------------------------------------
+# Rounding helpers (definitions of the storage formats; not shared with the GPU side)
+# --------------------------------------------------------------------------------------
+
+
+def bf16_round(a) -> np.ndarray:
+    """Round to the nearest bfloat16 value (8 significant bits), ties to even.
+
+    Written from the definition of the format: |v| = m * 2^e with m in [0.5, 1); keep
+    round_half_even(m * 2^8) * 2^(e - 8).  Works for float32 or float64 input and returns
+    float64 holding bf16-representable values.  (Overflow past the bf16 range is not
+    handled; the layer never produces such values.)
+    """
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def fp32_round(a) -> np.ndarray:
+    """Round to the nearest float32 value (IEEE RNE), returned as float64."""
+    return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------------------
+# E4M3 (OCP E4M3FN) codec.  [TR] "FP8 混合精度訓練" -> "E4M3 統一".
+# --------------------------------------------------------------------------------------
+
+
+def _e4m3_positive_table() -> np.ndarray:
+    """Values of the 127 non-negative finite codes 0x00..0x7E, in code order.
+
+    Code = (E << 3) | M.  E = 0: subnormal, value M * 2^-9.  E >= 1: (1 + M/8) * 2^(E-7).
+    Code 0x7F (E = 15, M = 7) is NaN; there is no infinity.
+    """
+    vals = np.empty(127, dtype=np.float64)
+    for code in range(127):
+        E, M = code >> 3, code & 7
+        vals[code] = M * 2.0 ** -9 if E == 0 else (1.0 + M / 8.0) * 2.0 ** (E - 7)
+    return vals
+
+
+_E4M3_POS = _e4m3_positive_table()
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8)
+    mag = codes & 0x7F
+    out = np.where(mag == 0x7F, np.nan, _E4M3_POS[np.minimum(mag, 126)])
+    return np.where(codes & 0x80, -out, out)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Encode real values (taken exactly as given) to E4M3 codes.
+
+    Round to nearest, ties to the even code (the one whose mantissa LSB is 0); magnitudes
+    at or above 448 saturate to 448; NaN -> 0x7F (with the input's sign bit).
+    The nearest value is found by a search over the table of representable magnitudes.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    sign = np.signbit(v)
+    a = np.abs(v)
+    nan = np.isnan(a)
+    a = np.where(nan, 0.0, a)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")  # first table value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_hi = _E4M3_POS[hi] - a
+    d_lo = a - _E4M3_POS[lo]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a >= E4M3_MAX, 126, code)
+    code = np.where(_E4M3_POS[hi] == a, hi, code)  # exact hits
+    code = np.where(nan, 0x7F, code).astype(np.uint8)
+    return np.where(sign, code | 0x80, code).astype(np.uint8)
+
+
+def e4m3_half_ulp(v) -> np.ndarray:
+    """Half the E4M3 spacing at magnitude |v| (|v| <= 448).
+
+    The spacing is 2^(floor(log2|v|) - 3) for |v| >= 2^-6 and 2^-9 below.
+    """
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return 0.5 * 2.0 ** (e - 3)
+
+
+def _tile_scale(amax32: np.ndarray) -> np.ndarray:
+    """s = fl32(amax / 448) in IEEE float32; an all-zero tile gets s = 1."""
+    s = (amax32.astype(np.float32) / np.float32(E4M3_MAX)).astype(np.float32)
+    return np.where(amax32 == 0, np.float32(1.0), s).astype(np.float32)
+
+
+def quant_1x128(x):
+    """Online 1x128 tile quantisation of activations.  [TR] "FP8 混合精度訓練" ->
+    "細粒度量子化" (activation tiles 1x128) and "オンライン量子化" (scale from the
+    tile's current max |x|).
+
+    x: [rows, cols] values representable in float32 (cols % 128 == 0).
+    Returns (q uint8 [rows, cols], s float32 [rows, cols // 128]).
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    rows, cols = x32.shape
+    assert cols % 128 == 0
+    t = x32.reshape(rows, cols // 128, 128)
+    amax = np.max(np.abs(t), axis=2)
+    s = _tile_scale(amax)
+    v = (t / s[:, :, None]).astype(np.float32)  # IEEE float32 division
+    q = e4m3_encode(v).reshape(rows, cols)
+    return q, s
+
+
+def quant_128x128(w):
+    """128x128 block quantisation of a weight matrix [n, k] (n, k % 128 == 0).
+    [TR] "FP8 混合精度訓練" -> "細粒度量子化" (weights per 128x128 block).
+    Returns (q uint8 [n, k], s float32 [n // 128, k // 128])."""
+    w32 = np.asarray(w, dtype=np.float32)
+    n, k = w32.shape
+    assert n % 128 == 0 and k % 128 == 0
+    b = w32.reshape(n // 128, 128, k // 128, 128)
+    amax = np.max(np.abs(b), axis=(1, 3))
+    s = _tile_scale(amax)
+    v = (b / s[:, None, :, None]).astype(np.float32)
+    q = e4m3_encode(v).reshape(n, k)
+    return q, s
+
+
+def dequant_1x128(q, s) -> np.ndarray:
+    rows, cols = q.shape
+    return (e4m3_decode(q).reshape(rows, cols // 128, 128) * s.astype(np.float64)[:, :, None]).reshape(rows, cols)
+
+
+def dequant_128x128(q, s) -> np.ndarray:
+    n, k = q.shape
+    v = e4m3_decode(q).reshape(n // 128, 128, k // 128, 128)
+    return (v * s.astype(np.float64)[:, None, :, None]).reshape(n, k)
+
+
+# --------------------------------------------------------------------------------------
+# Routing.  [TR] "DeepSeekMoE と補助損失なしの負荷分散".
+# --------------------------------------------------------------------------------------
+
+
+def sigmoid(u):
+    u = np.asarray(u, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-u))
+
+
+def _rank_desc(values: np.ndarray, ids: np.ndarray):
+    """Order candidates by value descending, equal values by id ascending; NaN last."""
+    key = np.where(np.isnan(values), -np.inf, values)
+    order = sorted(range(len(ids)), key=lambda j: (-key[j], ids[j]))
+    return [int(ids[j]) for j in order], [float(key[j]) for j in order]
+
+
+def route(x, w_router, bias, top_k: int, n_group: int = 1, topk_group: int = 1):
+    """Affinity, bias-adjusted selection and gates for every token.
+
+    s_{t,i} = sigmoid(x_t . e_i); z_{t,i} = s_{t,i} + b_i; S_t = the top_k experts by z
+    (restricted to the topk_group best groups when n_group > 1); gates are the selected
+    ORIGINAL affinities s normalised to sum to one -- the bias only decides selection.
+
+    Returns a dict with idx [T, K] (descending z), gate [T, K], s [T, N], z [T, N], and the
+    tie margins used by parity tests: ``margin`` (z of the K-th pick minus the best
+    non-picked allowed z) and ``group_margin`` (score of the last kept group minus the best
+    dropped group; +inf without groups).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_router, dtype=np.float64)
+    b = np.asarray(bias, dtype=np.float64)
+    T = x.shape[0]
+    N = w.shape[0]
+    assert 1 <= top_k <= N and N % n_group == 0
+    gsz = N // n_group
+    if n_group > 1:
+        assert gsz >= 2 and 1 <= topk_group <= n_group and top_k <= topk_group * gsz
+    s = sigmoid(x @ w.T)
+    z = s + b[None, :]
+    idx = np.zeros((T, top_k), dtype=np.int64)
+    gate = np.zeros((T, top_k), dtype=np.float64)
+    margin = np.full(T, np.inf)
+    gmargin = np.full(T, np.inf)
+    for t in range(T):
+        allowed = np.arange(N)
+        if n_group > 1:
+            gscore = np.empty(n_group)
+            for g in range(n_group):
+                zz = np.sort(np.where(np.isnan(z[t, g * gsz:(g + 1) * gsz]), -np.inf,
+                                      z[t, g * gsz:(g + 1) * gsz]))[::-1]
+                gscore[g] = zz[0] + zz[1]
+            gorder, gvals = _rank_desc(gscore, np.arange(n_group))
+            kept = sorted(gorder[:topk_group])
+            if topk_group < n_group:
+                gmargin[t] = gvals[topk_group - 1] - gvals[topk_group]
+            allowed = np.concatenate([np.arange(g * gsz, (g + 1) * gsz) for g in kept])
+        order, vals = _rank_desc(z[t, allowed], allowed)
+        sel = order[:top_k]
+        if top_k < len(order):
+            margin[t] = vals[top_k - 1] - vals[top_k]
+        idx[t] = sel
+        ss = s[t, sel]
+        gate[t] = ss / ss.sum()
+    return {"idx": idx, "gate": gate, "s": s, "z": z, "margin": margin, "group_margin": gmargin}
+
+
+# --------------------------------------------------------------------------------------
+# Load histogram, permutation, combine, bias update.
+# --------------------------------------------------------------------------------------
+
+
+def expert_counts(idx, n_experts: int) -> np.ndarray:
+    """load_i = number of (token, slot) pairs routed to expert i over the whole batch
+    ([TR] "DeepSeekMoE と補助損失なしの負荷分散": the load is monitored over the batch)."""
+    counts = np.zeros(n_experts, dtype=np.int64)
+    for e in np.asarray(idx).reshape(-1):
+        counts[e] += 1
+    return counts
+
+
+def permute(idx, n_experts: int, n_shared: int = 1):
+    """Expert-major, token-ascending order of all (token, slot) pairs (a counting sort),
+    followed by one segment of all T tokens in order for the shared expert.
+
+    Returns (offsets [n_experts + n_shared + 1], sorted_token [T*(K+n_shared)],
+    pair_pos [T, K]) with sorted_token[pair_pos[t, k]] == t.
+    """
+    idx = np.asarray(idx)
+    T, K = idx.shape
+    counts = expert_counts(idx, n_experts)
+    offsets = np.zeros(n_experts + n_shared + 1, dtype=np.int64)
+    for e in range(n_experts):
+        offsets[e + 1] = offsets[e] + counts[e]
+    for j in range(n_shared):
+        offsets[n_experts + j + 1] = offsets[n_experts + j] + T
+    cursor = offsets[:n_experts].copy()
+    sorted_token = np.zeros(T * (K + n_shared), dtype=np.int64)
+    pair_pos = np.zeros((T, K), dtype=np.int64)
+    for t in range(T):
+        for k in range(K):
+            e = idx[t, k]
+            pos = cursor[e]
+            cursor[e] += 1
+            sorted_token[pos] = t
+            pair_pos[t, k] = pos
+    for j in range(n_shared):
+        base = offsets[n_experts + j]
+        sorted_token[base:base + T] = np.arange(T)
+    return offsets, sorted_token, pair_pos
+
+
+def combine(y_routed, y_shared, pair_pos, gate) -> np.ndarray:
+    """out_t = y_shared[t] + sum_k gate[t, k] * y_routed[pair_pos[t, k]] (float64).
+    ([PFN] "MoEの歴史とDeepSeekMoE-V3の特徴": the chosen experts' results come back and are
+    merged with the always-on shared expert; [TR] "DualPipe パイプライン並列化": the
+    combine stage.)"""
+    y_routed = np.asarray(y_routed, dtype=np.float64)
+    pair_pos = np.asarray(pair_pos)
+    gate = np.asarray(gate, dtype=np.float64)
+    T, K = pair_pos.shape
+    out = np.zeros((T, y_routed.shape[1]))
+    for k in range(K):
+        out += gate[:, k:k + 1] * y_routed[pair_pos[:, k]]
+    if y_shared is not None:
+        out += np.asarray(y_shared, dtype=np.float64)
+    return out
+
+
+def bias_update(bias, counts, T: int, top_k: int, gamma: float) -> np.ndarray:
+    """Aux-loss-free bias step ([TR] "DeepSeekMoE と補助損失なしの負荷分散"): an overloaded
+    expert's bias drops by gamma, an underloaded one's rises by gamma, an expert exactly at
+    the mean load T*K/N is left alone.  One float32 add per expert."""
+    bias32 = np.asarray(bias, dtype=np.float32)
+    counts = np.asarray(counts, dtype=np.int64)
+    N = bias32.shape[0]
+    diff = counts * N - int(T) * int(top_k)  # load - mean, scaled by N, in integers
+    step = np.where(diff > 0, np.float32(-gamma), np.float32(gamma)).astype(np.float32)
+    moved = (bias32 + step).astype(np.float32)
+    return np.where(diff == 0, bias32, moved).astype(np.float32)
+
+
+# --------------------------------------------------------------------------------------
+# Expert FFN and the whole layer.
+# --------------------------------------------------------------------------------------
+
+
+def silu(a):
+    a = np.asarray(a, dtype=np.float64)
+    return a / (1.0 + np.exp(-a))
+
+
+def swiglu_hidden(x_rows, w13) -> np.ndarray:
+    """h = silu(x W1^T) * (x W3^T) with W1 = w13[:I], W3 = w13[I:] (float64)."""
+    I = w13.shape[0] // 2
+    w13 = np.asarray(w13, dtype=np.float64)
+    a = x_rows @ w13[:I].T
+    c = x_rows @ w13[I:].T
+    return silu(a) * c
+
+
+def swiglu_ffn(x_rows, w13, w2) -> np.ndarray:
+    """Expert FFN: W2 (silu(W1 x) * (W3 x)), float64, no intermediate rounding."""
+    return swiglu_hidden(np.asarray(x_rows, dtype=np.float64), w13) @ np.asarray(w2, np.float64).T
+
+
+def forward_dense(x, w_router, bias, w13, w2, top_k, n_group=1, topk_group=1):
+    """The layer as a dense masked mixture over ALL experts (tiny shapes only):
+    out_t = FFN_shared(x_t) + sum_i G_{t,i} FFN_i(x_t), G zero outside the selection.
+    w13: [N+1, 2I, d], w2: [N+1, d, I]; the shared expert is index N."""
+    x = np.asarray(x, dtype=np.float64)
+    N = np.asarray(w_router).shape[0]
+    r = route(x, w_router, bias, top_k, n_group, topk_group)
+    T = x.shape[0]
+    G = np.zeros((T, N))
+    for t in range(T):
+        G[t, r["idx"][t]] = r["gate"][t]
+    out = swiglu_ffn(x, w13[N], w2[N])
+    for i in range(N):
+        out = out + G[:, i:i + 1] * swiglu_ffn(x, w13[i], w2[i])
+    return out, r
+
+
+def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str = "exact"):
+    """The layer computed the sparse way: permute, per-expert FFN on gathered rows, combine.
+
+    idx, gate: [T, K] routing decisions and gates (from ``route``).
+    expert_weights(e) -> (w13_e [2I, d], w2_e [d, I]) for e in 0..n_experts, where
+    e == n_experts is the shared expert.
+    precision:
+      "exact" -- float64 throughout;
+      "bf16"  -- models the stored bfloat16 intermediates: h and the routed expert outputs
+                 are rounded to bf16, the shared expert output to float32;
+      "fp8"   -- models the FP8 path of [TR] "FP8 混合精度訓練": x quantised per 1x128
+                 tile, weights per 128x128 block, h (as float32) re-quantised per 1x128
+                 tile along I, products accumulated exactly (float64 stands in for the
+                 FP32 promotion every 128 elements), routed outputs rounded to bf16,
+                 shared output to float32.
+    Returns (out [T, d] float64, extras dict with the permutation and per-row outputs).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    idx = np.asarray(idx)
+    gate = np.asarray(gate, dtype=np.float64)
+    T, K = idx.shape
+    offsets, sorted_token, pair_pos = permute(idx, n_experts, 1)
+    if precision == "fp8":
+        xq, xs = quant_1x128(x)
+        x_in = dequant_1x128(xq, xs)
+    else:
+        x_in = x
+    d = x.shape[1]
+    y_routed = np.zeros((T * K, d))
+    y_shared = np.zeros((T, d))
+    for e in range(n_experts + 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        we13, we2 = expert_weights(e)
+        y = expert_rows(x_in[sorted_token[lo:hi]], we13, we2, precision)
+        if e < n_experts:
+            y_routed[lo:hi] = bf16_round(y) if precision in ("bf16", "fp8") else y
+        else:
+            y_shared[:] = fp32_round(y) if precision in ("bf16", "fp8") else y
+    out = combine(y_routed, y_shared, pair_pos, gate)
+    return out, {"offsets": offsets, "sorted_token": sorted_token, "pair_pos": pair_pos,
+                 "y_routed": y_routed, "y_shared": y_shared}
+
+
+def expert_rows(rows, w13, w2, precision: str = "exact", return_h: bool = False):
+    """One expert's FFN on already-gathered input rows (already dequantised on the fp8
+    path), with the intermediate rounding of ``precision`` (see ``forward_sparse``).
+    Returns y [m, d] before its own storage rounding (and h as stored, if asked)."""
+    rows = np.asarray(rows, dtype=np.float64)
+    if precision == "fp8":
+        q13, s13 = quant_128x128(w13)
+        q2, s2 = quant_128x128(w2)
+        h = swiglu_hidden(rows, dequant_128x128(q13, s13))
+        hq, hs = quant_1x128(fp32_round(h))
+        h_st = dequant_1x128(hq, hs)
+        y = h_st @ dequant_128x128(q2, s2).T
+    else:
+        h = swiglu_hidden(rows, w13)
+        h_st = bf16_round(h) if precision == "bf16" else h
+        y = h_st @ np.asarray(w2, dtype=np.float64).T
+    return (y, h_st) if return_h else y
+
+
+def forward(x, w_router, bias, w13, w2, top_k, n_group=1, topk_group=1, precision="exact"):
+    """Route on the (bf16) input in high precision, then run the sparse layer.
+    w13: [N+1, 2I, d], w2: [N+1, d, I]; the shared expert is index N."""
+    N = np.asarray(w_router).shape[0]
+    r = route(x, w_router, bias, top_k, n_group, topk_group)
+    out, extra = forward_sparse(x, r["idx"], r["gate"], N, lambda e: (w13[e], w2[e]), precision)
+    return out, r, extra
+
+
+def layer_flops(T: int, d: int, n_experts: int, top_k: int, inter: int, n_shared: int = 1) -> int:
+    """Algorithmic FLOPs of one forward: router 2 T d N plus 6 d I per active expert-row."""
+    return 2 * T * d * n_experts + 6 * d * inter * T * (top_k + n_shared)

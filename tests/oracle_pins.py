@@ -1,0 +1,367 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with its pin.
+``test_oracle_pins.py`` runs them; ``test_oracle_mutations.py`` plants plausible mistakes
+in the oracle and checks that at least one pin fails for each.
+
+What the pins rest on:
+* library routines: torch's bfloat16 and float8_e4m3fn conversions, torch.sigmoid,
+  torch.nn.functional.silu and matmul, numpy bincount / stable argsort;
+* the OCP E4M3FN format's published constants (max 448, min subnormal 2^-9, ...);
+* brute force over all K-subsets / all expert pairs on tiny inputs;
+* closed forms (hand-computed bias steps, exactly representable fp8 products);
+* invariants the pages fix ("DeepSeek-V3 Technical Report" wiki summary,
+  "DeepSeekMoE と補助損失なしの負荷分散": K distinct experts per token, gates from the
+  normalised original affinities so they sum to one and do not depend on the bias,
+  overloaded -> -gamma, underloaded -> +gamma, no token dropped).
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import torch
+
+from oracle import moe_oracle as O
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------------ storage formats
+
+
+def pin_bf16_round_vs_torch():
+    r = _rng(1)
+    v = (r.standard_normal(20000) * np.exp2(r.integers(-30, 30, 20000))).astype(np.float32)
+    # exact midpoints between neighbouring bf16 values (ties must go to even)
+    b = torch.from_numpy(r.standard_normal(4000).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    mid = (b.view(np.uint32) + np.uint32(0x8000)).view(np.float32)
+    v = np.concatenate([v, mid, -mid, np.float32([0.0, 1.0, -2.5])])
+    ref = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+    got = O.bf16_round(v)
+    assert np.array_equal(got, ref), "bf16 rounding differs from torch"
+
+
+def pin_e4m3_constants():
+    d = O.e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert d[0x7E] == 448.0 and d[0xFE] == -448.0          # largest finite
+    assert d[0x01] == 2.0 ** -9                            # smallest subnormal
+    assert d[0x07] == 7 * 2.0 ** -9                        # largest subnormal
+    assert d[0x08] == 2.0 ** -6                            # smallest normal
+    assert d[0x38] == 1.0 and d[0x39] == 1.125 and d[0x40] == 2.0
+    assert d[0x00] == 0.0 and np.signbit(d[0x80])
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF])
+    assert np.sum(np.isnan(d)) == 2                        # no other NaN, no infinities
+    assert np.all(np.isfinite(d[~np.isnan(d)]))
+
+
+def pin_e4m3_vs_torch():
+    r = _rng(2)
+    v = np.concatenate([
+        r.uniform(-448, 448, 50000),
+        r.standard_normal(50000) * np.exp2(r.integers(-12, 8, 50000)),
+    ]).astype(np.float32)
+    pos = O.e4m3_decode(np.arange(0, 127, dtype=np.uint8))
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)     # exact in fp32
+    v = np.concatenate([v, mids, -mids, pos.astype(np.float32)])
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_encode(v)
+    assert np.array_equal(got, ref), "E4M3 encode differs from torch.float8_e4m3fn"
+
+
+def pin_e4m3_roundtrip_ties_saturation():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(codes)), codes)
+    pos = O.e4m3_decode(np.arange(0, 127, dtype=np.uint8))
+    for c in range(126):  # midpoint between code c and c+1 goes to the even one
+        m = (pos[c] + pos[c + 1]) / 2
+        want = c if c % 2 == 0 else c + 1
+        assert O.e4m3_encode(m) == want, (c, m)
+        # just off the midpoint goes to the nearer one
+        assert O.e4m3_encode(np.nextafter(m, 0)) == c
+        assert O.e4m3_encode(np.nextafter(m, 1e9)) == c + 1
+    assert O.e4m3_encode(449.0) == 0x7E and O.e4m3_encode(1e30) == 0x7E
+    assert O.e4m3_encode(-500.0) == 0xFE
+    assert O.e4m3_encode(-1e-6) == 0x80 and O.e4m3_encode(1e-6) == 0x00
+
+
+def pin_quant_1x128_properties():
+    r = _rng(3)
+    x = r.standard_normal((37, 512)).astype(np.float32)
+    x[5, 128:256] = 0.0                                     # an all-zero tile
+    x[7, 300] = 250.0                                       # an outlier tile
+    x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    q, s = O.quant_1x128(x)
+    assert q.shape == x.shape and s.shape == (37, 4) and s.dtype == np.float32
+    t = np.abs(x).reshape(37, 4, 128)
+    amax = t.max(axis=2)
+    nz = amax > 0
+    assert np.array_equal(s[nz], (amax[nz].astype(np.float32) / np.float32(448)))
+    assert s[5, 1] == 1.0 and np.all(q[5, 128:256] == 0)
+    # the element equal to the tile max maps to +/-448 exactly
+    j = np.argmax(t, axis=2)
+    for rr in range(37):
+        for c in range(4):
+            if nz[rr, c]:
+                assert (q[rr, c * 128 + j[rr, c]] & 0x7F) == 0x7E
+    # quantise-dequantise error <= half an E4M3 step at |x|/s, times s
+    deq = O.dequant_1x128(q, s)
+    sc = np.repeat(s.astype(np.float64), 128, axis=1)
+    bound = O.e4m3_half_ulp(x / sc) * sc
+    assert np.all(np.abs(deq - x) <= bound * (1 + 1e-6))
+
+
+def pin_quant_exact_layouts():
+    """Tiles/blocks whose values are E4M3 numbers times a per-tile power of two quantise
+    exactly, so dequant(quant(x)) == x; distinct scales per tile/block catch any mix-up of
+    which scale belongs to which tile (a transposed scale index, a wrong tile width)."""
+    r = _rng(4)
+    pos = O.e4m3_decode(np.arange(0, 127, dtype=np.uint8))
+    rows, cols = 6, 384
+    codes = r.integers(0, 127, size=(rows, cols))
+    vals = pos[codes] * np.where(r.random((rows, cols)) < 0.5, -1, 1)
+    e = r.integers(-6, 4, size=(rows, cols // 128))
+    x = vals.reshape(rows, 3, 128).copy()
+    x[:, :, 0] = 448.0                                     # pin every tile's amax
+    x = x * np.exp2(e)[:, :, None]
+    x = x.reshape(rows, cols)
+    q, s = O.quant_1x128(x)
+    assert np.array_equal(s, np.exp2(e).astype(np.float32))
+    assert np.array_equal(O.dequant_1x128(q, s), x)
+    # 128x128 blocks of a [256, 384] weight, each with its own power-of-two scale
+    n, k = 256, 384
+    codes = r.integers(0, 127, size=(n, k))
+    w = (pos[codes] * np.where(r.random((n, k)) < 0.5, -1, 1)).reshape(2, 128, 3, 128)
+    eb = r.integers(-9, -3, size=(2, 3))
+    w[:, 0, :, 0] = 448.0
+    w = (w * np.exp2(eb)[:, None, :, None]).reshape(n, k)
+    qw, sw = O.quant_128x128(w)
+    assert np.array_equal(sw, np.exp2(eb).astype(np.float32))
+    assert np.array_equal(O.dequant_128x128(qw, sw), w)
+    # exact GEMM of exactly-representable operands: integer arithmetic gives the result
+    # (every tile holds a 7, so s = 7/448 = 2^-6 and the codes are exact)
+    a_int = r.integers(-7, 8, size=(4, k))
+    b_int = r.integers(-7, 8, size=(5, k))
+    a_int[:, ::128] = 7
+    b_int[:, ::128] = -7
+    qa, sa = O.quant_1x128(a_int.astype(np.float32))
+    qb, sb = O.quant_1x128(b_int.astype(np.float32))
+    got = O.dequant_1x128(qa, sa) @ O.dequant_1x128(qb, sb).T
+    assert np.array_equal(got, (a_int @ b_int.T).astype(np.float64))
+
+
+# ------------------------------------------------------------------ routing
+
+
+def _tiny_router(seed, T=24, d=32, N=8, scale=1.0):
+    r = _rng(seed)
+    x = r.standard_normal((T, d))
+    w = r.standard_normal((N, d)) * 0.3 * scale
+    b = r.uniform(-0.05, 0.05, N).astype(np.float32)
+    return x, w, b
+
+
+def pin_route_bruteforce():
+    """Top-K by z equals the K-subset of largest total z (all subsets enumerated); gates
+    are the subset's sigmoid affinities (torch.sigmoid) over their sum."""
+    for seed in range(4):
+        x, w, b = _tiny_router(seed)
+        K = 3
+        r = O.route(x, w, b, K)
+        s_ref = torch.sigmoid(torch.from_numpy(x) @ torch.from_numpy(w).T).numpy()
+        z_ref = s_ref + b.astype(np.float64)
+        assert np.allclose(r["s"], s_ref, rtol=0, atol=1e-15)
+        for t in range(x.shape[0]):
+            best = max(itertools.combinations(range(w.shape[0]), K),
+                       key=lambda S: sum(z_ref[t, list(S)]))
+            assert set(r["idx"][t]) == set(best)
+            assert len(set(r["idx"][t])) == K
+            # descending z order
+            assert all(z_ref[t, r["idx"][t][i]] >= z_ref[t, r["idx"][t][i + 1]] for i in range(K - 1))
+            g = s_ref[t, list(r["idx"][t])]
+            assert np.allclose(r["gate"][t], g / g.sum(), rtol=0, atol=1e-15)
+            assert abs(r["gate"][t].sum() - 1.0) < 1e-14
+
+
+def pin_route_bias_only_selects():
+    x, w, b = _tiny_router(11)
+    K = 2
+    r0 = O.route(x, w, b, K)
+    # a constant shift of every bias changes nothing
+    r1 = O.route(x, w, b + np.float32(0.25), K)
+    assert np.array_equal(r0["idx"], r1["idx"]) and np.allclose(r0["gate"], r1["gate"], atol=1e-15)
+    # forcing expert j: it is picked for every token and its gate is still s_j / sum s
+    j = 5
+    bf = b.copy()
+    bf[j] = 10.0
+    rf = O.route(x, w, bf, K)
+    s = torch.sigmoid(torch.from_numpy(x) @ torch.from_numpy(w).T).numpy()
+    for t in range(x.shape[0]):
+        assert rf["idx"][t][0] == j
+        sel = list(rf["idx"][t])
+        assert np.allclose(rf["gate"][t], s[t, sel] / s[t, sel].sum(), atol=1e-15)
+    # two bias vectors that give the same selection give bit-identical gates
+    rb = O.route(x, w, b * np.float32(1.0001), K)
+    same = np.all(np.sort(rb["idx"], 1) == np.sort(r0["idx"], 1), axis=1)
+    assert same.any()
+    for t in np.nonzero(same)[0]:
+        g0 = dict(zip(r0["idx"][t], r0["gate"][t]))
+        g1 = dict(zip(rb["idx"][t], rb["gate"][t]))
+        assert all(g0[e] == g1[e] for e in g0)
+
+
+def pin_route_special_cases():
+    x, w, b = _tiny_router(12)
+    N = w.shape[0]
+    r = O.route(x, w, b, N)                         # K = N: every expert, gates = s / sum s
+    s = torch.sigmoid(torch.from_numpy(x) @ torch.from_numpy(w).T).numpy()
+    for t in range(x.shape[0]):
+        g = dict(zip(r["idx"][t], r["gate"][t]))
+        assert np.allclose([g[e] for e in range(N)], s[t] / s[t].sum(), atol=1e-15)
+    # one group is the ungrouped router
+    ra = O.route(x, w, b, 3)
+    rg = O.route(x, w, b, 3, n_group=1, topk_group=1)
+    assert np.array_equal(ra["idx"], rg["idx"])
+    # keeping every group is the ungrouped router too
+    rk = O.route(x, w, b, 3, n_group=4, topk_group=4)
+    assert np.array_equal(ra["idx"], rk["idx"])
+    # exact ties: equal z -> the lower index first
+    xt = np.zeros((1, 4))
+    wt = np.zeros((6, 4))
+    rt = O.route(xt, wt, np.zeros(6, np.float32), 3)
+    assert list(rt["idx"][0]) == [0, 1, 2] and np.allclose(rt["gate"][0], 1 / 3)
+
+
+def pin_route_groups_bruteforce():
+    """Group-limited routing: group score = the best pair sum inside the group (all pairs
+    enumerated), the topk_group best groups kept, then the best K-subset inside them."""
+    for seed in range(3):
+        x, w, b = _tiny_router(20 + seed, T=16, N=12)
+        n_group, topk_group, K = 4, 2, 3
+        r = O.route(x, w, b, K, n_group, topk_group)
+        s = torch.sigmoid(torch.from_numpy(x) @ torch.from_numpy(w).T).numpy()
+        z = s + b.astype(np.float64)
+        gs = 12 // n_group
+        for t in range(x.shape[0]):
+            score = [max(z[t, g * gs + i] + z[t, g * gs + j] for i, j in itertools.combinations(range(gs), 2))
+                     for g in range(n_group)]
+            kept = max(itertools.combinations(range(n_group), topk_group),
+                       key=lambda G: sum(score[g] for g in G))
+            allowed = [e for g in kept for e in range(g * gs, (g + 1) * gs)]
+            best = max(itertools.combinations(allowed, K), key=lambda S: sum(z[t, list(S)]))
+            assert set(r["idx"][t]) == set(best), (seed, t)
+            assert all((e // gs) in kept for e in r["idx"][t])
+
+
+# ------------------------------------------------------------------ permutation, counts
+
+
+def pin_counts_and_permute():
+    r = _rng(5)
+    T, K, N = 50, 3, 7
+    idx = np.stack([r.permutation(N)[:K] for _ in range(T)])
+    counts = O.expert_counts(idx, N)
+    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=N))
+    assert counts.sum() == T * K
+    off, st, pp = O.permute(idx, N, 1)
+    assert off[0] == 0 and np.array_equal(np.diff(off[:N + 1]), np.bincount(idx.ravel(), minlength=N))
+    assert off[N + 1] == T * K + T
+    order = np.argsort(idx.ravel(), kind="stable")          # expert-major, token order
+    assert np.array_equal(st[:T * K], order // K)
+    inv = np.empty(T * K, dtype=np.int64)
+    inv[order] = np.arange(T * K)
+    assert np.array_equal(pp.ravel(), inv)
+    assert np.array_equal(st[T * K:], np.arange(T))
+    for t in range(T):
+        for k in range(K):
+            assert st[pp[t, k]] == t
+
+
+def pin_bias_update_closed_form():
+    # N = 4 experts, T = 2 tokens, K = 2: mean load 1.  Loads 2, 1, 1, 0.
+    b = np.float32([0.5, -0.25, 0.0, 1.0])
+    got = O.bias_update(b, np.array([2, 1, 1, 0]), T=2, top_k=2, gamma=0.125)
+    assert np.array_equal(got, np.float32([0.375, -0.25, 0.0, 1.125]))
+    # balanced loads leave every bias (bit pattern included) alone
+    bz = np.float32([-0.0, 0.1, -3.0, 7.5])
+    got = O.bias_update(bz, np.array([1, 1, 1, 1]), T=2, top_k=2, gamma=0.001)
+    assert np.array_equal(got.view(np.uint32), bz.view(np.uint32))
+    # fl32(0.1f - 0.001f) = 0x3DCAC083 (found by exact rational arithmetic on the two floats)
+    got = O.bias_update(np.float32([0.1, 0.1]), np.array([2, 0]), T=2, top_k=1, gamma=0.001)
+    assert got.view(np.uint32)[0] == 0x3DCAC083 and got[1] > np.float32(0.1)
+
+
+# ------------------------------------------------------------------ FFN and the layer
+
+
+def _tiny_layer(seed, T=20, d=24, N=6, I=10, scale=0.3):
+    r = _rng(seed)
+    x = r.standard_normal((T, d))
+    wr = r.standard_normal((N, d)) * scale
+    b = r.uniform(-0.05, 0.05, N).astype(np.float32)
+    w13 = r.standard_normal((N + 1, 2 * I, d)) * scale
+    w2 = r.standard_normal((N + 1, d, I)) * scale
+    return x, wr, b, w13, w2
+
+
+def pin_single_expert_is_plain_swiglu():
+    """N = K = 1: the layer is two SwiGLU MLPs added (torch silu / matmul, float64)."""
+    x, wr, b, w13, w2 = _tiny_layer(6, N=1)
+    I = w13.shape[1] // 2
+    out, r, _ = O.forward(x, wr, b, w13, w2, top_k=1)
+    X = torch.from_numpy(x)
+
+    def mlp(e):
+        W1, W3 = torch.from_numpy(w13[e, :I]), torch.from_numpy(w13[e, I:])
+        return (torch.nn.functional.silu(X @ W1.T) * (X @ W3.T)) @ torch.from_numpy(w2[e]).T
+
+    ref = (mlp(0) + mlp(1)).numpy()
+    assert np.allclose(r["gate"], 1.0)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_dense_equals_sparse():
+    for seed, (ng, tg) in zip(range(3), [(1, 1), (3, 2), (2, 1)]):
+        x, wr, b, w13, w2 = _tiny_layer(30 + seed)
+        dense, r = O.forward_dense(x, wr, b, w13, w2, top_k=2, n_group=ng, topk_group=tg)
+        sparse, _, _ = O.forward(x, wr, b, w13, w2, top_k=2, n_group=ng, topk_group=tg)
+        assert np.allclose(dense, sparse, rtol=0, atol=1e-12)
+
+
+def pin_combine_closed_form():
+    y = np.array([[1.0, 2.0], [10.0, 20.0], [100.0, 200.0]])
+    sh = np.array([[0.5, 0.25], [-1.0, 1.0]])
+    pp = np.array([[2, 0], [1, 2]])
+    g = np.array([[0.75, 0.25], [0.5, 0.5]])
+    out = O.combine(y, sh, pp, g)
+    assert np.array_equal(out, np.array([[75.75, 150.75], [54.0, 111.0]]))
+
+
+def pin_fp8_layer_close_to_exact():
+    """The fp8 model is an approximation of the exact layer: small relative error."""
+    r = _rng(7)
+    T, d, N, I = 16, 256, 4, 128
+    x = torch.from_numpy(r.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    wr = r.standard_normal((N, d)) * 0.05
+    b = np.zeros(N, np.float32)
+    w13 = r.standard_normal((N + 1, 2 * I, d)) * 0.05
+    w2 = r.standard_normal((N + 1, d, I)) * 0.05
+    ex, _, _ = O.forward(x, wr, b, w13, w2, 2, precision="exact")
+    f8, _, _ = O.forward(x, wr, b, w13, w2, 2, precision="fp8")
+    bf, _, _ = O.forward(x, wr, b, w13, w2, 2, precision="bf16")
+    rms = np.sqrt(np.mean(ex ** 2))
+    # E4M3 keeps 3 mantissa bits (relative step 1/16 .. 1/8): a few percent RMS error
+    assert np.sqrt(np.mean((f8 - ex) ** 2)) / rms < 0.1
+    assert np.max(np.abs(f8 - ex)) / rms < 0.4
+    assert np.max(np.abs(bf - ex)) / rms < 0.03
+    assert np.max(np.abs(f8 - ex)) > np.max(np.abs(bf - ex))  # fp8 really quantises
+
+
+def pin_layer_flops():
+    # DeepSeek-V3 shape: 9 of 257 experts per token; 2*7168*256 + 6*7168*2048*9 per token
+    assert O.layer_flops(1, 7168, 256, 8, 2048) == 796_393_472
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

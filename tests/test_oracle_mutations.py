@@ -1,0 +1,175 @@
+"""Plant plausible mistakes in the CPU oracle and check that its pins catch every one.
+
+A pin set that lets a dropped term, a wrong sign, a swapped operand or a wrong rounding
+rule through would not justify trusting the oracle; each mutation below must make at
+least one pin fail.  The mutations are applied with monkeypatch, on the CPU only.
+"""
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from tests import oracle_pins as P
+
+
+def _any_pin_fails():
+    for pin in P.ALL_PINS:
+        try:
+            pin()
+        except Exception:
+            return pin.__name__
+    return None
+
+
+def _mut_gate_from_z(mp):
+    real = O.route
+
+    def route(x, w, b, k, n_group=1, topk_group=1):
+        r = real(x, w, b, k, n_group, topk_group)
+        zz = np.take_along_axis(r["z"], r["idx"], 1)
+        r["gate"] = zz / zz.sum(1, keepdims=True)
+        return r
+    mp.setattr(O, "route", route)
+
+
+def _mut_ascending(mp):
+    real = O._rank_desc
+
+    def rank(values, ids):
+        o, v = real(values, ids)
+        return o[::-1], v[::-1]
+    mp.setattr(O, "_rank_desc", rank)
+
+
+def _mut_tie_higher_index(mp):
+    def rank(values, ids):
+        key = np.where(np.isnan(values), -np.inf, values)
+        order = sorted(range(len(ids)), key=lambda j: (-key[j], -ids[j]))
+        return [int(ids[j]) for j in order], [float(key[j]) for j in order]
+    mp.setattr(O, "_rank_desc", rank)
+
+
+def _mut_silu_sign(mp):
+    mp.setattr(O, "silu", lambda a: np.asarray(a, np.float64) / (1.0 + np.exp(np.asarray(a, np.float64))))
+
+
+def _mut_swap_w1_w3(mp):
+    def hidden(x_rows, w13):
+        I = w13.shape[0] // 2
+        w13 = np.asarray(w13, np.float64)
+        return O.silu(x_rows @ w13[I:].T) * (x_rows @ w13[:I].T)
+    mp.setattr(O, "swiglu_hidden", hidden)
+
+
+def _mut_bias_sign(mp):
+    real = O.bias_update
+    mp.setattr(O, "bias_update", lambda b, c, T, k, g: real(b, c, T, k, -g))
+
+
+def _mut_bias_mean_off(mp):
+    real = O.bias_update
+    mp.setattr(O, "bias_update", lambda b, c, T, k, g: real(b, c, T, k + 1, g))
+
+
+def _mut_e4m3_ties_odd(mp):
+    def enc(v):
+        v = np.asarray(v, np.float64)
+        sign = np.signbit(v)
+        a = np.abs(v)
+        hi = np.minimum(np.searchsorted(O._E4M3_POS, a, side="left"), 126)
+        lo = np.maximum(hi - 1, 0)
+        dh, dl = O._E4M3_POS[hi] - a, a - O._E4M3_POS[lo]
+        code = np.where((dh < dl) | ((dh == dl) & (hi % 2 == 1)), hi, lo)
+        code = np.where(a >= 448, 126, code)
+        code = np.where(O._E4M3_POS[hi] == a, hi, code).astype(np.uint8)
+        return np.where(sign, code | 0x80, code).astype(np.uint8)
+    mp.setattr(O, "e4m3_encode", enc)
+
+
+def _mut_fnuz_scale(mp):
+    mp.setattr(O, "_tile_scale", lambda amax: np.where(amax == 0, np.float32(1), (amax.astype(np.float32) / np.float32(240))).astype(np.float32))
+
+
+def _mut_bf16_truncate(mp):
+    def trunc(a):
+        a = np.asarray(a, np.float64)
+        m, e = np.frexp(a)
+        return np.ldexp(np.trunc(m * 256.0), e - 8)
+    mp.setattr(O, "bf16_round", trunc)
+
+
+def _mut_permute_token_desc(mp):
+    real = O.permute
+
+    def perm(idx, n, ns=1):
+        idx = np.asarray(idx)
+        off, st, pp = real(idx[::-1], n, ns)
+        T = idx.shape[0]
+        st = st.copy()
+        st[:T * idx.shape[1]] = T - 1 - st[:T * idx.shape[1]]
+        return off, st, pp[::-1]
+    mp.setattr(O, "permute", perm)
+
+
+def _mut_combine_no_shared(mp):
+    real = O.combine
+    mp.setattr(O, "combine", lambda y, sh, pp, g: real(y, None, pp, g))
+
+
+def _mut_group_max_not_top2(mp):
+    real = O.route
+
+    def route(x, w, b, k, n_group=1, topk_group=1):
+        if n_group == 1:
+            return real(x, w, b, k)
+        # use only the single best z of each group as the group score
+        x = np.asarray(x, np.float64)
+        s = O.sigmoid(x @ np.asarray(w, np.float64).T)
+        z = s + np.asarray(b, np.float64)
+        N = z.shape[1]
+        gs = N // n_group
+        r = real(x, w, b, k, n_group, topk_group)
+        for t in range(x.shape[0]):
+            sc = z[t].reshape(n_group, gs).max(1)
+            kept = sorted(np.argsort(-sc, kind="stable")[:topk_group])
+            allowed = np.concatenate([np.arange(g * gs, (g + 1) * gs) for g in kept])
+            sel = allowed[np.argsort(-z[t, allowed], kind="stable")[:k]]
+            r["idx"][t] = sel
+            r["gate"][t] = s[t, sel] / s[t, sel].sum()
+        return r
+    mp.setattr(O, "route", route)
+
+
+def _mut_sigmoid_softmax(mp):
+    def sm(u):
+        u = np.asarray(u, np.float64)
+        e = np.exp(u - u.max(axis=-1, keepdims=True))
+        return e / e.sum(axis=-1, keepdims=True)
+    mp.setattr(O, "sigmoid", sm)
+
+
+def _mut_quant_transposed_block_scale(mp):
+    real = O.dequant_128x128
+
+    def deq(q, s):
+        if s.shape[0] == s.shape[1]:
+            return real(q, s.T)
+        n, k = q.shape
+        v = O.e4m3_decode(q).reshape(n // 128, 128, k // 128, 128)
+        s2 = s.reshape(-1)[::-1].reshape(s.shape)  # scales attached to the wrong blocks
+        return (v * s2.astype(np.float64)[:, None, :, None]).reshape(n, k)
+    mp.setattr(O, "dequant_128x128", deq)
+
+
+MUTATIONS = [
+    _mut_gate_from_z, _mut_ascending, _mut_tie_higher_index, _mut_silu_sign, _mut_swap_w1_w3,
+    _mut_bias_sign, _mut_bias_mean_off, _mut_e4m3_ties_odd, _mut_fnuz_scale,
+    _mut_bf16_truncate, _mut_permute_token_desc, _mut_combine_no_shared,
+    _mut_group_max_not_top2, _mut_sigmoid_softmax, _mut_quant_transposed_block_scale,
+]
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__[5:])
+def test_mutation_is_caught(mutation, monkeypatch):
+    mutation(monkeypatch)
+    caught = _any_pin_fails()
+    assert caught is not None, f"no pin catches {mutation.__name__}"
