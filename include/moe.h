@@ -1,0 +1,227 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the forward pass of one DeepSeekMoE layer on one MI355X
+ * (gfx950), with sigmoid routing, the aux-loss-free routing bias and its load-driven
+ * update, in bf16 and in FP8 (E4M3) with 1x128 / 128x128 scaling.
+ *
+ * Sources: "DeepSeek-V3 Technical Report" (wiki summary page), sections
+ * "DeepSeekMoE と補助損失なしの負荷分散" and "FP8 混合精度訓練"; "Vol.25 DeepSeek-V3の技術と
+ * その影響", section "MoEの歴史とDeepSeekMoE-V3の特徴".
+ *
+ * Conventions shared by every entry point
+ *  - Every call returns a moe_status.  Arguments are checked on the host, synchronously,
+ *    before anything is launched; on an error nothing is launched and nothing is written,
+ *    and moe_last_error() (thread-local) describes the problem.
+ *  - Work is enqueued asynchronously on the caller's HIP stream; no call synchronises the
+ *    device or reads device memory back to the host.  A fault inside a kernel surfaces at
+ *    the caller's next synchronisation.
+ *  - Ownership: every pointer is caller-owned memory; pointers documented as "device" must
+ *    be device memory of the current device.  The library never allocates or frees device
+ *    memory and keeps no state between calls.  Scratch memory comes from the caller's
+ *    workspace, sized by the *_workspace_size() queries; it need not be initialised and its
+ *    contents are undefined after the call.
+ *  - Layout: row-major and contiguous unless an ld* (leading dimension, in elements) is
+ *    given.  Device pointers must be 16-byte aligned; leading dimensions must keep every
+ *    row 16-byte aligned.
+ *  - Types: bf16 tensors are passed as uint16_t (the bfloat16 bit pattern); FP8 tensors as
+ *    uint8_t holding OCP E4M3FN codes (bias 7, largest finite 448, no infinities, 0x7F /
+ *    0xFF NaN); scales are float32.
+ *  - Rows of the expert GEMMs follow the permutation of moe_permute: pairs sorted by expert
+ *    then token ("sorted rows"), followed by one segment of all T tokens for the shared
+ *    expert, whose group index is n_experts.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int moe_status;
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,      /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,     /* a size is out of range or inconsistent */
+  MOE_ERR_DTYPE = 3,     /* unsupported dtype / epilogue combination */
+  MOE_ERR_ALIGN = 4,     /* a pointer or leading dimension breaks 16-byte alignment */
+  MOE_ERR_WORKSPACE = 5, /* workspace missing or smaller than the query returned */
+  MOE_ERR_HIP = 6        /* a HIP launch reported an error */
+};
+
+enum { MOE_BF16 = 0, MOE_F32 = 1, MOE_FP8_E4M3 = 2 };
+enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1 };
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(moe_status s);
+/* Detail of the last error returned on this thread ("" if none). */
+const char* moe_last_error(void);
+/* Version of this ABI (bumped on any incompatible change). */
+int moe_abi_version(void);
+
+/* ------------------------------------------------------------------------------------
+ * moe_route -- router affinities, bias-adjusted top-K selection, gates, expert loads.
+ * "DeepSeek-V3 Technical Report", "DeepSeekMoE と補助損失なしの負荷分散": the token-to-
+ * expert affinity is a sigmoid, s[t,i] = sigmoid(x_t . e_i); the per-expert bias b_i is
+ * added to the affinity only to decide the routing, z = s + b; the gates are the selected
+ * ORIGINAL affinities normalised to sum to one; the load of every expert is counted over
+ * the whole batch.  With n_group > 1 the selection is first limited to the topk_group
+ * groups (of n_experts/n_group contiguous experts) with the largest sum of their two best
+ * z -- the single-GPU stand-in for the node limit M = 4 of the same section.
+ * The affinity is computed from bf16 inputs with fp32 accumulation; sigmoid, z, the
+ * selection and the gates are fp32 ("FP8 混合精度訓練": gating stays in high precision).
+ * Equal z: the lower expert index wins (likewise for equal group scores).
+ *
+ *   x           device bf16 [T, d]
+ *   w_router    device bf16 [n_experts, d] (row i = e_i)
+ *   bias        device f32 [n_experts]
+ *   topk_idx    device i32 [T, top_k] out: selected experts, descending z
+ *   topk_gate   device f32 [T, top_k] out: gates (sum to 1 per token)
+ *   expert_counts device i32 [n_experts] out: load per expert (overwritten)
+ *   scores      device f32 [T, n_experts] out, optional (NULL): the affinities s
+ *   ws          device workspace of moe_route_workspace_size(T, n_experts) bytes
+ * Limits: 0 <= T; 64 <= d, d % 64 == 0; 1 <= n_experts <= 256, n_experts % 4 == 0;
+ * 1 <= top_k <= n_experts; n_group in 1..64 dividing n_experts, with n_experts/n_group >= 2
+ * when n_group > 1; 1 <= topk_group <= n_group; top_k <= topk_group*n_experts/n_group.
+ * T == 0 writes zero counts only.
+ * ------------------------------------------------------------------------------------ */
+size_t moe_route_workspace_size(int T, int n_experts);
+moe_status moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T,
+                     int d, int n_experts, int top_k, int n_group, int topk_group,
+                     int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
+                     float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * moe_permute -- token permutation for the expert GEMMs (the within-GPU half of the
+ * dispatch stage of "DeepSeek-V3 Technical Report", "DualPipe パイプライン並列化").
+ * Pairs (t, k) are ordered by expert, then by token (deterministic, no atomics order),
+ * followed (n_shared == 1) by a segment holding every token once, in order, for the
+ * shared expert.  No token is dropped ("トークンドロップなし"): there is no capacity limit.
+ * The loads are recomputed here from topk_idx.
+ *
+ *   topk_idx        device i32 [T, top_k]; every token's entries must be distinct experts
+ *                   in [0, n_experts) (as moe_route produces).  An entry outside that range
+ *                   is skipped: its pair_pos is -1 and it takes no row.
+ *   expert_offsets  device i32 [n_experts + n_shared + 1] out: group g's rows are
+ *                   [off[g], off[g+1]); the shared expert is group n_experts.
+ *   sorted_token    device i32 [T * (top_k + n_shared)] out: token of each sorted row.
+ *   pair_pos        device i32 [T, top_k] out: sorted row of pair (t, k).
+ * Limits: 0 <= T; 1 <= top_k <= n_experts <= 256; n_shared in {0, 1}.
+ * ------------------------------------------------------------------------------------ */
+size_t moe_permute_workspace_size(int T, int n_experts);
+moe_status moe_permute(const int32_t* topk_idx, int T, int top_k, int n_experts, int n_shared,
+                       int32_t* expert_offsets, int32_t* sorted_token, int32_t* pair_pos,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * fp8_quant_1x128 -- online quantisation of activations in 1x128 tiles.
+ * "DeepSeek-V3 Technical Report", "FP8 混合精度訓練": activations are scaled per 1x128
+ * tile ("細粒度量子化") from the tile's current max |x| ("オンライン量子化") and stored
+ * as E4M3 ("E4M3 統一").  For each tile: s = fl32(amax / 448) (IEEE division; an
+ * all-zero tile gets s = 1) and q = RNE_E4M3(fl32(x / s)), saturating at +/-448; the code's
+ * sign bit is x's sign bit.
+ *
+ *   x      device bf16 [rows, cols], leading dimension ldx (elements, >= cols)
+ *   q      device u8 [rows, cols] out (contiguous)
+ *   scale  device f32 [rows, cols/128] out
+ * Limits: rows >= 0; cols >= 128, cols % 128 == 0; ldx % 8 == 0.
+ * ------------------------------------------------------------------------------------ */
+moe_status fp8_quant_1x128(const uint16_t* x, int rows, int cols, int64_t ldx, uint8_t* q,
+                           float* scale, hipStream_t stream);
+
+/* fp8_quant_128x128 -- the weight counterpart (one-time weight preparation, not on the
+ * per-batch path): n_mats matrices [n, k], one scale per 128x128 block, same rounding.
+ *   w      device bf16 [n_mats, n, k];  q device u8 [n_mats, n, k] out;
+ *   scale  device f32 [n_mats, n/128, k/128] out.
+ * Limits: n_mats >= 0; n, k >= 128 and multiples of 128. */
+moe_status fp8_quant_128x128(const uint16_t* w, int n_mats, int n, int k, uint8_t* q,
+                             float* scale, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * moe_grouped_gemm -- one GEMM per expert over that expert's sorted rows:
+ *   out[r, :] = A[r, :] . W[g]^T   for every row r of group g,
+ * the expert FFN layers of "DeepSeek-V3 Technical Report", "DeepSeekMoE と補助損失なしの
+ * 負荷分散" (expert width 2048).  With epilogue SWIGLU the GEMM is the gate/up projection:
+ * W[g] holds W1 in rows [0, N/2) and W3 in rows [N/2, N), and the stored output is
+ * h = silu(A W1^T) * (A W3^T), N/2 columns wide.  On the FP8 path ("FP8 混合精度訓練")
+ * A and W are E4M3 with one scale per 1x128 tile of A and per 128x128 block of W; every
+ * 128-element slice of K is multiplied on the matrix cores and its partial sum is scaled
+ * by s_A * s_W and added to an fp32 accumulator (the N_C = 128 promotion interval).  An
+ * FP8 output (the gate/up projection feeding the down projection) is quantised per 1x128
+ * tile exactly as fp8_quant_1x128 does.  bf16 inputs accumulate in fp32.
+ *
+ * Rows: group g (first_group <= g < first_group + n_groups) owns the sorted rows
+ * [group_offsets[g], group_offsets[g+1]).  Row r reads A row a_rows[r] when a_rows is not
+ * NULL (gather, e.g. a_rows = sorted_token and A = x), else A row r (A holds every sorted
+ * row, e.g. h); it writes out row r - group_offsets[first_group].  Groups are read on
+ * the device; empty groups cost nothing.  m_total must equal group_offsets[first_group +
+ * n_groups] - group_offsets[first_group] (it sizes the launch; the device values decide
+ * the work).
+ * ------------------------------------------------------------------------------------ */
+typedef struct moe_gemm_desc {
+  int in_dtype;                 /* MOE_BF16 or MOE_FP8_E4M3 (both A and W) */
+  const void* a;                /* device A [*, K], leading dimension lda (elements) */
+  const float* a_scale;         /* FP8: device f32 [*, K/128] (row-aligned with A); else NULL */
+  const int32_t* a_rows;        /* device i32 gather index per sorted row, or NULL */
+  int64_t lda;
+  const void* w;                /* device W [G][N][K] contiguous, G > last group used */
+  const float* w_scale;         /* FP8: device f32 [G][N/128][K/128]; else NULL */
+  const int32_t* group_offsets; /* device i32, at least first_group + n_groups + 1 entries */
+  int first_group;
+  int n_groups;                 /* 1..1024 */
+  int64_t m_total;              /* rows covered by the groups (see above) */
+  int N;                        /* rows of each W[g] (2*I for SWIGLU) */
+  int K;                        /* reduction length */
+  int epilogue;                 /* MOE_EPI_NONE or MOE_EPI_SWIGLU */
+  void* out;                    /* device output, leading dimension ldo (elements) */
+  int out_dtype;                /* MOE_BF16, MOE_F32, or MOE_FP8_E4M3 (+ out_scale) */
+  int64_t ldo;
+  float* out_scale;             /* FP8 output: device f32 [rows, out_cols/128]; else NULL */
+} moe_gemm_desc;
+/* Limits: K a positive multiple of 64 (bf16) or 128 (FP8); without an epilogue N a positive
+ * multiple of 128; with SWIGLU N/2 a positive multiple of 64 (bf16) or 128 (FP8); FP8 input
+ * needs a_scale and w_scale; an FP8 output needs FP8 input, SWIGLU and out_scale; SWIGLU
+ * output is bf16 or FP8; 0 <= m_total < 2^31; lda/ldo keep rows 16-byte aligned. */
+moe_status moe_grouped_gemm(const moe_gemm_desc* desc, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * moe_combine -- the weighted sum back into token order (the combine stage of
+ * "DeepSeek-V3 Technical Report", "DualPipe パイプライン並列化"; "Vol.25", "MoEの歴史と
+ * DeepSeekMoE-V3の特徴": the chosen experts' results are merged with the shared expert):
+ *   out[t] = y_shared[t] + sum_k gate[t,k] * y_routed[pair_pos[t,k]]
+ * accumulated in fp32 in the order k = 0..top_k-1 (acc = fma(gate, y, acc)), then the
+ * shared term added; stored as bf16 (round to nearest even) or f32.
+ *   y_routed  device bf16 [T*top_k (sorted rows), d]
+ *   y_shared  device f32 [T, d] or NULL (no shared expert)
+ *   pair_pos  device i32 [T, top_k] (entries < 0 are skipped)
+ *   topk_gate device f32 [T, top_k]
+ *   out       device [T, d], bf16 or f32 per out_dtype
+ * Limits: T >= 0; top_k >= 1; d >= 8, d % 8 == 0.
+ * ------------------------------------------------------------------------------------ */
+moe_status moe_combine(const uint16_t* y_routed, const float* y_shared, const int32_t* pair_pos,
+                       const float* topk_gate, int T, int top_k, int d, void* out,
+                       int out_dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * moe_bias_update -- the aux-loss-free load-balancing step ("DeepSeek-V3 Technical
+ * Report", "DeepSeekMoE と補助損失なしの負荷分散": monitor each expert's load over the
+ * batch; lower an overloaded expert's bias by gamma, raise an underloaded one's):
+ *   b_i <- b_i - gamma * sign(load_i - total/N)
+ * decided in integers (load_i * N vs total_assignments), one fp32 add of -gamma or +gamma;
+ * an expert exactly at the mean keeps its bias bit for bit.
+ *   bias           device f32 [n_experts], updated in place
+ *   expert_counts  device i32 [n_experts] (the loads, e.g. from moe_route)
+ *   total_assignments  T * top_k
+ * Limits: 1 <= n_experts <= 65536; total_assignments >= 0; gamma finite.
+ * ------------------------------------------------------------------------------------ */
+moe_status moe_bias_update(float* bias, const int32_t* expert_counts, int n_experts,
+                           int64_t total_assignments, float gamma, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,238 @@
+"""ctypes binding of libmoe.so: the C-ABI entry points under the same names.
+
+Argument marshalling only (tensor -> pointer, shape -> int, output allocation, the current
+HIP stream); every step of the layer runs in the library's HIP kernels.  There is no
+fallback: if the library is not built, or a tensor is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(7)
+MOE_BF16, MOE_F32, MOE_FP8_E4M3 = 0, 1, 2
+MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
+
+EXPORTS = (
+    "moe_status_str", "moe_last_error", "moe_abi_version",
+    "moe_route_workspace_size", "moe_route",
+    "moe_permute_workspace_size", "moe_permute",
+    "fp8_quant_1x128", "fp8_quant_128x128",
+    "moe_grouped_gemm", "moe_combine", "moe_bias_update",
+)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_f = ctypes.c_float
+
+
+class MoeGemmDesc(ctypes.Structure):
+    _fields_ = [
+        ("in_dtype", _i), ("a", _p), ("a_scale", _p), ("a_rows", _p), ("lda", _i64),
+        ("w", _p), ("w_scale", _p), ("group_offsets", _p), ("first_group", _i),
+        ("n_groups", _i), ("m_total", _i64), ("N", _i), ("K", _i), ("epilogue", _i),
+        ("out", _p), ("out_dtype", _i), ("ldo", _i64), ("out_scale", _p),
+    ]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        super().__init__(f"{fn} failed: {status_str(status)}: {detail}")
+        self.status = status
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m sparse_moe_layer_sigmoid_amd.build`"
+                " (there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_status_str.argtypes = [_i]
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_abi_version.restype = _i
+        L.moe_route_workspace_size.restype = _sz
+        L.moe_route_workspace_size.argtypes = [_i, _i]
+        L.moe_route.restype = _i
+        L.moe_route.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p]
+        L.moe_permute_workspace_size.restype = _sz
+        L.moe_permute_workspace_size.argtypes = [_i, _i]
+        L.moe_permute.restype = _i
+        L.moe_permute.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p, _sz, _p]
+        L.fp8_quant_1x128.restype = _i
+        L.fp8_quant_1x128.argtypes = [_p, _i, _i, _i64, _p, _p, _p]
+        L.fp8_quant_128x128.restype = _i
+        L.fp8_quant_128x128.argtypes = [_p, _i, _i, _i, _p, _p, _p]
+        L.moe_grouped_gemm.restype = _i
+        L.moe_grouped_gemm.argtypes = [ctypes.POINTER(MoeGemmDesc), _p]
+        L.moe_combine.restype = _i
+        L.moe_combine.argtypes = [_p, _p, _p, _p, _i, _i, _i, _p, _i, _p]
+        L.moe_bias_update.restype = _i
+        L.moe_bias_update.argtypes = [_p, _p, _i, _i64, _f, _p]
+        _LIB = L
+    return _LIB
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status, lib().moe_last_error().decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, dtype, name: str, contiguous: bool = True):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+# ----------------------------------------------------------------------------- entry points
+
+
+def moe_route(x, w_router, bias, top_k: int, n_group: int = 1, topk_group: int = 1,
+              want_scores: bool = False, out=None):
+    """Returns (topk_idx [T,K] int32, topk_gate [T,K] f32, expert_counts [N] int32, scores|None)."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(w_router, torch.bfloat16, "w_router")
+    _dev(bias, torch.float32, "bias")
+    T, d = x.shape
+    N = w_router.shape[0]
+    dev = x.device
+    if out is None:
+        out = {}
+    idx = out.get("topk_idx") if "topk_idx" in out else torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    gate = out.get("topk_gate") if "topk_gate" in out else torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    counts = out.get("expert_counts") if "expert_counts" in out else torch.empty(N, dtype=torch.int32, device=dev)
+    scores = torch.empty((T, N), dtype=torch.float32, device=dev) if want_scores else None
+    wsb = lib().moe_route_workspace_size(T, N)
+    ws = out.get("ws_route") if "ws_route" in out else torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    st = lib().moe_route(_ptr(x), _ptr(w_router), _ptr(bias), T, d, N, top_k, n_group, topk_group,
+                         _ptr(idx), _ptr(gate), _ptr(counts), _ptr(scores), _ptr(ws), ws.numel(), _stream(x))
+    _check("moe_route", st)
+    return idx, gate, counts, scores
+
+
+def moe_permute(topk_idx, n_experts: int, n_shared: int = 1, out=None):
+    """Returns (expert_offsets [N+n_shared+1], sorted_token [T*(K+n_shared)], pair_pos [T,K])."""
+    _dev(topk_idx, torch.int32, "topk_idx")
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    out = out or {}
+    offs = out["expert_offsets"] if "expert_offsets" in out else torch.empty(n_experts + n_shared + 1, dtype=torch.int32, device=dev)
+    st_ = out["sorted_token"] if "sorted_token" in out else torch.empty(T * (K + n_shared), dtype=torch.int32, device=dev)
+    pp = out["pair_pos"] if "pair_pos" in out else torch.empty((T, K), dtype=torch.int32, device=dev)
+    wsb = lib().moe_permute_workspace_size(T, n_experts)
+    ws = out["ws_permute"] if "ws_permute" in out else torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    st = lib().moe_permute(_ptr(topk_idx), T, K, n_experts, n_shared, _ptr(offs), _ptr(st_), _ptr(pp),
+                           _ptr(ws), ws.numel(), _stream(topk_idx))
+    _check("moe_permute", st)
+    return offs, st_, pp
+
+
+def fp8_quant_1x128(x, q=None, scale=None):
+    """x [rows, cols] bf16 (row stride may exceed cols) -> (q uint8 [rows, cols], scale f32 [rows, cols/128])."""
+    _dev(x, torch.bfloat16, "x", contiguous=False)
+    rows, cols = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
+    scale = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device) if scale is None else scale
+    st = lib().fp8_quant_1x128(_ptr(x), rows, cols, x.stride(0), _ptr(q), _ptr(scale), _stream(x))
+    _check("fp8_quant_1x128", st)
+    return q, scale
+
+
+def fp8_quant_128x128(w):
+    """w [n_mats, n, k] (or [n, k]) bf16 -> (q uint8 like w, scale f32 [n_mats, n/128, k/128])."""
+    _dev(w, torch.bfloat16, "w")
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    m, n, k = w3.shape
+    q = torch.empty((m, n, k), dtype=torch.uint8, device=w.device)
+    s = torch.empty((m, n // 128, k // 128), dtype=torch.float32, device=w.device)
+    st = lib().fp8_quant_128x128(_ptr(w3), m, n, k, _ptr(q), _ptr(s), _stream(w))
+    _check("fp8_quant_128x128", st)
+    return (q[0], s[0]) if squeeze else (q, s)
+
+
+_DT = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32, torch.uint8: MOE_FP8_E4M3}
+
+
+def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_total: int, out,
+                     a_scale=None, a_rows=None, w_scale=None, swiglu: bool = False, out_scale=None):
+    """out[r - off[first_group]] = epilogue(A[a_rows[r] or r] . W[g]^T) for each sorted row r
+    of group g.  a: bf16 or uint8 (E4M3) [*, K]; w: same dtype [G, N, K]; out: bf16 / f32 /
+    uint8 (E4M3, needs out_scale)."""
+    fp8 = a.dtype == torch.uint8
+    if w.dtype != a.dtype:
+        raise TypeError("a and w must share a dtype")
+    for t, nm in ((a, "a"), (w, "w"), (group_offsets, "group_offsets"), (out, "out")):
+        if not t.is_cuda:
+            raise TypeError(f"{nm} must be a GPU tensor")
+    if a.stride(-1) != 1 or out.stride(-1) != 1 or not w.is_contiguous():
+        raise ValueError("rows of a/out and all of w must be contiguous")
+    G, N, K = w.shape
+    desc = MoeGemmDesc(
+        in_dtype=MOE_FP8_E4M3 if fp8 else MOE_BF16, a=a.data_ptr(),
+        a_scale=a_scale.data_ptr() if a_scale is not None else None,
+        a_rows=a_rows.data_ptr() if a_rows is not None else None, lda=a.stride(0),
+        w=w.data_ptr(), w_scale=w_scale.data_ptr() if w_scale is not None else None,
+        group_offsets=group_offsets.data_ptr(), first_group=first_group, n_groups=n_groups,
+        m_total=m_total, N=N, K=K, epilogue=MOE_EPI_SWIGLU if swiglu else MOE_EPI_NONE,
+        out=out.data_ptr(), out_dtype=_DT[out.dtype], ldo=out.stride(0),
+        out_scale=out_scale.data_ptr() if out_scale is not None else None)
+    st = lib().moe_grouped_gemm(ctypes.byref(desc), _stream(a))
+    _check("moe_grouped_gemm", st)
+    return out
+
+
+def moe_combine(y_routed, y_shared, pair_pos, topk_gate, out_dtype=torch.bfloat16, out=None):
+    _dev(y_routed, torch.bfloat16, "y_routed")
+    _dev(pair_pos, torch.int32, "pair_pos")
+    _dev(topk_gate, torch.float32, "topk_gate")
+    if y_shared is not None:
+        _dev(y_shared, torch.float32, "y_shared")
+    T, K = pair_pos.shape
+    d = y_routed.shape[1]
+    if out is None:
+        out = torch.empty((T, d), dtype=out_dtype, device=y_routed.device)
+    st = lib().moe_combine(_ptr(y_routed), _ptr(y_shared), _ptr(pair_pos), _ptr(topk_gate), T, K, d,
+                           _ptr(out), _DT[out.dtype], _stream(y_routed))
+    _check("moe_combine", st)
+    return out
+
+
+def moe_bias_update(bias, expert_counts, total_assignments: int, gamma: float):
+    _dev(bias, torch.float32, "bias")
+    _dev(expert_counts, torch.int32, "expert_counts")
+    st = lib().moe_bias_update(_ptr(bias), _ptr(expert_counts), bias.numel(), int(total_assignments),
+                               float(gamma), _stream(bias))
+    _check("moe_bias_update", st)
+    return bias

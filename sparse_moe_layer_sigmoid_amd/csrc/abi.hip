@@ -1,0 +1,51 @@
+// Status strings, the thread-local error detail and the ABI version.
+#include <string>
+
+#include "abi_common.h"
+
+namespace moe {
+
+static thread_local std::string g_last_error;
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+moe_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+    case MOE_ERR_DTYPE: return "MOE_ERR_DTYPE";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return moe::g_last_error.c_str(); }
+
+int moe_abi_version(void) { return 1; }
+
+}  // extern "C"

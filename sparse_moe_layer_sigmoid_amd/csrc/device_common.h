@@ -1,0 +1,83 @@
+// Device-side helpers shared by the libmoe kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 bit pattern (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Unpack 8 bf16 held in a 16-byte word.
+__device__ __forceinline__ void unpack_bf16x8(const u32x4& v, float f[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+  }
+}
+
+// float -> OCP E4M3FN code, round to nearest even, saturating to +/-448, NaN -> 0x7F|sign.
+// The code's sign bit is the input's sign bit.  Written from the format's definition:
+// below 2^-6 the spacing is 2^-9 (subnormals, and code 8 is the smallest normal, so
+// rint(|v| * 2^9) is the code directly); above, keep 3 mantissa bits with RNE on the 20
+// dropped bits.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;   // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;  // |v| >= 448 (or inf): saturate
+  uint32_t q;
+  if (a < 0x3c800000u) {                      // |v| < 2^-6
+    q = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    const uint32_t e = (a >> 23) - 120u;      // E4M3 biased exponent, 1..15
+    const uint32_t mant = a & 0x7fffffu;
+    q = (e << 3) | (mant >> 20);
+    const uint32_t rem = mant & 0xfffffu;
+    q += (rem > 0x80000u) || (rem == 0x80000u && (q & 1u));
+  }
+  return sign | q;
+}
+
+// Matrix-core wrappers (gfx950).
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8_t& a, const bf16x8_t& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16x128 E4M3 x E4M3 -> f32 (format code 0 = E4M3 for both operands, no block scale).
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float max16(float v) {  // over the 16-lane group of this lane
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+}  // namespace moe

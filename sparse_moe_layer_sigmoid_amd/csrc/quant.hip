@@ -1,0 +1,118 @@
+// fp8_quant_1x128 / fp8_quant_128x128: online E4M3 quantisation with fine-grained scales.
+// "DeepSeek-V3 Technical Report" (wiki summary), "FP8 混合精度訓練": activations are scaled
+// per 1x128 tile and weights per 128x128 block ("細粒度量子化"), the scale coming from the
+// current max |value| of the tile or block ("オンライン量子化"), all stored as E4M3
+// ("E4M3 統一").  Rule: s = fl32(amax / 448) (s = 1 for an all-zero tile), q = RNE(x / s)
+// saturating at +/-448, both divisions IEEE-rounded so the codes are reproducible bit for bit.
+//
+// Both kernels are HBM-bound streaming passes: 16-byte loads of 8 bf16 per lane, the amax
+// reduced with lane shuffles (16 lanes per 1x128 tile) or shuffles + LDS (128x128 block).
+#include "abi_common.h"
+#include "device_common.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ u32x2 encode8(const float f[8], float s) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(f[i] / s) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(f[4 + i] / s) << (8 * i);
+  return u32x2{lo, hi};
+}
+
+// 256 threads = 16 tiles of 1x128; lane group of 16 handles one tile, 8 values per lane.
+__global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __restrict__ x,
+                                                          int64_t n_tiles, int tiles_per_row,
+                                                          int64_t ldx, uint8_t* __restrict__ q,
+                                                          float* __restrict__ scale) {
+  const int64_t tile = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (tile >= n_tiles) return;  // whole 16-lane groups leave together
+  const int sub = threadIdx.x & 15;
+  const int64_t r = tile / tiles_per_row;
+  const int c = (int)(tile - r * tiles_per_row);
+  const u32x4 v = *(const u32x4*)(x + r * ldx + (int64_t)c * 128 + sub * 8);
+  float f[8];
+  unpack_bf16x8(v, f);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = max16(amax);
+  const float s = (amax == 0.f) ? 1.0f : amax / 448.0f;
+  const int64_t cols = (int64_t)tiles_per_row * 128;
+  *(u32x2*)(q + r * cols + (int64_t)c * 128 + sub * 8) = encode8(f, s);
+  if (sub == 0) scale[tile] = s;
+}
+
+// One workgroup per 128x128 block: thread t covers columns 8*(t%16)..+7 of rows t/16 + 16 j.
+__global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __restrict__ w,
+                                                            int n, int k,
+                                                            uint8_t* __restrict__ q,
+                                                            float* __restrict__ scale) {
+  __shared__ float red[4];
+  const int nbk = k / 128, nbn = n / 128;
+  const int64_t blk = blockIdx.x;
+  const int64_t mat = blk / ((int64_t)nbn * nbk);
+  const int rem = (int)(blk - mat * nbn * nbk);
+  const int bn = rem / nbk, bk = rem - bn * nbk;
+  const int tid = threadIdx.x, c8 = (tid & 15) * 8, r0 = tid >> 4;
+  const uint16_t* base = w + (mat * n + (int64_t)bn * 128) * k + (int64_t)bk * 128 + c8;
+  float f[8][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const u32x4 v = *(const u32x4*)(base + (int64_t)(r0 + 16 * j) * k);
+    unpack_bf16x8(v, f[j]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[j][i]));
+  }
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = (amax == 0.f) ? 1.0f : amax / 448.0f;
+  uint8_t* qb = q + (mat * n + (int64_t)bn * 128) * k + (int64_t)bk * 128 + c8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) *(u32x2*)(qb + (int64_t)(r0 + 16 * j) * k) = encode8(f[j], s);
+  if (tid == 0) scale[blk] = s;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status fp8_quant_1x128(const uint16_t* x, int rows, int cols, int64_t ldx,
+                                      uint8_t* q, float* scale, hipStream_t stream) {
+  using namespace moe;
+  clear_error();
+  MOE_REQUIRE(x && q && scale, MOE_ERR_NULL, "fp8_quant_1x128: a required pointer is NULL");
+  MOE_REQUIRE(rows >= 0 && cols >= 128 && cols % 128 == 0, MOE_ERR_SHAPE,
+              "fp8_quant_1x128: rows=%d cols=%d (cols must be a positive multiple of 128)", rows, cols);
+  MOE_REQUIRE(ldx >= cols && ldx % 8 == 0, MOE_ERR_ALIGN, "fp8_quant_1x128: ldx=%lld must be >= cols and a multiple of 8",
+              (long long)ldx);
+  MOE_REQUIRE(aligned16(x) && ((uintptr_t)q & 7u) == 0, MOE_ERR_ALIGN,
+              "fp8_quant_1x128: x must be 16-byte and q 8-byte aligned");
+  const int tpr = cols / 128;
+  const int64_t n_tiles = (int64_t)rows * tpr;
+  if (n_tiles > 0) {
+    const int64_t grid = (n_tiles + 15) / 16;
+    MOE_REQUIRE(grid < (int64_t)1 << 31, MOE_ERR_SHAPE, "fp8_quant_1x128: too many tiles");
+    quant_1x128_kernel<<<(unsigned)grid, 256, 0, stream>>>(x, n_tiles, tpr, ldx, q, scale);
+  }
+  return check_launch("fp8_quant_1x128");
+}
+
+extern "C" moe_status fp8_quant_128x128(const uint16_t* w, int n_mats, int n, int k, uint8_t* q,
+                                        float* scale, hipStream_t stream) {
+  using namespace moe;
+  clear_error();
+  MOE_REQUIRE(w && q && scale, MOE_ERR_NULL, "fp8_quant_128x128: a required pointer is NULL");
+  MOE_REQUIRE(n_mats >= 0 && n >= 128 && k >= 128 && n % 128 == 0 && k % 128 == 0, MOE_ERR_SHAPE,
+              "fp8_quant_128x128: n_mats=%d n=%d k=%d (n, k positive multiples of 128)", n_mats, n, k);
+  MOE_REQUIRE(aligned16(w) && ((uintptr_t)q & 7u) == 0, MOE_ERR_ALIGN,
+              "fp8_quant_128x128: w must be 16-byte and q 8-byte aligned");
+  const int64_t blocks = (int64_t)n_mats * (n / 128) * (k / 128);
+  MOE_REQUIRE(blocks < (int64_t)1 << 31, MOE_ERR_SHAPE, "fp8_quant_128x128: too many blocks");
+  if (blocks > 0) quant_128x128_kernel<<<(unsigned)blocks, 256, 0, stream>>>(w, n, k, q, scale);
+  return check_launch("fp8_quant_128x128");
+}

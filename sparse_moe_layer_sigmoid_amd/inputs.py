@@ -188,3 +188,61 @@ def gen_all_weights(cfg: MoEConfig, device, threads: int = 16):
                 W13[e].copy_(a)
                 W2[e].copy_(b)
     return W13, W2
+
+
+# ------------------------------------------------------------------ unit-level test inputs
+
+
+def gen_routing(seed: int, T: int, K: int, N: int, zipf: float = 0.0):
+    """Synthetic routing decisions: idx [T, K] int32 (K distinct experts per token, drawn with
+    popularity proportional to rank^-zipf under a seeded permutation) and gates [T, K]
+    float32 (positive, each row summing to about one)."""
+    r = _rng(seed, 101)
+    w = np.arange(1, N + 1, dtype=np.float64) ** (-zipf)
+    w = w[r.permutation(N)]
+    w /= w.sum()
+    idx = np.stack([r.choice(N, size=K, replace=False, p=w) for _ in range(T)]).astype(np.int32) \
+        if T else np.zeros((0, K), np.int32)
+    g = r.random((T, K)) + 0.05
+    g = (g / g.sum(axis=1, keepdims=True)).astype(np.float32)
+    return torch.from_numpy(idx), torch.from_numpy(g)
+
+
+def gen_normal(seed: int, shape, std: float = 1.0, dtype=torch.bfloat16) -> torch.Tensor:
+    """N(0, std) values rounded to ``dtype`` (bf16 by default)."""
+    a = _rng(seed, 102).standard_normal(size=shape, dtype=np.float32) * np.float32(std)
+    return torch.from_numpy(a).to(dtype)
+
+
+def gen_group_sizes(seed: int, n_groups: int, mean: float, empty_frac: float = 0.1) -> np.ndarray:
+    """Ragged group sizes (Poisson around ``mean``, a fraction forced empty)."""
+    r = _rng(seed, 103)
+    sizes = r.poisson(mean, size=n_groups)
+    sizes[r.random(n_groups) < empty_frac] = 0
+    return sizes.astype(np.int64)
+
+
+def gen_e4m3_codes(seed: int, shape, small_int: bool = False) -> torch.Tensor:
+    """Random E4M3 codes (never NaN).  small_int: only codes of the integers -15..15."""
+    r = _rng(seed, 104)
+    if small_int:
+        # E4M3 codes of 0..15: 0, 1..7 -> 0x38.., see the format: v = (1+m/8) 2^(E-7)
+        ints = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48, 5: 0x4A, 6: 0x4C, 7: 0x4E,
+                8: 0x50, 9: 0x51, 10: 0x52, 11: 0x53, 12: 0x54, 13: 0x55, 14: 0x56, 15: 0x57}
+        mag = r.integers(0, 16, size=shape)
+        code = np.vectorize(ints.get)(mag).astype(np.uint8)
+        sign = (r.random(shape) < 0.5) & (mag > 0)
+        code = np.where(sign, code | 0x80, code).astype(np.uint8)
+    else:
+        code = r.integers(0, 0x7F, size=shape).astype(np.uint8)  # 0x00..0x7E
+        code = np.where(r.random(shape) < 0.5, code | 0x80, code).astype(np.uint8)
+    return torch.from_numpy(code)
+
+
+def gen_scales(seed: int, shape, pow2: bool = False) -> torch.Tensor:
+    """Positive float32 scales (log-uniform), or powers of two."""
+    r = _rng(seed, 105)
+    e = r.integers(-8, -2, size=shape)
+    if pow2:
+        return torch.from_numpy(np.exp2(e).astype(np.float32))
+    return torch.from_numpy((np.exp2(e) * r.uniform(1.0, 2.0, size=shape)).astype(np.float32))

@@ -1,0 +1,100 @@
+"""The C ABI without a GPU: the library loads, exports every symbol moe.h declares, and
+rejects bad arguments on the host before touching HIP (so these run anywhere the ROCm
+runtime libraries are installed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from sparse_moe_layer_sigmoid_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libmoe.so not built")
+    return L
+
+
+def test_header_declares_exactly_the_exports():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    declared = set(re.findall(r"\b(?:moe_status|size_t|int|const char\*)\s+(\w+)\s*\(", src))
+    L = _lib()
+    assert declared == set(L.EXPORTS)
+    lib = L.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    L = _lib()
+    assert L.lib().moe_abi_version() == 1
+    assert L.status_str(0) == "MOE_OK" and L.status_str(5) == "MOE_ERR_WORKSPACE"
+
+
+def _route(L, **kw):
+    a = dict(x=16, w=16, bias=16, T=8, d=128, N=16, K=2, ng=1, tg=1, idx=16, gate=16, counts=16,
+             scores=None, ws=16, wsb=1 << 20)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    return L.lib().moe_route(p(a["x"]), p(a["w"]), p(a["bias"]), a["T"], a["d"], a["N"], a["K"], a["ng"],
+                             a["tg"], p(a["idx"]), p(a["gate"]), p(a["counts"]), p(a["scores"]), p(a["ws"]),
+                             a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(ws=None), 1), (dict(T=-1), 2), (dict(d=100), 2), (dict(N=300), 2),
+    (dict(N=6), 2), (dict(K=0), 2), (dict(K=17), 2), (dict(ng=3), 2), (dict(ng=8, tg=9), 2),
+    (dict(ng=8, tg=1, K=3), 2), (dict(ng=16, tg=2), 2), (dict(x=8), 4), (dict(wsb=4), 5),
+])
+def test_route_rejects(kw, code):
+    L = _lib()
+    assert _route(L, **kw) == code
+    assert L.lib().moe_last_error().decode().startswith("moe_route")
+
+
+def test_other_entry_points_reject():
+    L = _lib()
+    lib = L.lib()
+    P = ctypes.c_void_p
+    assert lib.moe_permute(None, 4, 2, 8, 1, P(16), P(16), P(16), P(16), 1 << 20, None) == 1
+    assert lib.moe_permute(P(16), 4, 2, 8, 2, P(16), P(16), P(16), P(16), 1 << 20, None) == 2
+    assert lib.moe_permute(P(16), 4, 9, 8, 1, P(16), P(16), P(16), P(16), 1 << 20, None) == 2
+    assert lib.moe_permute(P(16), 4000, 2, 8, 1, P(16), P(16), P(16), P(16), 8, None) == 5
+    assert lib.fp8_quant_1x128(P(16), 4, 100, 100, P(16), P(16), None) == 2
+    assert lib.fp8_quant_1x128(P(16), 4, 128, 132, P(16), P(16), None) == 4
+    assert lib.fp8_quant_128x128(P(16), 1, 128, 64, P(16), P(16), None) == 2
+    assert lib.moe_combine(P(16), None, P(16), P(16), 4, 2, 12, P(16), 0, None) == 2
+    assert lib.moe_combine(P(16), None, P(16), P(16), 4, 2, 16, P(16), 2, None) == 3
+    assert lib.moe_bias_update(None, P(16), 8, 16, 0.001, None) == 1
+    assert lib.moe_bias_update(P(16), P(16), 8, 16, float("nan"), None) == 2
+
+
+def _gemm(L, **kw):
+    d = dict(in_dtype=0, a=16, lda=256, w=16, group_offsets=16, first_group=0, n_groups=4, m_total=100,
+             N=256, K=256, epilogue=0, out=16, out_dtype=1, ldo=256)
+    d.update(kw)
+    desc = L.MoeGemmDesc(**d)
+    return L.lib().moe_grouped_gemm(ctypes.byref(desc), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(a=None), 1), (dict(in_dtype=7), 3), (dict(epilogue=3), 3), (dict(out_dtype=9), 3),
+    (dict(out_dtype=2), 3), (dict(epilogue=1, out_dtype=1), 3), (dict(n_groups=0), 2),
+    (dict(K=96), 2), (dict(N=192), 2), (dict(epilogue=1, N=192, out_dtype=0), 2), (dict(in_dtype=2), 1),
+    (dict(in_dtype=2, a_scale=16, w_scale=16, K=192), 2), (dict(lda=200), 4), (dict(ldo=100), 4),
+    (dict(a=8), 4), (dict(m_total=-1), 2),
+])
+def test_gemm_rejects(kw, code):
+    L = _lib()
+    assert _gemm(L, **kw) == code, L.lib().moe_last_error()
+
+
+def test_workspace_queries():
+    L = _lib()
+    lib = L.lib()
+    assert lib.moe_route_workspace_size(4096, 256) > 0
+    assert lib.moe_route_workspace_size(-1, 256) == 0
+    assert lib.moe_permute_workspace_size(16384, 256) == 2 * 64 * 256 * 4

@@ -1,0 +1,405 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same seeded inputs,
+at sizes the oracle finishes in seconds that still span several tiles and ragged tails.
+
+Bars: bit-exact for indices, counts, permutation, fp8 codes and scales, bias updates (the
+routing excluding only tokens whose oracle z gap is under 1e-6); max |out - ref| / rms(ref)
+<= 1e-2 (bf16) and 3e-2 (fp8) for the layer output, checked on the fp32 result before the
+final bf16 store, whose bf16 form must be the round-to-nearest-even of that fp32 result.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from sparse_moe_layer_sigmoid_amd import inputs as I
+from tests.gpu_common import (BF16_TOL, FP8_TOL, check_permutation_properties, check_route,
+                              np64, rel_err, say)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def M():
+    import sparse_moe_layer_sigmoid_amd as m
+    return m
+
+
+# ------------------------------------------------------------------ quantisation
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 128), (37, 512), (300, 7168)])
+def test_quant_1x128_bitexact(rows, cols):
+    say(f"quant_1x128 rows={rows} cols={cols}")
+    x = I.gen_normal(rows * 7 + cols, (rows, cols), 1.0)
+    xn = x.float().numpy()
+    if rows > 5:  # an all-zero tile, outliers, a tile of tiny values, negative zeros
+        xn[3, :128] = 0.0
+        xn[4, 5] = 300.0
+        xn[5, 128:256] *= 1e-30
+        xn[2, 0:128] = -0.0
+        x = torch.from_numpy(xn).to(torch.bfloat16)
+    q, s = M().fp8_quant_1x128(x.to(DEV))
+    qo, so = O.quant_1x128(x.float().numpy())
+    assert np.array_equal(s.cpu().numpy(), so)
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+def test_quant_1x128_strided_rows():
+    x = I.gen_normal(5, (64, 768), 2.0).to(DEV)
+    view = x[:, 128:640]  # ldx = 768 > cols = 512
+    q, s = M().fp8_quant_1x128(view)
+    qo, so = O.quant_1x128(view.float().cpu().numpy())
+    assert np.array_equal(q.cpu().numpy(), qo) and np.array_equal(s.cpu().numpy(), so)
+
+
+def test_quant_128x128_bitexact():
+    w = I.gen_normal(9, (3, 256, 384), 0.006)
+    w[1, :128, :128] = 0
+    q, s = M().fp8_quant_128x128(w.to(DEV))
+    for m in range(3):
+        qo, so = O.quant_128x128(w[m].float().numpy())
+        assert np.array_equal(s[m].cpu().numpy(), so)
+        assert np.array_equal(q[m].cpu().numpy(), qo)
+
+
+def test_e4m3_convert_dense_sweep():
+    """A dense sweep of the device E4M3 conversion through fp8_quant_1x128: tiles whose max
+    is 448 (so s = 1 and the codes are the conversion of the bf16 values themselves), plus
+    scaled tiles (x / s exercises non-representable fp32 quotients), all bf16 magnitudes."""
+    mags = np.arange(0, 0x7F80, dtype=np.uint32)  # every finite non-negative bf16 pattern
+    vals = (mags << 16).view(np.float32)
+    vals = vals[vals < 448.0]
+    n = (len(vals) + 126) // 127 * 127
+    v = np.zeros(n, np.float32)
+    v[:len(vals)] = vals
+    tiles = v.reshape(-1, 127)
+    x = np.concatenate([np.full((tiles.shape[0], 1), 448.0, np.float32), tiles], axis=1)
+    x = np.concatenate([x, -x, x * np.float32(3.7)], axis=0)
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    q, s = M().fp8_quant_1x128(xt.to(DEV))
+    qo, so = O.quant_1x128(xt.float().numpy())
+    assert np.array_equal(s.cpu().numpy(), so)
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+# ------------------------------------------------------------------ routing
+
+
+@pytest.mark.parametrize("T,d,N,K,ng,tg", [
+    (64, 256, 16, 2, 1, 1),      # the tiny config's shape
+    (300, 512, 64, 6, 1, 1),     # ragged token count, several token tiles
+    (257, 256, 256, 8, 8, 4),    # V3 expert count with the group limit
+    (5000, 256, 32, 4, 4, 2),    # more than one token tile size
+])
+def test_route_parity(T, d, N, K, ng, tg):
+    say(f"route T={T} d={d} N={N} K={K} groups={ng}/{tg}")
+    x = I.gen_normal(T + d, (T, d), 1.0)
+    wr = I.gen_normal(N + 1, (N, d), 0.5 / np.sqrt(d))
+    bias = torch.from_numpy(np.random.default_rng(N).uniform(-0.01, 0.01, N).astype(np.float32))
+    idx, gate, counts, scores = M().moe_route(x.to(DEV), wr.to(DEV), bias.to(DEV), K, ng, tg, want_scores=True)
+    r = O.route(np64(x), np64(wr), bias.numpy(), K, ng, tg)
+    tie = check_route(idx, gate, counts, scores, r, N, K)
+    say(f"  tie-window tokens: {int(tie.sum())}")
+
+
+def test_route_bias_changes_selection_not_gates():
+    T, d, N, K = 128, 256, 16, 2
+    x = I.gen_normal(11, (T, d), 1.0).to(DEV)
+    wr = I.gen_normal(12, (N, d), 0.05).to(DEV)
+    b0 = torch.zeros(N, dtype=torch.float32, device=DEV)
+    b1 = b0.clone()
+    b1[7] = 10.0  # expert 7 is forced into every token's selection
+    i0, g0, _, s0 = M().moe_route(x, wr, b0, K, want_scores=True)
+    i1, g1, c1, _ = M().moe_route(x, wr, b1, K)
+    assert bool((i1[:, 0] == 7).all()) and int(c1[7]) == T
+    s = s0.cpu().numpy()
+    i1n, g1n = i1.cpu().numpy(), g1.cpu().numpy()
+    for t in range(T):
+        sel = i1n[t]
+        np.testing.assert_allclose(g1n[t], s[t, sel] / s[t, sel].sum(), rtol=0, atol=1e-6)
+
+
+def test_route_empty_and_extremes():
+    d, N = 256, 16
+    wr = I.gen_normal(3, (N, d), 0.05).to(DEV)
+    bias = torch.zeros(N, dtype=torch.float32, device=DEV)
+    idx, gate, counts, _ = M().moe_route(torch.empty((0, d), dtype=torch.bfloat16, device=DEV), wr, bias, 2)
+    assert idx.shape == (0, 2) and int(counts.sum()) == 0
+    x = I.gen_normal(4, (33, d), 1.0)
+    idx, gate, counts, _ = M().moe_route(x.to(DEV), wr, bias, N)  # K = N: every expert
+    r = O.route(np64(x), np64(wr.cpu()), np.zeros(N, np.float32), N)
+    assert all(set(row) == set(range(N)) for row in idx.cpu().numpy())
+    np.testing.assert_allclose(np.sort(gate.cpu().numpy(), 1), np.sort(r["gate"], 1), atol=1e-6)
+    assert np.array_equal(counts.cpu().numpy(), np.full(N, 33))
+
+
+# ------------------------------------------------------------------ permutation
+
+
+@pytest.mark.parametrize("T,K,N,zipf", [(1, 1, 4, 0.0), (300, 8, 256, 1.1), (1000, 2, 16, 0.0), (4096, 8, 256, 0.0)])
+def test_permute_bitexact(T, K, N, zipf):
+    say(f"permute T={T} K={K} N={N}")
+    idx, _ = I.gen_routing(T * 31 + N, T, K, N, zipf)
+    offs, st, pp = M().moe_permute(idx.to(DEV), N, 1)
+    oo, so, po = O.permute(idx.numpy(), N, 1)
+    assert np.array_equal(offs.cpu().numpy(), oo)
+    assert np.array_equal(st.cpu().numpy(), so)
+    assert np.array_equal(pp.cpu().numpy(), po)
+    check_permutation_properties(offs, st, pp, idx, N)
+
+
+def test_permute_empty_and_invalid():
+    idx = torch.zeros((0, 2), dtype=torch.int32, device=DEV)
+    offs, st, pp = M().moe_permute(idx, 8, 1)
+    assert offs.cpu().tolist() == [0] * 10
+    bad = torch.tensor([[0, 9], [1, 2], [-1, 3]], dtype=torch.int32, device=DEV)  # 9 and -1 invalid
+    offs, st, pp = M().moe_permute(bad, 8, 1)
+    ppn = pp.cpu().numpy()
+    assert ppn[0, 1] == -1 and ppn[2, 0] == -1
+    assert offs.cpu().tolist()[8:] == [4, 7]
+    assert st.cpu().numpy()[:4].tolist() == [0, 1, 1, 2]
+
+
+# ------------------------------------------------------------------ grouped GEMM
+
+
+def _offsets(sizes):
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("swiglu,out_dtype", [(False, torch.float32), (False, torch.bfloat16), (True, torch.bfloat16)])
+def test_gemm_bf16(swiglu, out_dtype):
+    G, K = 6, 384
+    N = 256
+    sizes = I.gen_group_sizes(1, G, 90)
+    sizes[2] = 0
+    sizes[4] = 257  # three row tiles, ragged tail
+    offs = _offsets(sizes)
+    rows = int(offs[-1])
+    T = 200
+    a_rows = np.random.default_rng(5).integers(0, T, rows).astype(np.int32)
+    A = I.gen_normal(21, (T, K), 1.0)
+    W = I.gen_normal(22, (G, N, K), 0.05)
+    oc = N // 2 if swiglu else N
+    out = torch.empty((rows, oc), dtype=out_dtype, device=DEV)
+    M().moe_grouped_gemm(A.to(DEV), W.to(DEV), torch.from_numpy(offs).to(DEV), 0, G, rows, out,
+                         a_rows=torch.from_numpy(a_rows).to(DEV), swiglu=swiglu)
+    got = np64(out)
+    An, Wn = np64(A), np64(W)
+    for g in range(G):
+        lo, hi = offs[g], offs[g + 1]
+        if hi == lo:
+            continue
+        xr = An[a_rows[lo:hi]]
+        ref = O.swiglu_hidden(xr, Wn[g]) if swiglu else xr @ Wn[g].T
+        if out_dtype == torch.float32:
+            assert rel_err(got[lo:hi], ref) < 1e-5, g
+        else:  # one bf16 rounding of the fp32 result
+            assert np.all(np.abs(got[lo:hi] - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6 * np.sqrt(np.mean(ref ** 2))), g
+
+
+def test_gemm_subrange_and_plain_rows():
+    """first_group > 0 and A indexed by the global sorted row (the shared-expert launch)."""
+    G, N, K = 4, 128, 128
+    sizes = np.array([10, 0, 70, 130])
+    offs = _offsets(sizes)
+    rows = int(offs[-1])
+    A = I.gen_normal(31, (rows, K), 1.0)
+    W = I.gen_normal(32, (G, N, K), 0.05)
+    out = torch.empty((int(sizes[2] + sizes[3]), N), dtype=torch.float32, device=DEV)
+    M().moe_grouped_gemm(A.to(DEV), W.to(DEV), torch.from_numpy(offs).to(DEV), 2, 2, int(sizes[2] + sizes[3]), out)
+    got = np64(out)
+    An, Wn = np64(A), np64(W)
+    ref = np.concatenate([An[offs[2]:offs[3]] @ Wn[2].T, An[offs[3]:offs[4]] @ Wn[3].T])
+    assert rel_err(got, ref) < 1e-5
+
+
+def test_gemm_fp8_exact():
+    """E4M3 codes of small integers with power-of-two scales: every product and every sum is
+    exact in fp32, so the fp8 GEMM must equal the oracle bit for bit.  This pins the MFMA
+    operand layout, the per-128-K promotion and the scale indexing (per row tile of A, per
+    128x128 block of W)."""
+    G, N, K = 3, 256, 512
+    sizes = np.array([5, 130, 64])
+    offs = _offsets(sizes)
+    rows = int(offs[-1])
+    T = 100
+    a_rows = np.random.default_rng(2).integers(0, T, rows).astype(np.int32)
+    Aq = I.gen_e4m3_codes(41, (T, K), small_int=True)
+    As = I.gen_scales(42, (T, K // 128), pow2=True)
+    Wq = I.gen_e4m3_codes(43, (G, N, K), small_int=True)
+    Ws = I.gen_scales(44, (G, N // 128, K // 128), pow2=True)
+    out = torch.empty((rows, N), dtype=torch.float32, device=DEV)
+    M().moe_grouped_gemm(Aq.to(DEV), Wq.to(DEV), torch.from_numpy(offs).to(DEV), 0, G, rows, out,
+                         a_scale=As.to(DEV), a_rows=torch.from_numpy(a_rows).to(DEV), w_scale=Ws.to(DEV))
+    got = out.cpu().numpy().astype(np.float64)
+    A = O.dequant_1x128(Aq.numpy(), As.numpy())
+    for g in range(G):
+        Wd = O.dequant_128x128(Wq[g].numpy(), Ws[g].numpy())
+        ref = A[a_rows[offs[g]:offs[g + 1]]] @ Wd.T
+        assert np.array_equal(got[offs[g]:offs[g + 1]], ref), g
+
+
+@pytest.mark.parametrize("swiglu,out_kind", [(False, "f32"), (True, "bf16"), (True, "fp8")])
+def test_gemm_fp8_random(swiglu, out_kind):
+    G, K = 5, 512
+    N = 512 if swiglu else 256
+    sizes = I.gen_group_sizes(7, G, 100)
+    sizes[1] = 0
+    sizes[3] = 260
+    offs = _offsets(sizes)
+    rows = int(offs[-1])
+    T = 300
+    a_rows = np.random.default_rng(3).integers(0, T, rows).astype(np.int32)
+    Aq = I.gen_e4m3_codes(51, (T, K))
+    As = I.gen_scales(52, (T, K // 128))
+    Wq = I.gen_e4m3_codes(53, (G, N, K))
+    Ws = I.gen_scales(54, (G, N // 128, K // 128))
+    oc = N // 2 if swiglu else N
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[out_kind]
+    out = torch.empty((rows, oc), dtype=dt, device=DEV)
+    osc = torch.empty((rows, oc // 128), dtype=torch.float32, device=DEV) if out_kind == "fp8" else None
+    M().moe_grouped_gemm(Aq.to(DEV), Wq.to(DEV), torch.from_numpy(offs).to(DEV), 0, G, rows, out,
+                         a_scale=As.to(DEV), a_rows=torch.from_numpy(a_rows).to(DEV), w_scale=Ws.to(DEV),
+                         swiglu=swiglu, out_scale=osc)
+    A = O.dequant_1x128(Aq.numpy(), As.numpy())
+    ref = np.zeros((rows, oc))
+    for g in range(G):
+        if sizes[g] == 0:
+            continue
+        Wd = O.dequant_128x128(Wq[g].numpy(), Ws[g].numpy())
+        xr = A[a_rows[offs[g]:offs[g + 1]]]
+        ref[offs[g]:offs[g + 1]] = O.swiglu_hidden(xr, Wd) if swiglu else xr @ Wd.T
+    if out_kind == "fp8":
+        got = O.dequant_1x128(out.cpu().numpy(), osc.cpu().numpy())
+        qo, so = O.quant_1x128(O.fp32_round(ref))
+        np.testing.assert_allclose(osc.cpu().numpy(), so, rtol=1e-5)
+        same = np.mean(out.cpu().numpy() == qo)
+        say(f"  fp8 h codes identical to the oracle's: {same:.5f}")
+        assert same > 0.99
+        assert rel_err(got, ref) < FP8_TOL
+    elif out_kind == "bf16":
+        assert rel_err(np64(out), ref) < 1e-2
+    else:
+        assert rel_err(np64(out), ref) < 1e-5
+
+
+# ------------------------------------------------------------------ combine and bias update
+
+
+@pytest.mark.parametrize("T,K,d", [(1, 1, 8), (77, 8, 7168), (300, 2, 256)])
+def test_combine(T, K, d):
+    idx, gate = I.gen_routing(T + K, T, K, 16)
+    pp = torch.from_numpy(np.random.default_rng(T).permutation(T * K).reshape(T, K).astype(np.int32))
+    y = I.gen_normal(61, (T * K, d), 1.0)
+    ysh = I.gen_normal(62, (T, d), 1.0, dtype=torch.float32)
+    o32 = M().moe_combine(y.to(DEV), ysh.to(DEV), pp.to(DEV), gate.to(DEV), torch.float32)
+    o16 = M().moe_combine(y.to(DEV), ysh.to(DEV), pp.to(DEV), gate.to(DEV), torch.bfloat16)
+    ref = O.combine(np64(y), np64(ysh), pp.numpy(), gate.numpy().astype(np.float64))
+    assert rel_err(np64(o32), ref) < 1e-6
+    assert torch.equal(o16.cpu(), o32.cpu().to(torch.bfloat16))
+    o_ns = M().moe_combine(y.to(DEV), None, pp.to(DEV), gate.to(DEV), torch.float32)
+    assert rel_err(np64(o_ns), O.combine(np64(y), None, pp.numpy(), gate.numpy().astype(np.float64))) < 1e-6
+
+
+def test_bias_update_bitexact():
+    N, T, K = 256, 4096, 8
+    rng = np.random.default_rng(9)
+    counts = rng.poisson(T * K / N, N).astype(np.int32)
+    counts[:4] = T * K // N  # exactly at the mean: unchanged
+    bias = rng.uniform(-0.01, 0.01, N).astype(np.float32)
+    bias[0] = -0.0
+    b = torch.from_numpy(bias).to(DEV)
+    M().moe_bias_update(b, torch.from_numpy(counts).to(DEV), T * K, 0.001)
+    want = O.bias_update(bias, counts, T, K, 0.001)
+    assert np.array_equal(b.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+# ------------------------------------------------------------------ the whole layer
+
+
+def _layer_case(cfg):
+    x = I.gen_x(cfg)
+    wr = I.gen_router(cfg)
+    bias = I.gen_bias(cfg)
+    experts = [I.gen_expert(cfg, e) for e in range(cfg.groups)]
+    W13 = torch.stack([e[0] for e in experts]).to(torch.bfloat16)
+    W2 = torch.stack([e[1] for e in experts]).to(torch.bfloat16)
+    return x.to(torch.bfloat16), wr.to(torch.bfloat16), bias, W13, W2
+
+
+@pytest.mark.parametrize("cfg", [
+    I.TINY,
+    I.small(I.V3_BF16, name="bf16_small", T=300, d=512, n_experts=32, top_k=4, inter=128, w_std=0.04, router_std=0.04),
+    I.small(I.V3_GROUP, name="group_small", T=257, d=256, n_experts=64, top_k=6, inter=64, n_group=8, topk_group=4,
+            w_std=0.05, router_std=0.05),
+], ids=lambda c: c.name)
+def test_layer_bf16(cfg):
+    say(f"layer bf16 {cfg.name}")
+    x, wr, bias, W13, W2 = _layer_case(cfg)
+    layer = M().MoELayer(wr.to(DEV), W13.to(DEV), W2.to(DEV), bias.to(DEV), cfg.top_k, cfg.n_group, cfg.topk_group)
+    out32, buf = layer.forward(x.to(DEV), out_dtype=torch.float32, keep=True)
+    out16 = M().moe_combine(buf["y"], buf["y_shared"], buf["pair_pos"], buf["topk_gate"], torch.bfloat16)
+    assert torch.equal(out16.cpu(), out32.cpu().to(torch.bfloat16))
+    x64 = np64(x)
+    r = O.route(x64, np64(wr), bias.numpy(), cfg.top_k, cfg.n_group, cfg.topk_group)
+    tie = check_route(buf["topk_idx"], buf["topk_gate"], buf["expert_counts"], None, r, cfg.n_experts, cfg.top_k)
+    check_permutation_properties(buf["expert_offsets"], buf["sorted_token"], buf["pair_pos"], buf["topk_idx"], cfg.n_experts)
+    W13n, W2n = np64(W13), np64(W2)
+    ref, _ = O.forward_sparse(x64, r["idx"], r["gate"], cfg.n_experts, lambda e: (W13n[e], W2n[e]), "bf16")
+    keep = ~tie
+    err = rel_err(np64(out32)[keep], ref[keep])
+    exact, _ = O.forward_sparse(x64, r["idx"], r["gate"], cfg.n_experts, lambda e: (W13n[e], W2n[e]), "exact")
+    say(f"  err vs bf16-modelling oracle {err:.2e}; vs exact fp64 {rel_err(np64(out32)[keep], exact[keep]):.2e}; "
+        f"bf16 store vs exact {rel_err(np64(out16)[keep], exact[keep]):.2e}")
+    assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("cfg", [
+    I.small(I.V3_FP8, name="fp8_small", T=300, d=512, n_experts=32, top_k=4, inter=256, w_std=0.04, router_std=0.04),
+    I.small(I.V3_FP8, name="fp8_small_2", T=129, d=256, n_experts=16, top_k=8, inter=128, w_std=0.05, router_std=0.05),
+], ids=lambda c: c.name)
+def test_layer_fp8(cfg):
+    say(f"layer fp8 {cfg.name}")
+    x, wr, bias, W13, W2 = _layer_case(cfg)
+    layer = M().MoELayer(wr.to(DEV), W13.to(DEV), W2.to(DEV), bias.to(DEV), cfg.top_k, fp8=True)
+    out32, buf = layer.forward(x.to(DEV), out_dtype=torch.float32, keep=True)
+    x64 = np64(x)
+    r = O.route(x64, np64(wr), bias.numpy(), cfg.top_k)
+    tie = check_route(buf["topk_idx"], buf["topk_gate"], buf["expert_counts"], None, r, cfg.n_experts, cfg.top_k)
+    # the quantised activations are bit-exact with the oracle's
+    xq, xs = O.quant_1x128(x.float().numpy())
+    assert np.array_equal(buf["xq"].cpu().numpy(), xq) and np.array_equal(buf["xs"].cpu().numpy(), xs)
+    wq, ws = O.quant_128x128(W13[3].float().numpy())
+    assert np.array_equal(layer.W13[3].cpu().numpy(), wq) and np.array_equal(layer.W13_s[3].cpu().numpy(), ws)
+    W13n, W2n = np64(W13), np64(W2)
+    ref, _ = O.forward_sparse(x64, r["idx"], r["gate"], cfg.n_experts, lambda e: (W13n[e], W2n[e]), "fp8")
+    keep = ~tie
+    err = rel_err(np64(out32)[keep], ref[keep])
+    bf, _ = O.forward_sparse(x64, r["idx"], r["gate"], cfg.n_experts, lambda e: (W13n[e], W2n[e]), "bf16")
+    say(f"  err vs fp8-modelling oracle {err:.2e} (fp8 model vs bf16 model {rel_err(ref[keep], bf[keep]):.2e})")
+    assert err <= FP8_TOL
+
+
+def test_layer_bias_update_loop():
+    """A few training-mode steps: the device bias follows the oracle's update of the device
+    loads bit for bit, and the loads equal the histogram of the device routing."""
+    cfg = I.small(I.V3_BF16, name="loop", T=256, d=256, n_experts=32, top_k=4, inter=64)
+    x, wr, bias, W13, W2 = _layer_case(cfg)
+    layer = M().MoELayer(wr.to(DEV), W13.to(DEV), W2.to(DEV), bias.to(DEV), cfg.top_k)
+    b = bias.numpy().copy()
+    for step in range(5):
+        _, buf = layer.forward(x.to(DEV), update_bias=True, gamma=0.01, keep=True)
+        counts = buf["expert_counts"].cpu().numpy()
+        assert np.array_equal(counts, np.bincount(buf["topk_idx"].cpu().numpy().ravel(), minlength=cfg.n_experts))
+        b = O.bias_update(b, counts, cfg.T, cfg.top_k, 0.01)
+        assert np.array_equal(layer.bias.cpu().numpy().view(np.uint32), b.view(np.uint32)), step
+
+
+def test_layer_deterministic():
+    cfg = I.small(I.V3_BF16, name="det", T=200, d=256, n_experts=16, top_k=4, inter=64)
+    x, wr, bias, W13, W2 = _layer_case(cfg)
+    layer = M().MoELayer(wr.to(DEV), W13.to(DEV), W2.to(DEV), bias.to(DEV), cfg.top_k)
+    a = layer.forward(x.to(DEV))
+    b = layer.forward(x.to(DEV))
+    assert torch.equal(a, b)
