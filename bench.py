@@ -1,0 +1,307 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
+                    [--no-cpu-baseline]
+
+One step = one training-mode forward of one DeepSeekMoE layer over one batch of synthetic
+tokens: route -> permute -> [fp8 quantisation of x] -> gate/up grouped GEMM + SwiGLU ->
+down grouped GEMMs -> combine -> bias update.  Inputs and weights are resident in HBM
+before the timed region.  The headline workload is the DeepSeek-V3-shaped bf16 layer at
+T = 4096 tokens (d = 7168, 256 routed + 1 shared SwiGLU experts of width 2048, top-8);
+the fp8 layer at T = 16384 and the decode-shaped fp8 run (T = 256, Zipf-skewed bias, 100
+steps of the bias update) are reported in the same line under "secondary".
+
+Prints ONE JSON line.  Weights are random (no checkpoint); inputs are seeded synthetic data.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="v3_bf16_T4096")
+    p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--decode-steps", type=int, default=None)
+    return p.parse_args()
+
+
+class KernelTimer:
+    """HIP events around one launch on the stream it runs on; averages over the timed steps."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def wrap(self, fn, *a, **kw):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record(t.cuda.current_stream())
+        r = fn(*a, **kw)
+        e.record(t.cuda.current_stream())
+        self.pairs.append((s, e))
+        return r
+
+    def mean_ms(self):
+        if not self.pairs:
+            return None
+        return sum(s.elapsed_time(e) for s, e in self.pairs) / len(self.pairs)
+
+
+def run_layer_steps(torch, M, layer, xs, steps, warmup, timer_gate_up, gamma, update_bias=True):
+    """Warm up, then time `steps` forwards (events on the current stream)."""
+    L = M._lib
+    orig = L.moe_grouped_gemm
+    state = {"timing": False}
+
+    def gg(*a, **kw):
+        if state["timing"] and kw.get("swiglu"):
+            return timer_gate_up.wrap(orig, *a, **kw)
+        return orig(*a, **kw)
+
+    import sparse_moe_layer_sigmoid_amd.layer as layer_mod
+    layer_mod.L.moe_grouped_gemm = gg
+    try:
+        for i in range(warmup):
+            layer.forward(xs[i % len(xs)], update_bias=update_bias, gamma=gamma)
+        torch.cuda.synchronize()
+        state["timing"] = True
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            layer.forward(xs[i % len(xs)], update_bias=update_bias, gamma=gamma)
+        end.record()
+        torch.cuda.synchronize()
+        state["timing"] = False
+        return start.elapsed_time(end) / steps
+    finally:
+        layer_mod.L.moe_grouped_gemm = orig
+
+
+def gate_up_bytes(cfg, counts_np, fp8: bool):
+    """Algorithmic HBM bytes of one gate/up launch: the W13 of every expert with at least one
+    row (plus the shared one) read once, each gathered input row read once, h written once."""
+    esz = 1 if fp8 else 2
+    active = int((counts_np > 0).sum()) + 1
+    w = active * 2 * cfg.inter * cfg.d * esz
+    if fp8:
+        w += active * (2 * cfg.inter // 128) * (cfg.d // 128) * 4
+    rows = cfg.rows
+    a = rows * cfg.d * esz + (rows * (cfg.d // 128) * 4 if fp8 else 0)
+    h = rows * cfg.inter * esz + (rows * (cfg.inter // 128) * 4 if fp8 else 0)
+    return w + a + h
+
+
+def step_bytes(cfg, counts_np, fp8: bool):
+    """Algorithmic bytes of one whole-layer step (weights of active experts + router once,
+    x in, out written): the decode-shaped run's GB/s numerator."""
+    esz = 1 if fp8 else 2
+    active = int((counts_np > 0).sum()) + 1
+    w = active * 3 * cfg.inter * cfg.d * esz
+    if fp8:
+        w += active * ((2 * cfg.inter // 128) * (cfg.d // 128) + (cfg.d // 128) * (cfg.inter // 128)) * 4
+    return w + cfg.n_experts * cfg.d * 2 + 2 * cfg.T * cfg.d * 2
+
+
+def kernel_src_sha():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "sparse_moe_layer_sigmoid_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_tag):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they were taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha") != kernel_src_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, x_cpu, wr_cpu, bias_cpu, counts_hint=None):
+    """The CPU oracle, untuned, on a bounded sample of the workload: full fp64 routing of a
+    token sample plus the FFN of a sample of experts on their routed rows; scaled to the
+    whole step by algorithmic FLOPs."""
+    import numpy as np
+
+    from oracle import moe_oracle as O
+    from sparse_moe_layer_sigmoid_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    n_tok = min(cfg.T, 1024)
+    x64 = x_cpu[:n_tok].double().numpy()
+    t0 = time.perf_counter()
+    r = O.route(x64, wr_cpu.double().numpy(), bias_cpu.numpy(), cfg.top_k, cfg.n_group, cfg.topk_group)
+    t_route = time.perf_counter() - t0
+    # FFN of n_exp routed experts on the rows the sampled tokens send them, plus the shared
+    # expert on the same tokens
+    n_exp = 4
+    idx = r["idx"]
+    experts = list(range(n_exp))
+    weights = {e: I.gen_expert(cfg, e) for e in experts + [cfg.n_experts]}
+    t1 = time.perf_counter()
+    rows_done = 0
+    for e in experts + [cfg.n_experts]:
+        toks = np.arange(n_tok) if e == cfg.n_experts else np.nonzero((idx == e).any(axis=1))[0]
+        if len(toks) == 0:
+            continue
+        w13, w2 = weights[e]
+        O.expert_rows(x64[toks], w13.double().numpy(), w2.double().numpy(), "exact")
+        rows_done += len(toks)
+    t_ffn = time.perf_counter() - t1
+    route_flops = 2 * n_tok * cfg.d * cfg.n_experts
+    ffn_flops = 6 * cfg.d * cfg.inter * rows_done
+    total_flops = O.layer_flops(cfg.T, cfg.d, cfg.n_experts, cfg.top_k, cfg.inter)
+    # seconds for the whole step at the sample's per-FLOP rates
+    est = t_route * (2 * cfg.T * cfg.d * cfg.n_experts) / route_flops + t_ffn * (total_flops - 2 * cfg.T * cfg.d * cfg.n_experts) / ffn_flops
+    return {"value": round(cfg.T / est, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"fp64 oracle: routing of {n_tok} tokens ({t_route:.1f}s) + SwiGLU FFN of experts "
+                       f"{experts} and the shared expert on those tokens' rows ({rows_done} rows, {t_ffn:.1f}s); "
+                       f"scaled to the full T={cfg.T} step by algorithmic FLOPs"),
+            "seconds_measured": round(t_route + t_ffn, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1 "
+                          "(the multi-GPU expert-parallel path is a design, not built)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import sparse_moe_layer_sigmoid_amd as M
+    from oracle import moe_oracle as O
+    from sparse_moe_layer_sigmoid_amd import inputs as I
+
+    M.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfgs = {c.name: c for c in I.CONFIGS.values()}
+    cfg = cfgs[args.workload]
+    t0 = time.time()
+    log(f"[bench] generating V3 weights for {cfg.groups} experts ...")
+    W13, W2 = I.gen_all_weights(cfg, dev)
+    log(f"[bench] weights ready in {time.time() - t0:.1f}s")
+    wr_cpu = I.gen_router(cfg).to(torch.bfloat16)
+    wr = wr_cpu.to(dev)
+
+    def measure(cfg, fp8, steps, warmup, n_batches=1):
+        bias_cpu = I.gen_bias(cfg)
+        layer = M.MoELayer(wr, W13, W2, bias_cpu.to(dev), cfg.top_k, cfg.n_group, cfg.topk_group, fp8=fp8)
+        xs_cpu = [I.gen_x(cfg, step=None if n_batches == 1 else i) for i in range(n_batches)]
+        xs = [x.to(dev) for x in xs_cpu]
+        _, buf = layer.forward(xs[0], keep=True)
+        counts0 = buf["expert_counts"].cpu().numpy()
+        layer.bias.copy_(bias_cpu.to(dev))
+        timer = KernelTimer(torch)
+        ms = run_layer_steps(torch, M, layer, xs, steps, warmup, timer, cfg.gamma)
+        return layer, xs_cpu, bias_cpu, counts0, ms, timer.mean_ms()
+
+    # ---------------------------------------------------------------- headline workload
+    fp8_main = cfg.dtype == "fp8"
+    layer, xs_cpu, bias_cpu, counts0, ms, gu_ms = measure(cfg, fp8_main, args.steps, args.warmup)
+    flops = O.layer_flops(cfg.T, cfg.d, cfg.n_experts, cfg.top_k, cfg.inter)
+    tok_s = cfg.T / (ms / 1e3)
+    gu_bytes = gate_up_bytes(cfg, counts0, fp8_main)
+    achieved = gu_bytes / (gu_ms / 1e3) / 1e9
+    tag = f"gate_up_{cfg.name}"
+    line = {
+        "metric": "MoE-layer tokens/s (T=4096 bf16 DeepSeek-V3 layer); % MFMA peak; decode GB/s",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8" if fp8_main else "bf16", "data": "synthetic (seeded N(0,1) x, random-init weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_routed": cfg.n_experts, "n_shared": 1,
+                   "top_k": cfg.top_k, "inter": cfg.inter, "n_group": cfg.n_group, "topk_group": cfg.topk_group,
+                   "step": "route+permute+gateup_swiglu+down+combine+bias_update"},
+        "tflops": round(flops / (ms / 1e3) / 1e12, 2),
+        "mfma_frac": round(flops / (ms / 1e3) / 1e12 / (FP8_PEAK_TFLOPS if fp8_main else BF16_PEAK_TFLOPS), 4),
+        "roofline": {"kernel": "grouped_gemm gate/up + SwiGLU", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(tag), "avg_launch_ms": round(gu_ms, 4),
+                     "algorithmic_bytes_per_launch": int(gu_bytes)},
+    }
+    log(f"[bench] {cfg.name}: {ms:.3f} ms/step, {tok_s:,.0f} tok/s, gate/up {gu_ms:.3f} ms ({achieved:.0f} GB/s)")
+
+    # ---------------------------------------------------------------- secondary workloads
+    if not args.no_secondary:
+        sec = []
+        c3 = I.V3_FP8
+        l3, _, _, counts3, ms3, gu3 = measure(c3, True, max(5, args.steps // 2), 3)
+        f3 = O.layer_flops(c3.T, c3.d, c3.n_experts, c3.top_k, c3.inter)
+        fl3 = 4 * c3.rows * c3.d * c3.inter
+        sec.append({"workload": c3.name, "dtype": "fp8", "ms_per_step": round(ms3, 4),
+                    "tokens_per_s": round(c3.T / (ms3 / 1e3), 1), "tflops": round(f3 / (ms3 / 1e3) / 1e12, 2),
+                    "mfma_frac_fp8_peak": round(f3 / (ms3 / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                    "gate_up_ms": round(gu3, 4),
+                    "gate_up_mfma_frac": round(fl3 / (gu3 / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4)})
+        log(f"[bench] {c3.name}: {ms3:.3f} ms/step")
+        del l3
+        c4 = I.V3_DECODE
+        n4 = args.decode_steps or c4.steps
+        bias4 = I.gen_bias(c4)
+        l4 = M.MoELayer(wr, W13, W2, bias4.to(dev), c4.top_k, fp8=True)
+        xs4 = [I.gen_x(c4, step=i).to(dev) for i in range(n4)]
+        for i in range(3):
+            l4.forward(xs4[i])
+        l4.bias.copy_(bias4.to(dev))
+        torch.cuda.synchronize()
+        loads, gbs, times = [], [], []
+        for i in range(n4):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            _, buf = l4.forward(xs4[i], update_bias=True, gamma=c4.gamma, keep=True)
+            e.record()
+            torch.cuda.synchronize()
+            t = s.elapsed_time(e)
+            cnt = buf["expert_counts"].cpu().numpy()
+            loads.append(float(cnt.max() / cnt.mean()))
+            gbs.append(step_bytes(c4, cnt, True) / (t / 1e3) / 1e9)
+            times.append(t)
+        sec.append({"workload": c4.name, "dtype": "fp8", "steps": n4,
+                    "ms_per_step_median": round(float(np.median(times)), 4),
+                    "gbs_median": round(float(np.median(gbs)), 1),
+                    "hbm_frac_median": round(float(np.median(gbs)) / HBM_PEAK_GBS, 4),
+                    "max_over_mean_load_first": round(loads[0], 3), "max_over_mean_load_last": round(loads[-1], 3),
+                    "max_over_mean_load_series_every10": [round(v, 3) for v in loads[::10]]})
+        log(f"[bench] {c4.name}: median {np.median(times):.3f} ms, {np.median(gbs):.0f} GB/s, load {loads[0]:.2f}->{loads[-1]:.2f}")
+        line["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        line["cpu_baseline"] = cpu_baseline(cfg, xs_cpu[0].to(torch.bfloat16), wr_cpu, bias_cpu)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -86,7 +86,7 @@ int moe_abi_version(void);
  * Limits: 0 <= T; 64 <= d, d % 64 == 0; 1 <= n_experts <= 256, n_experts % 4 == 0;
  * 1 <= top_k <= n_experts; n_group in 1..64 dividing n_experts, with n_experts/n_group >= 2
  * when n_group > 1; 1 <= topk_group <= n_group; top_k <= topk_group*n_experts/n_group.
- * T == 0 writes zero counts only.
+ * T == 0 writes zero counts only; x, topk_idx and topk_gate may then be NULL.
  * ------------------------------------------------------------------------------------ */
 size_t moe_route_workspace_size(int T, int n_experts);
 moe_status moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T,
@@ -109,7 +109,8 @@ moe_status moe_route(const uint16_t* x, const uint16_t* w_router, const float* b
  *                   [off[g], off[g+1]); the shared expert is group n_experts.
  *   sorted_token    device i32 [T * (top_k + n_shared)] out: token of each sorted row.
  *   pair_pos        device i32 [T, top_k] out: sorted row of pair (t, k).
- * Limits: 0 <= T; 1 <= top_k <= n_experts <= 256; n_shared in {0, 1}.
+ * Limits: 0 <= T; 1 <= top_k <= n_experts <= 256; n_shared in {0, 1}.  With T == 0 only the
+ * offsets are written (all zero) and topk_idx, sorted_token and pair_pos may be NULL.
  * ------------------------------------------------------------------------------------ */
 size_t moe_permute_workspace_size(int T, int n_experts);
 moe_status moe_permute(const int32_t* topk_idx, int T, int top_k, int n_experts, int n_shared,

@@ -361,7 +361,7 @@ def forward_dense(x, w_router, bias, w13, w2, top_k, n_group=1, topk_group=1):
     return out, r
 
 
-def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str = "exact"):
+def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str = "exact", workers: int = 1):
     """The layer computed the sparse way: permute, per-expert FFN on gathered rows, combine.
 
     idx, gate: [T, K] routing decisions and gates (from ``route``).
@@ -376,6 +376,7 @@ def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str 
                  tile along I, products accumulated exactly (float64 stands in for the
                  FP32 promotion every 128 elements), routed outputs rounded to bf16,
                  shared output to float32.
+    workers > 1 evaluates the experts concurrently (same arithmetic, for large inputs).
     Returns (out [T, d] float64, extras dict with the permutation and per-row outputs).
     """
     x = np.asarray(x, dtype=np.float64)
@@ -391,12 +392,20 @@ def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str 
     d = x.shape[1]
     y_routed = np.zeros((T * K, d))
     y_shared = np.zeros((T, d))
-    for e in range(n_experts + 1):
+
+    def one(e):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        if hi == lo:
-            continue
         we13, we2 = expert_weights(e)
-        y = expert_rows(x_in[sorted_token[lo:hi]], we13, we2, precision)
+        return e, lo, hi, expert_rows(x_in[sorted_token[lo:hi]], we13, we2, precision)
+
+    todo = [e for e in range(n_experts + 1) if offsets[e + 1] > offsets[e]]
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            results = list(ex.map(one, todo))
+    else:
+        results = [one(e) for e in todo]
+    for e, lo, hi, y in results:
         if e < n_experts:
             y_routed[lo:hi] = bf16_round(y) if precision in ("bf16", "fp8") else y
         else:

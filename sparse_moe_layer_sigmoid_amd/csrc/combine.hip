@@ -80,7 +80,8 @@ extern "C" moe_status moe_combine(const uint16_t* y_routed, const float* y_share
                                   hipStream_t stream) {
   using namespace moe;
   clear_error();
-  MOE_REQUIRE(y_routed && pair_pos && topk_gate && out, MOE_ERR_NULL, "moe_combine: a required pointer is NULL");
+  MOE_REQUIRE(T == 0 || (y_routed && pair_pos && topk_gate && out), MOE_ERR_NULL,
+              "moe_combine: a required pointer is NULL");
   MOE_REQUIRE(T >= 0 && top_k >= 1 && d >= 8 && d % 8 == 0, MOE_ERR_SHAPE,
               "moe_combine: T=%d top_k=%d d=%d (d must be a positive multiple of 8)", T, top_k, d);
   MOE_REQUIRE(out_dtype == MOE_BF16 || out_dtype == MOE_F32, MOE_ERR_DTYPE,

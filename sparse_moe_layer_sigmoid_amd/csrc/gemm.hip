@@ -346,7 +346,7 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
   using namespace moe;
   clear_error();
   MOE_REQUIRE(d != nullptr, MOE_ERR_NULL, "moe_grouped_gemm: desc is NULL");
-  MOE_REQUIRE(d->a && d->w && d->group_offsets && d->out, MOE_ERR_NULL,
+  MOE_REQUIRE(d->w && d->group_offsets && (d->m_total == 0 || (d->a && d->out)), MOE_ERR_NULL,
               "moe_grouped_gemm: a, w, group_offsets and out are required");
   const bool fp8 = d->in_dtype == MOE_FP8_E4M3;
   MOE_REQUIRE(fp8 || d->in_dtype == MOE_BF16, MOE_ERR_DTYPE, "moe_grouped_gemm: in_dtype must be MOE_BF16 or MOE_FP8_E4M3");

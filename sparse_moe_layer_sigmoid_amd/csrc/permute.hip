@@ -117,7 +117,7 @@ extern "C" moe_status moe_permute(const int32_t* topk_idx, int T, int top_k, int
                                   hipStream_t stream) {
   using namespace moe;
   clear_error();
-  MOE_REQUIRE(topk_idx && expert_offsets && sorted_token && pair_pos && ws, MOE_ERR_NULL,
+  MOE_REQUIRE(expert_offsets && ws && (T == 0 || (topk_idx && sorted_token && pair_pos)), MOE_ERR_NULL,
               "moe_permute: a required pointer is NULL");
   MOE_REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_permute: T=%d < 0", T);
   MOE_REQUIRE(n_experts >= 1 && n_experts <= 256, MOE_ERR_SHAPE,

@@ -85,7 +85,7 @@ extern "C" moe_status fp8_quant_1x128(const uint16_t* x, int rows, int cols, int
                                       uint8_t* q, float* scale, hipStream_t stream) {
   using namespace moe;
   clear_error();
-  MOE_REQUIRE(x && q && scale, MOE_ERR_NULL, "fp8_quant_1x128: a required pointer is NULL");
+  MOE_REQUIRE(rows == 0 || (x && q && scale), MOE_ERR_NULL, "fp8_quant_1x128: a required pointer is NULL");
   MOE_REQUIRE(rows >= 0 && cols >= 128 && cols % 128 == 0, MOE_ERR_SHAPE,
               "fp8_quant_1x128: rows=%d cols=%d (cols must be a positive multiple of 128)", rows, cols);
   MOE_REQUIRE(ldx >= cols && ldx % 8 == 0, MOE_ERR_ALIGN, "fp8_quant_1x128: ldx=%lld must be >= cols and a multiple of 8",

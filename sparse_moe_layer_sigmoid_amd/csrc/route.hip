@@ -249,7 +249,7 @@ extern "C" moe_status moe_route(const uint16_t* x, const uint16_t* w_router, con
                                 size_t ws_bytes, hipStream_t stream) {
   using namespace moe;
   clear_error();
-  MOE_REQUIRE(x && w_router && bias && topk_idx && topk_gate && expert_counts && ws,
+  MOE_REQUIRE(w_router && bias && expert_counts && ws && (T == 0 || (x && topk_idx && topk_gate)),
               MOE_ERR_NULL, "moe_route: a required pointer is NULL");
   MOE_REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_route: T=%d < 0", T);
   MOE_REQUIRE(d >= 64 && d % 64 == 0, MOE_ERR_SHAPE, "moe_route: d=%d must be a positive multiple of 64", d);

@@ -1,0 +1,160 @@
+"""GPU parity at the workloads' full sizes (DeepSeek-V3-shaped layer: d = 7168, 256 routed +
+1 shared SwiGLU experts of width 2048, top-8), in the launch configuration the benchmark
+times.  The routing, loads and permutation are checked for every token (bit-exact outside the
+1e-6 tie window; properties that hold at any size); the layer output is checked on sampled
+tokens that the CPU oracle recomputes one by one (their experts' weights regenerated on the
+host from the same seeded streams).
+"""
+import time
+from concurrent.futures import ThreadPoolExecutor
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from sparse_moe_layer_sigmoid_amd import inputs as I
+from tests.gpu_common import (BF16_TOL, FP8_TOL, TIE_WINDOW, check_permutation_properties, check_route,
+                              np64, rel_err, say)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(900)]
+DEV = "cuda:0"
+
+
+def M():
+    import sparse_moe_layer_sigmoid_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def v3():
+    t0 = time.time()
+    say("[fullsize] generating the V3 layer weights (257 experts) ...")
+    W13, W2 = I.gen_all_weights(I.V3_BF16, DEV)
+    wr_cpu = I.gen_router(I.V3_BF16)
+    torch.cuda.synchronize()
+    say(f"[fullsize] weights ready in {time.time() - t0:.1f}s")
+    ns = SimpleNamespace(W13=W13, W2=W2, wr_cpu=wr_cpu, wr=wr_cpu.to(DEV), fp8_layer=None)
+    yield ns
+    del ns.W13, ns.W2, ns.fp8_layer
+    torch.cuda.empty_cache()
+
+
+def fp8_layer(v3, bias, cfg):
+    if v3.fp8_layer is None:
+        say("[fullsize] quantising the weights to E4M3 (128x128 blocks) ...")
+        v3.fp8_layer = M().MoELayer(v3.wr, v3.W13, v3.W2, bias.to(DEV), cfg.top_k, fp8=True)
+    v3.fp8_layer.bias = bias.to(DEV).clone()
+    return v3.fp8_layer
+
+
+def _expert_fetcher(cfg, ids):
+    with ThreadPoolExecutor(16) as ex:
+        got = dict(zip(ids, ex.map(lambda e: I.gen_expert(cfg, e), ids)))
+    return lambda e: (got[e][0].double().numpy(), got[e][1].double().numpy())
+
+
+def _sampled_output_check(cfg, x_cpu, r, tie, out32, precision, n_tokens, tol):
+    cand = np.nonzero(~tie)[0]
+    pick = cand[np.linspace(0, len(cand) - 1, n_tokens).astype(int)]
+    experts = sorted(set(int(e) for e in r["idx"][pick].ravel()) | {cfg.n_experts})
+    say(f"[fullsize] oracle on {len(pick)} sampled tokens ({len(experts)} experts, {precision}) ...")
+    t0 = time.time()
+    fetch = _expert_fetcher(cfg, experts)
+    ref, _ = O.forward_sparse(x_cpu[pick].double().numpy(), r["idx"][pick], r["gate"][pick], cfg.n_experts,
+                              fetch, precision, workers=16)
+    got = np64(out32[torch.as_tensor(pick, device=out32.device)])
+    err = rel_err(got, ref)
+    say(f"[fullsize] {cfg.name}: max|out - oracle| / rms = {err:.3e} (tol {tol}) [{time.time() - t0:.0f}s]")
+    assert err <= tol
+    return err
+
+
+def _route_and_layer(v3, cfg, fp8):
+    x_cpu = I.gen_x(cfg)
+    bias = I.gen_bias(cfg)
+    if fp8:
+        layer = fp8_layer(v3, bias, cfg)
+    else:
+        layer = M().MoELayer(v3.wr, v3.W13, v3.W2, bias.to(DEV), cfg.top_k, cfg.n_group, cfg.topk_group)
+    x = x_cpu.to(DEV)
+    out32, buf = layer.forward(x, out_dtype=torch.float32, keep=True)
+    out16 = M().moe_combine(buf["y"], buf["y_shared"], buf["pair_pos"], buf["topk_gate"], torch.bfloat16)
+    assert torch.equal(out16, out32.to(torch.bfloat16))  # bf16 output = RNE of the fp32 result
+    say(f"[fullsize] {cfg.name}: oracle routing of {cfg.T} tokens ...")
+    r = O.route(np64(x_cpu), np64(v3.wr_cpu), bias.numpy(), cfg.top_k, cfg.n_group, cfg.topk_group)
+    idx, gate, counts, scores = M().moe_route(x, v3.wr, bias.to(DEV), cfg.top_k, cfg.n_group, cfg.topk_group,
+                                              want_scores=True)
+    tie = check_route(idx, gate, counts, scores, r, cfg.n_experts, cfg.top_k)
+    assert torch.equal(idx, buf["topk_idx"]) and torch.equal(counts, buf["expert_counts"])
+    check_permutation_properties(buf["expert_offsets"], buf["sorted_token"], buf["pair_pos"], buf["topk_idx"],
+                                 cfg.n_experts)
+    say(f"[fullsize] {cfg.name}: routing parity ok, {int(tie.sum())} tie-window tokens; "
+        f"max/mean load {counts.max().item() / counts.float().mean().item():.2f}")
+    return x_cpu, bias, r, tie, out32, buf
+
+
+def test_v3_bf16_T4096(v3):
+    cfg = I.V3_BF16
+    x_cpu, bias, r, tie, out32, buf = _route_and_layer(v3, cfg, False)
+    _sampled_output_check(cfg, x_cpu, r, tie, out32, "bf16", 12, BF16_TOL)
+
+
+def test_v3_group_bf16_T8192(v3):
+    cfg = I.V3_GROUP
+    x_cpu, bias, r, tie, out32, buf = _route_and_layer(v3, cfg, False)
+    gi = buf["topk_idx"].cpu().numpy()
+    # the group limit: every token's experts come from at most topk_group groups of 32
+    assert max(len(set(row // (cfg.n_experts // cfg.n_group))) for row in gi) <= cfg.topk_group
+    _sampled_output_check(cfg, x_cpu, r, tie, out32, "bf16", 8, BF16_TOL)
+
+
+def test_v3_fp8_T16384(v3):
+    cfg = I.V3_FP8
+    x_cpu, bias, r, tie, out32, buf = _route_and_layer(v3, cfg, True)
+    xq, xs = O.quant_1x128(x_cpu.float().numpy()[:512])
+    assert np.array_equal(buf["xq"][:512].cpu().numpy(), xq) and np.array_equal(buf["xs"][:512].cpu().numpy(), xs)
+    _sampled_output_check(cfg, x_cpu, r, tie, out32, "fp8", 3, FP8_TOL)
+
+
+def test_v3_decode_bias_loop(v3):
+    """The decode-shaped run: 100 training-mode steps of T = 256 fresh tokens with the
+    Zipf-skewed bias.  While no token falls in the tie window the GPU's loads and bias
+    trajectory equal the oracle's bit for bit; every step the loads equal the histogram of
+    the GPU's own routing and each bias moved by exactly -gamma, 0 or +gamma as the rule
+    dictates for those loads."""
+    cfg = I.V3_DECODE
+    bias = I.gen_bias(cfg)
+    layer = fp8_layer(v3, bias, cfg)
+    b_orc = bias.numpy().copy()
+    in_sync = True
+    loads = []
+    wr64 = np64(v3.wr_cpu)
+    for step in range(cfg.steps):
+        x_cpu = I.gen_x(cfg, step=step)
+        b_prev = layer.bias.cpu().numpy().copy()
+        out32, buf = layer.forward(x_cpu.to(DEV), out_dtype=torch.float32, update_bias=True, gamma=cfg.gamma,
+                                   keep=True)
+        gi = buf["topk_idx"].cpu().numpy()
+        gc = buf["expert_counts"].cpu().numpy()
+        b_gpu = layer.bias.cpu().numpy()
+        assert np.array_equal(gc, np.bincount(gi.ravel(), minlength=cfg.n_experts))
+        diff = gc.astype(np.int64) * cfg.n_experts - cfg.T * cfg.top_k
+        want = np.where(diff > 0, (b_prev + np.float32(-cfg.gamma)).astype(np.float32),
+                        np.where(diff < 0, (b_prev + np.float32(cfg.gamma)).astype(np.float32), b_prev))
+        assert np.array_equal(b_gpu.view(np.uint32), want.view(np.uint32)), step
+        loads.append(gc.max() / gc.mean())
+        if in_sync:
+            r = O.route(np64(x_cpu), wr64, b_orc, cfg.top_k)
+            tie = check_route(buf["topk_idx"], buf["topk_gate"], buf["expert_counts"], None, r, cfg.n_experts,
+                              cfg.top_k)
+            if tie.any():
+                in_sync = False
+                say(f"[fullsize] decode: tie-window token at step {step}; bit-exact trajectory check ends here")
+            else:
+                b_orc = O.bias_update(b_orc, O.expert_counts(r["idx"], cfg.n_experts), cfg.T, cfg.top_k, cfg.gamma)
+                assert np.array_equal(b_gpu.view(np.uint32), b_orc.view(np.uint32)), step
+            if step == 0:
+                _sampled_output_check(cfg, x_cpu, r, tie, out32, "fp8", 2, FP8_TOL)
+    say(f"[fullsize] decode: max/mean load {loads[0]:.2f} (step 0) -> {loads[-1]:.2f} (step {cfg.steps - 1})")
