@@ -71,8 +71,12 @@ int moe_abi_version(void);
  * the whole batch.  With n_group > 1 the selection is first limited to the topk_group
  * groups (of n_experts/n_group contiguous experts) with the largest sum of their two best
  * z -- the single-GPU stand-in for the node limit M = 4 of the same section.
- * The affinity is computed from bf16 inputs with fp32 accumulation; sigmoid, z, the
- * selection and the gates are fp32 ("FP8 混合精度訓練": gating stays in high precision).
+ * Precision ("FP8 混合精度訓練": gating stays in high precision): the affinities come from
+ * bf16 products with fp32 sums promoted out of the matrix cores every 256 elements; sigmoid,
+ * z, the selection and the gates are fp32.  A token whose fp32 decision margin (gap between
+ * the K-th and (K+1)-th z, or half the gap between the last kept and best dropped group
+ * score) is below 4e-6 is recomputed entirely in fp64 (exact products, fp64 sums, sigmoid,
+ * selection and gates), so the chosen experts match an fp64 evaluation of the definition.
  * Equal z: the lower expert index wins (likewise for equal group scores).
  *
  *   x           device bf16 [T, d]
@@ -83,9 +87,10 @@ int moe_abi_version(void);
  *   expert_counts device i32 [n_experts] out: load per expert (overwritten)
  *   scores      device f32 [T, n_experts] out, optional (NULL): the affinities s
  *   ws          device workspace of moe_route_workspace_size(T, n_experts) bytes
- * Limits: 0 <= T; 64 <= d, d % 64 == 0; 1 <= n_experts <= 256, n_experts % 4 == 0;
- * 1 <= top_k <= n_experts; n_group in 1..64 dividing n_experts, with n_experts/n_group >= 2
- * when n_group > 1; 1 <= topk_group <= n_group; top_k <= topk_group*n_experts/n_group.
+ * Limits: 0 <= T; 64 <= d, d % 64 == 0; 4 <= n_experts <= 256, n_experts % 4 == 0;
+ * 1 <= top_k <= n_experts; n_group in 1..64 dividing n_experts, with n_experts/n_group a
+ * power of two >= 4 when n_group > 1; 1 <= topk_group <= n_group;
+ * top_k <= topk_group*n_experts/n_group; ws 16-byte aligned.
  * T == 0 writes zero counts only; x, topk_idx and topk_gate may then be NULL.
  * ------------------------------------------------------------------------------------ */
 size_t moe_route_workspace_size(int T, int n_experts);

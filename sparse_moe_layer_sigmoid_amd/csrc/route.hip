@@ -1,20 +1,27 @@
-// moe_route: router affinities on the matrix cores, sigmoid, bias-adjusted top-K (with an
-// optional group limit), normalised gates and the per-expert load histogram.
+// moe_route: router affinities, sigmoid, bias-adjusted top-K (with an optional group
+// limit), normalised gates and the per-expert load histogram.
 //
 // "DeepSeek-V3 Technical Report" (wiki summary), "DeepSeekMoE と補助損失なしの負荷分散":
 // sigmoid affinity; the bias b_i is added to the affinity only to choose the experts; the
 // gates are the chosen original affinities normalised; the load is counted per batch; each
 // token is limited to M = 4 nodes (here: the topk_group best of n_group expert groups).
-// "FP8 混合精度訓練": the gating stays in high precision (bf16 products, fp32 sums).
+// "FP8 混合精度訓練": the gating stays in high precision (bf16 products, fp32 or better sums,
+// partial sums promoted out of the matrix cores every 256 elements).
 //
-// Design (gfx950): one workgroup of 4 waves owns TM tokens and all (<= 256) experts.  The
-// TM x 256-element slice of x is staged in LDS and shared by the 4 waves; each wave owns 64
-// experts and streams their router rows straight from L2 into 16x16x32 bf16 MFMAs.  The
-// logits land in LDS; then each wave walks its tokens with one expert quadruple per lane
-// (lane l holds experts 4l..4l+3) and picks the top-K by wave-wide argmax rounds (shuffle
-// butterflies; ties to the lower index).  Loads are counted in an LDS histogram per block
-// and reduced by a second one-workgroup kernel (integer sums: the result is exact and
-// independent of scheduling).
+// Four kernels:
+//  1. logits: a split-K MFMA GEMM.  A workgroup (4 waves) owns 64 tokens x all experts x one
+//     K slice; x and router rows are staged through LDS in 128-byte K steps (double
+//     buffered, XOR-swizzled); every 256 elements of K the 16x16x32 bf16 MFMA partial sum is
+//     added into an fp32 accumulator (the matrix cores truncate inside their adder, so long
+//     chains are avoided).  Partial logits of each slice go to the workspace.
+//  2. select: one wave per token (lane l holds experts 4l..4l+3) sums the slices in a fixed
+//     order, forms s and z, picks the top-K by wave-wide argmax rounds (ties to the lower
+//     index) and measures the decision margin: the gap between the K-th and (K+1)-th z, and
+//     between the last kept and the best dropped group score.
+//  3. refine + count: tokens whose fp32 margin is below kRefineGap are recomputed in fp64
+//     (exact bf16 products, fp64 sums, fp64 sigmoid and selection), so the choice of experts
+//     does not depend on the matrix cores' rounding; then each block histograms its tokens.
+//  4. reduce: one wave per expert sums the block histograms (integer sums: exact).
 #include <math.h>
 
 #include "abi_common.h"
@@ -24,18 +31,22 @@ namespace moe {
 namespace {
 
 constexpr uint32_t kNone = 0x7fffffffu;
+constexpr float kRefineGap = 4e-6f;  // fp32 decision margin below which a token is redone in fp64
+constexpr int kTM = 64;              // tokens per logits workgroup
+constexpr int kRows = 64 + 256;      // LDS rows per stage: 64 tokens + 256 router rows
 
-// (v, i) beats (bv, bi): larger value, or equal value and lower index; kNone never wins.
-__device__ __forceinline__ bool beats(float v, uint32_t i, float bv, uint32_t bi) {
+template <typename V>
+__device__ __forceinline__ bool beats(V v, uint32_t i, V bv, uint32_t bi) {
   if (i == kNone) return false;
   if (bi == kNone) return true;
   return v > bv || (v == bv && i < bi);
 }
 
-__device__ __forceinline__ void wave_argmax(float& bv, uint32_t& bi) {
+template <typename V>
+__device__ __forceinline__ void wave_argmax(V& bv, uint32_t& bi) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(bv, o, kWave);
+    const V ov = __shfl_xor(bv, o, kWave);
     const uint32_t oi = (uint32_t)__shfl_xor((int)bi, o, kWave);
     if (beats(ov, oi, bv, bi)) {
       bv = ov;
@@ -44,202 +55,365 @@ __device__ __forceinline__ void wave_argmax(float& bv, uint32_t& bi) {
   }
 }
 
-template <int TM>
-__global__ __launch_bounds__(256) void route_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int T, int d, int N, int K, int n_group, int topk_group,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
-    float* __restrict__ scores, int32_t* __restrict__ blk_counts) {
-  constexpr int KC = 256;      // K-slice of x staged in LDS (elements)
-  constexpr int XS = KC + 8;   // padded LDS row (elements): 528 B keeps MFMA reads conflict-free
-  constexpr int MT = TM / 16;  // 16-token MFMA tiles per wave
-  __shared__ __attribute__((aligned(16))) uint16_t xs[TM * XS];
-  __shared__ float lg[TM][257];
-  __shared__ int cnt[256];
-  __shared__ float zg[4][256];
+template <typename V>
+__device__ __forceinline__ V sigmoid_v(V u);
+template <>
+__device__ __forceinline__ float sigmoid_v<float>(float u) { return 1.0f / (1.0f + expf(-u)); }
+template <>
+__device__ __forceinline__ double sigmoid_v<double>(double u) { return 1.0 / (1.0 + exp(-u)); }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * TM;
-  cnt[tid] = 0;
-
-  f32x4 acc[MT][4];
+// Selection for one token by one wave.  u[r] is the logit of expert 4*lane + r.  Writes the
+// outputs when `write`; returns the decision margin (min of the expert gap and half the
+// group gap), +inf when nothing competes.
+template <typename V>
+__device__ V select_token(const V u[4], const float* __restrict__ bias, int N, int K, int n_group,
+                          int topk_group, int64_t t, bool write, int32_t* __restrict__ topk_idx,
+                          float* __restrict__ topk_gate, float* __restrict__ scores) {
+  const int lane = threadIdx.x & 63;
+  const V inf = (V)INFINITY;
+  V s4[4], z4[4];
+  bool av[4];
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int lrow = lane & 15, lk = (lane >> 4) * 8;
-  for (int kc0 = 0; kc0 < d; kc0 += KC) {
-    const int kcn = min(KC, d - kc0);
-    const int cpr = kcn / 8;
-    __syncthreads();
-    for (int q = tid; q < TM * cpr; q += 256) {
-      const int row = q / cpr, c = q - row * cpr;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (t0 + row < T) v = *(const u32x4*)(x + (size_t)(t0 + row) * d + kc0 + c * 8);
-      *(u32x4*)(xs + row * XS + c * 8) = v;
-    }
-    __syncthreads();
-    for (int kk = 0; kk < kcn; kk += 32) {
-      bf16x8_t bfr[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = wave * 64 + j * 16 + lrow;
-        if (e < N) {
-          bfr[j] = *(const bf16x8_t*)(wr + (size_t)e * d + kc0 + kk + lk);
-        } else {
-          bfr[j] = bf16x8_t{};
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const bf16x8_t a = *(const bf16x8_t*)(xs + (i * 16 + lrow) * XS + kk + lk);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(a, bfr[j], acc[i][j]);
-      }
+  for (int r = 0; r < 4; ++r) {
+    const int e = lane * 4 + r;
+    if (e < N) {
+      const V s = sigmoid_v<V>(u[r]);
+      V z = s + (V)bias[e];
+      if (z != z) z = -inf;  // NaN ranks below every number
+      s4[r] = s;
+      z4[r] = z;
+      av[r] = true;
+    } else {
+      s4[r] = (V)0;
+      z4[r] = -inf;
+      av[r] = false;
     }
   }
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lg[i * 16 + (lane >> 4) * 4 + r][wave * 64 + j * 16 + lrow] = acc[i][j][r];
-  __syncthreads();
+  if (write && scores != nullptr && lane * 4 < N)
+    *(f32x4*)(scores + t * N + lane * 4) = f32x4{(float)s4[0], (float)s4[1], (float)s4[2], (float)s4[3]};
 
-  const int gs = N / n_group;
-  for (int it = 0; it < TM / 4; ++it) {
-    const int tl = wave + 4 * it;
-    const int t = t0 + tl;
-    const bool valid = t < T;  // uniform across the wave
-    float s4[4], z4[4];
-    bool av[4];
+  V margin = inf;
+  if (n_group > 1) {
+    const int gs = N / n_group;  // a power of two >= 4: a lane's four experts share a group
+    const int lanes_per_group = gs >> 2;
+    const int g = (lane * 4) / gs;
+    V m1 = -inf, m2 = -inf;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int e = lane * 4 + r;
-      if (e < N) {
-        const float u = lg[tl][e];
-        const float s = 1.0f / (1.0f + expf(-u));
-        float z = s + bias[e];
-        if (z != z) z = -INFINITY;  // NaN ranks below every number
-        s4[r] = s;
-        z4[r] = z;
-        av[r] = true;
-      } else {
-        s4[r] = 0.f;
-        z4[r] = -INFINITY;
-        av[r] = false;
+      const V v = z4[r];
+      if (v > m1) {
+        m2 = m1;
+        m1 = v;
+      } else if (v > m2) {
+        m2 = v;
       }
     }
-    if (scores != nullptr && valid && lane * 4 < N)
-      *(f32x4*)(scores + (size_t)t * N + lane * 4) = f32x4{s4[0], s4[1], s4[2], s4[3]};
-
-    if (n_group > 1) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (lane * 4 + r < N) zg[wave][lane * 4 + r] = z4[r];
-      __syncthreads();
-      float gscore = -INFINITY;
-      if (lane < n_group) {
-        float m1 = -INFINITY, m2 = -INFINITY;
-        for (int i = 0; i < gs; ++i) {
-          const float v = zg[wave][lane * gs + i];
-          if (v > m1) {
-            m2 = m1;
-            m1 = v;
-          } else if (v > m2) {
-            m2 = v;
-          }
-        }
-        gscore = m1 + m2;
-      }
-      bool gav = lane < n_group;
-      uint64_t kept = 0;
-      for (int rr = 0; rr < topk_group; ++rr) {
-        float bv = gscore;
-        uint32_t bi = gav ? (uint32_t)lane : kNone;
-        wave_argmax(bv, bi);
-        if (bi == kNone) break;
-        kept |= 1ull << bi;
-        if ((uint32_t)lane == bi) gav = false;
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (av[r] && !((kept >> ((lane * 4 + r) / gs)) & 1ull)) av[r] = false;
-      __syncthreads();
+    for (int o = 1; o < lanes_per_group; o <<= 1) {
+      const V p1 = __shfl_xor(m1, o, kWave), p2 = __shfl_xor(m2, o, kWave);
+      const V lo = m1 < p1 ? m1 : p1;
+      const V hi2 = m2 > p2 ? m2 : p2;
+      m1 = m1 > p1 ? m1 : p1;
+      m2 = lo > hi2 ? lo : hi2;
     }
-
-    float sum = 0.f;
-    int my_idx[4] = {0, 0, 0, 0};
-    float my_s[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < K; ++k) {
-      float bv = 0.f;
-      uint32_t bi = kNone;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (av[r] && beats(z4[r], (uint32_t)(lane * 4 + r), bv, bi)) {
-          bv = z4[r];
-          bi = (uint32_t)(lane * 4 + r);
-        }
+    const bool leader = (lane % lanes_per_group) == 0 && g < n_group;
+    const V gscore = m1 + m2;
+    bool gav = leader;
+    uint64_t kept = 0;
+    V last = (V)0;
+    for (int rr = 0; rr <= topk_group; ++rr) {
+      if (rr == n_group) break;
+      V bv = gscore;
+      uint32_t bi = gav ? (uint32_t)g : kNone;
       wave_argmax(bv, bi);
-      if (bi == kNone) break;  // cannot happen within the documented limits
-      const int owner = (int)(bi >> 2), slot = (int)(bi & 3u);
-      float mine = s4[0];
-#pragma unroll
-      for (int r = 1; r < 4; ++r)
-        if (slot == r) mine = s4[r];
-      const float sk = __shfl(mine, owner, kWave);
-      if (lane == owner) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (slot == r) av[r] = false;
+      if (bi == kNone) break;
+      if (rr == topk_group) {
+        margin = (last - bv) * (V)0.5;  // a group score moves twice as much as one z
+        break;
       }
-      sum += sk;
-      if (lane == (k & 63)) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if ((k >> 6) == q) {
-            my_idx[q] = (int)bi;
-            my_s[q] = sk;
-          }
-      }
-      if (valid && lane == 0) atomicAdd(&cnt[bi], 1);
+      kept |= 1ull << bi;
+      last = bv;
+      if (gav && (uint32_t)g == bi) gav = false;
     }
-    if (valid) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k = q * 64 + lane;
-        if (k < K) {
-          topk_idx[(size_t)t * K + k] = my_idx[q];
-          topk_gate[(size_t)t * K + k] = my_s[q] / sum;
+    for (int r = 0; r < 4; ++r)
+      if (av[r] && !((kept >> g) & 1ull)) av[r] = false;
+  }
+
+  V sum = (V)0, zk = (V)0;
+  int my_idx[4] = {0, 0, 0, 0};
+  V my_s[4] = {(V)0, (V)0, (V)0, (V)0};
+  for (int k = 0; k <= K; ++k) {
+    V bv = (V)0;
+    uint32_t bi = kNone;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (av[r] && beats(z4[r], (uint32_t)(lane * 4 + r), bv, bi)) {
+        bv = z4[r];
+        bi = (uint32_t)(lane * 4 + r);
+      }
+    wave_argmax(bv, bi);
+    if (bi == kNone) break;
+    if (k == K) {  // the best expert left out: the decision margin
+      const V gap = zk - bv;
+      margin = gap < margin ? gap : margin;
+      break;
+    }
+    zk = bv;
+    const int owner = (int)(bi >> 2), slot = (int)(bi & 3u);
+    V mine = s4[0];
+#pragma unroll
+    for (int r = 1; r < 4; ++r)
+      if (slot == r) mine = s4[r];
+    const V sk = __shfl(mine, owner, kWave);
+    if (lane == owner) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (slot == r) av[r] = false;
+    }
+    sum += sk;
+    if (lane == (k & 63)) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if ((k >> 6) == q) {
+          my_idx[q] = (int)bi;
+          my_s[q] = sk;
         }
+    }
+  }
+  if (write) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = q * 64 + lane;
+      if (k < K) {
+        topk_idx[t * K + k] = my_idx[q];
+        topk_gate[t * K + k] = (float)(my_s[q] / sum);
       }
     }
   }
+  return margin;
+}
+
+// ---- kernel 1: split-K logits ----
+__global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wr,
+                                                           int T, int d, int N, int splits,
+                                                           float* __restrict__ part) {
+  constexpr int STAGE = kRows * 128;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile = blockIdx.x / splits, split = blockIdx.x - tile * splits;
+  const int t0 = tile * kTM;
+  const int nsteps_all = d / 64;
+  const int ks0 = (int)((int64_t)split * nsteps_all / splits);
+  const int ks1 = (int)((int64_t)(split + 1) * nsteps_all / splits);
+  const int cch = tid & 7;
+  // 10 chunks of 16 B per thread per stage: rows r = tid/8 + 32 i (i < 10): 0..63 tokens, 64.. router
+  const uint8_t* src[10];
+  bool live[10];
+  int dst[10];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    if (r < kTM) {
+      live[i] = t0 + r < T;
+      src[i] = reinterpret_cast<const uint8_t*>(x + (int64_t)min(t0 + r, T - 1) * d) + cch * 16;
+    } else {
+      const int e = r - kTM;
+      live[i] = e < N;
+      src[i] = reinterpret_cast<const uint8_t*>(wr + (int64_t)min(e, N - 1) * d) + cch * 16;
+    }
+    dst[i] = r * 128 + ((cch ^ (r & 7)) << 4);
+  }
+  u32x4 reg[10];
+  auto gload = [&](int ks) {
+#pragma unroll
+    for (int i = 0; i < 10; ++i)
+      reg[i] = live[i] ? *(const u32x4*)(src[i] + (int64_t)ks * 128) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 10; ++i) *(u32x4*)(smem + buf * STAGE + dst[i]) = reg[i];
+  };
+  f32x4 acc[4][4], prt[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = prt[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int lr = lane & 15, lg = lane >> 4;
+  if (ks0 < ks1) {
+    gload(ks0);
+    sstore(0);
+  }
   __syncthreads();
-  if (tid < N) blk_counts[(size_t)blockIdx.x * N + tid] = cnt[tid];
+  for (int ks = ks0; ks < ks1; ++ks) {
+    const int cur = (ks - ks0) & 1;
+    const bool more = ks + 1 < ks1;
+    if (more) gload(ks + 1);
+    const uint8_t* S = smem + cur * STAGE;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ch = h * 4 + lg;
+      bf16x8_t af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = i * 16 + lr;
+        af[i] = *(const bf16x8_t*)(S + r * 128 + ((ch ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = kTM + wave * 64 + j * 16 + lr;
+        bf[j] = *(const bf16x8_t*)(S + r * 128 + ((ch ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) prt[i][j] = mfma_bf16(af[i], bf[j], prt[i][j]);
+    }
+    if (((ks + 1) & 3) == 0 || !more) {  // promote every 256 elements of K
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] += prt[i][j];
+          prt[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    if (more) sstore(cur ^ 1);
+    __syncthreads();
+  }
+  float* out = part + (int64_t)split * T * 256;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + i * 16 + lg * 4 + r;
+      if (t < T) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[(int64_t)t * 256 + wave * 64 + j * 16 + lr] = acc[i][j][r];
+      }
+    }
 }
 
-__global__ __launch_bounds__(256) void counts_reduce_kernel(const int32_t* __restrict__ blk,
-                                                            int nb, int N,
-                                                            int32_t* __restrict__ counts) {
-  const int e = threadIdx.x;
-  if (e >= N) return;
+// ---- kernel 2: fp32 selection, one wave per token ----
+__global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ part, int splits,
+                                                           const float* __restrict__ bias, int T, int N,
+                                                           int K, int n_group, int topk_group,
+                                                           int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_gate,
+                                                           float* __restrict__ scores,
+                                                           int32_t* __restrict__ flags) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole waves leave together
+  const int lane = threadIdx.x & 63;
+  float u[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < splits; ++s) {
+    const f32x4 v = *(const f32x4*)(part + ((int64_t)s * T + t) * 256 + lane * 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) u[r] += v[r];
+  }
+  const float margin = select_token<float>(u, bias, N, K, n_group, topk_group, t, true, topk_idx, topk_gate, scores);
+  if (lane == 0) flags[t] = margin < kRefineGap ? 1 : 0;
+}
+
+// ---- kernel 3: fp64 refinement of near-tie tokens, then per-block load histogram ----
+__global__ __launch_bounds__(256) void route_refine_count_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
+    int T, int d, int N, int K, int n_group, int topk_group, const int32_t* __restrict__ flags,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, float* __restrict__ scores,
+    int32_t* __restrict__ blk_counts) {
+  __shared__ double u64[256];
+  __shared__ int list[64];
+  __shared__ int nlist;
+  __shared__ int cnt[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * 64;
+  cnt[tid] = 0;
+  if (wave == 0) {
+    const int t = t0 + lane;
+    const bool f = t < T && flags[t] != 0;
+    const uint64_t m = __ballot(f);
+    if (f) list[__popcll(m & ((1ull << lane) - 1ull))] = t;
+    if (lane == 0) nlist = __popcll(m);
+  }
+  __syncthreads();
+  const int nd = d / 8;  // 16-byte chunks per row
+  for (int i = 0; i < nlist; ++i) {
+    const int64_t t = list[i];
+    const uint16_t* xr = x + t * d;
+    // wave w owns experts w, w+4, ...; lanes split K; products of bf16 are exact in fp32
+    for (int e = wave; e < N; e += 4) {
+      const uint16_t* er = wr + (int64_t)e * d;
+      double a = 0.0;
+      for (int c = lane; c < nd; c += 64) {
+        const u32x4 xv = *(const u32x4*)(xr + c * 8);
+        const u32x4 ev = *(const u32x4*)(er + c * 8);
+        float xf[8], ef[8];
+        unpack_bf16x8(xv, xf);
+        unpack_bf16x8(ev, ef);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a += (double)(xf[q] * ef[q]);
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+      if (lane == 0) u64[e] = a;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      double u[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) u[r] = (lane * 4 + r < N) ? u64[lane * 4 + r] : 0.0;
+      select_token<double>(u, bias, N, K, n_group, topk_group, t, true, topk_idx, topk_gate, scores);
+    }
+    __syncthreads();
+  }
+  if (tid < 64 && t0 + tid < T) {
+    const int64_t t = t0 + tid;
+    for (int k = 0; k < K; ++k) atomicAdd(&cnt[topk_idx[t * K + k]], 1);
+  }
+  __syncthreads();
+  if (tid < N) blk_counts[(int64_t)blockIdx.x * N + tid] = cnt[tid];
+}
+
+// ---- kernel 4: one wave per expert sums the block histograms ----
+__global__ __launch_bounds__(64) void counts_reduce_kernel(const int32_t* __restrict__ blk, int nb, int N,
+                                                           int32_t* __restrict__ counts) {
+  const int e = blockIdx.x, lane = threadIdx.x;
   int s = 0;
-  for (int b = 0; b < nb; ++b) s += blk[(size_t)b * N + e];
-  counts[e] = s;
+  for (int b = lane; b < nb; b += 64) s += blk[(int64_t)b * N + e];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+  if (lane == 0) counts[e] = s;
 }
 
-int route_tile(int T) { return T <= 4096 ? 16 : (T <= 8192 ? 32 : 64); }
+int route_splits(int T, int d) {
+  const int tiles = (T + kTM - 1) / kTM;
+  int s = tiles > 0 ? 512 / tiles : 1;
+  s = s < 1 ? 1 : (s > 8 ? 8 : s);
+  return s > d / 64 ? d / 64 : s;
+}
+
+struct RouteWs {
+  size_t part_off, flags_off, blk_off, total;
+};
+
+RouteWs route_ws(int T, int d, int N) {
+  RouteWs w;
+  const int S = route_splits(T, d);
+  const int nb = T > 0 ? (T + 63) / 64 : 1;
+  w.part_off = 0;
+  w.flags_off = (size_t)S * (size_t)T * 256 * sizeof(float);
+  w.blk_off = w.flags_off + (((size_t)T * sizeof(int32_t) + 255) & ~(size_t)255);
+  w.total = w.blk_off + (size_t)nb * (size_t)N * sizeof(int32_t);
+  return w;
+}
 
 }  // namespace
 }  // namespace moe
 
 extern "C" size_t moe_route_workspace_size(int T, int n_experts) {
   if (T < 0 || n_experts <= 0) return 0;
-  const int tm = moe::route_tile(T);
-  const int nb = T > 0 ? (T + tm - 1) / tm : 1;
-  return (size_t)nb * (size_t)n_experts * sizeof(int32_t);
+  // sized for the largest split count (d only limits it further)
+  return moe::route_ws(T, 1 << 20, n_experts).total;
 }
 
 extern "C" moe_status moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias,
@@ -253,7 +427,7 @@ extern "C" moe_status moe_route(const uint16_t* x, const uint16_t* w_router, con
               MOE_ERR_NULL, "moe_route: a required pointer is NULL");
   MOE_REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_route: T=%d < 0", T);
   MOE_REQUIRE(d >= 64 && d % 64 == 0, MOE_ERR_SHAPE, "moe_route: d=%d must be a positive multiple of 64", d);
-  MOE_REQUIRE(n_experts >= 1 && n_experts <= 256 && n_experts % 4 == 0, MOE_ERR_SHAPE,
+  MOE_REQUIRE(n_experts >= 4 && n_experts <= 256 && n_experts % 4 == 0, MOE_ERR_SHAPE,
               "moe_route: n_experts=%d must be in [4, 256] and a multiple of 4", n_experts);
   MOE_REQUIRE(top_k >= 1 && top_k <= n_experts, MOE_ERR_SHAPE,
               "moe_route: top_k=%d must be in [1, n_experts=%d]", top_k, n_experts);
@@ -262,28 +436,33 @@ extern "C" moe_status moe_route(const uint16_t* x, const uint16_t* w_router, con
   MOE_REQUIRE(topk_group >= 1 && topk_group <= n_group, MOE_ERR_SHAPE,
               "moe_route: topk_group=%d must be in [1, n_group=%d]", topk_group, n_group);
   if (n_group > 1) {
-    MOE_REQUIRE(n_experts / n_group >= 2, MOE_ERR_SHAPE,
-                "moe_route: groups need at least 2 experts (n_experts/n_group=%d)", n_experts / n_group);
-    MOE_REQUIRE(top_k <= topk_group * (n_experts / n_group), MOE_ERR_SHAPE,
-                "moe_route: top_k=%d exceeds the %d experts of the kept groups", top_k,
-                topk_group * (n_experts / n_group));
+    const int gs = n_experts / n_group;
+    MOE_REQUIRE(gs >= 4 && (gs & (gs - 1)) == 0, MOE_ERR_SHAPE,
+                "moe_route: groups must hold a power of two >= 4 experts (n_experts/n_group=%d)", gs);
+    MOE_REQUIRE(top_k <= topk_group * gs, MOE_ERR_SHAPE,
+                "moe_route: top_k=%d exceeds the %d experts of the kept groups", top_k, topk_group * gs);
   }
   MOE_REQUIRE(aligned16(x) && aligned16(w_router) && (scores == nullptr || aligned16(scores)),
               MOE_ERR_ALIGN, "moe_route: x, w_router and scores must be 16-byte aligned");
   const size_t need = moe_route_workspace_size(T, n_experts);
-  MOE_REQUIRE(ws_bytes >= need, MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu bytes", ws_bytes, need);
+  MOE_REQUIRE(ws_bytes >= need && aligned16(ws), MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu bytes (or unaligned)",
+              ws_bytes, need);
 
-  int32_t* blk = static_cast<int32_t*>(ws);
-  const int tm = route_tile(T);
-  const int nb = (T + tm - 1) / tm;
-  if (nb > 0) {
-    if (tm == 16)
-      route_kernel<16><<<nb, 256, 0, stream>>>(x, w_router, bias, T, d, n_experts, top_k, n_group, topk_group, topk_idx, topk_gate, scores, blk);
-    else if (tm == 32)
-      route_kernel<32><<<nb, 256, 0, stream>>>(x, w_router, bias, T, d, n_experts, top_k, n_group, topk_group, topk_idx, topk_gate, scores, blk);
-    else
-      route_kernel<64><<<nb, 256, 0, stream>>>(x, w_router, bias, T, d, n_experts, top_k, n_group, topk_group, topk_idx, topk_gate, scores, blk);
+  const RouteWs L = route_ws(T, d, n_experts);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* part = reinterpret_cast<float*>(base + L.part_off);
+  int32_t* flags = reinterpret_cast<int32_t*>(base + L.flags_off);
+  int32_t* blk = reinterpret_cast<int32_t*>(base + L.blk_off);
+  const int S = route_splits(T, d);
+  const int tiles = (T + kTM - 1) / kTM;
+  const int nb = (T + 63) / 64;
+  if (T > 0) {
+    route_logits_kernel<<<tiles * S, 256, 0, stream>>>(x, w_router, T, d, n_experts, S, part);
+    route_select_kernel<<<(T + 3) / 4, 256, 0, stream>>>(part, S, bias, T, n_experts, top_k, n_group, topk_group,
+                                                         topk_idx, topk_gate, scores, flags);
+    route_refine_count_kernel<<<nb, 256, 0, stream>>>(x, w_router, bias, T, d, n_experts, top_k, n_group, topk_group,
+                                                      flags, topk_idx, topk_gate, scores, blk);
   }
-  counts_reduce_kernel<<<1, 256, 0, stream>>>(blk, nb, n_experts, expert_counts);
+  counts_reduce_kernel<<<n_experts, 64, 0, stream>>>(blk, nb, n_experts, expert_counts);
   return check_launch("moe_route");
 }

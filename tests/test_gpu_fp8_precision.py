@@ -1,0 +1,82 @@
+"""Accumulation precision of the E4M3 path on gfx950 -- the counterpart of the pages'
+finding that H800 FP8 GEMMs accumulate with about 14 bits ("DeepSeek-V3 Technical Report"
+(wiki summary), "FP8 混合精度訓練" -> "高精度累積"), measured through moe_grouped_gemm.
+
+What the matrix cores do (pinned here): within a 128-element K slice, products are summed in
+groups of 8 after alignment to the group's largest product, keeping about 13 bits below it;
+subnormal E4M3 inputs are multiplied exactly; across 128-element slices the library
+promotes every partial sum into an fp32 accumulator (scaled by s_A * s_W), so long K adds
+no further loss: a K = 7168 sum of exactly representable products is exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from tests.gpu_common import say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _gemm_f32(Aq, Wq, scale_a=None, scale_w=None):
+    import sparse_moe_layer_sigmoid_amd as M
+    rows, K = Aq.shape
+    N = Wq.shape[0]
+    As = torch.ones((rows, K // 128), dtype=torch.float32) if scale_a is None else scale_a
+    Ws = torch.ones((1, N // 128, K // 128), dtype=torch.float32) if scale_w is None else scale_w
+    out = torch.empty((rows, N), dtype=torch.float32, device=DEV)
+    offs = torch.tensor([0, rows], dtype=torch.int32, device=DEV)
+    M.moe_grouped_gemm(Aq.to(DEV), Wq[None].to(DEV), offs, 0, 1, rows, out, a_scale=As.to(DEV), w_scale=Ws.to(DEV))
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _codes(vals):
+    return torch.from_numpy(O.e4m3_encode(np.asarray(vals, np.float64)))
+
+
+def test_group_alignment_and_subnormals():
+    K, N = 128, 128
+    rows = []
+    rows.append([448.0] + [2.0 ** -6] * 127)   # small terms sharing a group with 448
+    rows.append([448.0] + [0.25] * 127)        # 10.8 bits below: kept
+    rows.append([2.0 ** -9] * 128)             # subnormal inputs
+    rows.append([7 * 2.0 ** -9] * 128)
+    rows.append([256.0, -256.0] + [0.5] * 126)
+    rows += [[0.0] * 128] * 11
+    A = _codes(rows)
+    W = _codes(np.ones((N, K)))
+    got = _gemm_f32(A, W)[:, 0]
+    exact = O.e4m3_decode(A.numpy()).sum(axis=1)
+    say(f"  448 + 127*2^-6: got {got[0]!r}, exact {exact[0]!r}")
+    assert got[1] == exact[1] and got[2] == exact[2] and got[3] == exact[3] and got[4] == exact[4]
+    # the group holding 448 drops its 7 terms of 2^-6; the other 15 groups are exact
+    assert got[0] in (exact[0], 448.0 + 120 * 2.0 ** -6)
+
+
+def test_random_dot_precision_bits():
+    rng = np.random.default_rng(0)
+    K, N, rows = 1024, 256, 64
+    A = torch.from_numpy((rng.integers(0, 0x7F, (rows, K)) | (rng.integers(0, 2, (rows, K)) << 7)).astype(np.uint8))
+    W = torch.from_numpy((rng.integers(0, 0x7F, (N, K)) | (rng.integers(0, 2, (N, K)) << 7)).astype(np.uint8))
+    got = _gemm_f32(A, W)
+    a, w = O.e4m3_decode(A.numpy()), O.e4m3_decode(W.numpy())
+    exact = a @ w.T
+    rel = np.max(np.abs(got - exact) / (np.abs(a) @ np.abs(w).T))
+    say(f"  random E4M3 dot products: max |err| / sum|a w| = {rel:.3e} ({-np.log2(rel):.1f} bits)")
+    assert rel <= 2.0 ** -10
+
+
+def test_long_k_promotion_is_exact():
+    """K = 7168 (56 slices of 128): small-integer codes with power-of-two scales make every
+    partial sum exact, so the promoted fp32 accumulation must be exact too."""
+    rng = np.random.default_rng(1)
+    K, N, rows = 7168, 128, 32
+    ai = rng.integers(-15, 16, (rows, K))
+    wi = rng.integers(-15, 16, (N, K))
+    sa = np.exp2(rng.integers(-4, 2, (rows, K // 128))).astype(np.float32)
+    sw = np.exp2(rng.integers(-6, -1, (1, N // 128, K // 128))).astype(np.float32)
+    got = _gemm_f32(_codes(ai), _codes(wi), torch.from_numpy(sa), torch.from_numpy(sw))
+    a = ai * np.repeat(sa, 128, axis=1)
+    w = wi * np.repeat(np.repeat(sw[0], 128, axis=0), 128, axis=1)
+    assert np.array_equal(got, a @ w.T)

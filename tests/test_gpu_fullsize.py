@@ -115,7 +115,7 @@ def test_v3_fp8_T16384(v3):
     x_cpu, bias, r, tie, out32, buf = _route_and_layer(v3, cfg, True)
     xq, xs = O.quant_1x128(x_cpu.float().numpy()[:512])
     assert np.array_equal(buf["xq"][:512].cpu().numpy(), xq) and np.array_equal(buf["xs"][:512].cpu().numpy(), xs)
-    _sampled_output_check(cfg, x_cpu, r, tie, out32, "fp8", 3, FP8_TOL)
+    _sampled_output_check(cfg, x_cpu, r, tie, out32, "fp8", 12, FP8_TOL)
 
 
 def test_v3_decode_bias_loop(v3):

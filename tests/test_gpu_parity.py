@@ -240,6 +240,13 @@ def test_gemm_fp8_exact():
         assert np.array_equal(got[offs[g]:offs[g + 1]], ref), g
 
 
+# The gfx950 E4M3 matrix cores sum each group of 8 products after aligning them to the
+# group's largest one, keeping about 13 bits below it (measured in test_gpu_fp8_precision):
+# a dot product's error is bounded by a small multiple of 2^-12 * sum |a_k w_k|.  The bound
+# used below is 2^-10 * sum |a_k w_k| (4x margin).
+FP8_DOT_REL = 2.0 ** -10
+
+
 @pytest.mark.parametrize("swiglu,out_kind", [(False, "f32"), (True, "bf16"), (True, "fp8")])
 def test_gemm_fp8_random(swiglu, out_kind):
     G, K = 5, 512
@@ -251,37 +258,57 @@ def test_gemm_fp8_random(swiglu, out_kind):
     rows = int(offs[-1])
     T = 300
     a_rows = np.random.default_rng(3).integers(0, T, rows).astype(np.int32)
-    Aq = I.gen_e4m3_codes(51, (T, K))
-    As = I.gen_scales(52, (T, K // 128))
-    Wq = I.gen_e4m3_codes(53, (G, N, K))
-    Ws = I.gen_scales(54, (G, N // 128, K // 128))
+    # realistic operands: N(0,1) activations and N(0, 0.006) weights, each quantised by the
+    # GPU kernels and (independently, bit-exactly) by the oracle
+    A = I.gen_normal(51, (T, K), 1.0)
+    W = I.gen_normal(53, (G, N, K), 0.006)
+    Aq, As = M().fp8_quant_1x128(A.to(DEV))
+    Wq, Ws = M().fp8_quant_128x128(W.to(DEV))
+    Aqo, Aso = O.quant_1x128(A.float().numpy())
+    assert np.array_equal(Aq.cpu().numpy(), Aqo) and np.array_equal(As.cpu().numpy(), Aso)
     oc = N // 2 if swiglu else N
     dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[out_kind]
     out = torch.empty((rows, oc), dtype=dt, device=DEV)
     osc = torch.empty((rows, oc // 128), dtype=torch.float32, device=DEV) if out_kind == "fp8" else None
-    M().moe_grouped_gemm(Aq.to(DEV), Wq.to(DEV), torch.from_numpy(offs).to(DEV), 0, G, rows, out,
-                         a_scale=As.to(DEV), a_rows=torch.from_numpy(a_rows).to(DEV), w_scale=Ws.to(DEV),
-                         swiglu=swiglu, out_scale=osc)
-    A = O.dequant_1x128(Aq.numpy(), As.numpy())
+    M().moe_grouped_gemm(Aq, Wq, torch.from_numpy(offs).to(DEV), 0, G, rows, out, a_scale=As,
+                         a_rows=torch.from_numpy(a_rows).to(DEV), w_scale=Ws, swiglu=swiglu, out_scale=osc)
+    Ad = O.dequant_1x128(Aqo, Aso)
     ref = np.zeros((rows, oc))
+    bound = np.zeros((rows, oc))
     for g in range(G):
         if sizes[g] == 0:
             continue
-        Wd = O.dequant_128x128(Wq[g].numpy(), Ws[g].numpy())
-        xr = A[a_rows[offs[g]:offs[g + 1]]]
-        ref[offs[g]:offs[g + 1]] = O.swiglu_hidden(xr, Wd) if swiglu else xr @ Wd.T
+        wq, ws = O.quant_128x128(W[g].float().numpy())
+        Wd = O.dequant_128x128(wq, ws)
+        xr = Ad[a_rows[offs[g]:offs[g + 1]]]
+        if swiglu:
+            I_ = N // 2
+            a, c = xr @ Wd[:I_].T, xr @ Wd[I_:].T
+            da = FP8_DOT_REL * (np.abs(xr) @ np.abs(Wd[:I_]).T)
+            dc = FP8_DOT_REL * (np.abs(xr) @ np.abs(Wd[I_:]).T)
+            ref[offs[g]:offs[g + 1]] = O.silu(a) * c
+            bound[offs[g]:offs[g + 1]] = 1.1 * da * np.abs(c) + np.abs(O.silu(a)) * dc + da * dc
+        else:
+            ref[offs[g]:offs[g + 1]] = xr @ Wd.T
+            bound[offs[g]:offs[g + 1]] = FP8_DOT_REL * (np.abs(xr) @ np.abs(Wd).T)
+    rms = np.sqrt(np.mean(ref ** 2))
     if out_kind == "fp8":
         got = O.dequant_1x128(out.cpu().numpy(), osc.cpu().numpy())
         qo, so = O.quant_1x128(O.fp32_round(ref))
-        np.testing.assert_allclose(osc.cpu().numpy(), so, rtol=1e-5)
+        np.testing.assert_allclose(osc.cpu().numpy(), so, rtol=1e-3)
         same = np.mean(out.cpu().numpy() == qo)
         say(f"  fp8 h codes identical to the oracle's: {same:.5f}")
-        assert same > 0.99
-        assert rel_err(got, ref) < FP8_TOL
+        assert same > 0.98
+        # within the dot-product bound plus one E4M3 step of the stored value
+        step = 2 * O.e4m3_half_ulp(ref / np.repeat(so, 128, axis=1)) * np.repeat(so, 128, axis=1)
+        assert np.all(np.abs(got - ref) <= bound + step * 1.001 + 1e-6 * rms)
     elif out_kind == "bf16":
-        assert rel_err(np64(out), ref) < 1e-2
+        got = np64(out)
+        assert np.all(np.abs(got - ref) <= bound + np.abs(ref) * 2.0 ** -8 + 1e-6 * rms)
     else:
-        assert rel_err(np64(out), ref) < 1e-5
+        got = np64(out)
+        assert np.all(np.abs(got - ref) <= bound + 1e-6 * rms)
+    say(f"  max |err| / bound = {np.max(np.abs(got - ref) / (bound + 1e-30)):.3f}, rel err {rel_err(got, ref):.2e}")
 
 
 # ------------------------------------------------------------------ combine and bias update
@@ -355,8 +382,13 @@ def test_layer_bf16(cfg):
     assert err <= BF16_TOL
 
 
+# Reduced copies of the fp8 workload keep its structure per token: at d = 7168 a 0.1% outlier
+# rate puts about 7 outliers (x100) in every token, so a reduced d keeps 7.2 outliers per token.
 @pytest.mark.parametrize("cfg", [
-    I.small(I.V3_FP8, name="fp8_small", T=300, d=512, n_experts=32, top_k=4, inter=256, w_std=0.04, router_std=0.04),
+    I.small(I.V3_FP8, name="fp8_small", T=300, d=512, n_experts=32, top_k=4, inter=256, w_std=0.04,
+            router_std=0.04, outlier_frac=7.2 / 512),
+    I.small(I.V3_FP8, name="fp8_small_no_outliers", T=300, d=512, n_experts=32, top_k=4, inter=256, w_std=0.04,
+            router_std=0.04, outlier_frac=0.0),
     I.small(I.V3_FP8, name="fp8_small_2", T=129, d=256, n_experts=16, top_k=8, inter=128, w_std=0.05, router_std=0.05),
 ], ids=lambda c: c.name)
 def test_layer_fp8(cfg):
