@@ -187,10 +187,11 @@ typedef struct moe_gemm_desc {
   int64_t ldo;
   float* out_scale;             /* FP8 output: device f32 [rows, out_cols/128]; else NULL */
 } moe_gemm_desc;
-/* Limits: K a positive multiple of 64 (bf16) or 128 (FP8); without an epilogue N a positive
- * multiple of 128; with SWIGLU N/2 a positive multiple of 64 (bf16) or 128 (FP8); FP8 input
- * needs a_scale and w_scale; an FP8 output needs FP8 input, SWIGLU and out_scale; SWIGLU
- * output is bf16 or FP8; 0 <= m_total < 2^31; lda/ldo keep rows 16-byte aligned. */
+/* Limits: K a positive multiple of 64 (bf16) or 128 (FP8); N a positive multiple of 128 (bf16)
+ * or 256 (FP8) -- with SWIGLU that is N/2 a multiple of 64 or 128; FP8 input needs a_scale and
+ * w_scale (4-byte aligned); an FP8 output needs FP8 input, SWIGLU and out_scale; SWIGLU
+ * output is bf16 or FP8; 1 <= n_groups <= 1024; 0 <= m_total < 2^31; one W[g] < 2 GiB;
+ * lda/ldo keep rows 16-byte aligned. */
 moe_status moe_grouped_gemm(const moe_gemm_desc* desc, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------

@@ -10,20 +10,28 @@
 //    is re-quantised per 1x128 tile in the epilogue ("オンライン量子化").
 //
 // Design (CDNA4 first):
-//  * A workgroup owns a BM x BN output tile of one expert.  Tiles are found on the device:
-//    each workgroup scans the group offsets (one wave, shuffles) to map its linear index to
-//    (expert, row block); the launch is sized by an upper bound, surplus workgroups exit.
-//  * Each K step moves 128 bytes per row (64 bf16 or 128 E4M3) of A and W through LDS with
-//    16-byte loads, double buffered (prefetch into registers during the MFMAs, one barrier
-//    per step).  LDS rows are 128 B with the 16-byte chunks XOR-swizzled by (row & 7) so the
-//    MFMA operand reads (16 rows x one chunk) hit distinct banks.
-//  * A rows are gathered through the permutation (token -> sorted row) while loading; rows
-//    past the end of an expert's segment re-read a valid row and are not stored.
+//  * Persistent workgroups, one per CU.  Each builds the per-expert tile table once (from the
+//    device-side group offsets: no host synchronisation), then walks its share of the tiles.
+//    Tiles are ordered (expert, column block, row block); each of the 8 XCDs gets a
+//    contiguous range of that order and its workgroups stride through it, so the
+//    activations of an expert and each weight block are fetched into that XCD's L2 once and
+//    reused there (workgroup b runs on XCD b mod 8).
+//  * Operands move HBM -> LDS with direct-to-LDS DMA (global_load_lds_dwordx4): each wave
+//    instruction fills 8 rows x 128 bytes, the 16-byte chunks XOR-swizzled by (row & 7) so
+//    the MFMA operand reads hit distinct banks.  A ring of STAGES K steps (128 bytes of K per
+//    row: 64 bf16 or 128 E4M3) runs continuously across tile boundaries, with explicit
+//    vmcnt waits and one barrier per step; the gather indices of the next tile are fetched a
+//    whole tile ahead so the ring never drains.
+//  * A rows are gathered through the permutation (token of each sorted row); rows past an
+//    expert's segment re-read its last row and are not stored.
 //  * SwiGLU: the B tile holds BN/2 gate rows then the matching BN/2 up rows, and each wave
 //    owns matching gate and up columns, so h is formed in registers.
-//  * Outputs are staged through LDS and written as full 16-byte row chunks (bf16 and fp8);
-//    fp32 outputs are written straight from the accumulators.
+//  * The epilogue writes from registers (a tile's waves cover whole 128-byte lines, which
+//    merge in L2); the fp8 output's per-row amax over its 128 columns is reduced across
+//    waves in a small LDS array.
 #include <math.h>
+
+#include <type_traits>
 
 #include "abi_common.h"
 #include "device_common.h"
@@ -32,159 +40,226 @@ namespace moe {
 namespace {
 
 enum { OUT_BF16 = 0, OUT_F32 = 1, OUT_FP8 = 2 };
+constexpr int kMaxGroups = 1024;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// s_waitcnt through the builtin (so the compiler's own wait tracking sees it): gfx9
+// encoding, vmcnt in bits [3:0] and [15:14], expcnt [6:4] = 7 and lgkmcnt [11:8] = 15 (no wait).
+#define MOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+#define MOE_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14))
+// Workgroup barrier without the release fence of __syncthreads (which would wait for every
+// outstanding DMA); LDS visibility of finished DMA is ensured by the vmcnt waits.
+#define MOE_BARRIER()                \
+  do {                               \
+    MOE_WAIT_LGKM0();                \
+    __builtin_amdgcn_s_barrier();    \
+    asm volatile("" ::: "memory");   \
+  } while (0)
 
 struct GemmArgs {
   const uint8_t* a;
   const float* a_scale;
   const int32_t* a_rows;
-  int64_t lda_b;      // bytes per A row
+  int64_t lda_b;        // bytes per A row
   const uint8_t* w;
   const float* w_scale;
   const int32_t* offs;  // group_offsets + first_group (n_groups + 1 entries)
   int first_group;
   int n_groups;
-  int N;              // rows of each W[g]
-  int ksteps;         // number of 128-byte K steps
-  int ksb;            // K / 128: scale columns (FP8)
-  int64_t w_row_b;    // bytes per W row
-  int n_tiles;        // output tiles along N
+  int N;                // rows of each W[g]
+  int ksteps;           // number of 128-byte K steps
+  int ksb;              // K / 128: scale columns (FP8)
+  int64_t w_row_b;      // bytes per W row
+  int n_tiles;          // output tiles along N
   uint8_t* out;
-  int64_t ldo_b;      // bytes per output row
+  int64_t ldo_b;        // bytes per output row
   float* out_scale;
   int out_scale_ld;
 };
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
-template <int BM, int BN, int WGM, int WGN, bool FP8, bool SWIGLU, int OUT>
+struct TileInfo {
+  int g;      // group index relative to first_group
+  int nt;     // column block
+  int row0;   // first global sorted row
+  int nrows;  // valid rows (1..BM)
+};
+
+// Decode logical tile L (order: group, column block, row block) from the LDS prefix table.
+template <int BM>
+__device__ __forceinline__ TileInfo decode_tile(int L, const int* tstart, int G, const int32_t* offs) {
+  int lo = 0, hi = G;  // largest g with tstart[g] <= L (then tstart[g+1] > L: never empty)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tstart[mid] <= L) lo = mid;
+    else hi = mid;
+  }
+  const int g = lo;
+  const int local = L - tstart[g];
+  const int m0 = offs[g], m1 = offs[g + 1];
+  const int mt_g = (m1 - m0 + BM - 1) / BM;
+  TileInfo t;
+  t.g = g;
+  t.nt = local / mt_g;
+  const int mt = local - t.nt * mt_g;
+  t.row0 = m0 + mt * BM;
+  t.nrows = min(BM, m1 - t.row0);
+  return t;
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool FP8, bool SWIGLU, int OUT>
 __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p) {
-  constexpr int NT = WGM * WGN * 64;
+  constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM;  // rows per wave
   constexpr int WN = BN / WGN;  // W rows (output columns; gate+up for SwiGLU) per wave
   constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int A_CPT = BM * 8 / NT, B_CPT = BN * 8 / NT;
   constexpr int A_BYTES = BM * 128, STAGE = (BM + BN) * 128;
-  constexpr int OC = SWIGLU ? BN / 2 : BN;  // output columns of a tile
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile / thread mismatch");
+  constexpr int A_PW = BM / 8 / NW;               // A DMA instructions per wave per stage
+  constexpr int B_PW = BN / 8 / NW;               // B DMA instructions per wave per stage
+  constexpr int SC_W = FP8 ? (BM + 63) / 64 : 0;  // 64-row blocks of A scales per stage
+  constexpr int OC = SWIGLU ? BN / 2 : BN;
+  constexpr int L_STAGE = A_PW + B_PW + (FP8 ? 1 : 0);  // DMA instructions per wave per stage
+  static_assert(A_PW * 8 * NW == BM && B_PW * 8 * NW == BN, "DMA instructions must split evenly over waves");
+  static_assert(SC_W <= NW, "one wave per 64 rows of A scales");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(!SWIGLU || TN % 2 == 0, "SwiGLU waves need matching gate and up tiles");
   static_assert(OUT != OUT_FP8 || (FP8 && SWIGLU && OC == 128), "fp8 output = one 1x128 tile per row");
   static_assert(!FP8 || (SWIGLU ? WN / 2 <= 128 : WN <= 128), "a wave must sit inside one 128-row scale block");
+  static_assert(STAGES == 3, "the ring is written for three slots");
+  static_assert(L_STAGE * (STAGES - 2) <= 63, "vmcnt budget");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-  __shared__ float s_as[FP8 ? 2 * BM : 1];
+  // one LDS array per ring slot: distinct objects, so the compiler can tell the DMA target of
+  // a step apart from the slot being read and adds no waits of its own
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot2[STAGE];
+  // A scales: every wave issues one 64-float DMA per stage (waves past the tile's rows fill
+  // a spare region), so all waves have the same DMA count and no branch around it
+  __shared__ __attribute__((aligned(16))) float sas0[FP8 ? 64 * NW : 1];
+  __shared__ __attribute__((aligned(16))) float sas1[FP8 ? 64 * NW : 1];
+  __shared__ __attribute__((aligned(16))) float sas2[FP8 ? 64 * NW : 1];
   __shared__ float s_red[OUT == OUT_FP8 ? WGN * BM : 1];
-  __shared__ int s_info[3];
+  __shared__ int s_tstart[kMaxGroups + 1];
+  __shared__ int s_offs[kMaxGroups + 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave - wm * WGN;
-  const int mt = blockIdx.x / p.n_tiles;
-  const int nt = blockIdx.x - mt * p.n_tiles;
+  const int G = p.n_groups;
 
-  // ---- map this workgroup's row block to (group, first row, valid rows) ----
+  // ---- tile table: group offsets and exclusive prefix of (row blocks x column blocks) ----
+  for (int g = tid; g <= G; g += NW * 64) s_offs[g] = p.offs[g];
   if (wave == 0) {
-    const int G = p.n_groups;
     const int per = (G + 63) >> 6;
     const int g0 = min(G, lane * per), g1 = min(G, g0 + per);
     int local = 0;
-    for (int g = g0; g < g1; ++g) local += (p.offs[g + 1] - p.offs[g] + BM - 1) / BM;
+    for (int g = g0; g < g1; ++g) local += (p.offs[g + 1] - p.offs[g] + BM - 1) / BM * p.n_tiles;
     int incl = local;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int v = __shfl_up(incl, o, kWave);
       if (lane >= o) incl += v;
     }
-    const int total = __shfl(incl, 63, kWave);
-    if (lane == 0 && mt >= total) s_info[0] = -1;
     int run = incl - local;
-    if (mt >= run && mt < incl) {
-      for (int g = g0; g < g1; ++g) {
-        const int c = (p.offs[g + 1] - p.offs[g] + BM - 1) / BM;
-        if (mt < run + c) {
-          const int r0 = p.offs[g] + (mt - run) * BM;
-          s_info[0] = g;
-          s_info[1] = r0;
-          s_info[2] = min(BM, p.offs[g + 1] - r0);
-          break;
-        }
-        run += c;
-      }
+    for (int g = g0; g < g1; ++g) {
+      s_tstart[g] = run;
+      run += (p.offs[g + 1] - p.offs[g] + BM - 1) / BM * p.n_tiles;
     }
+    if (lane == 63) s_tstart[G] = incl;
   }
   __syncthreads();
-  const int gl = s_info[0];
-  if (gl < 0) return;
-  const int row0 = s_info[1], nrows = s_info[2];
-  const int g = p.first_group + gl;
-  const int base_row = p.offs[0];
+  const int total = s_tstart[G];
+  const int n_xcd = gridDim.x >= 8 ? 8 : 1;
+  const int xcd = blockIdx.x % n_xcd, slot = blockIdx.x / n_xcd, per_xcd = gridDim.x / n_xcd;
+  const int t_begin = (int)((int64_t)total * xcd / n_xcd), t_end = (int)((int64_t)total * (xcd + 1) / n_xcd);
+  const int n_my = t_end - t_begin > slot ? (t_end - t_begin - slot + per_xcd - 1) / per_xcd : 0;
+  const int ksteps = p.ksteps;
+  const int total_steps = n_my * ksteps;
+  if (total_steps == 0) return;
 
-  // ---- per-thread global sources and LDS destinations ----
-  const int cch = tid & 7;
-  const uint8_t* a_src[A_CPT];
-  int a_lds[A_CPT];
+  // ---- loader state ----
+  const int cch = lane & 7;
+  const int lrow = lane >> 3;  // row within an 8-row DMA instruction
+  const uint8_t* a_ptr[A_PW];
+  int a_nxt[A_PW];
+  int b_off[B_PW];
+  const float* s_ptr = p.a_scale;
+  int s_nxt = 0;
+  int lq = -1;  // index (in this workgroup's list) of the tile being loaded
+  const uint8_t* wbase = p.w;
+
+  auto tile_of = [&](int q) { return decode_tile<BM>(t_begin + slot + q * per_xcd, s_tstart, G, s_offs); };
+  // gather sources of a tile's rows (global loads whose values are used one tile later)
+  auto fetch_rows = [&](const TileInfo& t, int* dst, int& sdst) {
 #pragma unroll
-  for (int i = 0; i < A_CPT; ++i) {
-    const int rr = (tid >> 3) + i * (NT / 8);
-    const int r = row0 + min(rr, nrows - 1);
-    const int64_t src = p.a_rows ? (int64_t)p.a_rows[r] : (int64_t)r;
-    a_src[i] = p.a + src * p.lda_b + cch * 16;
-    a_lds[i] = rr * 128 + ((cch ^ (rr & 7)) << 4);
-  }
-  const uint8_t* wg = p.w + (int64_t)g * p.N * p.w_row_b;
-  const uint8_t* b_src[B_CPT];
-  int b_lds[B_CPT];
-#pragma unroll
-  for (int i = 0; i < B_CPT; ++i) {
-    const int rr = (tid >> 3) + i * (NT / 8);
-    int n;
-    if (SWIGLU) n = (rr < BN / 2) ? nt * (BN / 2) + rr : p.N / 2 + nt * (BN / 2) + (rr - BN / 2);
-    else n = nt * BN + rr;
-    b_src[i] = wg + (int64_t)n * p.w_row_b + cch * 16;
-    b_lds[i] = A_BYTES + rr * 128 + ((cch ^ (rr & 7)) << 4);
-  }
-  const float* sa_src = nullptr;
-  const float* sw_a = nullptr;  // scale row of this wave's (gate) columns
-  const float* sw_b = nullptr;  // scale row of this wave's up columns (SwiGLU)
-  if (FP8) {
-    if (tid < BM) {
-      const int r = row0 + min(tid, nrows - 1);
-      const int64_t src = p.a_rows ? (int64_t)p.a_rows[r] : (int64_t)r;
-      sa_src = p.a_scale + src * p.ksb;
+    for (int i = 0; i < A_PW; ++i) {
+      const int rr = 8 * (wave * A_PW + i) + lrow;
+      const int r = t.row0 + min(rr, t.nrows - 1);
+      dst[i] = p.a_rows ? p.a_rows[r] : r;
     }
-    const float* swg = p.w_scale + (int64_t)g * (p.N / 128) * p.ksb;
-    if (SWIGLU) {
-      sw_a = swg + (int64_t)((nt * (BN / 2) + wn * (WN / 2)) / 128) * p.ksb;
-      sw_b = swg + (int64_t)((p.N / 2 + nt * (BN / 2) + wn * (WN / 2)) / 128) * p.ksb;
-    } else {
-      sw_a = swg + (int64_t)((nt * BN + wn * WN) / 128) * p.ksb;
-      sw_b = sw_a;
+    if (FP8) {
+      const int r = t.row0 + min(64 * wave + lane, t.nrows - 1);
+      sdst = p.a_rows ? p.a_rows[r] : r;
     }
+  };
+  auto set_rows = [&](const int* src, int ssrc) {
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) {
+      const int rr = 8 * (wave * A_PW + i) + lrow;
+      a_ptr[i] = p.a + (int64_t)src[i] * p.lda_b + ((cch ^ (rr & 7)) << 4);
+    }
+    if (FP8) s_ptr = p.a_scale + (int64_t)ssrc * p.ksb;
+  };
+  auto set_b = [&](const TileInfo& t) {
+#pragma unroll
+    for (int i = 0; i < B_PW; ++i) {
+      const int rr = 8 * (wave * B_PW + i) + lrow;
+      int n;
+      if (SWIGLU) n = (rr < BN / 2) ? t.nt * (BN / 2) + rr : p.N / 2 + t.nt * (BN / 2) + (rr - BN / 2);
+      else n = t.nt * BN + rr;
+      b_off[i] = (int)(n * p.w_row_b) + ((cch ^ (rr & 7)) << 4);
+    }
+    wbase = p.w + (int64_t)(p.first_group + t.g) * p.N * p.w_row_b;
+  };
+  // issue the DMA of global step js (clamped to the last step: every step issues one batch,
+  // so the number of batches in flight is constant) into ring slot SL
+  auto issue = [&](auto slot_c, int js) {
+    constexpr int SL = decltype(slot_c)::value;
+    uint8_t* st = SL == 0 ? slot0 : (SL == 1 ? slot1 : slot2);
+    float* sa = SL == 0 ? sas0 : (SL == 1 ? sas1 : sas2);
+    js = min(js, total_steps - 1);
+    const int q = js / ksteps, kt = js - q * ksteps;
+    if (q != lq) {  // entering a new tile: its rows were fetched one tile earlier
+      set_b(tile_of(q));
+      if (q > 0) set_rows(a_nxt, s_nxt);
+      if (q + 1 < n_my) fetch_rows(tile_of(q + 1), a_nxt, s_nxt);
+      lq = q;
+    }
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void*)(a_ptr[i] + kt * 128), (lds_void*)(st + (wave * A_PW + i) * 1024), 16, 0, 0);
+    const uint8_t* bb = wbase + kt * 128;
+#pragma unroll
+    for (int i = 0; i < B_PW; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void*)(bb + (uint32_t)b_off[i]),
+                                       (lds_void*)(st + A_BYTES + (wave * B_PW + i) * 1024), 16, 0, 0);
+    if (FP8) __builtin_amdgcn_global_load_lds((glb_void*)(s_ptr + kt), (lds_void*)(sa + wave * 64), 4, 0, 0);
+  };
+
+  // rows of the first tile (the ring is empty, so waiting for them costs nothing)
+  {
+    int src0[A_PW];
+    int ssrc0 = 0;
+    fetch_rows(tile_of(0), src0, ssrc0);
+    set_rows(src0, ssrc0);
   }
+  issue(std::integral_constant<int, 0>(), 0);
+  issue(std::integral_constant<int, 1>(), 1);
 
-  f32x4 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 ra[A_CPT], rb[B_CPT];
-  float rsa = 0.f;
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_CPT; ++i) ra[i] = *(const u32x4*)(a_src[i] + (int64_t)kt * 128);
-#pragma unroll
-    for (int i = 0; i < B_CPT; ++i) rb[i] = *(const u32x4*)(b_src[i] + (int64_t)kt * 128);
-    if (FP8 && tid < BM) rsa = sa_src[kt];
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* s = smem + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < A_CPT; ++i) *(u32x4*)(s + a_lds[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_CPT; ++i) *(u32x4*)(s + b_lds[i]) = rb[i];
-    if (FP8 && tid < BM) s_as[buf * BM + tid] = rsa;
-  };
-
+  // ---- compute state ----
   const int lr = lane & 15, lg = lane >> 4;
   int a_row[TM], b_row[TN];
 #pragma unroll
@@ -194,15 +269,40 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     if (SWIGLU) b_row[j] = (j < TN / 2) ? wn * (WN / 2) + j * 16 + lr : BN / 2 + wn * (WN / 2) + (j - TN / 2) * 16 + lr;
     else b_row[j] = wn * WN + j * 16 + lr;
   }
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  TileInfo ct = tile_of(0);
+  const float* sw_a = p.w_scale;
+  const float* sw_b = p.w_scale;
+  auto set_scales = [&]() {
+    if (FP8) {
+      const float* swg = p.w_scale + (int64_t)(p.first_group + ct.g) * (p.N / 128) * p.ksb;
+      if (SWIGLU) {
+        sw_a = swg + (int64_t)((ct.nt * (BN / 2) + wn * (WN / 2)) / 128) * p.ksb;
+        sw_b = swg + (int64_t)((p.N / 2 + ct.nt * (BN / 2) + wn * (WN / 2)) / 128) * p.ksb;
+      } else {
+        sw_a = swg + (int64_t)((ct.nt * BN + wn * WN) / 128) * p.ksb;
+        sw_b = sw_a;
+      }
+    }
+  };
+  set_scales();
+  const int base_row = s_offs[0];
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < p.ksteps; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < p.ksteps;
-    if (more) gload(kt + 1);
-    const uint8_t* As = smem + cur * STAGE;
+  // one step: wait for its DMA (one later batch stays in flight), issue the DMA two steps
+  // ahead into the slot read last step, multiply, and finish the tile on its last step
+  auto step = [&](auto slot_c, int j) {
+    constexpr int SL = decltype(slot_c)::value;
+    const uint8_t* As = SL == 0 ? slot0 : (SL == 1 ? slot1 : slot2);
+    const float* sas = SL == 0 ? sas0 : (SL == 1 ? sas1 : sas2);
+    const int kt = j % ksteps;
+    MOE_WAIT_VM(L_STAGE * (STAGES - 2));
+    MOE_BARRIER();
+    issue(std::integral_constant<int, (SL + STAGES - 1) % STAGES>(), j + STAGES - 1);
+
     const uint8_t* Bs = As + A_BYTES;
     if (!FP8) {
 #pragma unroll
@@ -212,11 +312,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
 #pragma unroll
         for (int i = 0; i < TM; ++i) af[i] = *(const bf16x8_t*)(As + a_row[i] * 128 + ((ch ^ (a_row[i] & 7)) << 4));
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bfr[j] = *(const bf16x8_t*)(Bs + b_row[j] * 128 + ((ch ^ (b_row[j] & 7)) << 4));
+        for (int jj = 0; jj < TN; ++jj) bfr[jj] = *(const bf16x8_t*)(Bs + b_row[jj] * 128 + ((ch ^ (b_row[jj] & 7)) << 4));
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j) acc[i][j] = mfma_bf16(af[i], bfr[j], acc[i][j]);
+          for (int jj = 0; jj < TN; ++jj) acc[i][jj] = mfma_bf16(af[i], bfr[jj], acc[i][jj]);
       }
     } else {
       const int ch = lg * 2;
@@ -229,114 +329,142 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
         af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const uint8_t* rowp = Bs + b_row[j] * 128;
-        const u32x4 lo = *(const u32x4*)(rowp + ((ch ^ (b_row[j] & 7)) << 4));
-        const u32x4 hi = *(const u32x4*)(rowp + (((ch + 1) ^ (b_row[j] & 7)) << 4));
-        bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      for (int jj = 0; jj < TN; ++jj) {
+        const uint8_t* rowp = Bs + b_row[jj] * 128;
+        const u32x4 lo = *(const u32x4*)(rowp + ((ch ^ (b_row[jj] & 7)) << 4));
+        const u32x4 hi = *(const u32x4*)(rowp + (((ch + 1) ^ (b_row[jj] & 7)) << 4));
+        bfr[jj] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
-      const float swa = sw_a[kt], swb = sw_b[kt];
-      const float* sas = s_as + cur * BM;
+      // weight-block scales: wave-uniform addresses, read through the scalar cache
+      typedef __attribute__((address_space(4))) const float cfloat;
+      const float swa = *(cfloat*)(uintptr_t)(sw_a + kt);
+      const float swb = *(cfloat*)(uintptr_t)(sw_b + kt);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         float sa[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sa[r] = sas[wm * WM + i * 16 + lg * 4 + r];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const float sw = (SWIGLU && j >= TN / 2) ? swb : swa;
-          const f32x4 part = mfma_fp8(af[i], bfr[j], f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int jj = 0; jj < TN; ++jj) {
+          const float sw = (SWIGLU && jj >= TN / 2) ? swb : swa;
+          const f32x4 part = mfma_fp8(af[i], bfr[jj], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[r], sa[r] * sw, acc[i][j][r]);
+          for (int r = 0; r < 4; ++r) acc[i][jj][r] = fmaf(part[r], sa[r] * sw, acc[i][jj][r]);
         }
       }
     }
-    if (more) sstore(cur ^ 1);
-    __syncthreads();
-  }
 
-  // ---- epilogue ----
-  constexpr int TO = SWIGLU ? TN / 2 : TN;  // output 16-column tiles per wave
-  const int64_t orow0 = (int64_t)(row0 - base_row);
-  float v[TM][TO][4];
+    if (kt == ksteps - 1) {
+      // ---- epilogue of tile ct ----
+      constexpr int TO = SWIGLU ? TN / 2 : TN;
+      const int64_t orow0 = (int64_t)(ct.row0 - base_row);
+      const int col_w = (SWIGLU ? wn * (WN / 2) : wn * WN) + lr;
+      float v[TM][TO][4];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TO; ++j)
+        for (int jj = 0; jj < TO; ++jj)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        v[i][j][r] = SWIGLU ? silu(acc[i][j][r]) * acc[i][j + TO][r] : acc[i][j][r];
-  const int col_w = SWIGLU ? wn * (WN / 2) : wn * WN;  // first output column of this wave
-
-  if (OUT == OUT_F32) {
+          for (int r = 0; r < 4; ++r) v[i][jj][r] = SWIGLU ? silu(acc[i][jj][r]) * acc[i][jj + TO][r] : acc[i][jj][r];
+      if (OUT == OUT_FP8) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = wm * WM + i * 16 + lg * 4 + r;
-        if (m < nrows) {
-          float* o = reinterpret_cast<float*>(p.out + (orow0 + m) * p.ldo_b) + nt * OC + col_w + lr;
+          for (int r = 0; r < 4; ++r) {
+            float mx = 0.f;
 #pragma unroll
-          for (int j = 0; j < TO; ++j) o[j * 16] = v[i][j][r];
+            for (int jj = 0; jj < TO; ++jj) mx = fmaxf(mx, fabsf(v[i][jj][r]));
+            mx = max16(mx);
+            s_red[wn * BM + wm * WM + i * 16 + lg * 4 + r] = mx;  // the 16 lanes agree
+          }
+        MOE_BARRIER();
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = wm * WM + i * 16 + lg * 4 + r;
+          float s = 1.0f;
+          if (OUT == OUT_FP8) {
+            float amax = 0.f;
+#pragma unroll
+            for (int q = 0; q < WGN; ++q) amax = fmaxf(amax, s_red[q * BM + m]);
+            s = (amax == 0.f) ? 1.0f : amax / 448.0f;
+          }
+          if (m < ct.nrows) {
+            uint8_t* orow = p.out + (orow0 + m) * p.ldo_b;
+            const int c0 = ct.nt * OC + col_w;
+#pragma unroll
+            for (int jj = 0; jj < TO; ++jj) {
+              const int c = c0 + jj * 16;
+              if (OUT == OUT_F32) reinterpret_cast<float*>(orow)[c] = v[i][jj][r];
+              else if (OUT == OUT_BF16) reinterpret_cast<uint16_t*>(orow)[c] = (uint16_t)f32_to_bf16_rne(v[i][jj][r]);
+              else orow[c] = (uint8_t)f32_to_e4m3(v[i][jj][r] / s);
+            }
+            if (OUT == OUT_FP8 && wn == 0 && lr == 0) p.out_scale[(orow0 + m) * p.out_scale_ld + ct.nt] = s;
+          }
         }
+      if (OUT == OUT_FP8) MOE_BARRIER();  // s_red is rewritten by the next tile
+      // next tile of the compute side
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (j + 1 < total_steps) {
+        ct = tile_of((j + 1) / ksteps);
+        set_scales();
       }
-    return;
-  }
+    }
+  };
 
-  constexpr int ESZ = (OUT == OUT_BF16) ? 2 : 1;
-  constexpr int SROW = OC * ESZ + 16;  // staged row pitch (bytes)
-  static_assert(BM * SROW <= 2 * STAGE, "staging does not fit");
-  uint8_t* stage = smem;
-  if (OUT == OUT_BF16) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = wm * WM + i * 16 + lg * 4 + r;
-#pragma unroll
-        for (int j = 0; j < TO; ++j)
-          *reinterpret_cast<uint16_t*>(stage + m * SROW + (col_w + j * 16 + lr) * 2) = (uint16_t)f32_to_bf16_rne(v[i][j][r]);
-      }
-  } else {  // OUT_FP8: per-row amax over the tile's 128 columns, then E4M3 codes
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float mx = 0.f;
-#pragma unroll
-        for (int j = 0; j < TO; ++j) mx = fmaxf(mx, fabsf(v[i][j][r]));
-        mx = max16(mx);
-        if (lr == 0) s_red[wn * BM + wm * WM + i * 16 + lg * 4 + r] = mx;
-      }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = wm * WM + i * 16 + lg * 4 + r;
-        float amax = 0.f;
-#pragma unroll
-        for (int q = 0; q < WGN; ++q) amax = fmaxf(amax, s_red[q * BM + m]);
-        const float s = (amax == 0.f) ? 1.0f : amax / 448.0f;
-#pragma unroll
-        for (int j = 0; j < TO; ++j) stage[m * SROW + col_w + j * 16 + lr] = (uint8_t)f32_to_e4m3(v[i][j][r] / s);
-        if (wn == 0 && lr == 0 && m < nrows) p.out_scale[(orow0 + m) * p.out_scale_ld + nt] = s;
-      }
+  int j = 0;
+  for (; j + 3 <= total_steps; j += 3) {
+    step(std::integral_constant<int, 0>(), j);
+    step(std::integral_constant<int, 1>(), j + 1);
+    step(std::integral_constant<int, 2>(), j + 2);
   }
-  __syncthreads();
-  constexpr int CPR = OC * ESZ / 16;  // 16-byte chunks per output row
-  for (int q = tid; q < nrows * CPR; q += NT) {
-    const int m = q / CPR, c = q - m * CPR;
-    *(u32x4*)(p.out + (orow0 + m) * p.ldo_b + (int64_t)nt * OC * ESZ + c * 16) = *(const u32x4*)(stage + m * SROW + c * 16);
-  }
+  if (j < total_steps) step(std::integral_constant<int, 0>(), j);
+  if (j + 1 < total_steps) step(std::integral_constant<int, 1>(), j + 1);
+  MOE_WAIT_VM(0);  // the clamped tail DMA must land before the workgroup retires
 }
 
-template <int BM, int BN, int WGM, int WGN, bool FP8, bool SWIGLU, int OUT>
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v >= 8)
+      cus = v / 8 * 8;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool FP8, bool SWIGLU, int OUT>
 void launch(const GemmArgs& a, int64_t m_total, hipStream_t stream) {
   const int64_t mtiles = (m_total + (int64_t)a.n_groups * (BM - 1)) / BM;
-  const int64_t grid = mtiles * a.n_tiles;
-  if (grid <= 0) return;
-  grouped_gemm_kernel<BM, BN, WGM, WGN, FP8, SWIGLU, OUT><<<(unsigned)grid, WGM * WGN * 64, 0, stream>>>(a);
+  const int64_t upper = mtiles * a.n_tiles;
+  if (upper <= 0) return;
+  const int cus = device_cus();
+  const int64_t grid = upper < cus ? ((upper + 7) / 8) * 8 : cus;
+  grouped_gemm_kernel<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT><<<(unsigned)grid, WGM * WGN * 64, 0, stream>>>(a);
+}
+
+// bf16: 8 waves of 64x64; E4M3: 4 waves of 64x128 (the per-block promotion needs the
+// registers of one wave per SIMD).  Decode-sized groups: 64-row blocks, 8 waves of 64x32.
+// Narrow bf16 outputs (N/2 or N not a multiple of 128 / 256): 128-column blocks, 4 waves.
+template <bool FP8, bool SWIGLU, int OUT>
+void dispatch(const GemmArgs& a, int64_t m_total, bool small, bool narrow, hipStream_t stream) {
+  if constexpr (!FP8) {
+    if (narrow) {
+      launch<64, 128, 1, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
+      return;
+    }
+  }
+  if (small) launch<64, 256, 1, 8, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
+  else if constexpr (FP8) launch<128, 256, 2, 2, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
+  else launch<128, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
 }
 
 }  // namespace
@@ -358,20 +486,18 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
   MOE_REQUIRE(d->out_dtype != MOE_FP8_E4M3 || (fp8 && swiglu), MOE_ERR_DTYPE,
               "moe_grouped_gemm: an FP8 output needs FP8 inputs and the SwiGLU epilogue");
   MOE_REQUIRE(!(swiglu && d->out_dtype == MOE_F32), MOE_ERR_DTYPE, "moe_grouped_gemm: SwiGLU output must be bf16 or FP8");
-  MOE_REQUIRE(d->n_groups >= 1 && d->n_groups <= 1024 && d->first_group >= 0, MOE_ERR_SHAPE,
+  MOE_REQUIRE(d->n_groups >= 1 && d->n_groups <= kMaxGroups && d->first_group >= 0, MOE_ERR_SHAPE,
               "moe_grouped_gemm: n_groups=%d first_group=%d", d->n_groups, d->first_group);
   MOE_REQUIRE(d->m_total >= 0 && d->m_total < ((int64_t)1 << 31), MOE_ERR_SHAPE, "moe_grouped_gemm: m_total=%lld",
               (long long)d->m_total);
   const int kstep_elems = fp8 ? 128 : 64;
   MOE_REQUIRE(d->K >= kstep_elems && d->K % kstep_elems == 0, MOE_ERR_SHAPE,
               "moe_grouped_gemm: K=%d must be a positive multiple of %d", d->K, kstep_elems);
-  if (swiglu) {
-    const int half_mult = fp8 ? 128 : 64;
-    MOE_REQUIRE(d->N >= 2 * half_mult && (d->N / 2) % half_mult == 0 && d->N % 2 == 0, MOE_ERR_SHAPE,
-                "moe_grouped_gemm: SwiGLU needs N/2 a positive multiple of %d (N=%d)", half_mult, d->N);
-  } else {
-    MOE_REQUIRE(d->N >= 128 && d->N % 128 == 0, MOE_ERR_SHAPE, "moe_grouped_gemm: N=%d must be a positive multiple of 128", d->N);
-  }
+  // column blocks: bf16 128 (SwiGLU: 64 + 64), E4M3 256 (SwiGLU: 128 + 128, one 1x128 h tile)
+  const int ncols_min = fp8 ? 256 : 128;
+  MOE_REQUIRE(d->N >= ncols_min && d->N % ncols_min == 0, MOE_ERR_SHAPE,
+              "moe_grouped_gemm: N=%d must be a positive multiple of %d%s", d->N, ncols_min,
+              swiglu ? " (N/2 gate + N/2 up rows)" : "");
   if (fp8) MOE_REQUIRE(d->a_scale && d->w_scale, MOE_ERR_NULL, "moe_grouped_gemm: FP8 inputs need a_scale and w_scale");
   if (d->out_dtype == MOE_FP8_E4M3) MOE_REQUIRE(d->out_scale, MOE_ERR_NULL, "moe_grouped_gemm: FP8 output needs out_scale");
   const int esz = fp8 ? 1 : 2;
@@ -381,6 +507,9 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
   MOE_REQUIRE(d->ldo >= out_cols && (d->ldo * osz) % 16 == 0, MOE_ERR_ALIGN, "moe_grouped_gemm: ldo=%lld", (long long)d->ldo);
   MOE_REQUIRE(aligned16(d->a) && aligned16(d->w) && aligned16(d->out), MOE_ERR_ALIGN,
               "moe_grouped_gemm: a, w and out must be 16-byte aligned");
+  MOE_REQUIRE(!fp8 || ((reinterpret_cast<uintptr_t>(d->a_scale) & 3u) == 0 && (reinterpret_cast<uintptr_t>(d->w_scale) & 3u) == 0),
+              MOE_ERR_ALIGN, "moe_grouped_gemm: scales must be 4-byte aligned");
+  MOE_REQUIRE((int64_t)d->N * d->K * esz < ((int64_t)1 << 31), MOE_ERR_SHAPE, "moe_grouped_gemm: one W[g] exceeds 2 GiB");
 
   GemmArgs a;
   a.a = static_cast<const uint8_t*>(d->a);
@@ -400,22 +529,21 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
   a.ldo_b = d->ldo * osz;
   a.out_scale = d->out_scale;
   a.out_scale_ld = out_cols / 128;
+  const bool narrow = !fp8 && d->N % 256 != 0;
+  a.n_tiles = out_cols / ((swiglu ? 128 : 256) >> (narrow ? 1 : 0));
 
+  // Tile shape by regime: many rows per expert -> 128-row blocks; few (decode) -> 64.
+  const bool small = d->m_total / d->n_groups < 64;
   if (!fp8) {
-    a.n_tiles = swiglu ? (d->N / 2) / 64 : d->N / 128;
-    if (swiglu) launch<128, 128, 2, 2, false, true, OUT_BF16>(a, d->m_total, stream);
-    else if (d->out_dtype == MOE_BF16) launch<128, 128, 2, 2, false, false, OUT_BF16>(a, d->m_total, stream);
-    else launch<128, 128, 2, 2, false, false, OUT_F32>(a, d->m_total, stream);
+    if (swiglu) dispatch<false, true, OUT_BF16>(a, d->m_total, small, narrow, stream);
+    else if (d->out_dtype == MOE_BF16) dispatch<false, false, OUT_BF16>(a, d->m_total, small, narrow, stream);
+    else dispatch<false, false, OUT_F32>(a, d->m_total, small, narrow, stream);
   } else {
     if (swiglu) {
-      a.n_tiles = (d->N / 2) / 128;
-      if (d->out_dtype == MOE_FP8_E4M3) launch<128, 256, 2, 4, true, true, OUT_FP8>(a, d->m_total, stream);
-      else launch<128, 256, 2, 4, true, true, OUT_BF16>(a, d->m_total, stream);
-    } else {
-      a.n_tiles = d->N / 128;
-      if (d->out_dtype == MOE_BF16) launch<128, 128, 2, 2, true, false, OUT_BF16>(a, d->m_total, stream);
-      else launch<128, 128, 2, 2, true, false, OUT_F32>(a, d->m_total, stream);
-    }
+      if (d->out_dtype == MOE_FP8_E4M3) dispatch<true, true, OUT_FP8>(a, d->m_total, small, narrow, stream);
+      else dispatch<true, true, OUT_BF16>(a, d->m_total, small, narrow, stream);
+    } else if (d->out_dtype == MOE_BF16) dispatch<true, false, OUT_BF16>(a, d->m_total, small, narrow, stream);
+    else dispatch<true, false, OUT_F32>(a, d->m_total, small, narrow, stream);
   }
   return check_launch("moe_grouped_gemm");
 }

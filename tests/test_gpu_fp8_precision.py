@@ -36,7 +36,7 @@ def _codes(vals):
 
 
 def test_group_alignment_and_subnormals():
-    K, N = 128, 128
+    K, N = 128, 256
     rows = []
     rows.append([448.0] + [2.0 ** -6] * 127)   # small terms sharing a group with 448
     rows.append([448.0] + [0.25] * 127)        # 10.8 bits below: kept
@@ -71,7 +71,7 @@ def test_long_k_promotion_is_exact():
     """K = 7168 (56 slices of 128): small-integer codes with power-of-two scales make every
     partial sum exact, so the promoted fp32 accumulation must be exact too."""
     rng = np.random.default_rng(1)
-    K, N, rows = 7168, 128, 32
+    K, N, rows = 7168, 256, 32
     ai = rng.integers(-15, 16, (rows, K))
     wi = rng.integers(-15, 16, (N, K))
     sa = np.exp2(rng.integers(-4, 2, (rows, K // 128))).astype(np.float32)
