@@ -72,6 +72,7 @@ struct GemmArgs {
   int ksteps;           // number of 128-byte K steps
   int ksb;              // K / 128: scale columns (FP8)
   int64_t w_row_b;      // bytes per W row
+  int out_cols;         // output columns (N, or N / 2 after SwiGLU)
   int n_tiles;          // output tiles along N
   uint8_t* out;
   int64_t ldo_b;        // bytes per output row
@@ -128,19 +129,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   static_assert(!SWIGLU || TN % 2 == 0, "SwiGLU waves need matching gate and up tiles");
   static_assert(OUT != OUT_FP8 || (FP8 && SWIGLU && OC == 128), "fp8 output = one 1x128 tile per row");
   static_assert(!FP8 || (SWIGLU ? WN / 2 <= 128 : WN <= 128), "a wave must sit inside one 128-row scale block");
-  static_assert(STAGES == 3, "the ring is written for three slots");
+  static_assert(STAGES == 2 || STAGES == 3, "the ring has two or three slots");
   static_assert(L_STAGE * (STAGES - 2) <= 63, "vmcnt budget");
 
   // one LDS array per ring slot: distinct objects, so the compiler can tell the DMA target of
   // a step apart from the slot being read and adds no waits of its own
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t slot2[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot2[STAGES > 2 ? STAGE : 16];
   // A scales: every wave issues one 64-float DMA per stage (waves past the tile's rows fill
   // a spare region), so all waves have the same DMA count and no branch around it
   __shared__ __attribute__((aligned(16))) float sas0[FP8 ? 64 * NW : 1];
   __shared__ __attribute__((aligned(16))) float sas1[FP8 ? 64 * NW : 1];
-  __shared__ __attribute__((aligned(16))) float sas2[FP8 ? 64 * NW : 1];
+  __shared__ __attribute__((aligned(16))) float sas2[FP8 && STAGES > 2 ? 64 * NW : 1];
   __shared__ float s_red[OUT == OUT_FP8 ? WGN * BM : 1];
   __shared__ int s_tstart[kMaxGroups + 1];
   __shared__ int s_offs[kMaxGroups + 1];
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     set_rows(src0, ssrc0);
   }
   issue(std::integral_constant<int, 0>(), 0);
-  issue(std::integral_constant<int, 1>(), 1);
+  if constexpr (STAGES > 2) issue(std::integral_constant<int, 1>(), 1);
 
   // ---- compute state ----
   const int lr = lane & 15, lg = lane >> 4;
@@ -292,8 +293,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   set_scales();
   const int base_row = s_offs[0];
 
-  // one step: wait for its DMA (one later batch stays in flight), issue the DMA two steps
-  // ahead into the slot read last step, multiply, and finish the tile on its last step
+  // one step: wait for its DMA (STAGES - 2 later batches stay in flight), issue the DMA
+  // STAGES - 1 steps ahead into the slot read last step, multiply, and finish the tile on
+  // its last step
   auto step = [&](auto slot_c, int j) {
     constexpr int SL = decltype(slot_c)::value;
     const uint8_t* As = SL == 0 ? slot0 : (SL == 1 ? slot1 : slot2);
@@ -339,17 +341,29 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       typedef __attribute__((address_space(4))) const float cfloat;
       const float swa = *(cfloat*)(uintptr_t)(sw_a + kt);
       const float swb = *(cfloat*)(uintptr_t)(sw_b + kt);
+      // combined per-row scales s_A * s_W of this K block
+      float sca[TM][4], scb[TM][4];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        float sa[4];
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sa[r] = sas[wm * WM + i * 16 + lg * 4 + r];
+        for (int r = 0; r < 4; ++r) {
+          const float sa = sas[wm * WM + i * 16 + lg * 4 + r];
+          sca[i][r] = sa * swa;
+          scb[i][r] = sa * swb;
+        }
+      // every tile's partial sum gets its own registers and its promotion (fp32 FMA into the
+      // accumulator) trails the matrix core by two tiles, so MFMAs issue back to back while
+      // the VALU promotes the previous results
+      constexpr int NT = TM * TN;
+      f32x4 pq[NT];
 #pragma unroll
-        for (int jj = 0; jj < TN; ++jj) {
-          const float sw = (SWIGLU && jj >= TN / 2) ? swb : swa;
-          const f32x4 part = mfma_fp8(af[i], bfr[jj], f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int t = 0; t < NT + 2; ++t) {
+        if (t < NT) pq[t] = mfma_fp8(af[t / TN], bfr[t % TN], f32x4{0.f, 0.f, 0.f, 0.f});
+        if (t >= 2) {
+          const int u = t - 2, i = u / TN, jj = u % TN;
+          const bool up = SWIGLU && jj >= TN / 2;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][jj][r] = fmaf(part[r], sa[r] * sw, acc[i][jj][r]);
+          for (int r = 0; r < 4; ++r) acc[i][jj][r] = fmaf(pq[u][r], up ? scb[i][r] : sca[i][r], acc[i][jj][r]);
         }
       }
     }
@@ -418,13 +432,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   };
 
   int j = 0;
-  for (; j + 3 <= total_steps; j += 3) {
+  for (; j + STAGES <= total_steps; j += STAGES) {
     step(std::integral_constant<int, 0>(), j);
     step(std::integral_constant<int, 1>(), j + 1);
-    step(std::integral_constant<int, 2>(), j + 2);
+    if constexpr (STAGES > 2) step(std::integral_constant<int, 2 % STAGES>(), j + 2);
   }
   if (j < total_steps) step(std::integral_constant<int, 0>(), j);
-  if (j + 1 < total_steps) step(std::integral_constant<int, 1>(), j + 1);
+  if constexpr (STAGES > 2)
+    if (j + 1 < total_steps) step(std::integral_constant<int, 1>(), j + 1);
   MOE_WAIT_VM(0);  // the clamped tail DMA must land before the workgroup retires
 }
 
@@ -442,7 +457,8 @@ int device_cus() {
 }
 
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool FP8, bool SWIGLU, int OUT>
-void launch(const GemmArgs& a, int64_t m_total, hipStream_t stream) {
+void launch(GemmArgs a, int64_t m_total, hipStream_t stream) {
+  a.n_tiles = a.out_cols / (SWIGLU ? BN / 2 : BN);
   const int64_t mtiles = (m_total + (int64_t)a.n_groups * (BM - 1)) / BM;
   const int64_t upper = mtiles * a.n_tiles;
   if (upper <= 0) return;
@@ -451,8 +467,10 @@ void launch(const GemmArgs& a, int64_t m_total, hipStream_t stream) {
   grouped_gemm_kernel<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT><<<(unsigned)grid, WGM * WGN * 64, 0, stream>>>(a);
 }
 
-// bf16: 8 waves of 64x64; E4M3: 4 waves of 64x128 (the per-block promotion needs the
-// registers of one wave per SIMD).  Decode-sized groups: 64-row blocks, 8 waves of 64x32.
+// bf16: 8 waves of 64x64, three-slot ring; E4M3: 4 waves of 64x128 (the per-block promotion
+// needs the registers of one wave per SIMD), two-slot ring (measured faster than three on the
+// T = 16384 routing: the third slot costs registers).  Decode-sized groups: 64-row blocks, 8
+// waves of 64x32.
 // Narrow bf16 outputs (N/2 or N not a multiple of 128 / 256): 128-column blocks, 4 waves.
 template <bool FP8, bool SWIGLU, int OUT>
 void dispatch(const GemmArgs& a, int64_t m_total, bool small, bool narrow, hipStream_t stream) {
@@ -463,7 +481,7 @@ void dispatch(const GemmArgs& a, int64_t m_total, bool small, bool narrow, hipSt
     }
   }
   if (small) launch<64, 256, 1, 8, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
-  else if constexpr (FP8) launch<128, 256, 2, 2, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
+  else if constexpr (FP8) launch<128, 256, 2, 2, 2, FP8, SWIGLU, OUT>(a, m_total, stream);
   else launch<128, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
 }
 
@@ -529,8 +547,9 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
   a.ldo_b = d->ldo * osz;
   a.out_scale = d->out_scale;
   a.out_scale_ld = out_cols / 128;
+  a.out_cols = out_cols;
+  a.n_tiles = 0;  // set per tile shape at launch
   const bool narrow = !fp8 && d->N % 256 != 0;
-  a.n_tiles = out_cols / ((swiglu ? 128 : 256) >> (narrow ? 1 : 0));
 
   // Tile shape by regime: many rows per expert -> 128-row blocks; few (decode) -> 64.
   const bool small = d->m_total / d->n_groups < 64;

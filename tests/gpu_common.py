@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -85,3 +86,79 @@ def check_permutation_properties(offs, sorted_token, pair_pos, idx, n_experts):
         assert np.all(np.diff(seg) > 0)
         assert (gi[seg] == e).any(axis=1).all()
     assert np.array_equal(st[T * K:], np.arange(T))
+
+
+# The fp8 matrix cores add products in groups of 8 K and keep about 13 bits below each
+# group's largest term (measured in test_gpu_fp8_precision): a dot product's error is a small
+# multiple of 2^-12 * sum |a_k w_k|.  The bound used in the checks is 2^-10 * sum |a_k w_k|.
+FP8_DOT_REL = 2.0 ** -10
+
+
+def fp8_staged_check(pick, x_rows, gi, pp, gate_of, n_experts, expert_weights, buf, out32, tol):
+    """The fp8 layer checked stage by stage on the tokens `pick`.
+
+    The stored h of the fp8 path is an E4M3 code chosen by rounding a floating-point value,
+    so where the device's and the oracle's accumulations straddle a rounding midpoint, two
+    codes are both correct.  The check therefore (1) bounds every stored h value, the device
+    code times its 1x128 scale, against the oracle's exact h: within one E4M3 half-step at
+    the device's scale plus the fp8 dot-product bound pushed through SwiGLU, and the device's
+    tile scales against the oracle's; then (2) recomputes the down projections and the
+    combine in the oracle from the device's stored h and compares the layer output at `tol`.
+
+    x_rows: [len(pick), d] the picked tokens' bf16 inputs (float64).
+    gi, pp: the device's top-K indices and pair rows (numpy), for all tokens.
+    gate_of(t, e): the oracle's gate of expert e for token t.
+    Returns (staged error, fraction of h codes equal to the oracle's)."""
+    h_codes = buf["h"].cpu().numpy()
+    h_scales = buf["hs"].cpu().numpy()
+    shared_base = int(buf["expert_offsets"][n_experts].item())
+    K = gi.shape[1]
+    xq, xs = O.quant_1x128(O.fp32_round(x_rows))
+    xd = O.dequant_1x128(xq, xs)
+    def deq_pair(e):
+        w13, w2 = expert_weights(e)
+        return O.dequant_128x128(*O.quant_128x128(w13)), O.dequant_128x128(*O.quant_128x128(w2))
+
+    needed = sorted({int(e) for t in pick for e in gi[t]} | {n_experts})
+    with ThreadPoolExecutor(16) as ex:
+        cache = dict(zip(needed, ex.map(deq_pair, needed)))
+    deq = cache.__getitem__
+
+    y_routed = np.zeros((len(pick) * K, x_rows.shape[1]))
+    y_shared = np.zeros((len(pick), x_rows.shape[1]))
+    gates = np.zeros((len(pick), K))
+    n_same = n_all = 0
+    for j, t in enumerate(pick):
+        for k in range(K + 1):
+            e = int(gi[t, k]) if k < K else n_experts
+            row = int(pp[t, k]) if k < K else shared_base + int(t)
+            w13, w2 = deq(e)
+            inter = w13.shape[0] // 2
+            a = xd[j] @ w13[:inter].T
+            c = xd[j] @ w13[inter:].T
+            h = O.silu(a) * c
+            da = FP8_DOT_REL * (np.abs(xd[j]) @ np.abs(w13[:inter]).T)
+            dc = FP8_DOT_REL * (np.abs(xd[j]) @ np.abs(w13[inter:]).T)
+            eps = 1.1 * da * np.abs(c) + np.abs(O.silu(a)) * dc + da * dc + 2.0 ** -18 * np.abs(h)
+            s_dev = h_scales[row].astype(np.float64)
+            s_orc = O.quant_1x128(O.fp32_round(h[None]))[1][0].astype(np.float64)
+            tile_eps = eps.reshape(-1, 128).max(axis=1)
+            assert np.all(np.abs(s_dev - s_orc) <= tile_eps / 448 + 2.0 ** -22 * s_orc), (t, e)
+            s_el = np.repeat(s_dev, 128)
+            h_dev = O.dequant_1x128(h_codes[row][None], h_scales[row][None])[0]
+            step = O.e4m3_half_ulp(np.minimum((np.abs(h) + eps) / s_el, 448.0)) * s_el
+            bad = np.abs(h_dev - h) > step * 1.0001 + eps
+            assert not bad.any(), (t, e, np.nonzero(bad)[0][:5], h_dev[bad][:5], h[bad][:5])
+            n_same += int(np.sum(h_codes[row] == O.quant_1x128(O.fp32_round(h[None]))[0][0]))
+            n_all += h.size
+            y = h_dev @ w2.T
+            if k < K:
+                y_routed[j * K + k] = O.bf16_round(y)
+                gates[j, k] = gate_of(int(t), e)
+            else:
+                y_shared[j] = O.fp32_round(y)
+    ref = O.combine(y_routed, y_shared, np.arange(len(pick) * K).reshape(len(pick), K), gates)
+    got = out32[torch.as_tensor(np.asarray(pick), device=out32.device)].cpu().numpy().astype(np.float64)
+    err = rel_err(got, ref)
+    assert err <= tol, err
+    return err, n_same / max(n_all, 1)

@@ -16,7 +16,7 @@ import torch
 from oracle import moe_oracle as O
 from sparse_moe_layer_sigmoid_amd import inputs as I
 from tests.gpu_common import (BF16_TOL, FP8_TOL, TIE_WINDOW, check_permutation_properties, check_route,
-                              np64, rel_err, say)
+                              fp8_staged_check, np64, rel_err, say)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(900)]
 DEV = "cuda:0"
@@ -55,7 +55,7 @@ def _expert_fetcher(cfg, ids):
     return lambda e: (got[e][0].double().numpy(), got[e][1].double().numpy())
 
 
-def _sampled_output_check(cfg, x_cpu, r, tie, out32, precision, n_tokens, tol):
+def _sampled_output_check(cfg, x_cpu, r, tie, out32, precision, n_tokens, tol, buf=None):
     cand = np.nonzero(~tie)[0]
     pick = cand[np.linspace(0, len(cand) - 1, n_tokens).astype(int)]
     experts = sorted(set(int(e) for e in r["idx"][pick].ravel()) | {cfg.n_experts})
@@ -68,6 +68,13 @@ def _sampled_output_check(cfg, x_cpu, r, tie, out32, precision, n_tokens, tol):
     err = rel_err(got, ref)
     say(f"[fullsize] {cfg.name}: max|out - oracle| / rms = {err:.3e} (tol {tol}) [{time.time() - t0:.0f}s]")
     assert err <= tol
+    if precision == "fp8" and buf is not None:
+        gates = {int(t): dict(zip(r["idx"][t], r["gate"][t])) for t in pick}
+        staged, same = fp8_staged_check(pick, x_cpu[pick].double().numpy(), buf["topk_idx"].cpu().numpy(),
+                                        buf["pair_pos"].cpu().numpy(), lambda t, e: gates[t][e], cfg.n_experts,
+                                        fetch, buf, out32, tol)
+        say(f"[fullsize] {cfg.name}: staged: h codes equal to the oracle's {same:.5f}, output from the device h "
+            f"{staged:.3e}")
     return err
 
 
@@ -115,7 +122,7 @@ def test_v3_fp8_T16384(v3):
     x_cpu, bias, r, tie, out32, buf = _route_and_layer(v3, cfg, True)
     xq, xs = O.quant_1x128(x_cpu.float().numpy()[:512])
     assert np.array_equal(buf["xq"][:512].cpu().numpy(), xq) and np.array_equal(buf["xs"][:512].cpu().numpy(), xs)
-    _sampled_output_check(cfg, x_cpu, r, tie, out32, "fp8", 12, FP8_TOL)
+    _sampled_output_check(cfg, x_cpu, r, tie, out32, "fp8", 12, FP8_TOL, buf)
 
 
 def test_v3_decode_bias_loop(v3):
@@ -156,5 +163,5 @@ def test_v3_decode_bias_loop(v3):
                 b_orc = O.bias_update(b_orc, O.expert_counts(r["idx"], cfg.n_experts), cfg.T, cfg.top_k, cfg.gamma)
                 assert np.array_equal(b_gpu.view(np.uint32), b_orc.view(np.uint32)), step
             if step == 0:
-                _sampled_output_check(cfg, x_cpu, r, tie, out32, "fp8", 2, FP8_TOL)
+                _sampled_output_check(cfg, x_cpu, r, tie, out32, "fp8", 2, FP8_TOL, buf)
     say(f"[fullsize] decode: max/mean load {loads[0]:.2f} (step 0) -> {loads[-1]:.2f} (step {cfg.steps - 1})")
