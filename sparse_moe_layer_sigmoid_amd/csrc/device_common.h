@@ -41,22 +41,33 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4& v, float f[8]) {
 // rint(|v| * 2^9) is the code directly); above, keep 3 mantissa bits with RNE on the 20
 // dropped bits.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  // branch-free: every lane takes both roundings and selects, so a wave never diverges
   const uint32_t u = __float_as_uint(v);
   const uint32_t sign = (u >> 24) & 0x80u;
   const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return sign | 0x7fu;   // NaN
-  if (a >= 0x43e00000u) return sign | 0x7eu;  // |v| >= 448 (or inf): saturate
-  uint32_t q;
-  if (a < 0x3c800000u) {                      // |v| < 2^-6
-    q = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  } else {
-    const uint32_t e = (a >> 23) - 120u;      // E4M3 biased exponent, 1..15
-    const uint32_t mant = a & 0x7fffffu;
-    q = (e << 3) | (mant >> 20);
-    const uint32_t rem = mant & 0xfffffu;
-    q += (rem > 0x80000u) || (rem == 0x80000u && (q & 1u));
-  }
+  // normal range: round the 20 dropped mantissa bits to nearest even in the integer domain
+  // (a carry moves into the exponent field), then rebias the exponent from 127 to 7
+  const uint32_t qn = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  // below 2^-6: multiples of 2^-9, rounded to nearest even by the hardware
+  const uint32_t qs = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  uint32_t q = a < 0x3c800000u ? qs : qn;
+  q = a >= 0x43e00000u ? 0x7eu : q;  // |v| >= 448 (or inf): saturate
+  q = a > 0x7f800000u ? 0x7fu : q;   // NaN
   return sign | q;
+}
+
+// 1/s refined by one Newton step from the hardware reciprocal (close to correctly rounded).
+__device__ __forceinline__ float recip_refined(float s) {
+  const float r = __builtin_amdgcn_rcpf(s);
+  return fmaf(fmaf(-s, r, 1.0f), r, r);
+}
+
+// v / s from the refined reciprocal rs of s: the product, then one correction with the exact
+// residual v - q s, which lands on the correctly rounded quotient in all but rare
+// double-rounding cases.
+__device__ __forceinline__ float quotient(float v, float s, float rs) {
+  const float q0 = v * rs;
+  return fmaf(fmaf(-q0, s, v), rs, q0);
 }
 
 // Matrix-core wrappers (gfx950).

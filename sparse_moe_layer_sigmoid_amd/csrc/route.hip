@@ -8,7 +8,7 @@
 // "FP8 混合精度訓練": the gating stays in high precision (bf16 products, fp32 or better sums,
 // partial sums promoted out of the matrix cores every 256 elements).
 //
-// Four kernels:
+// Five kernels:
 //  1. logits: a split-K MFMA GEMM.  A workgroup (4 waves) owns 64 tokens x all experts x one
 //     K slice; x and router rows are staged through LDS in 128-byte K steps (double
 //     buffered, XOR-swizzled); every 256 elements of K the 16x16x32 bf16 MFMA partial sum is
@@ -18,10 +18,12 @@
 //     order, forms s and z, picks the top-K by wave-wide argmax rounds (ties to the lower
 //     index) and measures the decision margin: the gap between the K-th and (K+1)-th z, and
 //     between the last kept and the best dropped group score.
-//  3. refine + count: tokens whose fp32 margin is below kRefineGap are recomputed in fp64
-//     (exact bf16 products, fp64 sums, fp64 sigmoid and selection), so the choice of experts
-//     does not depend on the matrix cores' rounding; then each block histograms its tokens.
-//  4. reduce: one wave per expert sums the block histograms (integer sums: exact).
+//  3. refine: tokens whose fp32 margin is below kRefineGap (listed by the select kernel) are
+//     recomputed in fp64 (exact bf16 products, fp64 sums, fp64 sigmoid and selection), one
+//     workgroup per token, so the choice of experts does not depend on the matrix cores'
+//     rounding.
+//  4. count: each block of 64 tokens histograms its tokens' experts.
+//  5. reduce: one wave per expert sums the block histograms (integer sums: exact).
 #include <math.h>
 
 #include "abi_common.h"
@@ -197,8 +199,10 @@ __device__ V select_token(const V u[4], const float* __restrict__ bias, int N, i
 __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ wr,
                                                            int T, int d, int N, int splits,
-                                                           float* __restrict__ part) {
+                                                           float* __restrict__ part,
+                                                           int32_t* __restrict__ n_flagged) {
   constexpr int STAGE = kRows * 128;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_flagged = 0;  // the select kernel appends after this one
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x / splits, split = blockIdx.x - tile * splits;
@@ -301,7 +305,8 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
                                                            int32_t* __restrict__ topk_idx,
                                                            float* __restrict__ topk_gate,
                                                            float* __restrict__ scores,
-                                                           int32_t* __restrict__ flags) {
+                                                           int32_t* __restrict__ n_flagged,
+                                                           int32_t* __restrict__ flagged) {
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole waves leave together
   const int lane = threadIdx.x & 63;
@@ -312,38 +317,30 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
     for (int r = 0; r < 4; ++r) u[r] += v[r];
   }
   const float margin = select_token<float>(u, bias, N, K, n_group, topk_group, t, true, topk_idx, topk_gate, scores);
-  if (lane == 0) flags[t] = margin < kRefineGap ? 1 : 0;
+  if (lane == 0 && margin < kRefineGap) flagged[atomicAdd(n_flagged, 1)] = (int32_t)t;
 }
 
-// ---- kernel 3: fp64 refinement of near-tie tokens, then per-block load histogram ----
-__global__ __launch_bounds__(256) void route_refine_count_kernel(
+// ---- kernel 3: fp64 refinement of the flagged (near-tie) tokens ----
+// One workgroup per flagged token (grid-strided over the list): wave w takes experts w,
+// w + kRefineWaves, ...; its lanes split K into 16-byte chunks and keep eight independent
+// fp64 partial sums (one per element of a chunk), so the fp64 adds pipeline.  Each token's
+// result depends on that token alone, so the list's order does not matter.
+constexpr int kRefineWaves = 16;
+__global__ __launch_bounds__(kRefineWaves * 64) void route_refine_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
-    int T, int d, int N, int K, int n_group, int topk_group, const int32_t* __restrict__ flags,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, float* __restrict__ scores,
-    int32_t* __restrict__ blk_counts) {
+    int d, int N, int K, int n_group, int topk_group, const int32_t* __restrict__ n_flagged,
+    const int32_t* __restrict__ flagged, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+    float* __restrict__ scores) {
   __shared__ double u64[256];
-  __shared__ int list[64];
-  __shared__ int nlist;
-  __shared__ int cnt[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * 64;
-  cnt[tid] = 0;
-  if (wave == 0) {
-    const int t = t0 + lane;
-    const bool f = t < T && flags[t] != 0;
-    const uint64_t m = __ballot(f);
-    if (f) list[__popcll(m & ((1ull << lane) - 1ull))] = t;
-    if (lane == 0) nlist = __popcll(m);
-  }
-  __syncthreads();
+  const int nf = *n_flagged;
   const int nd = d / 8;  // 16-byte chunks per row
-  for (int i = 0; i < nlist; ++i) {
-    const int64_t t = list[i];
+  for (int i = blockIdx.x; i < nf; i += gridDim.x) {
+    const int64_t t = flagged[i];
     const uint16_t* xr = x + t * d;
-    // wave w owns experts w, w+4, ...; lanes split K; products of bf16 are exact in fp32
-    for (int e = wave; e < N; e += 4) {
+    for (int e = wave; e < N; e += kRefineWaves) {
       const uint16_t* er = wr + (int64_t)e * d;
-      double a = 0.0;
+      double a[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
       for (int c = lane; c < nd; c += 64) {
         const u32x4 xv = *(const u32x4*)(xr + c * 8);
         const u32x4 ev = *(const u32x4*)(er + c * 8);
@@ -351,11 +348,12 @@ __global__ __launch_bounds__(256) void route_refine_count_kernel(
         unpack_bf16x8(xv, xf);
         unpack_bf16x8(ev, ef);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) a += (double)(xf[q] * ef[q]);
+        for (int q = 0; q < 8; ++q) a[q] += (double)(xf[q] * ef[q]);  // bf16 products are exact in fp32
       }
+      double sum = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
-      if (lane == 0) u64[e] = a;
+      for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+      if (lane == 0) u64[e] = sum;
     }
     __syncthreads();
     if (wave == 0) {
@@ -366,15 +364,23 @@ __global__ __launch_bounds__(256) void route_refine_count_kernel(
     }
     __syncthreads();
   }
-  if (tid < 64 && t0 + tid < T) {
-    const int64_t t = t0 + tid;
-    for (int k = 0; k < K; ++k) atomicAdd(&cnt[topk_idx[t * K + k]], 1);
-  }
-  __syncthreads();
-  if (tid < N) blk_counts[(int64_t)blockIdx.x * N + tid] = cnt[tid];
 }
 
-// ---- kernel 4: one wave per expert sums the block histograms ----
+// ---- kernel 4: per-block load histogram (64 tokens per block) ----
+__global__ __launch_bounds__(64) void route_count_kernel(const int32_t* __restrict__ topk_idx, int T, int N, int K,
+                                                         int32_t* __restrict__ blk_counts) {
+  __shared__ int cnt[256];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < N; e += 64) cnt[e] = 0;
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * 64 + lane;
+  if (t < T)
+    for (int k = 0; k < K; ++k) atomicAdd(&cnt[topk_idx[t * K + k]], 1);
+  __syncthreads();
+  for (int e = lane; e < N; e += 64) blk_counts[(int64_t)blockIdx.x * N + e] = cnt[e];
+}
+
+// ---- kernel 5: one wave per expert sums the block histograms ----
 __global__ __launch_bounds__(64) void counts_reduce_kernel(const int32_t* __restrict__ blk, int nb, int N,
                                                            int32_t* __restrict__ counts) {
   const int e = blockIdx.x, lane = threadIdx.x;
@@ -393,7 +399,7 @@ int route_splits(int T, int d) {
 }
 
 struct RouteWs {
-  size_t part_off, flags_off, blk_off, total;
+  size_t part_off, nflag_off, list_off, blk_off, total;
 };
 
 RouteWs route_ws(int T, int d, int N) {
@@ -401,8 +407,9 @@ RouteWs route_ws(int T, int d, int N) {
   const int S = route_splits(T, d);
   const int nb = T > 0 ? (T + 63) / 64 : 1;
   w.part_off = 0;
-  w.flags_off = (size_t)S * (size_t)T * 256 * sizeof(float);
-  w.blk_off = w.flags_off + (((size_t)T * sizeof(int32_t) + 255) & ~(size_t)255);
+  w.nflag_off = (size_t)S * (size_t)T * 256 * sizeof(float);
+  w.list_off = w.nflag_off + 256;
+  w.blk_off = w.list_off + (((size_t)T * sizeof(int32_t) + 255) & ~(size_t)255);
   w.total = w.blk_off + (size_t)nb * (size_t)N * sizeof(int32_t);
   return w;
 }
@@ -451,17 +458,19 @@ extern "C" moe_status moe_route(const uint16_t* x, const uint16_t* w_router, con
   const RouteWs L = route_ws(T, d, n_experts);
   uint8_t* base = static_cast<uint8_t*>(ws);
   float* part = reinterpret_cast<float*>(base + L.part_off);
-  int32_t* flags = reinterpret_cast<int32_t*>(base + L.flags_off);
+  int32_t* n_flagged = reinterpret_cast<int32_t*>(base + L.nflag_off);
+  int32_t* flagged = reinterpret_cast<int32_t*>(base + L.list_off);
   int32_t* blk = reinterpret_cast<int32_t*>(base + L.blk_off);
   const int S = route_splits(T, d);
   const int tiles = (T + kTM - 1) / kTM;
   const int nb = (T + 63) / 64;
   if (T > 0) {
-    route_logits_kernel<<<tiles * S, 256, 0, stream>>>(x, w_router, T, d, n_experts, S, part);
+    route_logits_kernel<<<tiles * S, 256, 0, stream>>>(x, w_router, T, d, n_experts, S, part, n_flagged);
     route_select_kernel<<<(T + 3) / 4, 256, 0, stream>>>(part, S, bias, T, n_experts, top_k, n_group, topk_group,
-                                                         topk_idx, topk_gate, scores, flags);
-    route_refine_count_kernel<<<nb, 256, 0, stream>>>(x, w_router, bias, T, d, n_experts, top_k, n_group, topk_group,
-                                                      flags, topk_idx, topk_gate, scores, blk);
+                                                         topk_idx, topk_gate, scores, n_flagged, flagged);
+    route_refine_kernel<<<T < 256 ? T : 256, kRefineWaves * 64, 0, stream>>>(
+        x, w_router, bias, d, n_experts, top_k, n_group, topk_group, n_flagged, flagged, topk_idx, topk_gate, scores);
+    route_count_kernel<<<nb, 64, 0, stream>>>(topk_idx, T, n_experts, top_k, blk);
   }
   counts_reduce_kernel<<<n_experts, 64, 0, stream>>>(blk, nb, n_experts, expert_counts);
   return check_launch("moe_route");

@@ -214,21 +214,29 @@ def test_gemm_subrange_and_plain_rows():
     assert rel_err(got, ref) < 1e-5
 
 
-def test_gemm_fp8_exact():
+@pytest.mark.parametrize("sizes,K", [
+    ([5, 130, 64], 512),             # 128-row tiles, one partial chunk of A scales per tile
+    ([5, 130, 64, 300], 2176),       # 17 K blocks: chunks of 8, 8 and 1 across many tiles
+    ([5, 30, 20, 9, 1, 0, 40], 1152),  # decode-sized groups (64-row tiles, three-slot ring), 8 + 1
+], ids=["K512", "K2176", "small_K1152"])
+def test_gemm_fp8_exact(sizes, K):
     """E4M3 codes of small integers with power-of-two scales: every product and every sum is
     exact in fp32, so the fp8 GEMM must equal the oracle bit for bit.  This pins the MFMA
     operand layout, the per-128-K promotion and the scale indexing (per row tile of A, per
-    128x128 block of W)."""
-    G, N, K = 3, 256, 512
-    sizes = np.array([5, 130, 64])
+    128x128 block of W), across K-block counts that leave partial chunks of A scales."""
+    G, N = len(sizes), 256
+    sizes = np.array(sizes)
     offs = _offsets(sizes)
     rows = int(offs[-1])
     T = 100
     a_rows = np.random.default_rng(2).integers(0, T, rows).astype(np.int32)
     Aq = I.gen_e4m3_codes(41, (T, K), small_int=True)
-    As = I.gen_scales(42, (T, K // 128), pow2=True)
     Wq = I.gen_e4m3_codes(43, (G, N, K), small_int=True)
-    Ws = I.gen_scales(44, (G, N // 128, K // 128), pow2=True)
+    # power-of-two scales from two neighbouring binades each, so every product s_a s_w lies in
+    # [2^-9, 2^-7] and all partial sums (|sum| <= K * 225 * 2^-7) are multiples of 2^-9 below
+    # 2^21 units: exact in fp32 whatever the order
+    As = torch.where(I.gen_scales(42, (T, K // 128), pow2=True) <= 2.0 ** -6, 2.0 ** -4, 2.0 ** -3).float()
+    Ws = torch.where(I.gen_scales(44, (G, N // 128, K // 128), pow2=True) <= 2.0 ** -6, 2.0 ** -5, 2.0 ** -4).float()
     out = torch.empty((rows, N), dtype=torch.float32, device=DEV)
     M().moe_grouped_gemm(Aq.to(DEV), Wq.to(DEV), torch.from_numpy(offs).to(DEV), 0, G, rows, out,
                          a_scale=As.to(DEV), a_rows=torch.from_numpy(a_rows).to(DEV), w_scale=Ws.to(DEV))
