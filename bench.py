@@ -44,6 +44,11 @@ def parse():
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--decode-steps", type=int, default=None)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="first copy 1 GiB device-to-device twice (the reference dispatch for HBM counters)")
+    p.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of a --calibrate-copy bench "
+                        "into profiles/traffic_<kernel>_<workload>.json, then exit")
     return p.parse_args()
 
 
@@ -145,6 +150,48 @@ def measured_traffic(kernel_tag):
     return rec.get("bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30
+
+
+def _pmc_rows(d, counter):
+    """(kernel name, value) per dispatch of `counter` from a rocprofv3 --pmc csv directory."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Dispatch_Id"], r["Kernel_Name"])
+                out[key] = out.get(key, 0.0) + float(r["Counter_Value"])
+    return [(k[1], v) for k, v in sorted(out.items(), key=lambda kv: int(kv[0][0]))]
+
+
+def ingest_pmc(fetch_dir, write_dir, workload):
+    """HBM bytes per launch of the gate/up kernel from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by the factor that maps the same counter on a 1 GiB device copy
+    to 1 GiB."""
+    fp8 = "fp8" in workload
+    want = f"{'true' if fp8 else 'false'}, true, {2 if fp8 else 0}>"
+    rec = {"workload": workload, "kernel_src_sha": kernel_src_sha(), "copy_bytes": COPY_BYTES}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(d, counter)
+        copies = [v for n, v in rows if "copyBuffer" in n and v * 1024 > COPY_BYTES / 4]
+        gemm = [v for n, v in rows if "grouped_gemm_kernel" in n and want in n]
+        if not copies or not gemm:
+            raise SystemExit(f"{counter}: no calibration copy or no gate/up dispatch in {d}")
+        factor = COPY_BYTES / (sum(copies) / len(copies) * 1024)
+        kib = sum(gemm) / len(gemm)
+        rec[counter.lower()] = {"kib_per_dispatch": round(kib, 1), "copy_factor": round(factor, 4),
+                                "bytes_per_launch": int(kib * 1024 * factor), "dispatches": len(gemm)}
+    rec["bytes_per_launch"] = rec["fetch_size"]["bytes_per_launch"] + rec["write_size"]["bytes_per_launch"]
+    path = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(cfg, wr_cpu, bias_cpu, W13_cpu, W2_cpu, budget_s=10.0, max_steps=8):
     """The CPU oracle, untuned, on whole steps of the workload: per step, fp64 routing of all
     T tokens of a fresh batch, the permutation, the SwiGLU FFN of every expert (the shared
@@ -206,6 +253,9 @@ def main():
     import numpy as np
     import torch
 
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload)
+        return
     import sparse_moe_layer_sigmoid_amd as M
     from oracle import moe_oracle as O
     from sparse_moe_layer_sigmoid_amd import inputs as I
@@ -213,6 +263,13 @@ def main():
     M.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfgs = {c.name: c for c in I.CONFIGS.values()}
     cfg = cfgs[args.workload]
     t0 = time.time()
@@ -269,7 +326,7 @@ def main():
         sec.append({"workload": c3.name, "dtype": "fp8", "ms_per_step": round(ms3, 4),
                     "tokens_per_s": round(c3.T / (ms3 / 1e3), 1), "tflops": round(f3 / (ms3 / 1e3) / 1e12, 2),
                     "mfma_frac_fp8_peak": round(f3 / (ms3 / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4),
-                    "gate_up_ms": round(gu3, 4),
+                    "gate_up_ms": round(gu3, 4), "gate_up_traffic": measured_traffic(f"gate_up_{c3.name}"),
                     "gate_up_mfma_frac": round(fl3 / (gu3 / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4)})
         log(f"[bench] {c3.name}: {ms3:.3f} ms/step")
         del l3
