@@ -186,12 +186,22 @@ typedef struct moe_gemm_desc {
   int out_dtype;                /* MOE_BF16, MOE_F32, or MOE_FP8_E4M3 (+ out_scale) */
   int64_t ldo;
   float* out_scale;             /* FP8 output: device f32 [rows, out_cols/128]; else NULL */
+  /* Optional split output: the last tail_groups groups write f32 rows to out_tail (row r of
+   * such a group lands in out_tail row r - group_offsets[first_group + n_groups - tail_groups],
+   * leading dimension ldo_tail) instead of out; the other groups write out as above.  One
+   * launch then covers the routed experts (bf16 rows) and the shared expert (f32 rows).
+   * tail_groups = 0 disables it (out_tail ignored). */
+  int tail_groups;
+  void* out_tail;
+  int64_t ldo_tail;
 } moe_gemm_desc;
 /* Limits: K a positive multiple of 64 (bf16) or 128 (FP8); N a positive multiple of 128 (bf16)
  * or 256 (FP8) -- with SWIGLU that is N/2 a multiple of 64 or 128; FP8 input needs a_scale and
  * w_scale (4-byte aligned); an FP8 output needs FP8 input, SWIGLU and out_scale; SWIGLU
  * output is bf16 or FP8; 1 <= n_groups <= 1024; 0 <= m_total < 2^31; one W[g] < 2 GiB;
- * lda/ldo keep rows 16-byte aligned. */
+ * lda/ldo keep rows 16-byte aligned.  A split output (tail_groups > 0) needs epilogue NONE,
+ * out_dtype MOE_BF16, tail_groups <= n_groups and a 16-byte aligned out_tail with
+ * ldo_tail >= N. */
 moe_status moe_grouped_gemm(const moe_gemm_desc* desc, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------

@@ -38,6 +38,7 @@ class MoeGemmDesc(ctypes.Structure):
         ("w", _p), ("w_scale", _p), ("group_offsets", _p), ("first_group", _i),
         ("n_groups", _i), ("m_total", _i64), ("N", _i), ("K", _i), ("epilogue", _i),
         ("out", _p), ("out_dtype", _i), ("ldo", _i64), ("out_scale", _p),
+        ("tail_groups", _i), ("out_tail", _p), ("ldo_tail", _i64),
     ]
 
 
@@ -186,16 +187,22 @@ _DT = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32, torch.uint8: MOE_FP8_E4
 
 
 def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_total: int, out,
-                     a_scale=None, a_rows=None, w_scale=None, swiglu: bool = False, out_scale=None):
+                     a_scale=None, a_rows=None, w_scale=None, swiglu: bool = False, out_scale=None,
+                     out_tail=None, tail_groups: int = 0):
     """out[r - off[first_group]] = epilogue(A[a_rows[r] or r] . W[g]^T) for each sorted row r
     of group g.  a: bf16 or uint8 (E4M3) [*, K]; w: same dtype [G, N, K]; out: bf16 / f32 /
-    uint8 (E4M3, needs out_scale)."""
+    uint8 (E4M3, needs out_scale).  With tail_groups > 0 the last tail_groups groups write
+    f32 rows to out_tail instead (row r -> r - off[first_group + n_groups - tail_groups])."""
     fp8 = a.dtype == torch.uint8
     if w.dtype != a.dtype:
         raise TypeError("a and w must share a dtype")
     for t, nm in ((a, "a"), (w, "w"), (group_offsets, "group_offsets"), (out, "out")):
         if not t.is_cuda:
             raise TypeError(f"{nm} must be a GPU tensor")
+    if tail_groups:
+        _dev(out_tail, torch.float32, "out_tail", contiguous=False)
+        if out_tail.stride(-1) != 1:
+            raise ValueError("rows of out_tail must be contiguous")
     if a.stride(-1) != 1 or out.stride(-1) != 1 or not w.is_contiguous():
         raise ValueError("rows of a/out and all of w must be contiguous")
     G, N, K = w.shape
@@ -207,7 +214,9 @@ def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_tot
         group_offsets=group_offsets.data_ptr(), first_group=first_group, n_groups=n_groups,
         m_total=m_total, N=N, K=K, epilogue=MOE_EPI_SWIGLU if swiglu else MOE_EPI_NONE,
         out=out.data_ptr(), out_dtype=_DT[out.dtype], ldo=out.stride(0),
-        out_scale=out_scale.data_ptr() if out_scale is not None else None)
+        out_scale=out_scale.data_ptr() if out_scale is not None else None,
+        tail_groups=tail_groups, out_tail=out_tail.data_ptr() if tail_groups else None,
+        ldo_tail=out_tail.stride(0) if tail_groups else 0)
     st = lib().moe_grouped_gemm(ctypes.byref(desc), _stream(a))
     _check("moe_grouped_gemm", st)
     return out

@@ -89,6 +89,9 @@ struct GemmArgs {
   int64_t ldo_b;        // bytes per output row
   float* out_scale;
   int out_scale_ld;
+  int tail_first;       // first group (relative) writing the f32 tail output; n_groups if none
+  uint8_t* out_tail;
+  int64_t ldo_tail_b;   // bytes per tail output row
 };
 
 __device__ __forceinline__ float silu(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
@@ -484,7 +487,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
             s = (amax == 0.f) ? 1.0f : amax / 448.0f;
           }
           const float rs = recip_refined(s);
-          if (m < ct.nrows) {
+          if (OUT == OUT_BF16 && !SWIGLU && ct.g >= p.tail_first) {
+            // split output: this group's rows go to the f32 tail
+            if (m < ct.nrows) {
+              float* trow = reinterpret_cast<float*>(p.out_tail + (int64_t)(ct.row0 - s_offs[p.tail_first] + m) * p.ldo_tail_b);
+              const int c0 = ct.nt * OC + col_w;
+#pragma unroll
+              for (int jj = 0; jj < TO; ++jj) trow[c0 + jj * 16] = v[i][jj][r];
+            }
+          } else if (m < ct.nrows) {
             uint8_t* orow = p.out + (orow0 + m) * p.ldo_b;
             const int c0 = ct.nt * OC + col_w;
 #pragma unroll
@@ -608,6 +619,16 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
   MOE_REQUIRE(!fp8 || ((reinterpret_cast<uintptr_t>(d->a_scale) & 3u) == 0 && (reinterpret_cast<uintptr_t>(d->w_scale) & 3u) == 0),
               MOE_ERR_ALIGN, "moe_grouped_gemm: scales must be 4-byte aligned");
   MOE_REQUIRE((int64_t)d->N * d->K * esz < ((int64_t)1 << 31), MOE_ERR_SHAPE, "moe_grouped_gemm: one W[g] exceeds 2 GiB");
+  MOE_REQUIRE(d->tail_groups >= 0 && d->tail_groups <= d->n_groups, MOE_ERR_SHAPE,
+              "moe_grouped_gemm: tail_groups=%d must be in [0, n_groups=%d]", d->tail_groups, d->n_groups);
+  if (d->tail_groups > 0) {
+    MOE_REQUIRE(!swiglu && d->out_dtype == MOE_BF16, MOE_ERR_DTYPE,
+                "moe_grouped_gemm: a split output needs epilogue NONE and a bf16 main output");
+    MOE_REQUIRE(d->m_total == 0 || d->out_tail, MOE_ERR_NULL, "moe_grouped_gemm: out_tail is NULL");
+    MOE_REQUIRE(d->ldo_tail >= out_cols && (d->ldo_tail * 4) % 16 == 0 && aligned16(d->out_tail), MOE_ERR_ALIGN,
+                "moe_grouped_gemm: out_tail must be 16-byte aligned with ldo_tail >= %d (ldo_tail=%lld)", out_cols,
+                (long long)d->ldo_tail);
+  }
 
   GemmArgs a;
   a.a = static_cast<const uint8_t*>(d->a);
@@ -627,6 +648,9 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
   a.ldo_b = d->ldo * osz;
   a.out_scale = d->out_scale;
   a.out_scale_ld = out_cols / 128;
+  a.tail_first = d->n_groups - d->tail_groups;
+  a.out_tail = static_cast<uint8_t*>(d->out_tail);
+  a.ldo_tail_b = d->ldo_tail * 4;
   a.out_cols = out_cols;
   a.n_tiles = 0;  // set per tile shape at launch
   const bool narrow = !fp8 && d->N % 256 != 0;

@@ -4,7 +4,7 @@ Holds the (device-resident) weights and allocates the per-batch buffers; every s
 in libmoe's kernels:
 
     route -> permute -> [fp8: quantise x per 1x128] -> gate/up grouped GEMM + SwiGLU
-          -> down grouped GEMM (routed experts, bf16 rows) -> down GEMM (shared, fp32 rows)
+          -> down grouped GEMM (routed experts to bf16 rows, the shared expert to fp32 rows)
           -> combine -> [bias update]
 
 Layer definition: "DeepSeek-V3 Technical Report" (wiki summary), "DeepSeekMoE と補助損失
@@ -62,8 +62,10 @@ class MoELayer:
             L.moe_grouped_gemm(x, self.W13, offs, 0, N + 1, rows, h, a_rows=sorted_token, swiglu=True)
         y = torch.empty((T * K, d), dtype=torch.bfloat16, device=dev)
         ysh = torch.empty((T, d), dtype=torch.float32, device=dev)
-        L.moe_grouped_gemm(h, self.W2, offs, 0, N, T * K, y, a_scale=hs, w_scale=self.W2_s)
-        L.moe_grouped_gemm(h, self.W2, offs, N, 1, T, ysh, a_scale=hs, w_scale=self.W2_s)
+        # one launch for all N + 1 down projections: routed rows to y (bf16), the shared
+        # expert's rows (the last group) to ysh (f32)
+        L.moe_grouped_gemm(h, self.W2, offs, 0, N + 1, rows, y, a_scale=hs, w_scale=self.W2_s, out_tail=ysh,
+                           tail_groups=1)
         out = L.moe_combine(y, ysh, pair_pos, gate, out_dtype)
         if update_bias:
             L.moe_bias_update(self.bias, counts, T * K, gamma)

@@ -30,7 +30,7 @@ def test_header_declares_exactly_the_exports():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.lib().moe_abi_version() == 1
+    assert L.lib().moe_abi_version() == 2
     assert L.status_str(0) == "MOE_OK" and L.status_str(5) == "MOE_ERR_WORKSPACE"
 
 
@@ -86,6 +86,10 @@ def _gemm(L, **kw):
     (dict(K=96), 2), (dict(N=192), 2), (dict(epilogue=1, N=192, out_dtype=0), 2), (dict(in_dtype=2), 1),
     (dict(in_dtype=2, a_scale=16, w_scale=16, K=192), 2), (dict(lda=200), 4), (dict(ldo=100), 4),
     (dict(a=8), 4), (dict(m_total=-1), 2),
+    (dict(tail_groups=5), 2), (dict(tail_groups=-1), 2), (dict(tail_groups=1, out_tail=16, ldo_tail=256), 3),
+    (dict(tail_groups=1, out_dtype=0, ldo=256), 1), (dict(tail_groups=1, out_dtype=0, out_tail=8, ldo_tail=256), 4),
+    (dict(tail_groups=1, out_dtype=0, out_tail=16, ldo_tail=100), 4),
+    (dict(tail_groups=1, out_dtype=0, out_tail=16, ldo_tail=256, epilogue=1, N=512), 3),
 ])
 def test_gemm_rejects(kw, code):
     L = _lib()

@@ -198,6 +198,35 @@ def test_gemm_bf16(swiglu, out_dtype):
             assert np.all(np.abs(got[lo:hi] - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6 * np.sqrt(np.mean(ref ** 2))), g
 
 
+@pytest.mark.parametrize("fp8,tail", [(False, 1), (False, 2), (True, 1)], ids=["bf16_tail1", "bf16_tail2", "fp8_tail1"])
+def test_gemm_split_output(fp8, tail):
+    """One launch over all groups with the last `tail` groups written as f32 rows to a second
+    buffer equals, bit for bit, the two launches it replaces (bf16 main rows, f32 tail rows):
+    the tile arithmetic does not depend on the launch."""
+    G, N, K = 5, 256, 256
+    sizes = np.array([40, 0, 130, 70, 200])
+    offs = _offsets(sizes)
+    rows = int(offs[-1])
+    if fp8:
+        A = I.gen_e4m3_codes(61, (rows, K), small_int=True)
+        W = I.gen_e4m3_codes(62, (G, N, K), small_int=True)
+        kw = dict(a_scale=I.gen_scales(63, (rows, K // 128)).to(DEV), w_scale=I.gen_scales(64, (G, N // 128, K // 128)).to(DEV))
+    else:
+        A = I.gen_normal(61, (rows, K), 1.0)
+        W = I.gen_normal(62, (G, N, K), 0.05)
+        kw = {}
+    A, W, o = A.to(DEV), W.to(DEV), torch.from_numpy(offs).to(DEV)
+    split = int(offs[G - tail])
+    main = torch.empty((split, N), dtype=torch.bfloat16, device=DEV)
+    tail_out = torch.empty((rows - split, N), dtype=torch.float32, device=DEV)
+    M().moe_grouped_gemm(A, W, o, 0, G, rows, main, out_tail=tail_out, tail_groups=tail, **kw)
+    ref_main = torch.empty_like(main)
+    ref_tail = torch.empty_like(tail_out)
+    M().moe_grouped_gemm(A, W, o, 0, G - tail, split, ref_main, **kw)
+    M().moe_grouped_gemm(A, W, o, G - tail, tail, rows - split, ref_tail, **kw)
+    assert torch.equal(main, ref_main) and torch.equal(tail_out, ref_tail)
+
+
 def test_gemm_subrange_and_plain_rows():
     """first_group > 0 and A indexed by the global sorted row (the shared-expert launch)."""
     G, N, K = 4, 128, 128
