@@ -216,7 +216,7 @@ moe_status moe_grouped_gemm(const moe_gemm_desc* desc, hipStream_t stream);
  *   pair_pos  device i32 [T, top_k] (entries < 0 are skipped)
  *   topk_gate device f32 [T, top_k]
  *   out       device [T, d], bf16 or f32 per out_dtype
- * Limits: T >= 0; top_k >= 1; d >= 8, d % 8 == 0.
+ * Limits: T >= 0; 1 <= top_k <= 256; d >= 8, d % 8 == 0.
  * ------------------------------------------------------------------------------------ */
 moe_status moe_combine(const uint16_t* y_routed, const float* y_shared, const int32_t* pair_pos,
                        const float* topk_gate, int T, int top_k, int d, void* out,

@@ -6,7 +6,8 @@
 // chosen experts return their results, merged with the always-on shared expert):
 //   out[t] = y_shared[t] + sum_k gate[t,k] * y_routed[pair_pos[t,k]]   (fp32, k in order)
 // An HBM-bound gather: one workgroup per token, 16-byte loads of 8 bf16 per lane, the
-// token's pair rows and gates read once (wave-uniform) per workgroup.
+// token's pair rows and gates read once into LDS per workgroup, all of a thread's routed
+// rows loaded before its FMAs.
 //
 // Bias update ("DeepSeekMoE と補助損失なしの負荷分散"): the expert's load over the batch is
 // compared with the mean in integers (load * N vs T * K); an overloaded expert's bias drops
@@ -17,27 +18,49 @@
 namespace moe {
 namespace {
 
+constexpr int kMaxCombineK = 256;
+
+// One workgroup per token: its pair rows and gates are read once into LDS; every thread owns
+// 16-byte column chunks and issues the loads of all its routed rows before the FMAs (which keep
+// the k order), so each thread has up to top_k gathers in flight.
 template <bool OUT_F32>
-__global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict__ y,
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const float* __restrict__ ysh,
                                                       const int32_t* __restrict__ pair_pos,
                                                       const float* __restrict__ gate, int K,
                                                       int d, void* __restrict__ out) {
+  __shared__ int s_p[kMaxCombineK];
+  __shared__ float s_g[kMaxCombineK];
   const int64_t t = blockIdx.x;
+  for (int k = threadIdx.x; k < K; k += blockDim.x) {
+    s_p[k] = pair_pos[t * K + k];
+    s_g[k] = gate[t * K + k];
+  }
+  __syncthreads();
   const int nc = d / 8;
   for (int c = threadIdx.x; c < nc; c += blockDim.x) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int p = pair_pos[t * K + k];
-      if (p < 0) continue;
-      const float g = gate[t * K + k];
-      const u32x4 v = *(const u32x4*)(y + (int64_t)p * d + c * 8);
-      float f[8];
-      unpack_bf16x8(v, f);
+    for (int k0 = 0; k0 < K; k0 += 8) {
+      u32x4 v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, f[i], acc[i]);
+      for (int q = 0; q < 8; ++q) {
+        const int k = k0 + q;
+        const int p = k < K ? s_p[k] : -1;
+        v[q] = p >= 0 ? *(const u32x4*)(y + (int64_t)p * d + c * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int k = k0 + q;
+        if (k < K && s_p[k] >= 0) {  // entries < 0 are skipped
+          const float g = s_g[k];
+          float f[8];
+          unpack_bf16x8(v[q], f);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, f[i], acc[i]);
+        }
+      }
     }
     if (ysh != nullptr) {
       const f32x4 a = *(const f32x4*)(ysh + t * d + c * 8);
@@ -82,7 +105,7 @@ extern "C" moe_status moe_combine(const uint16_t* y_routed, const float* y_share
   clear_error();
   MOE_REQUIRE(T == 0 || (y_routed && pair_pos && topk_gate && out), MOE_ERR_NULL,
               "moe_combine: a required pointer is NULL");
-  MOE_REQUIRE(T >= 0 && top_k >= 1 && d >= 8 && d % 8 == 0, MOE_ERR_SHAPE,
+  MOE_REQUIRE(T >= 0 && top_k >= 1 && top_k <= kMaxCombineK && d >= 8 && d % 8 == 0, MOE_ERR_SHAPE,
               "moe_combine: T=%d top_k=%d d=%d (d must be a positive multiple of 8)", T, top_k, d);
   MOE_REQUIRE(out_dtype == MOE_BF16 || out_dtype == MOE_F32, MOE_ERR_DTYPE,
               "moe_combine: out_dtype must be MOE_BF16 or MOE_F32");
@@ -90,9 +113,9 @@ extern "C" moe_status moe_combine(const uint16_t* y_routed, const float* y_share
               MOE_ERR_ALIGN, "moe_combine: y_routed, y_shared and out must be 16-byte aligned");
   if (T > 0) {
     if (out_dtype == MOE_F32)
-      combine_kernel<true><<<T, 128, 0, stream>>>(y_routed, y_shared, pair_pos, topk_gate, top_k, d, out);
+      combine_kernel<true><<<T, 256, 0, stream>>>(y_routed, y_shared, pair_pos, topk_gate, top_k, d, out);
     else
-      combine_kernel<false><<<T, 128, 0, stream>>>(y_routed, y_shared, pair_pos, topk_gate, top_k, d, out);
+      combine_kernel<false><<<T, 256, 0, stream>>>(y_routed, y_shared, pair_pos, topk_gate, top_k, d, out);
   }
   return check_launch("moe_combine");
 }

@@ -9,11 +9,11 @@
 // partial sums promoted out of the matrix cores every 256 elements).
 //
 // Five kernels:
-//  1. logits: a split-K MFMA GEMM.  A workgroup (4 waves) owns 64 tokens x all experts x one
-//     K slice; x and router rows are staged through LDS in 128-byte K steps (double
-//     buffered, XOR-swizzled); every 256 elements of K the 16x16x32 bf16 MFMA partial sum is
-//     added into an fp32 accumulator (the matrix cores truncate inside their adder, so long
-//     chains are avoided).  Partial logits of each slice go to the workspace.
+//  1. logits: a split-K MFMA GEMM.  A workgroup (8 waves of 64 tokens x 64 experts) owns 128
+//     tokens x all experts x one K slice; x and router rows are staged through LDS in 128-byte
+//     K steps (double buffered, XOR-swizzled); every 256 elements of K the 16x16x32 bf16 MFMA
+//     partial sum is added into an fp32 accumulator (the matrix cores truncate inside their
+//     adder, so long chains are avoided).  Partial logits of each slice go to the workspace.
 //  2. select: one wave per token (lane l holds experts 4l..4l+3) sums the slices in a fixed
 //     order, forms s and z, picks the top-K by wave-wide argmax rounds (ties to the lower
 //     index) and measures the decision margin: the gap between the K-th and (K+1)-th z, and
@@ -34,8 +34,10 @@ namespace {
 
 constexpr uint32_t kNone = 0x7fffffffu;
 constexpr float kRefineGap = 4e-6f;  // fp32 decision margin below which a token is redone in fp64
-constexpr int kTM = 64;              // tokens per logits workgroup
-constexpr int kRows = 64 + 256;      // LDS rows per stage: 64 tokens + 256 router rows
+constexpr int kTM = 128;             // tokens per logits workgroup (the router rows are re-read once per kTM tokens)
+constexpr int kRows = kTM + 256;     // LDS rows per stage: kTM tokens + 256 router rows
+constexpr int kLogitsThreads = 512;  // 8 waves: 2 token halves x 4 expert quarters, 64 x 64 each
+constexpr int kChunks = kRows * 8 / kLogitsThreads;  // 16-byte chunks per thread per stage
 
 template <typename V>
 __device__ __forceinline__ bool beats(V v, uint32_t i, V bv, uint32_t bi) {
@@ -196,7 +198,7 @@ __device__ V select_token(const V u[4], const float* __restrict__ bias, int N, i
 }
 
 // ---- kernel 1: split-K logits ----
-__global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(kLogitsThreads) void route_logits_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ wr,
                                                            int T, int d, int N, int splits,
                                                            float* __restrict__ part,
@@ -205,19 +207,20 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __res
   if (blockIdx.x == 0 && threadIdx.x == 0) *n_flagged = 0;  // the select kernel appends after this one
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // token half, expert quarter
   const int tile = blockIdx.x / splits, split = blockIdx.x - tile * splits;
   const int t0 = tile * kTM;
   const int nsteps_all = d / 64;
   const int ks0 = (int)((int64_t)split * nsteps_all / splits);
   const int ks1 = (int)((int64_t)(split + 1) * nsteps_all / splits);
   const int cch = tid & 7;
-  // 10 chunks of 16 B per thread per stage: rows r = tid/8 + 32 i (i < 10): 0..63 tokens, 64.. router
-  const uint8_t* src[10];
-  bool live[10];
-  int dst[10];
+  // kChunks chunks of 16 B per thread per stage: rows r = tid/8 + 64 i: [0, kTM) tokens, then router
+  const uint8_t* src[kChunks];
+  bool live[kChunks];
+  int dst[kChunks];
 #pragma unroll
-  for (int i = 0; i < 10; ++i) {
-    const int r = (tid >> 3) + 32 * i;
+  for (int i = 0; i < kChunks; ++i) {
+    const int r = (tid >> 3) + (kLogitsThreads / 8) * i;
     if (r < kTM) {
       live[i] = t0 + r < T;
       src[i] = reinterpret_cast<const uint8_t*>(x + (int64_t)min(t0 + r, T - 1) * d) + cch * 16;
@@ -228,15 +231,15 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __res
     }
     dst[i] = r * 128 + ((cch ^ (r & 7)) << 4);
   }
-  u32x4 reg[10];
+  u32x4 reg[kChunks];
   auto gload = [&](int ks) {
 #pragma unroll
-    for (int i = 0; i < 10; ++i)
+    for (int i = 0; i < kChunks; ++i)
       reg[i] = live[i] ? *(const u32x4*)(src[i] + (int64_t)ks * 128) : u32x4{0u, 0u, 0u, 0u};
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 10; ++i) *(u32x4*)(smem + buf * STAGE + dst[i]) = reg[i];
+    for (int i = 0; i < kChunks; ++i) *(u32x4*)(smem + buf * STAGE + dst[i]) = reg[i];
   };
   f32x4 acc[4][4], prt[4][4];
 #pragma unroll
@@ -260,12 +263,12 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __res
       bf16x8_t af[4], bf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = i * 16 + lr;
+        const int r = wm * 64 + i * 16 + lr;
         af[i] = *(const bf16x8_t*)(S + r * 128 + ((ch ^ (r & 7)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = kTM + wave * 64 + j * 16 + lr;
+        const int r = kTM + wn * 64 + j * 16 + lr;
         bf[j] = *(const bf16x8_t*)(S + r * 128 + ((ch ^ (r & 7)) << 4));
       }
 #pragma unroll
@@ -290,10 +293,10 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __res
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = t0 + i * 16 + lg * 4 + r;
+      const int t = t0 + wm * 64 + i * 16 + lg * 4 + r;
       if (t < T) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[(int64_t)t * 256 + wave * 64 + j * 16 + lr] = acc[i][j][r];
+        for (int j = 0; j < 4; ++j) out[(int64_t)t * 256 + wn * 64 + j * 16 + lr] = acc[i][j][r];
       }
     }
 }
@@ -465,7 +468,7 @@ extern "C" moe_status moe_route(const uint16_t* x, const uint16_t* w_router, con
   const int tiles = (T + kTM - 1) / kTM;
   const int nb = (T + 63) / 64;
   if (T > 0) {
-    route_logits_kernel<<<tiles * S, 256, 0, stream>>>(x, w_router, T, d, n_experts, S, part, n_flagged);
+    route_logits_kernel<<<tiles * S, kLogitsThreads, 0, stream>>>(x, w_router, T, d, n_experts, S, part, n_flagged);
     route_select_kernel<<<(T + 3) / 4, 256, 0, stream>>>(part, S, bias, T, n_experts, top_k, n_group, topk_group,
                                                          topk_idx, topk_gate, scores, n_flagged, flagged);
     route_refine_kernel<<<T < 256 ? T : 256, kRefineWaves * 64, 0, stream>>>(
