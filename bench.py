@@ -8,8 +8,9 @@ tokens: route -> permute -> [fp8 quantisation of x] -> gate/up grouped GEMM + Sw
 down grouped GEMMs -> combine -> bias update.  Inputs and weights are resident in HBM
 before the timed region.  The headline workload is the DeepSeek-V3-shaped bf16 layer at
 T = 4096 tokens (d = 7168, 256 routed + 1 shared SwiGLU experts of width 2048, top-8);
-the fp8 layer at T = 16384 and the decode-shaped fp8 run (T = 256, Zipf-skewed bias, 100
-steps of the bias update) are reported in the same line under "secondary".
+the fp8 layer at T = 16384, the group-limited bf16 layer at T = 8192 and the decode-shaped
+fp8 run (T = 256, Zipf-skewed bias, 100 steps of the bias update) are reported in the same
+line under "secondary".
 
 Prints ONE JSON line.  Weights are random (no checkpoint); inputs are seeded synthetic data.
 """
@@ -330,6 +331,14 @@ def main():
                     "gate_up_mfma_frac": round(fl3 / (gu3 / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4)})
         log(f"[bench] {c3.name}: {ms3:.3f} ms/step")
         del l3
+        c2 = I.V3_GROUP
+        l2, _, _, _, ms2, _ = measure(c2, False, max(5, args.steps // 2), 3)
+        f2 = O.layer_flops(c2.T, c2.d, c2.n_experts, c2.top_k, c2.inter)
+        sec.append({"workload": c2.name, "dtype": "bf16", "ms_per_step": round(ms2, 4),
+                    "tokens_per_s": round(c2.T / (ms2 / 1e3), 1), "tflops": round(f2 / (ms2 / 1e3) / 1e12, 2),
+                    "mfma_frac_bf16_peak": round(f2 / (ms2 / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)})
+        log(f"[bench] {c2.name}: {ms2:.3f} ms/step")
+        del l2
         c4 = I.V3_DECODE
         n4 = args.decode_steps or c4.steps
         bias4 = I.gen_bias(c4)
