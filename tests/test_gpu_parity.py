@@ -227,6 +227,32 @@ def test_gemm_split_output(fp8, tail):
     assert torch.equal(main, ref_main) and torch.equal(tail_out, ref_tail)
 
 
+def test_gemm_empty_groups_and_many_groups():
+    """All groups empty: nothing is written.  1024 groups (the limit) of 0..5 rows each (the
+    decode-sized tile path): every group equals its own matmul."""
+    N, K = 256, 256
+    W = I.gen_normal(71, (4, N, K), 0.05).to(DEV)
+    A = I.gen_normal(72, (8, K), 1.0).to(DEV)
+    offs = torch.zeros(4, dtype=torch.int32, device=DEV)
+    out = torch.full((1, N), 7.0, dtype=torch.float32, device=DEV)
+    M().moe_grouped_gemm(A, W, offs, 0, 3, 0, out)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    G = 1024
+    sizes = np.random.default_rng(73).integers(0, 6, G)
+    o = _offsets(sizes)
+    rows = int(o[-1])
+    Wg = I.gen_normal(74, (G, 128, 128), 0.05)
+    Ag = I.gen_normal(75, (rows, 128), 1.0)
+    outg = torch.empty((rows, 128), dtype=torch.float32, device=DEV)
+    M().moe_grouped_gemm(Ag.to(DEV), Wg.to(DEV), torch.from_numpy(o).to(DEV), 0, G, rows, outg)
+    got, An, Wn = np64(outg), np64(Ag), np64(Wg)
+    for g in range(G):
+        if o[g + 1] > o[g]:
+            ref = An[o[g]:o[g + 1]] @ Wn[g].T
+            assert np.max(np.abs(got[o[g]:o[g + 1]] - ref)) <= 1e-5 * max(1.0, np.max(np.abs(ref))), g
+
+
 def test_gemm_subrange_and_plain_rows():
     """first_group > 0 and A indexed by the global sorted row (the shared-expert launch)."""
     G, N, K = 4, 128, 128
@@ -362,6 +388,23 @@ def test_combine(T, K, d):
     assert rel_err(np64(o_ns), O.combine(np64(y), None, pp.numpy(), gate.numpy().astype(np.float64))) < 1e-6
 
 
+def test_combine_skips_negative_pairs():
+    """pair rows < 0 (pairs dropped by the permutation) contribute nothing."""
+    T, K, d = 50, 4, 256
+    idx, gate = I.gen_routing(91, T, K, 16)
+    pp = np.random.default_rng(92).permutation(T * K).reshape(T, K).astype(np.int32)
+    pp[::3, 1] = -1
+    pp[7, :] = -1
+    y = I.gen_normal(93, (T * K, d), 1.0)
+    ysh = I.gen_normal(94, (T, d), 1.0, dtype=torch.float32)
+    o32 = M().moe_combine(y.to(DEV), ysh.to(DEV), torch.from_numpy(pp).to(DEV), gate.to(DEV), torch.float32)
+    g = gate.numpy().astype(np.float64).copy()
+    g[pp < 0] = 0.0
+    ref = O.combine(np64(y), np64(ysh), np.maximum(pp, 0), g)
+    assert rel_err(np64(o32), ref) < 1e-6
+    assert np.array_equal(np64(o32)[7], np64(ysh)[7])
+
+
 def test_bias_update_bitexact():
     N, T, K = 256, 4096, 8
     rng = np.random.default_rng(9)
@@ -452,6 +495,22 @@ def test_layer_fp8(cfg):
     err = rel_err(np64(out32)[keep], ref[keep])
     say(f"  staged: h codes equal to the oracle's {same:.5f}, output from the device h {staged:.2e} "
         f"(tol {FP8_TOL}); end to end vs the oracle's fp8 pipeline {err:.2e}")
+
+
+@pytest.mark.parametrize("T", [1, 129])
+def test_layer_bf16_token_counts(T):
+    """A single token (every expert group but K + 1 empty) and a ragged token count."""
+    cfg = I.small(I.V3_BF16, name=f"tok{T}", T=T, d=256, n_experts=32, top_k=4, inter=128, w_std=0.05, router_std=0.05)
+    x, wr, bias, W13, W2 = _layer_case(cfg)
+    layer = M().MoELayer(wr.to(DEV), W13.to(DEV), W2.to(DEV), bias.to(DEV), cfg.top_k)
+    out32, buf = layer.forward(x.to(DEV), out_dtype=torch.float32, keep=True)
+    x64 = np64(x)
+    r = O.route(x64, np64(wr), bias.numpy(), cfg.top_k)
+    tie = check_route(buf["topk_idx"], buf["topk_gate"], buf["expert_counts"], None, r, cfg.n_experts, cfg.top_k)
+    W13n, W2n = np64(W13), np64(W2)
+    ref, _ = O.forward_sparse(x64, r["idx"], r["gate"], cfg.n_experts, lambda e: (W13n[e], W2n[e]), "bf16")
+    keep = ~tie
+    assert rel_err(np64(out32)[keep], ref[keep]) <= BF16_TOL
 
 
 def test_layer_bias_update_loop():
