@@ -134,14 +134,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   constexpr int A_BYTES = BM * 128, STAGE = (BM + BN) * 128;
   constexpr int A_PW = BM / 8 / NW;               // A DMA instructions per wave per stage
   constexpr int B_PW = BN / 8 / NW;               // B DMA instructions per wave per stage
-  // A scales arrive in chunks of SC_CH K blocks: [BM rows][SC_CH] floats, one 4-byte DMA per
-  // lane, SC_PW instructions per wave per chunk, into one of SC_NB LDS buffers in turn.  A
+  // Scales arrive in chunks of SC_CH K blocks, one 4-byte DMA per lane, into one of SC_NB LDS
+  // buffers in turn: BM * SC_CH A scales (SC_PW instructions per wave) and, from wave 0, the
+  // two weight-block scales of the tile's columns for the same K blocks (SC_WS floats).  A
   // chunk's DMA is issued STAGES - 1 steps before its first step and overwrites the chunk
   // SC_NB earlier, whose last step is at least SC_NB steps back: SC_NB = STAGES keeps it behind
   // the barrier of the issuing step.
   constexpr int SC_CH = 8;
   constexpr int SC_NB = STAGES;
   constexpr int SC_PW = FP8 ? BM * SC_CH / 64 / NW : 0;
+  constexpr int SC_WS = 64;                      // weight-scale area: [SC_CH][2] used, one DMA wide
+  constexpr int SC_BUF = BM * SC_CH + SC_WS;     // floats per chunk buffer
   constexpr int OC = SWIGLU ? BN / 2 : BN;
   constexpr int L_STAGE = A_PW + B_PW;  // data DMA instructions per wave per stage (a scale chunk adds SC_PW)
   static_assert(A_PW * 8 * NW == BM && B_PW * 8 * NW == BN, "DMA instructions must split evenly over waves");
@@ -150,6 +153,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   static_assert(!SWIGLU || TN % 2 == 0, "SwiGLU waves need matching gate and up tiles");
   static_assert(OUT != OUT_FP8 || (FP8 && SWIGLU && OC == 128), "fp8 output = one 1x128 tile per row");
   static_assert(!FP8 || (SWIGLU ? WN / 2 <= 128 : WN <= 128), "a wave must sit inside one 128-row scale block");
+  static_assert(!FP8 || (BN == 256 && TM == 4), "E4M3 tiles: two 128-row weight blocks, 4 row tiles per wave");
   static_assert(STAGES == 2 || STAGES == 3, "the ring has two or three slots");
   // Round synchronisation pays where a round's workgroups share most of their operands and
   // the launch is bandwidth-bound: the bf16 gate/up projection with 128-row blocks (the
@@ -164,8 +168,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t slot2[STAGES > 2 ? STAGE : 16];
-  // A scales: SC_NB chunk buffers, used in turn over the sequence of chunks this workgroup loads
-  __shared__ __attribute__((aligned(16))) float s_sc[FP8 ? SC_NB * BM * SC_CH : 1];
+  // scales: SC_NB chunk buffers, used in turn over the sequence of chunks this workgroup loads
+  __shared__ __attribute__((aligned(16))) float s_sc[FP8 ? SC_NB * SC_BUF : 1];
   __shared__ float s_red[OUT == OUT_FP8 ? WGN * BM : 1];
   __shared__ int s_tstart[kMaxGroups + 1];
   __shared__ int s_offs[kMaxGroups + 1];
@@ -235,12 +239,26 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   int b_off[B_PW];
   const float* s_ptr[SC_PW > 0 ? SC_PW : 1];
   int s_nxt[SC_PW > 0 ? SC_PW : 1];
-  // LDS slot (row, c) of a chunk holds K block c ^ ((row >> 2) & 7): the four row groups a
-  // scale read touches then sit in distinct banks
+  // A-scale chunk layout: [BM / 4 row groups][SC_CH K blocks, swizzled][4 rows].  Row group
+  // g = wm * 16 + lr holds rows wm * WM + i * 16 + lr (i = 0..3), the four rows whose products
+  // one lane accumulates, so a K step reads its four scales with one 16-byte LDS read; the K
+  // block slot is XORed with (g & 7) to spread the 16 row groups of a read over the banks.
+  // DMA lane (instruction q, lane l) fills dword d = q * 64 + l: row group d / 32, slot
+  // (d / 4) % 8, row index d % 4; its 8 consecutive slots of a row read 32 contiguous bytes.
   static_assert(SC_CH == 8, "the scale swizzle assumes 8 K blocks per chunk");
   int sc_col[SC_PW > 0 ? SC_PW : 1];  // K block (within a chunk) that each scale DMA of this lane fetches
+  int sc_row[SC_PW > 0 ? SC_PW : 1];  // tile row that each scale DMA of this lane fetches
 #pragma unroll
-  for (int i = 0; i < SC_PW; ++i) sc_col[i] = (lane % SC_CH) ^ ((((wave * SC_PW + i) * 64 + lane) / SC_CH >> 2) & 7);
+  for (int i = 0; i < SC_PW; ++i) {
+    const int d = (wave * SC_PW + i) * 64 + lane;
+    const int grp = d >> 5;
+    sc_col[i] = ((d >> 2) & 7) ^ (grp & 7);
+    sc_row[i] = (grp >> 4) * WM + (d & 3) * 16 + (grp & 15);
+  }
+  // weight-block scales (wave 0): lane l loads K block (l & 15) >> 1 of block (l & 1) -- the
+  // gate and up blocks under SwiGLU, else the tile's two 128-column blocks; lanes 16..63
+  // repeat lanes 0..15 into the padding
+  const float* w_sc_ptr = p.w_scale;
   int sc_issue = 0;                 // buffer of the next chunk to issue
   int lq = -1;  // index (in this workgroup's list) of the tile being loaded
   const uint8_t* wbase = p.w;
@@ -256,8 +274,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     }
 #pragma unroll
     for (int i = 0; i < SC_PW; ++i) {
-      const int rr = ((wave * SC_PW + i) * 64 + lane) / SC_CH;
-      const int r = t.row0 + min(rr, t.nrows - 1);
+      const int r = t.row0 + min(sc_row[i], t.nrows - 1);
       sdst[i] = p.a_rows ? p.a_rows[r] : r;
     }
   };
@@ -280,6 +297,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       b_off[i] = (int)(n * p.w_row_b) + ((cch ^ (rr & 7)) << 4);
     }
     wbase = p.w + (int64_t)(p.first_group + t.g) * p.N * p.w_row_b;
+    if (FP8) {
+      const int sel = lane & 1;
+      const int nblk = SWIGLU ? (sel ? p.N / 2 + t.nt * (BN / 2) : t.nt * (BN / 2)) / 128 : (t.nt * BN) / 128 + sel;
+      w_sc_ptr = p.w_scale + ((int64_t)(p.first_group + t.g) * (p.N / 128) + nblk) * p.ksb + ((lane & 15) >> 1);
+    }
   };
   // issue the DMA of global step js (clamped to the last step: every step issues one batch,
   // so the number of batches in flight is constant) into ring slot SL
@@ -304,12 +326,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       __builtin_amdgcn_global_load_lds((glb_void*)(bb + (uint32_t)b_off[i]),
                                        (lds_void*)(st + A_BYTES + (wave * B_PW + i) * 1024), 16, 0, 0);
     if (FP8 && !past_end && kt % SC_CH == 0) {
-      // the A scales of K blocks [kt, kt + SC_CH) of the tile's rows (clamped to the last block)
-      float* sc = s_sc + sc_issue * (BM * SC_CH);
+      // the scales of K blocks [kt, kt + SC_CH) of the tile's rows and weight blocks (clamped
+      // to the last block)
+      float* sc = s_sc + sc_issue * SC_BUF;
 #pragma unroll
       for (int i = 0; i < SC_PW; ++i)
         __builtin_amdgcn_global_load_lds((glb_void*)(s_ptr[i] + min(kt + sc_col[i], p.ksb - 1)),
                                          (lds_void*)(sc + (wave * SC_PW + i) * 64), 4, 0, 0);
+      if (wave == 0)
+        __builtin_amdgcn_global_load_lds((glb_void*)(w_sc_ptr + min(kt, p.ksb - 1 - ((lane & 15) >> 1))),
+                                         (lds_void*)(sc + BM * SC_CH), 4, 0, 0);
       sc_issue = sc_issue + 1 == SC_NB ? 0 : sc_issue + 1;
     }
   };
@@ -326,35 +352,20 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
 
   // ---- compute state ----
   const int lr = lane & 15, lg = lane >> 4;
-  int a_row[TM], b_row[TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) a_row[i] = wm * WM + i * 16 + lr;
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    if (SWIGLU) b_row[j] = (j < TN / 2) ? wn * (WN / 2) + j * 16 + lr : BN / 2 + wn * (WN / 2) + (j - TN / 2) * 16 + lr;
-    else b_row[j] = wn * WN + j * 16 + lr;
-  }
   f32x4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
   TileInfo ct = tile_of(0);
-  const float* sw_a = p.w_scale;
-  const float* sw_b = p.w_scale;
-  auto set_scales = [&]() {
-    if (FP8) {
-      const float* swg = p.w_scale + (int64_t)(p.first_group + ct.g) * (p.N / 128) * p.ksb;
-      if (SWIGLU) {
-        sw_a = swg + (int64_t)((ct.nt * (BN / 2) + wn * (WN / 2)) / 128) * p.ksb;
-        sw_b = swg + (int64_t)((p.N / 2 + ct.nt * (BN / 2) + wn * (WN / 2)) / 128) * p.ksb;
-      } else {
-        sw_a = swg + (int64_t)((ct.nt * BN + wn * WN) / 128) * p.ksb;
-        sw_b = sw_a;
-      }
-    }
-  };
-  set_scales();
+  // operand reads: row & 7 = lr & 7 for every row a lane reads (tile offsets are multiples of
+  // 16), so its two swizzled 16-byte chunks (lg and lg + 4) sit at fixed byte offsets lo / hi
+  // from the row start and every read is one base register plus a constant
+  const int sw_lo = (lg ^ (lr & 7)) << 4, sw_hi = sw_lo ^ 64;
+  const int fa_lo = (wm * WM + lr) * 128 + sw_lo, fa_hi = (wm * WM + lr) * 128 + sw_hi;
+  const int fb_row = SWIGLU ? wn * (WN / 2) + lr : wn * WN + lr;
+  const int fb_lo = fb_row * 128 + sw_lo, fb_hi = fb_row * 128 + sw_hi;
+  const int fs_off = (wm * 16 + lr) * (SC_CH * 4);  // this lane's scale row group
   const int base_row = s_offs[0];
   int sc_use = 0;  // buffer of the chunk being consumed (same sequence as sc_issue)
 
@@ -385,12 +396,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     if (!FP8) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int ch = ks * 4 + lg;
         bf16x8_t af[TM], bfr[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = *(const bf16x8_t*)(As + a_row[i] * 128 + ((ch ^ (a_row[i] & 7)) << 4));
+        for (int i = 0; i < TM; ++i) af[i] = *(const bf16x8_t*)(As + (ks ? fa_hi : fa_lo) + i * 16 * 128);
 #pragma unroll
-        for (int jj = 0; jj < TN; ++jj) bfr[jj] = *(const bf16x8_t*)(Bs + b_row[jj] * 128 + ((ch ^ (b_row[jj] & 7)) << 4));
+        for (int jj = 0; jj < TN; ++jj) {
+          const int ro = (SWIGLU && jj >= TN / 2 ? BN / 2 + (jj - TN / 2) * 16 : jj * 16) * 128;
+          bfr[jj] = *(const bf16x8_t*)(Bs + (ks ? fb_hi : fb_lo) + ro);
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -399,61 +412,58 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     } else {
       // a lane's 32 bytes of the 128-element K slice are chunks lg and lg + 4 (the same K
       // permutation for A and B leaves the product unchanged); each read then covers the 16
-      // lanes' rows at distinct swizzled chunks, like the bf16 path, and hits distinct banks
-      const int ch = lg;
+      // lanes' rows at distinct swizzled chunks and hits distinct banks
       i32x8 af[TM], bfr[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const uint8_t* rowp = As + a_row[i] * 128;
-        const u32x4 lo = *(const u32x4*)(rowp + ((ch ^ (a_row[i] & 7)) << 4));
-        const u32x4 hi = *(const u32x4*)(rowp + (((ch + 4) ^ (a_row[i] & 7)) << 4));
+        const u32x4 lo = *(const u32x4*)(As + fa_lo + i * 16 * 128);
+        const u32x4 hi = *(const u32x4*)(As + fa_hi + i * 16 * 128);
         af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
 #pragma unroll
       for (int jj = 0; jj < TN; ++jj) {
-        const uint8_t* rowp = Bs + b_row[jj] * 128;
-        const u32x4 lo = *(const u32x4*)(rowp + ((ch ^ (b_row[jj] & 7)) << 4));
-        const u32x4 hi = *(const u32x4*)(rowp + (((ch + 4) ^ (b_row[jj] & 7)) << 4));
+        const int ro = (SWIGLU && jj >= TN / 2 ? BN / 2 + (jj - TN / 2) * 16 : jj * 16) * 128;
+        const u32x4 lo = *(const u32x4*)(Bs + fb_lo + ro);
+        const u32x4 hi = *(const u32x4*)(Bs + fb_hi + ro);
         bfr[jj] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
-      // weight-block scales: wave-uniform addresses, read through the scalar cache
-      typedef __attribute__((address_space(4))) const float cfloat;
-      const float swa = *(cfloat*)(uintptr_t)(sw_a + kt);
-      const float swb = *(cfloat*)(uintptr_t)(sw_b + kt);
-      // combined per-row scales s_A * s_W of this K block
-      float sca[TM][4], scb[TM][4];
+      // this K block's scales: s_A of the lane's four rows (one 16-byte read) and the two
+      // weight-block scales (one broadcast read)
+      const int kc = kt % SC_CH;
+      const float* scb = s_sc + sc_use * SC_BUF;
+      const f32x4 sa = *(const f32x4*)(scb + fs_off + ((kc ^ (lr & 7)) << 2));
+      const float* swp = scb + BM * SC_CH + 2 * kc;
+      const float sw0 = SWIGLU || (wn * WN) / 128 == 0 ? swp[0] : swp[1], sw1 = swp[1];
+      float s0[TM], s1[TM];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int srow = wm * WM + i * 16 + lg * 4 + r;
-          const float sa = s_sc[sc_use * (BM * SC_CH) + srow * SC_CH + ((kt % SC_CH) ^ ((srow >> 2) & 7))];
-          sca[i][r] = sa * swa;
-          scb[i][r] = sa * swb;
-        }
-      // every tile's partial sum gets its own registers and its promotion (fp32 FMA into the
+      for (int i = 0; i < TM; ++i) {
+        s0[i] = sa[i] * sw0;
+        s1[i] = SWIGLU ? sa[i] * sw1 : s0[i];
+      }
+      // products with W as the first operand: a lane's four results of tile (i, jj) are
+      // columns lg * 4 .. lg * 4 + 3 of row lr, so one combined scale s_A * s_W covers them.
+      // Every tile's partial sum gets its own registers and its promotion (fp32 FMA into the
       // accumulator) trails the matrix core by two tiles, so MFMAs issue back to back while
       // the VALU promotes the previous results
       constexpr int NT = TM * TN;
       f32x4 pq[NT];
 #pragma unroll
       for (int t = 0; t < NT + 2; ++t) {
-        if (t < NT) pq[t] = mfma_fp8(af[t / TN], bfr[t % TN], f32x4{0.f, 0.f, 0.f, 0.f});
+        if (t < NT) pq[t] = mfma_fp8(bfr[t % TN], af[t / TN], f32x4{0.f, 0.f, 0.f, 0.f});
         if (t >= 2) {
           const int u = t - 2, i = u / TN, jj = u % TN;
-          const bool up = SWIGLU && jj >= TN / 2;
+          const float sc = SWIGLU && jj >= TN / 2 ? s1[i] : s0[i];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][jj][r] = fmaf(pq[u][r], up ? scb[i][r] : sca[i][r], acc[i][jj][r]);
+          for (int r = 0; r < 4; ++r) acc[i][jj][r] = fmaf(pq[u][r], sc, acc[i][jj][r]);
         }
       }
-      if (kt % SC_CH == SC_CH - 1 || kt == ksteps - 1) sc_use = sc_use + 1 == SC_NB ? 0 : sc_use + 1;  // chunk done
+      if (kc == SC_CH - 1 || kt == ksteps - 1) sc_use = sc_use + 1 == SC_NB ? 0 : sc_use + 1;  // chunk done
     }
 
     if (kt == ksteps - 1) {
       // ---- epilogue of tile ct ----
       constexpr int TO = SWIGLU ? TN / 2 : TN;
       const int64_t orow0 = (int64_t)(ct.row0 - base_row);
-      const int col_w = (SWIGLU ? wn * (WN / 2) : wn * WN) + lr;
       float v[TM][TO][4];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -461,63 +471,100 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
         for (int jj = 0; jj < TO; ++jj)
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[i][jj][r] = SWIGLU ? silu(acc[i][jj][r]) * acc[i][jj + TO][r] : acc[i][jj][r];
-      if (OUT == OUT_FP8) {
+      if constexpr (FP8) {
+        // E4M3 layout: lane holds row wm * WM + i * 16 + lr, columns col_w + jj * 16 + 0..3
+        const int col_w = (SWIGLU ? wn * (WN / 2) : wn * WN) + lg * 4;
+        if (OUT == OUT_FP8) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
+          for (int i = 0; i < TM; ++i) {
             float mx = 0.f;
 #pragma unroll
-            for (int jj = 0; jj < TO; ++jj) mx = fmaxf(mx, fabsf(v[i][jj][r]));
-            mx = max16(mx);
-            s_red[wn * BM + wm * WM + i * 16 + lg * 4 + r] = mx;  // the 16 lanes agree
+            for (int jj = 0; jj < TO; ++jj)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(v[i][jj][r]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            if (lg == 0) s_red[wn * BM + wm * WM + i * 16 + lr] = mx;  // the 4 lanes of the row agree
           }
-        MOE_BARRIER();
-      }
+          MOE_BARRIER();
+        }
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = wm * WM + i * 16 + lg * 4 + r;
-          float s = 1.0f;
-          if (OUT == OUT_FP8) {
-            float amax = 0.f;
-#pragma unroll
-            for (int q = 0; q < WGN; ++q) amax = fmaxf(amax, s_red[q * BM + m]);
-            s = (amax == 0.f) ? 1.0f : amax / 448.0f;
-          }
-          const float rs = recip_refined(s);
+        for (int i = 0; i < TM; ++i) {
+          const int m = wm * WM + i * 16 + lr;
+          const int c0 = ct.nt * OC + col_w;
           if (OUT == OUT_BF16 && !SWIGLU && ct.g >= p.tail_first) {
             // split output: this group's rows go to the f32 tail
             if (m < ct.nrows) {
               float* trow = reinterpret_cast<float*>(p.out_tail + (int64_t)(ct.row0 - s_offs[p.tail_first] + m) * p.ldo_tail_b);
-              const int c0 = ct.nt * OC + col_w;
 #pragma unroll
-              for (int jj = 0; jj < TO; ++jj) trow[c0 + jj * 16] = v[i][jj][r];
+              for (int jj = 0; jj < TO; ++jj)
+                *reinterpret_cast<f32x4*>(trow + c0 + jj * 16) = f32x4{v[i][jj][0], v[i][jj][1], v[i][jj][2], v[i][jj][3]};
+            }
+          } else if (OUT == OUT_FP8) {
+            float amax = 0.f;
+#pragma unroll
+            for (int q = 0; q < WGN; ++q) amax = fmaxf(amax, s_red[q * BM + m]);
+            const float s = (amax == 0.f) ? 1.0f : amax / 448.0f;
+            const float rs = recip_refined(s);
+            if (m < ct.nrows) {
+              uint8_t* orow = p.out + (orow0 + m) * p.ldo_b;
+#pragma unroll
+              for (int jj = 0; jj < TO; ++jj) {
+                uint32_t w4 = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) w4 |= f32_to_e4m3(quotient(v[i][jj][r], s, rs)) << (8 * r);
+                *reinterpret_cast<uint32_t*>(orow + c0 + jj * 16) = w4;
+              }
+              if (wn == 0 && lg == 0) p.out_scale[(orow0 + m) * p.out_scale_ld + ct.nt] = s;
             }
           } else if (m < ct.nrows) {
             uint8_t* orow = p.out + (orow0 + m) * p.ldo_b;
-            const int c0 = ct.nt * OC + col_w;
 #pragma unroll
             for (int jj = 0; jj < TO; ++jj) {
-              const int c = c0 + jj * 16;
-              if (OUT == OUT_F32) reinterpret_cast<float*>(orow)[c] = v[i][jj][r];
-              else if (OUT == OUT_BF16) reinterpret_cast<uint16_t*>(orow)[c] = (uint16_t)f32_to_bf16_rne(v[i][jj][r]);
-              else orow[c] = (uint8_t)f32_to_e4m3(quotient(v[i][jj][r], s, rs));
+              if (OUT == OUT_F32)
+                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(orow) + c0 + jj * 16) =
+                    f32x4{v[i][jj][0], v[i][jj][1], v[i][jj][2], v[i][jj][3]};
+              else
+                *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(orow) + c0 + jj * 16) =
+                    u32x2{f32_to_bf16_rne(v[i][jj][0]) | (f32_to_bf16_rne(v[i][jj][1]) << 16),
+                          f32_to_bf16_rne(v[i][jj][2]) | (f32_to_bf16_rne(v[i][jj][3]) << 16)};
             }
-            if (OUT == OUT_FP8 && wn == 0 && lr == 0) p.out_scale[(orow0 + m) * p.out_scale_ld + ct.nt] = s;
           }
         }
-      if (OUT == OUT_FP8) MOE_BARRIER();  // s_red is rewritten by the next tile
+        if (OUT == OUT_FP8) MOE_BARRIER();  // s_red is rewritten by the next tile
+      } else {
+        // bf16 layout: lane holds rows wm * WM + i * 16 + lg * 4 + r, column col_w + jj * 16
+        const int col_w = (SWIGLU ? wn * (WN / 2) : wn * WN) + lr;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = wm * WM + i * 16 + lg * 4 + r;
+            const int c0 = ct.nt * OC + col_w;
+            if (OUT == OUT_BF16 && !SWIGLU && ct.g >= p.tail_first) {
+              // split output: this group's rows go to the f32 tail
+              if (m < ct.nrows) {
+                float* trow = reinterpret_cast<float*>(p.out_tail + (int64_t)(ct.row0 - s_offs[p.tail_first] + m) * p.ldo_tail_b);
+#pragma unroll
+                for (int jj = 0; jj < TO; ++jj) trow[c0 + jj * 16] = v[i][jj][r];
+              }
+            } else if (m < ct.nrows) {
+              uint8_t* orow = p.out + (orow0 + m) * p.ldo_b;
+#pragma unroll
+              for (int jj = 0; jj < TO; ++jj) {
+                const int c = c0 + jj * 16;
+                if (OUT == OUT_F32) reinterpret_cast<float*>(orow)[c] = v[i][jj][r];
+                else reinterpret_cast<uint16_t*>(orow)[c] = (uint16_t)f32_to_bf16_rne(v[i][jj][r]);
+              }
+            }
+          }
+      }
       // next tile of the compute side
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (j + 1 < total_steps) {
-        ct = tile_of((j + 1) / ksteps);
-        set_scales();
-      }
+      if (j + 1 < total_steps) ct = tile_of((j + 1) / ksteps);
     }
   };
 
