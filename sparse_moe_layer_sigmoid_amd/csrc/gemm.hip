@@ -103,6 +103,14 @@ struct TileInfo {
   int nrows;  // valid rows (1..BM)
 };
 
+typedef __attribute__((address_space(4))) const int32_t cint32;
+
+// A wave-uniform read of a group offset through the scalar cache (the offsets are not written
+// by the kernel; scalar loads keep them off the vector-memory counter the DMA ring waits on).
+__device__ __forceinline__ int load_offset(const int32_t* offs, int g) {
+  return *(cint32*)(uintptr_t)(offs + __builtin_amdgcn_readfirstlane(g));
+}
+
 // Decode logical tile L (order: group, column block, row block) from the LDS prefix table.
 template <int BM>
 __device__ __forceinline__ TileInfo decode_tile(int L, const int* tstart, int G, const int32_t* offs) {
@@ -114,7 +122,7 @@ __device__ __forceinline__ TileInfo decode_tile(int L, const int* tstart, int G,
   }
   const int g = lo;
   const int local = L - tstart[g];
-  const int m0 = offs[g], m1 = offs[g + 1];
+  const int m0 = load_offset(offs, g), m1 = load_offset(offs, g + 1);
   const int mt_g = (m1 - m0 + BM - 1) / BM;
   TileInfo t;
   t.g = g;
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   constexpr int SC_CH = 8;
   constexpr int SC_NB = STAGES;
   constexpr int SC_PW = FP8 ? BM * SC_CH / 64 / NW : 0;
-  constexpr int SC_WS = 64;                      // weight-scale area: [SC_CH][2] used, one DMA wide
+  constexpr int SC_WS = 2 * SC_CH;               // weight-scale area: [SC_CH][2]
   constexpr int SC_BUF = BM * SC_CH + SC_WS;     // floats per chunk buffer
   constexpr int OC = SWIGLU ? BN / 2 : BN;
   constexpr int L_STAGE = A_PW + B_PW;  // data DMA instructions per wave per stage (a scale chunk adds SC_PW)
@@ -171,16 +179,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   // scales: SC_NB chunk buffers, used in turn over the sequence of chunks this workgroup loads
   __shared__ __attribute__((aligned(16))) float s_sc[FP8 ? SC_NB * SC_BUF : 1];
   __shared__ float s_red[OUT == OUT_FP8 ? WGN * BM : 1];
-  __shared__ int s_tstart[kMaxGroups + 1];
-  __shared__ int s_offs[kMaxGroups + 1];
+  // tile prefix table (G + 1 ints), sized at launch
+  extern __shared__ int s_tstart[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave - wm * WGN;
   const int G = p.n_groups;
 
-  // ---- tile table: group offsets and exclusive prefix of (row blocks x column blocks) ----
-  for (int g = tid; g <= G; g += NW * 64) s_offs[g] = p.offs[g];
+  // ---- tile table: exclusive prefix of (row blocks x column blocks) over the groups ----
   if (wave == 0) {
     const int per = (G + 63) >> 6;
     const int g0 = min(G, lane * per), g1 = min(G, g0 + per);
@@ -242,7 +249,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   // A-scale chunk layout: [BM / 4 row groups][SC_CH K blocks, swizzled][4 rows].  Row group
   // g = wm * 16 + lr holds rows wm * WM + i * 16 + lr (i = 0..3), the four rows whose products
   // one lane accumulates, so a K step reads its four scales with one 16-byte LDS read; the K
-  // block slot is XORed with (g & 7) to spread the 16 row groups of a read over the banks.
+  // block slot is XORed with ((g >> 1) & 7), which puts the 16 row groups of a read (two per
+  // 256-byte bank row) on distinct banks.
   // DMA lane (instruction q, lane l) fills dword d = q * 64 + l: row group d / 32, slot
   // (d / 4) % 8, row index d % 4; its 8 consecutive slots of a row read 32 contiguous bytes.
   static_assert(SC_CH == 8, "the scale swizzle assumes 8 K blocks per chunk");
@@ -252,18 +260,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   for (int i = 0; i < SC_PW; ++i) {
     const int d = (wave * SC_PW + i) * 64 + lane;
     const int grp = d >> 5;
-    sc_col[i] = ((d >> 2) & 7) ^ (grp & 7);
+    sc_col[i] = ((d >> 2) & 7) ^ ((grp >> 1) & 7);
     sc_row[i] = (grp >> 4) * WM + (d & 3) * 16 + (grp & 15);
   }
-  // weight-block scales (wave 0): lane l loads K block (l & 15) >> 1 of block (l & 1) -- the
-  // gate and up blocks under SwiGLU, else the tile's two 128-column blocks; lanes 16..63
-  // repeat lanes 0..15 into the padding
+  // weight-block scales (lanes 0..15 of wave 0): lane l loads K block l >> 1 of block l & 1 --
+  // the gate and up blocks under SwiGLU, else the tile's two 128-column blocks
   const float* w_sc_ptr = p.w_scale;
   int sc_issue = 0;                 // buffer of the next chunk to issue
   int lq = -1;  // index (in this workgroup's list) of the tile being loaded
   const uint8_t* wbase = p.w;
 
-  auto tile_of = [&](int q) { return decode_tile<BM>(t_begin + slot + q * per_xcd, s_tstart, G, s_offs); };
+  auto tile_of = [&](int q) { return decode_tile<BM>(t_begin + slot + q * per_xcd, s_tstart, G, p.offs); };
   // gather sources of a tile's rows (global loads whose values are used one tile later)
   auto fetch_rows = [&](const TileInfo& t, int* dst, int* sdst) {
 #pragma unroll
@@ -305,9 +312,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   };
   // issue the DMA of global step js (clamped to the last step: every step issues one batch,
   // so the number of batches in flight is constant) into ring slot SL
-  auto issue = [&](auto slot_c, int js) {
-    constexpr int SL = decltype(slot_c)::value;
-    uint8_t* st = SL == 0 ? slot0 : (SL == 1 ? slot1 : slot2);
+  int dma_kt = 0;            // K step of the batch being issued
+  bool dma_scales = false;   // the batch starts a scale chunk
+  // tile bookkeeping for the batch of global step js (clamped to the last step: every step
+  // issues one batch, so the number of batches in flight is constant)
+  auto issue_prep = [&](int js) __attribute__((always_inline)) {
     const bool past_end = js >= total_steps;
     js = min(js, total_steps - 1);
     const int q = js / ksteps, kt = js - q * ksteps;
@@ -317,28 +326,59 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       if (q + 1 < n_my) fetch_rows(tile_of(q + 1), a_nxt, s_nxt);
       lq = q;
     }
-#pragma unroll
-    for (int i = 0; i < A_PW; ++i)
-      __builtin_amdgcn_global_load_lds((glb_void*)(a_ptr[i] + kt * 128), (lds_void*)(st + (wave * A_PW + i) * 1024), 16, 0, 0);
-    const uint8_t* bb = wbase + kt * 128;
-#pragma unroll
-    for (int i = 0; i < B_PW; ++i)
-      __builtin_amdgcn_global_load_lds((glb_void*)(bb + (uint32_t)b_off[i]),
+    dma_kt = kt;
+    dma_scales = FP8 && !past_end && kt % SC_CH == 0;
+  };
+  // data DMA instruction k (0 .. L_STAGE - 1: A rows, then B rows) of the prepared batch into
+  // ring slot SL
+  auto issue_one = [&](auto slot_c, int k) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    uint8_t* st = SL == 0 ? slot0 : (SL == 1 ? slot1 : slot2);
+    if (k < A_PW) {
+      __builtin_amdgcn_global_load_lds((glb_void*)(a_ptr[k] + dma_kt * 128), (lds_void*)(st + (wave * A_PW + k) * 1024), 16, 0, 0);
+    } else {
+      const int i = k - A_PW;
+      __builtin_amdgcn_global_load_lds((glb_void*)(wbase + dma_kt * 128 + (uint32_t)b_off[i]),
                                        (lds_void*)(st + A_BYTES + (wave * B_PW + i) * 1024), 16, 0, 0);
-    if (FP8 && !past_end && kt % SC_CH == 0) {
-      // the scales of K blocks [kt, kt + SC_CH) of the tile's rows and weight blocks (clamped
-      // to the last block)
+    }
+  };
+  // the scales of K blocks [kt, kt + SC_CH) of the tile's rows and weight blocks (clamped to
+  // the last block), when the prepared batch starts a chunk
+  auto issue_scales = [&]() __attribute__((always_inline)) {
+    if (dma_scales) {
+      const int kt = dma_kt;
       float* sc = s_sc + sc_issue * SC_BUF;
 #pragma unroll
       for (int i = 0; i < SC_PW; ++i)
         __builtin_amdgcn_global_load_lds((glb_void*)(s_ptr[i] + min(kt + sc_col[i], p.ksb - 1)),
                                          (lds_void*)(sc + (wave * SC_PW + i) * 64), 4, 0, 0);
-      if (wave == 0)
+      if (wave == 0 && lane < SC_WS)
         __builtin_amdgcn_global_load_lds((glb_void*)(w_sc_ptr + min(kt, p.ksb - 1 - ((lane & 15) >> 1))),
                                          (lds_void*)(sc + BM * SC_CH), 4, 0, 0);
       sc_issue = sc_issue + 1 == SC_NB ? 0 : sc_issue + 1;
     }
   };
+  // the whole batch at once (the ring's first steps)
+  auto issue = [&](auto slot_c, int js) __attribute__((always_inline)) {
+    issue_prep(js);
+#pragma unroll
+    for (int k = 0; k < L_STAGE; ++k) issue_one(slot_c, k);
+    issue_scales();
+  };
+  // Inside a step the batch's instructions are spread over the MFMA sequence (instruction k
+  // after MFMA dma_pos(k, n) of n), each fenced so the compiler keeps it there: a wave that
+  // issued its whole batch at once would stall until the texture unit had taken it
+  // (~16 cycles per 1 KB instruction per CU), while spread out they queue behind nothing.
+  auto dma_in = [&](auto slot_c, int t, int n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < L_STAGE; ++k)
+      if (t == (k + 1) * n / (L_STAGE + 1)) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_one(slot_c, k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+
 
   // rows of the first tile (the ring is empty, so waiting for them costs nothing)
   {
@@ -366,158 +406,132 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   const int fb_row = SWIGLU ? wn * (WN / 2) + lr : wn * WN + lr;
   const int fb_lo = fb_row * 128 + sw_lo, fb_hi = fb_row * 128 + sw_hi;
   const int fs_off = (wm * 16 + lr) * (SC_CH * 4);  // this lane's scale row group
-  const int base_row = s_offs[0];
+  const int base_row = load_offset(p.offs, 0);
+  const int tail_row = load_offset(p.offs, min(p.tail_first, G));
   int sc_use = 0;  // buffer of the chunk being consumed (same sequence as sc_issue)
 
-  // one step: wait for its DMA (STAGES - 2 later batches stay in flight), issue the DMA
-  // STAGES - 1 steps ahead into the slot read last step, multiply, and finish the tile on
-  // its last step
-  auto step = [&](auto slot_c, int j) {
-    constexpr int SL = decltype(slot_c)::value;
-    const uint8_t* As = SL == 0 ? slot0 : (SL == 1 ? slot1 : slot2);
-    const int kt = j % ksteps;
-    if (kRoundSync && kt == 0 && j > 0) {  // a new round: arrive for the last one, wait for the XCD
-      if (tid == 0) {
-        const int q = j / ksteps;
-        __hip_atomic_fetch_add(&g_round_sync[xcd], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned int tgt = round_target(q);
-#pragma unroll 1
-        for (int it = 0; it < kSyncSpins; ++it) {
-          if (__hip_atomic_load(&g_round_sync[xcd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= tgt) break;
-          __builtin_amdgcn_s_sleep(2);
-        }
-      }
-    }
-    MOE_WAIT_VM(L_STAGE * (STAGES - 2));
-    MOE_BARRIER();
-    issue(std::integral_constant<int, (SL + STAGES - 1) % STAGES>(), j + STAGES - 1);
+  constexpr int TO = SWIGLU ? TN / 2 : TN;  // output tiles per wave row block
 
+  // ---- E4M3 K step, in two halves: operand + scale reads, then the products ----
+  // A lane's 32 bytes of the 128-element K slice are chunks lg and lg + 4 (the same K
+  // permutation for A and B leaves the product unchanged); each read then covers the 16
+  // lanes' rows at distinct swizzled chunks and hits distinct banks.  The scales of the K
+  // block: s_A of the lane's four rows (one 16-byte read) and the two weight-block scales
+  // (one broadcast read), combined into s_A * s_W per row tile.
+  auto fp8_read = [&](const uint8_t* As, int kt, i32x8(&af)[TM], i32x8(&bfr)[TN], float(&s0)[TM],
+                      float(&s1)[TM]) __attribute__((always_inline)) {
     const uint8_t* Bs = As + A_BYTES;
-    if (!FP8) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = *(const bf16x8_t*)(As + (ks ? fa_hi : fa_lo) + i * 16 * 128);
-#pragma unroll
-        for (int jj = 0; jj < TN; ++jj) {
-          const int ro = (SWIGLU && jj >= TN / 2 ? BN / 2 + (jj - TN / 2) * 16 : jj * 16) * 128;
-          bfr[jj] = *(const bf16x8_t*)(Bs + (ks ? fb_hi : fb_lo) + ro);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int jj = 0; jj < TN; ++jj) acc[i][jj] = mfma_bf16(af[i], bfr[jj], acc[i][jj]);
-      }
-    } else {
-      // a lane's 32 bytes of the 128-element K slice are chunks lg and lg + 4 (the same K
-      // permutation for A and B leaves the product unchanged); each read then covers the 16
-      // lanes' rows at distinct swizzled chunks and hits distinct banks
-      i32x8 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const u32x4 lo = *(const u32x4*)(As + fa_lo + i * 16 * 128);
-        const u32x4 hi = *(const u32x4*)(As + fa_hi + i * 16 * 128);
-        af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
-#pragma unroll
-      for (int jj = 0; jj < TN; ++jj) {
-        const int ro = (SWIGLU && jj >= TN / 2 ? BN / 2 + (jj - TN / 2) * 16 : jj * 16) * 128;
-        const u32x4 lo = *(const u32x4*)(Bs + fb_lo + ro);
-        const u32x4 hi = *(const u32x4*)(Bs + fb_hi + ro);
-        bfr[jj] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
-      // this K block's scales: s_A of the lane's four rows (one 16-byte read) and the two
-      // weight-block scales (one broadcast read)
-      const int kc = kt % SC_CH;
-      const float* scb = s_sc + sc_use * SC_BUF;
-      const f32x4 sa = *(const f32x4*)(scb + fs_off + ((kc ^ (lr & 7)) << 2));
-      const float* swp = scb + BM * SC_CH + 2 * kc;
-      const float sw0 = SWIGLU || (wn * WN) / 128 == 0 ? swp[0] : swp[1], sw1 = swp[1];
-      float s0[TM], s1[TM];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        s0[i] = sa[i] * sw0;
-        s1[i] = SWIGLU ? sa[i] * sw1 : s0[i];
-      }
-      // products with W as the first operand: a lane's four results of tile (i, jj) are
-      // columns lg * 4 .. lg * 4 + 3 of row lr, so one combined scale s_A * s_W covers them.
-      // Every tile's partial sum gets its own registers and its promotion (fp32 FMA into the
-      // accumulator) trails the matrix core by two tiles, so MFMAs issue back to back while
-      // the VALU promotes the previous results
-      constexpr int NT = TM * TN;
-      f32x4 pq[NT];
-#pragma unroll
-      for (int t = 0; t < NT + 2; ++t) {
-        if (t < NT) pq[t] = mfma_fp8(bfr[t % TN], af[t / TN], f32x4{0.f, 0.f, 0.f, 0.f});
-        if (t >= 2) {
-          const int u = t - 2, i = u / TN, jj = u % TN;
-          const float sc = SWIGLU && jj >= TN / 2 ? s1[i] : s0[i];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][jj][r] = fmaf(pq[u][r], sc, acc[i][jj][r]);
-        }
-      }
-      if (kc == SC_CH - 1 || kt == ksteps - 1) sc_use = sc_use + 1 == SC_NB ? 0 : sc_use + 1;  // chunk done
+    for (int i = 0; i < TM; ++i) {
+      const u32x4 lo = *(const u32x4*)(As + fa_lo + i * 16 * 128);
+      const u32x4 hi = *(const u32x4*)(As + fa_hi + i * 16 * 128);
+      af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
-
-    if (kt == ksteps - 1) {
-      // ---- epilogue of tile ct ----
-      constexpr int TO = SWIGLU ? TN / 2 : TN;
-      const int64_t orow0 = (int64_t)(ct.row0 - base_row);
-      float v[TM][TO][4];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+    for (int jj = 0; jj < TN; ++jj) {
+      const int ro = (SWIGLU && jj >= TN / 2 ? BN / 2 + (jj - TN / 2) * 16 : jj * 16) * 128;
+      const u32x4 lo = *(const u32x4*)(Bs + fb_lo + ro);
+      const u32x4 hi = *(const u32x4*)(Bs + fb_hi + ro);
+      bfr[jj] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    const int kc = kt % SC_CH;
+    const float* scb = s_sc + sc_use * SC_BUF;
+    const f32x4 sa = *(const f32x4*)(scb + fs_off + ((kc ^ ((lr >> 1) & 7)) << 2));
+    const float* swp = scb + BM * SC_CH + 2 * kc;
+    const float sw0 = SWIGLU || (wn * WN) / 128 == 0 ? swp[0] : swp[1], sw1 = swp[1];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      s0[i] = sa[i] * sw0;
+      s1[i] = SWIGLU ? sa[i] * sw1 : s0[i];
+    }
+    if (kc == SC_CH - 1 || kt == ksteps - 1) sc_use = sc_use + 1 == SC_NB ? 0 : sc_use + 1;  // chunk done
+  };
+  // Products with W as the first operand: a lane's four results of tile (i, jj) are columns
+  // lg * 4 .. lg * 4 + 3 of row lr, so one combined scale covers them.  Every tile's partial
+  // sum gets its own registers and its promotion (fp32 FMA into the accumulator) trails the
+  // matrix core by two tiles, so MFMAs issue back to back while the VALU promotes.
+  auto fp8_math = [&](auto slot_c, const i32x8(&af)[TM], const i32x8(&bfr)[TN], const float(&s0)[TM],
+                      const float(&s1)[TM]) __attribute__((always_inline)) {
+    constexpr int NT = TM * TN;
+    f32x4 pq[NT];
+#pragma unroll
+    for (int t = 0; t < NT + 2; ++t) {
+      if (t < NT) {
+        pq[t] = mfma_fp8(bfr[t % TN], af[t / TN], f32x4{0.f, 0.f, 0.f, 0.f});
+        dma_in(slot_c, t, NT);
+      }
+      if (t >= 2) {
+        const int u = t - 2, i = u / TN, jj = u % TN;
+        const float sc = SWIGLU && jj >= TN / 2 ? s1[i] : s0[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][jj][r] = fmaf(pq[u][r], sc, acc[i][jj][r]);
+      }
+    }
+  };
+
+  // ---- epilogue of a tile: values (SwiGLU applied; the accumulators restart at zero), the
+  // per-row amax of an E4M3 output into s_red, then the stores ----
+  auto epi_values = [&](float(&v)[TM][TO][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TO; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[i][jj][r] = SWIGLU ? silu(acc[i][jj][r]) * acc[i][jj + TO][r] : acc[i][jj][r];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // E4M3 layout (FP8): lane holds row wm * WM + i * 16 + lr, columns col_w + jj * 16 + 0..3;
+  // bf16 layout: rows wm * WM + i * 16 + lg * 4 + r, column col_w + jj * 16
+  auto epi_reduce = [&](const float(&v)[TM][TO][4]) __attribute__((always_inline)) {
+    if constexpr (OUT == OUT_FP8) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        float mx = 0.f;
 #pragma unroll
         for (int jj = 0; jj < TO; ++jj)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[i][jj][r] = SWIGLU ? silu(acc[i][jj][r]) * acc[i][jj + TO][r] : acc[i][jj][r];
-      if constexpr (FP8) {
-        // E4M3 layout: lane holds row wm * WM + i * 16 + lr, columns col_w + jj * 16 + 0..3
-        const int col_w = (SWIGLU ? wn * (WN / 2) : wn * WN) + lg * 4;
-        if (OUT == OUT_FP8) {
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(v[i][jj][r]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        if (lg == 0) s_red[wn * BM + wm * WM + i * 16 + lr] = mx;  // the 4 lanes of the row agree
+      }
+    }
+  };
+  auto epi_store = [&](const float(&v)[TM][TO][4], const TileInfo& et) __attribute__((always_inline)) {
+    const int64_t orow0 = (int64_t)(et.row0 - base_row);
+    const bool tail = OUT == OUT_BF16 && !SWIGLU && et.g >= p.tail_first;  // split output: f32 tail rows
+    if constexpr (FP8) {
+      const int c0 = et.nt * OC + (SWIGLU ? wn * (WN / 2) : wn * WN) + lg * 4;
 #pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            float mx = 0.f;
+      for (int i = 0; i < TM; ++i) {
+        const int m = wm * WM + i * 16 + lr;
+        if (OUT == OUT_FP8) {
+          float amax = 0.f;
+#pragma unroll
+          for (int q = 0; q < WGN; ++q) amax = fmaxf(amax, s_red[q * BM + m]);
+          const float s = (amax == 0.f) ? 1.0f : amax / 448.0f;
+          const float rs = recip_refined(s);
+          if (m < et.nrows) {
+            uint8_t* orow = p.out + (orow0 + m) * p.ldo_b;
+#pragma unroll
+            for (int jj = 0; jj < TO; ++jj) {
+              uint32_t w4 = 0;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) w4 |= f32_to_e4m3(quotient(v[i][jj][r], s, rs)) << (8 * r);
+              *reinterpret_cast<uint32_t*>(orow + c0 + jj * 16) = w4;
+            }
+            if (wn == 0 && lg == 0) p.out_scale[(orow0 + m) * p.out_scale_ld + et.nt] = s;
+          }
+        } else if (m < et.nrows) {
+          if (tail) {
+            float* trow = reinterpret_cast<float*>(p.out_tail + (int64_t)(et.row0 - tail_row + m) * p.ldo_tail_b);
 #pragma unroll
             for (int jj = 0; jj < TO; ++jj)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(v[i][jj][r]));
-            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-            if (lg == 0) s_red[wn * BM + wm * WM + i * 16 + lr] = mx;  // the 4 lanes of the row agree
-          }
-          MOE_BARRIER();
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int m = wm * WM + i * 16 + lr;
-          const int c0 = ct.nt * OC + col_w;
-          if (OUT == OUT_BF16 && !SWIGLU && ct.g >= p.tail_first) {
-            // split output: this group's rows go to the f32 tail
-            if (m < ct.nrows) {
-              float* trow = reinterpret_cast<float*>(p.out_tail + (int64_t)(ct.row0 - s_offs[p.tail_first] + m) * p.ldo_tail_b);
-#pragma unroll
-              for (int jj = 0; jj < TO; ++jj)
-                *reinterpret_cast<f32x4*>(trow + c0 + jj * 16) = f32x4{v[i][jj][0], v[i][jj][1], v[i][jj][2], v[i][jj][3]};
-            }
-          } else if (OUT == OUT_FP8) {
-            float amax = 0.f;
-#pragma unroll
-            for (int q = 0; q < WGN; ++q) amax = fmaxf(amax, s_red[q * BM + m]);
-            const float s = (amax == 0.f) ? 1.0f : amax / 448.0f;
-            const float rs = recip_refined(s);
-            if (m < ct.nrows) {
-              uint8_t* orow = p.out + (orow0 + m) * p.ldo_b;
-#pragma unroll
-              for (int jj = 0; jj < TO; ++jj) {
-                uint32_t w4 = 0;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) w4 |= f32_to_e4m3(quotient(v[i][jj][r], s, rs)) << (8 * r);
-                *reinterpret_cast<uint32_t*>(orow + c0 + jj * 16) = w4;
-              }
-              if (wn == 0 && lg == 0) p.out_scale[(orow0 + m) * p.out_scale_ld + ct.nt] = s;
-            }
-          } else if (m < ct.nrows) {
+              *reinterpret_cast<f32x4*>(trow + c0 + jj * 16) = f32x4{v[i][jj][0], v[i][jj][1], v[i][jj][2], v[i][jj][3]};
+          } else {
             uint8_t* orow = p.out + (orow0 + m) * p.ldo_b;
 #pragma unroll
             for (int jj = 0; jj < TO; ++jj) {
@@ -531,52 +545,110 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
             }
           }
         }
-        if (OUT == OUT_FP8) MOE_BARRIER();  // s_red is rewritten by the next tile
-      } else {
-        // bf16 layout: lane holds rows wm * WM + i * 16 + lg * 4 + r, column col_w + jj * 16
-        const int col_w = (SWIGLU ? wn * (WN / 2) : wn * WN) + lr;
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = wm * WM + i * 16 + lg * 4 + r;
-            const int c0 = ct.nt * OC + col_w;
-            if (OUT == OUT_BF16 && !SWIGLU && ct.g >= p.tail_first) {
-              // split output: this group's rows go to the f32 tail
-              if (m < ct.nrows) {
-                float* trow = reinterpret_cast<float*>(p.out_tail + (int64_t)(ct.row0 - s_offs[p.tail_first] + m) * p.ldo_tail_b);
-#pragma unroll
-                for (int jj = 0; jj < TO; ++jj) trow[c0 + jj * 16] = v[i][jj][r];
-              }
-            } else if (m < ct.nrows) {
-              uint8_t* orow = p.out + (orow0 + m) * p.ldo_b;
-#pragma unroll
-              for (int jj = 0; jj < TO; ++jj) {
-                const int c = c0 + jj * 16;
-                if (OUT == OUT_F32) reinterpret_cast<float*>(orow)[c] = v[i][jj][r];
-                else reinterpret_cast<uint16_t*>(orow)[c] = (uint16_t)f32_to_bf16_rne(v[i][jj][r]);
-              }
-            }
-          }
       }
-      // next tile of the compute side
+    } else {
+      const int c0 = et.nt * OC + (SWIGLU ? wn * (WN / 2) : wn * WN) + lr;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (j + 1 < total_steps) ct = tile_of((j + 1) / ksteps);
+        for (int r = 0; r < 4; ++r) {
+          const int m = wm * WM + i * 16 + lg * 4 + r;
+          if (m >= et.nrows) continue;
+          if (tail) {
+            float* trow = reinterpret_cast<float*>(p.out_tail + (int64_t)(et.row0 - tail_row + m) * p.ldo_tail_b);
+#pragma unroll
+            for (int jj = 0; jj < TO; ++jj) trow[c0 + jj * 16] = v[i][jj][r];
+          } else {
+            uint8_t* orow = p.out + (orow0 + m) * p.ldo_b;
+#pragma unroll
+            for (int jj = 0; jj < TO; ++jj) {
+              const int c = c0 + jj * 16;
+              if (OUT == OUT_F32) reinterpret_cast<float*>(orow)[c] = v[i][jj][r];
+              else reinterpret_cast<uint16_t*>(orow)[c] = (uint16_t)f32_to_bf16_rne(v[i][jj][r]);
+            }
+          }
+        }
     }
   };
 
-  int j = 0;
-  for (; j + STAGES <= total_steps; j += STAGES) {
-    step(std::integral_constant<int, 0>(), j);
-    step(std::integral_constant<int, 1>(), j + 1);
-    if constexpr (STAGES > 2) step(std::integral_constant<int, 2 % STAGES>(), j + 2);
+  {
+    // one step: wait for its DMA (STAGES - 2 later batches stay in flight), issue the DMA
+    // STAGES - 1 steps ahead into the slot read last step, multiply, and finish the tile on
+    // its last step
+    auto step = [&](auto slot_c, int j) __attribute__((always_inline)) {
+      constexpr int SL = decltype(slot_c)::value;
+      const uint8_t* As = SL == 0 ? slot0 : (SL == 1 ? slot1 : slot2);
+      const int kt = j % ksteps;
+      if (kRoundSync && kt == 0 && j > 0) {  // a new round: arrive for the last one, wait for the XCD
+        if (tid == 0) {
+          const int q = j / ksteps;
+          __hip_atomic_fetch_add(&g_round_sync[xcd], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const unsigned int tgt = round_target(q);
+#pragma unroll 1
+          for (int it = 0; it < kSyncSpins; ++it) {
+            if (__hip_atomic_load(&g_round_sync[xcd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= tgt) break;
+            __builtin_amdgcn_s_sleep(2);
+          }
+        }
+      }
+      MOE_WAIT_VM(L_STAGE * (STAGES - 2));
+      MOE_BARRIER();
+      // the DMA of step j + STAGES - 1 goes to the slot read last step; its instructions are
+      // spread over this step's MFMAs
+      constexpr auto dslot = std::integral_constant<int, (SL + STAGES - 1) % STAGES>();
+      issue_prep(j + STAGES - 1);
+
+      if constexpr (!FP8) {
+        const uint8_t* Bs = As + A_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+          for (int i = 0; i < TM; ++i) af[i] = *(const bf16x8_t*)(As + (ks ? fa_hi : fa_lo) + i * 16 * 128);
+#pragma unroll
+          for (int jj = 0; jj < TN; ++jj) {
+            const int ro = (SWIGLU && jj >= TN / 2 ? BN / 2 + (jj - TN / 2) * 16 : jj * 16) * 128;
+            bfr[jj] = *(const bf16x8_t*)(Bs + (ks ? fb_hi : fb_lo) + ro);
+          }
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < TN; ++jj) {
+              acc[i][jj] = mfma_bf16(af[i], bfr[jj], acc[i][jj]);
+              dma_in(dslot, (ks * TM + i) * TN + jj, 2 * TM * TN);
+            }
+        }
+      } else {
+        i32x8 af[TM], bfr[TN];
+        float s0[TM], s1[TM];
+        fp8_read(As, kt, af, bfr, s0, s1);
+        fp8_math(dslot, af, bfr, s0, s1);
+      }
+      issue_scales();
+
+      if (kt == ksteps - 1) {
+        float v[TM][TO][4];
+        epi_values(v);
+        if (OUT == OUT_FP8) {
+          epi_reduce(v);
+          MOE_BARRIER();
+        }
+        epi_store(v, ct);
+        if (OUT == OUT_FP8) MOE_BARRIER();  // s_red is rewritten by the next tile
+        if (j + 1 < total_steps) ct = tile_of((j + 1) / ksteps);
+      }
+    };
+
+    int j = 0;
+    for (; j + STAGES <= total_steps; j += STAGES) {
+      step(std::integral_constant<int, 0>(), j);
+      step(std::integral_constant<int, 1>(), j + 1);
+      if constexpr (STAGES > 2) step(std::integral_constant<int, 2 % STAGES>(), j + 2);
+    }
+    if (j < total_steps) step(std::integral_constant<int, 0>(), j);
+    if constexpr (STAGES > 2)
+      if (j + 1 < total_steps) step(std::integral_constant<int, 1>(), j + 1);
   }
-  if (j < total_steps) step(std::integral_constant<int, 0>(), j);
-  if constexpr (STAGES > 2)
-    if (j + 1 < total_steps) step(std::integral_constant<int, 1>(), j + 1);
   MOE_WAIT_VM(0);  // the clamped tail DMA must land before the workgroup retires
   leave();
 }
@@ -594,6 +666,28 @@ int device_cus() {
   return cus;
 }
 
+constexpr size_t kLdsBytes = 160 * 1024;
+
+// Static LDS of one kernel instantiation (queried once).
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool FP8, bool SWIGLU, int OUT>
+size_t static_lds() {
+  static size_t bytes = 0;
+  if (bytes == 0) {
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&grouped_gemm_kernel<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT>)) ==
+        hipSuccess)
+      bytes = attr.sharedSizeBytes;
+    else
+      bytes = kLdsBytes;  // unknown: treat as full, so callers take a smaller configuration
+  }
+  return bytes;
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool FP8, bool SWIGLU, int OUT>
+bool fits(const GemmArgs& a) {
+  return static_lds<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT>() + (size_t)(a.n_groups + 1) * 4 <= kLdsBytes;
+}
+
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool FP8, bool SWIGLU, int OUT>
 void launch(GemmArgs a, int64_t m_total, hipStream_t stream) {
   a.n_tiles = a.out_cols / (SWIGLU ? BN / 2 : BN);
@@ -602,12 +696,12 @@ void launch(GemmArgs a, int64_t m_total, hipStream_t stream) {
   if (upper <= 0) return;
   const int cus = device_cus();
   const int64_t grid = upper < cus ? ((upper + 7) / 8) * 8 : cus;
-  grouped_gemm_kernel<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT><<<(unsigned)grid, WGM * WGN * 64, 0, stream>>>(a);
+  const size_t dyn = (size_t)(a.n_groups + 1) * 4;  // the tile prefix table
+  grouped_gemm_kernel<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT><<<(unsigned)grid, WGM * WGN * 64, dyn, stream>>>(a);
 }
 
-// bf16: 8 waves of 64x64, three-slot ring; E4M3: 8 waves of 64x64 and a two-slot ring (two
-// waves per SIMD hide the promotion's VALU work behind the other wave's MFMAs: 8.2 -> 7.2 ms
-// against 4 waves of 64x128 on the T = 16384 routing; a third slot costs registers).
+// bf16: 8 waves of 64x64, three-slot ring.  E4M3: 8 waves of 64x64 and a three-slot ring
+// where its LDS (147 KB of ring, the scale chunks and the tile table) fits, else two slots.
 // Decode-sized groups: 64-row blocks, 8 waves of 64x32.
 // Narrow bf16 outputs (N/2 or N not a multiple of 128 / 256): 128-column blocks, 4 waves.
 template <bool FP8, bool SWIGLU, int OUT>
@@ -619,8 +713,10 @@ void dispatch(const GemmArgs& a, int64_t m_total, bool small, bool narrow, hipSt
     }
   }
   if (small) launch<64, 256, 1, 8, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
-  else if constexpr (FP8) launch<128, 256, 2, 4, 2, FP8, SWIGLU, OUT>(a, m_total, stream);
-  else launch<128, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
+  else if constexpr (FP8) {
+    if (fits<128, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a)) launch<128, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
+    else launch<128, 256, 2, 4, 2, FP8, SWIGLU, OUT>(a, m_total, stream);
+  } else launch<128, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
 }
 
 }  // namespace
