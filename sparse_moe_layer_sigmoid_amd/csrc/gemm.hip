@@ -140,7 +140,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   constexpr int WN = BN / WGN;  // W rows (output columns; gate+up for SwiGLU) per wave
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int A_BYTES = BM * 128, STAGE = (BM + BN) * 128;
-  constexpr int A_PW = BM / 8 / NW;               // A DMA instructions per wave per stage
+  // A DMA instruction q (rows 8q .. 8q + 7) is issued by wave q mod NW; with BM / 8 not a
+  // multiple of NW the first waves issue one more (A_PW vs A_PW_MIN)
+  constexpr int A_ROWS8 = BM / 8;
+  constexpr int A_PW = (A_ROWS8 + NW - 1) / NW;     // A DMA instructions per wave per stage (at most)
+  constexpr int A_PW_MIN = A_ROWS8 / NW;            // ... (at least)
   constexpr int B_PW = BN / 8 / NW;               // B DMA instructions per wave per stage
   // Scales arrive in chunks of SC_CH K blocks, one 4-byte DMA per lane, into one of SC_NB LDS
   // buffers in turn: BM * SC_CH A scales (SC_PW instructions per wave) and, from wave 0, the
@@ -154,9 +158,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   constexpr int SC_WS = 2 * SC_CH;               // weight-scale area: [SC_CH][2]
   constexpr int SC_BUF = BM * SC_CH + SC_WS;     // floats per chunk buffer
   constexpr int OC = SWIGLU ? BN / 2 : BN;
-  constexpr int L_STAGE = A_PW + B_PW;  // data DMA instructions per wave per stage (a scale chunk adds SC_PW)
-  static_assert(A_PW * 8 * NW == BM && B_PW * 8 * NW == BN, "DMA instructions must split evenly over waves");
-  static_assert(!FP8 || (SC_PW >= 1 && SC_PW * 64 * NW == BM * SC_CH), "scale chunk DMA must split evenly over waves");
+  // data DMA instructions per wave per stage: L_ISSUE at most, L_STAGE at least (the vmcnt
+  // waits allow L_STAGE later instructions in flight; a wave that issued more only waits
+  // longer; a scale chunk adds SC_PW)
+  constexpr int L_ISSUE = A_PW + B_PW;
+  constexpr int L_STAGE = A_PW_MIN + B_PW;
+  static_assert(A_ROWS8 * 8 == BM && B_PW * 8 * NW == BN && A_PW_MIN >= 1, "DMA rows must split over waves");
+  static_assert(!FP8 || (SC_PW >= 1 && SC_PW * 64 * NW == BM * SC_CH && A_PW == A_PW_MIN),
+                "scale chunk DMA must split evenly over waves");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(!SWIGLU || TN % 2 == 0, "SwiGLU waves need matching gate and up tiles");
   static_assert(OUT != OUT_FP8 || (FP8 && SWIGLU && OC == 128), "fp8 output = one 1x128 tile per row");
@@ -168,7 +177,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   // bf16 T = 4096 routing: 3.99 -> 3.69 ms).  Elsewhere it measured neutral or slower (the
   // down projections, whose rounds span several experts, the E4M3 kernels, decode-sized
   // blocks), so it is compiled out there.
-  constexpr bool kRoundSync = SWIGLU && !FP8 && BM == 128;
+  constexpr bool kRoundSync = SWIGLU && !FP8 && BM >= 128;
   static_assert(L_STAGE * (STAGES - 2) <= 63, "vmcnt budget");
 
   // one LDS array per ring slot: distinct objects, so the compiler can tell the DMA target of
@@ -275,7 +284,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   auto fetch_rows = [&](const TileInfo& t, int* dst, int* sdst) {
 #pragma unroll
     for (int i = 0; i < A_PW; ++i) {
-      const int rr = 8 * (wave * A_PW + i) + lrow;
+      const int q = wave + NW * i;
+      const int rr = 8 * min(q, A_ROWS8 - 1) + lrow;
       const int r = t.row0 + min(rr, t.nrows - 1);
       dst[i] = p.a_rows ? p.a_rows[r] : r;
     }
@@ -288,7 +298,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   auto set_rows = [&](const int* src, const int* ssrc) {
 #pragma unroll
     for (int i = 0; i < A_PW; ++i) {
-      const int rr = 8 * (wave * A_PW + i) + lrow;
+      const int rr = 8 * (wave + NW * i) + lrow;
       a_ptr[i] = p.a + (int64_t)src[i] * p.lda_b + ((cch ^ (rr & 7)) << 4);
     }
 #pragma unroll
@@ -329,13 +339,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     dma_kt = kt;
     dma_scales = FP8 && !past_end && kt % SC_CH == 0;
   };
-  // data DMA instruction k (0 .. L_STAGE - 1: A rows, then B rows) of the prepared batch into
+  // data DMA instruction k (0 .. L_ISSUE - 1: A rows, then B rows) of the prepared batch into
   // ring slot SL
   auto issue_one = [&](auto slot_c, int k) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot_c)::value;
     uint8_t* st = SL == 0 ? slot0 : (SL == 1 ? slot1 : slot2);
     if (k < A_PW) {
-      __builtin_amdgcn_global_load_lds((glb_void*)(a_ptr[k] + dma_kt * 128), (lds_void*)(st + (wave * A_PW + k) * 1024), 16, 0, 0);
+      const int q = wave + NW * k;
+      if (A_PW == A_PW_MIN || q < A_ROWS8)
+        __builtin_amdgcn_global_load_lds((glb_void*)(a_ptr[k] + dma_kt * 128), (lds_void*)(st + q * 1024), 16, 0, 0);
     } else {
       const int i = k - A_PW;
       __builtin_amdgcn_global_load_lds((glb_void*)(wbase + dma_kt * 128 + (uint32_t)b_off[i]),
@@ -362,7 +374,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   auto issue = [&](auto slot_c, int js) __attribute__((always_inline)) {
     issue_prep(js);
 #pragma unroll
-    for (int k = 0; k < L_STAGE; ++k) issue_one(slot_c, k);
+    for (int k = 0; k < L_ISSUE; ++k) issue_one(slot_c, k);
     issue_scales();
   };
   // Inside a step the batch's instructions are spread over the MFMA sequence (instruction k
@@ -371,8 +383,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   // (~16 cycles per 1 KB instruction per CU), while spread out they queue behind nothing.
   auto dma_in = [&](auto slot_c, int t, int n) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < L_STAGE; ++k)
-      if (t == (k + 1) * n / (L_STAGE + 1)) {
+    for (int k = 0; k < L_ISSUE; ++k)
+      if (t == (k + 1) * n / (L_ISSUE + 1)) {
         __builtin_amdgcn_sched_barrier(0);
         issue_one(slot_c, k);
         __builtin_amdgcn_sched_barrier(0);
@@ -700,7 +712,28 @@ void launch(GemmArgs a, int64_t m_total, hipStream_t stream) {
   grouped_gemm_kernel<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT><<<(unsigned)grid, WGM * WGN * 64, dyn, stream>>>(a);
 }
 
-// bf16: 8 waves of 64x64, three-slot ring.  E4M3: 8 waves of 64x64 and a three-slot ring
+// Row-block height for bf16 groups of about mu rows (the group sizes live on the device, so
+// the host uses the mean): the expected row tiles per group, with a group's rows taken as
+// normal with standard deviation sqrt(mu) (routing counts), times the relative cost of a
+// tile step -- 160-row steps move ~11% more LDS bytes than 128-row steps (196 vs 176 KB).
+// At 128 +- 11 rows per expert (T = 4096) 128-row blocks need ~1.5 tiles per expert, 160-row
+// blocks ~1.0.
+bool prefer_tall_rows(int64_t m_total, int n_groups) {
+  const double mu = (double)m_total / n_groups;
+  if (mu < 96.0) return false;
+  const double sd = sqrt(mu);
+  double e128 = 0, e160 = 0, wsum = 0;
+  for (int k = -8; k <= 8; ++k) {
+    const double z = k * 0.375, w = exp(-0.5 * z * z), rows = fmax(1.0, mu + z * sd);
+    e128 += w * ceil(rows / 128.0);
+    e160 += w * ceil(rows / 160.0);
+    wsum += w;
+  }
+  return e160 * 1.11 < e128;
+}
+
+// bf16: 8 waves of 64x64 (or 80x64 with 160-row blocks, see above), three-slot ring.
+// E4M3: 8 waves of 64x64 and a three-slot ring
 // where its LDS (147 KB of ring, the scale chunks and the tile table) fits, else two slots.
 // Decode-sized groups: 64-row blocks, 8 waves of 64x32.
 // Narrow bf16 outputs (N/2 or N not a multiple of 128 / 256): 128-column blocks, 4 waves.
@@ -713,10 +746,15 @@ void dispatch(const GemmArgs& a, int64_t m_total, bool small, bool narrow, hipSt
     }
   }
   if (small) launch<64, 256, 1, 8, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
-  else if constexpr (FP8) {
+  else if constexpr (!FP8) {
+    if (prefer_tall_rows(m_total, a.n_groups) && fits<160, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a))
+      launch<160, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
+    else
+      launch<128, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
+  } else {
     if (fits<128, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a)) launch<128, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
     else launch<128, 256, 2, 4, 2, FP8, SWIGLU, OUT>(a, m_total, stream);
-  } else launch<128, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
+  }
 }
 
 }  // namespace

@@ -198,6 +198,42 @@ def test_gemm_bf16(swiglu, out_dtype):
             assert np.all(np.abs(got[lo:hi] - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6 * np.sqrt(np.mean(ref ** 2))), g
 
 
+@pytest.mark.parametrize("sizes", [[80, 0, 129, 40, 128, 97, 1], [150, 161, 0, 320, 97, 5, 170, 160]],
+                         ids=["rows128", "rows160"])
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_gemm_bf16_row_blocks(sizes, swiglu):
+    """Both bf16 row-block heights: ~68 rows per group on average take 128-row blocks, ~133
+    take 160-row blocks (five 16-row tiles per wave, A rows loaded by 20 DMA instructions over
+    8 waves).  Ragged groups, an empty one, groups of exactly one block and of one row; the
+    shared-style f32 tail output on the last group."""
+    G, N, K = len(sizes), 256, 192
+    sizes = np.array(sizes)
+    offs = _offsets(sizes)
+    rows = int(offs[-1])
+    T = 333
+    a_rows = np.random.default_rng(9).integers(0, T, rows).astype(np.int32)
+    A = I.gen_normal(71, (T, K), 1.0)
+    W = I.gen_normal(72, (G, N, K), 0.05)
+    oc = N // 2 if swiglu else N
+    split = int(offs[G - 1])
+    out = torch.empty((rows if swiglu else split, oc), dtype=torch.bfloat16, device=DEV)
+    kw = {} if swiglu else dict(out_tail=torch.empty((rows - split, oc), dtype=torch.float32, device=DEV), tail_groups=1)
+    M().moe_grouped_gemm(A.to(DEV), W.to(DEV), torch.from_numpy(offs).to(DEV), 0, G, rows, out,
+                         a_rows=torch.from_numpy(a_rows).to(DEV), swiglu=swiglu, **kw)
+    got = np64(out) if swiglu else np.concatenate([np64(out), np64(kw["out_tail"])])
+    An, Wn = np64(A), np64(W)
+    for g in range(G):
+        lo, hi = offs[g], offs[g + 1]
+        if hi == lo:
+            continue
+        xr = An[a_rows[lo:hi]]
+        ref = O.swiglu_hidden(xr, Wn[g]) if swiglu else xr @ Wn[g].T
+        if not swiglu and g == G - 1:
+            assert rel_err(got[lo:hi], ref) < 1e-5, g
+        else:  # one bf16 rounding of the fp32 result
+            assert np.all(np.abs(got[lo:hi] - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6 * np.sqrt(np.mean(ref ** 2))), g
+
+
 @pytest.mark.parametrize("fp8,tail", [(False, 1), (False, 2), (True, 1)], ids=["bf16_tail1", "bf16_tail2", "fp8_tail1"])
 def test_gemm_split_output(fp8, tail):
     """One launch over all groups with the last `tail` groups written as f32 rows to a second
