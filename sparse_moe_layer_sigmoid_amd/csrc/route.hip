@@ -19,9 +19,10 @@
 //     index) and measures the decision margin: the gap between the K-th and (K+1)-th z, and
 //     between the last kept and the best dropped group score.
 //  3. refine: tokens whose fp32 margin is below kRefineGap (listed by the select kernel) are
-//     recomputed in fp64 (exact bf16 products, fp64 sums, fp64 sigmoid and selection), one
-//     workgroup per token, so the choice of experts does not depend on the matrix cores'
-//     rounding.
+//     recomputed in fp64 (exact bf16 products, fp64 sums, fp64 sigmoid and selection), so the
+//     choice of experts does not depend on the matrix cores' rounding: their fp64 logits by
+//     workgroups of (listed token, 16 experts) into the workspace (the split-K partials are
+//     dead by then), then one wave per listed token selects.
 //  4. count: each block of 64 tokens histograms its tokens' experts.
 //  5. reduce: one wave per expert sums the block histograms (integer sums: exact).
 #include <math.h>
@@ -323,25 +324,27 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
   if (lane == 0 && margin < kRefineGap) flagged[atomicAdd(n_flagged, 1)] = (int32_t)t;
 }
 
-// ---- kernel 3: fp64 refinement of the flagged (near-tie) tokens ----
-// One workgroup per flagged token (grid-strided over the list): wave w takes experts w,
-// w + kRefineWaves, ...; its lanes split K into 16-byte chunks and keep eight independent
-// fp64 partial sums (one per element of a chunk), so the fp64 adds pipeline.  Each token's
-// result depends on that token alone, so the list's order does not matter.
-constexpr int kRefineWaves = 16;
-__global__ __launch_bounds__(kRefineWaves * 64) void route_refine_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
-    int d, int N, int K, int n_group, int topk_group, const int32_t* __restrict__ n_flagged,
-    const int32_t* __restrict__ flagged, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
-    float* __restrict__ scores) {
-  __shared__ double u64[256];
+// ---- kernel 3a: fp64 logits of the flagged (near-tie) tokens ----
+// Workgroup (x, y) takes listed tokens x, x + gridDim.x, ... and experts 16y .. 16y + 15: wave
+// w computes experts 16y + w, 16y + w + 4, ...; its lanes split K into 16-byte chunks and keep
+// eight independent fp64 partial sums (one per element of a chunk), so the fp64 adds
+// pipeline.  Spreading a token over N / 16 workgroups keeps the router-row reads (the whole
+// W_r per token) off one CU: a handful of listed tokens used to take ~110 us.  Each logit
+// depends on its token and expert alone, so the list's order does not matter.
+constexpr int kRefineChunk = 16;  // experts per workgroup
+__global__ __launch_bounds__(256) void route_refine_logits_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ wr, int d, int N,
+                                                                  const int32_t* __restrict__ n_flagged,
+                                                                  const int32_t* __restrict__ flagged,
+                                                                  double* __restrict__ l64) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nf = *n_flagged;
   const int nd = d / 8;  // 16-byte chunks per row
+  const int e0 = blockIdx.y * kRefineChunk, e1 = min(N, e0 + kRefineChunk);
   for (int i = blockIdx.x; i < nf; i += gridDim.x) {
     const int64_t t = flagged[i];
     const uint16_t* xr = x + t * d;
-    for (int e = wave; e < N; e += kRefineWaves) {
+    for (int e = e0 + wave; e < e1; e += 4) {
       const uint16_t* er = wr + (int64_t)e * d;
       double a[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
       for (int c = lane; c < nd; c += 64) {
@@ -356,16 +359,28 @@ __global__ __launch_bounds__(kRefineWaves * 64) void route_refine_kernel(
       double sum = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
-      if (lane == 0) u64[e] = sum;
+      if (lane == 0) l64[(int64_t)i * 256 + e] = sum;
     }
-    __syncthreads();
-    if (wave == 0) {
-      double u[4];
+  }
+}
+
+// ---- kernel 3b: fp64 selection and gates of the flagged tokens, one wave per token ----
+__global__ __launch_bounds__(256) void route_refine_select_kernel(const float* __restrict__ bias, int N, int K,
+                                                                  int n_group, int topk_group,
+                                                                  const int32_t* __restrict__ n_flagged,
+                                                                  const int32_t* __restrict__ flagged,
+                                                                  const double* __restrict__ l64,
+                                                                  int32_t* __restrict__ topk_idx,
+                                                                  float* __restrict__ topk_gate,
+                                                                  float* __restrict__ scores) {
+  const int lane = threadIdx.x & 63;
+  const int nf = *n_flagged;
+  for (int i = blockIdx.x * 4 + (threadIdx.x >> 6); i < nf; i += gridDim.x * 4) {
+    const int64_t t = flagged[i];
+    double u[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) u[r] = (lane * 4 + r < N) ? u64[lane * 4 + r] : 0.0;
-      select_token<double>(u, bias, N, K, n_group, topk_group, t, true, topk_idx, topk_gate, scores);
-    }
-    __syncthreads();
+    for (int r = 0; r < 4; ++r) u[r] = (lane * 4 + r < N) ? l64[(int64_t)i * 256 + lane * 4 + r] : 0.0;
+    select_token<double>(u, bias, N, K, n_group, topk_group, t, true, topk_idx, topk_gate, scores);
   }
 }
 
@@ -409,8 +424,8 @@ RouteWs route_ws(int T, int d, int N) {
   RouteWs w;
   const int S = route_splits(T, d);
   const int nb = T > 0 ? (T + 63) / 64 : 1;
-  w.part_off = 0;
-  w.nflag_off = (size_t)S * (size_t)T * 256 * sizeof(float);
+  w.part_off = 0;  // split-K partials, then the fp64 logits of the flagged tokens
+  w.nflag_off = (size_t)(S > 2 ? S : 2) * (size_t)T * 256 * sizeof(float);
   w.list_off = w.nflag_off + 256;
   w.blk_off = w.list_off + (((size_t)T * sizeof(int32_t) + 255) & ~(size_t)255);
   w.total = w.blk_off + (size_t)nb * (size_t)N * sizeof(int32_t);
@@ -471,8 +486,11 @@ extern "C" moe_status moe_route(const uint16_t* x, const uint16_t* w_router, con
     route_logits_kernel<<<tiles * S, kLogitsThreads, 0, stream>>>(x, w_router, T, d, n_experts, S, part, n_flagged);
     route_select_kernel<<<(T + 3) / 4, 256, 0, stream>>>(part, S, bias, T, n_experts, top_k, n_group, topk_group,
                                                          topk_idx, topk_gate, scores, n_flagged, flagged);
-    route_refine_kernel<<<T < 256 ? T : 256, kRefineWaves * 64, 0, stream>>>(
-        x, w_router, bias, d, n_experts, top_k, n_group, topk_group, n_flagged, flagged, topk_idx, topk_gate, scores);
+    double* l64 = reinterpret_cast<double*>(part);  // the partials are consumed by now
+    route_refine_logits_kernel<<<dim3(T < 64 ? T : 64, (n_experts + kRefineChunk - 1) / kRefineChunk), 256, 0, stream>>>(
+        x, w_router, d, n_experts, n_flagged, flagged, l64);
+    route_refine_select_kernel<<<(T + 3) / 4 < 256 ? (T + 3) / 4 : 256, 256, 0, stream>>>(
+        bias, n_experts, top_k, n_group, topk_group, n_flagged, flagged, l64, topk_idx, topk_gate, scores);
     route_count_kernel<<<nb, 64, 0, stream>>>(topk_idx, T, n_experts, top_k, blk);
   }
   counts_reduce_kernel<<<n_experts, 64, 0, stream>>>(blk, nb, n_experts, expert_counts);

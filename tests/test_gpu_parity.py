@@ -102,6 +102,29 @@ def test_route_parity(T, d, N, K, ng, tg):
     say(f"  tie-window tokens: {int(tie.sum())}")
 
 
+@pytest.mark.parametrize("ng,tg", [(1, 1), (4, 2)])
+def test_route_exact_ties_take_the_fp64_path(ng, tg):
+    """Experts 5, 9 and 40 have identical router rows and the same large bias, so every token's
+    top-2 is an exact three-way tie: the fp32 margin is 0, every token is listed for the fp64
+    re-evaluation (300 tokens: the logits kernel strides over them; 64 experts: four 16-expert
+    workgroups per token), and the tie goes to the lower indices, as in the oracle."""
+    T, d, N, K = 300, 256, 64, 2
+    x = I.gen_normal(81, (T, d), 1.0)
+    wr = I.gen_normal(82, (N, d), 0.5 / np.sqrt(d))
+    wr[9] = wr[5]
+    wr[40] = wr[5]
+    bias = np.zeros(N, np.float32)
+    bias[[5, 9, 40]] = 10.0
+    idx, gate, counts, _ = M().moe_route(x.to(DEV), wr.to(DEV), torch.from_numpy(bias).to(DEV), K, ng, tg)
+    r = O.route(np64(x), np64(wr), bias, K, ng, tg)
+    assert np.array_equal(r["idx"], np.tile([5, 9], (T, 1)))
+    assert np.array_equal(idx.cpu().numpy(), r["idx"])
+    assert np.array_equal(gate.cpu().numpy(), np.full((T, K), 0.5, np.float32))
+    want = np.zeros(N, np.int64)
+    want[[5, 9]] = T
+    assert np.array_equal(counts.cpu().numpy(), want)
+
+
 def test_route_bias_changes_selection_not_gates():
     T, d, N, K = 128, 256, 16, 2
     x = I.gen_normal(11, (T, d), 1.0).to(DEV)
