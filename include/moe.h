@@ -17,11 +17,12 @@
  *  - Ownership: every pointer is caller-owned memory; pointers documented as "device" must
  *    be device memory of the current device.  The library never allocates or frees device
  *    memory and keeps no state between calls, with one exception: the bf16 SwiGLU launches
- *    of moe_grouped_gemm pace their workgroups with nine arrival counters in a static device
- *    array (one copy per device); every launch leaves them at zero, and launches that overlap
- *    on one device share them, which can cost time but never changes a result.  Scratch
- *    memory comes from the caller's workspace, sized by the *_workspace_size() queries; it
- *    need not be initialised and its contents are undefined after the call.
+ *    of moe_grouped_gemm with 128-row blocks pace their workgroups with nine arrival counters
+ *    in a static device array (one copy per device); every launch leaves them at zero, and
+ *    launches that overlap on one device share them, which can cost time but never changes
+ *    a result.  Scratch memory comes from the caller's workspace, sized by the
+ *    *_workspace_size() queries; it need not be initialised and its contents are undefined
+ *    after the call.
  *  - Layout: row-major and contiguous unless an ld* (leading dimension, in elements) is
  *    given.  Device pointers must be 16-byte aligned; leading dimensions must keep every
  *    row 16-byte aligned.

@@ -174,10 +174,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   static_assert(STAGES == 2 || STAGES == 3, "the ring has two or three slots");
   // Round synchronisation pays where a round's workgroups share most of their operands and
   // the launch is bandwidth-bound: the bf16 gate/up projection with 128-row blocks (the
-  // bf16 T = 4096 routing: 3.99 -> 3.69 ms).  Elsewhere it measured neutral or slower (the
-  // down projections, whose rounds span several experts, the E4M3 kernels, decode-sized
-  // blocks), so it is compiled out there.
-  constexpr bool kRoundSync = SWIGLU && !FP8 && BM >= 128;
+  // bf16 T = 4096 routing: 3.99 -> 3.69 ms), where an expert's rows span two blocks that
+  // share its weights.  Elsewhere it measured neutral or slower (160-row blocks, which hold
+  // most experts in one block: 3.33 -> 3.11 ms without it; the down projections, whose
+  // rounds span several experts; the E4M3 kernels; decode-sized blocks), so it is compiled
+  // out there.
+  constexpr bool kRoundSync = SWIGLU && !FP8 && BM == 128;
   static_assert(L_STAGE * (STAGES - 2) <= 63, "vmcnt budget");
 
   // one LDS array per ring slot: distinct objects, so the compiler can tell the DMA target of
