@@ -365,6 +365,35 @@ def test_gemm_fp8_exact(sizes, K):
 # FP8_DOT_REL: the fp8 dot-product error bound (see tests/gpu_common.py).
 
 
+def test_gemm_fp8_two_slot_ring_matches_three():
+    """An E4M3 SwiGLU launch with an E4M3 output whose tile table outgrows the three-slot
+    ring's spare LDS (460 groups) takes the two-slot ring; the same groups split over two
+    launches take the three-slot ring.  The tile arithmetic does not depend on the ring, so
+    codes and scales agree bit for bit."""
+    G, K, N = 460, 256, 256
+    sizes = np.random.default_rng(17).integers(60, 81, G)
+    sizes[5] = 0
+    offs = _offsets(sizes)
+    rows = int(offs[-1])
+    A = I.gen_normal(91, (rows, K), 1.0)
+    W = I.gen_normal(92, (G, N, K), 0.006)
+    Aq, As = M().fp8_quant_1x128(A.to(DEV))
+    Wq, Ws = M().fp8_quant_128x128(W.to(DEV))
+    o = torch.from_numpy(offs).to(DEV)
+    one = torch.empty((rows, N // 2), dtype=torch.uint8, device=DEV)
+    one_s = torch.empty((rows, 1), dtype=torch.float32, device=DEV)
+    M().moe_grouped_gemm(Aq, Wq, o, 0, G, rows, one, a_scale=As, w_scale=Ws, swiglu=True, out_scale=one_s)
+    two = torch.empty_like(one)
+    two_s = torch.empty_like(one_s)
+    h = G // 2
+    split = int(offs[h])
+    M().moe_grouped_gemm(Aq, Wq, o, 0, h, split, two[:split], a_scale=As, w_scale=Ws, swiglu=True,
+                         out_scale=two_s[:split])
+    M().moe_grouped_gemm(Aq, Wq, o, h, G - h, rows - split, two[split:], a_scale=As, w_scale=Ws,
+                         swiglu=True, out_scale=two_s[split:])
+    assert torch.equal(one, two) and torch.equal(one_s, two_s)
+
+
 @pytest.mark.parametrize("swiglu,out_kind", [(False, "f32"), (True, "bf16"), (True, "fp8")])
 def test_gemm_fp8_random(swiglu, out_kind):
     G, K = 5, 512
