@@ -42,7 +42,9 @@ __global__ __launch_bounds__(kTok) void permute_count_kernel(const int32_t* __re
                                           __popcll(masks[2][e]) + __popcll(masks[3][e]);
 }
 
-// One workgroup: blk_base[b][e] = offsets[e] + sum_{b' < b} blk_cnt[b'][e].
+// One workgroup: blk_base[b][e] = sum_{b' < b} blk_cnt[b'][e] (the scatter adds offsets[e]),
+// offsets = exclusive scan of the expert totals.  The block counts are read 16 at a time, so
+// the loads of a thread are in flight together rather than one per loop trip.
 __global__ __launch_bounds__(256) void permute_scan_kernel(const int32_t* __restrict__ blk_cnt,
                                                            int32_t* __restrict__ blk_base,
                                                            int nb, int N, int T, int n_shared,
@@ -51,10 +53,16 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(const int32_t* __rest
   const int e = threadIdx.x;
   int run = 0;
   if (e < N) {
-    for (int b = 0; b < nb; ++b) {
-      const int c = blk_cnt[(size_t)b * N + e];
-      blk_base[(size_t)b * N + e] = run;
-      run += c;
+    constexpr int kBatch = 16;
+    for (int b0 = 0; b0 < nb; b0 += kBatch) {
+      int c[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) c[i] = b0 + i < nb ? blk_cnt[(size_t)(b0 + i) * N + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (b0 + i < nb) blk_base[(size_t)(b0 + i) * N + e] = run;
+        run += c[i];
+      }
     }
   }
   tot[e] = (e < N) ? run : 0;
@@ -67,10 +75,7 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(const int32_t* __rest
     __syncthreads();
   }
   const int excl = tot[e] - ((e < N) ? run : 0);
-  if (e < N) {
-    offsets[e] = excl;
-    for (int b = 0; b < nb; ++b) blk_base[(size_t)b * N + e] += excl;
-  }
+  if (e < N) offsets[e] = excl;
   if (e == 0) {
     const int routed = tot[255];
     offsets[N] = routed;
@@ -92,7 +97,7 @@ __global__ __launch_bounds__(kTok) void permute_scatter_kernel(
     const int e = idx[(size_t)t * K + k];
     int pos = -1;
     if (e >= 0 && e < N) {
-      pos = blk_base[(size_t)blockIdx.x * N + e];
+      pos = offsets[e] + blk_base[(size_t)blockIdx.x * N + e];
       for (int w = 0; w < wave; ++w) pos += __popcll(masks[w][e]);
       pos += __popcll(masks[wave][e] & below);
       sorted_token[pos] = t;
