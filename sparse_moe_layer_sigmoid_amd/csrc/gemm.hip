@@ -17,20 +17,27 @@
 //    activations of an expert and each weight block are fetched into that XCD's L2 once and
 //    reused there (workgroup b runs on XCD b mod 8).  Reuse needs the workgroups of a round
 //    to walk K together; left alone they drift apart by whole tiles over a launch, so in the
-//    bf16 gate/up kernels each workgroup waits at the start of a round until the XCD's other
-//    workgroups have finished the previous one (an arrival counter per XCD; the wait is
-//    bounded, so it only ever costs time, and the last workgroup to leave resets the
-//    counters for the next launch).
+//    bf16 gate/up kernel with 128-row blocks each workgroup waits at the start of a round
+//    until the XCD's other workgroups have finished the previous one (an arrival counter per
+//    XCD; the wait is bounded, so it only ever costs time, and the last workgroup to leave
+//    resets the counters for the next launch).
+//  * Row blocks of 128 rows (8 waves of 64x64), or 160 rows (8 waves of 80x64) for bf16
+//    launches whose experts hold ~100-600 rows, where they need fewer row tiles per expert;
+//    64 rows for decode-sized groups.
 //  * Operands move HBM -> LDS with direct-to-LDS DMA (global_load_lds_dwordx4): each wave
 //    instruction fills 8 rows x 128 bytes, the 16-byte chunks XOR-swizzled by (row & 7) so
 //    the MFMA operand reads hit distinct banks.  A ring of STAGES K steps (128 bytes of K per
 //    row: 64 bf16 or 128 E4M3) runs continuously across tile boundaries, with explicit
-//    vmcnt waits and one barrier per step; the gather indices of the next tile are fetched a
-//    whole tile ahead so the ring never drains.
+//    vmcnt waits and one barrier per step; a step's DMA instructions are spread over its
+//    MFMAs; the gather indices of the next tile are fetched a whole tile ahead so the ring
+//    never drains.
 //  * A rows are gathered through the permutation (token of each sorted row); rows past an
 //    expert's segment re-read its last row and are not stored.
 //  * SwiGLU: the B tile holds BN/2 gate rows then the matching BN/2 up rows, and each wave
 //    owns matching gate and up columns, so h is formed in registers.
+//  * E4M3 products are formed W-first (D^T = W A^T): a lane's four results are four columns
+//    of one token row, so one combined scale s_A * s_W promotes them; the scales of 8 K
+//    blocks arrive by DMA into LDS beside the operands.
 //  * The epilogue writes from registers (a tile's waves cover whole 128-byte lines, which
 //    merge in L2); the fp8 output's per-row amax over its 128 columns is reduced across
 //    waves in a small LDS array.
