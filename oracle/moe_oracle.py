@@ -17,7 +17,10 @@ Sources (the pages this follows; cited by page title and section):
   high precision).
 * [PFN] "Vol.25 DeepSeek-V3の技術とその影響" (preferred.jp), section
   "MoEの歴史とDeepSeekMoE-V3の特徴": one always-on shared expert plus 8 of 256 routed
-  experts per token, whose results are combined.
+  experts per token, whose results are combined; "学習と推論の課題と解決策" (values of a
+  1x128 / 128x128 tile can share an exponent) and "ハードウェアデザインへの提案" (requests
+  for quantisation support in hardware), with [TR] "考察" (native tile / block quantisation
+  in the matrix unit) -- the power-of-two scale variant below.
 
 Readings taken where the pages are silent (each is listed again in the design doc):
 
@@ -33,7 +36,10 @@ Readings taken where the pages are silent (each is listed again in the design doc):
   integers as load * N vs T * K;
 * E4M3 = OCP E4M3FN (bias 7, max 448, no infinities); q = RNE(fl32(v / s)) with
   s = fl32(amax / 448), saturating at +/-448, amax = 0 -> s = 1; the sign bit of q is the
-  sign bit of v (so a negative value that rounds to zero gives code 0x80).
+  sign bit of v (so a negative value that rounds to zero gives code 0x80);
+* power-of-two variant: the tile scale is the smallest 2^k with amax / 2^k <= 448
+  (k in [-127, 127], k = 0 for an all-zero tile), stored as the E8M0 code k + 127, and
+  q = RNE(v / 2^k) (an exact division).
 """
 from __future__ import annotations
 
@@ -176,6 +182,64 @@ def dequant_128x128(q, s) -> np.ndarray:
     n, k = q.shape
     v = e4m3_decode(q).reshape(n // 128, 128, k // 128, 128)
     return (v * s.astype(np.float64)[:, None, :, None]).reshape(n, k)
+
+
+# --------------------------------------------------------------------------------------
+# Power-of-two tile scales (a shared exponent per tile, stored as an E8M0 code).
+# [PFN] "学習と推論の課題と解決策": inside a 1x128 or 128x128 tile the values can share one
+# exponent; [TR] "考察" and [PFN] "ハードウェアデザインへの提案": the authors ask for tile /
+# block quantisation supported natively by the matrix unit.  Reading: the tile's scale is
+# the smallest power of two 2^k with amax / 2^k <= 448 (the fp32 rule s = amax / 448 rounded
+# up to a power of two), k clamped to [-127, 127]; an all-zero tile gets k = 0.  The code is
+# k + 127 (E8M0: value 2^(code - 127)).  Dividing by 2^k is exact, so q = RNE_E4M3(x / 2^k).
+# --------------------------------------------------------------------------------------
+
+E8M0_BIAS = 127
+
+
+def e8m0_exponent(amax) -> np.ndarray:
+    """k = the smallest integer with amax <= 448 * 2^k, clamped to [-127, 127]; 0 for amax = 0.
+
+    A first guess from log2 is corrected by the two exact comparisons of the definition
+    (448 * 2^k is exact in float64), so the result does not depend on log2's rounding."""
+    a = np.asarray(amax, dtype=np.float64)
+    pos = a > 0
+    with np.errstate(divide="ignore"):
+        k = np.where(pos, np.ceil(np.log2(np.where(pos, a, 1.0) / E4M3_MAX)), 0.0)
+    for _ in range(2):
+        k = np.where(pos & (a > E4M3_MAX * np.exp2(k)), k + 1, k)          # 2^k too small
+        k = np.where(pos & (a <= E4M3_MAX * np.exp2(k - 1)), k - 1, k)     # 2^(k-1) suffices
+    return np.clip(k, -127, 127).astype(np.int64)
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """Value of E8M0 codes 0..254: 2^(code - 127) (code 255 is NaN and never produced)."""
+    c = np.asarray(codes).astype(np.int64)
+    return np.where(c == 255, np.nan, np.exp2((c - E8M0_BIAS).astype(np.float64)))
+
+
+def quant_1x128_e8m0(x):
+    """1x128 tile quantisation with a power-of-two scale per tile (see above).
+    Returns (q uint8 [rows, cols], codes uint8 [rows, cols // 128])."""
+    x64 = np.asarray(x, dtype=np.float64)
+    rows, cols = x64.shape
+    assert cols % 128 == 0
+    t = x64.reshape(rows, cols // 128, 128)
+    k = e8m0_exponent(np.max(np.abs(t), axis=2))
+    q = e4m3_encode(t / np.exp2(k)[:, :, None]).reshape(rows, cols)
+    return q, (k + E8M0_BIAS).astype(np.uint8)
+
+
+def quant_128x128_e8m0(w):
+    """128x128 block quantisation with a power-of-two scale per block.
+    Returns (q uint8 [n, k], codes uint8 [n // 128, k // 128])."""
+    w64 = np.asarray(w, dtype=np.float64)
+    n, kk = w64.shape
+    assert n % 128 == 0 and kk % 128 == 0
+    b = w64.reshape(n // 128, 128, kk // 128, 128)
+    k = e8m0_exponent(np.max(np.abs(b), axis=(1, 3)))
+    q = e4m3_encode(b / np.exp2(k)[:, None, :, None]).reshape(n, kk)
+    return q, (k + E8M0_BIAS).astype(np.uint8)
 
 
 # --------------------------------------------------------------------------------------
@@ -375,7 +439,9 @@ def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str 
                  tile, weights per 128x128 block, h (as float32) re-quantised per 1x128
                  tile along I, products accumulated exactly (float64 stands in for the
                  FP32 promotion every 128 elements), routed outputs rounded to bf16,
-                 shared output to float32.
+                 shared output to float32;
+      "fp8_e8m0" -- the same with power-of-two tile scales (``quant_1x128_e8m0``,
+                 ``quant_128x128_e8m0``).
     workers > 1 evaluates the experts concurrently (same arithmetic, for large inputs).
     Returns (out [T, d] float64, extras dict with the permutation and per-row outputs).
     """
@@ -384,8 +450,8 @@ def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str 
     gate = np.asarray(gate, dtype=np.float64)
     T, K = idx.shape
     offsets, sorted_token, pair_pos = permute(idx, n_experts, 1)
-    if precision == "fp8":
-        xq, xs = quant_1x128(x)
+    if precision in ("fp8", "fp8_e8m0"):
+        xq, xs = _quantisers(precision)[1](x)
         x_in = dequant_1x128(xq, xs)
     else:
         x_in = x
@@ -407,12 +473,28 @@ def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str 
         results = [one(e) for e in todo]
     for e, lo, hi, y in results:
         if e < n_experts:
-            y_routed[lo:hi] = bf16_round(y) if precision in ("bf16", "fp8") else y
+            y_routed[lo:hi] = bf16_round(y) if precision != "exact" else y
         else:
-            y_shared[:] = fp32_round(y) if precision in ("bf16", "fp8") else y
+            y_shared[:] = fp32_round(y) if precision != "exact" else y
     out = combine(y_routed, y_shared, pair_pos, gate)
     return out, {"offsets": offsets, "sorted_token": sorted_token, "pair_pos": pair_pos,
                  "y_routed": y_routed, "y_shared": y_shared}
+
+
+def _quantisers(precision: str):
+    """(weight quantiser, activation quantiser) of an fp8 precision, each returning
+    (E4M3 codes, scale values as float64)."""
+    if precision == "fp8":
+        return quant_128x128, quant_1x128
+
+    def qw(w):
+        q, c = quant_128x128_e8m0(w)
+        return q, e8m0_decode(c)
+
+    def qa(x):
+        q, c = quant_1x128_e8m0(x)
+        return q, e8m0_decode(c)
+    return qw, qa
 
 
 def expert_rows(rows, w13, w2, precision: str = "exact", return_h: bool = False):
@@ -420,11 +502,12 @@ def expert_rows(rows, w13, w2, precision: str = "exact", return_h: bool = False)
     path), with the intermediate rounding of ``precision`` (see ``forward_sparse``).
     Returns y [m, d] before its own storage rounding (and h as stored, if asked)."""
     rows = np.asarray(rows, dtype=np.float64)
-    if precision == "fp8":
-        q13, s13 = quant_128x128(w13)
-        q2, s2 = quant_128x128(w2)
+    if precision in ("fp8", "fp8_e8m0"):
+        qw, qa = _quantisers(precision)
+        q13, s13 = qw(w13)
+        q2, s2 = qw(w2)
         h = swiglu_hidden(rows, dequant_128x128(q13, s13))
-        hq, hs = quant_1x128(fp32_round(h))
+        hq, hs = qa(fp32_round(h))
         h_st = dequant_1x128(hq, hs)
         y = h_st @ dequant_128x128(q2, s2).T
     else:

@@ -152,6 +152,113 @@ def pin_quant_exact_layouts():
     assert np.array_equal(got, (a_int @ b_int.T).astype(np.float64))
 
 
+# ------------------------------------------------------------------ power-of-two (E8M0) scales
+
+
+def _smallest_pow2_exponent(amax: float) -> int:
+    """Brute force over every exponent of the E8M0 range, in exact rational arithmetic."""
+    from fractions import Fraction
+    if amax == 0:
+        return 0
+    a = Fraction(float(amax))
+    for k in range(-127, 128):
+        if a <= 448 * Fraction(2) ** k:
+            return k
+    raise AssertionError("amax beyond 448 * 2^127")
+
+
+def pin_e8m0_exponent_bruteforce():
+    """The scale exponent is the smallest k with amax <= 448 * 2^k (clamped at -127),
+    checked against an exhaustive search at boundaries and on random magnitudes."""
+    r = _rng(11)
+    vals = [0.0, 1.0, 448.0, 224.0, 3.5, 1.75, 3.4e38, 2.0 ** -149, 2.0 ** -126, 1e-38]
+    for k in (-127, -60, -9, -1, 0, 1, 7, 60, 119):
+        b = 448.0 * 2.0 ** k
+        vals += [b, float(np.nextafter(np.float32(b), np.float32(np.inf))),
+                 float(np.nextafter(np.float32(b), np.float32(0)))]
+    vals += list((r.random(300) * 2.0 ** r.integers(-140, 120, 300)).astype(np.float32).astype(np.float64))
+    vals = np.array(vals, dtype=np.float64)
+    got = O.e8m0_exponent(vals)
+    want = np.array([_smallest_pow2_exponent(v) for v in vals])
+    assert np.array_equal(got, want), vals[got != want][:5]
+
+
+def pin_e8m0_format_constants():
+    """E8M0 (OCP microscaling scale format): unsigned 8-bit exponent, bias 127, 0xFF = NaN."""
+    assert O.e8m0_decode(np.uint8(127)) == 1.0 and O.e8m0_decode(np.uint8(128)) == 2.0
+    assert O.e8m0_decode(np.uint8(0)) == 2.0 ** -127 and O.e8m0_decode(np.uint8(254)) == 2.0 ** 127
+    assert np.isnan(O.e8m0_decode(np.uint8(255)))
+
+
+def pin_quant_e8m0_exact_layouts():
+    """Tiles of E4M3 numbers times a per-tile power of two, whose largest magnitude lies in
+    (224, 448] * 2^e, get code e + 127 and quantise exactly; distinct exponents per tile /
+    block catch a scale attached to the wrong tile.  A max just above 448 * 2^e moves to
+    code e + 128."""
+    r = _rng(12)
+    pos = O.e4m3_decode(np.arange(0, 127, dtype=np.uint8))
+    rows, cols = 6, 384
+    vals = pos[r.integers(0, 121, size=(rows, cols))] * np.where(r.random((rows, cols)) < 0.5, -1, 1)
+    e = r.integers(-20, 20, size=(rows, cols // 128))
+    x = vals.reshape(rows, 3, 128).copy()
+    x[:, :, 5] = np.where(r.random((rows, 3)) < 0.5, 448.0, -240.0)   # amax in (224, 448]
+    x = (x * np.exp2(e)[:, :, None]).reshape(rows, cols)
+    q, c = O.quant_1x128_e8m0(x)
+    assert c.dtype == np.uint8 and np.array_equal(c.astype(np.int64), e + 127)
+    assert np.array_equal(O.dequant_1x128(q, O.e8m0_decode(c)), x)
+    x2 = x.copy()
+    x2[0, 5] = 448.0 * 2.0 ** e[0, 0] * (1 + 2.0 ** -20)
+    _, c2 = O.quant_1x128_e8m0(x2)
+    assert int(c2[0, 0]) == e[0, 0] + 128 and np.array_equal(c2[1:], c[1:])
+    n, k = 256, 384
+    w = (pos[r.integers(0, 121, size=(n, k))] * np.where(r.random((n, k)) < 0.5, -1, 1)).reshape(2, 128, 3, 128)
+    eb = r.integers(-12, -2, size=(2, 3))
+    w[:, 3, :, 7] = -288.0
+    w = (w * np.exp2(eb)[:, None, :, None]).reshape(n, k)
+    qw, cw = O.quant_128x128_e8m0(w)
+    assert np.array_equal(cw.astype(np.int64), eb + 127)
+    assert np.array_equal(O.dequant_128x128(qw, O.e8m0_decode(cw)), w)
+
+
+def pin_quant_e8m0_against_fp32_rule():
+    """The power-of-two scale is the fp32 scale amax / 448 rounded up to a power of two
+    (so 1 <= s_pow2 / s_fp32 < 2), and the round trip stays within half an E4M3 step."""
+    r = _rng(13)
+    x = r.standard_normal((29, 512)).astype(np.float32)
+    x[3, 100] = 900.0
+    x[4, 128:256] = 0.0
+    x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    _, s32 = O.quant_1x128(x)
+    q, c = O.quant_1x128_e8m0(x)
+    s2 = O.e8m0_decode(c)
+    ratio = s2 / s32.astype(np.float64)
+    nz = np.abs(x).reshape(29, 4, 128).max(axis=2) > 0
+    assert np.all((ratio[nz] >= 1) & (ratio[nz] < 2)) and np.all(c[~nz] == 127)
+    deq = O.dequant_1x128(q, s2)
+    sc = np.repeat(s2, 128, axis=1)
+    assert np.all(np.abs(deq - x) <= O.e4m3_half_ulp(x / sc) * sc)
+
+
+def pin_fp8_e8m0_layer_close_to_exact():
+    """The power-of-two-scale fp8 layer approximates the exact layer about as well as the
+    fp32-scale one (at most one bit of headroom lost per tile)."""
+    r = _rng(14)
+    T, d, N, I = 16, 256, 4, 128
+    x = torch.from_numpy(r.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    wr = r.standard_normal((N, d)) * 0.05
+    b = np.zeros(N, np.float32)
+    w13 = r.standard_normal((N + 1, 2 * I, d)) * 0.05
+    w2 = r.standard_normal((N + 1, d, I)) * 0.05
+    ex, _, _ = O.forward(x, wr, b, w13, w2, 2, precision="exact")
+    f8, _, _ = O.forward(x, wr, b, w13, w2, 2, precision="fp8")
+    e8, _, _ = O.forward(x, wr, b, w13, w2, 2, precision="fp8_e8m0")
+    rms = np.sqrt(np.mean(ex ** 2))
+    err8 = np.sqrt(np.mean((e8 - ex) ** 2)) / rms
+    assert err8 < 0.1 and np.max(np.abs(e8 - ex)) / rms < 0.4
+    assert err8 < 2.0 * np.sqrt(np.mean((f8 - ex) ** 2)) / rms
+    assert not np.array_equal(e8, f8)  # the scale rule really differs
+
+
 # ------------------------------------------------------------------ routing
 
 

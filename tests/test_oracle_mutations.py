@@ -160,11 +160,35 @@ def _mut_quant_transposed_block_scale(mp):
     mp.setattr(O, "dequant_128x128", deq)
 
 
+def _mut_e8m0_floor(mp):
+    """Round the exponent down instead of up (the tile max then saturates)."""
+    def ex(amax):
+        a = np.asarray(amax, np.float64)
+        with np.errstate(divide="ignore"):
+            k = np.where(a > 0, np.floor(np.log2(np.where(a > 0, a, 1.0) / 448.0)), 0.0)
+        return np.clip(k, -127, 127).astype(np.int64)
+    mp.setattr(O, "e8m0_exponent", ex)
+
+
+def _mut_e8m0_bias_126(mp):
+    mp.setattr(O, "E8M0_BIAS", 126)
+
+
+def _mut_e8m0_scale_wrong_tile(mp):
+    real = O.quant_1x128_e8m0
+
+    def quant(x):
+        q, c = real(x)
+        return q, np.roll(c, 1, axis=1)  # each tile's code attached to its neighbour
+    mp.setattr(O, "quant_1x128_e8m0", quant)
+
+
 MUTATIONS = [
     _mut_gate_from_z, _mut_ascending, _mut_tie_higher_index, _mut_silu_sign, _mut_swap_w1_w3,
     _mut_bias_sign, _mut_bias_mean_off, _mut_e4m3_ties_odd, _mut_fnuz_scale,
     _mut_bf16_truncate, _mut_permute_token_desc, _mut_combine_no_shared,
     _mut_group_max_not_top2, _mut_sigmoid_softmax, _mut_quant_transposed_block_scale,
+    _mut_e8m0_floor, _mut_e8m0_bias_126, _mut_e8m0_scale_wrong_tile,
 ]
 
 
