@@ -10,7 +10,8 @@ before the timed region.  The headline workload is the DeepSeek-V3-shaped bf16 l
 T = 4096 tokens (d = 7168, 256 routed + 1 shared SwiGLU experts of width 2048, top-8);
 the fp8 layer at T = 16384, the group-limited bf16 layer at T = 8192 and the decode-shaped
 fp8 run (T = 256, Zipf-skewed bias, 100 steps of the bias update) are reported in the same
-line under "secondary".
+line under "secondary", with the fp8 layer at T = 16384 also run with power-of-two (E8M0)
+tile scales.  A workload name ending in "_e8m0" selects those scales for the main run.
 
 Prints ONE JSON line.  Weights are random (no checkpoint); inputs are seeded synthetic data.
 """
@@ -105,17 +106,17 @@ def run_layer_steps(torch, M, layer, xs, steps, warmup, timer_gate_up, gamma, up
         layer_mod.L.moe_grouped_gemm = orig
 
 
-def gate_up_bytes(cfg, counts_np, fp8: bool):
+def gate_up_bytes(cfg, counts_np, fp8: bool, scale_bytes: int = 4):
     """Algorithmic HBM bytes of one gate/up launch: the W13 of every expert with at least one
-    row (plus the shared one) read once, each gathered input row read once, h written once."""
+    row (plus the shared one) read once, each gathered input row read once, h written once
+    (fp8: with their scales, scale_bytes each)."""
     esz = 1 if fp8 else 2
+    sb = scale_bytes if fp8 else 0
     active = int((counts_np > 0).sum()) + 1
-    w = active * 2 * cfg.inter * cfg.d * esz
-    if fp8:
-        w += active * (2 * cfg.inter // 128) * (cfg.d // 128) * 4
+    w = active * 2 * cfg.inter * cfg.d * esz + active * (2 * cfg.inter // 128) * (cfg.d // 128) * sb
     rows = cfg.rows
-    a = rows * cfg.d * esz + (rows * (cfg.d // 128) * 4 if fp8 else 0)
-    h = rows * cfg.inter * esz + (rows * (cfg.inter // 128) * 4 if fp8 else 0)
+    a = rows * cfg.d * esz + rows * (cfg.d // 128) * sb
+    h = rows * cfg.inter * esz + rows * (cfg.inter // 128) * sb
     return w + a + h
 
 
@@ -173,8 +174,9 @@ def ingest_pmc(fetch_dir, write_dir, workload):
     """HBM bytes per launch of the gate/up kernel from FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by the factor that maps the same counter on a 1 GiB device copy
     to 1 GiB."""
-    fp8 = "fp8" in workload
-    want = f"{'true' if fp8 else 'false'}, true, {2 if fp8 else 0}>"
+    # template arguments <..., input kind (0 bf16, 1 E4M3 + f32 scales, 2 E4M3 + E8M0), SwiGLU, output>
+    kind = 2 if workload.endswith("_e8m0") else (1 if "fp8" in workload else 0)
+    want = f"{kind}, true, {2 if kind else 0}>"
     rec = {"workload": workload, "kernel_src_sha": kernel_src_sha(), "copy_bytes": COPY_BYTES}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _pmc_rows(d, counter)
@@ -272,7 +274,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     cfgs = {c.name: c for c in I.CONFIGS.values()}
-    cfg = cfgs[args.workload]
+    main_e8m0 = args.workload.endswith("_e8m0")
+    cfg = cfgs[args.workload[:-len("_e8m0")] if main_e8m0 else args.workload]
     t0 = time.time()
     log(f"[bench] generating V3 weights for {cfg.groups} experts ...")
     W13, W2 = I.gen_all_weights(cfg, dev)
@@ -280,9 +283,10 @@ def main():
     wr_cpu = I.gen_router(cfg).to(torch.bfloat16)
     wr = wr_cpu.to(dev)
 
-    def measure(cfg, fp8, steps, warmup, n_batches=1):
+    def measure(cfg, fp8, steps, warmup, n_batches=1, scales="f32"):
         bias_cpu = I.gen_bias(cfg)
-        layer = M.MoELayer(wr, W13, W2, bias_cpu.to(dev), cfg.top_k, cfg.n_group, cfg.topk_group, fp8=fp8)
+        layer = M.MoELayer(wr, W13, W2, bias_cpu.to(dev), cfg.top_k, cfg.n_group, cfg.topk_group, fp8=fp8,
+                           fp8_scales=scales)
         xs_cpu = [I.gen_x(cfg, step=None if n_batches == 1 else i) for i in range(n_batches)]
         xs = [x.to(dev) for x in xs_cpu]
         _, buf = layer.forward(xs[0], keep=True)
@@ -294,18 +298,19 @@ def main():
 
     # ---------------------------------------------------------------- headline workload
     fp8_main = cfg.dtype == "fp8"
-    layer, xs_cpu, bias_cpu, counts0, ms, gu_ms = measure(cfg, fp8_main, args.steps, args.warmup)
+    layer, xs_cpu, bias_cpu, counts0, ms, gu_ms = measure(cfg, fp8_main, args.steps, args.warmup,
+                                                          scales="e8m0" if main_e8m0 else "f32")
     flops = O.layer_flops(cfg.T, cfg.d, cfg.n_experts, cfg.top_k, cfg.inter)
     tok_s = cfg.T / (ms / 1e3)
-    gu_bytes = gate_up_bytes(cfg, counts0, fp8_main)
+    gu_bytes = gate_up_bytes(cfg, counts0, fp8_main, 1 if main_e8m0 else 4)
     achieved = gu_bytes / (gu_ms / 1e3) / 1e9
-    tag = f"gate_up_{cfg.name}"
+    tag = f"gate_up_{args.workload}"
     line = {
         "metric": "MoE-layer tokens/s + % MFMA peak (T=4096 bf16, T=16384 fp8); decode GB/s",
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8" if fp8_main else "bf16", "data": "synthetic (seeded N(0,1) x, random-init weights)",
-        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_routed": cfg.n_experts, "n_shared": 1,
+        "config": {"workload": args.workload, "T": cfg.T, "d_model": cfg.d, "n_routed": cfg.n_experts, "n_shared": 1,
                    "top_k": cfg.top_k, "inter": cfg.inter, "n_group": cfg.n_group, "topk_group": cfg.topk_group,
                    "step": "route+permute+gateup_swiglu+down+combine+bias_update"},
         "tflops": round(flops / (ms / 1e3) / 1e12, 2),
@@ -315,7 +320,7 @@ def main():
                      "traffic": measured_traffic(tag), "avg_launch_ms": round(gu_ms, 4),
                      "algorithmic_bytes_per_launch": int(gu_bytes)},
     }
-    log(f"[bench] {cfg.name}: {ms:.3f} ms/step, {tok_s:,.0f} tok/s, gate/up {gu_ms:.3f} ms ({achieved:.0f} GB/s)")
+    log(f"[bench] {args.workload}: {ms:.3f} ms/step, {tok_s:,.0f} tok/s, gate/up {gu_ms:.3f} ms ({achieved:.0f} GB/s)")
 
     # ---------------------------------------------------------------- secondary workloads
     if not args.no_secondary:
@@ -329,8 +334,18 @@ def main():
                     "mfma_frac_fp8_peak": round(f3 / (ms3 / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4),
                     "gate_up_ms": round(gu3, 4), "gate_up_traffic": measured_traffic(f"gate_up_{c3.name}"),
                     "gate_up_mfma_frac": round(fl3 / (gu3 / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4)})
-        log(f"[bench] {c3.name}: {ms3:.3f} ms/step")
+        log(f"[bench] {c3.name}: {ms3:.3f} ms/step, gate/up {gu3:.3f} ms")
         del l3
+        # the same layer with power-of-two (E8M0) tile scales applied by the matrix cores
+        l3e, _, _, _, ms3e, gu3e = measure(c3, True, max(5, args.steps // 2), 3, scales="e8m0")
+        sec.append({"workload": c3.name + "_e8m0", "dtype": "fp8", "scales": "e8m0", "ms_per_step": round(ms3e, 4),
+                    "tokens_per_s": round(c3.T / (ms3e / 1e3), 1), "tflops": round(f3 / (ms3e / 1e3) / 1e12, 2),
+                    "mfma_frac_fp8_peak": round(f3 / (ms3e / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                    "gate_up_ms": round(gu3e, 4),
+                    "gate_up_traffic": measured_traffic(f"gate_up_{c3.name}_e8m0"),
+                    "gate_up_mfma_frac": round(fl3 / (gu3e / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4)})
+        log(f"[bench] {c3.name}_e8m0: {ms3e:.3f} ms/step, gate/up {gu3e:.3f} ms")
+        del l3e
         c2 = I.V3_GROUP
         l2, _, _, _, ms2, _ = measure(c2, False, max(5, args.steps // 2), 3)
         f2 = O.layer_flops(c2.T, c2.d, c2.n_experts, c2.top_k, c2.inter)

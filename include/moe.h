@@ -58,6 +58,8 @@ enum {
 
 enum { MOE_BF16 = 0, MOE_F32 = 1, MOE_FP8_E4M3 = 2 };
 enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1 };
+/* Scale formats of FP8 tensors: float32 scales, or E8M0 codes (uint8, value 2^(code-127)). */
+enum { MOE_SCALE_F32 = 0, MOE_SCALE_E8M0 = 1 };
 
 /* Human-readable name of a status code (static string). */
 const char* moe_status_str(moe_status s);
@@ -151,6 +153,22 @@ moe_status fp8_quant_128x128(const uint16_t* w, int n_mats, int n, int k, uint8_
                              float* scale, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * fp8_quant_1x128_e8m0 / fp8_quant_128x128_e8m0 -- the same tiles with a power-of-two
+ * scale ("Vol.25 DeepSeek-V3の技術とその影響", "学習と推論の課題と解決策": the values of a
+ * 1x128 / 128x128 tile can share one exponent; "DeepSeek-V3 Technical Report", "考察", and
+ * the talk's "ハードウェアデザインへの提案": tile / block scaling supported by the matrix
+ * unit itself).  For each tile: k = the smallest integer with amax <= 448 * 2^k, clamped
+ * to [-127, 127] (k = 0 for an all-zero tile); scale code = k + 127 (E8M0, value
+ * 2^(code-127)); q = RNE_E4M3(x * 2^-k) (an exact product), the code's sign bit being x's.
+ * Arguments and limits as fp8_quant_1x128 / fp8_quant_128x128, with the scales written as
+ * uint8 codes: [rows, cols/128] and [n_mats, n/128, k/128].
+ * ------------------------------------------------------------------------------------ */
+moe_status fp8_quant_1x128_e8m0(const uint16_t* x, int rows, int cols, int64_t ldx, uint8_t* q,
+                                uint8_t* scale, hipStream_t stream);
+moe_status fp8_quant_128x128_e8m0(const uint16_t* w, int n_mats, int n, int k, uint8_t* q,
+                                  uint8_t* scale, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * moe_grouped_gemm -- one GEMM per expert over that expert's sorted rows:
  *   out[r, :] = A[r, :] . W[g]^T   for every row r of group g,
  * the expert FFN layers of "DeepSeek-V3 Technical Report", "DeepSeekMoE と補助損失なしの
@@ -162,6 +180,11 @@ moe_status fp8_quant_128x128(const uint16_t* w, int n_mats, int n, int k, uint8_
  * by s_A * s_W and added to an fp32 accumulator (the N_C = 128 promotion interval).  An
  * FP8 output (the gate/up projection feeding the down projection) is quantised per 1x128
  * tile exactly as fp8_quant_1x128 does.  bf16 inputs accumulate in fp32.
+ * With scale_fmt = MOE_SCALE_E8M0 every FP8 scale (a_scale, w_scale, out_scale) is an E8M0
+ * code (uint8, same shapes) as fp8_quant_*_e8m0 writes them: the matrix cores apply the
+ * power-of-two scales of both operands to each 128-element slice and accumulate straight
+ * into fp32 (no separate promotion step), and an FP8 output is quantised as
+ * fp8_quant_1x128_e8m0 does.
  *
  * Rows: group g (first_group <= g < first_group + n_groups) owns the sorted rows
  * [group_offsets[g], group_offsets[g+1]).  Row r reads A row a_rows[r] when a_rows is not
@@ -174,11 +197,12 @@ moe_status fp8_quant_128x128(const uint16_t* w, int n_mats, int n, int k, uint8_
 typedef struct moe_gemm_desc {
   int in_dtype;                 /* MOE_BF16 or MOE_FP8_E4M3 (both A and W) */
   const void* a;                /* device A [*, K], leading dimension lda (elements) */
-  const float* a_scale;         /* FP8: device f32 [*, K/128] (row-aligned with A); else NULL */
+  const void* a_scale;          /* FP8: device [*, K/128] scales (row-aligned with A), f32 or
+                                   E8M0 per scale_fmt; else NULL */
   const int32_t* a_rows;        /* device i32 gather index per sorted row, or NULL */
   int64_t lda;
   const void* w;                /* device W [G][N][K] contiguous, G > last group used */
-  const float* w_scale;         /* FP8: device f32 [G][N/128][K/128]; else NULL */
+  const void* w_scale;          /* FP8: device [G][N/128][K/128] scales per scale_fmt; else NULL */
   const int32_t* group_offsets; /* device i32, at least first_group + n_groups + 1 entries */
   int first_group;
   int n_groups;                 /* 1..1024 */
@@ -189,7 +213,7 @@ typedef struct moe_gemm_desc {
   void* out;                    /* device output, leading dimension ldo (elements) */
   int out_dtype;                /* MOE_BF16, MOE_F32, or MOE_FP8_E4M3 (+ out_scale) */
   int64_t ldo;
-  float* out_scale;             /* FP8 output: device f32 [rows, out_cols/128]; else NULL */
+  void* out_scale;              /* FP8 output: device [rows, out_cols/128] scales per scale_fmt */
   /* Optional split output: the last tail_groups groups write f32 rows to out_tail (row r of
    * such a group lands in out_tail row r - group_offsets[first_group + n_groups - tail_groups],
    * leading dimension ldo_tail) instead of out; the other groups write out as above.  One
@@ -198,6 +222,7 @@ typedef struct moe_gemm_desc {
   int tail_groups;
   void* out_tail;
   int64_t ldo_tail;
+  int scale_fmt;                /* MOE_SCALE_F32 (0) or MOE_SCALE_E8M0 (FP8 only) */
 } moe_gemm_desc;
 /* Limits: K a positive multiple of 64 (bf16) or 128 (FP8); N a positive multiple of 128 (bf16)
  * or 256 (FP8) -- with SWIGLU that is N/2 a multiple of 64 or 128; FP8 input needs a_scale and
@@ -205,7 +230,8 @@ typedef struct moe_gemm_desc {
  * output is bf16 or FP8; 1 <= n_groups <= 1024; 0 <= m_total < 2^31; one W[g] < 2 GiB;
  * lda/ldo keep rows 16-byte aligned.  A split output (tail_groups > 0) needs epilogue NONE,
  * out_dtype MOE_BF16, tail_groups <= n_groups and a 16-byte aligned out_tail with
- * ldo_tail >= N. */
+ * ldo_tail >= N.  E8M0 scales need K a multiple of 512 (each scale row is read 4 codes at a
+ * time). */
 moe_status moe_grouped_gemm(const moe_gemm_desc* desc, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------

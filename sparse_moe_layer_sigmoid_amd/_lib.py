@@ -16,12 +16,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(7)
 MOE_BF16, MOE_F32, MOE_FP8_E4M3 = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
+MOE_SCALE_F32, MOE_SCALE_E8M0 = 0, 1
 
 EXPORTS = (
     "moe_status_str", "moe_last_error", "moe_abi_version",
     "moe_route_workspace_size", "moe_route",
     "moe_permute_workspace_size", "moe_permute",
-    "fp8_quant_1x128", "fp8_quant_128x128",
+    "fp8_quant_1x128", "fp8_quant_128x128", "fp8_quant_1x128_e8m0", "fp8_quant_128x128_e8m0",
     "moe_grouped_gemm", "moe_combine", "moe_bias_update",
 )
 
@@ -38,7 +39,7 @@ class MoeGemmDesc(ctypes.Structure):
         ("w", _p), ("w_scale", _p), ("group_offsets", _p), ("first_group", _i),
         ("n_groups", _i), ("m_total", _i64), ("N", _i), ("K", _i), ("epilogue", _i),
         ("out", _p), ("out_dtype", _i), ("ldo", _i64), ("out_scale", _p),
-        ("tail_groups", _i), ("out_tail", _p), ("ldo_tail", _i64),
+        ("tail_groups", _i), ("out_tail", _p), ("ldo_tail", _i64), ("scale_fmt", _i),
     ]
 
 
@@ -77,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.fp8_quant_1x128.argtypes = [_p, _i, _i, _i64, _p, _p, _p]
         L.fp8_quant_128x128.restype = _i
         L.fp8_quant_128x128.argtypes = [_p, _i, _i, _i, _p, _p, _p]
+        L.fp8_quant_1x128_e8m0.restype = _i
+        L.fp8_quant_1x128_e8m0.argtypes = [_p, _i, _i, _i64, _p, _p, _p]
+        L.fp8_quant_128x128_e8m0.restype = _i
+        L.fp8_quant_128x128_e8m0.argtypes = [_p, _i, _i, _i, _p, _p, _p]
         L.moe_grouped_gemm.restype = _i
         L.moe_grouped_gemm.argtypes = [ctypes.POINTER(MoeGemmDesc), _p]
         L.moe_combine.restype = _i
@@ -157,30 +162,48 @@ def moe_permute(topk_idx, n_experts: int, n_shared: int = 1, out=None):
     return offs, st_, pp
 
 
-def fp8_quant_1x128(x, q=None, scale=None):
-    """x [rows, cols] bf16 (row stride may exceed cols) -> (q uint8 [rows, cols], scale f32 [rows, cols/128])."""
+def _quant_1x128(fn, sdtype, x, q, scale):
     _dev(x, torch.bfloat16, "x", contiguous=False)
     rows, cols = x.shape
     if x.stride(1) != 1:
         raise ValueError("x rows must be contiguous")
     q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
-    scale = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device) if scale is None else scale
-    st = lib().fp8_quant_1x128(_ptr(x), rows, cols, x.stride(0), _ptr(q), _ptr(scale), _stream(x))
-    _check("fp8_quant_1x128", st)
+    scale = torch.empty((rows, cols // 128), dtype=sdtype, device=x.device) if scale is None else scale
+    st = getattr(lib(), fn)(_ptr(x), rows, cols, x.stride(0), _ptr(q), _ptr(scale), _stream(x))
+    _check(fn, st)
     return q, scale
 
 
-def fp8_quant_128x128(w):
-    """w [n_mats, n, k] (or [n, k]) bf16 -> (q uint8 like w, scale f32 [n_mats, n/128, k/128])."""
+def _quant_128x128(fn, sdtype, w):
     _dev(w, torch.bfloat16, "w")
     squeeze = w.dim() == 2
     w3 = w.unsqueeze(0) if squeeze else w
     m, n, k = w3.shape
     q = torch.empty((m, n, k), dtype=torch.uint8, device=w.device)
-    s = torch.empty((m, n // 128, k // 128), dtype=torch.float32, device=w.device)
-    st = lib().fp8_quant_128x128(_ptr(w3), m, n, k, _ptr(q), _ptr(s), _stream(w))
-    _check("fp8_quant_128x128", st)
+    s = torch.empty((m, n // 128, k // 128), dtype=sdtype, device=w.device)
+    st = getattr(lib(), fn)(_ptr(w3), m, n, k, _ptr(q), _ptr(s), _stream(w))
+    _check(fn, st)
     return (q[0], s[0]) if squeeze else (q, s)
+
+
+def fp8_quant_1x128(x, q=None, scale=None):
+    """x [rows, cols] bf16 (row stride may exceed cols) -> (q uint8 [rows, cols], scale f32 [rows, cols/128])."""
+    return _quant_1x128("fp8_quant_1x128", torch.float32, x, q, scale)
+
+
+def fp8_quant_128x128(w):
+    """w [n_mats, n, k] (or [n, k]) bf16 -> (q uint8 like w, scale f32 [n_mats, n/128, k/128])."""
+    return _quant_128x128("fp8_quant_128x128", torch.float32, w)
+
+
+def fp8_quant_1x128_e8m0(x, q=None, scale=None):
+    """As fp8_quant_1x128 with power-of-two scales: scale = E8M0 codes, uint8 [rows, cols/128]."""
+    return _quant_1x128("fp8_quant_1x128_e8m0", torch.uint8, x, q, scale)
+
+
+def fp8_quant_128x128_e8m0(w):
+    """As fp8_quant_128x128 with power-of-two scales: scale = E8M0 codes, uint8 [n_mats, n/128, k/128]."""
+    return _quant_128x128("fp8_quant_128x128_e8m0", torch.uint8, w)
 
 
 _DT = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32, torch.uint8: MOE_FP8_E4M3}
@@ -192,8 +215,13 @@ def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_tot
     """out[r - off[first_group]] = epilogue(A[a_rows[r] or r] . W[g]^T) for each sorted row r
     of group g.  a: bf16 or uint8 (E4M3) [*, K]; w: same dtype [G, N, K]; out: bf16 / f32 /
     uint8 (E4M3, needs out_scale).  With tail_groups > 0 the last tail_groups groups write
-    f32 rows to out_tail instead (row r -> r - off[first_group + n_groups - tail_groups])."""
+    f32 rows to out_tail instead (row r -> r - off[first_group + n_groups - tail_groups]).
+    FP8 scales are f32, or E8M0 codes when they are uint8 tensors (all of them alike)."""
     fp8 = a.dtype == torch.uint8
+    scales = [s for s in (a_scale, w_scale, out_scale) if s is not None]
+    e8 = fp8 and any(s.dtype == torch.uint8 for s in scales)
+    if e8 and any(s.dtype != torch.uint8 for s in scales):
+        raise TypeError("FP8 scales must all be float32 or all uint8 (E8M0)")
     if w.dtype != a.dtype:
         raise TypeError("a and w must share a dtype")
     for t, nm in ((a, "a"), (w, "w"), (group_offsets, "group_offsets"), (out, "out")):
@@ -216,7 +244,8 @@ def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_tot
         out=out.data_ptr(), out_dtype=_DT[out.dtype], ldo=out.stride(0),
         out_scale=out_scale.data_ptr() if out_scale is not None else None,
         tail_groups=tail_groups, out_tail=out_tail.data_ptr() if tail_groups else None,
-        ldo_tail=out_tail.stride(0) if tail_groups else 0)
+        ldo_tail=out_tail.stride(0) if tail_groups else 0,
+        scale_fmt=MOE_SCALE_E8M0 if e8 else MOE_SCALE_F32)
     st = lib().moe_grouped_gemm(ctypes.byref(desc), _stream(a))
     _check("moe_grouped_gemm", st)
     return out

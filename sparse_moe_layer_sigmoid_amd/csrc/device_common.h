@@ -70,6 +70,19 @@ __device__ __forceinline__ float quotient(float v, float s, float rs) {
   return fmaf(fmaf(-q0, s, v), rs, q0);
 }
 
+// Power-of-two tile scale: the smallest k with amax <= 448 * 2^k, clamped to [-127, 127]
+// (0 for an all-zero tile), read off amax's bits: for amax = 1.f * 2^E, 448 = 1.75 * 2^8, so
+// k = E - 8 when the significand is <= 1.75 (fraction bits <= 0x600000), else E - 7.
+// Subnormal amax (< 2^-126) lies far below 448 * 2^-127 and takes the clamp.
+__device__ __forceinline__ int e8m0_exponent(float amax) {
+  const uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
+  const int e = (int)(u >> 23) - 127;
+  const int k = e - 8 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return u == 0 ? 0 : (u < 0x00800000u ? -127 : min(127, max(-127, k)));
+}
+// 2^k as a float for k in [-126, 127] (exact).
+__device__ __forceinline__ float pow2f(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
 // Matrix-core wrappers (gfx950).
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8_t& a, const bf16x8_t& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -77,6 +90,11 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8_t& a, const bf16x8_t& b,
 // 16x16x128 E4M3 x E4M3 -> f32 (format code 0 = E4M3 for both operands, no block scale).
 __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// The same with E8M0 block scales: each lane's operand rows (its 32 K values) are scaled by
+// 2^(code - 127) of the low byte of sa (first operand) / sb (second operand).
+__device__ __forceinline__ f32x4 mfma_fp8_e8m0(const i32x8& a, const i32x8& b, f32x4 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

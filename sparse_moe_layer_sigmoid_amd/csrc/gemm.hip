@@ -8,6 +8,11 @@
 //    16x16x128 MFMA whose partial sum is scaled by s_A * s_W and added to an fp32
 //    accumulator ("高精度累積", N_C = 128); the gate/up output feeding the down projection
 //    is re-quantised per 1x128 tile in the epilogue ("オンライン量子化").
+//  * Power-of-two tile scales ("Vol.25 DeepSeek-V3の技術とその影響", "学習と推論の課題と解決
+//    策": a tile shares one exponent; the report's "考察" asks for block scaling inside the
+//    matrix unit): with E8M0 scale codes the block-scaled MFMA applies 2^(code - 127) per
+//    operand row and 32-element K group itself, so every K slice accumulates straight into
+//    the fp32 accumulator (no partial sums, no promotion FMAs).
 //
 // Design (CDNA4 first):
 //  * Persistent workgroups, one per CU.  Each builds the per-expert tile table once (from the
@@ -78,11 +83,11 @@ typedef __attribute__((address_space(1))) void glb_void;
 
 struct GemmArgs {
   const uint8_t* a;
-  const float* a_scale;
+  const void* a_scale;   // f32 or E8M0 codes (u8)
   const int32_t* a_rows;
   int64_t lda_b;        // bytes per A row
   const uint8_t* w;
-  const float* w_scale;
+  const void* w_scale;
   const int32_t* offs;  // group_offsets + first_group (n_groups + 1 entries)
   int first_group;
   int n_groups;
@@ -94,7 +99,7 @@ struct GemmArgs {
   int n_tiles;          // output tiles along N
   uint8_t* out;
   int64_t ldo_b;        // bytes per output row
-  float* out_scale;
+  void* out_scale;
   int out_scale_ld;
   int tail_first;       // first group (relative) writing the f32 tail output; n_groups if none
   uint8_t* out_tail;
@@ -140,8 +145,11 @@ __device__ __forceinline__ TileInfo decode_tile(int L, const int* tstart, int G,
   return t;
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool FP8, bool SWIGLU, int OUT>
+// FP8: 0 = bf16 inputs; 1 = E4M3 with f32 scales (promotion every K slice); 2 = E4M3 with
+// E8M0 scales (applied by the matrix core).
+template <int BM, int BN, int WGM, int WGN, int STAGES, int FP8, bool SWIGLU, int OUT>
 __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p) {
+  constexpr bool E8 = FP8 == 2;
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM;  // rows per wave
   constexpr int WN = BN / WGN;  // W rows (output columns; gate+up for SwiGLU) per wave
@@ -158,12 +166,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   // two weight-block scales of the tile's columns for the same K blocks (SC_WS floats).  A
   // chunk's DMA is issued STAGES - 1 steps before its first step and overwrites the chunk
   // SC_NB earlier, whose last step is at least SC_NB steps back: SC_NB = STAGES keeps it behind
-  // the barrier of the issuing step.
-  constexpr int SC_CH = 8;
+  // the barrier of the issuing step.  E8M0 codes are bytes: a chunk then spans 256 * NW / BM
+  // K blocks, so that its A codes (one dword = 4 K blocks of a row) are one DMA per lane.
+  constexpr int SC_CH = E8 ? 256 * NW / BM : 8;
   constexpr int SC_NB = STAGES;
-  constexpr int SC_PW = FP8 ? BM * SC_CH / 64 / NW : 0;
-  constexpr int SC_WS = 2 * SC_CH;               // weight-scale area: [SC_CH][2]
-  constexpr int SC_BUF = BM * SC_CH + SC_WS;     // floats per chunk buffer
+  constexpr int SC_DW = E8 ? BM * SC_CH / 4 : BM * SC_CH;  // dwords of A scales per chunk
+  constexpr int SC_PW = FP8 ? SC_DW / 64 / NW : 0;
+  constexpr int SC_WS = E8 ? SC_CH / 2 : 2 * SC_CH;  // weight-scale dwords: [2 blocks][SC_CH K blocks]
+  constexpr int SC_BUF = SC_DW + SC_WS;              // dwords per chunk buffer
   constexpr int OC = SWIGLU ? BN / 2 : BN;
   // data DMA instructions per wave per stage: L_ISSUE at most, L_STAGE at least (the vmcnt
   // waits allow L_STAGE later instructions in flight; a wave that issued more only waits
@@ -171,8 +181,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   constexpr int L_ISSUE = A_PW + B_PW;
   constexpr int L_STAGE = A_PW_MIN + B_PW;
   static_assert(A_ROWS8 * 8 == BM && B_PW * 8 * NW == BN && A_PW_MIN >= 1, "DMA rows must split over waves");
-  static_assert(!FP8 || (SC_PW >= 1 && SC_PW * 64 * NW == BM * SC_CH && A_PW == A_PW_MIN),
+  static_assert(!FP8 || (SC_PW >= 1 && SC_PW * 64 * NW == SC_DW && A_PW == A_PW_MIN),
                 "scale chunk DMA must split evenly over waves");
+  static_assert(!E8 || (SC_CH % 4 == 0 && SC_WS <= 64), "E8M0 chunks hold whole dwords of 4 K blocks");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(!SWIGLU || TN % 2 == 0, "SwiGLU waves need matching gate and up tiles");
   static_assert(OUT != OUT_FP8 || (FP8 && SWIGLU && OC == 128), "fp8 output = one 1x128 tile per row");
@@ -262,7 +273,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   const uint8_t* a_ptr[A_PW];
   int a_nxt[A_PW];
   int b_off[B_PW];
-  const float* s_ptr[SC_PW > 0 ? SC_PW : 1];
+  const float* s_ptr[SC_PW > 0 ? SC_PW : 1];     // f32 scale rows
+  const uint8_t* s8_ptr[SC_PW > 0 ? SC_PW : 1];  // E8M0 code rows
   int s_nxt[SC_PW > 0 ? SC_PW : 1];
   // A-scale chunk layout: [BM / 4 row groups][SC_CH K blocks, swizzled][4 rows].  Row group
   // g = wm * 16 + lr holds rows wm * WM + i * 16 + lr (i = 0..3), the four rows whose products
@@ -271,19 +283,32 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   // 256-byte bank row) on distinct banks.
   // DMA lane (instruction q, lane l) fills dword d = q * 64 + l: row group d / 32, slot
   // (d / 4) % 8, row index d % 4; its 8 consecutive slots of a row read 32 contiguous bytes.
-  static_assert(SC_CH == 8, "the scale swizzle assumes 8 K blocks per chunk");
+  static_assert(E8 || SC_CH == 8, "the scale swizzle assumes 8 K blocks per chunk");
   int sc_col[SC_PW > 0 ? SC_PW : 1];  // K block (within a chunk) that each scale DMA of this lane fetches
   int sc_row[SC_PW > 0 ? SC_PW : 1];  // tile row that each scale DMA of this lane fetches
+  // E8M0 chunk layout: [BM / 4 row groups][SC_CH / 4 dwords of 4 K blocks][4 rows], so a K
+  // step reads the codes of a lane's four rows with one 16-byte read; DMA dword d holds row
+  // index d % 4 of group d / SC_CH, K blocks 4 * ((d / 4) % (SC_CH / 4)) .. + 3.
 #pragma unroll
   for (int i = 0; i < SC_PW; ++i) {
     const int d = (wave * SC_PW + i) * 64 + lane;
-    const int grp = d >> 5;
-    sc_col[i] = ((d >> 2) & 7) ^ ((grp >> 1) & 7);
-    sc_row[i] = (grp >> 4) * WM + (d & 3) * 16 + (grp & 15);
+    if constexpr (E8) {
+      const int grp = d / SC_CH;
+      sc_col[i] = 4 * ((d >> 2) % (SC_CH / 4));
+      sc_row[i] = (grp >> 4) * WM + (d & 3) * 16 + (grp & 15);
+    } else {
+      const int grp = d >> 5;
+      sc_col[i] = ((d >> 2) & 7) ^ ((grp >> 1) & 7);
+      sc_row[i] = (grp >> 4) * WM + (d & 3) * 16 + (grp & 15);
+    }
   }
   // weight-block scales (lanes 0..15 of wave 0): lane l loads K block l >> 1 of block l & 1 --
   // the gate and up blocks under SwiGLU, else the tile's two 128-column blocks
-  const float* w_sc_ptr = p.w_scale;
+  const float* w_sc_ptr = static_cast<const float*>(p.w_scale);
+  // E8M0: lane l < SC_WS loads the dword of K blocks 4 * (l % (SC_CH / 4)) .. + 3 of weight
+  // block l / (SC_CH / 4) (gate / up under SwiGLU, else the tile's two 128-column blocks)
+  const uint8_t* w_sc8 = static_cast<const uint8_t*>(p.w_scale);
+  const int w_kq4 = 4 * (lane % (SC_CH / 4 > 0 ? SC_CH / 4 : 1));
   int sc_issue = 0;                 // buffer of the next chunk to issue
   int lq = -1;  // index (in this workgroup's list) of the tile being loaded
   const uint8_t* wbase = p.w;
@@ -311,7 +336,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       a_ptr[i] = p.a + (int64_t)src[i] * p.lda_b + ((cch ^ (rr & 7)) << 4);
     }
 #pragma unroll
-    for (int i = 0; i < SC_PW; ++i) s_ptr[i] = p.a_scale + (int64_t)ssrc[i] * p.ksb;
+    for (int i = 0; i < SC_PW; ++i) {
+      if constexpr (E8) s8_ptr[i] = static_cast<const uint8_t*>(p.a_scale) + (int64_t)ssrc[i] * p.ksb;
+      else s_ptr[i] = static_cast<const float*>(p.a_scale) + (int64_t)ssrc[i] * p.ksb;
+    }
   };
   auto set_b = [&](const TileInfo& t) {
 #pragma unroll
@@ -323,10 +351,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       b_off[i] = (int)(n * p.w_row_b) + ((cch ^ (rr & 7)) << 4);
     }
     wbase = p.w + (int64_t)(p.first_group + t.g) * p.N * p.w_row_b;
-    if (FP8) {
+    if constexpr (E8) {
+      const int sel = (lane / (SC_CH / 4)) & 1;
+      const int nblk = SWIGLU ? (sel ? p.N / 2 + t.nt * (BN / 2) : t.nt * (BN / 2)) / 128 : (t.nt * BN) / 128 + sel;
+      w_sc8 = static_cast<const uint8_t*>(p.w_scale) + ((int64_t)(p.first_group + t.g) * (p.N / 128) + nblk) * p.ksb;
+    } else if constexpr (FP8 != 0) {
       const int sel = lane & 1;
       const int nblk = SWIGLU ? (sel ? p.N / 2 + t.nt * (BN / 2) : t.nt * (BN / 2)) / 128 : (t.nt * BN) / 128 + sel;
-      w_sc_ptr = p.w_scale + ((int64_t)(p.first_group + t.g) * (p.N / 128) + nblk) * p.ksb + ((lane & 15) >> 1);
+      w_sc_ptr = static_cast<const float*>(p.w_scale) + ((int64_t)(p.first_group + t.g) * (p.N / 128) + nblk) * p.ksb +
+                 ((lane & 15) >> 1);
     }
   };
   // issue the DMA of global step js (clamped to the last step: every step issues one batch,
@@ -346,7 +379,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       lq = q;
     }
     dma_kt = kt;
-    dma_scales = FP8 && !past_end && kt % SC_CH == 0;
+    dma_scales = FP8 != 0 && !past_end && kt % SC_CH == 0;
   };
   // data DMA instruction k (0 .. L_ISSUE - 1: A rows, then B rows) of the prepared batch into
   // ring slot SL
@@ -369,13 +402,23 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     if (dma_scales) {
       const int kt = dma_kt;
       float* sc = s_sc + sc_issue * SC_BUF;
+      if constexpr (E8) {  // dwords of 4 codes; the last dword of a row is the clamp (ksb % 4 == 0)
 #pragma unroll
-      for (int i = 0; i < SC_PW; ++i)
-        __builtin_amdgcn_global_load_lds((glb_void*)(s_ptr[i] + min(kt + sc_col[i], p.ksb - 1)),
-                                         (lds_void*)(sc + (wave * SC_PW + i) * 64), 4, 0, 0);
-      if (wave == 0 && lane < SC_WS)
-        __builtin_amdgcn_global_load_lds((glb_void*)(w_sc_ptr + min(kt, p.ksb - 1 - ((lane & 15) >> 1))),
-                                         (lds_void*)(sc + BM * SC_CH), 4, 0, 0);
+        for (int i = 0; i < SC_PW; ++i)
+          __builtin_amdgcn_global_load_lds((glb_void*)(s8_ptr[i] + min(kt + sc_col[i], p.ksb - 4)),
+                                           (lds_void*)(sc + (wave * SC_PW + i) * 64), 4, 0, 0);
+        if (wave == 0 && lane < SC_WS)
+          __builtin_amdgcn_global_load_lds((glb_void*)(w_sc8 + min(kt + w_kq4, p.ksb - 4)), (lds_void*)(sc + SC_DW), 4,
+                                           0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < SC_PW; ++i)
+          __builtin_amdgcn_global_load_lds((glb_void*)(s_ptr[i] + min(kt + sc_col[i], p.ksb - 1)),
+                                           (lds_void*)(sc + (wave * SC_PW + i) * 64), 4, 0, 0);
+        if (wave == 0 && lane < SC_WS)
+          __builtin_amdgcn_global_load_lds((glb_void*)(w_sc_ptr + min(kt, p.ksb - 1 - ((lane & 15) >> 1))),
+                                           (lds_void*)(sc + BM * SC_CH), 4, 0, 0);
+      }
       sc_issue = sc_issue + 1 == SC_NB ? 0 : sc_issue + 1;
     }
   };
@@ -426,7 +469,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   const int fa_lo = (wm * WM + lr) * 128 + sw_lo, fa_hi = (wm * WM + lr) * 128 + sw_hi;
   const int fb_row = SWIGLU ? wn * (WN / 2) + lr : wn * WN + lr;
   const int fb_lo = fb_row * 128 + sw_lo, fb_hi = fb_row * 128 + sw_hi;
-  const int fs_off = (wm * 16 + lr) * (SC_CH * 4);  // this lane's scale row group
+  const int fs_off = (wm * 16 + lr) * (SC_CH * 4);  // this lane's scale row group (f32)
+  const int fs8_off = (wm * 16 + lr) * SC_CH;       // ... (E8M0: dwords)
   const int base_row = load_offset(p.offs, 0);
   const int tail_row = load_offset(p.offs, min(p.tail_first, G));
   int sc_use = 0;  // buffer of the chunk being consumed (same sequence as sc_issue)
@@ -490,6 +534,48 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     }
   };
 
+  // ---- E8M0 K step: the same operand reads, the codes of the lane's four rows (one 16-byte
+  // read, byte kc % 4 of each dword) and of the two weight blocks; every product goes straight
+  // into its accumulator with the codes as the MFMA's block scales ----
+  auto e8_read = [&](const uint8_t* As, int kt, i32x8(&af)[TM], i32x8(&bfr)[TN], int(&sa)[TM], int& sw0, int& sw1)
+      __attribute__((always_inline)) {
+    const uint8_t* Bs = As + A_BYTES;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const u32x4 lo = *(const u32x4*)(As + fa_lo + i * 16 * 128);
+      const u32x4 hi = *(const u32x4*)(As + fa_hi + i * 16 * 128);
+      af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+#pragma unroll
+    for (int jj = 0; jj < TN; ++jj) {
+      const int ro = (SWIGLU && jj >= TN / 2 ? BN / 2 + (jj - TN / 2) * 16 : jj * 16) * 128;
+      const u32x4 lo = *(const u32x4*)(Bs + fb_lo + ro);
+      const u32x4 hi = *(const u32x4*)(Bs + fb_hi + ro);
+      bfr[jj] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    const int kc = kt % SC_CH;
+    const uint32_t* scb = reinterpret_cast<const uint32_t*>(s_sc) + sc_use * SC_BUF;
+    const u32x4 d4 = *(const u32x4*)(scb + fs8_off + ((kc >> 2) << 2));
+    const int sh = (kc & 3) << 3;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] = (int)((d4[i] >> sh) & 255u);
+    const uint32_t* swp = scb + SC_DW + (kc >> 2);
+    const uint32_t w0 = swp[0], w1 = swp[SC_CH / 4];
+    sw0 = (int)(((SWIGLU || (wn * WN) / 128 == 0 ? w0 : w1) >> sh) & 255u);
+    sw1 = (int)((w1 >> sh) & 255u);
+    if (kc == SC_CH - 1 || kt == ksteps - 1) sc_use = sc_use + 1 == SC_NB ? 0 : sc_use + 1;  // chunk done
+  };
+  auto e8_math = [&](auto slot_c, const i32x8(&af)[TM], const i32x8(&bfr)[TN], const int(&sa)[TM], int sw0, int sw1)
+      __attribute__((always_inline)) {
+    constexpr int NT = TM * TN;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int i = t / TN, jj = t % TN;
+      acc[i][jj] = mfma_fp8_e8m0(bfr[jj], af[i], acc[i][jj], SWIGLU && jj >= TN / 2 ? sw1 : sw0, sa[i]);
+      dma_in(slot_c, t, NT);
+    }
+  };
+
   // ---- epilogue of a tile: values (SwiGLU applied; the accumulators restart at zero), the
   // per-row amax of an E4M3 output into s_red, then the stores ----
   auto epi_values = [&](float(&v)[TM][TO][4]) __attribute__((always_inline)) {
@@ -533,18 +619,35 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
           float amax = 0.f;
 #pragma unroll
           for (int q = 0; q < WGN; ++q) amax = fmaxf(amax, s_red[q * BM + m]);
-          const float s = (amax == 0.f) ? 1.0f : amax / 448.0f;
-          const float rs = recip_refined(s);
-          if (m < et.nrows) {
-            uint8_t* orow = p.out + (orow0 + m) * p.ldo_b;
+          if constexpr (E8) {  // power-of-two scale: exact products by 2^-k
+            const int k = e8m0_exponent(amax);
+            const float inv = pow2f(-k);
+            if (m < et.nrows) {
+              uint8_t* orow = p.out + (orow0 + m) * p.ldo_b;
 #pragma unroll
-            for (int jj = 0; jj < TO; ++jj) {
-              uint32_t w4 = 0;
+              for (int jj = 0; jj < TO; ++jj) {
+                uint32_t w4 = 0;
 #pragma unroll
-              for (int r = 0; r < 4; ++r) w4 |= f32_to_e4m3(quotient(v[i][jj][r], s, rs)) << (8 * r);
-              *reinterpret_cast<uint32_t*>(orow + c0 + jj * 16) = w4;
+                for (int r = 0; r < 4; ++r) w4 |= f32_to_e4m3(v[i][jj][r] * inv) << (8 * r);
+                *reinterpret_cast<uint32_t*>(orow + c0 + jj * 16) = w4;
+              }
+              if (wn == 0 && lg == 0)
+                static_cast<uint8_t*>(p.out_scale)[(orow0 + m) * p.out_scale_ld + et.nt] = (uint8_t)(k + 127);
             }
-            if (wn == 0 && lg == 0) p.out_scale[(orow0 + m) * p.out_scale_ld + et.nt] = s;
+          } else {
+            const float s = (amax == 0.f) ? 1.0f : amax / 448.0f;
+            const float rs = recip_refined(s);
+            if (m < et.nrows) {
+              uint8_t* orow = p.out + (orow0 + m) * p.ldo_b;
+#pragma unroll
+              for (int jj = 0; jj < TO; ++jj) {
+                uint32_t w4 = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) w4 |= f32_to_e4m3(quotient(v[i][jj][r], s, rs)) << (8 * r);
+                *reinterpret_cast<uint32_t*>(orow + c0 + jj * 16) = w4;
+              }
+              if (wn == 0 && lg == 0) static_cast<float*>(p.out_scale)[(orow0 + m) * p.out_scale_ld + et.nt] = s;
+            }
           }
         } else if (m < et.nrows) {
           if (tail) {
@@ -639,6 +742,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
               dma_in(dslot, (ks * TM + i) * TN + jj, 2 * TM * TN);
             }
         }
+      } else if constexpr (E8) {
+        i32x8 af[TM], bfr[TN];
+        int sa[TM], sw0, sw1;
+        e8_read(As, kt, af, bfr, sa, sw0, sw1);
+        e8_math(dslot, af, bfr, sa, sw0, sw1);
       } else {
         i32x8 af[TM], bfr[TN];
         float s0[TM], s1[TM];
@@ -690,7 +798,7 @@ int device_cus() {
 constexpr size_t kLdsBytes = 160 * 1024;
 
 // Static LDS of one kernel instantiation (queried once).
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool FP8, bool SWIGLU, int OUT>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int FP8, bool SWIGLU, int OUT>
 size_t static_lds() {
   static size_t bytes = 0;
   if (bytes == 0) {
@@ -704,12 +812,12 @@ size_t static_lds() {
   return bytes;
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool FP8, bool SWIGLU, int OUT>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int FP8, bool SWIGLU, int OUT>
 bool fits(const GemmArgs& a) {
   return static_lds<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT>() + (size_t)(a.n_groups + 1) * 4 <= kLdsBytes;
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool FP8, bool SWIGLU, int OUT>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int FP8, bool SWIGLU, int OUT>
 void launch(GemmArgs a, int64_t m_total, hipStream_t stream) {
   a.n_tiles = a.out_cols / (SWIGLU ? BN / 2 : BN);
   const int64_t mtiles = (m_total + (int64_t)a.n_groups * (BM - 1)) / BM;
@@ -731,12 +839,11 @@ bool prefer_tall_rows(int64_t m_total, int n_groups) {
   const double mu = (double)m_total / n_groups;
   if (mu < 96.0) return false;
   const double sd = sqrt(mu);
-  double e128 = 0, e160 = 0, wsum = 0;
+  double e128 = 0, e160 = 0;
   for (int k = -8; k <= 8; ++k) {
     const double z = k * 0.375, w = exp(-0.5 * z * z), rows = fmax(1.0, mu + z * sd);
     e128 += w * ceil(rows / 128.0);
     e160 += w * ceil(rows / 160.0);
-    wsum += w;
   }
   return e160 * 1.11 < e128;
 }
@@ -746,7 +853,7 @@ bool prefer_tall_rows(int64_t m_total, int n_groups) {
 // where its LDS (147 KB of ring, the scale chunks and the tile table) fits, else two slots.
 // Decode-sized groups: 64-row blocks, 8 waves of 64x32.
 // Narrow bf16 outputs (N/2 or N not a multiple of 128 / 256): 128-column blocks, 4 waves.
-template <bool FP8, bool SWIGLU, int OUT>
+template <int FP8, bool SWIGLU, int OUT>
 void dispatch(const GemmArgs& a, int64_t m_total, bool small, bool narrow, hipStream_t stream) {
   if constexpr (!FP8) {
     if (narrow) {
@@ -798,6 +905,11 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
               "moe_grouped_gemm: N=%d must be a positive multiple of %d%s", d->N, ncols_min,
               swiglu ? " (N/2 gate + N/2 up rows)" : "");
   if (fp8) MOE_REQUIRE(d->a_scale && d->w_scale, MOE_ERR_NULL, "moe_grouped_gemm: FP8 inputs need a_scale and w_scale");
+  MOE_REQUIRE(d->scale_fmt == MOE_SCALE_F32 || d->scale_fmt == MOE_SCALE_E8M0, MOE_ERR_DTYPE,
+              "moe_grouped_gemm: unknown scale_fmt %d", d->scale_fmt);
+  const bool e8 = fp8 && d->scale_fmt == MOE_SCALE_E8M0;
+  MOE_REQUIRE(!e8 || d->K % 512 == 0, MOE_ERR_SHAPE,
+              "moe_grouped_gemm: E8M0 scales need K a multiple of 512 (K=%d)", d->K);
   if (d->out_dtype == MOE_FP8_E4M3) MOE_REQUIRE(d->out_scale, MOE_ERR_NULL, "moe_grouped_gemm: FP8 output needs out_scale");
   const int esz = fp8 ? 1 : 2;
   const int osz = d->out_dtype == MOE_F32 ? 4 : (d->out_dtype == MOE_BF16 ? 2 : 1);
@@ -848,15 +960,21 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
   // Tile shape by regime: many rows per expert -> 128-row blocks; few (decode) -> 64.
   const bool small = d->m_total / d->n_groups < 64;
   if (!fp8) {
-    if (swiglu) dispatch<false, true, OUT_BF16>(a, d->m_total, small, narrow, stream);
-    else if (d->out_dtype == MOE_BF16) dispatch<false, false, OUT_BF16>(a, d->m_total, small, narrow, stream);
-    else dispatch<false, false, OUT_F32>(a, d->m_total, small, narrow, stream);
+    if (swiglu) dispatch<0, true, OUT_BF16>(a, d->m_total, small, narrow, stream);
+    else if (d->out_dtype == MOE_BF16) dispatch<0, false, OUT_BF16>(a, d->m_total, small, narrow, stream);
+    else dispatch<0, false, OUT_F32>(a, d->m_total, small, narrow, stream);
+  } else if (!e8) {
+    if (swiglu) {
+      if (d->out_dtype == MOE_FP8_E4M3) dispatch<1, true, OUT_FP8>(a, d->m_total, small, narrow, stream);
+      else dispatch<1, true, OUT_BF16>(a, d->m_total, small, narrow, stream);
+    } else if (d->out_dtype == MOE_BF16) dispatch<1, false, OUT_BF16>(a, d->m_total, small, narrow, stream);
+    else dispatch<1, false, OUT_F32>(a, d->m_total, small, narrow, stream);
   } else {
     if (swiglu) {
-      if (d->out_dtype == MOE_FP8_E4M3) dispatch<true, true, OUT_FP8>(a, d->m_total, small, narrow, stream);
-      else dispatch<true, true, OUT_BF16>(a, d->m_total, small, narrow, stream);
-    } else if (d->out_dtype == MOE_BF16) dispatch<true, false, OUT_BF16>(a, d->m_total, small, narrow, stream);
-    else dispatch<true, false, OUT_F32>(a, d->m_total, small, narrow, stream);
+      if (d->out_dtype == MOE_FP8_E4M3) dispatch<2, true, OUT_FP8>(a, d->m_total, small, narrow, stream);
+      else dispatch<2, true, OUT_BF16>(a, d->m_total, small, narrow, stream);
+    } else if (d->out_dtype == MOE_BF16) dispatch<2, false, OUT_BF16>(a, d->m_total, small, narrow, stream);
+    else dispatch<2, false, OUT_F32>(a, d->m_total, small, narrow, stream);
   }
   return check_launch("moe_grouped_gemm");
 }

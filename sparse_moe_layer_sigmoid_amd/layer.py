@@ -21,10 +21,13 @@ from . import _lib as L
 
 class MoELayer:
     def __init__(self, w_router, W13, W2, bias, top_k: int, n_group: int = 1, topk_group: int = 1,
-                 fp8: bool = False):
+                 fp8: bool = False, fp8_scales: str = "f32"):
         """w_router [N, d] bf16; W13 [N+1, 2I, d] bf16 (rows [0,I) gate, [I,2I) up; expert N is
         the shared one); W2 [N+1, d, I] bf16; bias [N] f32.  With fp8=True the weights are
-        block-quantised once (128x128, E4M3) and the layer runs the FP8 path."""
+        block-quantised once (128x128, E4M3) and the layer runs the FP8 path, with f32 tile
+        scales (fp8_scales="f32") or power-of-two ones stored as E8M0 codes ("e8m0")."""
+        if fp8_scales not in ("f32", "e8m0"):
+            raise ValueError(f"fp8_scales must be 'f32' or 'e8m0', got {fp8_scales!r}")
         self.w_router = w_router
         self.bias = bias
         self.N = w_router.shape[0]
@@ -34,9 +37,11 @@ class MoELayer:
         self.n_group = n_group
         self.topk_group = topk_group
         self.fp8 = fp8
+        self.e8m0 = fp8 and fp8_scales == "e8m0"
         if fp8:
-            self.W13, self.W13_s = L.fp8_quant_128x128(W13)
-            self.W2, self.W2_s = L.fp8_quant_128x128(W2)
+            qw = L.fp8_quant_128x128_e8m0 if self.e8m0 else L.fp8_quant_128x128
+            self.W13, self.W13_s = qw(W13)
+            self.W2, self.W2_s = qw(W2)
         else:
             self.W13, self.W13_s = W13, None
             self.W2, self.W2_s = W2, None
@@ -51,9 +56,9 @@ class MoELayer:
         offs, sorted_token, pair_pos = L.moe_permute(idx, N, 1)
         rows = T * (K + 1)
         if self.fp8:
-            xq, xs = L.fp8_quant_1x128(x)
+            xq, xs = (L.fp8_quant_1x128_e8m0 if self.e8m0 else L.fp8_quant_1x128)(x)
             h = torch.empty((rows, I), dtype=torch.uint8, device=dev)
-            hs = torch.empty((rows, I // 128), dtype=torch.float32, device=dev)
+            hs = torch.empty((rows, I // 128), dtype=xs.dtype, device=dev)
             L.moe_grouped_gemm(xq, self.W13, offs, 0, N + 1, rows, h, a_scale=xs, a_rows=sorted_token,
                                w_scale=self.W13_s, swiglu=True, out_scale=hs)
         else:

@@ -94,7 +94,7 @@ def check_permutation_properties(offs, sorted_token, pair_pos, idx, n_experts):
 FP8_DOT_REL = 2.0 ** -10
 
 
-def fp8_staged_check(pick, x_rows, gi, pp, gate_of, n_experts, expert_weights, buf, out32, tol):
+def fp8_staged_check(pick, x_rows, gi, pp, gate_of, n_experts, expert_weights, buf, out32, tol, e8m0=False):
     """The fp8 layer checked stage by stage on the tokens `pick`.
 
     The stored h of the fp8 path is an E4M3 code chosen by rounding a floating-point value,
@@ -108,16 +108,22 @@ def fp8_staged_check(pick, x_rows, gi, pp, gate_of, n_experts, expert_weights, b
     x_rows: [len(pick), d] the picked tokens' bf16 inputs (float64).
     gi, pp: the device's top-K indices and pair rows (numpy), for all tokens.
     gate_of(t, e): the oracle's gate of expert e for token t.
+    e8m0: the power-of-two scale variant (the device's scales are E8M0 codes); a device h
+    scale may then be the neighbouring power of two when the tile max lies within the
+    dot-product error of a power-of-two boundary.
     Returns (staged error, fraction of h codes equal to the oracle's)."""
+    qw, qa = O._quantisers("fp8_e8m0" if e8m0 else "fp8")
     h_codes = buf["h"].cpu().numpy()
     h_scales = buf["hs"].cpu().numpy()
+    if e8m0:
+        h_scales = O.e8m0_decode(h_scales)
     shared_base = int(buf["expert_offsets"][n_experts].item())
     K = gi.shape[1]
-    xq, xs = O.quant_1x128(O.fp32_round(x_rows))
-    xd = O.dequant_1x128(xq, xs)
+    xd = O.dequant_1x128(*qa(O.fp32_round(x_rows)))
+
     def deq_pair(e):
         w13, w2 = expert_weights(e)
-        return O.dequant_128x128(*O.quant_128x128(w13)), O.dequant_128x128(*O.quant_128x128(w2))
+        return O.dequant_128x128(*qw(w13)), O.dequant_128x128(*qw(w2))
 
     needed = sorted({int(e) for t in pick for e in gi[t]} | {n_experts})
     with ThreadPoolExecutor(16) as ex:
@@ -141,15 +147,22 @@ def fp8_staged_check(pick, x_rows, gi, pp, gate_of, n_experts, expert_weights, b
             dc = FP8_DOT_REL * (np.abs(xd[j]) @ np.abs(w13[inter:]).T)
             eps = 1.1 * da * np.abs(c) + np.abs(O.silu(a)) * dc + da * dc + 2.0 ** -18 * np.abs(h)
             s_dev = h_scales[row].astype(np.float64)
-            s_orc = O.quant_1x128(O.fp32_round(h[None]))[1][0].astype(np.float64)
+            s_orc = qa(O.fp32_round(h[None]))[1][0].astype(np.float64)
             tile_eps = eps.reshape(-1, 128).max(axis=1)
-            assert np.all(np.abs(s_dev - s_orc) <= tile_eps / 448 + 2.0 ** -22 * s_orc), (t, e)
+            if e8m0:
+                amax = np.abs(h).reshape(-1, 128).max(axis=1)
+                may_be_zero = amax - tile_eps <= 0  # an all-zero tile takes scale 1
+                lo = np.where(may_be_zero, 2.0 ** -127, np.exp2(O.e8m0_exponent(np.maximum(amax - tile_eps, 0.0))))
+                hi = np.maximum(np.exp2(O.e8m0_exponent(amax + tile_eps)), np.where(may_be_zero, 1.0, 0.0))
+                assert np.all((s_dev >= np.minimum(lo, s_orc)) & (s_dev <= np.maximum(hi, s_orc))), (t, e)
+            else:
+                assert np.all(np.abs(s_dev - s_orc) <= tile_eps / 448 + 2.0 ** -22 * s_orc), (t, e)
             s_el = np.repeat(s_dev, 128)
             h_dev = O.dequant_1x128(h_codes[row][None], h_scales[row][None])[0]
             step = O.e4m3_half_ulp(np.minimum((np.abs(h) + eps) / s_el, 448.0)) * s_el
             bad = np.abs(h_dev - h) > step * 1.0001 + eps
             assert not bad.any(), (t, e, np.nonzero(bad)[0][:5], h_dev[bad][:5], h[bad][:5])
-            n_same += int(np.sum(h_codes[row] == O.quant_1x128(O.fp32_round(h[None]))[0][0]))
+            n_same += int(np.sum(h_codes[row] == qa(O.fp32_round(h[None]))[0][0]))
             n_all += h.size
             y = h_dev @ w2.T
             if k < K:

@@ -30,7 +30,7 @@ def test_header_declares_exactly_the_exports():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.lib().moe_abi_version() == 2
+    assert L.lib().moe_abi_version() == 3
     assert L.status_str(0) == "MOE_OK" and L.status_str(5) == "MOE_ERR_WORKSPACE"
 
 
@@ -66,6 +66,10 @@ def test_other_entry_points_reject():
     assert lib.fp8_quant_1x128(P(16), 4, 100, 100, P(16), P(16), None) == 2
     assert lib.fp8_quant_1x128(P(16), 4, 128, 132, P(16), P(16), None) == 4
     assert lib.fp8_quant_128x128(P(16), 1, 128, 64, P(16), P(16), None) == 2
+    assert lib.fp8_quant_1x128_e8m0(P(16), 4, 100, 100, P(16), P(16), None) == 2
+    assert lib.fp8_quant_1x128_e8m0(None, 4, 128, 128, P(16), P(16), None) == 1
+    assert lib.fp8_quant_128x128_e8m0(P(16), 1, 128, 64, P(16), P(16), None) == 2
+    assert lib.fp8_quant_128x128_e8m0(P(8), 1, 128, 128, P(16), P(16), None) == 4
     assert lib.moe_combine(P(16), None, P(16), P(16), 4, 2, 12, P(16), 0, None) == 2
     assert lib.moe_combine(P(16), None, P(16), P(16), 4, 2, 16, P(16), 2, None) == 3
     assert lib.moe_bias_update(None, P(16), 8, 16, 0.001, None) == 1
@@ -90,6 +94,8 @@ def _gemm(L, **kw):
     (dict(tail_groups=1, out_dtype=0, ldo=256), 1), (dict(tail_groups=1, out_dtype=0, out_tail=8, ldo_tail=256), 4),
     (dict(tail_groups=1, out_dtype=0, out_tail=16, ldo_tail=100), 4),
     (dict(tail_groups=1, out_dtype=0, out_tail=16, ldo_tail=256, epilogue=1, N=512), 3),
+    (dict(in_dtype=2, a_scale=16, w_scale=16, scale_fmt=5), 3),
+    (dict(in_dtype=2, a_scale=16, w_scale=16, scale_fmt=1, K=256, lda=256), 2),
 ])
 def test_gemm_rejects(kw, code):
     L = _lib()

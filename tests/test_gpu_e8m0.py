@@ -1,0 +1,203 @@
+"""GPU parity of the power-of-two (E8M0) tile-scale variant against the CPU oracle.
+
+Bars: the quantisers' E4M3 codes and E8M0 scale codes bit-exact; the grouped GEMM bit-exact
+on exactly representable operands (which pins the block-scaled MFMA's operand and scale
+layout and the scale-chunk indexing) and within the fp8 dot-product bound on realistic ones;
+the layer checked stage by stage against the oracle's "fp8_e8m0" precision at 3e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from sparse_moe_layer_sigmoid_amd import inputs as I
+from tests.gpu_common import FP8_DOT_REL, FP8_TOL, check_route, fp8_staged_check, np64, rel_err, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def M():
+    import sparse_moe_layer_sigmoid_amd as m
+    return m
+
+
+def _offsets(sizes):
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 128), (37, 512), (300, 7168)])
+def test_quant_1x128_e8m0_bitexact(rows, cols):
+    say(f"quant_1x128_e8m0 rows={rows} cols={cols}")
+    xn = I.gen_normal(rows * 5 + cols, (rows, cols), 1.0).float().numpy()
+    if rows > 5:
+        xn[3, :128] = 0.0                    # all-zero tile: code 127
+        xn[4, 5] = 300.0                     # an outlier
+        xn[5, 128:256] *= 2.0 ** -125        # exponent clamped at -127
+        xn[2, 0:128] = -0.0                  # negative zeros keep their sign bit
+        xn[6, :128] = np.clip(xn[6, :128], -3.0, 3.0)
+        xn[6, 7] = 3.5                       # amax = 448 * 2^-7 exactly: code 120
+        xn[6, 128:256] = np.clip(xn[6, 128:256], -3.0, 3.0)
+        xn[6, 130] = -3.515625               # next bf16 above 3.5: code 121
+    x = torch.from_numpy(xn).to(torch.bfloat16)
+    q, s = M().fp8_quant_1x128_e8m0(x.to(DEV))
+    qo, so = O.quant_1x128_e8m0(x.float().numpy())
+    assert s.dtype == torch.uint8
+    assert np.array_equal(s.cpu().numpy(), so)
+    assert np.array_equal(q.cpu().numpy(), qo)
+    if rows > 5:
+        assert so[3, 0] == 127 and so[5, 1] == 0 and so[6, 0] == 120 and so[6, 1] == 121
+
+
+def test_quant_128x128_e8m0_bitexact():
+    w = I.gen_normal(9, (3, 256, 384), 0.006)
+    w[1, :128, :128] = 0
+    q, s = M().fp8_quant_128x128_e8m0(w.to(DEV))
+    for m in range(3):
+        qo, so = O.quant_128x128_e8m0(w[m].float().numpy())
+        assert np.array_equal(s[m].cpu().numpy(), so)
+        assert np.array_equal(q[m].cpu().numpy(), qo)
+
+
+@pytest.mark.parametrize("sizes,K", [
+    ([5, 130, 64], 512),                     # 128-row tiles, one partial chunk of 16 K blocks
+    ([5, 130, 64, 300], 2560),               # 20 K blocks: chunks of 16 and 4 across many tiles
+    ([70, 200], 7168),                       # the layer's d: 56 K blocks = 16 + 16 + 16 + 8
+    ([5, 30, 20, 9, 1, 0, 40], 4608),        # decode-sized groups (64-row tiles, chunks of 32 and 4)
+], ids=["K512", "K2560", "K7168", "small_K4608"])
+def test_gemm_e8m0_exact(sizes, K):
+    """E4M3 codes of small integers with power-of-two scales from neighbouring binades: every
+    product and partial sum is exact in fp32, so the GEMM equals the oracle bit for bit.  This
+    pins which operand row and K group each E8M0 code scales, per row tile of A and per
+    128x128 block of W, across chunk boundaries."""
+    G, N = len(sizes), 256
+    sizes = np.array(sizes)
+    offs = _offsets(sizes)
+    rows = int(offs[-1])
+    T = 300
+    a_rows = np.random.default_rng(2).integers(0, T, rows).astype(np.int32)
+    Aq = I.gen_e4m3_codes(41, (T, K), small_int=True)
+    Wq = I.gen_e4m3_codes(43, (G, N, K), small_int=True)
+    Ac = torch.where(I.gen_scales(42, (T, K // 128), pow2=True) <= 2.0 ** -6, 123, 124).to(torch.uint8)
+    Wc = torch.where(I.gen_scales(44, (G, N // 128, K // 128), pow2=True) <= 2.0 ** -6, 122, 123).to(torch.uint8)
+    out = torch.empty((rows, N), dtype=torch.float32, device=DEV)
+    M().moe_grouped_gemm(Aq.to(DEV), Wq.to(DEV), torch.from_numpy(offs).to(DEV), 0, G, rows, out,
+                         a_scale=Ac.to(DEV), a_rows=torch.from_numpy(a_rows).to(DEV), w_scale=Wc.to(DEV))
+    got = out.cpu().numpy().astype(np.float64)
+    A = O.dequant_1x128(Aq.numpy(), O.e8m0_decode(Ac.numpy()))
+    for g in range(G):
+        Wd = O.dequant_128x128(Wq[g].numpy(), O.e8m0_decode(Wc[g].numpy()))
+        ref = A[a_rows[offs[g]:offs[g + 1]]] @ Wd.T
+        assert np.array_equal(got[offs[g]:offs[g + 1]], ref), g
+
+
+@pytest.mark.parametrize("swiglu,out_kind", [(False, "f32"), (False, "bf16"), (True, "bf16"), (True, "fp8")])
+def test_gemm_e8m0_random(swiglu, out_kind):
+    G, K = 5, 1024
+    N = 512 if swiglu else 256
+    sizes = I.gen_group_sizes(7, G, 100)
+    sizes[1] = 0
+    sizes[3] = 260
+    offs = _offsets(sizes)
+    rows = int(offs[-1])
+    T = 300
+    a_rows = np.random.default_rng(3).integers(0, T, rows).astype(np.int32)
+    A = I.gen_normal(51, (T, K), 1.0)
+    W = I.gen_normal(53, (G, N, K), 0.006)
+    Aq, As = M().fp8_quant_1x128_e8m0(A.to(DEV))
+    Wq, Ws = M().fp8_quant_128x128_e8m0(W.to(DEV))
+    Aqo, Aso = O.quant_1x128_e8m0(A.float().numpy())
+    assert np.array_equal(Aq.cpu().numpy(), Aqo) and np.array_equal(As.cpu().numpy(), Aso)
+    oc = N // 2 if swiglu else N
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[out_kind]
+    out = torch.empty((rows, oc), dtype=dt, device=DEV)
+    osc = torch.empty((rows, oc // 128), dtype=torch.uint8, device=DEV) if out_kind == "fp8" else None
+    M().moe_grouped_gemm(Aq, Wq, torch.from_numpy(offs).to(DEV), 0, G, rows, out, a_scale=As,
+                         a_rows=torch.from_numpy(a_rows).to(DEV), w_scale=Ws, swiglu=swiglu, out_scale=osc)
+    Ad = O.dequant_1x128(Aqo, O.e8m0_decode(Aso))
+    ref = np.zeros((rows, oc))
+    bound = np.zeros((rows, oc))
+    for g in range(G):
+        if sizes[g] == 0:
+            continue
+        wq, wc = O.quant_128x128_e8m0(W[g].float().numpy())
+        Wd = O.dequant_128x128(wq, O.e8m0_decode(wc))
+        xr = Ad[a_rows[offs[g]:offs[g + 1]]]
+        if swiglu:
+            I_ = N // 2
+            a, c = xr @ Wd[:I_].T, xr @ Wd[I_:].T
+            da = FP8_DOT_REL * (np.abs(xr) @ np.abs(Wd[:I_]).T)
+            dc = FP8_DOT_REL * (np.abs(xr) @ np.abs(Wd[I_:]).T)
+            ref[offs[g]:offs[g + 1]] = O.silu(a) * c
+            bound[offs[g]:offs[g + 1]] = 1.1 * da * np.abs(c) + np.abs(O.silu(a)) * dc + da * dc
+        else:
+            ref[offs[g]:offs[g + 1]] = xr @ Wd.T
+            bound[offs[g]:offs[g + 1]] = FP8_DOT_REL * (np.abs(xr) @ np.abs(Wd).T)
+    rms = np.sqrt(np.mean(ref ** 2))
+    if out_kind == "fp8":
+        codes = osc.cpu().numpy()
+        qo, so = O.quant_1x128_e8m0(O.fp32_round(ref))
+        # a scale code may be one binade off only where the row's amax lies within the
+        # dot-product bound of a power-of-two boundary
+        amax = np.abs(ref).reshape(rows, -1, 128).max(axis=2)
+        tol = bound.reshape(rows, -1, 128).max(axis=2)
+        lo = O.e8m0_exponent(np.maximum(amax - tol, 0.0)) + 127
+        hi = O.e8m0_exponent(amax + tol) + 127
+        assert np.all((codes >= lo) & (codes <= hi))
+        say(f"  h scale codes identical to the oracle's: {np.mean(codes == so):.5f}")
+        sc = np.repeat(O.e8m0_decode(codes), 128, axis=1)
+        got = O.dequant_1x128(out.cpu().numpy(), O.e8m0_decode(codes))
+        same = np.mean(out.cpu().numpy() == qo)
+        say(f"  fp8 h codes identical to the oracle's: {same:.5f}")
+        assert same > 0.98
+        step = 2 * O.e4m3_half_ulp(np.minimum(np.abs(ref) / sc, 448.0)) * sc
+        assert np.all(np.abs(got - ref) <= bound + step * 1.001 + 1e-6 * rms)
+    elif out_kind == "bf16":
+        got = np64(out)
+        assert np.all(np.abs(got - ref) <= bound + np.abs(ref) * 2.0 ** -8 + 1e-6 * rms)
+    else:
+        got = np64(out)
+        assert np.all(np.abs(got - ref) <= bound + 1e-6 * rms)
+    say(f"  max |err| / bound = {np.max(np.abs(got - ref) / (bound + 1e-30)):.3f}, rel err {rel_err(got, ref):.2e}")
+
+
+def _layer_case(cfg):
+    x = I.gen_x(cfg)
+    wr = I.gen_router(cfg)
+    bias = I.gen_bias(cfg)
+    experts = [I.gen_expert(cfg, e) for e in range(cfg.groups)]
+    W13 = torch.stack([e[0] for e in experts]).to(torch.bfloat16)
+    W2 = torch.stack([e[1] for e in experts]).to(torch.bfloat16)
+    return x.to(torch.bfloat16), wr.to(torch.bfloat16), bias, W13, W2
+
+
+# K of both projections (d and the expert width) must be a multiple of 512 with E8M0 scales.
+@pytest.mark.parametrize("cfg", [
+    I.small(I.V3_FP8, name="e8m0_small", T=300, d=512, n_experts=32, top_k=4, inter=512, w_std=0.04,
+            router_std=0.04, outlier_frac=7.2 / 512),
+    I.small(I.V3_FP8, name="e8m0_small_2", T=129, d=1024, n_experts=16, top_k=8, inter=512, w_std=0.03,
+            router_std=0.03),
+], ids=lambda c: c.name)
+def test_layer_fp8_e8m0(cfg):
+    say(f"layer fp8 e8m0 {cfg.name}")
+    x, wr, bias, W13, W2 = _layer_case(cfg)
+    layer = M().MoELayer(wr.to(DEV), W13.to(DEV), W2.to(DEV), bias.to(DEV), cfg.top_k, fp8=True, fp8_scales="e8m0")
+    out32, buf = layer.forward(x.to(DEV), out_dtype=torch.float32, keep=True)
+    x64 = np64(x)
+    r = O.route(x64, np64(wr), bias.numpy(), cfg.top_k)
+    tie = check_route(buf["topk_idx"], buf["topk_gate"], buf["expert_counts"], None, r, cfg.n_experts, cfg.top_k)
+    xq, xs = O.quant_1x128_e8m0(x.float().numpy())
+    assert np.array_equal(buf["xq"].cpu().numpy(), xq) and np.array_equal(buf["xs"].cpu().numpy(), xs)
+    wq, ws = O.quant_128x128_e8m0(W13[3].float().numpy())
+    assert np.array_equal(layer.W13[3].cpu().numpy(), wq) and np.array_equal(layer.W13_s[3].cpu().numpy(), ws)
+    W13n, W2n = np64(W13), np64(W2)
+    keep = ~tie
+    pick = np.nonzero(keep)[0]
+    gates = [dict(zip(r["idx"][t], r["gate"][t])) for t in range(cfg.T)]
+    staged, same = fp8_staged_check(pick, x64[pick], buf["topk_idx"].cpu().numpy(), buf["pair_pos"].cpu().numpy(),
+                                    lambda t, e: gates[t][e], cfg.n_experts, lambda e: (W13n[e], W2n[e]), buf,
+                                    out32, FP8_TOL, e8m0=True)
+    ref, _ = O.forward_sparse(x64, r["idx"], r["gate"], cfg.n_experts, lambda e: (W13n[e], W2n[e]), "fp8_e8m0")
+    err = rel_err(np64(out32)[keep], ref[keep])
+    say(f"  staged: h codes equal to the oracle's {same:.5f}, output from the device h {staged:.2e} "
+        f"(tol {FP8_TOL}); end to end vs the oracle's fp8_e8m0 pipeline {err:.2e}")

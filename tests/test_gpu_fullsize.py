@@ -35,9 +35,9 @@ def v3():
     wr_cpu = I.gen_router(I.V3_BF16)
     torch.cuda.synchronize()
     say(f"[fullsize] weights ready in {time.time() - t0:.1f}s")
-    ns = SimpleNamespace(W13=W13, W2=W2, wr_cpu=wr_cpu, wr=wr_cpu.to(DEV), fp8_layer=None)
+    ns = SimpleNamespace(W13=W13, W2=W2, wr_cpu=wr_cpu, wr=wr_cpu.to(DEV), fp8_layer=None, e8m0_layer=None)
     yield ns
-    del ns.W13, ns.W2, ns.fp8_layer
+    del ns.W13, ns.W2, ns.fp8_layer, ns.e8m0_layer
     torch.cuda.empty_cache()
 
 
@@ -68,11 +68,11 @@ def _sampled_output_check(cfg, x_cpu, r, tie, out32, precision, n_tokens, tol, b
     err = rel_err(got, ref)
     say(f"[fullsize] {cfg.name}: max|out - oracle| / rms = {err:.3e} (tol {tol}) [{time.time() - t0:.0f}s]")
     assert err <= tol
-    if precision == "fp8" and buf is not None:
+    if precision in ("fp8", "fp8_e8m0") and buf is not None:
         gates = {int(t): dict(zip(r["idx"][t], r["gate"][t])) for t in pick}
         staged, same = fp8_staged_check(pick, x_cpu[pick].double().numpy(), buf["topk_idx"].cpu().numpy(),
                                         buf["pair_pos"].cpu().numpy(), lambda t, e: gates[t][e], cfg.n_experts,
-                                        fetch, buf, out32, tol)
+                                        fetch, buf, out32, tol, e8m0=precision == "fp8_e8m0")
         say(f"[fullsize] {cfg.name}: staged: h codes equal to the oracle's {same:.5f}, output from the device h "
             f"{staged:.3e}")
     return err
@@ -123,6 +123,23 @@ def test_v3_fp8_T16384(v3):
     xq, xs = O.quant_1x128(x_cpu.float().numpy()[:512])
     assert np.array_equal(buf["xq"][:512].cpu().numpy(), xq) and np.array_equal(buf["xs"][:512].cpu().numpy(), xs)
     _sampled_output_check(cfg, x_cpu, r, tie, out32, "fp8", 12, FP8_TOL, buf)
+
+
+def test_v3_fp8_e8m0_T16384(v3):
+    """The T = 16384 E4M3 workload with power-of-two (E8M0) tile scales."""
+    cfg = I.V3_FP8
+    x_cpu = I.gen_x(cfg)
+    bias = I.gen_bias(cfg)
+    say("[fullsize] quantising the weights to E4M3 with E8M0 block scales ...")
+    v3.e8m0_layer = M().MoELayer(v3.wr, v3.W13, v3.W2, bias.to(DEV), cfg.top_k, fp8=True, fp8_scales="e8m0")
+    out32, buf = v3.e8m0_layer.forward(x_cpu.to(DEV), out_dtype=torch.float32, keep=True)
+    xq, xs = O.quant_1x128_e8m0(x_cpu.float().numpy()[:512])
+    assert np.array_equal(buf["xq"][:512].cpu().numpy(), xq) and np.array_equal(buf["xs"][:512].cpu().numpy(), xs)
+    r = O.route(np64(x_cpu), np64(v3.wr_cpu), bias.numpy(), cfg.top_k)
+    tie = check_route(buf["topk_idx"], buf["topk_gate"], buf["expert_counts"], None, r, cfg.n_experts, cfg.top_k)
+    _sampled_output_check(cfg, x_cpu, r, tie, out32, "fp8_e8m0", 12, FP8_TOL, buf)
+    v3.e8m0_layer = None
+    torch.cuda.empty_cache()
 
 
 def test_v3_decode_bias_loop(v3):
