@@ -526,6 +526,76 @@ def forward(x, w_router, bias, w13, w2, top_k, n_group=1, topk_group=1, precisio
     return out, r, extra
 
 
+# --------------------------------------------------------------------------------------
+# Backward pass.  [TR] "FP8 混合精度訓練": the training step runs the layer's Fprop, Dgrad
+# and Wgrad GEMMs; the gradients below are the chain rule of the forward definition above.
+# The selection (top-K of z, and the bias inside z) is piecewise constant, so no gradient
+# flows through it or to the bias; the gates carry the router's gradient.
+# --------------------------------------------------------------------------------------
+
+
+def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, topk_group: int = 1):
+    """Gradients of L = sum(d_out * out) for the layer ``forward`` computes (float64).
+
+    For every expert e and the rows routed to it (every token for the shared expert N):
+      a = x W1^T, c = x W3^T, h = silu(a) c, y = h W2^T;
+      dy = gate * d_out (routed) or d_out (shared); dgate = <d_out, y>;
+      dW2 = dy^T h;  dh = dy W2;  da = dh c silu'(a), silu'(a) = sig(a) (1 + a (1 - sig(a)));
+      dc = dh silu(a);  dW13 = [da | dc]^T x;  dx += da W1 + dc W3.
+    Router, with the gates g_k = s_k / S over the selected affinities (S = sum of them):
+      ds_k = (dgate_k - sum_j g_j dgate_j) / S;  du_k = ds_k s_k (1 - s_k);
+      dx += sum_k du_k e_{idx_k};  dW_r[idx_k] += du_k x.
+    Returns dx [T, d], dw_router [N, d], dw13 [N+1, 2I, d], dw2 [N+1, d, I] and the
+    intermediates dgate [T, K], du [T, K] and the routing dict."""
+    x = np.asarray(x, dtype=np.float64)
+    wr = np.asarray(w_router, dtype=np.float64)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    r = route(x, wr, bias, top_k, n_group, topk_group)
+    idx, gate, s = r["idx"], r["gate"], r["s"]
+    T, d = x.shape
+    N = wr.shape[0]
+    I = np.asarray(w13[0]).shape[0] // 2
+    dx = np.zeros((T, d))
+    dw13 = np.zeros((N + 1, 2 * I, d))
+    dw2 = np.zeros((N + 1, d, I))
+    dgate = np.zeros((T, top_k))
+    for e in range(N + 1):
+        if e < N:
+            tok, slot = np.nonzero(idx == e)   # each token picks distinct experts: tok is unique
+        else:
+            tok = np.arange(T)
+        if len(tok) == 0:
+            continue
+        we13 = np.asarray(w13[e], dtype=np.float64)
+        we2 = np.asarray(w2[e], dtype=np.float64)
+        xe = x[tok]
+        a = xe @ we13[:I].T
+        c = xe @ we13[I:].T
+        sg = sigmoid(a)
+        h = a * sg * c
+        if e < N:
+            dy = gate[tok, slot][:, None] * d_out[tok]
+            dgate[tok, slot] = np.sum(d_out[tok] * (h @ we2.T), axis=1)
+        else:
+            dy = d_out
+        dw2[e] = dy.T @ h
+        dh = dy @ we2
+        da = dh * c * sg * (1.0 + a * (1.0 - sg))
+        dc = dh * a * sg
+        dw13[e, :I] = da.T @ xe
+        dw13[e, I:] = dc.T @ xe
+        dx[tok] += da @ we13[:I] + dc @ we13[I:]
+    ssel = np.take_along_axis(s, idx, axis=1)
+    S = ssel.sum(axis=1, keepdims=True)
+    ds = (dgate - np.sum(gate * dgate, axis=1, keepdims=True)) / S
+    du = ds * ssel * (1.0 - ssel)
+    dwr = np.zeros((N, d))
+    for k in range(top_k):
+        dx += du[:, k:k + 1] * wr[idx[:, k]]
+        np.add.at(dwr, idx[:, k], du[:, k:k + 1] * x)
+    return {"dx": dx, "dw_router": dwr, "dw13": dw13, "dw2": dw2, "dgate": dgate, "du": du, "route": r}
+
+
 def layer_flops(T: int, d: int, n_experts: int, top_k: int, inter: int, n_shared: int = 1) -> int:
     """Algorithmic FLOPs of one forward: router 2 T d N plus 6 d I per active expert-row."""
     return 2 * T * d * n_experts + 6 * d * inter * T * (top_k + n_shared)

@@ -466,6 +466,65 @@ def pin_fp8_layer_close_to_exact():
     assert np.max(np.abs(f8 - ex)) > np.max(np.abs(bf - ex))  # fp8 really quantises
 
 
+# ------------------------------------------------------------------ backward
+
+
+def _fd_check(seed, n_group=1, topk_group=1, K=2):
+    """Central finite differences of the (pinned) dense forward against ``backward`` along
+    random directions in x, W_r, W13 and W2.  The selection must not change within the step,
+    which is asserted."""
+    x, wr, b, w13, w2 = _tiny_layer(seed, T=9, d=12, N=8, I=6, scale=0.4)
+    r = _rng(seed + 100)
+    d_out = r.standard_normal((9, 12))
+    g = O.backward(x, wr, b, w13, w2, K, d_out, n_group, topk_group)
+    params = {"x": x, "wr": wr, "w13": w13, "w2": w2}
+    grads = {"x": g["dx"], "wr": g["dw_router"], "w13": g["dw13"], "w2": g["dw2"]}
+
+    def loss(p):
+        out, rr = O.forward_dense(p["x"], p["wr"], b, p["w13"], p["w2"], K, n_group, topk_group)
+        return float(np.sum(d_out * out)), rr["idx"]
+
+    _, idx0 = loss(params)
+    eps = 1e-6
+    for name in params:
+        for _ in range(3):
+            v = r.standard_normal(params[name].shape)
+            hi = dict(params, **{name: params[name] + eps * v})
+            lo = dict(params, **{name: params[name] - eps * v})
+            lh, ih = loss(hi)
+            ll, il = loss(lo)
+            assert np.array_equal(ih, idx0) and np.array_equal(il, idx0), "selection moved"
+            fd = (lh - ll) / (2 * eps)
+            an = float(np.sum(grads[name] * v))
+            assert abs(fd - an) <= 1e-6 * (abs(an) + 1.0), (name, fd, an)
+
+
+def pin_backward_finite_differences():
+    _fd_check(21)
+
+
+def pin_backward_finite_differences_groups():
+    _fd_check(22, n_group=4, topk_group=2, K=3)
+
+
+def pin_backward_closed_forms():
+    """K = N = 1: the single gate is 1 whatever the affinity, so the router gets no gradient;
+    the shared expert's gradients are those of a plain SwiGLU FFN, checked against torch
+    autograd of the textbook form (float64)."""
+    x, wr, b, w13, w2 = _tiny_layer(23, T=5, d=8, N=1, I=4, scale=0.5)
+    d_out = _rng(24).standard_normal((5, 8))
+    g = O.backward(x, wr, b, w13, w2, 1, d_out)
+    assert np.all(g["du"] == 0) and np.all(g["dw_router"] == 0)
+    xt = torch.tensor(x, requires_grad=True)
+    w13t = torch.tensor(w13[1], requires_grad=True)
+    w2t = torch.tensor(w2[1], requires_grad=True)
+    a, c = xt @ w13t[:4].T, xt @ w13t[4:].T
+    out = (torch.nn.functional.silu(a) * c) @ w2t.T
+    (out * torch.tensor(d_out)).sum().backward()
+    assert np.allclose(g["dw13"][1], w13t.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(g["dw2"][1], w2t.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
 def pin_layer_flops():
     # DeepSeek-V3 shape: 9 of 257 experts per token; 2*7168*256 + 6*7168*2048*9 per token
     assert O.layer_flops(1, 7168, 256, 8, 2048) == 796_393_472

@@ -183,12 +183,71 @@ def _mut_e8m0_scale_wrong_tile(mp):
     mp.setattr(O, "quant_1x128_e8m0", quant)
 
 
+def _mut_backward(mp, what):
+    real = O.backward
+
+    def bwd(x, wr, b, w13, w2, K, d_out, n_group=1, topk_group=1):
+        g = real(x, wr, b, w13, w2, K, d_out, n_group, topk_group)
+        g = dict(g)
+        if what == "no_norm_term":      # forget that the gates are normalised
+            r = g["route"]
+            ssel = np.take_along_axis(r["s"], r["idx"], axis=1)
+            S = ssel.sum(axis=1, keepdims=True)
+            extra = (np.sum(r["gate"] * g["dgate"], axis=1, keepdims=True) / S) * ssel * (1 - ssel)
+            dx = g["dx"].copy()
+            dwr = g["dw_router"].copy()
+            for k in range(K):
+                dx += extra[:, k:k + 1] * np.asarray(wr)[r["idx"][:, k]]
+                np.add.at(dwr, r["idx"][:, k], extra[:, k:k + 1] * np.asarray(x))
+            g["dx"], g["dw_router"] = dx, dwr
+        elif what == "swap_w13_halves":
+            I = g["dw13"].shape[1] // 2
+            g["dw13"] = np.concatenate([g["dw13"][:, I:], g["dw13"][:, :I]], axis=1)
+        elif what == "dw2_transposed_rows":
+            g["dw2"] = g["dw2"][:, ::-1]
+        return g
+    mp.setattr(O, "backward", bwd)
+
+
+def _mut_bwd_no_norm_term(mp):
+    _mut_backward(mp, "no_norm_term")
+
+
+def _mut_bwd_swap_w13_halves(mp):
+    _mut_backward(mp, "swap_w13_halves")
+
+
+def _mut_bwd_dw2_rows(mp):
+    _mut_backward(mp, "dw2_transposed_rows")
+
+
+def _mut_bwd_silu_grad(mp):
+    real_sig = O.sigmoid
+    calls = {"n": 0}
+    real = O.backward
+
+    def bwd(*a, **kw):
+        # sigmoid is called once for the router, then once per expert: perturb the experts'
+        def sig(u):
+            calls["n"] += 1
+            v = real_sig(u)
+            return v if calls["n"] == 1 else v * 0.999 + 0.0005
+        calls["n"] = 0
+        mp.setattr(O, "sigmoid", sig)
+        try:
+            return real(*a, **kw)
+        finally:
+            mp.setattr(O, "sigmoid", real_sig)
+    mp.setattr(O, "backward", bwd)
+
+
 MUTATIONS = [
     _mut_gate_from_z, _mut_ascending, _mut_tie_higher_index, _mut_silu_sign, _mut_swap_w1_w3,
     _mut_bias_sign, _mut_bias_mean_off, _mut_e4m3_ties_odd, _mut_fnuz_scale,
     _mut_bf16_truncate, _mut_permute_token_desc, _mut_combine_no_shared,
     _mut_group_max_not_top2, _mut_sigmoid_softmax, _mut_quant_transposed_block_scale,
     _mut_e8m0_floor, _mut_e8m0_bias_126, _mut_e8m0_scale_wrong_tile,
+    _mut_bwd_no_norm_term, _mut_bwd_swap_w13_halves, _mut_bwd_dw2_rows, _mut_bwd_silu_grad,
 ]
 
 
