@@ -223,6 +223,8 @@ typedef struct moe_gemm_desc {
   void* out_tail;
   int64_t ldo_tail;
   int scale_fmt;                /* MOE_SCALE_F32 (0) or MOE_SCALE_E8M0 (FP8 only) */
+  int64_t ldw;                  /* row stride of each W[g] in elements (0: K); W[g] starts at
+                                   w + g * N * ldw */
 } moe_gemm_desc;
 /* Limits: K a positive multiple of 64 (bf16) or 128 (FP8); N a positive multiple of 128 (bf16)
  * or 256 (FP8) -- with SWIGLU that is N/2 a multiple of 64 or 128; FP8 input needs a_scale and
@@ -266,6 +268,76 @@ moe_status moe_combine(const uint16_t* y_routed, const float* y_shared, const in
  * ------------------------------------------------------------------------------------ */
 moe_status moe_bias_update(float* bias, const int32_t* expert_counts, int n_experts,
                            int64_t total_assignments, float gamma, hipStream_t stream);
+
+/* ====================================================================================
+ * Backward pass.  "DeepSeek-V3 Technical Report", "FP8 混合精度訓練": a training step runs
+ * the layer's Fprop, Dgrad and Wgrad GEMMs.  The gradients are the chain rule of the forward
+ * definition ("DeepSeekMoE と補助損失なしの負荷分散"): with L = sum(d_out * out), gates
+ * g_k = s_k / S over the selected affinities (S = their sum) and the selection (and bias)
+ * carrying no gradient:
+ *   dy = g * d_out at a routed pair's sorted row, d_out at the token's shared row;
+ *   dg_k = <d_out, y_k>;  du_k = s_k (1 - s_k) (dg_k - sum_j g_j dg_j) / S;
+ *   per expert: dh = dy W2, [da | dc] = [dh c silu'(a) | dh silu(a)], dx_rows = [da | dc] W13,
+ *   dW2 = dy^T h, dW13 = [da | dc]^T x_rows;  router: dx += sum_k du_k e_{idx_k},
+ *   dW_r[idx_k] += du_k x.
+ * The GEMMs run on moe_grouped_gemm (Dgrad with transposed weights, Wgrad per expert over
+ * transposed row segments, see moe_segment_transpose); the calls below are the pieces
+ * between them.
+ * ==================================================================================== */
+
+/* moe_combine_backward -- the combine's and router's gradients for every token t.
+ *   d_out     device bf16 [T, d]: gradient of the layer output
+ *   y_routed  device bf16 [T*top_k, d]: the forward's routed expert outputs (sorted rows)
+ *   topk_idx, topk_gate, pair_pos: the forward's routing and permutation ([T, top_k])
+ *   scores    device f32 [T, n_experts]: the forward's affinities s (moe_route's scores)
+ *   dy        device bf16 [T*(top_k+1), d] out: rows pair_pos[t,k] = RNE(g_k d_out[t]), rows
+ *             T*top_k + t = d_out[t] (the down projection's input gradient, sorted rows)
+ *   du        device f32 [T, top_k] out: router logit gradients of the selected experts
+ *   du_row    device f32 [T*top_k] out: du by sorted row (du_row[pair_pos[t,k]] = du[t,k])
+ * dg is accumulated in fp32 in a fixed order; the rest is fp32.  Limits: T >= 0;
+ * 1 <= top_k <= min(32, n_experts); d >= 8, d % 8 == 0; routing and permutation as moe_route
+ * and moe_permute produce them (valid, distinct experts).  With T == 0 nothing is done. */
+moe_status moe_combine_backward(const uint16_t* d_out, const uint16_t* y_routed,
+                                const int32_t* topk_idx, const float* topk_gate,
+                                const float* scores, const int32_t* pair_pos, int T, int top_k,
+                                int d, int n_experts, uint16_t* dy, float* du, float* du_row,
+                                hipStream_t stream);
+
+/* moe_swiglu_backward -- through h = silu(a) c, elementwise over rows x inter:
+ *   da = dh c sig(a) (1 + a (1 - sig(a))),  dc = dh a sig(a)   (fp32, stored RNE bf16)
+ *   ac   device f32 [rows, 2*inter]: a in columns [0, inter), c in [inter, 2*inter)
+ *        (the gate/up GEMM without its SwiGLU epilogue)
+ *   dh   device f32 [rows, inter]
+ *   dac  device bf16 [rows, 2*inter] out: da | dc
+ * Limits: rows >= 0; inter >= 4, inter % 4 == 0. */
+moe_status moe_swiglu_backward(const float* ac, const float* dh, int64_t rows, int inter,
+                               uint16_t* dac, hipStream_t stream);
+
+/* moe_segment_transpose -- row segments of a bf16 matrix become zero-padded column blocks of
+ * its transpose: for segment g (rows [seg_offsets[g], seg_offsets[g+1]) of the logical
+ * source), column dst_cols[g] + i of dst holds source row seg_offsets[g] + i (read through
+ * src_rows if not NULL) for i < the segment's length, and zeros up to dst_cols[g+1].
+ *   src         device bf16, rows of `cols` elements, leading dimension ld_src
+ *   src_rows    device i32 gather index per logical row, or NULL
+ *   seg_offsets device i32 [n_segments+1];  dst_cols device i32 [n_segments+1], non-decreasing,
+ *               dst_cols[g+1] - dst_cols[g] >= the segment's length, dst_cols[n_segments] =
+ *               total_cols
+ *   dst         device bf16 [cols, ld_dst] out (columns [0, total_cols) written)
+ * Limits: n_segments >= 1; cols and total_cols multiples of 8; leading dimensions keep rows
+ * 16-byte aligned.  (Used for the Wgrad operands and, once, for transposed weight copies.) */
+moe_status moe_segment_transpose(const uint16_t* src, int64_t ld_src, const int32_t* src_rows,
+                                 const int32_t* seg_offsets, const int32_t* dst_cols,
+                                 int n_segments, int cols, int total_cols, uint16_t* dst,
+                                 int64_t ld_dst, hipStream_t stream);
+
+/* moe_router_wgrad -- dW_r[e] = sum over expert e's sorted rows r of du_row[r] x[sorted_token[r]]
+ * (fp32, rows in order).
+ *   x device bf16 [T, d]; sorted_token, expert_offsets from moe_permute; du_row from
+ *   moe_combine_backward; dw_router device f32 [n_experts, d] out (overwritten).
+ * Limits: 1 <= n_experts <= 65535; d % 8 == 0. */
+moe_status moe_router_wgrad(const uint16_t* x, const int32_t* sorted_token,
+                            const int32_t* expert_offsets, const float* du_row, int n_experts,
+                            int d, float* dw_router, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -534,7 +534,8 @@ def forward(x, w_router, bias, w13, w2, top_k, n_group=1, topk_group=1, precisio
 # --------------------------------------------------------------------------------------
 
 
-def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, topk_group: int = 1):
+def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, topk_group: int = 1,
+             precision: str = "exact"):
     """Gradients of L = sum(d_out * out) for the layer ``forward`` computes (float64).
 
     For every expert e and the rows routed to it (every token for the shared expert N):
@@ -545,8 +546,13 @@ def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, to
     Router, with the gates g_k = s_k / S over the selected affinities (S = sum of them):
       ds_k = (dgate_k - sum_j g_j dgate_j) / S;  du_k = ds_k s_k (1 - s_k);
       dx += sum_k du_k e_{idx_k};  dW_r[idx_k] += du_k x.
+    precision "bf16" models the stored bfloat16 intermediates of the bf16 path: the forward's h
+    and routed y, dy (the float32 product g * d_out, then bf16), [da | dc] and the routed rows'
+    dx contributions are rounded to bf16 (RNE); everything else stays float64.
     Returns dx [T, d], dw_router [N, d], dw13 [N+1, 2I, d], dw2 [N+1, d, I] and the
     intermediates dgate [T, K], du [T, K] and the routing dict."""
+    assert precision in ("exact", "bf16")
+    rnd = bf16_round if precision == "bf16" else (lambda v: v)
     x = np.asarray(x, dtype=np.float64)
     wr = np.asarray(w_router, dtype=np.float64)
     d_out = np.asarray(d_out, dtype=np.float64)
@@ -572,19 +578,21 @@ def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, to
         a = xe @ we13[:I].T
         c = xe @ we13[I:].T
         sg = sigmoid(a)
-        h = a * sg * c
+        h = rnd(a * sg * c)
         if e < N:
             dy = gate[tok, slot][:, None] * d_out[tok]
-            dgate[tok, slot] = np.sum(d_out[tok] * (h @ we2.T), axis=1)
+            dy = rnd(fp32_round(dy)) if precision == "bf16" else dy
+            dgate[tok, slot] = np.sum(d_out[tok] * rnd(h @ we2.T), axis=1)
         else:
             dy = d_out
         dw2[e] = dy.T @ h
         dh = dy @ we2
-        da = dh * c * sg * (1.0 + a * (1.0 - sg))
-        dc = dh * a * sg
+        da = rnd(dh * c * sg * (1.0 + a * (1.0 - sg)))
+        dc = rnd(dh * a * sg)
         dw13[e, :I] = da.T @ xe
         dw13[e, I:] = dc.T @ xe
-        dx[tok] += da @ we13[:I] + dc @ we13[I:]
+        dxe = da @ we13[:I] + dc @ we13[I:]
+        dx[tok] += rnd(dxe) if e < N else dxe
     ssel = np.take_along_axis(s, idx, axis=1)
     S = ssel.sum(axis=1, keepdims=True)
     ds = (dgate - np.sum(gate * dgate, axis=1, keepdims=True)) / S

@@ -24,6 +24,7 @@ EXPORTS = (
     "moe_permute_workspace_size", "moe_permute",
     "fp8_quant_1x128", "fp8_quant_128x128", "fp8_quant_1x128_e8m0", "fp8_quant_128x128_e8m0",
     "moe_grouped_gemm", "moe_combine", "moe_bias_update",
+    "moe_combine_backward", "moe_swiglu_backward", "moe_segment_transpose", "moe_router_wgrad",
 )
 
 _p = ctypes.c_void_p
@@ -39,7 +40,7 @@ class MoeGemmDesc(ctypes.Structure):
         ("w", _p), ("w_scale", _p), ("group_offsets", _p), ("first_group", _i),
         ("n_groups", _i), ("m_total", _i64), ("N", _i), ("K", _i), ("epilogue", _i),
         ("out", _p), ("out_dtype", _i), ("ldo", _i64), ("out_scale", _p),
-        ("tail_groups", _i), ("out_tail", _p), ("ldo_tail", _i64), ("scale_fmt", _i),
+        ("tail_groups", _i), ("out_tail", _p), ("ldo_tail", _i64), ("scale_fmt", _i), ("ldw", _i64),
     ]
 
 
@@ -88,6 +89,14 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [_p, _p, _p, _p, _i, _i, _i, _p, _i, _p]
         L.moe_bias_update.restype = _i
         L.moe_bias_update.argtypes = [_p, _p, _i, _i64, _f, _p]
+        L.moe_combine_backward.restype = _i
+        L.moe_combine_backward.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _p, _p]
+        L.moe_swiglu_backward.restype = _i
+        L.moe_swiglu_backward.argtypes = [_p, _p, _i64, _i, _p, _p]
+        L.moe_segment_transpose.restype = _i
+        L.moe_segment_transpose.argtypes = [_p, _i64, _p, _p, _p, _i, _i, _i, _p, _i64, _p]
+        L.moe_router_wgrad.restype = _i
+        L.moe_router_wgrad.argtypes = [_p, _p, _p, _p, _i, _i, _p, _p]
         _LIB = L
     return _LIB
 
@@ -231,9 +240,10 @@ def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_tot
         _dev(out_tail, torch.float32, "out_tail", contiguous=False)
         if out_tail.stride(-1) != 1:
             raise ValueError("rows of out_tail must be contiguous")
-    if a.stride(-1) != 1 or out.stride(-1) != 1 or not w.is_contiguous():
-        raise ValueError("rows of a/out and all of w must be contiguous")
     G, N, K = w.shape
+    if a.stride(-1) != 1 or out.stride(-1) != 1 or w.stride(-1) != 1 or (G > 1 and w.stride(0) != N * w.stride(1)):
+        raise ValueError("rows of a/out/w must be contiguous and the W[g] packed (stride N * ldw)")
+    ldw = w.stride(1)
     desc = MoeGemmDesc(
         in_dtype=MOE_FP8_E4M3 if fp8 else MOE_BF16, a=a.data_ptr(),
         a_scale=a_scale.data_ptr() if a_scale is not None else None,
@@ -245,7 +255,7 @@ def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_tot
         out_scale=out_scale.data_ptr() if out_scale is not None else None,
         tail_groups=tail_groups, out_tail=out_tail.data_ptr() if tail_groups else None,
         ldo_tail=out_tail.stride(0) if tail_groups else 0,
-        scale_fmt=MOE_SCALE_E8M0 if e8 else MOE_SCALE_F32)
+        scale_fmt=MOE_SCALE_E8M0 if e8 else MOE_SCALE_F32, ldw=0 if ldw == K else ldw)
     st = lib().moe_grouped_gemm(ctypes.byref(desc), _stream(a))
     _check("moe_grouped_gemm", st)
     return out
@@ -274,3 +284,66 @@ def moe_bias_update(bias, expert_counts, total_assignments: int, gamma: float):
                                float(gamma), _stream(bias))
     _check("moe_bias_update", st)
     return bias
+
+
+# ----------------------------------------------------------------------------- backward
+
+
+def moe_combine_backward(d_out, y_routed, topk_idx, topk_gate, scores, pair_pos, out=None):
+    """-> (dy bf16 [T*(K+1), d], du f32 [T, K], du_row f32 [T*K])."""
+    _dev(d_out, torch.bfloat16, "d_out")
+    _dev(y_routed, torch.bfloat16, "y_routed")
+    _dev(scores, torch.float32, "scores")
+    T, K = topk_idx.shape
+    d = d_out.shape[1]
+    dev = d_out.device
+    out = out or {}
+    dy = out.get("dy", None)
+    if dy is None:
+        dy = torch.empty((T * (K + 1), d), dtype=torch.bfloat16, device=dev)
+    du = torch.empty((T, K), dtype=torch.float32, device=dev)
+    du_row = torch.empty(T * K, dtype=torch.float32, device=dev)
+    st = lib().moe_combine_backward(_ptr(d_out), _ptr(y_routed), _ptr(topk_idx), _ptr(topk_gate), _ptr(scores),
+                                    _ptr(pair_pos), T, K, d, scores.shape[1], _ptr(dy), _ptr(du), _ptr(du_row),
+                                    _stream(d_out))
+    _check("moe_combine_backward", st)
+    return dy, du, du_row
+
+
+def moe_swiglu_backward(ac, dh, dac=None):
+    """ac f32 [rows, 2I] (a | c), dh f32 [rows, I] -> dac bf16 [rows, 2I] (da | dc)."""
+    _dev(ac, torch.float32, "ac")
+    _dev(dh, torch.float32, "dh")
+    rows, I = dh.shape
+    if dac is None:
+        dac = torch.empty((rows, 2 * I), dtype=torch.bfloat16, device=dh.device)
+    st = lib().moe_swiglu_backward(_ptr(ac), _ptr(dh), rows, I, _ptr(dac), _stream(dh))
+    _check("moe_swiglu_backward", st)
+    return dac
+
+
+def moe_segment_transpose(src, seg_offsets, dst_cols, total_cols: int, src_rows=None, dst=None):
+    """Row segments of src [*, C] (gathered through src_rows if given) -> zero-padded column
+    blocks of dst [C, total_cols] bf16."""
+    _dev(src, torch.bfloat16, "src", contiguous=False)
+    if src.stride(-1) != 1:
+        raise ValueError("rows of src must be contiguous")
+    C = src.shape[1]
+    if dst is None:
+        dst = torch.empty((C, total_cols), dtype=torch.bfloat16, device=src.device)
+    G = seg_offsets.numel() - 1
+    st = lib().moe_segment_transpose(_ptr(src), src.stride(0), _ptr(src_rows), _ptr(seg_offsets), _ptr(dst_cols), G,
+                                     C, total_cols, _ptr(dst), dst.stride(0), _stream(src))
+    _check("moe_segment_transpose", st)
+    return dst
+
+
+def moe_router_wgrad(x, sorted_token, expert_offsets, du_row, n_experts: int, out=None):
+    _dev(x, torch.bfloat16, "x")
+    d = x.shape[1]
+    if out is None:
+        out = torch.empty((n_experts, d), dtype=torch.float32, device=x.device)
+    st = lib().moe_router_wgrad(_ptr(x), _ptr(sorted_token), _ptr(expert_offsets), _ptr(du_row), n_experts, d,
+                                _ptr(out), _stream(x))
+    _check("moe_router_wgrad", st)
+    return out

@@ -46,6 +46,6 @@ const char* moe_status_str(moe_status s) {
 
 const char* moe_last_error(void) { return moe::g_last_error.c_str(); }
 
-int moe_abi_version(void) { return 3; }
+int moe_abi_version(void) { return 4; }
 
 }  // extern "C"

@@ -920,7 +920,9 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
               "moe_grouped_gemm: a, w and out must be 16-byte aligned");
   MOE_REQUIRE(!fp8 || ((reinterpret_cast<uintptr_t>(d->a_scale) & 3u) == 0 && (reinterpret_cast<uintptr_t>(d->w_scale) & 3u) == 0),
               MOE_ERR_ALIGN, "moe_grouped_gemm: scales must be 4-byte aligned");
-  MOE_REQUIRE((int64_t)d->N * d->K * esz < ((int64_t)1 << 31), MOE_ERR_SHAPE, "moe_grouped_gemm: one W[g] exceeds 2 GiB");
+  const int64_t ldw = d->ldw ? d->ldw : d->K;
+  MOE_REQUIRE(ldw >= d->K && (ldw * esz) % 16 == 0, MOE_ERR_ALIGN, "moe_grouped_gemm: ldw=%lld", (long long)d->ldw);
+  MOE_REQUIRE((int64_t)d->N * ldw * esz < ((int64_t)1 << 31), MOE_ERR_SHAPE, "moe_grouped_gemm: one W[g] exceeds 2 GiB");
   MOE_REQUIRE(d->tail_groups >= 0 && d->tail_groups <= d->n_groups, MOE_ERR_SHAPE,
               "moe_grouped_gemm: tail_groups=%d must be in [0, n_groups=%d]", d->tail_groups, d->n_groups);
   if (d->tail_groups > 0) {
@@ -945,7 +947,7 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
   a.N = d->N;
   a.ksteps = d->K * esz / 128;
   a.ksb = d->K / 128;
-  a.w_row_b = (int64_t)d->K * esz;
+  a.w_row_b = ldw * esz;
   a.out = static_cast<uint8_t*>(d->out);
   a.ldo_b = d->ldo * osz;
   a.out_scale = d->out_scale;

@@ -52,7 +52,8 @@ class MoELayer:
         T, d = x.shape
         N, K, I = self.N, self.top_k, self.I
         dev = x.device
-        idx, gate, counts, _ = L.moe_route(x, self.w_router, self.bias, K, self.n_group, self.topk_group)
+        idx, gate, counts, scores = L.moe_route(x, self.w_router, self.bias, K, self.n_group, self.topk_group,
+                                                want_scores=keep)
         offs, sorted_token, pair_pos = L.moe_permute(idx, N, 1)
         rows = T * (K + 1)
         if self.fp8:
@@ -75,7 +76,83 @@ class MoELayer:
         if update_bias:
             L.moe_bias_update(self.bias, counts, T * K, gamma)
         if keep:
-            return out, {"topk_idx": idx, "topk_gate": gate, "expert_counts": counts,
+            return out, {"x": x, "scores": scores, "topk_idx": idx, "topk_gate": gate, "expert_counts": counts,
                          "expert_offsets": offs, "sorted_token": sorted_token, "pair_pos": pair_pos,
                          "xq": xq, "xs": xs, "h": h, "hs": hs, "y": y, "y_shared": ysh}
         return out
+
+    # ------------------------------------------------------------------ backward (bf16 path)
+
+    def _transposed_weights(self):
+        """W13^T [N+1, d, 2I] and W2^T [N+1, I, d] (bf16), made once, for the Dgrad GEMMs."""
+        if getattr(self, "_W13T", None) is None:
+            if self.fp8:
+                raise NotImplementedError("the backward pass runs on the bf16 path")
+            G, I2, d = self.W13.shape
+            dev = self.W13.device
+            one = lambda n: torch.tensor([0, n], dtype=torch.int32, device=dev)
+            self._W13T = torch.empty((G, d, I2), dtype=torch.bfloat16, device=dev)
+            self._W2T = torch.empty((G, I2 // 2, d), dtype=torch.bfloat16, device=dev)
+            s13, s2 = one(I2), one(d)
+            for g in range(G):
+                L.moe_segment_transpose(self.W13[g], s13, s13, I2, dst=self._W13T[g])
+                L.moe_segment_transpose(self.W2[g], s2, s2, d, dst=self._W2T[g])
+        return self._W13T, self._W2T
+
+    def backward(self, d_out, buf):
+        """Gradients of sum(d_out * out) for the forward that returned `buf` (keep=True):
+        dict of dx [T, d], dw_router [N, d], dw13 [N+1, 2I, d], dw2 [N+1, d, I], all f32.
+
+        Sequence: combine backward (dy, router logit gradients) -> Dgrad of the down projection
+        (dh = dy W2) -> gate/up recomputed without SwiGLU (a | c) -> SwiGLU backward -> Dgrad of
+        the gate/up projection (dx rows) -> two combines (router term + shared rows, then the
+        routed rows) -> Wgrad per expert over transposed row segments -> router Wgrad."""
+        W13T, W2T = self._transposed_weights()
+        x = buf["x"]
+        T, d = x.shape
+        N, K, I = self.N, self.top_k, self.I
+        G = N + 1
+        rows = T * (K + 1)
+        dev = x.device
+        offs, st_, pp = buf["expert_offsets"], buf["sorted_token"], buf["pair_pos"]
+        d_out = d_out.to(torch.bfloat16).contiguous()
+        dy, du, du_row = L.moe_combine_backward(d_out, buf["y"], buf["topk_idx"], buf["topk_gate"], buf["scores"], pp)
+        dh = torch.empty((rows, I), dtype=torch.float32, device=dev)
+        L.moe_grouped_gemm(dy, W2T, offs, 0, G, rows, dh)
+        ac = torch.empty((rows, 2 * I), dtype=torch.float32, device=dev)
+        L.moe_grouped_gemm(x, self.W13, offs, 0, G, rows, ac, a_rows=st_)
+        dac = L.moe_swiglu_backward(ac, dh)
+        del ac
+        dxr = torch.empty((T * K, d), dtype=torch.bfloat16, device=dev)
+        dxs = torch.empty((T, d), dtype=torch.float32, device=dev)
+        L.moe_grouped_gemm(dac, W13T, offs, 0, G, rows, dxr, out_tail=dxs, tail_groups=1)
+        # dx = sum_k dxr[pair] + dxs + sum_k du_k e_{idx_k}: the router term and the shared rows
+        # first (a combine over the router rows), then the routed rows
+        part = L.moe_combine(self.w_router, dxs, buf["topk_idx"], du, torch.float32)
+        dx = L.moe_combine(dxr, part, pp, torch.ones((T, K), dtype=torch.float32, device=dev), torch.float32)
+        # Wgrad: each expert's rows as the reduction axis, padded to a multiple of 64
+        offs_h = offs.cpu().numpy().astype("int64")
+        lens = offs_h[1:] - offs_h[:-1]
+        pads = ((lens + 63) // 64) * 64
+        cols = [0]
+        for p in pads:
+            cols.append(cols[-1] + int(p))
+        total = cols[-1]
+        dst_cols = torch.tensor(cols, dtype=torch.int32, device=dev)
+        dyT = L.moe_segment_transpose(dy, offs, dst_cols, total)
+        hT = L.moe_segment_transpose(buf["h"], offs, dst_cols, total)
+        dacT = L.moe_segment_transpose(dac, offs, dst_cols, total)
+        xT = L.moe_segment_transpose(x, offs, dst_cols, total, src_rows=st_)
+        dw2 = torch.zeros((G, d, I), dtype=torch.float32, device=dev)
+        dw13 = torch.zeros((G, 2 * I, d), dtype=torch.float32, device=dev)
+        g_d = torch.tensor([0, d], dtype=torch.int32, device=dev)
+        g_2i = torch.tensor([0, 2 * I], dtype=torch.int32, device=dev)
+        for e in range(G):
+            if lens[e] == 0:
+                continue
+            c0, kp = cols[e], int(pads[e])
+            L.moe_grouped_gemm(dyT[:, c0:c0 + kp], hT[:, c0:c0 + kp].unsqueeze(0), g_d, 0, 1, d, dw2[e])
+            L.moe_grouped_gemm(dacT[:, c0:c0 + kp], xT[:, c0:c0 + kp].unsqueeze(0), g_2i, 0, 1, 2 * I, dw13[e])
+        dwr = L.moe_router_wgrad(x, st_, offs, du_row, N)
+        return {"dx": dx, "dw_router": dwr, "dw13": dw13, "dw2": dw2, "du": du, "du_row": du_row, "dy": dy,
+                "dac": dac, "dx_routed": dxr, "dx_shared": dxs}

@@ -525,6 +525,17 @@ def pin_backward_closed_forms():
     assert np.allclose(g["dw2"][1], w2t.grad.numpy(), rtol=1e-12, atol=1e-12)
 
 
+def pin_backward_bf16_model_close_to_exact():
+    """The bf16-storage model of the backward is a small perturbation of the exact gradients."""
+    x, wr, b, w13, w2 = _tiny_layer(25, T=16, d=32, N=6, I=16, scale=0.3)
+    d_out = _rng(26).standard_normal((16, 32))
+    ex = O.backward(x, wr, b, w13, w2, 2, d_out)
+    bf = O.backward(x, wr, b, w13, w2, 2, d_out, precision="bf16")
+    for k in ("dx", "dw_router", "dw13", "dw2"):
+        e = np.max(np.abs(bf[k] - ex[k])) / np.sqrt(np.mean(ex[k] ** 2))
+        assert 0 < e < 0.05, (k, e)
+
+
 def pin_layer_flops():
     # DeepSeek-V3 shape: 9 of 257 experts per token; 2*7168*256 + 6*7168*2048*9 per token
     assert O.layer_flops(1, 7168, 256, 8, 2048) == 796_393_472

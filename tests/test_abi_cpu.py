@@ -30,7 +30,7 @@ def test_header_declares_exactly_the_exports():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.lib().moe_abi_version() == 3
+    assert L.lib().moe_abi_version() == 4
     assert L.status_str(0) == "MOE_OK" and L.status_str(5) == "MOE_ERR_WORKSPACE"
 
 
