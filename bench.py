@@ -346,6 +346,34 @@ def main():
                     "gate_up_mfma_frac": round(fl3 / (gu3e / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4)})
         log(f"[bench] {c3.name}_e8m0: {ms3e:.3f} ms/step, gate/up {gu3e:.3f} ms")
         del l3e
+        # the backward pass of the headline layer (bf16): gradients of x, the router and every
+        # expert's weights for a seeded d_out
+        lb = M.MoELayer(wr, W13, W2, bias_cpu.to(dev), cfg.top_k, cfg.n_group, cfg.topk_group)
+        xb = xs_cpu[0].to(dev)
+        _, bufb = lb.forward(xb, keep=True)
+        d_out = I.gen_normal(cfg.seed + 900, (cfg.T, cfg.d), 1.0).to(dev)
+        gb = lb.backward(d_out, bufb)  # warm-up; makes the transposed weight copies once
+        keep_g = {"dw13": gb["dw13"], "dw2": gb["dw2"]}  # weight gradients reused across steps
+        del gb
+        torch.cuda.synchronize()
+        nb = 3
+        sb, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        sb.record()
+        for _ in range(nb):
+            gb = lb.backward(d_out, bufb, keep_g)
+            del gb
+        eb.record()
+        torch.cuda.synchronize()
+        msb = sb.elapsed_time(eb) / nb
+        fb = 2 * O.layer_flops(cfg.T, cfg.d, cfg.n_experts, cfg.top_k, cfg.inter) + 4 * cfg.rows * cfg.d * cfg.inter
+        sec.append({"workload": cfg.name + "_backward", "dtype": "bf16", "ms_per_step": round(msb, 4),
+                    "tokens_per_s": round(cfg.T / (msb / 1e3), 1), "tflops": round(fb / (msb / 1e3) / 1e12, 2),
+                    "mfma_frac_bf16_peak": round(fb / (msb / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                    "note": "dx, dW_r, dW13, dW2 (f32); gate/up products recomputed; weight-transpose copies made "
+                            "once, outside the timed region"})
+        log(f"[bench] {cfg.name}_backward: {msb:.3f} ms per backward")
+        del lb, bufb, d_out, keep_g
+        torch.cuda.empty_cache()
         c2 = I.V3_GROUP
         l2, _, _, _, ms2, _ = measure(c2, False, max(5, args.steps // 2), 3)
         f2 = O.layer_flops(c2.T, c2.d, c2.n_experts, c2.top_k, c2.inter)

@@ -317,6 +317,9 @@ moe_status moe_swiglu_backward(const float* ac, const float* dh, int64_t rows, i
  * its transpose: for segment g (rows [seg_offsets[g], seg_offsets[g+1]) of the logical
  * source), column dst_cols[g] + i of dst holds source row seg_offsets[g] + i (read through
  * src_rows if not NULL) for i < the segment's length, and zeros up to dst_cols[g+1].
+ * With seg_stride > 0 each segment instead gets its own block: element (c, i) of segment g
+ * at dst + g * seg_stride + c * ld_dst + i, i < dst_cols[g+1] - dst_cols[g] (equal widths make
+ * [n_segments][cols][width] operands for one grouped GEMM over all segments).
  *   src         device bf16, rows of `cols` elements, leading dimension ld_src
  *   src_rows    device i32 gather index per logical row, or NULL
  *   seg_offsets device i32 [n_segments+1];  dst_cols device i32 [n_segments+1], non-decreasing,
@@ -328,7 +331,7 @@ moe_status moe_swiglu_backward(const float* ac, const float* dh, int64_t rows, i
 moe_status moe_segment_transpose(const uint16_t* src, int64_t ld_src, const int32_t* src_rows,
                                  const int32_t* seg_offsets, const int32_t* dst_cols,
                                  int n_segments, int cols, int total_cols, uint16_t* dst,
-                                 int64_t ld_dst, hipStream_t stream);
+                                 int64_t ld_dst, int64_t seg_stride, hipStream_t stream);
 
 /* moe_router_wgrad -- dW_r[e] = sum over expert e's sorted rows r of du_row[r] x[sorted_token[r]]
  * (fp32, rows in order).

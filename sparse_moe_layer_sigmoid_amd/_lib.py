@@ -94,7 +94,7 @@ def lib() -> ctypes.CDLL:
         L.moe_swiglu_backward.restype = _i
         L.moe_swiglu_backward.argtypes = [_p, _p, _i64, _i, _p, _p]
         L.moe_segment_transpose.restype = _i
-        L.moe_segment_transpose.argtypes = [_p, _i64, _p, _p, _p, _i, _i, _i, _p, _i64, _p]
+        L.moe_segment_transpose.argtypes = [_p, _i64, _p, _p, _p, _i, _i, _i, _p, _i64, _i64, _p]
         L.moe_router_wgrad.restype = _i
         L.moe_router_wgrad.argtypes = [_p, _p, _p, _p, _i, _i, _p, _p]
         _LIB = L
@@ -322,18 +322,21 @@ def moe_swiglu_backward(ac, dh, dac=None):
     return dac
 
 
-def moe_segment_transpose(src, seg_offsets, dst_cols, total_cols: int, src_rows=None, dst=None):
+def moe_segment_transpose(src, seg_offsets, dst_cols, total_cols: int, src_rows=None, dst=None, width: int = 0):
     """Row segments of src [*, C] (gathered through src_rows if given) -> zero-padded column
-    blocks of dst [C, total_cols] bf16."""
+    blocks of dst [C, total_cols] bf16; with width > 0 (and dst_cols = g * width) separate
+    blocks dst [G, C, width]."""
     _dev(src, torch.bfloat16, "src", contiguous=False)
     if src.stride(-1) != 1:
         raise ValueError("rows of src must be contiguous")
     C = src.shape[1]
-    if dst is None:
-        dst = torch.empty((C, total_cols), dtype=torch.bfloat16, device=src.device)
     G = seg_offsets.numel() - 1
+    if dst is None:
+        shape = (G, C, width) if width else (C, total_cols)
+        dst = torch.empty(shape, dtype=torch.bfloat16, device=src.device)
+    ld = width if width else dst.stride(0)
     st = lib().moe_segment_transpose(_ptr(src), src.stride(0), _ptr(src_rows), _ptr(seg_offsets), _ptr(dst_cols), G,
-                                     C, total_cols, _ptr(dst), dst.stride(0), _stream(src))
+                                     C, total_cols, _ptr(dst), ld, C * width if width else 0, _stream(src))
     _check("moe_segment_transpose", st)
     return dst
 

@@ -12,9 +12,11 @@
 //  * moe_swiglu_backward: da = dh c silu'(a), dc = dh silu(a), silu'(a) = sig(a)(1 + a(1 - sig(a))),
 //    four elements per lane, HBM-bound.
 //  * moe_segment_transpose: row segments of a row-major matrix (optionally gathered) become
-//    column blocks of its transpose, each padded with zero columns to a given start, so each
-//    expert's weight-gradient GEMM reduces over its own rows with K-contiguous operands.
-//    64 x 64 tiles through LDS; both the loads and the stores are 16-byte and coalesced.
+//    column blocks of its transpose, each padded with zero columns to a given start (or, with
+//    a segment stride, separate zero-padded [cols, width] blocks), so each expert's
+//    weight-gradient GEMM reduces over its own rows with K-contiguous operands, and equal-width
+//    blocks let one grouped GEMM cover every expert.  64 x 64 tiles through LDS; both the loads
+//    and the stores are 16-byte and coalesced.
 //  * moe_router_wgrad: dW_r[e] = sum over e's sorted rows r of du_row[r] * x[token(r)], one
 //    workgroup per (expert, 2048 columns), rows in order (deterministic).
 #include "abi_common.h"
@@ -126,13 +128,14 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(const float* __res
 // Output column j of the transpose: source row of segment g = the segment whose padded column
 // block holds j, or -1 for a padding column.
 __device__ __forceinline__ int transpose_source(int j, const int32_t* __restrict__ seg, const int32_t* __restrict__ col,
-                                                int G, const int32_t* __restrict__ gather) {
+                                                int G, const int32_t* __restrict__ gather, int* g_out) {
   int lo = 0, hi = G;  // largest g with col[g] <= j
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (col[mid] <= j) lo = mid;
     else hi = mid;
   }
+  *g_out = lo;
   const int local = j - col[lo];
   if (local >= seg[lo + 1] - seg[lo]) return -1;
   const int r = seg[lo] + local;
@@ -145,7 +148,8 @@ __global__ __launch_bounds__(256) void segment_transpose_kernel(const uint16_t* 
                                                                 const int32_t* __restrict__ gather,
                                                                 const int32_t* __restrict__ seg,
                                                                 const int32_t* __restrict__ col, int G, int C,
-                                                                int total, uint16_t* __restrict__ dst, int64_t ldd) {
+                                                                int total, uint16_t* __restrict__ dst, int64_t ldd,
+                                                                int64_t seg_stride) {
   __shared__ uint16_t tile[64][64 + 8];
   const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int tid = threadIdx.x;
@@ -156,7 +160,8 @@ __global__ __launch_bounds__(256) void segment_transpose_kernel(const uint16_t* 
     const int j = j0 + jl;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (j < total && c0 + ch * 8 < C) {
-      const int s = transpose_source(j, seg, col, G, gather);
+      int g;
+      const int s = transpose_source(j, seg, col, G, gather, &g);
       if (s >= 0) v = *(const u32x4*)(src + (int64_t)s * lds + c0 + ch * 8);
     }
 #pragma unroll
@@ -175,7 +180,17 @@ __global__ __launch_bounds__(256) void segment_transpose_kernel(const uint16_t* 
       u32x4 o;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = (uint32_t)tile[jc * 8 + 2 * i][cl] | ((uint32_t)tile[jc * 8 + 2 * i + 1][cl] << 16);
-      *(u32x4*)(dst + (int64_t)c * ldd + j) = o;
+      int64_t at = (int64_t)c * ldd + j;
+      if (seg_stride > 0) {  // blocked: segment g's block at g * seg_stride, columns from its start
+        int lo = 0, hi = G;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (col[mid] <= j) lo = mid;
+          else hi = mid;
+        }
+        at = (int64_t)lo * seg_stride + (int64_t)c * ldd + (j - col[lo]);
+      }
+      *(u32x4*)(dst + at) = o;
     }
   }
 }
@@ -247,7 +262,7 @@ extern "C" moe_status moe_swiglu_backward(const float* ac, const float* dh, int6
 extern "C" moe_status moe_segment_transpose(const uint16_t* src, int64_t ld_src, const int32_t* src_rows,
                                             const int32_t* seg_offsets, const int32_t* dst_cols, int n_segments,
                                             int cols, int total_cols, uint16_t* dst, int64_t ld_dst,
-                                            hipStream_t stream) {
+                                            int64_t seg_stride, hipStream_t stream) {
   using namespace moe;
   clear_error();
   MOE_REQUIRE(seg_offsets && dst_cols && (total_cols == 0 || (src && dst)), MOE_ERR_NULL,
@@ -255,14 +270,16 @@ extern "C" moe_status moe_segment_transpose(const uint16_t* src, int64_t ld_src,
   MOE_REQUIRE(n_segments >= 1 && cols >= 8 && cols % 8 == 0 && total_cols >= 0 && total_cols % 8 == 0, MOE_ERR_SHAPE,
               "moe_segment_transpose: n_segments=%d cols=%d total_cols=%d (cols, total_cols multiples of 8)",
               n_segments, cols, total_cols);
-  MOE_REQUIRE(ld_src >= cols && ld_src % 8 == 0 && ld_dst >= total_cols && ld_dst % 8 == 0 && aligned16(src) &&
-                  aligned16(dst),
+  MOE_REQUIRE(seg_stride >= 0 && seg_stride % 8 == 0, MOE_ERR_ALIGN, "moe_segment_transpose: seg_stride=%lld",
+              (long long)seg_stride);
+  MOE_REQUIRE(ld_src >= cols && ld_src % 8 == 0 && ld_dst % 8 == 0 && (seg_stride > 0 || ld_dst >= total_cols) &&
+                  aligned16(src) && aligned16(dst),
               MOE_ERR_ALIGN, "moe_segment_transpose: ld_src=%lld ld_dst=%lld must keep rows 16-byte aligned",
               (long long)ld_src, (long long)ld_dst);
   if (total_cols > 0) {
     const dim3 grid((total_cols + 63) / 64, (cols + 63) / 64);
     segment_transpose_kernel<<<grid, 256, 0, stream>>>(src, ld_src, src_rows, seg_offsets, dst_cols, n_segments, cols,
-                                                       total_cols, dst, ld_dst);
+                                                       total_cols, dst, ld_dst, seg_stride);
   }
   return check_launch("moe_segment_transpose");
 }

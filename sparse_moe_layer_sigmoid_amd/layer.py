@@ -99,9 +99,10 @@ class MoELayer:
                 L.moe_segment_transpose(self.W2[g], s2, s2, d, dst=self._W2T[g])
         return self._W13T, self._W2T
 
-    def backward(self, d_out, buf):
+    def backward(self, d_out, buf, grads=None):
         """Gradients of sum(d_out * out) for the forward that returned `buf` (keep=True):
         dict of dx [T, d], dw_router [N, d], dw13 [N+1, 2I, d], dw2 [N+1, d, I], all f32.
+        `grads` may hold preallocated dw13 / dw2 tensors (overwritten) to reuse across steps.
 
         Sequence: combine backward (dy, router logit gradients) -> Dgrad of the down projection
         (dh = dy W2) -> gate/up recomputed without SwiGLU (a | c) -> SwiGLU backward -> Dgrad of
@@ -115,6 +116,9 @@ class MoELayer:
         rows = T * (K + 1)
         dev = x.device
         offs, st_, pp = buf["expert_offsets"], buf["sorted_token"], buf["pair_pos"]
+        # the expert sizes size the weight-gradient operands: read once, before any launch, so
+        # the rest of the pass is queued without waiting
+        lens = (offs[1:] - offs[:-1]).cpu()
         d_out = d_out.to(torch.bfloat16).contiguous()
         dy, du, du_row = L.moe_combine_backward(d_out, buf["y"], buf["topk_idx"], buf["topk_gate"], buf["scores"], pp)
         dh = torch.empty((rows, I), dtype=torch.float32, device=dev)
@@ -130,29 +134,43 @@ class MoELayer:
         # first (a combine over the router rows), then the routed rows
         part = L.moe_combine(self.w_router, dxs, buf["topk_idx"], du, torch.float32)
         dx = L.moe_combine(dxr, part, pp, torch.ones((T, K), dtype=torch.float32, device=dev), torch.float32)
-        # Wgrad: each expert's rows as the reduction axis, padded to a multiple of 64
-        offs_h = offs.cpu().numpy().astype("int64")
-        lens = offs_h[1:] - offs_h[:-1]
-        pads = ((lens + 63) // 64) * 64
-        cols = [0]
-        for p in pads:
-            cols.append(cols[-1] + int(p))
-        total = cols[-1]
-        dst_cols = torch.tensor(cols, dtype=torch.int32, device=dev)
-        dyT = L.moe_segment_transpose(dy, offs, dst_cols, total)
-        hT = L.moe_segment_transpose(buf["h"], offs, dst_cols, total)
-        dacT = L.moe_segment_transpose(dac, offs, dst_cols, total)
-        xT = L.moe_segment_transpose(x, offs, dst_cols, total, src_rows=st_)
-        dw2 = torch.zeros((G, d, I), dtype=torch.float32, device=dev)
-        dw13 = torch.zeros((G, 2 * I, d), dtype=torch.float32, device=dev)
-        g_d = torch.tensor([0, d], dtype=torch.int32, device=dev)
-        g_2i = torch.tensor([0, 2 * I], dtype=torch.int32, device=dev)
-        for e in range(G):
-            if lens[e] == 0:
-                continue
-            c0, kp = cols[e], int(pads[e])
-            L.moe_grouped_gemm(dyT[:, c0:c0 + kp], hT[:, c0:c0 + kp].unsqueeze(0), g_d, 0, 1, d, dw2[e])
-            L.moe_grouped_gemm(dacT[:, c0:c0 + kp], xT[:, c0:c0 + kp].unsqueeze(0), g_2i, 0, 1, 2 * I, dw13[e])
+        # Wgrad: each expert's rows are the reduction axis.  The routed experts' rows become
+        # equal-width zero-padded blocks [N][C][kmax] (kmax = the largest routed segment,
+        # rounded up to 64), so one grouped GEMM covers all of them (an empty expert's blocks
+        # are zeros, so its gradient comes out zero); the shared expert (all T tokens) has
+        # its own launch.
+        kmax = max(64, (int(lens[:N].max()) + 63) // 64 * 64)
+        kp_s = (int(lens[N]) + 63) // 64 * 64
+        cols_r = torch.arange(0, (N + 1) * kmax, kmax, dtype=torch.int32, device=dev)
+        cols_s = torch.tensor([0, kp_s], dtype=torch.int32, device=dev)
+        seg_r, seg_s = offs[:N + 1], offs[N:N + 2]
+        T_ = lambda src, seg, cols, total, width=0, rows_=None: L.moe_segment_transpose(
+            src, seg, cols, total, src_rows=rows_, width=width)
+        dyT = T_(dy, seg_r, cols_r, N * kmax, kmax)                 # [N, d, kmax]
+        hT = T_(buf["h"], seg_r, cols_r, N * kmax, kmax)            # [N, I, kmax]
+        dacT = T_(dac, seg_r, cols_r, N * kmax, kmax)               # [N, 2I, kmax]
+        xT = T_(x, seg_r, cols_r, N * kmax, kmax, st_)              # [N, d, kmax]
+        grads = grads or {}
+        dw2 = grads.get("dw2")
+        dw13 = grads.get("dw13")
+        if dw2 is None:
+            dw2 = torch.empty((G, d, I), dtype=torch.float32, device=dev)
+        if dw13 is None:
+            dw13 = torch.empty((G, 2 * I, d), dtype=torch.float32, device=dev)
+        g_d = torch.arange(0, (N + 1) * d, d, dtype=torch.int32, device=dev)
+        g_2i = torch.arange(0, (N + 1) * 2 * I, 2 * I, dtype=torch.int32, device=dev)
+        L.moe_grouped_gemm(dyT.view(N * d, kmax), hT, g_d, 0, N, N * d, dw2[:N].view(N * d, I))
+        L.moe_grouped_gemm(dacT.view(N * 2 * I, kmax), xT, g_2i, 0, N, N * 2 * I, dw13[:N].view(N * 2 * I, d))
+        if kp_s > 0:
+            dyT_s = T_(dy, seg_s, cols_s, kp_s)                     # [d, kp_s]
+            hT_s = T_(buf["h"], seg_s, cols_s, kp_s)
+            dacT_s = T_(dac, seg_s, cols_s, kp_s)
+            xT_s = T_(x, seg_s, cols_s, kp_s, 0, st_)
+            L.moe_grouped_gemm(dyT_s, hT_s.unsqueeze(0), g_d[:2], 0, 1, d, dw2[N])
+            L.moe_grouped_gemm(dacT_s, xT_s.unsqueeze(0), g_2i[:2], 0, 1, 2 * I, dw13[N])
+        else:
+            dw2[N].zero_()
+            dw13[N].zero_()
         dwr = L.moe_router_wgrad(x, st_, offs, du_row, N)
         return {"dx": dx, "dw_router": dwr, "dw13": dw13, "dw2": dw2, "du": du, "du_row": du_row, "dy": dy,
                 "dac": dac, "dx_routed": dxr, "dx_shared": dxs}

@@ -42,6 +42,23 @@ def test_segment_transpose_bitexact():
     assert np.array_equal(out.float().cpu().numpy(), want)
 
 
+def test_segment_transpose_blocked():
+    """Equal-width blocks [G][C][width]: segment g's rows land in its own zero-padded block."""
+    lens = np.array([3, 0, 64, 40, 1])
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    width = 64
+    cols = np.arange(0, (len(lens) + 1) * width, width).astype(np.int32)
+    C = 72
+    src = I.gen_normal(74, (int(offs[-1]), C), 1.0)
+    out = M()._lib.moe_segment_transpose(src.to(DEV), torch.from_numpy(offs).to(DEV), torch.from_numpy(cols).to(DEV),
+                                         int(cols[-1]), width=width)
+    want = np.zeros((len(lens), C, width), dtype=np.float32)
+    s = src.float().numpy()
+    for g in range(len(lens)):
+        want[g, :, :lens[g]] = s[offs[g]:offs[g + 1]].T
+    assert np.array_equal(out.float().cpu().numpy(), want)
+
+
 def test_swiglu_backward():
     rows, inter = 77, 256
     ac = I.gen_normal(72, (rows, 2 * inter), 2.0, dtype=torch.float32)
