@@ -142,6 +142,82 @@ def test_v3_fp8_e8m0_T16384(v3):
     torch.cuda.empty_cache()
 
 
+class _LazyExperts:
+    """Expert weights regenerated on the host one at a time, as the oracle asks for them."""
+
+    def __init__(self, cfg, which):
+        self.cfg, self.which, self.cache = cfg, which, {}
+
+    def __getitem__(self, e):
+        if e not in self.cache:
+            self.cache[e] = I.gen_expert(self.cfg, e)[self.which].double().numpy()
+        return self.cache[e]
+
+
+def test_v3_bf16_T4096_backward(v3):
+    """The backward at the headline shape.  Staged, for sampled experts (a hot one, a light one,
+    the shared one) and sampled tokens: every device stage against float64 recomputed from the
+    device's own upstream values.  End to end: the sampled tokens' dx against the oracle's
+    bf16-storage model (a token's dx depends only on its own experts)."""
+    cfg = I.V3_BF16
+    x_cpu = I.gen_x(cfg)
+    bias = I.gen_bias(cfg)
+    layer = M().MoELayer(v3.wr, v3.W13, v3.W2, bias.to(DEV), cfg.top_k)
+    out, buf = layer.forward(x_cpu.to(DEV), out_dtype=torch.float32, keep=True)
+    d_out = I.gen_normal(cfg.seed + 900, (cfg.T, cfg.d), 1.0)
+    t0 = time.time()
+    g = layer.backward(d_out.to(DEV), buf)
+    torch.cuda.synchronize()
+    say(f"[fullsize] backward done in {time.time() - t0:.2f}s (first call: includes the weight transposes)")
+    offs = buf["expert_offsets"].cpu().numpy()
+    st_ = buf["sorted_token"].cpu().numpy()
+    pp = buf["pair_pos"].cpu().numpy()
+    idx = buf["topk_idx"].cpu().numpy()
+    x64 = np64(x_cpu)
+    wr64 = np64(v3.wr_cpu)
+    lens = offs[1:] - offs[:-1]
+    experts = [int(np.argmax(lens[:cfg.n_experts])), int(np.argmin(np.where(lens[:cfg.n_experts] > 0, lens[:cfg.n_experts], 1 << 30))),
+               cfg.n_experts]
+    I_ = cfg.inter
+    dy = np64(g["dy"])
+    dac = np64(g["dac"])
+    h = np64(buf["h"])
+    du_row = g["du_row"].cpu().numpy().astype(np.float64)
+    dw_r = g["dw_router"].cpu().numpy().astype(np.float64)
+    for e in experts:
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        w13, w2 = (t_.double().numpy() for t_ in I.gen_expert(cfg, e))
+        xe = x64[st_[lo:hi]]
+        a, c = xe @ w13[:I_].T, xe @ w13[I_:].T
+        dh = dy[lo:hi] @ w2
+        sg = O.sigmoid(a)
+        dac_ref = np.concatenate([dh * c * sg * (1 + a * (1 - sg)), dh * a * sg], axis=1)
+        half = np.exp2(np.floor(np.log2(np.maximum(np.abs(dac_ref), 1e-30))) - 8)
+        worst = np.max(np.abs(dac[lo:hi] - dac_ref) / (half * 1.001 + 1e-4 * np.sqrt(np.mean(dac_ref ** 2))))
+        e2 = rel_err(g["dw2"][e].cpu().numpy(), dy[lo:hi].T @ h[lo:hi])
+        e13 = rel_err(g["dw13"][e].cpu().numpy(), dac[lo:hi].T @ xe)
+        say(f"[fullsize] expert {e} ({hi - lo} rows): dac {worst:.3f} of its bound, dW2 {e2:.2e}, dW13 {e13:.2e}")
+        assert worst <= 1.0 and e2 <= 1e-4 and e13 <= 1e-4
+        if e < cfg.n_experts:
+            er = rel_err(dw_r[e], du_row[lo:hi] @ xe)
+            assert er <= 1e-4, er
+    pick = np.linspace(0, cfg.T - 1, 12).astype(int)
+    dx = g["dx"].cpu().numpy().astype(np.float64)
+    dxr = np64(g["dx_routed"])
+    dxs = g["dx_shared"].cpu().numpy().astype(np.float64)
+    du = g["du"].cpu().numpy().astype(np.float64)
+    staged = dxs[pick] + sum(du[pick, k:k + 1] * wr64[idx[pick, k]] + dxr[pp[pick, k]] for k in range(cfg.top_k))
+    es = rel_err(dx[pick], staged)
+    say(f"[fullsize] oracle backward (bf16 model) on {len(pick)} sampled tokens ...")
+    t0 = time.time()
+    model = O.backward(x64[pick], wr64, bias.numpy(), _LazyExperts(cfg, 0), _LazyExperts(cfg, 1), cfg.top_k,
+                       np64(d_out)[pick], precision="bf16")
+    assert np.array_equal(model["route"]["idx"], idx[pick])
+    ee = rel_err(dx[pick], model["dx"])
+    say(f"[fullsize] backward dx: staged {es:.2e}, vs the bf16 model {ee:.2e} (tol 1e-2) [{time.time() - t0:.0f}s]")
+    assert es <= 1e-4 and ee <= 1e-2
+
+
 def test_v3_decode_bias_loop(v3):
     """The decode-shaped run: 100 training-mode steps of T = 256 fresh tokens with the
     Zipf-skewed bias.  While no token falls in the tie window the GPU's loads and bias
