@@ -335,7 +335,31 @@ def main():
                     "gate_up_ms": round(gu3, 4), "gate_up_traffic": measured_traffic(f"gate_up_{c3.name}"),
                     "gate_up_mfma_frac": round(fl3 / (gu3 / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4)})
         log(f"[bench] {c3.name}: {ms3:.3f} ms/step, gate/up {gu3:.3f} ms")
-        del l3
+        # its backward on the FP8 path (E4M3 Dgrad and Wgrad)
+        x3 = I.gen_x(c3).to(dev)
+        _, buf3 = l3.forward(x3, keep=True)
+        d3 = I.gen_normal(c3.seed + 900, (c3.T, c3.d), 1.0).to(dev)
+        g3 = l3.backward(d3, buf3)  # warm-up; makes the transposed E4M3 weights once
+        keep3 = {"dw13": g3["dw13"], "dw2": g3["dw2"]}
+        del g3
+        torch.cuda.synchronize()
+        s3, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s3.record()
+        for _ in range(3):
+            g3 = l3.backward(d3, buf3, keep3)
+            del g3
+        e3.record()
+        torch.cuda.synchronize()
+        ms3b = s3.elapsed_time(e3) / 3
+        fb3 = 2 * f3 + 4 * c3.rows * c3.d * c3.inter
+        sec.append({"workload": c3.name + "_backward", "dtype": "fp8", "ms_per_step": round(ms3b, 4),
+                    "tokens_per_s": round(c3.T / (ms3b / 1e3), 1), "tflops": round(fb3 / (ms3b / 1e3) / 1e12, 2),
+                    "mfma_frac_fp8_peak": round(fb3 / (ms3b / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                    "note": "E4M3 Dgrad and Wgrad (1x128 / 128x128 scales, transposed operands quantised); f32 "
+                            "weight gradients"})
+        log(f"[bench] {c3.name}_backward: {ms3b:.3f} ms per backward")
+        del l3, buf3, d3, keep3, x3
+        torch.cuda.empty_cache()
         # the same layer with power-of-two (E8M0) tile scales applied by the matrix cores
         l3e, _, _, _, ms3e, gu3e = measure(c3, True, max(5, args.steps // 2), 3, scales="e8m0")
         sec.append({"workload": c3.name + "_e8m0", "dtype": "fp8", "scales": "e8m0", "ms_per_step": round(ms3e, 4),

@@ -165,6 +165,13 @@ moe_status fp8_quant_128x128(const uint16_t* w, int n_mats, int n, int k, uint8_
  * ------------------------------------------------------------------------------------ */
 moe_status fp8_quant_1x128_e8m0(const uint16_t* x, int rows, int cols, int64_t ldx, uint8_t* q,
                                 uint8_t* scale, hipStream_t stream);
+
+/* fp8_dequant_1x128 -- the inverse view: out = RNE_bf16(decode(q) * scale) per 1x128 tile (the
+ * FP8 backward's Wgrad takes the stored E4M3 h of the forward this way).
+ *   q device u8 [rows, cols]; scale device f32 [rows, cols/128]; out device bf16 [rows, cols].
+ * Limits: rows >= 0; cols >= 128, cols % 128 == 0. */
+moe_status fp8_dequant_1x128(const uint8_t* q, const float* scale, int rows, int cols,
+                             uint16_t* out, hipStream_t stream);
 moe_status fp8_quant_128x128_e8m0(const uint16_t* w, int n_mats, int n, int k, uint8_t* q,
                                   uint8_t* scale, hipStream_t stream);
 

@@ -549,10 +549,19 @@ def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, to
     precision "bf16" models the stored bfloat16 intermediates of the bf16 path: the forward's h
     and routed y, dy (the float32 product g * d_out, then bf16), [da | dc] and the routed rows'
     dx contributions are rounded to bf16 (RNE); everything else stays float64.
+    precision "fp8" models the FP8 path ([TR] "FP8 混合精度訓練": Fprop, Dgrad and Wgrad in E4M3
+    with 1x128 / 128x128 scaling): the forward as ``forward_sparse(..., "fp8")`` computes it
+    (E4M3 x and weights, h stored as 1x128 E4M3, routed y bf16); Dgrad: dy and [da | dc] (bf16)
+    quantised 1x128 along their reduction axis against the 128x128-quantised weights (the
+    blocks of W^T are those of W, transposed); Wgrad: per expert, the operands transposed with
+    the tokens as the reduction axis, zero-padded to a multiple of 128 from the expert's first
+    row, dy^T and [da | dc]^T quantised 1x128 along the tokens, h^T (the stored E4M3 h as bf16)
+    and x^T (the bf16 input) in 128x128 blocks; sums exact (float64).
     Returns dx [T, d], dw_router [N, d], dw13 [N+1, 2I, d], dw2 [N+1, d, I] and the
     intermediates dgate [T, K], du [T, K] and the routing dict."""
-    assert precision in ("exact", "bf16")
-    rnd = bf16_round if precision == "bf16" else (lambda v: v)
+    assert precision in ("exact", "bf16", "fp8")
+    fp8 = precision == "fp8"
+    rnd = bf16_round if precision != "exact" else (lambda v: v)
     x = np.asarray(x, dtype=np.float64)
     wr = np.asarray(w_router, dtype=np.float64)
     d_out = np.asarray(d_out, dtype=np.float64)
@@ -565,6 +574,14 @@ def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, to
     dw13 = np.zeros((N + 1, 2 * I, d))
     dw2 = np.zeros((N + 1, d, I))
     dgate = np.zeros((T, top_k))
+    x_in = dequant_1x128(*quant_1x128(x)) if fp8 else x
+
+    def q_rows(m):     # 1x128 along the last axis, dequantised
+        return dequant_1x128(*quant_1x128(m))
+
+    def pad128(m):     # zero columns up to a multiple of 128
+        return np.pad(m, ((0, 0), (0, (-m.shape[1]) % 128)))
+
     for e in range(N + 1):
         if e < N:
             tok, slot = np.nonzero(idx == e)   # each token picks distinct experts: tok is unique
@@ -574,24 +591,35 @@ def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, to
             continue
         we13 = np.asarray(w13[e], dtype=np.float64)
         we2 = np.asarray(w2[e], dtype=np.float64)
-        xe = x[tok]
+        if fp8:
+            we13 = dequant_128x128(*quant_128x128(we13))
+            we2 = dequant_128x128(*quant_128x128(we2))
+        xe = x_in[tok]
         a = xe @ we13[:I].T
         c = xe @ we13[I:].T
         sg = sigmoid(a)
-        h = rnd(a * sg * c)
+        h = a * sg * c
+        h = q_rows(fp32_round(h)) if fp8 else rnd(h)
         if e < N:
             dy = gate[tok, slot][:, None] * d_out[tok]
-            dy = rnd(fp32_round(dy)) if precision == "bf16" else dy
+            dy = rnd(fp32_round(dy)) if precision != "exact" else dy
             dgate[tok, slot] = np.sum(d_out[tok] * rnd(h @ we2.T), axis=1)
         else:
             dy = d_out
-        dw2[e] = dy.T @ h
-        dh = dy @ we2
+        dh = (q_rows(dy) if fp8 else dy) @ we2
         da = rnd(dh * c * sg * (1.0 + a * (1.0 - sg)))
         dc = rnd(dh * a * sg)
-        dw13[e, :I] = da.T @ xe
-        dw13[e, I:] = dc.T @ xe
-        dxe = da @ we13[:I] + dc @ we13[I:]
+        dac = np.concatenate([da, dc], axis=1)
+        if fp8:
+            dxe = q_rows(dac) @ we13
+            n = len(tok)
+            dw2[e] = q_rows(pad128(dy.T)) @ dequant_128x128(*quant_128x128(pad128(bf16_round(h).T))).T
+            dw13[e] = q_rows(pad128(dac.T)) @ dequant_128x128(*quant_128x128(pad128(x[tok].T))).T
+            assert dw2[e].shape == (d, I) and n > 0
+        else:
+            dw2[e] = dy.T @ h
+            dw13[e] = dac.T @ xe
+            dxe = dac @ we13
         dx[tok] += rnd(dxe) if e < N else dxe
     ssel = np.take_along_axis(s, idx, axis=1)
     S = ssel.sum(axis=1, keepdims=True)

@@ -22,7 +22,7 @@ EXPORTS = (
     "moe_status_str", "moe_last_error", "moe_abi_version",
     "moe_route_workspace_size", "moe_route",
     "moe_permute_workspace_size", "moe_permute",
-    "fp8_quant_1x128", "fp8_quant_128x128", "fp8_quant_1x128_e8m0", "fp8_quant_128x128_e8m0",
+    "fp8_quant_1x128", "fp8_quant_128x128", "fp8_quant_1x128_e8m0", "fp8_quant_128x128_e8m0", "fp8_dequant_1x128",
     "moe_grouped_gemm", "moe_combine", "moe_bias_update",
     "moe_combine_backward", "moe_swiglu_backward", "moe_segment_transpose", "moe_router_wgrad",
 )
@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_quant_1x128_e8m0.argtypes = [_p, _i, _i, _i64, _p, _p, _p]
         L.fp8_quant_128x128_e8m0.restype = _i
         L.fp8_quant_128x128_e8m0.argtypes = [_p, _i, _i, _i, _p, _p, _p]
+        L.fp8_dequant_1x128.restype = _i
+        L.fp8_dequant_1x128.argtypes = [_p, _p, _i, _i, _p, _p]
         L.moe_grouped_gemm.restype = _i
         L.moe_grouped_gemm.argtypes = [ctypes.POINTER(MoeGemmDesc), _p]
         L.moe_combine.restype = _i
@@ -208,6 +210,16 @@ def fp8_quant_128x128(w):
 def fp8_quant_1x128_e8m0(x, q=None, scale=None):
     """As fp8_quant_1x128 with power-of-two scales: scale = E8M0 codes, uint8 [rows, cols/128]."""
     return _quant_1x128("fp8_quant_1x128_e8m0", torch.uint8, x, q, scale)
+
+
+def fp8_dequant_1x128(q, scale, out=None):
+    """q uint8 [rows, cols] E4M3 + scale f32 [rows, cols/128] -> bf16 [rows, cols] (RNE of q * s)."""
+    rows, cols = q.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=q.device)
+    st = lib().fp8_dequant_1x128(_ptr(q), _ptr(scale), rows, cols, _ptr(out), _stream(q))
+    _check("fp8_dequant_1x128", st)
+    return out
 
 
 def fp8_quant_128x128_e8m0(w):

@@ -146,6 +146,35 @@ moe_status quant_128x128(const char* fn, const uint16_t* w, int n_mats, int n, i
   return check_launch(fn);
 }
 
+// E4M3 code -> float (exact): E = 0 is M * 2^-9, else (1 + M/8) * 2^(E-7), rebuilt as fp32 bits.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 24, e = (c >> 3) & 15u, m = c & 7u;
+  const float sub = (float)m * (1.0f / 512.0f);
+  const float v = e == 0 ? sub : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return __uint_as_float(__float_as_uint(v) | s);
+}
+
+// q * s per 1x128 tile, stored RNE bf16: 8 codes per lane.
+__global__ __launch_bounds__(256) void dequant_1x128_kernel(const uint8_t* __restrict__ q, const float* __restrict__ scale,
+                                                            int64_t n8, int cols, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int64_t e0 = i * 8;
+  const int64_t r = e0 / cols;
+  const int c = (int)(e0 - r * cols);
+  const float s = scale[r * (cols / 128) + c / 128];
+  const u32x2 w = *(const u32x2*)(q + e0);
+  u32x4 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t word = k < 2 ? w[0] : w[1];
+    const int sh = (k & 1) * 16;
+    const float lo = e4m3_to_f32((word >> sh) & 255u) * s, hi = e4m3_to_f32((word >> (sh + 8)) & 255u) * s;
+    o[k] = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  }
+  *(u32x4*)(out + e0) = o;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -167,4 +196,21 @@ extern "C" moe_status fp8_quant_1x128_e8m0(const uint16_t* x, int rows, int cols
 extern "C" moe_status fp8_quant_128x128_e8m0(const uint16_t* w, int n_mats, int n, int k, uint8_t* q,
                                              uint8_t* scale, hipStream_t stream) {
   return moe::quant_128x128<true>("fp8_quant_128x128_e8m0", w, n_mats, n, k, q, scale, stream);
+}
+
+extern "C" moe_status fp8_dequant_1x128(const uint8_t* q, const float* scale, int rows, int cols, uint16_t* out,
+                                        hipStream_t stream) {
+  using namespace moe;
+  clear_error();
+  MOE_REQUIRE(rows == 0 || (q && scale && out), MOE_ERR_NULL, "fp8_dequant_1x128: a required pointer is NULL");
+  MOE_REQUIRE(rows >= 0 && cols >= 128 && cols % 128 == 0, MOE_ERR_SHAPE, "fp8_dequant_1x128: rows=%d cols=%d", rows, cols);
+  MOE_REQUIRE(((uintptr_t)q & 7u) == 0 && aligned16(out), MOE_ERR_ALIGN,
+              "fp8_dequant_1x128: q must be 8-byte and out 16-byte aligned");
+  const int64_t n8 = (int64_t)rows * cols / 8;
+  if (n8 > 0) {
+    const int64_t grid = (n8 + 255) / 256;
+    MOE_REQUIRE(grid < (int64_t)1 << 31, MOE_ERR_SHAPE, "fp8_dequant_1x128: too many rows");
+    dequant_1x128_kernel<<<(unsigned)grid, 256, 0, stream>>>(q, scale, n8, cols, out);
+  }
+  return check_launch("fp8_dequant_1x128");
 }

@@ -38,6 +38,8 @@ class MoELayer:
         self.topk_group = topk_group
         self.fp8 = fp8
         self.e8m0 = fp8 and fp8_scales == "e8m0"
+        # the FP8 backward quantises W^T itself, from the bf16 weights (held by reference)
+        self._src = (W13, W2) if fp8 else None
         if fp8:
             qw = L.fp8_quant_128x128_e8m0 if self.e8m0 else L.fp8_quant_128x128
             self.W13, self.W13_s = qw(W13)
@@ -84,31 +86,47 @@ class MoELayer:
     # ------------------------------------------------------------------ backward (bf16 path)
 
     def _transposed_weights(self):
-        """W13^T [N+1, d, 2I] and W2^T [N+1, I, d] (bf16), made once, for the Dgrad GEMMs."""
-        if getattr(self, "_W13T", None) is None:
-            if self.fp8:
-                raise NotImplementedError("the backward pass runs on the bf16 path")
-            G, I2, d = self.W13.shape
-            dev = self.W13.device
+        """W13^T [N+1, d, 2I] and W2^T [N+1, I, d] for the Dgrad GEMMs, made once: bf16, or on
+        the FP8 path E4M3 with 128x128 block scales (the blocks of W^T are those of W,
+        transposed, so these are the forward's codes and scales in transposed order)."""
+        if getattr(self, "_WT", None) is None:
+            if self.e8m0:
+                raise NotImplementedError("the backward pass runs on the bf16 and the f32-scale FP8 paths")
+            W13, W2 = self._src if self.fp8 else (self.W13, self.W2)
+            G, I2, d = W13.shape
+            dev = W13.device
             one = lambda n: torch.tensor([0, n], dtype=torch.int32, device=dev)
-            self._W13T = torch.empty((G, d, I2), dtype=torch.bfloat16, device=dev)
-            self._W2T = torch.empty((G, I2 // 2, d), dtype=torch.bfloat16, device=dev)
+            W13T = torch.empty((G, d, I2), dtype=torch.bfloat16, device=dev)
+            W2T = torch.empty((G, I2 // 2, d), dtype=torch.bfloat16, device=dev)
             s13, s2 = one(I2), one(d)
             for g in range(G):
-                L.moe_segment_transpose(self.W13[g], s13, s13, I2, dst=self._W13T[g])
-                L.moe_segment_transpose(self.W2[g], s2, s2, d, dst=self._W2T[g])
-        return self._W13T, self._W2T
+                L.moe_segment_transpose(W13[g], s13, s13, I2, dst=W13T[g])
+                L.moe_segment_transpose(W2[g], s2, s2, d, dst=W2T[g])
+            if self.fp8:
+                W13T, W13T_s = L.fp8_quant_128x128(W13T)
+                W2T, W2T_s = L.fp8_quant_128x128(W2T)
+                self._WT = (W13T, W2T, W13T_s, W2T_s)
+            else:
+                self._WT = (W13T, W2T, None, None)
+        return self._WT
 
-    def backward(self, d_out, buf, grads=None):
+    def backward(self, d_out, buf, grads=None, keep: bool = False):
         """Gradients of sum(d_out * out) for the forward that returned `buf` (keep=True):
         dict of dx [T, d], dw_router [N, d], dw13 [N+1, 2I, d], dw2 [N+1, d, I], all f32.
-        `grads` may hold preallocated dw13 / dw2 tensors (overwritten) to reuse across steps.
+        `grads` may hold preallocated dw13 / dw2 tensors (overwritten) to reuse across steps;
+        keep=True adds the intermediates (dy, du, dac, the input-gradient rows, FP8 operands).
+        On the FP8 path ([TR] "FP8 混合精度訓練": Dgrad and Wgrad in E4M3) every GEMM operand is
+        E4M3: dy and [da | dc] quantised 1x128 along their reduction axis against the 128x128
+        weight blocks (Dgrad); for Wgrad the transposed dy and [da | dc] quantised 1x128 along
+        the tokens and the transposed h (the stored E4M3 h, as bf16) and x in 128x128 blocks.
 
         Sequence: combine backward (dy, router logit gradients) -> Dgrad of the down projection
         (dh = dy W2) -> gate/up recomputed without SwiGLU (a | c) -> SwiGLU backward -> Dgrad of
         the gate/up projection (dx rows) -> two combines (router term + shared rows, then the
         routed rows) -> Wgrad per expert over transposed row segments -> router Wgrad."""
-        W13T, W2T = self._transposed_weights()
+        W13T, W2T, W13T_s, W2T_s = self._transposed_weights()
+        fp8 = self.fp8
+        q1 = L.fp8_quant_1x128
         x = buf["x"]
         T, d = x.shape
         N, K, I = self.N, self.top_k, self.I
@@ -121,15 +139,27 @@ class MoELayer:
         lens = (offs[1:] - offs[:-1]).cpu()
         d_out = d_out.to(torch.bfloat16).contiguous()
         dy, du, du_row = L.moe_combine_backward(d_out, buf["y"], buf["topk_idx"], buf["topk_gate"], buf["scores"], pp)
+        extra = {}
         dh = torch.empty((rows, I), dtype=torch.float32, device=dev)
-        L.moe_grouped_gemm(dy, W2T, offs, 0, G, rows, dh)
         ac = torch.empty((rows, 2 * I), dtype=torch.float32, device=dev)
-        L.moe_grouped_gemm(x, self.W13, offs, 0, G, rows, ac, a_rows=st_)
-        dac = L.moe_swiglu_backward(ac, dh)
-        del ac
         dxr = torch.empty((T * K, d), dtype=torch.bfloat16, device=dev)
         dxs = torch.empty((T, d), dtype=torch.float32, device=dev)
-        L.moe_grouped_gemm(dac, W13T, offs, 0, G, rows, dxr, out_tail=dxs, tail_groups=1)
+        if fp8:
+            dyq, dys = q1(dy)
+            L.moe_grouped_gemm(dyq, W2T, offs, 0, G, rows, dh, a_scale=dys, w_scale=W2T_s)
+            L.moe_grouped_gemm(buf["xq"], self.W13, offs, 0, G, rows, ac, a_scale=buf["xs"], a_rows=st_,
+                               w_scale=self.W13_s)
+            dac = L.moe_swiglu_backward(ac, dh)
+            dacq, dacs = q1(dac)
+            L.moe_grouped_gemm(dacq, W13T, offs, 0, G, rows, dxr, a_scale=dacs, w_scale=W13T_s, out_tail=dxs,
+                               tail_groups=1)
+            extra.update(dyq=dyq, dys=dys, dacq=dacq, dacs=dacs)
+        else:
+            L.moe_grouped_gemm(dy, W2T, offs, 0, G, rows, dh)
+            L.moe_grouped_gemm(x, self.W13, offs, 0, G, rows, ac, a_rows=st_)
+            dac = L.moe_swiglu_backward(ac, dh)
+            L.moe_grouped_gemm(dac, W13T, offs, 0, G, rows, dxr, out_tail=dxs, tail_groups=1)
+        del ac, dh
         # dx = sum_k dxr[pair] + dxs + sum_k du_k e_{idx_k}: the router term and the shared rows
         # first (a combine over the router rows), then the routed rows
         part = L.moe_combine(self.w_router, dxs, buf["topk_idx"], du, torch.float32)
@@ -139,15 +169,17 @@ class MoELayer:
         # rounded up to 64), so one grouped GEMM covers all of them (an empty expert's blocks
         # are zeros, so its gradient comes out zero); the shared expert (all T tokens) has
         # its own launch.
-        kmax = max(64, (int(lens[:N].max()) + 63) // 64 * 64)
-        kp_s = (int(lens[N]) + 63) // 64 * 64
+        kq = 128 if fp8 else 64  # K granule of the GEMM
+        kmax = max(kq, (int(lens[:N].max()) + kq - 1) // kq * kq)
+        kp_s = (int(lens[N]) + kq - 1) // kq * kq
         cols_r = torch.arange(0, (N + 1) * kmax, kmax, dtype=torch.int32, device=dev)
         cols_s = torch.tensor([0, kp_s], dtype=torch.int32, device=dev)
         seg_r, seg_s = offs[:N + 1], offs[N:N + 2]
         T_ = lambda src, seg, cols, total, width=0, rows_=None: L.moe_segment_transpose(
             src, seg, cols, total, src_rows=rows_, width=width)
+        h = L.fp8_dequant_1x128(buf["h"], buf["hs"]) if fp8 else buf["h"]
         dyT = T_(dy, seg_r, cols_r, N * kmax, kmax)                 # [N, d, kmax]
-        hT = T_(buf["h"], seg_r, cols_r, N * kmax, kmax)            # [N, I, kmax]
+        hT = T_(h, seg_r, cols_r, N * kmax, kmax)                   # [N, I, kmax]
         dacT = T_(dac, seg_r, cols_r, N * kmax, kmax)               # [N, 2I, kmax]
         xT = T_(x, seg_r, cols_r, N * kmax, kmax, st_)              # [N, d, kmax]
         grads = grads or {}
@@ -159,18 +191,32 @@ class MoELayer:
             dw13 = torch.empty((G, 2 * I, d), dtype=torch.float32, device=dev)
         g_d = torch.arange(0, (N + 1) * d, d, dtype=torch.int32, device=dev)
         g_2i = torch.arange(0, (N + 1) * 2 * I, 2 * I, dtype=torch.int32, device=dev)
-        L.moe_grouped_gemm(dyT.view(N * d, kmax), hT, g_d, 0, N, N * d, dw2[:N].view(N * d, I))
-        L.moe_grouped_gemm(dacT.view(N * 2 * I, kmax), xT, g_2i, 0, N, N * 2 * I, dw13[:N].view(N * 2 * I, d))
+        def wgrad(a_t, b_t, offsets, n_groups, m, out):
+            """out = A . B^T per group: A [n_groups * rows, k] (1x128 along k on the FP8 path),
+            B [n_groups, cols, k] (128x128 blocks)."""
+            if fp8:
+                aq, as_ = q1(a_t)
+                bq, bs = L.fp8_quant_128x128(b_t)
+                L.moe_grouped_gemm(aq, bq, offsets, 0, n_groups, m, out, a_scale=as_, w_scale=bs)
+                if keep:
+                    extra.setdefault("wgrad_operands", []).append((aq, as_, bq, bs))
+            else:
+                L.moe_grouped_gemm(a_t, b_t, offsets, 0, n_groups, m, out)
+
+        wgrad(dyT.view(N * d, kmax), hT, g_d, N, N * d, dw2[:N].view(N * d, I))
+        wgrad(dacT.view(N * 2 * I, kmax), xT, g_2i, N, N * 2 * I, dw13[:N].view(N * 2 * I, d))
         if kp_s > 0:
             dyT_s = T_(dy, seg_s, cols_s, kp_s)                     # [d, kp_s]
-            hT_s = T_(buf["h"], seg_s, cols_s, kp_s)
+            hT_s = T_(h, seg_s, cols_s, kp_s)
             dacT_s = T_(dac, seg_s, cols_s, kp_s)
             xT_s = T_(x, seg_s, cols_s, kp_s, 0, st_)
-            L.moe_grouped_gemm(dyT_s, hT_s.unsqueeze(0), g_d[:2], 0, 1, d, dw2[N])
-            L.moe_grouped_gemm(dacT_s, xT_s.unsqueeze(0), g_2i[:2], 0, 1, 2 * I, dw13[N])
+            wgrad(dyT_s, hT_s.unsqueeze(0), g_d[:2], 1, d, dw2[N])
+            wgrad(dacT_s, xT_s.unsqueeze(0), g_2i[:2], 1, 2 * I, dw13[N])
         else:
             dw2[N].zero_()
             dw13[N].zero_()
         dwr = L.moe_router_wgrad(x, st_, offs, du_row, N)
-        return {"dx": dx, "dw_router": dwr, "dw13": dw13, "dw2": dw2, "du": du, "du_row": du_row, "dy": dy,
-                "dac": dac, "dx_routed": dxr, "dx_shared": dxs}
+        res = {"dx": dx, "dw_router": dwr, "dw13": dw13, "dw2": dw2}
+        if keep:
+            res.update(du=du, du_row=du_row, dy=dy, dac=dac, dx_routed=dxr, dx_shared=dxs, **extra)
+        return res

@@ -536,6 +536,29 @@ def pin_backward_bf16_model_close_to_exact():
         assert 0 < e < 0.05, (k, e)
 
 
+def pin_backward_fp8_model_close_to_exact():
+    """The fp8 model of the backward approximates the exact gradients (E4M3 keeps 3 mantissa
+    bits: a few percent of RMS; a dropped term, a wrong operand or a misplaced scale would not)
+    and is not the bf16 model.  Which axis each operand is quantised along is a reading of the
+    pages that this closeness cannot tell apart; the GPU parity tests hold the device to it."""
+    r = _rng(27)
+    T, d, N, I = 40, 256, 4, 128
+    x = torch.from_numpy(r.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    wr = r.standard_normal((N, d)) * 0.05
+    b = np.zeros(N, np.float32)
+    w13 = r.standard_normal((N + 1, 2 * I, d)) * 0.05
+    w2 = r.standard_normal((N + 1, d, I)) * 0.05
+    d_out = torch.from_numpy(r.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    ex = O.backward(x, wr, b, w13, w2, 2, d_out)
+    f8 = O.backward(x, wr, b, w13, w2, 2, d_out, precision="fp8")
+    bf = O.backward(x, wr, b, w13, w2, 2, d_out, precision="bf16")
+    for k in ("dx", "dw_router", "dw13", "dw2"):
+        rms = np.sqrt(np.mean(ex[k] ** 2))
+        e8 = np.sqrt(np.mean((f8[k] - ex[k]) ** 2)) / rms
+        assert 0.001 < e8 < 0.12, (k, e8)
+        assert not np.array_equal(f8[k], bf[k])
+
+
 def pin_layer_flops():
     # DeepSeek-V3 shape: 9 of 257 experts per token; 2*7168*256 + 6*7168*2048*9 per token
     assert O.layer_flops(1, 7168, 256, 8, 2048) == 796_393_472
