@@ -535,7 +535,7 @@ def forward(x, w_router, bias, w13, w2, top_k, n_group=1, topk_group=1, precisio
 
 
 def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, topk_group: int = 1,
-             precision: str = "exact"):
+             precision: str = "exact", workers: int = 1):
     """Gradients of L = sum(d_out * out) for the layer ``forward`` computes (float64).
 
     For every expert e and the rows routed to it (every token for the shared expert N):
@@ -557,6 +557,8 @@ def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, to
     the tokens as the reduction axis, zero-padded to a multiple of 128 from the expert's first
     row, dy^T and [da | dc]^T quantised 1x128 along the tokens, h^T (the stored E4M3 h as bf16)
     and x^T (the bf16 input) in 128x128 blocks; sums exact (float64).
+    workers > 1 evaluates the experts concurrently (same arithmetic; their contributions are
+    added in expert order).
     Returns dx [T, d], dw_router [N, d], dw13 [N+1, 2I, d], dw2 [N+1, d, I] and the
     intermediates dgate [T, K], du [T, K] and the routing dict."""
     assert precision in ("exact", "bf16", "fp8")
@@ -582,13 +584,14 @@ def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, to
     def pad128(m):     # zero columns up to a multiple of 128
         return np.pad(m, ((0, 0), (0, (-m.shape[1]) % 128)))
 
-    for e in range(N + 1):
+    def one(e):
+        """Expert e's contributions: (tok, slot, dgate values, dW2, dW13, dx rows) or None."""
         if e < N:
             tok, slot = np.nonzero(idx == e)   # each token picks distinct experts: tok is unique
         else:
-            tok = np.arange(T)
+            tok, slot = np.arange(T), None
         if len(tok) == 0:
-            continue
+            return None
         we13 = np.asarray(w13[e], dtype=np.float64)
         we2 = np.asarray(w2[e], dtype=np.float64)
         if fp8:
@@ -600,10 +603,11 @@ def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, to
         sg = sigmoid(a)
         h = a * sg * c
         h = q_rows(fp32_round(h)) if fp8 else rnd(h)
+        dg = None
         if e < N:
             dy = gate[tok, slot][:, None] * d_out[tok]
             dy = rnd(fp32_round(dy)) if precision != "exact" else dy
-            dgate[tok, slot] = np.sum(d_out[tok] * rnd(h @ we2.T), axis=1)
+            dg = np.sum(d_out[tok] * rnd(h @ we2.T), axis=1)
         else:
             dy = d_out
         dh = (q_rows(dy) if fp8 else dy) @ we2
@@ -612,15 +616,27 @@ def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, to
         dac = np.concatenate([da, dc], axis=1)
         if fp8:
             dxe = q_rows(dac) @ we13
-            n = len(tok)
-            dw2[e] = q_rows(pad128(dy.T)) @ dequant_128x128(*quant_128x128(pad128(bf16_round(h).T))).T
-            dw13[e] = q_rows(pad128(dac.T)) @ dequant_128x128(*quant_128x128(pad128(x[tok].T))).T
-            assert dw2[e].shape == (d, I) and n > 0
+            dw2_e = q_rows(pad128(dy.T)) @ dequant_128x128(*quant_128x128(pad128(bf16_round(h).T))).T
+            dw13_e = q_rows(pad128(dac.T)) @ dequant_128x128(*quant_128x128(pad128(x[tok].T))).T
         else:
-            dw2[e] = dy.T @ h
-            dw13[e] = dac.T @ xe
+            dw2_e = dy.T @ h
+            dw13_e = dac.T @ xe
             dxe = dac @ we13
-        dx[tok] += rnd(dxe) if e < N else dxe
+        return tok, slot, dg, dw2_e, dw13_e, rnd(dxe) if e < N else dxe
+
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            results = list(ex.map(one, range(N + 1)))
+    else:
+        results = [one(e) for e in range(N + 1)]
+    for e, res in enumerate(results):
+        if res is None:
+            continue
+        tok, slot, dg, dw2[e], dw13[e], dxe = res
+        if dg is not None:
+            dgate[tok, slot] = dg
+        dx[tok] += dxe
     ssel = np.take_along_axis(s, idx, axis=1)
     S = ssel.sum(axis=1, keepdims=True)
     ds = (dgate - np.sum(gate * dgate, axis=1, keepdims=True)) / S

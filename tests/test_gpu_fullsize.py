@@ -211,11 +211,85 @@ def test_v3_bf16_T4096_backward(v3):
     say(f"[fullsize] oracle backward (bf16 model) on {len(pick)} sampled tokens ...")
     t0 = time.time()
     model = O.backward(x64[pick], wr64, bias.numpy(), _LazyExperts(cfg, 0), _LazyExperts(cfg, 1), cfg.top_k,
-                       np64(d_out)[pick], precision="bf16")
+                       np64(d_out)[pick], precision="bf16", workers=16)
     assert np.array_equal(model["route"]["idx"], idx[pick])
     ee = rel_err(dx[pick], model["dx"])
     say(f"[fullsize] backward dx: staged {es:.2e}, vs the bf16 model {ee:.2e} (tol 1e-2) [{time.time() - t0:.0f}s]")
     assert es <= 1e-4 and ee <= 1e-2
+
+
+def test_v3_fp8_T16384_backward(v3):
+    """The FP8 backward at T = 16384.  Staged on sampled rows and experts: the 1x128
+    quantisations bit-exact, [da | dc] and the Wgrad GEMMs within the measured E4M3 dot-product
+    bound of float64 on the device's own operands; end to end: sampled tokens' dx against the
+    oracle's fp8 model at 3e-2 of its rms."""
+    from tests.gpu_common import FP8_DOT_REL
+    cfg = I.V3_FP8
+    x_cpu = I.gen_x(cfg)
+    bias = I.gen_bias(cfg)
+    layer = fp8_layer(v3, bias, cfg)
+    out, buf = layer.forward(x_cpu.to(DEV), out_dtype=torch.float32, keep=True)
+    d_out = I.gen_normal(cfg.seed + 900, (cfg.T, cfg.d), 1.0)
+    t0 = time.time()
+    g = layer.backward(d_out.to(DEV), buf, keep=True)
+    torch.cuda.synchronize()
+    say(f"[fullsize] fp8 backward done in {time.time() - t0:.2f}s (first call: includes the weight transposes)")
+    offs = buf["expert_offsets"].cpu().numpy()
+    st_ = buf["sorted_token"].cpu().numpy()
+    pp = buf["pair_pos"].cpu().numpy()
+    idx = buf["topk_idx"].cpu().numpy()
+    N, K, I_ = cfg.n_experts, cfg.top_k, cfg.inter
+    lens = offs[1:] - offs[:-1]
+    experts = [int(np.argmax(lens[:N])), int(np.argmin(lens[:N])), 77]
+    dy_rows = np.concatenate([np.arange(offs[e], offs[e + 1]) for e in experts])
+    dy = g["dy"][torch.as_tensor(dy_rows, device=DEV)].float().cpu().numpy()
+    dyq, dys = O.quant_1x128(dy)
+    assert np.array_equal(g["dyq"][torch.as_tensor(dy_rows, device=DEV)].cpu().numpy(), dyq)
+    assert np.array_equal(g["dys"][torch.as_tensor(dy_rows, device=DEV)].cpu().numpy(), dys)
+    aq, as_, bq, bs = g["wgrad_operands"][0]   # routed dW2: A [N*d, kmax], B [N, I, kmax]
+    kmax = aq.shape[1]
+    at = 0
+    for e in experts:
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        n = hi - lo
+        xq = buf["xq"][torch.as_tensor(st_[lo:hi], device=DEV)].cpu().numpy()
+        xs = buf["xs"][torch.as_tensor(st_[lo:hi], device=DEV)].cpu().numpy()
+        xe = O.dequant_1x128(xq, xs)
+        w13 = O.dequant_128x128(layer.W13[e].cpu().numpy(), layer.W13_s[e].cpu().numpy())
+        w2 = O.dequant_128x128(layer.W2[e].cpu().numpy(), layer.W2_s[e].cpu().numpy())
+        dyd = O.dequant_1x128(dyq[at:at + n], dys[at:at + n])
+        a, c = xe @ w13[:I_].T, xe @ w13[I_:].T
+        ea = FP8_DOT_REL * (np.abs(xe) @ np.abs(w13[:I_]).T)
+        ec = FP8_DOT_REL * (np.abs(xe) @ np.abs(w13[I_:]).T)
+        dh = dyd @ w2
+        edh = FP8_DOT_REL * (np.abs(dyd) @ np.abs(w2))
+        sg = O.sigmoid(a)
+        want = np.concatenate([dh * c * sg * (1 + a * (1 - sg)), dh * a * sg], axis=1)
+        tol = 2 * np.concatenate([1.1 * np.abs(c) * edh + 1.1 * np.abs(dh) * ec + 0.6 * np.abs(dh * c) * ea,
+                                  np.abs(a * sg) * edh + 1.1 * np.abs(dh) * ea], axis=1)
+        got = np64(g["dac"][lo:hi])
+        half = np.exp2(np.floor(np.log2(np.maximum(np.abs(want) + tol, 1e-30))) - 8)
+        worst_dac = float(np.max(np.abs(got - want) / (half * 1.001 + tol + 1e-4 * np.sqrt(np.mean(want ** 2)))))
+        A = O.dequant_1x128(aq[e * cfg.d:(e + 1) * cfg.d].cpu().numpy(), as_[e * cfg.d:(e + 1) * cfg.d].cpu().numpy())
+        B = O.dequant_128x128(bq[e].cpu().numpy(), bs[e].cpu().numpy())
+        w_got = g["dw2"][e].cpu().numpy().astype(np.float64)
+        worst_w = float(np.max(np.abs(w_got - A @ B.T) / (FP8_DOT_REL * (np.abs(A) @ np.abs(B).T) + 1e-30)))
+        # the A operand is this expert's dy rows transposed, 1x128 along the tokens
+        want_q, _ = O.quant_1x128(np.pad(dy[at:at + n].T, ((0, 0), (0, kmax - n))))
+        assert np.array_equal(aq[e * cfg.d:(e + 1) * cfg.d].cpu().numpy(), want_q)
+        say(f"[fullsize] fp8 expert {e} ({n} rows): dac {worst_dac:.3f} of its bound, dW2 {worst_w:.3f} of the dot bound")
+        assert worst_dac <= 1.0 and worst_w <= 1.0
+        at += n
+    pick = np.linspace(0, cfg.T - 1, 10).astype(int)
+    say(f"[fullsize] oracle fp8 backward on {len(pick)} sampled tokens ...")
+    t0 = time.time()
+    model = O.backward(np64(x_cpu)[pick], np64(v3.wr_cpu), bias.numpy(), _LazyExperts(cfg, 0), _LazyExperts(cfg, 1),
+                       K, np64(d_out)[pick], precision="fp8", workers=16)
+    assert np.array_equal(model["route"]["idx"], idx[pick])
+    dx = g["dx"].cpu().numpy().astype(np.float64)[pick]
+    e = np.sqrt(np.mean((dx - model["dx"]) ** 2)) / np.sqrt(np.mean(model["dx"] ** 2))
+    say(f"[fullsize] fp8 backward dx vs the oracle's fp8 model: rms {e:.2e} (tol 3e-2) [{time.time() - t0:.0f}s]")
+    assert e <= 3e-2
 
 
 def test_v3_decode_bias_loop(v3):
