@@ -166,7 +166,7 @@ def test_v3_bf16_T4096_backward(v3):
     out, buf = layer.forward(x_cpu.to(DEV), out_dtype=torch.float32, keep=True)
     d_out = I.gen_normal(cfg.seed + 900, (cfg.T, cfg.d), 1.0)
     t0 = time.time()
-    g = layer.backward(d_out.to(DEV), buf)
+    g = layer.backward(d_out.to(DEV), buf, keep=True)
     torch.cuda.synchronize()
     say(f"[fullsize] backward done in {time.time() - t0:.2f}s (first call: includes the weight transposes)")
     offs = buf["expert_offsets"].cpu().numpy()
