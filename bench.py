@@ -431,6 +431,8 @@ def main():
                     "ms_per_step_median": round(float(np.median(times)), 4),
                     "gbs_median": round(float(np.median(gbs)), 1),
                     "hbm_frac_median": round(float(np.median(gbs)) / HBM_PEAK_GBS, 4),
+                    "gbs_median_first10": round(float(np.median(gbs[:10])), 1),
+                    "gbs_median_last10": round(float(np.median(gbs[-10:])), 1),
                     "max_over_mean_load_first": round(loads[0], 3), "max_over_mean_load_last": round(loads[-1], 3),
                     "max_over_mean_load_series_every10": [round(v, 3) for v in loads[::10]]})
         log(f"[bench] {c4.name}: median {np.median(times):.3f} ms, {np.median(gbs):.0f} GB/s, load {loads[0]:.2f}->{loads[-1]:.2f}")
