@@ -292,7 +292,8 @@ moe_status moe_bias_update(float* bias, const int32_t* expert_counts, int n_expe
  * between them.
  * ==================================================================================== */
 
-/* moe_combine_backward -- the combine's and router's gradients for every token t.
+/* moe_combine_backward -- the combine's and router's gradients for every token t.  A pair the
+ * permutation skipped (pair_pos < 0) contributes nothing: its du is 0 and no dy row is written.
  *   d_out     device bf16 [T, d]: gradient of the layer output
  *   y_routed  device bf16 [T*top_k, d]: the forward's routed expert outputs (sorted rows)
  *   topk_idx, topk_gate, pair_pos: the forward's routing and permutation ([T, top_k])

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
     unpack_bf16x8(ov, f);
 #pragma unroll
     for (int k = 0; k < kMaxBwdK; ++k) {
-      if (k < K) {
+      if (k < K && s_p[k] >= 0) {  // pairs skipped by the permutation (p < 0) carry nothing
         const int64_t p = s_p[k];
         float yv[8];
         unpack_bf16x8(*(const u32x4*)(y + p * d + c * 8), yv);
@@ -82,9 +82,11 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
   if (wave == 0) {
     // lane k < K: gate gradient, selected affinity; then the two sums over the K lanes
     float dg = 0.f, s = 0.f, g = 0.f;
-    if (lane < K) {
+    const int e = lane < K ? idx[(int64_t)t * K + lane] : -1;
+    const bool valid = lane < K && s_p[lane] >= 0 && e >= 0 && e < N;
+    if (valid) {
       dg = ((s_part[lane][0] + s_part[lane][1]) + s_part[lane][2]) + s_part[lane][3];
-      s = scores[(int64_t)t * N + idx[(int64_t)t * K + lane]];
+      s = scores[(int64_t)t * N + e];
       g = s_g[lane];
     }
     float S = s, gd = g * dg;
@@ -94,9 +96,9 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
       gd += __shfl_xor(gd, o, kWave);
     }
     if (lane < K) {
-      const float u = (dg - gd) / S * (s * (1.0f - s));
+      const float u = valid ? (dg - gd) / S * (s * (1.0f - s)) : 0.f;
       du[(int64_t)t * K + lane] = u;
-      du_row[s_p[lane]] = u;
+      if (valid) du_row[s_p[lane]] = u;
     }
   }
 }
@@ -137,7 +139,7 @@ __device__ __forceinline__ int transpose_source(int j, const int32_t* __restrict
   }
   *g_out = lo;
   const int local = j - col[lo];
-  if (local >= seg[lo + 1] - seg[lo]) return -1;
+  if (local < 0 || local >= seg[lo + 1] - seg[lo]) return -1;
   const int r = seg[lo] + local;
   return gather ? gather[r] : r;
 }

@@ -59,6 +59,37 @@ def test_segment_transpose_blocked():
     assert np.array_equal(out.float().cpu().numpy(), want)
 
 
+def test_combine_backward_skipped_pair():
+    """A pair the permutation skips (expert id out of range) contributes nothing: du = 0 there,
+    the token's other gates are normalised over its valid affinities, no dy row is written."""
+    T, K, N, d = 6, 3, 8, 64
+    idx = torch.tensor([[1, 4, 6], [0, -1, 3], [2, 5, 7], [7, 9, 0], [3, 1, 2], [6, 5, 4]], dtype=torch.int32)
+    offs, st_, pp = M()._lib.moe_permute(idx.to(DEV), N, 1)
+    ppn = pp.cpu().numpy()
+    assert ppn[1, 1] < 0 and ppn[3, 1] < 0
+    rows = int(offs[-1].item())
+    y = I.gen_normal(91, (T * K, d), 1.0)
+    d_out = I.gen_normal(92, (T, d), 1.0)
+    scores = torch.rand((T, N), generator=torch.Generator().manual_seed(3)) * 0.8 + 0.1
+    gate = torch.rand((T, K), generator=torch.Generator().manual_seed(4))
+    dy = torch.full((T * (K + 1), d), 7.0, dtype=torch.bfloat16, device=DEV)
+    dy_, du, du_row = M()._lib.moe_combine_backward(d_out.to(DEV), y.to(DEV), idx.to(DEV), gate.to(DEV),
+                                                    scores.to(DEV), pp, out={"dy": dy})
+    du = du.cpu().numpy().astype(np.float64)
+    yn, dn, sn, gn, ix = np64(y), np64(d_out), scores.double().numpy(), gate.double().numpy(), idx.numpy()
+    for t_ in range(T):
+        ok = ppn[t_] >= 0
+        dg = np.array([np.dot(dn[t_], yn[ppn[t_, k]]) if ok[k] else 0.0 for k in range(K)])
+        s = np.array([sn[t_, ix[t_, k]] if ok[k] else 0.0 for k in range(K)])
+        g = np.where(ok, gn[t_], 0.0)
+        want = np.where(ok, (dg - np.sum(g * dg)) / s.sum() * s * (1 - s), 0.0)
+        assert np.allclose(du[t_], want, rtol=1e-4, atol=1e-6), (t_, du[t_], want)
+    assert du[1, 1] == 0 and du[3, 1] == 0
+    written = set(ppn[ppn >= 0].tolist()) | set(range(T * K, T * (K + 1)))
+    untouched = [r for r in range(T * (K + 1)) if r not in written]
+    assert torch.all(dy_[untouched] == 7.0)
+
+
 def test_swiglu_backward():
     rows, inter = 77, 256
     ac = I.gen_normal(72, (rows, 2 * inter), 2.0, dtype=torch.float32)
