@@ -124,15 +124,24 @@ __device__ __forceinline__ int load_offset(const int32_t* offs, int g) {
 }
 
 // Decode logical tile L (order: group, column block, row block) from the LDS prefix table.
+// Every caller walks its tiles in increasing L, so the search for the group (the largest g with
+// tstart[g] <= L; then tstart[g + 1] > L, never an empty group) starts at the group of the
+// caller's previous tile (cur, updated): a few steps forward, else a binary search over the rest.
 template <int BM>
-__device__ __forceinline__ TileInfo decode_tile(int L, const int* tstart, int G, const int32_t* offs) {
-  int lo = 0, hi = G;  // largest g with tstart[g] <= L (then tstart[g+1] > L: never empty)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tstart[mid] <= L) lo = mid;
-    else hi = mid;
+__device__ __forceinline__ TileInfo decode_tile(int L, const int* tstart, int G, const int32_t* offs, int& cur) {
+  int g = cur;
+  for (int n = 0; n < 3 && g + 1 < G && __builtin_amdgcn_readfirstlane(tstart[g + 1]) <= L; ++n) ++g;
+  if (g + 1 < G && __builtin_amdgcn_readfirstlane(tstart[g + 1]) <= L) {
+    int lo = g, hi = G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tstart[mid] <= L) lo = mid;
+      else hi = mid;
+    }
+    g = lo;
   }
-  const int g = lo;
+  g = __builtin_amdgcn_readfirstlane(g);
+  cur = g;
   const int local = L - tstart[g];
   const int m0 = load_offset(offs, g), m1 = load_offset(offs, g + 1);
   const int mt_g = (m1 - m0 + BM - 1) / BM;
@@ -313,7 +322,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   int lq = -1;  // index (in this workgroup's list) of the tile being loaded
   const uint8_t* wbase = p.w;
 
-  auto tile_of = [&](int q) { return decode_tile<BM>(t_begin + slot + q * per_xcd, s_tstart, G, p.offs); };
+  // tile q of this workgroup; the three walks over the tiles (weight rows of the batch being
+  // loaded, gather rows one tile ahead, the tile being computed) keep their own search cursors
+  int cur_b = 0, cur_r = 0, cur_c = 0;
+  auto tile_of = [&](int q, int& cur) { return decode_tile<BM>(t_begin + slot + q * per_xcd, s_tstart, G, p.offs, cur); };
   // gather sources of a tile's rows (global loads whose values are used one tile later)
   auto fetch_rows = [&](const TileInfo& t, int* dst, int* sdst) {
 #pragma unroll
@@ -373,9 +385,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     js = min(js, total_steps - 1);
     const int q = js / ksteps, kt = js - q * ksteps;
     if (q != lq) {  // entering a new tile: its rows were fetched one tile earlier
-      set_b(tile_of(q));
+      set_b(tile_of(q, cur_b));
       if (q > 0) set_rows(a_nxt, s_nxt);
-      if (q + 1 < n_my) fetch_rows(tile_of(q + 1), a_nxt, s_nxt);
+      if (q + 1 < n_my) fetch_rows(tile_of(q + 1, cur_r), a_nxt, s_nxt);
       lq = q;
     }
     dma_kt = kt;
@@ -448,7 +460,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   {
     int src0[A_PW];
     int ssrc0[SC_PW > 0 ? SC_PW : 1];
-    fetch_rows(tile_of(0), src0, ssrc0);
+    fetch_rows(tile_of(0, cur_r), src0, ssrc0);
     set_rows(src0, ssrc0);
   }
   issue(std::integral_constant<int, 0>(), 0);
@@ -461,7 +473,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-  TileInfo ct = tile_of(0);
+  TileInfo ct = tile_of(0, cur_c);
   // operand reads: row & 7 = lr & 7 for every row a lane reads (tile offsets are multiples of
   // 16), so its two swizzled 16-byte chunks (lg and lg + 4) sit at fixed byte offsets lo / hi
   // from the row start and every read is one base register plus a constant
@@ -764,7 +776,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
         }
         epi_store(v, ct);
         if (OUT == OUT_FP8) MOE_BARRIER();  // s_red is rewritten by the next tile
-        if (j + 1 < total_steps) ct = tile_of((j + 1) / ksteps);
+        if (j + 1 < total_steps) ct = tile_of((j + 1) / ksteps, cur_c);
       }
     };
 
