@@ -108,3 +108,59 @@ def test_workspace_queries():
     assert lib.moe_route_workspace_size(4096, 256) > 0
     assert lib.moe_route_workspace_size(-1, 256) == 0
     assert lib.moe_permute_workspace_size(16384, 256) == 2 * 64 * 256 * 4
+
+
+def _rejects(lib, fn, args, code):
+    st = getattr(lib, fn)(*args)
+    assert st == code, (fn, args, st, lib.moe_last_error())
+    assert lib.moe_last_error().decode().startswith(fn)
+
+
+def test_backward_entry_points_reject():
+    L = _lib()
+    lib = L.lib()
+    P = ctypes.c_void_p
+    p = [P(16)] * 6
+    # moe_combine_backward(d_out, y, idx, gate, scores, pair_pos, T, K, d, N, dy, du, du_row, stream)
+    cb = lambda T=4, K=2, d=16, N=8, ptrs=None, dy=P(16): (*(ptrs or p), T, K, d, N, dy, P(16), P(16), None)
+    _rejects(lib, "moe_combine_backward", cb(ptrs=[None] + p[1:]), 1)
+    _rejects(lib, "moe_combine_backward", cb(T=-1), 2)
+    _rejects(lib, "moe_combine_backward", cb(K=0), 2)
+    _rejects(lib, "moe_combine_backward", cb(K=33, N=64), 2)
+    _rejects(lib, "moe_combine_backward", cb(K=9, N=8), 2)
+    _rejects(lib, "moe_combine_backward", cb(d=12), 2)
+    _rejects(lib, "moe_combine_backward", cb(dy=P(8)), 4)
+    # moe_swiglu_backward(ac, dh, rows, inter, dac, stream)
+    _rejects(lib, "moe_swiglu_backward", (None, P(16), 4, 8, P(16), None), 1)
+    _rejects(lib, "moe_swiglu_backward", (P(16), P(16), -1, 8, P(16), None), 2)
+    _rejects(lib, "moe_swiglu_backward", (P(16), P(16), 4, 6, P(16), None), 2)
+    _rejects(lib, "moe_swiglu_backward", (P(16), P(16), 4, 8, P(4), None), 4)
+    # moe_segment_transpose(src, ld_src, src_rows, seg_offsets, dst_cols, n_seg, cols, total_cols, dst, ld_dst,
+    #                       seg_stride, stream)
+    st = lambda src=P(16), ld_src=64, n=2, cols=64, total=128, dst=P(16), ld_dst=128, ss=0: (
+        src, ld_src, None, P(16), P(16), n, cols, total, dst, ld_dst, ss, None)
+    _rejects(lib, "moe_segment_transpose", st(src=None), 1)
+    _rejects(lib, "moe_segment_transpose", st(n=0), 2)
+    _rejects(lib, "moe_segment_transpose", st(cols=60), 2)
+    _rejects(lib, "moe_segment_transpose", st(total=100), 2)
+    _rejects(lib, "moe_segment_transpose", st(ss=4), 4)
+    _rejects(lib, "moe_segment_transpose", st(ld_src=32), 4)
+    _rejects(lib, "moe_segment_transpose", st(ld_dst=64), 4)
+    _rejects(lib, "moe_segment_transpose", st(dst=P(8)), 4)
+    # moe_router_wgrad(x, sorted_token, expert_offsets, du_row, n_experts, d, dw_router, stream)
+    _rejects(lib, "moe_router_wgrad", (P(16), P(16), None, P(16), 8, 16, P(16), None), 1)
+    _rejects(lib, "moe_router_wgrad", (P(16), P(16), P(16), P(16), 0, 16, P(16), None), 2)
+    _rejects(lib, "moe_router_wgrad", (P(16), P(16), P(16), P(16), 8, 12, P(16), None), 2)
+    _rejects(lib, "moe_router_wgrad", (P(8), P(16), P(16), P(16), 8, 16, P(16), None), 4)
+    # fp8_dequant_1x128(q, scale, rows, cols, out, stream)
+    _rejects(lib, "fp8_dequant_1x128", (None, P(16), 4, 128, P(16), None), 1)
+    _rejects(lib, "fp8_dequant_1x128", (P(16), P(16), 4, 100, P(16), None), 2)
+    _rejects(lib, "fp8_dequant_1x128", (P(16), P(16), -1, 128, P(16), None), 2)
+    _rejects(lib, "fp8_dequant_1x128", (P(4), P(16), 4, 128, P(16), None), 4)
+
+
+@pytest.mark.parametrize("kw,code", [(dict(ldw=100), 4), (dict(ldw=260), 4)])
+def test_gemm_rejects_weight_stride(kw, code):
+    L = _lib()
+    assert _gemm(L, **kw) == code, L.lib().moe_last_error()
+    assert L.lib().moe_last_error().decode().startswith("moe_grouped_gemm")
