@@ -415,15 +415,20 @@ def main():
             l4.forward(xs4[i])
         l4.bias.copy_(bias4.to(dev))
         torch.cuda.synchronize()
-        loads, gbs, times = [], [], []
+        # the steps run back to back as in a decode loop (no host synchronisation between them):
+        # each is bracketed by its own events and its expert loads are copied into a device-side
+        # history, read once the loop has finished
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n4)]
+        hist = torch.empty((n4, c4.n_experts), dtype=torch.int32, device=dev)
         for i in range(n4):
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
+            ev[i][0].record()
             _, buf = l4.forward(xs4[i], update_bias=True, gamma=c4.gamma, keep=True)
-            e.record()
-            torch.cuda.synchronize()
-            t = s.elapsed_time(e)
-            cnt = buf["expert_counts"].cpu().numpy()
+            ev[i][1].record()
+            hist[i].copy_(buf["expert_counts"])
+        torch.cuda.synchronize()
+        loads, gbs, times = [], [], []
+        for i, cnt in enumerate(hist.cpu().numpy()):
+            t = ev[i][0].elapsed_time(ev[i][1])
             loads.append(float(cnt.max() / cnt.mean()))
             gbs.append(step_bytes(c4, cnt, True) / (t / 1e3) / 1e9)
             times.append(t)
