@@ -57,6 +57,11 @@ class MoELayer:
         idx, gate, counts, scores = L.moe_route(x, self.w_router, self.bias, K, self.n_group, self.topk_group,
                                                 want_scores=keep)
         offs, sorted_token, pair_pos = L.moe_permute(idx, N, 1)
+        if keep:  # the backward sizes its weight-gradient operands from these: copied to the host now
+            offs_host = torch.empty(offs.shape, dtype=offs.dtype, pin_memory=True)
+            offs_host.copy_(offs, non_blocking=True)
+            offs_ready = torch.cuda.Event()
+            offs_ready.record()
         rows = T * (K + 1)
         if self.fp8:
             xq, xs = (L.fp8_quant_1x128_e8m0 if self.e8m0 else L.fp8_quant_1x128)(x)
@@ -79,7 +84,8 @@ class MoELayer:
             L.moe_bias_update(self.bias, counts, T * K, gamma)
         if keep:
             return out, {"x": x, "scores": scores, "topk_idx": idx, "topk_gate": gate, "expert_counts": counts,
-                         "expert_offsets": offs, "sorted_token": sorted_token, "pair_pos": pair_pos,
+                         "expert_offsets": offs, "expert_offsets_host": (offs_host, offs_ready),
+                         "sorted_token": sorted_token, "pair_pos": pair_pos,
                          "xq": xq, "xs": xs, "h": h, "hs": hs, "y": y, "y_shared": ysh}
         return out
 
@@ -134,9 +140,12 @@ class MoELayer:
         rows = T * (K + 1)
         dev = x.device
         offs, st_, pp = buf["expert_offsets"], buf["sorted_token"], buf["pair_pos"]
-        # the expert sizes size the weight-gradient operands: read once, before any launch, so
-        # the rest of the pass is queued without waiting
-        lens = (offs[1:] - offs[:-1]).cpu()
+        # the expert sizes size the weight-gradient operands: the forward copied the offsets to
+        # pinned host memory right after the permutation, so this waits at most for that copy
+        # and the whole pass is then queued without waiting
+        offs_host, offs_ready = buf["expert_offsets_host"]
+        offs_ready.synchronize()
+        lens = offs_host[1:] - offs_host[:-1]
         d_out = d_out.to(torch.bfloat16).contiguous()
         dy, du, du_row = L.moe_combine_backward(d_out, buf["y"], buf["topk_idx"], buf["topk_gate"], buf["scores"], pp)
         extra = {}
