@@ -365,12 +365,13 @@ def test_gemm_fp8_exact(sizes, K):
 # FP8_DOT_REL: the fp8 dot-product error bound (see tests/gpu_common.py).
 
 
-def test_gemm_fp8_two_slot_ring_matches_three():
-    """An E4M3 SwiGLU launch with an E4M3 output whose tile table outgrows the three-slot
-    ring's spare LDS (460 groups) takes the two-slot ring; the same groups split over two
-    launches take the three-slot ring.  The tile arithmetic does not depend on the ring, so
-    codes and scales agree bit for bit."""
-    G, K, N = 460, 256, 256
+@pytest.mark.parametrize("swiglu,G", [(True, 460), (False, 1000)], ids=["swiglu_fp8_out", "f32_out"])
+def test_gemm_fp8_two_slot_ring_matches_three(swiglu, G):
+    """An E4M3 launch whose tile table outgrows the three-slot ring's spare LDS takes the
+    two-slot ring (SwiGLU with an E4M3 output: above 463 groups; f32 output: above 975); the
+    same groups split over two launches take the three-slot ring.  The tile arithmetic does
+    not depend on the ring, so the outputs (codes and scales) agree bit for bit."""
+    K, N = 256, 256
     sizes = np.random.default_rng(17).integers(60, 81, G)
     sizes[5] = 0
     offs = _offsets(sizes)
@@ -380,18 +381,23 @@ def test_gemm_fp8_two_slot_ring_matches_three():
     Aq, As = M().fp8_quant_1x128(A.to(DEV))
     Wq, Ws = M().fp8_quant_128x128(W.to(DEV))
     o = torch.from_numpy(offs).to(DEV)
-    one = torch.empty((rows, N // 2), dtype=torch.uint8, device=DEV)
-    one_s = torch.empty((rows, 1), dtype=torch.float32, device=DEV)
-    M().moe_grouped_gemm(Aq, Wq, o, 0, G, rows, one, a_scale=As, w_scale=Ws, swiglu=True, out_scale=one_s)
+    if swiglu:
+        one = torch.empty((rows, N // 2), dtype=torch.uint8, device=DEV)
+        one_s = torch.empty((rows, 1), dtype=torch.float32, device=DEV)
+    else:
+        one = torch.empty((rows, N), dtype=torch.float32, device=DEV)
+        one_s = torch.empty((rows, 1), dtype=torch.float32, device=DEV)
+    kw = lambda s: dict(a_scale=As, w_scale=Ws, swiglu=True, out_scale=s) if swiglu else dict(a_scale=As, w_scale=Ws)
+    M().moe_grouped_gemm(Aq, Wq, o, 0, G, rows, one, **kw(one_s))
     two = torch.empty_like(one)
     two_s = torch.empty_like(one_s)
     h = G // 2
     split = int(offs[h])
-    M().moe_grouped_gemm(Aq, Wq, o, 0, h, split, two[:split], a_scale=As, w_scale=Ws, swiglu=True,
-                         out_scale=two_s[:split])
-    M().moe_grouped_gemm(Aq, Wq, o, h, G - h, rows - split, two[split:], a_scale=As, w_scale=Ws,
-                         swiglu=True, out_scale=two_s[split:])
-    assert torch.equal(one, two) and torch.equal(one_s, two_s)
+    M().moe_grouped_gemm(Aq, Wq, o, 0, h, split, two[:split], **kw(two_s[:split]))
+    M().moe_grouped_gemm(Aq, Wq, o, h, G - h, rows - split, two[split:], **kw(two_s[split:]))
+    assert torch.equal(one, two)
+    if swiglu:
+        assert torch.equal(one_s, two_s)
 
 
 @pytest.mark.parametrize("swiglu,out_kind", [(False, "f32"), (True, "bf16"), (True, "fp8")])
