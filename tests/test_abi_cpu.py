@@ -164,3 +164,20 @@ def test_gemm_rejects_weight_stride(kw, code):
     L = _lib()
     assert _gemm(L, **kw) == code, L.lib().moe_last_error()
     assert L.lib().moe_last_error().decode().startswith("moe_grouped_gemm")
+
+
+def test_no_cpu_fallback(monkeypatch):
+    """Without libmoe.so the binding raises instead of computing anything, and CPU tensors are
+    refused before any library call: nothing on the product path runs on the host."""
+    import torch
+
+    from sparse_moe_layer_sigmoid_amd import _lib as L
+    monkeypatch.setattr(L, "_LIB", None)
+    monkeypatch.setattr(L, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libmoe.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        L.lib()
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="GPU tensor"):
+        L.fp8_quant_1x128(x)
+    with pytest.raises(TypeError, match="GPU tensor"):
+        L.moe_combine(x, None, torch.zeros((2, 2), dtype=torch.int32), torch.zeros((2, 2)))
