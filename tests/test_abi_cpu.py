@@ -181,3 +181,15 @@ def test_no_cpu_fallback(monkeypatch):
         L.fp8_quant_1x128(x)
     with pytest.raises(TypeError, match="GPU tensor"):
         L.moe_combine(x, None, torch.zeros((2, 2), dtype=torch.int32), torch.zeros((2, 2)))
+
+
+def test_package_does_not_import_the_oracle():
+    """The library package and its layer never load the CPU oracle (test infrastructure only)."""
+    import subprocess
+    import sys
+    code = ("import sys; import sparse_moe_layer_sigmoid_amd, sparse_moe_layer_sigmoid_amd.layer, "
+            "sparse_moe_layer_sigmoid_amd._lib, sparse_moe_layer_sigmoid_amd.inputs; "
+            "bad = [m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')]; "
+            "assert not bad, bad")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
