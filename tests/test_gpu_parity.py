@@ -632,6 +632,20 @@ def test_layer_all_tokens_on_the_same_experts(fp8):
     if not fp8:
         say(f"  skewed layer (bf16): {err:.2e}")
         assert err <= BF16_TOL
+        # backward: the weight gradients of the experts no token reached are exactly zero
+        d_out = I.gen_normal(cfg.seed + 900, (cfg.T, cfg.d), 1.0)
+        g = layer.backward(d_out.to(DEV), buf)
+        dw13, dw2 = g["dw13"][cfg.top_k:cfg.n_experts].cpu(), g["dw2"][cfg.top_k:cfg.n_experts].cpu()
+        assert bool((dw13 == 0).all()) and bool((dw2 == 0).all())
+        want = O.backward(x64, np64(wr), bias.numpy(), W13n, W2n, cfg.top_k, np64(d_out), precision="bf16")
+        active = np.r_[np.arange(cfg.top_k), cfg.n_experts]  # the zero blocks are checked above
+        for name in ("dx", "dw_router", "dw13", "dw2"):
+            got, ref = np64(g[name]), want[name]
+            if name in ("dw13", "dw2"):
+                got, ref = got[active], ref[active]
+            e = rel_err(got, ref)
+            say(f"  skewed backward {name}: {e:.2e}")
+            assert e <= BF16_TOL, name
         return
     # E4M3: stage by stage as in test_layer_fp8 (at this width one h code a step away from the
     # oracle's moves an output visibly, so the end-to-end figure is reported, not asserted)
