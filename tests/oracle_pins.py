@@ -559,9 +559,219 @@ def pin_backward_fp8_model_close_to_exact():
         assert not np.array_equal(f8[k], bf[k])
 
 
-def pin_layer_flops():
-    # DeepSeek-V3 shape: 9 of 257 experts per token; 2*7168*256 + 6*7168*2048*9 per token
-    assert O.layer_flops(1, 7168, 256, 8, 2048) == 796_393_472
+def pin_route_margins_bruteforce():
+    """The tie margins that decide which tokens the parity tests exclude: ``margin`` is the
+    gap between the K-th and the (K+1)-th largest z among the allowed experts, and
+    ``group_margin`` the gap between the last kept and the best dropped group score.  Checked
+    against a full sort of z (torch.sigmoid affinities) and an enumeration of every pair
+    inside each group, with the group limit on and off, and K = N (no (K+1)-th: +inf)."""
+    for seed in range(3):
+        x, w, b = _tiny_router(40 + seed, T=12, N=12)
+        s = torch.sigmoid(torch.from_numpy(x) @ torch.from_numpy(w).T).numpy()
+        z = s + b.astype(np.float64)
+        for K in (1, 3):
+            r = O.route(x, w, b, K)
+            for t in range(x.shape[0]):
+                zs = np.sort(z[t])[::-1]
+                assert abs(r["margin"][t] - (zs[K - 1] - zs[K])) <= 1e-15
+                assert r["group_margin"][t] == np.inf
+        n_group, topk_group, K = 4, 2, 3
+        gs = 12 // n_group
+        r = O.route(x, w, b, K, n_group, topk_group)
+        for t in range(x.shape[0]):
+            score = sorted((max(z[t, g * gs + i] + z[t, g * gs + j] for i, j in itertools.combinations(range(gs), 2))
+                            for g in range(n_group)), reverse=True)
+            assert abs(r["group_margin"][t] - (score[topk_group - 1] - score[topk_group])) <= 1e-15
+            kept = set(int(e) // gs for e in r["idx"][t])
+            allowed = np.sort(np.concatenate([z[t, g * gs:(g + 1) * gs] for g in range(n_group)
+                                              if g in kept or len(kept) < topk_group]))[::-1]
+            if len(kept) == topk_group:
+                assert abs(r["margin"][t] - (allowed[K - 1] - allowed[K])) <= 1e-15
+    x, w, b = _tiny_router(43, N=6)
+    assert np.all(O.route(x, w, b, 6)["margin"] == np.inf)
+
+
+def pin_e4m3_half_ulp_neighbours():
+    """Half the E4M3 spacing, at every positive code and at the midpoint of every pair of
+    neighbouring codes, equals half the distance between the two neighbours (the format's
+    spacing read off its value table); at 448 it is half the gap down to 416."""
+    pos = O.e4m3_decode(np.arange(0, 127, dtype=np.uint8))
+    gap = np.diff(pos)                                   # 126 gaps between codes 0..126
+    assert np.array_equal(O.e4m3_half_ulp(pos[:126]), gap / 2)
+    assert np.array_equal(O.e4m3_half_ulp(-pos[:126]), gap / 2)
+    assert np.array_equal(O.e4m3_half_ulp((pos[:126] + pos[1:]) / 2), gap / 2)
+    assert O.e4m3_half_ulp(448.0) == (448.0 - 416.0) / 2
+    assert O.e4m3_half_ulp(2.0 ** -6) == 2.0 ** -10 and O.e4m3_half_ulp(2.0 ** -7) == 2.0 ** -10
+
+
+def pin_forward_bf16_storage_handbuilt():
+    """The bf16 storage model of the forward on a hand-built expert whose values are exact
+    in float64, so every rounding it applies is visible in the result.
+
+    x = [1, 0]; W1 rows give a = [40, 48], for which silu(a) = a exactly in float64
+    (exp(-40) < 2^-54); W3 rows give c = [1 + 2^-6 + 2^-9, -(1/2 + 2^-9)], so
+    h = [40.703125, -24.09375] (binary 101000.101101 and -11000.00011), whose bf16 values are
+    40.75 and -24.125.  W2 = [[1, 1], [1/2, 1/4]] gives y = [16.625, 14.34375] from the stored
+    h (16.609375 and 14.328125 from the exact h).  The routed expert's y is stored in bf16
+    (14.34375 = 1110.01011: a tie, to the even 14.375), the shared expert's in float32, and
+    with one routed expert at gate 1 the output is their sum: [33.25, 28.71875]."""
+    x = np.array([[1.0, 0.0]])
+    w13 = np.array([[40.0, 0.0], [48.0, 0.0], [1.017578125, 0.0], [-0.501953125, 0.0]])
+    w2 = np.array([[1.0, 1.0], [0.5, 0.25]])
+    out, ex = O.forward_sparse(x, np.array([[0]]), np.array([[1.0]]), 1, lambda e: (w13, w2), "bf16")
+    assert np.array_equal(ex["y_routed"][0], [16.625, 14.375])
+    assert np.array_equal(ex["y_shared"][0], [16.625, 14.34375])
+    assert np.array_equal(out[0], [33.25, 28.71875])
+    y, h = O.expert_rows(x, w13, w2, "bf16", return_h=True)
+    assert np.array_equal(h[0], [40.75, -24.125]) and np.array_equal(y[0], [16.625, 14.34375])
+    ex_out, _ = O.forward_sparse(x, np.array([[0]]), np.array([[1.0]]), 1, lambda e: (w13, w2), "exact")
+    assert np.array_equal(ex_out[0], [33.21875, 28.65625])
+
+
+def pin_forward_fp8_storage_handbuilt():
+    """The FP8 model of the forward on a hand-built expert (d = I = 128) whose tile scales are
+    exact, so only the E4M3 roundings the pages' scheme applies move the result.
+
+    x = [1.03125, 7, 0, ...]: tile amax 7 -> s = 7/448 = 2^-6; 1.03125 / s = 66 rounds to the
+    E4M3 value 64, so the expert sees x = [1, 7, 0, ...].  W1 column 0 = a = [64, 40, 48, 40]
+    (block amax 112 -> s = 1/4, exact), W3 column 0 = c = [7, 0.4375, 0.4375, 1.75] (block amax
+    7 -> s = 2^-6, exact); silu(a) = a, so h = a c = [448, 17.5, 21, 70, 0, ...].  Its 1x128
+    tile has amax 448 -> s = 1, and E4M3 stores [448, 18, 20, 72]: 17.5 -> 18 (spacing 2),
+    21 -> 20 (a tie, to the even mantissa), 70 -> 72 (spacing 8).  W2 picks y = [h1, h2, h3,
+    h0 + h1/4] = [18, 20, 72, 452.5]; the routed copy is stored in bf16 (452.5 -> 452), the
+    shared one in float32, so out = [36, 40, 144, 904.5]."""
+    d = inter = 128
+    x = np.zeros((1, d))
+    x[0, 0], x[0, 1] = 1.03125, 7.0
+    w13 = np.zeros((2 * inter, d))
+    w2 = np.zeros((d, inter))
+    w13[0, 2], w13[inter, 2] = 112.0, 7.0
+    w13[:4, 0] = [64, 40, 48, 40]
+    w13[inter:inter + 4, 0] = [7, 0.4375, 0.4375, 1.75]
+    w2[127, 127] = 7.0
+    w2[0, 1] = w2[1, 2] = w2[2, 3] = w2[3, 0] = 1.0
+    w2[3, 1] = 0.25
+    out, ex = O.forward_sparse(x, np.array([[0]]), np.array([[1.0]]), 1, lambda e: (w13, w2), "fp8")
+    assert np.array_equal(ex["y_routed"][0, :4], [18, 20, 72, 452])
+    assert np.array_equal(ex["y_shared"][0, :4], [18, 20, 72, 452.5])
+    assert np.array_equal(out[0, :4], [36, 40, 144, 904.5]) and not np.any(out[0, 4:])
+
+
+def pin_backward_bf16_storage_handbuilt():
+    """The bf16 storage model of the backward on a hand-built layer (T = 1, d = I = 2, N = K = 2
+    plus the shared expert, all three experts with the same weights).
+
+    Router: x = [1, 0], router rows [0, 0] and [40, 0] -> s = [1/2, 1] (sigmoid(40) = 1 in
+    float64), so the gates are 2/3 (expert 1) and 1/3 (expert 0).  Experts: a = [40, 48]
+    (silu(a) = a, sigmoid(a) = 1), c = [3/4, 1 + 2^-6 + 2^-9] -> h = [30, 48.84375], stored
+    in bf16 as [30, 48.75].  d_out = [1, 1/2].
+    Expert 0: dy = bf16(fl32(d_out / 3)) = [0.333984375, 0.1669921875] (1/3 = 0.0101010...b
+    rounds up at its 8th bit), so dW2 = dy^T h = [[10.01953125, 16.28173828125],
+    [5.009765625, 8.140869140625]].  W2 = [[1, 1/2], [1/4, 1]] gives dh = dy W2 =
+    [0.375732421875, 0.333984375]; da = bf16(dh c) = [0.28125, 0.33984375] (from
+    0.2817993... and 0.3398551...), dc = bf16(dh a) = [15, 16] (from 15.029296875 and
+    16.03125); dW13 column 0 is [da | dc] (x = [1, 0]).
+    dx: the routed rows' contributions dac W13 are stored in bf16 (expert 0: 55.09375 -> 55,
+    expert 1: 110.1875 -> 110), the shared expert's (165.09375) in float64, and the router
+    term is zero (both experts return the same y, so the gates' gradient cancels):
+    dx = [330.09375, 0]."""
+    x = np.array([[1.0, 0.0]])
+    wr = np.array([[0.0, 0.0], [40.0, 0.0]])
+    w13 = np.zeros((3, 4, 2))
+    w13[:, :, 0] = [40, 48, 0.75, 1.017578125]
+    w2 = np.zeros((3, 2, 2))
+    w2[:] = [[1, 0.5], [0.25, 1]]
+    g = O.backward(x, wr, np.zeros(2, np.float32), w13, w2, 2, np.array([[1.0, 0.5]]), precision="bf16")
+    assert np.array_equal(g["route"]["idx"], [[1, 0]])
+    assert np.array_equal(g["dw2"][0], [[10.01953125, 16.28173828125], [5.009765625, 8.140869140625]])
+    assert np.array_equal(g["dw13"][0][:, 0], [0.28125, 0.33984375, 15.0, 16.0])
+    assert np.array_equal(g["dw13"][2][:, 0], [0.84375, 1.015625, 45.0, 48.0])
+    assert np.array_equal(g["dx"], [[330.09375, 0.0]]) and np.all(g["du"] == 0)
+
+
+def pin_backward_fp8_storage_handbuilt():
+    """The FP8 model of the backward on a hand-built layer: T = 3, d = I = 128, one routed
+    expert (K = 1, gate 1) plus the shared one, both with the same weights.  Every scale of
+    the Dgrad path is exact, so the E4M3 roundings there show as exact binary fractions; the
+    Wgrad tiles use fl32(v / 448) scales, given below as the exact float32 values.
+
+    Inputs: x rows [1, 7], [1.5, 7], [1.03125, 7] (then zeros); their 1x128 tiles have
+    s = 2^-6 and the third rounds 66 -> 64, i.e. to [1, 7].  W1 column 0 = [64, 40], W3
+    column 0 = [7, 15/32] (block scales 1/4 and 2^-6, exact).  h = silu(a) c with a = 64 x0,
+    40 x0 and c = 7 x0, 15/32 x0: token rows [448, 18.75] -> E4M3 [448, 18] (s = 1) and
+    [1008, 42.1875] -> [1008, 40.5] (s = 2.25, 42.1875 / 2.25 = 18.75 -> 18).
+    d_out rows [7, 0.8125], [7, 0.53125], [7, 0.5]; dy = d_out (gate 1, bf16 values).
+    Dgrad: dy is quantised 1x128 (s = 2^-6: 0.53125 -> 0.5, a tie to the even code 32); W2 = 1/4 at (0, 0), 1 at
+    (1, 1) -> dh = [7/4, dy1]; da = bf16(dh c), dc = bf16(dh a): token 0 da = [12.25,
+    0.380859375], dc = [112, 32.5].  [da | dc] is quantised per 1x128 tile: da's s = 7/256
+    (0.380859375 -> 14 * 7/256 = 0.3828125), dc's s = 1/4 (32.5 -> 32); dac W13 gives
+    1598.3125 for token 0, stored in bf16 (1600) for the routed rows, so dx[0, 0] = 3198.3125;
+    dx[:, 2] = bf16(112 da0) + 112 da0.
+    Wgrad (the tokens are the reduction axis; every Wgrad operand here spans one tile):
+    dy^T row 0 = [7, 7, 7] is exact; row 1 = [0.8125, 0.53125, 0.5] has s_dy = fl32(0.8125 /
+    448) and codes [448, 288, 288] (0.53125 / s_dy = 292.9, 0.5 / s_dy = 275.7).  h^T (bf16 of
+    the stored h) is one 128x128 block: rows [448, 1008, 448] and [18, 40.5, 18], amax 1008 ->
+    s = 2.25, 448 -> 432 (199.1 -> 192 of that scale).  x^T is one block with s = 2^-6, its
+    row 0 [1, 1.5, 1.03125] -> [1, 1.5, 1].  [da | dc]^T rows are 1x128 tiles along the
+    tokens: da0 = [12.25, 18.375, 12.25] (s = 21/512: 12.25 -> 11.8125), da1 = [0.380859375,
+    0.3515625, 0.234375] and dc1 = [32.5, 30, 20] (codes [448, 416, 288] of s_da = fl32(
+    0.380859375 / 448) and s_dc = fl32(32.5 / 448)), dc0 = [112, 168, 112] (s = 3/8: 112 -> 108).
+    So dW2[1, 0] = s_dy (448 * 432 + 288 * 1008 + 288 * 432) and dW13[I + 1, 0] =
+    s_dc (448 * 1 + 416 * 1.5 + 288 * 1)."""
+    d = inter = 128
+    x = np.zeros((3, d))
+    x[:, 0] = [1.0, 1.5, 1.03125]
+    x[:, 1] = 7.0
+    w13 = np.zeros((2, 2 * inter, d))
+    w2 = np.zeros((2, d, inter))
+    w13[:, 0, 0], w13[:, 1, 0], w13[:, 0, 2] = 64, 40, 112
+    w13[:, inter, 0], w13[:, inter + 1, 0] = 7, 0.46875
+    w2[:, 0, 0], w2[:, 1, 1], w2[:, 127, 127] = 0.25, 1, 7
+    d_out = np.zeros((3, d))
+    d_out[:, 0] = 7
+    d_out[:, 1] = [0.8125, 0.53125, 0.5]
+    g = O.backward(x, np.zeros((1, d)), np.zeros(1, np.float32), w13, w2, 1, d_out, precision="fp8")
+    s_dy = float.fromhex("0x1.db6db6p-10")     # fl32(0.8125 / 448)
+    s_da = float.fromhex("0x1.bdb6dcp-11")     # fl32(0.380859375 / 448)
+    s_dc = float.fromhex("0x1.292492p-4")      # fl32(32.5 / 448)
+    assert np.float32(0.8125 / 448) == s_dy and np.float32(0.380859375 / 448) == s_da \
+        and np.float32(32.5 / 448) == s_dc
+    assert np.array_equal(g["dx"][:, [0, 2]], [[3198.3125, 2748.0], [4764.828125, 4122.0], [3171.21875, 2748.0]])
+    assert not np.any(g["dx"][:, 1]) and not np.any(g["dx"][:, 3:])
+    assert np.array_equal(g["dw2"][0][:2, :2], [[7 * (432 + 1008 + 432), 7 * (18 + 40.5 + 18)],
+                                                [s_dy * (448 * 432 + 288 * 1008 + 288 * 432),
+                                                 s_dy * (448 * 18 + 288 * 40.5 + 288 * 18)]])
+    assert np.array_equal(g["dw13"][0][[0, 1, inter, inter + 1]][:, :2],
+                          [[11.8125 + 18.375 * 1.5 + 11.8125, 7 * (11.8125 + 18.375 + 11.8125)],
+                           [s_da * (448 + 416 * 1.5 + 288), 7 * s_da * (448 + 416 + 288)],
+                           [108 + 168 * 1.5 + 108, 7 * (108 + 168 + 108)],
+                           [s_dc * (448 + 416 * 1.5 + 288), 7 * s_dc * (448 + 416 + 288)]])
+    # the shared expert has the same weights and sees dy = d_out (bf16 values already)
+    assert np.array_equal(g["dw2"][1], g["dw2"][0]) and np.array_equal(g["dw13"][1], g["dw13"][0])
+
+    # The router's gradient reads the stored h through the gates' gradient: T = 1, two routed
+    # experts (K = 2) with gates 1/3 and 2/3 (router rows [0] and [40] on x0 = 1: s = 1/2 and 1).
+    # Both hold h = [448, 17.5] -> E4M3 [448, 18] (s = 1); expert 0's W2 returns y0 = h1, expert
+    # 1's y0 = h0 / 4 = 112; d_out = [1, 0, ...].  dgate = [18, 112], their gate-weighted sum is
+    # 242/3, and du0 = (18 - 242/3) / (3/2) * s0 (1 - s0) = -94/9 (with h1 = 17.5 it would be
+    # -10.5); du1 = 0 (s1 = 1).  dW_r[0] = du0 x.
+    x = np.zeros((1, d))
+    x[0, 0], x[0, 1] = 1.0, 7.0
+    wr = np.zeros((2, d))
+    wr[1, 0] = 40.0
+    w13 = np.zeros((3, 2 * inter, d))
+    w13[:, 0, 0], w13[:, 1, 0], w13[:, 0, 2] = 64, 40, 112
+    w13[:, inter, 0], w13[:, inter + 1, 0] = 7, 0.4375
+    w2 = np.zeros((3, d, inter))
+    w2[:, 127, 127] = 7
+    w2[0, 0, 1] = 1.0
+    w2[1, 0, 0] = 0.25
+    d_out = np.zeros((1, d))
+    d_out[0, 0] = 1.0
+    g = O.backward(x, wr, np.zeros(2, np.float32), w13, w2, 2, d_out, precision="fp8")
+    assert np.array_equal(g["route"]["idx"], [[1, 0]]) and np.array_equal(g["dgate"], [[112.0, 18.0]])
+    assert abs(g["du"][0, 1] + 94 / 9) < 1e-12 and g["du"][0, 0] == 0
+    assert np.allclose(g["dw_router"][0, :2], [-94 / 9, -7 * 94 / 9], rtol=0, atol=1e-11)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -4,6 +4,9 @@ A pin set that lets a dropped term, a wrong sign, a swapped operand or a wrong r
 rule through would not justify trusting the oracle; each mutation below must make at
 least one pin fail.  The mutations are applied with monkeypatch, on the CPU only.
 """
+import inspect
+import textwrap
+
 import numpy as np
 import pytest
 
@@ -241,6 +244,123 @@ def _mut_bwd_silu_grad(mp):
     mp.setattr(O, "backward", bwd)
 
 
+def _patch_source(mp, func_name, old, new):
+    """Plant a mistake by editing one line of an oracle function's source: the edited
+    function is compiled against a copy of the oracle module's globals and put in place of
+    the original for this test only."""
+    src = textwrap.dedent(inspect.getsource(getattr(O, func_name)))
+    assert src.count(old) == 1, (func_name, old)
+    ns = dict(O.__dict__)
+    exec(compile(src.replace(old, new), O.__file__, "exec"), ns)
+    mp.setattr(O, func_name, ns[func_name])
+
+
+def _mut_fwd_bf16_no_h_rounding(mp):
+    _patch_source(mp, "expert_rows", 'h_st = bf16_round(h) if precision == "bf16" else h', "h_st = h")
+
+
+def _mut_fwd_fp8_no_h_quant(mp):
+    _patch_source(mp, "expert_rows", "h_st = dequant_1x128(hq, hs)", "h_st = h")
+
+
+def _mut_fwd_routed_y_unrounded(mp):
+    _patch_source(mp, "forward_sparse", 'y_routed[lo:hi] = bf16_round(y) if precision != "exact" else y',
+                  "y_routed[lo:hi] = y")
+
+
+def _mut_fwd_shared_y_bf16(mp):
+    _patch_source(mp, "forward_sparse", 'y_shared[:] = fp32_round(y) if precision != "exact" else y',
+                  'y_shared[:] = bf16_round(y) if precision != "exact" else y')
+
+
+def _mut_fwd_fp8_x_unquantised(mp):
+    _patch_source(mp, "forward_sparse", "x_in = dequant_1x128(xq, xs)", "x_in = x")
+
+
+def _mut_route_margin_x100(mp):
+    _patch_source(mp, "route", "margin[t] = vals[top_k - 1] - vals[top_k]",
+                  "margin[t] = 100 * (vals[top_k - 1] - vals[top_k])")
+
+
+def _mut_route_group_margin_x100(mp):
+    _patch_source(mp, "route", "gmargin[t] = gvals[topk_group - 1] - gvals[topk_group]",
+                  "gmargin[t] = 100 * (gvals[topk_group - 1] - gvals[topk_group])")
+
+
+def _mut_route_margin_vs_kth(mp):
+    _patch_source(mp, "route", "margin[t] = vals[top_k - 1] - vals[top_k]",
+                  "margin[t] = vals[0] - vals[top_k]")
+
+
+def _mut_e4m3_half_ulp_doubled(mp):
+    real = O.e4m3_half_ulp
+    mp.setattr(O, "e4m3_half_ulp", lambda v: 2.0 * real(v))
+
+
+def _mut_e4m3_half_ulp_normal_spacing_everywhere(mp):
+    _patch_source(mp, "e4m3_half_ulp", "np.maximum(a, 2.0 ** -6)", "np.maximum(a, 2.0 ** -9)")
+
+
+def _mut_bwd_no_dy_rounding(mp):
+    _patch_source(mp, "backward", 'dy = rnd(fp32_round(dy)) if precision != "exact" else dy', "dy = dy")
+
+
+def _mut_bwd_no_da_rounding(mp):
+    _patch_source(mp, "backward", "da = rnd(dh * c * sg * (1.0 + a * (1.0 - sg)))",
+                  "da = dh * c * sg * (1.0 + a * (1.0 - sg))")
+
+
+def _mut_bwd_no_dc_rounding(mp):
+    _patch_source(mp, "backward", "dc = rnd(dh * a * sg)", "dc = dh * a * sg")
+
+
+def _mut_bwd_no_h_rounding(mp):
+    _patch_source(mp, "backward", "h = q_rows(fp32_round(h)) if fp8 else rnd(h)",
+                  "h = q_rows(fp32_round(h)) if fp8 else h")
+
+
+def _mut_bwd_fp8_no_h_quant(mp):
+    _patch_source(mp, "backward", "h = q_rows(fp32_round(h)) if fp8 else rnd(h)",
+                  "h = fp32_round(h) if fp8 else rnd(h)")
+
+
+def _mut_bwd_routed_dx_unrounded(mp):
+    _patch_source(mp, "backward", "rnd(dxe) if e < N else dxe", "dxe")
+
+
+def _mut_bwd_fp8_dgrad_dy_unquantised(mp):
+    _patch_source(mp, "backward", "dh = (q_rows(dy) if fp8 else dy) @ we2", "dh = dy @ we2")
+
+
+def _mut_bwd_fp8_dgrad_dac_unquantised(mp):
+    _patch_source(mp, "backward", "dxe = q_rows(dac) @ we13", "dxe = dac @ we13")
+
+
+def _mut_bwd_fp8_wgrad_dy_unquantised(mp):
+    _patch_source(mp, "backward", "dw2_e = q_rows(pad128(dy.T))", "dw2_e = pad128(dy.T)")
+
+
+def _mut_bwd_fp8_wgrad_h_unquantised(mp):
+    _patch_source(mp, "backward", "dequant_128x128(*quant_128x128(pad128(bf16_round(h).T))).T",
+                  "pad128(bf16_round(h).T).T")
+
+
+def _mut_bwd_fp8_wgrad_x_unquantised(mp):
+    _patch_source(mp, "backward", "dequant_128x128(*quant_128x128(pad128(x[tok].T))).T", "pad128(x[tok].T).T")
+
+
+def _mut_bwd_fp8_wgrad_dac_unquantised(mp):
+    _patch_source(mp, "backward", "dw13_e = q_rows(pad128(dac.T))", "dw13_e = pad128(dac.T)")
+
+
+def _mut_bwd_fp8_wgrad_dy_wrong_axis(mp):
+    _patch_source(mp, "backward", "dw2_e = q_rows(pad128(dy.T))", "dw2_e = pad128(q_rows(dy).T)")
+
+
+def _mut_bwd_fp8_x_unquantised(mp):
+    _patch_source(mp, "backward", "x_in = dequant_1x128(*quant_1x128(x)) if fp8 else x", "x_in = x")
+
+
 MUTATIONS = [
     _mut_gate_from_z, _mut_ascending, _mut_tie_higher_index, _mut_silu_sign, _mut_swap_w1_w3,
     _mut_bias_sign, _mut_bias_mean_off, _mut_e4m3_ties_odd, _mut_fnuz_scale,
@@ -248,6 +368,13 @@ MUTATIONS = [
     _mut_group_max_not_top2, _mut_sigmoid_softmax, _mut_quant_transposed_block_scale,
     _mut_e8m0_floor, _mut_e8m0_bias_126, _mut_e8m0_scale_wrong_tile,
     _mut_bwd_no_norm_term, _mut_bwd_swap_w13_halves, _mut_bwd_dw2_rows, _mut_bwd_silu_grad,
+    _mut_fwd_bf16_no_h_rounding, _mut_fwd_fp8_no_h_quant, _mut_fwd_routed_y_unrounded, _mut_fwd_shared_y_bf16,
+    _mut_fwd_fp8_x_unquantised, _mut_route_margin_x100, _mut_route_group_margin_x100, _mut_route_margin_vs_kth,
+    _mut_e4m3_half_ulp_doubled, _mut_e4m3_half_ulp_normal_spacing_everywhere, _mut_bwd_no_dy_rounding,
+    _mut_bwd_no_da_rounding, _mut_bwd_no_dc_rounding, _mut_bwd_no_h_rounding, _mut_bwd_fp8_no_h_quant,
+    _mut_bwd_routed_dx_unrounded, _mut_bwd_fp8_dgrad_dy_unquantised, _mut_bwd_fp8_dgrad_dac_unquantised,
+    _mut_bwd_fp8_wgrad_dy_unquantised, _mut_bwd_fp8_wgrad_h_unquantised, _mut_bwd_fp8_wgrad_x_unquantised,
+    _mut_bwd_fp8_wgrad_dac_unquantised, _mut_bwd_fp8_wgrad_dy_wrong_axis, _mut_bwd_fp8_x_unquantised,
 ]
 
 
