@@ -89,13 +89,13 @@ def _e4m3_positive_table() -> np.ndarray:
 
 
 _E4M3_POS = _e4m3_positive_table()
+# all 256 codes: bit 7 is the sign, 0x7F / 0xFF are NaN
+_E4M3_ALL = np.concatenate([_E4M3_POS, [np.nan], -_E4M3_POS, [np.nan]])
 
 
 def e4m3_decode(codes) -> np.ndarray:
-    codes = np.asarray(codes, dtype=np.uint8)
-    mag = codes & 0x7F
-    out = np.where(mag == 0x7F, np.nan, _E4M3_POS[np.minimum(mag, 126)])
-    return np.where(codes & 0x80, -out, out)
+    """Values of E4M3 codes (a lookup in the table of all 256 codes)."""
+    return _E4M3_ALL[np.asarray(codes, dtype=np.uint8)]
 
 
 def e4m3_encode(v) -> np.ndarray:
@@ -425,7 +425,8 @@ def forward_dense(x, w_router, bias, w13, w2, top_k, n_group=1, topk_group=1):
     return out, r
 
 
-def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str = "exact", workers: int = 1):
+def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str = "exact", workers: int = 1,
+                   weights_quantised: bool = False):
     """The layer computed the sparse way: permute, per-expert FFN on gathered rows, combine.
 
     idx, gate: [T, K] routing decisions and gates (from ``route``).
@@ -443,6 +444,10 @@ def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str 
       "fp8_e8m0" -- the same with power-of-two tile scales (``quant_1x128_e8m0``,
                  ``quant_128x128_e8m0``).
     workers > 1 evaluates the experts concurrently (same arithmetic, for large inputs).
+    weights_quantised (fp8 precisions): expert_weights(e) already returns the weights after
+    their 128x128 block quantisation (dequantised values), so they are not quantised again
+    (for callers that quantise each expert once and reuse it; quantising such values again
+    would give them back unchanged).
     Returns (out [T, d] float64, extras dict with the permutation and per-row outputs).
     """
     x = np.asarray(x, dtype=np.float64)
@@ -462,7 +467,8 @@ def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str 
     def one(e):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         we13, we2 = expert_weights(e)
-        return e, lo, hi, expert_rows(x_in[sorted_token[lo:hi]], we13, we2, precision)
+        return e, lo, hi, expert_rows(x_in[sorted_token[lo:hi]], we13, we2, precision,
+                                      weights_quantised=weights_quantised)
 
     todo = [e for e in range(n_experts + 1) if offsets[e + 1] > offsets[e]]
     if workers > 1:
@@ -497,19 +503,19 @@ def _quantisers(precision: str):
     return qw, qa
 
 
-def expert_rows(rows, w13, w2, precision: str = "exact", return_h: bool = False):
+def expert_rows(rows, w13, w2, precision: str = "exact", return_h: bool = False, weights_quantised: bool = False):
     """One expert's FFN on already-gathered input rows (already dequantised on the fp8
     path), with the intermediate rounding of ``precision`` (see ``forward_sparse``).
     Returns y [m, d] before its own storage rounding (and h as stored, if asked)."""
     rows = np.asarray(rows, dtype=np.float64)
     if precision in ("fp8", "fp8_e8m0"):
         qw, qa = _quantisers(precision)
-        q13, s13 = qw(w13)
-        q2, s2 = qw(w2)
-        h = swiglu_hidden(rows, dequant_128x128(q13, s13))
+        w13d = np.asarray(w13, np.float64) if weights_quantised else dequant_128x128(*qw(w13))
+        w2d = np.asarray(w2, np.float64) if weights_quantised else dequant_128x128(*qw(w2))
+        h = swiglu_hidden(rows, w13d)
         hq, hs = qa(fp32_round(h))
         h_st = dequant_1x128(hq, hs)
-        y = h_st @ dequant_128x128(q2, s2).T
+        y = h_st @ w2d.T
     else:
         h = swiglu_hidden(rows, w13)
         h_st = bf16_round(h) if precision == "bf16" else h

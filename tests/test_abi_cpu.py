@@ -30,7 +30,7 @@ def test_header_declares_exactly_the_exports():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.lib().moe_abi_version() == 4
+    assert L.lib().moe_abi_version() == 5
     assert L.status_str(0) == "MOE_OK" and L.status_str(5) == "MOE_ERR_WORKSPACE"
 
 
@@ -78,7 +78,7 @@ def test_other_entry_points_reject():
 
 def _gemm(L, **kw):
     d = dict(in_dtype=0, a=16, lda=256, w=16, group_offsets=16, first_group=0, n_groups=4, m_total=100,
-             N=256, K=256, epilogue=0, out=16, out_dtype=1, ldo=256)
+             N=256, K=256, epilogue=0, out=16, out_dtype=1, ldo=256, ws=16, ws_bytes=256)
     d.update(kw)
     desc = L.MoeGemmDesc(**d)
     return L.lib().moe_grouped_gemm(ctypes.byref(desc), None)
@@ -96,6 +96,7 @@ def _gemm(L, **kw):
     (dict(tail_groups=1, out_dtype=0, out_tail=16, ldo_tail=256, epilogue=1, N=512), 3),
     (dict(in_dtype=2, a_scale=16, w_scale=16, scale_fmt=5), 3),
     (dict(in_dtype=2, a_scale=16, w_scale=16, scale_fmt=1, K=256, lda=256), 2),
+    (dict(ws=None), 5), (dict(ws_bytes=255), 5), (dict(ws=8), 5),
 ])
 def test_gemm_rejects(kw, code):
     L = _lib()
@@ -108,6 +109,7 @@ def test_workspace_queries():
     assert lib.moe_route_workspace_size(4096, 256) > 0
     assert lib.moe_route_workspace_size(-1, 256) == 0
     assert lib.moe_permute_workspace_size(16384, 256) == 2 * 64 * 256 * 4
+    assert lib.moe_grouped_gemm_workspace_size() == 256
 
 
 def _rejects(lib, fn, args, code):

@@ -11,7 +11,8 @@ import torch
 
 from oracle import moe_oracle as O
 from sparse_moe_layer_sigmoid_amd import inputs as I
-from tests.gpu_common import FP8_DOT_REL, FP8_TOL, check_route, fp8_staged_check, np64, rel_err, say
+from tests.gpu_common import (FP8_DOT_REL, FP8_TOL, check_route, fp8_end_to_end_bar, fp8_staged_check, np64,
+                              rel_err, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -177,6 +178,9 @@ def _layer_case(cfg):
             router_std=0.04, outlier_frac=7.2 / 512),
     I.small(I.V3_FP8, name="e8m0_small_2", T=129, d=1024, n_experts=16, top_k=8, inter=512, w_std=0.03,
             router_std=0.03),
+    # the layer's width, I = 2048, with T, N and d reduced instead
+    I.small(I.V3_FP8, name="e8m0_I2048", T=256, d=1024, n_experts=16, top_k=4, inter=2048, w_std=0.03,
+            router_std=0.03, outlier_frac=7.2 / 1024),
 ], ids=lambda c: c.name)
 def test_layer_fp8_e8m0(cfg):
     say(f"layer fp8 e8m0 {cfg.name}")
@@ -201,3 +205,5 @@ def test_layer_fp8_e8m0(cfg):
     err = rel_err(np64(out32)[keep], ref[keep])
     say(f"  staged: h codes equal to the oracle's {same:.5f}, output from the device h {staged:.2e} "
         f"(tol {FP8_TOL}); end to end vs the oracle's fp8_e8m0 pipeline {err:.2e}")
+    if cfg.inter >= 2048:   # end to end at the layer's width; the staged check carries reduced widths
+        fp8_end_to_end_bar(err, cfg.name)

@@ -12,8 +12,8 @@ import torch
 
 from oracle import moe_oracle as O
 from sparse_moe_layer_sigmoid_amd import inputs as I
-from tests.gpu_common import (BF16_TOL, FP8_DOT_REL, FP8_TOL, fp8_staged_check, check_permutation_properties, check_route,
-                              np64, rel_err, say)
+from tests.gpu_common import (BF16_TOL, FP8_DOT_REL, FP8_TOL, fp8_end_to_end_bar, fp8_staged_check,
+                              check_permutation_properties, check_route, np64, rel_err, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -255,6 +255,47 @@ def test_gemm_bf16_row_blocks(sizes, swiglu):
             assert rel_err(got[lo:hi], ref) < 1e-5, g
         else:  # one bf16 rounding of the fp32 result
             assert np.all(np.abs(got[lo:hi] - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6 * np.sqrt(np.mean(ref ** 2))), g
+
+
+def test_gemm_round_sync_workspaces_two_streams():
+    """The bf16 SwiGLU launch with 128-row blocks keeps its workgroups in step with arrival
+    counters in the caller's workspace.  65 groups of ~90 rows x 8 column blocks give each XCD
+    three rounds, the last one partial (every workgroup must arrive for its last round, or the
+    waiters there run to their bound).  Two such launches on two streams with their own
+    workspaces, issued to overlap, give outputs bit-identical to the same launches run one
+    after the other, and both workspaces are zero again afterwards."""
+    G, N, K, T = 65, 2048, 1024, 3000
+    sizes = I.gen_group_sizes(31, G, 90, empty_frac=0.0)
+    offs = _offsets(sizes)
+    rows = int(offs[-1])
+    say(f"round-sync two streams: {G} groups, {rows} rows, N={N} K={K}")
+    a_rows = torch.from_numpy(np.random.default_rng(32).integers(0, T, rows).astype(np.int32)).to(DEV)
+    A = [I.gen_normal(33 + i, (T, K), 1.0).to(DEV) for i in range(2)]
+    W = [I.gen_normal(35 + i, (G, N, K), 0.05).to(DEV) for i in range(2)]
+    o = torch.from_numpy(offs).to(DEV)
+    wsz = M().lib().moe_grouped_gemm_workspace_size()
+    ws = [torch.zeros(wsz, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    serial = [torch.empty((rows, N // 2), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    for i in range(2):
+        M().moe_grouped_gemm(A[i], W[i], o, 0, G, rows, serial[i], a_rows=a_rows, swiglu=True, ws=ws[i])
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    par = [torch.empty_like(serial[0]) for _ in range(2)]
+    for rep in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                M().moe_grouped_gemm(A[i], W[i], o, 0, G, rows, par[i], a_rows=a_rows, swiglu=True, ws=ws[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(par[i], serial[i]), (rep, i)
+            assert int(ws[i].count_nonzero().item()) == 0, (rep, i)
+    # the serial result is the GEMM the oracle defines (sampled groups)
+    An, Wn, got = np64(A[0]), np64(W[0]), np64(serial[0])
+    ar = a_rows.cpu().numpy()
+    for g in (0, 31, G - 1):
+        lo, hi = offs[g], offs[g + 1]
+        ref = O.swiglu_hidden(An[ar[lo:hi]], Wn[g])
+        assert np.all(np.abs(got[lo:hi] - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6 * np.sqrt(np.mean(ref ** 2))), g
 
 
 @pytest.mark.parametrize("fp8,tail", [(False, 1), (False, 2), (True, 1)], ids=["bf16_tail1", "bf16_tail2", "fp8_tail1"])
@@ -560,6 +601,11 @@ def test_layer_bf16(cfg):
     I.small(I.V3_FP8, name="fp8_small_no_outliers", T=300, d=512, n_experts=32, top_k=4, inter=256, w_std=0.04,
             router_std=0.04, outlier_frac=0.0),
     I.small(I.V3_FP8, name="fp8_small_2", T=129, d=256, n_experts=16, top_k=8, inter=128, w_std=0.05, router_std=0.05),
+    # the layer's width, I = 2048, with T, N and d reduced instead
+    I.small(I.V3_FP8, name="fp8_I2048", T=256, d=1024, n_experts=16, top_k=4, inter=2048, w_std=0.03,
+            router_std=0.03, outlier_frac=7.2 / 1024),
+    I.small(I.V3_FP8, name="fp8_I2048_k8", T=200, d=512, n_experts=32, top_k=8, inter=2048, w_std=0.04,
+            router_std=0.04, outlier_frac=7.2 / 512),
 ], ids=lambda c: c.name)
 def test_layer_fp8(cfg):
     say(f"layer fp8 {cfg.name}")
@@ -582,13 +628,18 @@ def test_layer_fp8(cfg):
                                     lambda t, e: gates[t][e], cfg.n_experts, lambda e: (W13n[e], W2n[e]), buf,
                                     out32, FP8_TOL)
     # End to end against the oracle's own fp8 pipeline (its h codes rounded from exact sums):
-    # reported, not asserted.  At these reduced widths (I = 128..256) one h code a step away
-    # moves an output by a visible fraction of its RMS; at the layer's width (I = 2048) the
-    # full-size test asserts this comparison too.
+    # asserted at the layer's width (I = 2048).  At reduced widths (I = 128..256) a single h
+    # code one step from the oracle's (a legitimate difference: the two sums straddle a
+    # rounding midpoint) moves an output by a visible fraction of its RMS, so there the
+    # figure is reported and the staged check above carries the bar.
     ref, _ = O.forward_sparse(x64, r["idx"], r["gate"], cfg.n_experts, lambda e: (W13n[e], W2n[e]), "fp8")
     err = rel_err(np64(out32)[keep], ref[keep])
+    exact, _ = O.forward_sparse(x64, r["idx"], r["gate"], cfg.n_experts, lambda e: (W13n[e], W2n[e]), "exact")
     say(f"  staged: h codes equal to the oracle's {same:.5f}, output from the device h {staged:.2e} "
-        f"(tol {FP8_TOL}); end to end vs the oracle's fp8 pipeline {err:.2e}")
+        f"(tol {FP8_TOL}); end to end vs the oracle's fp8 pipeline {err:.2e}; vs the exact layer: device "
+        f"{rel_err(np64(out32)[keep], exact[keep]):.2e}, oracle fp8 pipeline {rel_err(ref[keep], exact[keep]):.2e}")
+    if cfg.inter >= 2048:
+        fp8_end_to_end_bar(err, cfg.name)
 
 
 @pytest.mark.parametrize("T", [1, 129])
@@ -612,8 +663,8 @@ def test_layer_all_tokens_on_the_same_experts(fp8):
     """The most skewed load the method allows: a bias of +10 on experts 0..K-1 makes every token
     select exactly those (the bias only selects; the gates stay the normalised affinities), so K
     groups hold all T rows, the shared expert holds T more and every other group is empty."""
-    cfg = I.small(I.V3_FP8 if fp8 else I.V3_BF16, name="skew", T=300, d=512, n_experts=32, top_k=4, inter=256,
-                  w_std=0.04, router_std=0.04, outlier_frac=0.0)
+    cfg = I.small(I.V3_FP8 if fp8 else I.V3_BF16, name="skew", T=300, d=512, n_experts=32, top_k=4,
+                  inter=2048 if fp8 else 256, w_std=0.04, router_std=0.04, outlier_frac=0.0)
     x, wr, _, W13, W2 = _layer_case(cfg)
     bias = torch.zeros(cfg.n_experts, dtype=torch.float32)
     bias[:cfg.top_k] = 10.0
@@ -647,8 +698,7 @@ def test_layer_all_tokens_on_the_same_experts(fp8):
             say(f"  skewed backward {name}: {e:.2e}")
             assert e <= BF16_TOL, name
         return
-    # E4M3: stage by stage as in test_layer_fp8 (at this width one h code a step away from the
-    # oracle's moves an output visibly, so the end-to-end figure is reported, not asserted)
+    # E4M3: stage by stage as in test_layer_fp8, and end to end at the layer's width
     pick = np.arange(cfg.T)
     gates = [dict(zip(r["idx"][t], r["gate"][t])) for t in range(cfg.T)]
     staged, same = fp8_staged_check(pick, x64, buf["topk_idx"].cpu().numpy(), buf["pair_pos"].cpu().numpy(),
@@ -656,6 +706,7 @@ def test_layer_all_tokens_on_the_same_experts(fp8):
                                     out32, FP8_TOL)
     say(f"  skewed layer (fp8): h codes equal to the oracle's {same:.5f}, output from the device h {staged:.2e}; "
         f"end to end {err:.2e}")
+    fp8_end_to_end_bar(err, "skew")
 
 
 def test_layer_bias_update_loop():
