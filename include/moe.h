@@ -16,13 +16,12 @@
  *    the caller's next synchronisation.
  *  - Ownership: every pointer is caller-owned memory; pointers documented as "device" must
  *    be device memory of the current device.  The library never allocates or frees device
- *    memory and keeps no state between calls, with one exception: the bf16 SwiGLU launches
- *    of moe_grouped_gemm with 128-row blocks pace their workgroups with nine arrival counters
- *    in a static device array (one copy per device); every launch leaves them at zero, and
- *    launches that overlap on one device share them, which can cost time but never changes
- *    a result.  Scratch memory comes from the caller's workspace, sized by the
- *    *_workspace_size() queries; it need not be initialised and its contents are undefined
- *    after the call.
+ *    memory and keeps no state between calls.  Scratch memory comes from the caller's
+ *    workspace, sized by the *_workspace_size() queries; for moe_route and moe_permute it need
+ *    not be initialised and its contents are undefined after the call; moe_grouped_gemm's
+ *    small workspace holds counters that must be zero when a call starts and that every call
+ *    leaves at zero (see there).  Calls that may run at the same time (on streams not ordered
+ *    with each other) need distinct workspaces; calls on one stream may share one.
  *  - Layout: row-major and contiguous unless an ld* (leading dimension, in elements) is
  *    given.  Device pointers must be 16-byte aligned; leading dimensions must keep every
  *    row 16-byte aligned.
@@ -232,6 +231,9 @@ typedef struct moe_gemm_desc {
   int scale_fmt;                /* MOE_SCALE_F32 (0) or MOE_SCALE_E8M0 (FP8 only) */
   int64_t ldw;                  /* row stride of each W[g] in elements (0: K); W[g] starts at
                                    w + g * N * ldw */
+  void* ws;                     /* device workspace of moe_grouped_gemm_workspace_size() bytes,
+                                   16-byte aligned, zero-filled before its first use */
+  size_t ws_bytes;
 } moe_gemm_desc;
 /* Limits: K a positive multiple of 64 (bf16) or 128 (FP8); N a positive multiple of 128 (bf16)
  * or 256 (FP8) -- with SWIGLU that is N/2 a multiple of 64 or 128; FP8 input needs a_scale and
@@ -241,6 +243,14 @@ typedef struct moe_gemm_desc {
  * out_dtype MOE_BF16, tail_groups <= n_groups and a 16-byte aligned out_tail with
  * ldo_tail >= N.  E8M0 scales need K a multiple of 512 (each scale row is read 4 codes at a
  * time). */
+/* Workspace of moe_grouped_gemm (256 bytes): arrival counters with which the workgroups of a
+ * launch keep in step, so that the rows of one expert that several workgroups process meet its
+ * weights in the same L2 (used by the bf16 SwiGLU launches with 128-row blocks).  The caller
+ * zero-fills it once; every call leaves it zero-filled again.  Calls that may overlap in time
+ * need distinct workspaces (sharing one could only make the bounded waits run to their bound,
+ * never change a result); calls on one stream may share one.  Missing or too small ->
+ * MOE_ERR_WORKSPACE. */
+size_t moe_grouped_gemm_workspace_size(void);
 moe_status moe_grouped_gemm(const moe_gemm_desc* desc, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------

@@ -23,7 +23,7 @@ EXPORTS = (
     "moe_route_workspace_size", "moe_route",
     "moe_permute_workspace_size", "moe_permute",
     "fp8_quant_1x128", "fp8_quant_128x128", "fp8_quant_1x128_e8m0", "fp8_quant_128x128_e8m0", "fp8_dequant_1x128",
-    "moe_grouped_gemm", "moe_combine", "moe_bias_update",
+    "moe_grouped_gemm_workspace_size", "moe_grouped_gemm", "moe_combine", "moe_bias_update",
     "moe_combine_backward", "moe_swiglu_backward", "moe_segment_transpose", "moe_router_wgrad",
 )
 
@@ -41,6 +41,7 @@ class MoeGemmDesc(ctypes.Structure):
         ("n_groups", _i), ("m_total", _i64), ("N", _i), ("K", _i), ("epilogue", _i),
         ("out", _p), ("out_dtype", _i), ("ldo", _i64), ("out_scale", _p),
         ("tail_groups", _i), ("out_tail", _p), ("ldo_tail", _i64), ("scale_fmt", _i), ("ldw", _i64),
+        ("ws", _p), ("ws_bytes", _sz),
     ]
 
 
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_quant_128x128_e8m0.argtypes = [_p, _i, _i, _i, _p, _p, _p]
         L.fp8_dequant_1x128.restype = _i
         L.fp8_dequant_1x128.argtypes = [_p, _p, _i, _i, _p, _p]
+        L.moe_grouped_gemm_workspace_size.restype = _sz
+        L.moe_grouped_gemm_workspace_size.argtypes = []
         L.moe_grouped_gemm.restype = _i
         L.moe_grouped_gemm.argtypes = [ctypes.POINTER(MoeGemmDesc), _p]
         L.moe_combine.restype = _i
@@ -229,15 +232,32 @@ def fp8_quant_128x128_e8m0(w):
 
 _DT = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32, torch.uint8: MOE_FP8_E4M3}
 
+_GEMM_WS = {}
+
+
+def gemm_workspace(device, stream=None) -> torch.Tensor:
+    """The zero-filled moe_grouped_gemm workspace of one stream (made on first use and kept).
+    Launches on one stream are ordered, so they may share it; every launch leaves it zeroed."""
+    device = torch.device(device)
+    stream = torch.cuda.current_stream(device) if stream is None else stream
+    key = (device.index, stream.cuda_stream)
+    ws = _GEMM_WS.get(key)
+    if ws is None:
+        ws = torch.zeros(lib().moe_grouped_gemm_workspace_size(), dtype=torch.uint8, device=device)
+        torch.cuda.current_stream(device).synchronize()  # the zero fill precedes any use on `stream`
+        _GEMM_WS[key] = ws
+    return ws
+
 
 def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_total: int, out,
                      a_scale=None, a_rows=None, w_scale=None, swiglu: bool = False, out_scale=None,
-                     out_tail=None, tail_groups: int = 0):
+                     out_tail=None, tail_groups: int = 0, ws=None):
     """out[r - off[first_group]] = epilogue(A[a_rows[r] or r] . W[g]^T) for each sorted row r
     of group g.  a: bf16 or uint8 (E4M3) [*, K]; w: same dtype [G, N, K]; out: bf16 / f32 /
     uint8 (E4M3, needs out_scale).  With tail_groups > 0 the last tail_groups groups write
     f32 rows to out_tail instead (row r -> r - off[first_group + n_groups - tail_groups]).
-    FP8 scales are f32, or E8M0 codes when they are uint8 tensors (all of them alike)."""
+    FP8 scales are f32, or E8M0 codes when they are uint8 tensors (all of them alike).
+    ws: the launch's workspace (default: the current stream's, see gemm_workspace)."""
     fp8 = a.dtype == torch.uint8
     scales = [s for s in (a_scale, w_scale, out_scale) if s is not None]
     e8 = fp8 and any(s.dtype == torch.uint8 for s in scales)
@@ -256,6 +276,9 @@ def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_tot
     if a.stride(-1) != 1 or out.stride(-1) != 1 or w.stride(-1) != 1 or (G > 1 and w.stride(0) != N * w.stride(1)):
         raise ValueError("rows of a/out/w must be contiguous and the W[g] packed (stride N * ldw)")
     ldw = w.stride(1)
+    if ws is None:
+        ws = gemm_workspace(a.device)
+    _dev(ws, torch.uint8, "ws")
     desc = MoeGemmDesc(
         in_dtype=MOE_FP8_E4M3 if fp8 else MOE_BF16, a=a.data_ptr(),
         a_scale=a_scale.data_ptr() if a_scale is not None else None,
@@ -267,7 +290,8 @@ def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_tot
         out_scale=out_scale.data_ptr() if out_scale is not None else None,
         tail_groups=tail_groups, out_tail=out_tail.data_ptr() if tail_groups else None,
         ldo_tail=out_tail.stride(0) if tail_groups else 0,
-        scale_fmt=MOE_SCALE_E8M0 if e8 else MOE_SCALE_F32, ldw=0 if ldw == K else ldw)
+        scale_fmt=MOE_SCALE_E8M0 if e8 else MOE_SCALE_F32, ldw=0 if ldw == K else ldw,
+        ws=ws.data_ptr(), ws_bytes=ws.numel())
     st = lib().moe_grouped_gemm(ctypes.byref(desc), _stream(a))
     _check("moe_grouped_gemm", st)
     return out

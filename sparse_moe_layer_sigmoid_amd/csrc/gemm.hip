@@ -24,8 +24,9 @@
 //    to walk K together; left alone they drift apart by whole tiles over a launch, so in the
 //    bf16 gate/up kernel with 128-row blocks each workgroup waits at the start of a round
 //    until the XCD's other workgroups have finished the previous one (an arrival counter per
-//    XCD; the wait is bounded, so it only ever costs time, and the last workgroup to leave
-//    resets the counters for the next launch).
+//    XCD in the caller's workspace; a workgroup arrives for each of its rounds, the last one
+//    as it leaves; the wait is bounded, so it only ever costs time, and the last workgroup to
+//    leave resets the counters for the next launch on that workspace).
 //  * Row blocks of 128 rows (8 waves of 64x64), or 160 rows (8 waves of 80x64) for bf16
 //    launches whose experts hold ~100-600 rows, where they need fewer row tiles per expert;
 //    64 rows for decode-sized groups.
@@ -59,11 +60,8 @@ namespace {
 enum { OUT_BF16 = 0, OUT_F32 = 1, OUT_FP8 = 2 };
 constexpr int kMaxGroups = 1024;
 constexpr int kSyncSpins = 400;  // bound of a round wait: ~1 us per poll
-
-// Round arrival counters per XCD and an exit counter (zero at load; every launch leaves them
-// zero).  Launches on one device that overlap in time share them: a wait may then run to its
-// bound, which costs time but never correctness.
-__device__ unsigned int g_round_sync[9];
+// The workspace: round arrival counters of the 8 XCDs and an exit counter, zero between launches.
+constexpr size_t kGemmWsBytes = 256;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
@@ -104,6 +102,7 @@ struct GemmArgs {
   int tail_first;       // first group (relative) writing the f32 tail output; n_groups if none
   uint8_t* out_tail;
   int64_t ldo_tail_b;   // bytes per tail output row
+  unsigned int* sync;   // workspace: [8] round arrivals per XCD, [8] exit counter
 };
 
 __device__ __forceinline__ float silu(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
@@ -261,13 +260,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     for (int r = 0; r < q; ++r) tgt += (unsigned int)max(0, min(per_xcd, xr - r * per_xcd));
     return tgt;
   };
+  // A workgroup arrives for round r - 1 as it starts round r, and for its last round as it
+  // leaves, so the counter of an XCD reaches round_target(q) once every workgroup with a tile
+  // in rounds < q has finished it.  The last workgroup to leave resets the counters.
   auto leave = [&]() {
-    if (tid == 0) {
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      const unsigned int prev = __hip_atomic_fetch_add(&g_round_sync[8], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == gridDim.x - 1) {  // last workgroup out: reset for the next launch
-        for (int x = 0; x < 8; ++x) __hip_atomic_store(&g_round_sync[x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&g_round_sync[8], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (kRoundSync) {
+      if (tid == 0) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (n_my > 0) __hip_atomic_fetch_add(&p.sync[xcd], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned int prev = __hip_atomic_fetch_add(&p.sync[8], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == gridDim.x - 1) {  // last workgroup out: reset for the next launch
+          for (int x = 0; x < 8; ++x) __hip_atomic_store(&p.sync[x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&p.sync[8], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
   };
@@ -725,11 +730,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       if (kRoundSync && kt == 0 && j > 0) {  // a new round: arrive for the last one, wait for the XCD
         if (tid == 0) {
           const int q = j / ksteps;
-          __hip_atomic_fetch_add(&g_round_sync[xcd], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(&p.sync[xcd], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const unsigned int tgt = round_target(q);
 #pragma unroll 1
           for (int it = 0; it < kSyncSpins; ++it) {
-            if (__hip_atomic_load(&g_round_sync[xcd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= tgt) break;
+            if (__hip_atomic_load(&p.sync[xcd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= tgt) break;
             __builtin_amdgcn_s_sleep(2);
           }
         }
@@ -900,6 +905,8 @@ void dispatch(const GemmArgs& a, int64_t m_total, bool small, bool narrow, hipSt
 }  // namespace
 }  // namespace moe
 
+extern "C" size_t moe_grouped_gemm_workspace_size(void) { return moe::kGemmWsBytes; }
+
 extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t stream) {
   using namespace moe;
   clear_error();
@@ -935,6 +942,8 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
   MOE_REQUIRE(!e8 || d->K % 512 == 0, MOE_ERR_SHAPE,
               "moe_grouped_gemm: E8M0 scales need K a multiple of 512 (K=%d)", d->K);
   if (d->out_dtype == MOE_FP8_E4M3) MOE_REQUIRE(d->out_scale, MOE_ERR_NULL, "moe_grouped_gemm: FP8 output needs out_scale");
+  MOE_REQUIRE(d->ws && d->ws_bytes >= kGemmWsBytes && aligned16(d->ws), MOE_ERR_WORKSPACE,
+              "moe_grouped_gemm: workspace %zu < %zu bytes (or NULL / unaligned)", d->ws_bytes, kGemmWsBytes);
   const int esz = fp8 ? 1 : 2;
   const int osz = d->out_dtype == MOE_F32 ? 4 : (d->out_dtype == MOE_BF16 ? 2 : 1);
   const int out_cols = swiglu ? d->N / 2 : d->N;
@@ -981,6 +990,7 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
   a.ldo_tail_b = d->ldo_tail * 4;
   a.out_cols = out_cols;
   a.n_tiles = 0;  // set per tile shape at launch
+  a.sync = static_cast<unsigned int*>(d->ws);
   const bool narrow = !fp8 && d->N % 256 != 0;
 
   // Tile shape by regime: many rows per expert -> 128-row blocks; few (decode) -> 64.
