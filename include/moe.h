@@ -104,6 +104,22 @@ moe_status moe_route(const uint16_t* x, const uint16_t* w_router, const float* b
                      int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
                      float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_route_noalloc -- moe_route for callers that cannot allocate device memory: code
+ * running under HIP graph capture, allocation-free serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and checks as moe_route without the workspace: its
+ * scratch is a static device array of the library, one copy per device (8.4 MB, held until
+ * the process ends), whose device address is looked up once per device on the first call
+ * there.  The call allocates nothing.
+ * Limits: those of moe_route, and T <= MOE_ROUTE_NOALLOC_MAX_T (1024 tokens); a larger T
+ * returns MOE_ERR_SHAPE with nothing launched.  Every call initialises the scratch it reads,
+ * but all calls on one device share that array: calls that may overlap in time on one
+ * device (unordered streams) race and must not be issued. */
+#define MOE_ROUTE_NOALLOC_MAX_T 1024
+moe_status moe_route_noalloc(const uint16_t* x, const uint16_t* w_router, const float* bias, int T,
+                             int d, int n_experts, int top_k, int n_group, int topk_group,
+                             int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
+                             float* scores, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------
  * moe_permute -- token permutation for the expert GEMMs (the within-GPU half of the
  * dispatch stage of "DeepSeek-V3 Technical Report", "DualPipe パイプライン並列化").

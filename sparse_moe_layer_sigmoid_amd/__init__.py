@@ -8,6 +8,6 @@ calls.  Nothing here falls back to a CPU implementation.
 """
 from ._lib import (EXPORTS, LIB_PATH, MoeError, fp8_quant_128x128, fp8_quant_128x128_e8m0,  # noqa: F401
                    fp8_quant_1x128, fp8_quant_1x128_e8m0, lib, moe_bias_update, moe_combine, moe_grouped_gemm,
-                   moe_permute, moe_route)
+                   moe_permute, moe_route, moe_route_noalloc)
 from .layer import MoELayer  # noqa: F401
 from .state import load_bias_state, save_bias_state  # noqa: F401

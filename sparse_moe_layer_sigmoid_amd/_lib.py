@@ -20,7 +20,7 @@ MOE_SCALE_F32, MOE_SCALE_E8M0 = 0, 1
 
 EXPORTS = (
     "moe_status_str", "moe_last_error", "moe_abi_version",
-    "moe_route_workspace_size", "moe_route",
+    "moe_route_workspace_size", "moe_route", "moe_route_noalloc",
     "moe_permute_workspace_size", "moe_permute",
     "fp8_quant_1x128", "fp8_quant_128x128", "fp8_quant_1x128_e8m0", "fp8_quant_128x128_e8m0", "fp8_dequant_1x128",
     "moe_grouped_gemm_workspace_size", "moe_grouped_gemm", "moe_combine", "moe_bias_update",
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route_workspace_size.argtypes = [_i, _i]
         L.moe_route.restype = _i
         L.moe_route.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p]
+        L.moe_route_noalloc.restype = _i
+        L.moe_route_noalloc.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p]
         L.moe_permute_workspace_size.restype = _sz
         L.moe_permute_workspace_size.argtypes = [_i, _i]
         L.moe_permute.restype = _i
@@ -156,6 +158,27 @@ def moe_route(x, w_router, bias, top_k: int, n_group: int = 1, topk_group: int =
     st = lib().moe_route(_ptr(x), _ptr(w_router), _ptr(bias), T, d, N, top_k, n_group, topk_group,
                          _ptr(idx), _ptr(gate), _ptr(counts), _ptr(scores), _ptr(ws), ws.numel(), _stream(x))
     _check("moe_route", st)
+    return idx, gate, counts, scores
+
+
+def moe_route_noalloc(x, w_router, bias, top_k: int, n_group: int = 1, topk_group: int = 1, out=None):
+    """moe_route with the library's static scratch instead of a workspace (T <= 1024); the
+    outputs are given in `out` (topk_idx, topk_gate, expert_counts, optional scores) or
+    allocated here.  Returns (topk_idx, topk_gate, expert_counts, scores|None)."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(w_router, torch.bfloat16, "w_router")
+    _dev(bias, torch.float32, "bias")
+    T, d = x.shape
+    N = w_router.shape[0]
+    dev = x.device
+    out = out or {}
+    idx = out["topk_idx"] if "topk_idx" in out else torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    gate = out["topk_gate"] if "topk_gate" in out else torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    counts = out["expert_counts"] if "expert_counts" in out else torch.empty(N, dtype=torch.int32, device=dev)
+    scores = out.get("scores")
+    st = lib().moe_route_noalloc(_ptr(x), _ptr(w_router), _ptr(bias), T, d, N, top_k, n_group, topk_group,
+                                 _ptr(idx), _ptr(gate), _ptr(counts), _ptr(scores), _stream(x))
+    _check("moe_route_noalloc", st)
     return idx, gate, counts, scores
 
 

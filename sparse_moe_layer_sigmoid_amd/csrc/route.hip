@@ -27,6 +27,8 @@
 //  5. reduce: one wave per expert sums the block histograms (integer sums: exact).
 #include <math.h>
 
+#include <mutex>
+
 #include "abi_common.h"
 #include "device_common.h"
 
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(64) void counts_reduce_kernel(const int32_t* __rest
   if (lane == 0) counts[e] = s;
 }
 
-int route_splits(int T, int d) {
+constexpr int route_splits(int T, int d) {
   const int tiles = (T + kTM - 1) / kTM;
   int s = tiles > 0 ? 512 / tiles : 1;
   s = s < 1 ? 1 : (s > 8 ? 8 : s);
@@ -420,8 +422,8 @@ struct RouteWs {
   size_t part_off, nflag_off, list_off, blk_off, total;
 };
 
-RouteWs route_ws(int T, int d, int N) {
-  RouteWs w;
+constexpr RouteWs route_ws(int T, int d, int N) {
+  RouteWs w{};
   const int S = route_splits(T, d);
   const int nb = T > 0 ? (T + 63) / 64 : 1;
   w.part_off = 0;  // split-K partials, then the fp64 logits of the flagged tokens
@@ -432,47 +434,68 @@ RouteWs route_ws(int T, int d, int N) {
   return w;
 }
 
-}  // namespace
-}  // namespace moe
+// Scratch of moe_route_noalloc: the workspace of moe_route for up to kNoAllocMaxT tokens and
+// 256 experts, as a static device array (one per device, held until the process ends: 8.4 MB).
+// Host code reaches it only through the address hipGetSymbolAddress gives for the current
+// device; the array's name is not a device address on the host.
+constexpr int kNoAllocMaxT = MOE_ROUTE_NOALLOC_MAX_T;
+constexpr size_t kNoAllocBytes = route_ws(kNoAllocMaxT, 1 << 20, 256).total;
+__device__ __align__(256) uint8_t scratch[kNoAllocBytes];
 
-extern "C" size_t moe_route_workspace_size(int T, int n_experts) {
-  if (T < 0 || n_experts <= 0) return 0;
-  // sized for the largest split count (d only limits it further)
-  return moe::route_ws(T, 1 << 20, n_experts).total;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept.
+moe_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  MOE_REQUIRE(e == hipSuccess, MOE_ERR_HIP, "moe_route_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  MOE_REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_ERR_HIP, "moe_route_noalloc: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    MOE_REQUIRE(e == hipSuccess && ptr != nullptr, MOE_ERR_HIP, "moe_route_noalloc: hipGetSymbolAddress: %s",
+                hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
-extern "C" moe_status moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias,
-                                int T, int d, int n_experts, int top_k, int n_group,
-                                int topk_group, int32_t* topk_idx, float* topk_gate,
-                                int32_t* expert_counts, float* scores, void* ws,
-                                size_t ws_bytes, hipStream_t stream) {
-  using namespace moe;
-  clear_error();
-  MOE_REQUIRE(w_router && bias && expert_counts && ws && (T == 0 || (x && topk_idx && topk_gate)),
-              MOE_ERR_NULL, "moe_route: a required pointer is NULL");
-  MOE_REQUIRE(T >= 0, MOE_ERR_SHAPE, "moe_route: T=%d < 0", T);
-  MOE_REQUIRE(d >= 64 && d % 64 == 0, MOE_ERR_SHAPE, "moe_route: d=%d must be a positive multiple of 64", d);
+moe_status route_check(const char* fn, const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int d,
+                       int n_experts, int top_k, int n_group, int topk_group, const int32_t* topk_idx,
+                       const float* topk_gate, const int32_t* expert_counts, const float* scores) {
+  MOE_REQUIRE(w_router && bias && expert_counts && (T == 0 || (x && topk_idx && topk_gate)),
+              MOE_ERR_NULL, "%s: a required pointer is NULL", fn);
+  MOE_REQUIRE(T >= 0, MOE_ERR_SHAPE, "%s: T=%d < 0", fn, T);
+  MOE_REQUIRE(d >= 64 && d % 64 == 0, MOE_ERR_SHAPE, "%s: d=%d must be a positive multiple of 64", fn, d);
   MOE_REQUIRE(n_experts >= 4 && n_experts <= 256 && n_experts % 4 == 0, MOE_ERR_SHAPE,
-              "moe_route: n_experts=%d must be in [4, 256] and a multiple of 4", n_experts);
+              "%s: n_experts=%d must be in [4, 256] and a multiple of 4", fn, n_experts);
   MOE_REQUIRE(top_k >= 1 && top_k <= n_experts, MOE_ERR_SHAPE,
-              "moe_route: top_k=%d must be in [1, n_experts=%d]", top_k, n_experts);
+              "%s: top_k=%d must be in [1, n_experts=%d]", fn, top_k, n_experts);
   MOE_REQUIRE(n_group >= 1 && n_group <= 64 && n_experts % n_group == 0, MOE_ERR_SHAPE,
-              "moe_route: n_group=%d must divide n_experts=%d and be <= 64", n_group, n_experts);
+              "%s: n_group=%d must divide n_experts=%d and be <= 64", fn, n_group, n_experts);
   MOE_REQUIRE(topk_group >= 1 && topk_group <= n_group, MOE_ERR_SHAPE,
-              "moe_route: topk_group=%d must be in [1, n_group=%d]", topk_group, n_group);
+              "%s: topk_group=%d must be in [1, n_group=%d]", fn, topk_group, n_group);
   if (n_group > 1) {
     const int gs = n_experts / n_group;
     MOE_REQUIRE(gs >= 4 && (gs & (gs - 1)) == 0, MOE_ERR_SHAPE,
-                "moe_route: groups must hold a power of two >= 4 experts (n_experts/n_group=%d)", gs);
+                "%s: groups must hold a power of two >= 4 experts (n_experts/n_group=%d)", fn, gs);
     MOE_REQUIRE(top_k <= topk_group * gs, MOE_ERR_SHAPE,
-                "moe_route: top_k=%d exceeds the %d experts of the kept groups", top_k, topk_group * gs);
+                "%s: top_k=%d exceeds the %d experts of the kept groups", fn, top_k, topk_group * gs);
   }
   MOE_REQUIRE(aligned16(x) && aligned16(w_router) && (scores == nullptr || aligned16(scores)),
-              MOE_ERR_ALIGN, "moe_route: x, w_router and scores must be 16-byte aligned");
-  const size_t need = moe_route_workspace_size(T, n_experts);
-  MOE_REQUIRE(ws_bytes >= need && aligned16(ws), MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu bytes (or unaligned)",
-              ws_bytes, need);
+              MOE_ERR_ALIGN, "%s: x, w_router and scores must be 16-byte aligned", fn);
+  return MOE_OK;
+}
 
+// The five kernels of one routing call, their scratch laid out in `ws` (route_ws bytes).
+void route_launch(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int d, int n_experts,
+                  int top_k, int n_group, int topk_group, int32_t* topk_idx, float* topk_gate,
+                  int32_t* expert_counts, float* scores, void* ws, hipStream_t stream) {
   const RouteWs L = route_ws(T, d, n_experts);
   uint8_t* base = static_cast<uint8_t*>(ws);
   float* part = reinterpret_cast<float*>(base + L.part_off);
@@ -494,5 +517,52 @@ extern "C" moe_status moe_route(const uint16_t* x, const uint16_t* w_router, con
     route_count_kernel<<<nb, 64, 0, stream>>>(topk_idx, T, n_experts, top_k, blk);
   }
   counts_reduce_kernel<<<n_experts, 64, 0, stream>>>(blk, nb, n_experts, expert_counts);
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" size_t moe_route_workspace_size(int T, int n_experts) {
+  if (T < 0 || n_experts <= 0) return 0;
+  // sized for the largest split count (d only limits it further)
+  return moe::route_ws(T, 1 << 20, n_experts).total;
+}
+
+extern "C" moe_status moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                                int T, int d, int n_experts, int top_k, int n_group,
+                                int topk_group, int32_t* topk_idx, float* topk_gate,
+                                int32_t* expert_counts, float* scores, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  using namespace moe;
+  clear_error();
+  const moe_status st = route_check("moe_route", x, w_router, bias, T, d, n_experts, top_k, n_group, topk_group,
+                                    topk_idx, topk_gate, expert_counts, scores);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(ws, MOE_ERR_NULL, "moe_route: a required pointer is NULL");
+  const size_t need = moe_route_workspace_size(T, n_experts);
+  MOE_REQUIRE(ws_bytes >= need && aligned16(ws), MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu bytes (or unaligned)",
+              ws_bytes, need);
+  route_launch(x, w_router, bias, T, d, n_experts, top_k, n_group, topk_group, topk_idx, topk_gate, expert_counts,
+               scores, ws, stream);
   return check_launch("moe_route");
+}
+
+extern "C" moe_status moe_route_noalloc(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                                        int T, int d, int n_experts, int top_k, int n_group,
+                                        int topk_group, int32_t* topk_idx, float* topk_gate,
+                                        int32_t* expert_counts, float* scores, hipStream_t stream) {
+  using namespace moe;
+  clear_error();
+  const moe_status st = route_check("moe_route_noalloc", x, w_router, bias, T, d, n_experts, top_k, n_group,
+                                    topk_group, topk_idx, topk_gate, expert_counts, scores);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(T <= kNoAllocMaxT, MOE_ERR_SHAPE, "moe_route_noalloc: T=%d exceeds the static scratch (T <= %d)", T,
+              kNoAllocMaxT);
+  static_assert(route_ws(kNoAllocMaxT, 1 << 20, 256).total == kNoAllocBytes, "scratch sized for the largest call");
+  void* ws = nullptr;
+  const moe_status se = scratch_of_current_device(&ws);
+  if (se != MOE_OK) return se;
+  route_launch(x, w_router, bias, T, d, n_experts, top_k, n_group, topk_group, topk_idx, topk_gate, expert_counts,
+               scores, ws, stream);
+  return check_launch("moe_route_noalloc");
 }

@@ -103,6 +103,23 @@ def test_gemm_rejects(kw, code):
     assert _gemm(L, **kw) == code, L.lib().moe_last_error()
 
 
+def test_route_noalloc_rejects():
+    """The allocation-free routing call checks its arguments like moe_route, and refuses T
+    beyond its static scratch (1024 tokens) before anything else happens."""
+    L = _lib()
+    lib = L.lib()
+    P = lambda n: ctypes.c_void_p(n)
+    ok = dict(x=P(16), w=P(16), b=P(16), T=1024, d=7168, N=256, K=8, ng=1, tg=1, idx=P(16), gate=P(16), cnt=P(16))
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.moe_route_noalloc(a["x"], a["w"], a["b"], a["T"], a["d"], a["N"], a["K"], a["ng"], a["tg"],
+                                     a["idx"], a["gate"], a["cnt"], None, None)
+    assert call(T=1025) == 2 and b"1024" in lib.moe_last_error()
+    assert call(w=None) == 1 and call(d=100) == 2 and call(K=300) == 2 and call(x=P(8)) == 4
+    assert lib.moe_last_error().decode().startswith("moe_route_noalloc")
+
+
 def test_workspace_queries():
     L = _lib()
     lib = L.lib()
