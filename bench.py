@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--decode-steps", type=int, default=None)
+    p.add_argument("--decode-sweep-steps", type=int, default=20)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first copy 1 GiB device-to-device twice (the reference dispatch for HBM counters)")
     p.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -76,19 +77,25 @@ class KernelTimer:
         return sum(s.elapsed_time(e) for s, e in self.pairs) / len(self.pairs)
 
 
-def run_layer_steps(torch, M, layer, xs, steps, warmup, timer_gate_up, gamma, update_bias=True):
-    """Warm up, then time `steps` forwards (events on the current stream)."""
-    L = M._lib
-    orig = L.moe_grouped_gemm
+def run_layer_steps(torch, M, layer, xs, steps, warmup, timers, gamma, update_bias=True):
+    """Warm up, then time `steps` forwards (events on the current stream).  timers: dict of
+    KernelTimer for "gate_up", "down" and "combine", filled during the timed steps."""
+    import sparse_moe_layer_sigmoid_amd.layer as layer_mod
+    L = layer_mod.L
+    orig_gg, orig_cb = L.moe_grouped_gemm, L.moe_combine
     state = {"timing": False}
 
     def gg(*a, **kw):
-        if state["timing"] and kw.get("swiglu"):
-            return timer_gate_up.wrap(orig, *a, **kw)
-        return orig(*a, **kw)
+        if state["timing"]:
+            return timers["gate_up" if kw.get("swiglu") else "down"].wrap(orig_gg, *a, **kw)
+        return orig_gg(*a, **kw)
 
-    import sparse_moe_layer_sigmoid_amd.layer as layer_mod
-    layer_mod.L.moe_grouped_gemm = gg
+    def cb(*a, **kw):
+        if state["timing"]:
+            return timers["combine"].wrap(orig_cb, *a, **kw)
+        return orig_cb(*a, **kw)
+
+    L.moe_grouped_gemm, L.moe_combine = gg, cb
     try:
         for i in range(warmup):
             layer.forward(xs[i % len(xs)], update_bias=update_bias, gamma=gamma)
@@ -103,21 +110,58 @@ def run_layer_steps(torch, M, layer, xs, steps, warmup, timer_gate_up, gamma, up
         state["timing"] = False
         return start.elapsed_time(end) / steps
     finally:
-        layer_mod.L.moe_grouped_gemm = orig
+        L.moe_grouped_gemm, L.moe_combine = orig_gg, orig_cb
+
+
+def kernel_fractions(cfg, counts, fp8, e8m0, km):
+    """Per-kernel achieved rates against their roofline: the GEMMs against the matrix-core
+    peak of their dtype (and HBM), the combine against HBM."""
+    fl_gu = 4 * cfg.rows * cfg.d * cfg.inter
+    fl_dn = 2 * cfg.rows * cfg.d * cfg.inter
+    peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
+    out = {}
+    for name, fl, by in (("gate_up", fl_gu, gate_up_bytes(cfg, counts, fp8, 1 if e8m0 else 4)),
+                         ("down", fl_dn, down_bytes(cfg, counts, fp8))):
+        ms = km[name]
+        tf = fl / (ms / 1e3) / 1e12
+        gbs = by / (ms / 1e3) / 1e9
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "mfma_frac": round(tf / peak, 4),
+                     "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    ms = km["combine"]
+    gbs = combine_bytes(cfg) / (ms / 1e3) / 1e9
+    out["combine"] = {"ms": round(ms, 4), "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def gate_up_bytes(cfg, counts_np, fp8: bool, scale_bytes: int = 4):
     """Algorithmic HBM bytes of one gate/up launch: the W13 of every expert with at least one
-    row (plus the shared one) read once, each gathered input row read once, h written once
-    (fp8: with their scales, scale_bytes each)."""
+    row (plus the shared one) read once, the input x read once (T rows: the gather of a
+    token's K + 1 rows re-reads it from cache, not from HBM), h written once (fp8: with
+    their scales, scale_bytes each)."""
     esz = 1 if fp8 else 2
     sb = scale_bytes if fp8 else 0
     active = int((counts_np > 0).sum()) + 1
     w = active * 2 * cfg.inter * cfg.d * esz + active * (2 * cfg.inter // 128) * (cfg.d // 128) * sb
-    rows = cfg.rows
-    a = rows * cfg.d * esz + rows * (cfg.d // 128) * sb
-    h = rows * cfg.inter * esz + rows * (cfg.inter // 128) * sb
+    a = cfg.T * cfg.d * esz + cfg.T * (cfg.d // 128) * sb
+    h = cfg.rows * cfg.inter * esz + cfg.rows * (cfg.inter // 128) * sb
     return w + a + h
+
+
+def down_bytes(cfg, counts_np, fp8: bool):
+    """Algorithmic HBM bytes of one down launch: the W2 of every active expert (and the
+    shared one) read once, h read once, routed y written in bf16 and the shared y in f32."""
+    esz = 1 if fp8 else 2
+    sb = 4 if fp8 else 0
+    active = int((counts_np > 0).sum()) + 1
+    w = active * cfg.d * cfg.inter * esz + active * (cfg.d // 128) * (cfg.inter // 128) * sb
+    h = cfg.rows * cfg.inter * esz + cfg.rows * (cfg.inter // 128) * sb
+    return w + h + cfg.T * cfg.top_k * cfg.d * 2 + cfg.T * cfg.d * 4
+
+
+def combine_bytes(cfg):
+    """Algorithmic HBM bytes of one combine: the K routed rows (bf16) and the shared row (f32)
+    of every token read once, the bf16 output written once."""
+    return cfg.T * cfg.top_k * cfg.d * 2 + cfg.T * cfg.d * 4 + cfg.T * cfg.d * 2
 
 
 def step_bytes(cfg, counts_np, fp8: bool):
@@ -247,6 +291,47 @@ def cpu_baseline(cfg, wr_cpu, bias_cpu, W13_cpu, W2_cpu, budget_s=10.0, max_step
             "seconds_measured": round(timed, 2)}
 
 
+def decode_skew_sweep(torch, M, I, wr, W13, W2, dev, steps):
+    """The decode shape (T = 256, E4M3 path) under three fixed routing skews, no bias update:
+    a zero bias (the router's own spread), the Zipf(1.1) popularity bias, and +10 on experts
+    0..7 (every token picks the same 8 experts: the hottest load the method allows).  Each
+    step is timed alone (events around it, steps back to back); reported per skew: median
+    time, tokens/s, the algorithmic bytes of the experts that receive tokens over the time,
+    max/mean load and the active-expert count."""
+    import numpy as np
+    c4 = I.V3_DECODE
+    xs = [I.gen_x(c4, step=i).to(dev) for i in range(steps)]
+    zipf = I.gen_bias(c4)
+    hot = torch.zeros(c4.n_experts, dtype=torch.float32)
+    hot[:c4.top_k] = 10.0
+    out = {"workload": c4.name + "_skew_sweep", "dtype": "fp8", "steps": steps}
+    layer = M.MoELayer(wr, W13, W2, zipf.to(dev), c4.top_k, fp8=True)
+    for name, b in (("zero_bias", torch.zeros(c4.n_experts)), ("zipf_1.1", zipf), ("hot8_plus10", hot)):
+        layer.bias = b.to(dev).clone()
+        for i in range(3):
+            layer.forward(xs[i])
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        hist = torch.empty((steps, c4.n_experts), dtype=torch.int32, device=dev)
+        for i in range(steps):
+            ev[i][0].record()
+            _, buf = layer.forward(xs[i], keep=True)
+            ev[i][1].record()
+            hist[i].copy_(buf["expert_counts"])
+        torch.cuda.synchronize()
+        h = hist.cpu().numpy()
+        t = np.array([a.elapsed_time(b_) for a, b_ in ev])
+        by = np.array([step_bytes(c4, c, True) for c in h])
+        out[name] = {"ms_median": round(float(np.median(t)), 4),
+                     "tokens_per_s": round(c4.T / (float(np.median(t)) / 1e3), 1),
+                     "gbs_median": round(float(np.median(by / (t / 1e3) / 1e9)), 1),
+                     "bytes_per_step_median": int(np.median(by)),
+                     "max_over_mean_load": round(float(np.median(h.max(axis=1) / h.mean(axis=1))), 2),
+                     "active_experts_median": int(np.median((h > 0).sum(axis=1)))}
+        log(f"[bench] decode skew {name}: {out[name]}")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -292,19 +377,33 @@ def main():
         _, buf = layer.forward(xs[0], keep=True)
         counts0 = buf["expert_counts"].cpu().numpy()
         layer.bias.copy_(bias_cpu.to(dev))
-        timer = KernelTimer(torch)
-        ms = run_layer_steps(torch, M, layer, xs, steps, warmup, timer, cfg.gamma)
-        return layer, xs_cpu, bias_cpu, counts0, ms, timer.mean_ms()
+        timers = {k: KernelTimer(torch) for k in ("gate_up", "down", "combine")}
+        ms = run_layer_steps(torch, M, layer, xs, steps, warmup, timers, cfg.gamma)
+        km = {k: t.mean_ms() for k, t in timers.items()}
+        kf = kernel_fractions(cfg, counts0, fp8, scales == "e8m0", km)
+        return layer, xs_cpu, bias_cpu, counts0, ms, km["gate_up"], kf
 
     # ---------------------------------------------------------------- headline workload
     fp8_main = cfg.dtype == "fp8"
-    layer, xs_cpu, bias_cpu, counts0, ms, gu_ms = measure(cfg, fp8_main, args.steps, args.warmup,
-                                                          scales="e8m0" if main_e8m0 else "f32")
+    layer, xs_cpu, bias_cpu, counts0, ms, gu_ms, kf = measure(cfg, fp8_main, args.steps, args.warmup,
+                                                              scales="e8m0" if main_e8m0 else "f32")
     flops = O.layer_flops(cfg.T, cfg.d, cfg.n_experts, cfg.top_k, cfg.inter)
     tok_s = cfg.T / (ms / 1e3)
     gu_bytes = gate_up_bytes(cfg, counts0, fp8_main, 1 if main_e8m0 else 4)
-    achieved = gu_bytes / (gu_ms / 1e3) / 1e9
+    gu_flop = 4 * cfg.rows * cfg.d * cfg.inter
     tag = f"gate_up_{args.workload}"
+    if fp8_main:  # compute-bound: the E4M3 gate/up against the matrix-core peak
+        achieved = gu_flop / (gu_ms / 1e3) / 1e12
+        roofline = {"kernel": "grouped_gemm gate/up + SwiGLU (E4M3)", "bound": "mfma", "achieved": round(achieved, 1),
+                    "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic(tag), "avg_launch_ms": round(gu_ms, 4),
+                    "algorithmic_flop_per_launch": int(gu_flop), "algorithmic_bytes_per_launch": int(gu_bytes)}
+    else:
+        achieved = gu_bytes / (gu_ms / 1e3) / 1e9
+        roofline = {"kernel": "grouped_gemm gate/up + SwiGLU", "bound": "hbm", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(tag), "avg_launch_ms": round(gu_ms, 4),
+                    "algorithmic_bytes_per_launch": int(gu_bytes)}
     line = {
         "metric": "MoE-layer tokens/s + % MFMA peak (T=4096 bf16, T=16384 fp8); decode GB/s",
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -315,25 +414,24 @@ def main():
                    "step": "route+permute+gateup_swiglu+down+combine+bias_update"},
         "tflops": round(flops / (ms / 1e3) / 1e12, 2),
         "mfma_frac": round(flops / (ms / 1e3) / 1e12 / (FP8_PEAK_TFLOPS if fp8_main else BF16_PEAK_TFLOPS), 4),
-        "roofline": {"kernel": "grouped_gemm gate/up + SwiGLU", "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(tag), "avg_launch_ms": round(gu_ms, 4),
-                     "algorithmic_bytes_per_launch": int(gu_bytes)},
+        "roofline": roofline,
+        "kernels": kf,
     }
-    log(f"[bench] {args.workload}: {ms:.3f} ms/step, {tok_s:,.0f} tok/s, gate/up {gu_ms:.3f} ms ({achieved:.0f} GB/s)")
+    log(f"[bench] {args.workload}: {ms:.3f} ms/step, {tok_s:,.0f} tok/s, gate/up {gu_ms:.3f} ms ({achieved:.0f} "
+        f"{roofline['unit']}), down {kf['down']['ms']:.3f} ms, combine {kf['combine']['ms']:.3f} ms")
 
     # ---------------------------------------------------------------- secondary workloads
     if not args.no_secondary:
         sec = []
         c3 = I.V3_FP8
-        l3, _, _, counts3, ms3, gu3 = measure(c3, True, max(5, args.steps // 2), 3)
+        l3, _, _, counts3, ms3, gu3, kf3 = measure(c3, True, max(5, args.steps // 2), 3)
         f3 = O.layer_flops(c3.T, c3.d, c3.n_experts, c3.top_k, c3.inter)
         fl3 = 4 * c3.rows * c3.d * c3.inter
         sec.append({"workload": c3.name, "dtype": "fp8", "ms_per_step": round(ms3, 4),
                     "tokens_per_s": round(c3.T / (ms3 / 1e3), 1), "tflops": round(f3 / (ms3 / 1e3) / 1e12, 2),
                     "mfma_frac_fp8_peak": round(f3 / (ms3 / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4),
                     "gate_up_ms": round(gu3, 4), "gate_up_traffic": measured_traffic(f"gate_up_{c3.name}"),
-                    "gate_up_mfma_frac": round(fl3 / (gu3 / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4)})
+                    "gate_up_mfma_frac": round(fl3 / (gu3 / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4), "kernels": kf3})
         log(f"[bench] {c3.name}: {ms3:.3f} ms/step, gate/up {gu3:.3f} ms")
         # its backward on the FP8 path (E4M3 Dgrad and Wgrad)
         x3 = I.gen_x(c3).to(dev)
@@ -361,13 +459,13 @@ def main():
         del l3, buf3, d3, keep3, x3
         torch.cuda.empty_cache()
         # the same layer with power-of-two (E8M0) tile scales applied by the matrix cores
-        l3e, _, _, _, ms3e, gu3e = measure(c3, True, max(5, args.steps // 2), 3, scales="e8m0")
+        l3e, _, _, _, ms3e, gu3e, kf3e = measure(c3, True, max(5, args.steps // 2), 3, scales="e8m0")
         sec.append({"workload": c3.name + "_e8m0", "dtype": "fp8", "scales": "e8m0", "ms_per_step": round(ms3e, 4),
                     "tokens_per_s": round(c3.T / (ms3e / 1e3), 1), "tflops": round(f3 / (ms3e / 1e3) / 1e12, 2),
                     "mfma_frac_fp8_peak": round(f3 / (ms3e / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4),
                     "gate_up_ms": round(gu3e, 4),
                     "gate_up_traffic": measured_traffic(f"gate_up_{c3.name}_e8m0"),
-                    "gate_up_mfma_frac": round(fl3 / (gu3e / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4)})
+                    "gate_up_mfma_frac": round(fl3 / (gu3e / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4), "kernels": kf3e})
         log(f"[bench] {c3.name}_e8m0: {ms3e:.3f} ms/step, gate/up {gu3e:.3f} ms")
         del l3e
         # the backward pass of the headline layer (bf16): gradients of x, the router and every
@@ -399,11 +497,11 @@ def main():
         del lb, bufb, d_out, keep_g
         torch.cuda.empty_cache()
         c2 = I.V3_GROUP
-        l2, _, _, _, ms2, _ = measure(c2, False, max(5, args.steps // 2), 3)
+        l2, _, _, _, ms2, _, kf2 = measure(c2, False, max(5, args.steps // 2), 3)
         f2 = O.layer_flops(c2.T, c2.d, c2.n_experts, c2.top_k, c2.inter)
         sec.append({"workload": c2.name, "dtype": "bf16", "ms_per_step": round(ms2, 4),
                     "tokens_per_s": round(c2.T / (ms2 / 1e3), 1), "tflops": round(f2 / (ms2 / 1e3) / 1e12, 2),
-                    "mfma_frac_bf16_peak": round(f2 / (ms2 / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)})
+                    "mfma_frac_bf16_peak": round(f2 / (ms2 / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4), "kernels": kf2})
         log(f"[bench] {c2.name}: {ms2:.3f} ms/step")
         del l2
         c4 = I.V3_DECODE
@@ -426,12 +524,13 @@ def main():
             ev[i][1].record()
             hist[i].copy_(buf["expert_counts"])
         torch.cuda.synchronize()
-        loads, gbs, times = [], [], []
+        loads, gbs, times, active = [], [], [], []
         for i, cnt in enumerate(hist.cpu().numpy()):
             t = ev[i][0].elapsed_time(ev[i][1])
             loads.append(float(cnt.max() / cnt.mean()))
             gbs.append(step_bytes(c4, cnt, True) / (t / 1e3) / 1e9)
             times.append(t)
+            active.append(int((cnt > 0).sum()))
         sec.append({"workload": c4.name, "dtype": "fp8", "steps": n4,
                     "ms_per_step_median": round(float(np.median(times)), 4),
                     "gbs_median": round(float(np.median(gbs)), 1),
@@ -439,8 +538,12 @@ def main():
                     "gbs_median_first10": round(float(np.median(gbs[:10])), 1),
                     "gbs_median_last10": round(float(np.median(gbs[-10:])), 1),
                     "max_over_mean_load_first": round(loads[0], 3), "max_over_mean_load_last": round(loads[-1], 3),
-                    "max_over_mean_load_series_every10": [round(v, 3) for v in loads[::10]]})
+                    "per_step": {"max_over_mean_load": [round(v, 2) for v in loads],
+                                 "active_experts": active, "gbs": [round(v) for v in gbs],
+                                 "ms": [round(v, 3) for v in times]}})
         log(f"[bench] {c4.name}: median {np.median(times):.3f} ms, {np.median(gbs):.0f} GB/s, load {loads[0]:.2f}->{loads[-1]:.2f}")
+        del l4, xs4, hist
+        sec.append(decode_skew_sweep(torch, M, I, wr, W13, W2, dev, args.decode_sweep_steps))
         line["secondary"] = sec
 
     if not args.no_cpu_baseline:
