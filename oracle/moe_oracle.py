@@ -103,22 +103,23 @@ def e4m3_encode(v) -> np.ndarray:
 
     Round to nearest, ties to the even code (the one whose mantissa LSB is 0); magnitudes
     at or above 448 saturate to 448; NaN -> 0x7F (with the input's sign bit).
-    The nearest value is found by a search over the table of representable magnitudes.
+    From the format's definition: |v| lies in the binade [2^e, 2^(e+1)), whose 8 values are
+    spaced 2^(e-3); below 2^-6 the subnormals keep the spacing 2^-9 of the lowest binade
+    (e = -6).  n = RNE(|v| / 2^(e-3)) (an exact division) is then 8..16 in a binade (16 being
+    the first value of the next one) or 0..8 below it, and the code (E << 3) | M, with
+    value (1 + M/8) 2^(E-7) for E >= 1 and M 2^-9 for E = 0, is (e + 6) * 8 + n.
     """
-    v = np.asarray(v, dtype=np.float64)
+    v = np.asarray(v)
+    if v.dtype != np.float32:
+        v = v.astype(np.float64)
     sign = np.signbit(v)
     a = np.abs(v)
     nan = np.isnan(a)
-    a = np.where(nan, 0.0, a)
-    hi = np.searchsorted(_E4M3_POS, a, side="left")  # first table value >= a
-    hi = np.minimum(hi, 126)
-    lo = np.maximum(hi - 1, 0)
-    d_hi = _E4M3_POS[hi] - a
-    d_lo = a - _E4M3_POS[lo]
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    code = np.where(pick_hi, hi, lo)
-    code = np.where(a >= E4M3_MAX, 126, code)
-    code = np.where(_E4M3_POS[hi] == a, hi, code)  # exact hits
+    _, e = np.frexp(a)                       # a = f 2^e, f in [0.5, 1): binade exponent e - 1
+    e = np.where(a < 2.0 ** -6, -6, e - 1)
+    n = np.rint(np.ldexp(a, 3 - e))          # round half to even
+    code = (e + 6) * 8 + n
+    code = np.where((a >= E4M3_MAX) | (code > 126), 126, code)
     code = np.where(nan, 0x7F, code).astype(np.uint8)
     return np.where(sign, code | 0x80, code).astype(np.uint8)
 
@@ -471,12 +472,7 @@ def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str 
                                       weights_quantised=weights_quantised)
 
     todo = [e for e in range(n_experts + 1) if offsets[e + 1] > offsets[e]]
-    if workers > 1:
-        from concurrent.futures import ThreadPoolExecutor
-        with ThreadPoolExecutor(workers) as ex:
-            results = list(ex.map(one, todo))
-    else:
-        results = [one(e) for e in todo]
+    results = _map_experts(one, todo, workers)
     for e, lo, hi, y in results:
         if e < n_experts:
             y_routed[lo:hi] = bf16_round(y) if precision != "exact" else y
@@ -485,6 +481,19 @@ def forward_sparse(x, idx, gate, n_experts: int, expert_weights, precision: str 
     out = combine(y_routed, y_shared, pair_pos, gate)
     return out, {"offsets": offsets, "sorted_token": sorted_token, "pair_pos": pair_pos,
                  "y_routed": y_routed, "y_shared": y_shared}
+
+
+def _map_experts(fn, experts, workers: int):
+    """[fn(e) for e in experts], on `workers` threads when workers > 1 (each with a
+    single-threaded BLAS, so the pool does not oversubscribe the cores).  Same arithmetic."""
+    experts = list(experts)
+    if workers <= 1:
+        return [fn(e) for e in experts]
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, experts))
 
 
 def _quantisers(precision: str):
@@ -630,12 +639,7 @@ def backward(x, w_router, bias, w13, w2, top_k: int, d_out, n_group: int = 1, to
             dxe = dac @ we13
         return tok, slot, dg, dw2_e, dw13_e, rnd(dxe) if e < N else dxe
 
-    if workers > 1:
-        from concurrent.futures import ThreadPoolExecutor
-        with ThreadPoolExecutor(workers) as ex:
-            results = list(ex.map(one, range(N + 1)))
-    else:
-        results = [one(e) for e in range(N + 1)]
+    results = _map_experts(one, range(N + 1), workers)
     for e, res in enumerate(results):
         if res is None:
             continue

@@ -205,7 +205,9 @@ def fp8_staged_check_batches(batches, n_experts, expert_weights, tol, e8m0=False
         return out
 
     from concurrent.futures import ThreadPoolExecutor
-    with ThreadPoolExecutor(workers) as ex:
+
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(workers) as ex:
         results = [r for rs in ex.map(one, sorted(pairs)) for r in rs]
     y_routed = [np.zeros((len(b["pick"]) * K, d)) for b in st]
     y_shared = [np.zeros((len(b["pick"]), d)) for b in st]

@@ -50,23 +50,45 @@ def fp8_layer(v3, bias, cfg):
     return v3.fp8_layer
 
 
-def _host_experts(cfg):
+class _Progress:
+    """Counts the experts an oracle pass has fetched and prints every 32nd (a long pass then
+    reports as it goes)."""
+
+    def __init__(self, what):
+        import threading
+        self.what, self.n, self.t0, self.lock = what, 0, time.time(), threading.Lock()
+
+    def tick(self):
+        with self.lock:
+            self.n += 1
+            if self.n % 32 == 0:
+                say(f"[fullsize]   {self.what}: {self.n} experts [{time.time() - self.t0:.0f}s]")
+
+
+def _host_experts(cfg, what="oracle"):
     """Expert e's weights regenerated on the host from the seeded streams (float64), for the
     oracle; each call draws them afresh, so the oracle's worker threads generate in parallel."""
-    return lambda e: tuple(t_.double().numpy() for t_ in I.gen_expert(cfg, e))
+    prog = _Progress(what)
+
+    def fetch(e):
+        prog.tick()
+        return tuple(t_.double().numpy() for t_ in I.gen_expert(cfg, e))
+    return fetch
 
 
 _FP8_CACHE = {}
 
 
-def _fp8_experts(cfg, precision="fp8"):
+def _fp8_experts(cfg, precision="fp8", what="oracle"):
     """Expert weights block-quantised (128x128, E4M3) by the oracle once per test module --
     codes and scales kept, ~11 GB for all 257 experts per scale format -- and handed to the
     oracle dequantised (weights_quantised=True)."""
     qw = O._quantisers(precision)[0]
     cache = _FP8_CACHE.setdefault((precision, cfg.weight_seed, cfg.d, cfg.inter, cfg.w_std), {})
+    prog = _Progress(what)
 
     def fetch(e):
+        prog.tick()
         if e not in cache:
             w13, w2 = (t_.double().numpy() for t_ in I.gen_expert(cfg, e))
             cache[e] = (qw(w13), qw(w2))
@@ -107,7 +129,8 @@ def _fp8_staged(cfg, x_cpu, r, tie, out32, buf, precision, every=8):
     gates = {int(t): dict(zip(r["idx"][t], r["gate"][t])) for t in pick}
     staged, same = fp8_staged_check(pick, x_cpu[pick].double().numpy(), buf["topk_idx"].cpu().numpy(),
                                     buf["pair_pos"].cpu().numpy(), lambda t, e: gates[t][e], cfg.n_experts,
-                                    _fp8_experts(cfg, precision), buf, out32, FP8_TOL, e8m0=precision == "fp8_e8m0",
+                                    _fp8_experts(cfg, precision, "staged"), buf, out32, FP8_TOL,
+                                    e8m0=precision == "fp8_e8m0",
                                     weights_quantised=True)
     say(f"[fullsize] {cfg.name}: staged: h codes equal to the oracle's {same:.5f}, output from the device h "
         f"{staged:.3e} (tol {FP8_TOL}) [{time.time() - t0:.0f}s]")
@@ -372,7 +395,7 @@ def _decode_output_checks(cfg, kept):
         batches.append(dict(pick=p_, x_rows=x_cpu[p_].double().numpy(), gi=buf["topk_idx"].cpu().numpy(),
                             pp=buf["pair_pos"].cpu().numpy(), gate_of=lambda t, e, g=gates: g[t][e], buf=buf,
                             out32=out32))
-    staged, same = fp8_staged_check_batches(batches, cfg.n_experts, _fp8_experts(cfg, "fp8"), FP8_TOL,
+    staged, same = fp8_staged_check_batches(batches, cfg.n_experts, _fp8_experts(cfg, "fp8", "staged"), FP8_TOL,
                                             weights_quantised=True)
     say(f"[fullsize] decode: staged per step {[f'{e:.3e}' for e in staged]} (tol {FP8_TOL}); h codes equal to the "
         f"oracle's {same:.5f} [{time.time() - t0:.0f}s]")
