@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
                     [--no-cpu-baseline]
+    python bench.py --ceilings     (the chip's measured ceilings; no layer)
 
 One step = one training-mode forward of one DeepSeekMoE layer over one batch of synthetic
 tokens: route -> permute -> [fp8 quantisation of x] -> gate/up grouped GEMM + SwiGLU ->
@@ -49,6 +50,9 @@ def parse():
     p.add_argument("--decode-sweep-steps", type=int, default=20)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first copy 1 GiB device-to-device twice (the reference dispatch for HBM counters)")
+    p.add_argument("--ceilings", action="store_true",
+                   help="run the ceiling micro-benchmarks (HBM read, DMA read in the GEMM's pattern, copy, "
+                        "LDS read, matrix cores, fp32 FMA) instead of the layer and print one JSON line")
     p.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of a --calibrate-copy bench "
                         "into profiles/traffic_<kernel>_<workload>.json, then exit")
@@ -332,6 +336,110 @@ def decode_skew_sweep(torch, M, I, wr, W13, W2, dev, steps):
     return out
 
 
+def run_ceilings(torch, dev):
+    """The chip's measured ceilings from libmoe_ceilings.so: each probe warmed up twice, then
+    timed five times with HIP events on the stream it runs on (the best run is reported);
+    per-clock figures from the probes' own s_memtime cycle counts (median over workgroups)."""
+    path = os.path.join(ROOT, "sparse_moe_layer_sigmoid_amd", "libmoe_ceilings.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: python -m sparse_moe_layer_sigmoid_amd.build")
+    lib = ctypes.CDLL(path)
+    P, S, I32, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int64
+    lib.moe_ceil_hbm_read.argtypes = [P, S, P, S, I32, P]
+    lib.moe_ceil_dma_read.argtypes = [P, I64, I32, P, S, I32, P]
+    lib.moe_ceil_lds_read.argtypes = [I32, I32, P, P, S, I32, P]
+    lib.moe_ceil_mfma.argtypes = [I32, I32, P, P, S, I32, P]
+    lib.moe_ceil_valu.argtypes = [I32, P, P, S, I32, P]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    sink = torch.empty(cus * 16 * 512, dtype=torch.int32, device=dev)
+    cycles = torch.empty(cus, dtype=torch.int64, device=dev)
+    sk, skn, cy = sink.data_ptr(), sink.numel(), cycles.data_ptr()
+
+    def timed(call, reps=5, warm=2):
+        for _ in range(warm):
+            rc = call()
+            if rc != 0:
+                raise RuntimeError(f"ceiling probe returned {rc}")
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    def med_cycles():
+        return float(cycles.cpu().double().median())
+
+    out = {"cus": cus}
+    buf = torch.empty(8 << 30, dtype=torch.uint8, device=dev)
+    rd = {}
+    for mult in (4, 8, 16):
+        ms = timed(lambda: lib.moe_ceil_hbm_read(buf.data_ptr(), buf.numel(), sk, skn, cus * mult, sp))
+        rd[f"grid_{mult}x"] = round(buf.numel() / (ms / 1e3) / 1e9, 1)
+    out["hbm_read_vector_GBs"] = {"bytes": buf.numel(), **rd, "best": max(rd.values())}
+    row_bytes = 7168 * 2
+    rows = buf.numel() // row_bytes // 256 * 256
+    ms = timed(lambda: lib.moe_ceil_dma_read(buf.data_ptr(), rows, row_bytes, sk, skn, cus, sp))
+    out["hbm_read_dma_gemm_pattern_GBs"] = {"rows": rows, "row_bytes": row_bytes, "grid": cus,
+                                            "GBs": round(rows * row_bytes / (ms / 1e3) / 1e9, 1)}
+    half = buf.numel() // 2
+    src, dst = buf[:half], buf[half:]
+    ms = timed(lambda: (dst.copy_(src), 0)[1])
+    out["d2d_copy_GBs"] = {"bytes_each_way": half, "GBs_read_plus_write": round(2 * half / (ms / 1e3) / 1e9, 1)}
+    del buf, src, dst
+    clocks = []
+    for width in (16, 8):
+        iters = 16384
+        ms = timed(lambda: lib.moe_ceil_lds_read(width, iters, cy, sk, skn, cus, sp))
+        per_block = 512 * width * iters
+        c = med_cycles()
+        clocks.append(c / (ms * 1e6))
+        out[f"lds_read_b{width * 8}"] = {"B_per_clk_per_CU": round(per_block / c, 1),
+                                          "TBs_chip": round(per_block * cus / (ms / 1e3) / 1e12, 2)}
+    for kind, name, fl in ((0, "mfma_bf16_16x16x32", 2 * 16 * 16 * 32), (1, "mfma_e4m3_16x16x128", 2 * 16 * 16 * 128),
+                           (2, "mfma_e4m3_16x16x128_promoted", 2 * 16 * 16 * 128)):
+        iters = 2048
+        ms = timed(lambda: lib.moe_ceil_mfma(kind, iters, cy, sk, skn, cus, sp))
+        flops = cus * 8 * iters * 8 * fl
+        c = med_cycles()
+        clocks.append(c / (ms * 1e6))
+        out[name] = {"TFLOPs": round(flops / (ms / 1e3) / 1e12, 1),
+                     "flop_per_clk_per_CU": round(flops / cus / c, 1)}
+    iters = 65536
+    ms = timed(lambda: lib.moe_ceil_valu(iters, cy, sk, skn, cus, sp))
+    flops = cus * 512 * iters * 8 * 2
+    c = med_cycles()
+    clocks.append(c / (ms * 1e6))
+    out["valu_fp32_fma"] = {"TFLOPs": round(flops / (ms / 1e3) / 1e12, 1), "flop_per_clk_per_CU": round(flops / cus / c, 1)}
+    out["shader_clock_GHz_per_probe"] = [round(x, 3) for x in clocks]
+    # the vendor library's dense GEMMs at the gate/up shape of 16384 tokens x 8 + 1 experts
+    # (one M x 2I x d product), for comparison with the grouped kernels: bf16 through
+    # torch.matmul, E4M3 with one scale per tensor through torch._scaled_mm
+    Mr, Nr, Kr = 147456, 4096, 7168
+    lib_gemm = {"M": Mr, "N": Nr, "K": Kr}
+    a = torch.randn(Mr, Kr, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(Nr, Kr, device=dev, dtype=torch.bfloat16)
+    ms = timed(lambda: (torch.matmul(a, b.t()), 0)[1], reps=3, warm=1)
+    lib_gemm["bf16_TFLOPs"] = round(2 * Mr * Nr * Kr / (ms / 1e3) / 1e12, 1)
+    try:
+        a8, b8 = a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn)
+        one = torch.ones((), device=dev, dtype=torch.float32)
+        ms = timed(lambda: (torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16), 0)[1],
+                   reps=3, warm=1)
+        lib_gemm["e4m3_tensor_scaled_TFLOPs"] = round(2 * Mr * Nr * Kr / (ms / 1e3) / 1e12, 1)
+    except Exception as e:  # the library may not offer this product on the installed stack
+        lib_gemm["e4m3_tensor_scaled_TFLOPs"] = None
+        lib_gemm["e4m3_error"] = str(e)[:200]
+    out["library_dense_gemm"] = lib_gemm
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -351,6 +459,10 @@ def main():
     M.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.ceilings:
+        print(json.dumps({"ceilings": run_ceilings(torch, dev), "device": torch.cuda.get_device_name(dev)}),
+              flush=True)
+        return
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -3,7 +3,9 @@
     python -m sparse_moe_layer_sigmoid_amd.build
 
 Every ``csrc/*.hip`` file is compiled to an object with hipcc (in parallel), then linked
-into ``sparse_moe_layer_sigmoid_amd/libmoe.so``.  Packed-FP32 instruction selection is
+into ``sparse_moe_layer_sigmoid_amd/libmoe.so``.  The ceiling micro-benchmarks
+(``ceilings/ceilings.hip``, measurement code driven by ``bench.py --ceilings``, not part of
+the layer) go into their own ``libmoe_ceilings.so``.  Packed-FP32 instruction selection is
 switched off for the device code (``-packed-fp32-ops``).
 """
 from __future__ import annotations
@@ -19,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libmoe.so")
+CEILINGS_SRC = os.path.join(PKG, "ceilings", "ceilings.hip")
+CEILINGS_LIB = os.path.join(PKG, "libmoe_ceilings.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -50,13 +54,15 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         s, o = pair
         return _run([HIPCC, *DEVICE_FLAGS, "-c", s, "-o", o])
 
+    ceil_obj = os.path.join(BUILD_DIR, "ceilings.o")
     with ThreadPoolExecutor(jobs) as ex:
-        logs = list(ex.map(compile_one, zip(srcs, objs)))
-    tmp = LIB_PATH + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB_PATH)
+        logs = list(ex.map(compile_one, zip(srcs + [CEILINGS_SRC], objs + [ceil_obj])))
+    for out, ins in ((LIB_PATH, objs), (CEILINGS_LIB, [ceil_obj])):
+        tmp = out + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *ins])
+        os.replace(tmp, out)
     if verbose:
-        for s, log in zip(srcs, logs):
+        for s, log in zip(srcs + [CEILINGS_SRC], logs):
             if log.strip():
                 print(f"--- {os.path.basename(s)}\n{log}", file=sys.stderr)
     return LIB_PATH

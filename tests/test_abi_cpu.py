@@ -212,3 +212,28 @@ def test_package_does_not_import_the_oracle():
             "assert not bad, bad")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
+
+
+def test_ceilings_library_exports_and_rejects():
+    """The ceiling micro-benchmarks (measurement code, their own library): every probe is
+    exported and refuses bad arguments on the host, before any launch."""
+    path = os.path.join(ROOT, "sparse_moe_layer_sigmoid_amd", "libmoe_ceilings.so")
+    if not os.path.exists(path):
+        pytest.skip("libmoe_ceilings.so not built")
+    lib = ctypes.CDLL(path)
+    P, S, I32, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int64
+    lib.moe_ceil_hbm_read.argtypes = [P, S, P, S, I32, P]
+    lib.moe_ceil_dma_read.argtypes = [P, I64, I32, P, S, I32, P]
+    lib.moe_ceil_lds_read.argtypes = [I32, I32, P, P, S, I32, P]
+    lib.moe_ceil_mfma.argtypes = [I32, I32, P, P, S, I32, P]
+    lib.moe_ceil_valu.argtypes = [I32, P, P, S, I32, P]
+    big = 1 << 20
+    assert lib.moe_ceil_hbm_read(16, 1000, 16, big, 4, None) == -1  # bytes not a multiple of 16
+    assert lib.moe_ceil_hbm_read(16, 1024, 16, 100, 4, None) == -1  # sink too small
+    assert lib.moe_ceil_dma_read(16, 300, 128, 16, big, 4, None) == -1  # rows not a multiple of 256
+    assert lib.moe_ceil_dma_read(16, 256, 100, 16, big, 4, None) == -1  # row bytes not a multiple of 128
+    assert lib.moe_ceil_lds_read(4, 16, 16, 16, big, 4, None) == -1  # width
+    assert lib.moe_ceil_lds_read(16, 20, 16, 16, big, 4, None) == -1  # iters not a multiple of 16
+    assert lib.moe_ceil_mfma(3, 16, 16, 16, big, 4, None) == -1  # kind
+    assert lib.moe_ceil_mfma(0, 16, None, 16, big, 4, None) == -1  # cycles
+    assert lib.moe_ceil_valu(0, 16, 16, big, 4, None) == -1  # iters

@@ -126,20 +126,24 @@ def test_route_exact_ties_take_the_fp64_path(ng, tg):
 
 
 def test_route_bias_changes_selection_not_gates():
+    """A large bias on one expert forces it into every selection, while the gates stay the
+    normalised original affinities: both routings against the oracle's, and the forced
+    expert's gate against the oracle's unbiased affinity."""
     T, d, N, K = 128, 256, 16, 2
-    x = I.gen_normal(11, (T, d), 1.0).to(DEV)
-    wr = I.gen_normal(12, (N, d), 0.05).to(DEV)
-    b0 = torch.zeros(N, dtype=torch.float32, device=DEV)
-    b1 = b0.clone()
+    x = I.gen_normal(11, (T, d), 1.0)
+    wr = I.gen_normal(12, (N, d), 0.05)
+    b0 = np.zeros(N, np.float32)
+    b1 = b0.copy()
     b1[7] = 10.0  # expert 7 is forced into every token's selection
-    i0, g0, _, s0 = M().moe_route(x, wr, b0, K, want_scores=True)
-    i1, g1, c1, _ = M().moe_route(x, wr, b1, K)
-    assert bool((i1[:, 0] == 7).all()) and int(c1[7]) == T
-    s = s0.cpu().numpy()
-    i1n, g1n = i1.cpu().numpy(), g1.cpu().numpy()
-    for t in range(T):
-        sel = i1n[t]
-        np.testing.assert_allclose(g1n[t], s[t, sel] / s[t, sel].sum(), rtol=0, atol=1e-6)
+    for b in (b0, b1):
+        i, g, c, s = M().moe_route(x.to(DEV), wr.to(DEV), torch.from_numpy(b).to(DEV), K, want_scores=True)
+        r = O.route(np64(x), np64(wr), b, K)
+        check_route(i, g, c, s, r, N, K)
+    assert bool((i[:, 0] == 7).all()) and int(c[7]) == T
+    s0 = O.route(np64(x), np64(wr), b0, K)["s"]
+    other = i.cpu().numpy()[:, 1]  # the device's second pick (valid even inside the tie window)
+    want7 = s0[:, 7] / (s0[:, 7] + s0[np.arange(T), other])
+    assert np.abs(g.cpu().numpy()[:, 0] - want7).max() <= 1e-6
 
 
 def test_route_empty_and_extremes():
