@@ -360,12 +360,32 @@ moe_status moe_swiglu_backward(const float* ac, const float* dh, int64_t rows, i
  *               dst_cols[g+1] - dst_cols[g] >= the segment's length, dst_cols[n_segments] =
  *               total_cols
  *   dst         device bf16 [cols, ld_dst] out (columns [0, total_cols) written)
- * Limits: n_segments >= 1; cols and total_cols multiples of 8; leading dimensions keep rows
- * 16-byte aligned.  (Used for the Wgrad operands and, once, for transposed weight copies.) */
+ * Limits: n_segments >= 1; cols and total_cols multiples of 8; with seg_stride > 0 the
+ * dst_cols entries are multiples of 8; leading dimensions keep rows 16-byte aligned.  (Used for
+ * the bf16 Wgrad operands and, once, for transposed weight copies.) */
 moe_status moe_segment_transpose(const uint16_t* src, int64_t ld_src, const int32_t* src_rows,
                                  const int32_t* seg_offsets, const int32_t* dst_cols,
                                  int n_segments, int cols, int total_cols, uint16_t* dst,
                                  int64_t ld_dst, int64_t seg_stride, hipStream_t stream);
+
+/* moe_segment_transpose_fp8 -- the Wgrad operands of the FP8 path ("FP8 混合精度訓練": Wgrad in
+ * E4M3 on transposed operands; "考察" asks for the transposition and the quantisation to be
+ * fused): segment g's rows become block g of q, [n_segments][cols][width] E4M3 codes, element
+ * (c, i) = source row seg_offsets[g] + i (through src_rows if not NULL), channel c, for i below
+ * the segment's length and zero beyond, quantised as fp8_quant_1x128 / fp8_quant_128x128 would
+ * quantise that bf16 block matrix (the same scales and codes, bit for bit):
+ *   block_scales = 0: 1x128 along the width; scale [n_segments * cols][width / 128] (the A
+ *                     operand of a Wgrad GEMM, the [n_segments * cols, width] view);
+ *   block_scales = 1: 128x128 blocks; scale [n_segments][cols / 128][width / 128] (its B operand).
+ *   src         device bf16, rows of `cols` elements, leading dimension ld_src
+ *   src_rows    device i32 gather index per logical row, or NULL
+ *   seg_offsets device i32 [n_segments + 1], non-decreasing; each segment at most `width` rows
+ *   q           device u8 [n_segments][cols][width] out;  scale device f32 out (above)
+ * Limits: n_segments >= 1; cols and width positive multiples of 128; ld_src >= cols, a multiple
+ * of 8; src 16-byte, q 8-byte, scale 4-byte aligned. */
+moe_status moe_segment_transpose_fp8(const uint16_t* src, int64_t ld_src, const int32_t* src_rows,
+                                     const int32_t* seg_offsets, int n_segments, int cols, int width,
+                                     int block_scales, uint8_t* q, float* scale, hipStream_t stream);
 
 /* moe_router_wgrad -- dW_r[e] = sum over expert e's sorted rows r of du_row[r] x[sorted_token[r]]
  * (fp32, rows in order).

@@ -24,7 +24,8 @@ EXPORTS = (
     "moe_permute_workspace_size", "moe_permute",
     "fp8_quant_1x128", "fp8_quant_128x128", "fp8_quant_1x128_e8m0", "fp8_quant_128x128_e8m0", "fp8_dequant_1x128",
     "moe_grouped_gemm_workspace_size", "moe_grouped_gemm", "moe_combine", "moe_bias_update",
-    "moe_combine_backward", "moe_swiglu_backward", "moe_segment_transpose", "moe_router_wgrad",
+    "moe_combine_backward", "moe_swiglu_backward", "moe_segment_transpose", "moe_segment_transpose_fp8",
+    "moe_router_wgrad",
 )
 
 _p = ctypes.c_void_p
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.moe_swiglu_backward.argtypes = [_p, _p, _i64, _i, _p, _p]
         L.moe_segment_transpose.restype = _i
         L.moe_segment_transpose.argtypes = [_p, _i64, _p, _p, _p, _i, _i, _i, _p, _i64, _i64, _p]
+        L.moe_segment_transpose_fp8.restype = _i
+        L.moe_segment_transpose_fp8.argtypes = [_p, _i64, _p, _p, _i, _i, _i, _i, _p, _p, _p]
         L.moe_router_wgrad.restype = _i
         L.moe_router_wgrad.argtypes = [_p, _p, _p, _p, _i, _i, _p, _p]
         _LIB = L
@@ -398,6 +401,26 @@ def moe_segment_transpose(src, seg_offsets, dst_cols, total_cols: int, src_rows=
                                      C, total_cols, _ptr(dst), ld, C * width if width else 0, _stream(src))
     _check("moe_segment_transpose", st)
     return dst
+
+
+def moe_segment_transpose_fp8(src, seg_offsets, width: int, src_rows=None, block_scales: bool = False):
+    """Row segments of src [*, C] (gathered through src_rows if given) -> E4M3 blocks q [G, C, width]
+    (zero-padded past each segment) with 1x128 scales along each block row ([G * C, width / 128],
+    block_scales=False) or one scale per 128x128 block ([G, C / 128, width / 128])."""
+    _dev(src, torch.bfloat16, "src", contiguous=False)
+    if src.stride(-1) != 1:
+        raise ValueError("rows of src must be contiguous")
+    C = src.shape[1]
+    G = seg_offsets.numel() - 1
+    q = torch.empty((G, C, width), dtype=torch.uint8, device=src.device)
+    if block_scales:
+        scale = torch.empty((G, C // 128, width // 128), dtype=torch.float32, device=src.device)
+    else:
+        scale = torch.empty((G * C, width // 128), dtype=torch.float32, device=src.device)
+    st = lib().moe_segment_transpose_fp8(_ptr(src), src.stride(0), _ptr(src_rows), _ptr(seg_offsets), G, C, width,
+                                         1 if block_scales else 0, _ptr(q), _ptr(scale), _stream(src))
+    _check("moe_segment_transpose_fp8", st)
+    return q, scale
 
 
 def moe_router_wgrad(x, sorted_token, expert_offsets, du_row, n_experts: int, out=None):

@@ -15,12 +15,18 @@
 //    column blocks of its transpose, each padded with zero columns to a given start (or, with
 //    a segment stride, separate zero-padded [cols, width] blocks), so each expert's
 //    weight-gradient GEMM reduces over its own rows with K-contiguous operands, and equal-width
-//    blocks let one grouped GEMM cover every expert.  64 x 64 tiles through LDS; both the loads
-//    and the stores are 16-byte and coalesced.
+//    blocks let one grouped GEMM cover every expert.  128 x 128 tiles, each lane an 8 x 8 block
+//    transposed in registers; 16-byte loads and stores.
+//  * moe_segment_transpose_fp8: the same into equal-width blocks, quantised to E4M3 on the way
+//    ("FP8 混合精度訓練": Wgrad runs in FP8 on transposed operands, and the report's "考察" asks
+//    for the transposition and the quantisation to be fused) with the 1x128 scales along each
+//    block row or one scale per 128x128 block, the codes those quantisers give on the bf16
+//    transpose.
 //  * moe_router_wgrad: dW_r[e] = sum over e's sorted rows r of du_row[r] * x[token(r)], one
 //    workgroup per (expert, 2048 columns), rows in order (deterministic).
 #include "abi_common.h"
 #include "device_common.h"
+#include "quant_common.h"
 
 namespace moe {
 namespace {
@@ -127,72 +133,129 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(const float* __res
                                               f32_to_bf16_rne(dc[2]) | (f32_to_bf16_rne(dc[3]) << 16)};
 }
 
-// Output column j of the transpose: source row of segment g = the segment whose padded column
-// block holds j, or -1 for a padding column.
-__device__ __forceinline__ int transpose_source(int j, const int32_t* __restrict__ seg, const int32_t* __restrict__ col,
-                                                int G, const int32_t* __restrict__ gather, int* g_out) {
-  int lo = 0, hi = G;  // largest g with col[g] <= j
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (col[mid] <= j) lo = mid;
-    else hi = mid;
-  }
-  *g_out = lo;
-  const int local = j - col[lo];
-  if (local < 0 || local >= seg[lo + 1] - seg[lo]) return -1;
-  const int r = seg[lo] + local;
-  return gather ? gather[r] : r;
+// A workgroup transposes 128 output columns (source rows) x 128 channels; wave w covers
+// channels 32w .. 32w + 31, lane (jb, ch) = (lane & 15, lane >> 4) the 8 output columns
+// 8 jb .. 8 jb + 7 and the 8 channels 32 w + 8 ch .. + 7: it loads 8 source rows of 16 bytes,
+// transposes the 8 x 8 block of bf16 in registers and stores 8 channel rows of 8 values.  A
+// load instruction of the wave covers 16 rows x 64 contiguous bytes, a store instruction 4
+// channel rows x 256 (bf16) or 128 (E4M3) contiguous bytes; no LDS.
+
+// Source row of output column j in segment block g (block start `start`), or -1 for a padding
+// column.
+__device__ __forceinline__ int column_source(int j, int g, int start, const int32_t* __restrict__ seg,
+                                             const int32_t* __restrict__ gather) {
+  const int r0 = seg[g], i = j - start;
+  if (i < 0 || i >= seg[g + 1] - r0) return -1;
+  return gather ? gather[r0 + i] : r0 + i;
 }
 
-// 64 output columns x 64 channels per workgroup.  Loads: row (output column) jl, 16-byte chunk
-// ch of its 64 channels; stores: channel row cl, 16-byte chunk of 8 output columns.
+// v[r] = 8 bf16 channels of source row r  ->  o[i] = 8 bf16 output columns of channel i.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&v)[8], u32x4 (&o)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int w = i >> 1, sh = (i & 1) * 16;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      o[i][k] = ((v[2 * k][w] >> sh) & 0xffffu) | (((v[2 * k + 1][w] >> sh) & 0xffffu) << 16);
+  }
+}
+
+__device__ __forceinline__ void load_rows(const uint16_t* __restrict__ src, int64_t lds, const int (&srow)[8], int c,
+                                          bool cvalid, u32x4 (&v)[8]) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    v[r] = u32x4{0u, 0u, 0u, 0u};
+    if (cvalid && srow[r] >= 0) v[r] = *(const u32x4*)(src + (int64_t)srow[r] * lds + c);
+  }
+}
+
+// bf16 output, any column blocks (dst_cols multiples of 8).
 __global__ __launch_bounds__(256) void segment_transpose_kernel(const uint16_t* __restrict__ src, int64_t lds,
                                                                 const int32_t* __restrict__ gather,
                                                                 const int32_t* __restrict__ seg,
                                                                 const int32_t* __restrict__ col, int G, int C,
                                                                 int total, uint16_t* __restrict__ dst, int64_t ldd,
                                                                 int64_t seg_stride) {
-  __shared__ uint16_t tile[64][64 + 8];
-  const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int e = tid + 256 * h;
-    const int jl = e >> 3, ch = e & 7;
-    const int j = j0 + jl;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (j < total && c0 + ch * 8 < C) {
-      int g;
-      const int s = transpose_source(j, seg, col, G, gather, &g);
-      if (s >= 0) v = *(const u32x4*)(src + (int64_t)s * lds + c0 + ch * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tile[jl][ch * 8 + 2 * i] = (uint16_t)(v[i] & 0xffffu);
-      tile[jl][ch * 8 + 2 * i + 1] = (uint16_t)(v[i] >> 16);
-    }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int jb = lane & 15, ch = lane >> 4;
+  const int j = blockIdx.x * 128 + jb * 8;
+  const int c = blockIdx.y * 128 + w * 32 + ch * 8;
+  if (j >= total) return;
+  int lo = 0, hi = G;  // the segment block holding column j: the largest g with col[g] <= j
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (col[mid] <= j) lo = mid;
+    else hi = mid;
   }
-  __syncthreads();
+  // the lane's 8 columns: a block boundary inside them moves the later ones to the next block
+  // (blocked output needs block starts that are multiples of 8, so it never happens there)
+  int srow[8];
+  int g = lo;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int e = tid + 256 * h;
-    const int cl = e >> 3, jc = e & 7;
-    const int c = c0 + cl, j = j0 + jc * 8;
-    if (c < C && j < total) {
-      u32x4 o;
+  for (int r = 0; r < 8; ++r) {
+    while (g + 1 < G && col[g + 1] <= j + r) ++g;
+    srow[r] = column_source(j + r, g, col[g], seg, gather);
+  }
+  u32x4 v[8], o[8];
+  load_rows(src, lds, srow, c, c < C, v);
+  transpose8x8(v, o);
+  const int64_t at = seg_stride > 0 ? (int64_t)lo * seg_stride + (j - col[lo]) : (int64_t)j;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = (uint32_t)tile[jc * 8 + 2 * i][cl] | ((uint32_t)tile[jc * 8 + 2 * i + 1][cl] << 16);
-      int64_t at = (int64_t)c * ldd + j;
-      if (seg_stride > 0) {  // blocked: segment g's block at g * seg_stride, columns from its start
-        int lo = 0, hi = G;
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (col[mid] <= j) lo = mid;
-          else hi = mid;
-        }
-        at = (int64_t)lo * seg_stride + (int64_t)c * ldd + (j - col[lo]);
-      }
-      *(u32x4*)(dst + at) = o;
+  for (int i = 0; i < 8; ++i)
+    if (c + i < C) *(u32x4*)(dst + at + (int64_t)(c + i) * ldd) = o[i];
+}
+
+// E4M3 output in equal-width blocks [G][C][width] with the scales of fp8_quant_1x128 applied
+// along each block row (BLOCK = false: scale [G * C][width / 128]) or of fp8_quant_128x128 per
+// block (BLOCK = true: scale [G][C / 128][width / 128]), the same rule and divisions as those
+// kernels, so the codes equal quantising the bf16 transpose.  The workgroup's 128 columns are
+// one 128-column tile of one block (width % 128 == 0), its 128 channels one 128-row block.
+template <bool BLOCK>
+__global__ __launch_bounds__(256) void segment_transpose_fp8_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                                    const int32_t* __restrict__ gather,
+                                                                    const int32_t* __restrict__ seg, int C, int width,
+                                                                    uint8_t* __restrict__ q, float* __restrict__ scale) {
+  __shared__ float red[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int jb = lane & 15, ch = lane >> 4;
+  const int tiles = width / 128;
+  const int g = blockIdx.x / tiles, tile = blockIdx.x - g * tiles;
+  const int jl = tile * 128 + jb * 8;  // column within the block
+  const int c = blockIdx.y * 128 + w * 32 + ch * 8;
+  int srow[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) srow[r] = column_source(jl + r, g, 0, seg, gather);
+  u32x4 v[8], o[8];
+  load_rows(src, lds, srow, c, true, v);
+  transpose8x8(v, o);
+  float f[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) unpack_bf16x8(o[i], f[i]);
+  uint8_t* qb = q + ((int64_t)g * C + c) * width + jl;
+  if constexpr (BLOCK) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(f[i][k]));
+    amax = wave_max(amax);
+    if (lane == 0) red[w] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = (amax == 0.f) ? 1.0f : amax / 448.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(u32x2*)(qb + (int64_t)i * width) = encode8(f[i], s);
+    if (threadIdx.x == 0) scale[((int64_t)g * (C / 128) + blockIdx.y) * tiles + tile] = s;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float amax = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(f[i][k]));
+      amax = max16(amax);  // the 16 lanes of this channel row hold its 128 columns
+      const float s = (amax == 0.f) ? 1.0f : amax / 448.0f;
+      *(u32x2*)(qb + (int64_t)i * width) = encode8(f[i], s);
+      if (jb == 0) scale[((int64_t)g * C + c + i) * tiles + tile] = s;
     }
   }
 }
@@ -279,11 +342,39 @@ extern "C" moe_status moe_segment_transpose(const uint16_t* src, int64_t ld_src,
               MOE_ERR_ALIGN, "moe_segment_transpose: ld_src=%lld ld_dst=%lld must keep rows 16-byte aligned",
               (long long)ld_src, (long long)ld_dst);
   if (total_cols > 0) {
-    const dim3 grid((total_cols + 63) / 64, (cols + 63) / 64);
+    const dim3 grid((total_cols + 127) / 128, (cols + 127) / 128);
     segment_transpose_kernel<<<grid, 256, 0, stream>>>(src, ld_src, src_rows, seg_offsets, dst_cols, n_segments, cols,
                                                        total_cols, dst, ld_dst, seg_stride);
   }
   return check_launch("moe_segment_transpose");
+}
+
+extern "C" moe_status moe_segment_transpose_fp8(const uint16_t* src, int64_t ld_src, const int32_t* src_rows,
+                                                const int32_t* seg_offsets, int n_segments, int cols, int width,
+                                                int block_scales, uint8_t* q, float* scale, hipStream_t stream) {
+  using namespace moe;
+  clear_error();
+  MOE_REQUIRE(src && seg_offsets && q && scale, MOE_ERR_NULL, "moe_segment_transpose_fp8: a required pointer is NULL");
+  MOE_REQUIRE(n_segments >= 1 && cols >= 128 && cols % 128 == 0 && cols / 128 <= 65535 && width >= 128 &&
+                  width % 128 == 0 && (block_scales == 0 || block_scales == 1) &&
+                  (int64_t)n_segments * (width / 128) < ((int64_t)1 << 31),
+              MOE_ERR_SHAPE,
+              "moe_segment_transpose_fp8: n_segments=%d cols=%d width=%d (multiples of 128) block_scales=%d (0 or 1)",
+              n_segments, cols, width, block_scales);
+  MOE_REQUIRE(ld_src >= cols && ld_src % 8 == 0 && aligned16(src) && ((uintptr_t)q & 7u) == 0 &&
+                  ((uintptr_t)scale & 3u) == 0,
+              MOE_ERR_ALIGN,
+              "moe_segment_transpose_fp8: ld_src=%lld (>= cols, a multiple of 8), src 16-byte, q 8-byte and scale "
+              "4-byte aligned",
+              (long long)ld_src);
+  const dim3 grid((unsigned)((int64_t)n_segments * (width / 128)), cols / 128);
+  if (block_scales)
+    segment_transpose_fp8_kernel<true><<<grid, 256, 0, stream>>>(src, ld_src, src_rows, seg_offsets, cols, width, q,
+                                                                 scale);
+  else
+    segment_transpose_fp8_kernel<false><<<grid, 256, 0, stream>>>(src, ld_src, src_rows, seg_offsets, cols, width, q,
+                                                                  scale);
+  return check_launch("moe_segment_transpose_fp8");
 }
 
 extern "C" moe_status moe_router_wgrad(const uint16_t* x, const int32_t* sorted_token, const int32_t* expert_offsets,

@@ -16,18 +16,10 @@
 // reduced with lane shuffles (16 lanes per 1x128 tile) or shuffles + LDS (128x128 block).
 #include "abi_common.h"
 #include "device_common.h"
+#include "quant_common.h"
 
 namespace moe {
 namespace {
-
-__device__ __forceinline__ u32x2 encode8(const float f[8], float s) {
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(f[i] / s) << (8 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(f[4 + i] / s) << (8 * i);
-  return u32x2{lo, hi};
-}
 
 // The same with a power-of-two scale: exact products by 2^-k.
 __device__ __forceinline__ u32x2 encode8_pow2(const float f[8], float inv) {

@@ -181,16 +181,8 @@ class MoELayer:
         kq = 128 if fp8 else 64  # K granule of the GEMM
         kmax = max(kq, (int(lens[:N].max()) + kq - 1) // kq * kq)
         kp_s = (int(lens[N]) + kq - 1) // kq * kq
-        cols_r = torch.arange(0, (N + 1) * kmax, kmax, dtype=torch.int32, device=dev)
-        cols_s = torch.tensor([0, kp_s], dtype=torch.int32, device=dev)
         seg_r, seg_s = offs[:N + 1], offs[N:N + 2]
-        T_ = lambda src, seg, cols, total, width=0, rows_=None: L.moe_segment_transpose(
-            src, seg, cols, total, src_rows=rows_, width=width)
         h = L.fp8_dequant_1x128(buf["h"], buf["hs"]) if fp8 else buf["h"]
-        dyT = T_(dy, seg_r, cols_r, N * kmax, kmax)                 # [N, d, kmax]
-        hT = T_(h, seg_r, cols_r, N * kmax, kmax)                   # [N, I, kmax]
-        dacT = T_(dac, seg_r, cols_r, N * kmax, kmax)               # [N, 2I, kmax]
-        xT = T_(x, seg_r, cols_r, N * kmax, kmax, st_)              # [N, d, kmax]
         grads = grads or {}
         dw2 = grads.get("dw2")
         dw13 = grads.get("dw13")
@@ -200,27 +192,30 @@ class MoELayer:
             dw13 = torch.empty((G, 2 * I, d), dtype=torch.float32, device=dev)
         g_d = torch.arange(0, (N + 1) * d, d, dtype=torch.int32, device=dev)
         g_2i = torch.arange(0, (N + 1) * 2 * I, 2 * I, dtype=torch.int32, device=dev)
-        def wgrad(a_t, b_t, offsets, n_groups, m, out):
-            """out = A . B^T per group: A [n_groups * rows, k] (1x128 along k on the FP8 path),
-            B [n_groups, cols, k] (128x128 blocks)."""
-            if fp8:
-                aq, as_ = q1(a_t)
-                bq, bs = L.fp8_quant_128x128(b_t)
-                L.moe_grouped_gemm(aq, bq, offsets, 0, n_groups, m, out, a_scale=as_, w_scale=bs)
-                if keep:
-                    extra.setdefault("wgrad_operands", []).append((aq, as_, bq, bs))
-            else:
-                L.moe_grouped_gemm(a_t, b_t, offsets, 0, n_groups, m, out)
 
-        wgrad(dyT.view(N * d, kmax), hT, g_d, N, N * d, dw2[:N].view(N * d, I))
-        wgrad(dacT.view(N * 2 * I, kmax), xT, g_2i, N, N * 2 * I, dw13[:N].view(N * 2 * I, d))
+        def wgrad(a_src, b_src, seg, width, rows_b, n_groups, offsets, out):
+            """out[g] = A_g^T B_g over segment g's rows: A = a_src rows, B = b_src rows (gathered
+            through rows_b), both transposed into zero-padded blocks of `width` columns; on the FP8
+            path quantised on the way (A 1x128 along the rows, B in 128x128 blocks)."""
+            C = a_src.shape[1]
+            if fp8:
+                aq, as_ = L.moe_segment_transpose_fp8(a_src, seg, width)
+                bq, bs = L.moe_segment_transpose_fp8(b_src, seg, width, src_rows=rows_b, block_scales=True)
+                L.moe_grouped_gemm(aq.view(n_groups * C, width), bq, offsets, 0, n_groups, n_groups * C, out,
+                                   a_scale=as_.view(n_groups * C, width // 128), w_scale=bs)
+                if keep:
+                    extra.setdefault("wgrad_operands", []).append((aq.view(n_groups * C, width), as_, bq, bs))
+            else:
+                cols = torch.arange(0, (n_groups + 1) * width, width, dtype=torch.int32, device=dev)
+                at = L.moe_segment_transpose(a_src, seg, cols, n_groups * width, width=width)
+                bt = L.moe_segment_transpose(b_src, seg, cols, n_groups * width, src_rows=rows_b, width=width)
+                L.moe_grouped_gemm(at.view(n_groups * C, width), bt, offsets, 0, n_groups, n_groups * C, out)
+
+        wgrad(dy, h, seg_r, kmax, None, N, g_d, dw2[:N].view(N * d, I))
+        wgrad(dac, x, seg_r, kmax, st_, N, g_2i, dw13[:N].view(N * 2 * I, d))
         if kp_s > 0:
-            dyT_s = T_(dy, seg_s, cols_s, kp_s)                     # [d, kp_s]
-            hT_s = T_(h, seg_s, cols_s, kp_s)
-            dacT_s = T_(dac, seg_s, cols_s, kp_s)
-            xT_s = T_(x, seg_s, cols_s, kp_s, 0, st_)
-            wgrad(dyT_s, hT_s.unsqueeze(0), g_d[:2], 1, d, dw2[N])
-            wgrad(dacT_s, xT_s.unsqueeze(0), g_2i[:2], 1, 2 * I, dw13[N])
+            wgrad(dy, h, seg_s, kp_s, None, 1, g_d[:2], dw2[N])
+            wgrad(dac, x, seg_s, kp_s, st_, 1, g_2i[:2], dw13[N])
         else:
             dw2[N].zero_()
             dw13[N].zero_()

@@ -166,6 +166,18 @@ def test_backward_entry_points_reject():
     _rejects(lib, "moe_segment_transpose", st(ld_src=32), 4)
     _rejects(lib, "moe_segment_transpose", st(ld_dst=64), 4)
     _rejects(lib, "moe_segment_transpose", st(dst=P(8)), 4)
+    # moe_segment_transpose_fp8(src, ld_src, src_rows, seg_offsets, n_seg, cols, width, block_scales, q, scale,
+    #                           stream)
+    sf = lambda src=P(16), ld_src=128, n=2, cols=128, width=128, bs=0, q=P(16), sc=P(16): (
+        src, ld_src, None, P(16), n, cols, width, bs, q, sc, None)
+    _rejects(lib, "moe_segment_transpose_fp8", sf(q=None), 1)
+    _rejects(lib, "moe_segment_transpose_fp8", sf(n=0), 2)
+    _rejects(lib, "moe_segment_transpose_fp8", sf(cols=64), 2)
+    _rejects(lib, "moe_segment_transpose_fp8", sf(width=192), 2)
+    _rejects(lib, "moe_segment_transpose_fp8", sf(bs=2), 2)
+    _rejects(lib, "moe_segment_transpose_fp8", sf(ld_src=64), 4)
+    _rejects(lib, "moe_segment_transpose_fp8", sf(src=P(8)), 4)
+    _rejects(lib, "moe_segment_transpose_fp8", sf(q=P(4)), 4)
     # moe_router_wgrad(x, sorted_token, expert_offsets, du_row, n_experts, d, dw_router, stream)
     _rejects(lib, "moe_router_wgrad", (P(16), P(16), None, P(16), 8, 16, P(16), None), 1)
     _rejects(lib, "moe_router_wgrad", (P(16), P(16), P(16), P(16), 0, 16, P(16), None), 2)

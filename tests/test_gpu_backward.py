@@ -59,6 +59,55 @@ def test_segment_transpose_blocked():
     assert np.array_equal(out.float().cpu().numpy(), want)
 
 
+def test_segment_transpose_unaligned_blocks():
+    """Column blocks that start at arbitrary columns (the lanes' 8-column groups straddle them)."""
+    lens = np.array([3, 0, 7, 20, 1, 9])
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pads = lens + np.array([2, 1, 0, 5, 3, 4])
+    cols = np.concatenate([[0], np.cumsum(pads)]).astype(np.int32)
+    total = (int(cols[-1]) + 7) // 8 * 8
+    cols[-1] = total
+    C = 24
+    src = I.gen_normal(77, (int(offs[-1]), C), 1.0)
+    out = M()._lib.moe_segment_transpose(src.to(DEV), torch.from_numpy(offs).to(DEV), torch.from_numpy(cols).to(DEV),
+                                         total)
+    want = np.zeros((C, total), dtype=np.float32)
+    s_ = src.float().numpy()
+    for g in range(len(lens)):
+        want[:, cols[g]:cols[g] + lens[g]] = s_[offs[g]:offs[g + 1]].T
+    assert np.array_equal(out.float().cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("block", [False, True])
+def test_segment_transpose_fp8_bitexact(block):
+    """The fused transpose + E4M3 quantisation against the oracle's quantisers applied to the
+    zero-padded transposed blocks: segments of 0, 1, 127, 128, 129 and 300 rows, gathered rows,
+    an all-zero block, outliers."""
+    lens = np.array([0, 1, 127, 128, 129, 300])
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    width, C = 384, 256
+    src = I.gen_normal(78, (900, C), 1.0).float().numpy()
+    src[5, :] *= 1e-30   # tiny values
+    src[17, 40] = 900.0  # an outlier
+    src = torch.from_numpy(src).to(torch.bfloat16)
+    gather = np.random.default_rng(6).integers(0, 900, int(offs[-1])).astype(np.int32)
+    q, sc = M()._lib.moe_segment_transpose_fp8(src.to(DEV), torch.from_numpy(offs).to(DEV), width,
+                                               src_rows=torch.from_numpy(gather).to(DEV), block_scales=block)
+    s_ = src.float().numpy()
+    blocks = np.zeros((len(lens), C, width), dtype=np.float32)
+    for g in range(len(lens)):
+        blocks[g, :, :lens[g]] = s_[gather[offs[g]:offs[g + 1]]].T
+    if block:
+        for g in range(len(lens)):
+            wq, ws = O.quant_128x128(blocks[g])
+            assert np.array_equal(q[g].cpu().numpy(), wq), g
+            assert np.array_equal(sc[g].cpu().numpy(), ws), g
+    else:
+        wq, ws = O.quant_1x128(blocks.reshape(len(lens) * C, width))
+        assert np.array_equal(q.cpu().numpy().reshape(len(lens) * C, width), wq)
+        assert np.array_equal(sc.cpu().numpy(), ws)
+
+
 def test_combine_backward_skipped_pair():
     """A pair the permutation skips (expert id out of range) contributes nothing: du = 0 there,
     the token's other gates are normalised over its valid affinities, no dy row is written."""
