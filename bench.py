@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
                     [--no-cpu-baseline]
     python bench.py --ceilings     (the chip's measured ceilings; no layer)
+    python bench.py --backward-only   (the two backward workloads alone)
 
 One step = one training-mode forward of one DeepSeekMoE layer over one batch of synthetic
 tokens: route -> permute -> [fp8 quantisation of x] -> gate/up grouped GEMM + SwiGLU ->
@@ -50,6 +51,8 @@ def parse():
     p.add_argument("--decode-sweep-steps", type=int, default=20)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first copy 1 GiB device-to-device twice (the reference dispatch for HBM counters)")
+    p.add_argument("--backward-only", action="store_true",
+                   help="time only the two backward workloads (bf16 T = 4096, E4M3 T = 16384) and print one JSON line")
     p.add_argument("--ceilings", action="store_true",
                    help="run the ceiling micro-benchmarks (HBM read, DMA read in the GEMM's pattern, copy, "
                         "LDS read, matrix cores, fp32 FMA) instead of the layer and print one JSON line")
@@ -336,6 +339,67 @@ def decode_skew_sweep(torch, M, I, wr, W13, W2, dev, steps):
     return out
 
 
+def time_backward(torch, layer, x, d_out, n=3):
+    """Mean time of n backward passes of `layer` for the forward of x (kept), after one warm-up
+    pass that also makes the transposed weight copies; the weight gradients are reused."""
+    _, buf = layer.forward(x, keep=True)
+    g = layer.backward(d_out, buf)
+    keep = {"dw13": g["dw13"], "dw2": g["dw2"]}
+    del g
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(n):
+        g = layer.backward(d_out, buf, keep)
+        del g
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / n
+
+
+def backward_record(name, dtype, T, ms, flops, peak, note):
+    return {"workload": name + "_backward", "dtype": dtype, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(T / (ms / 1e3), 1), "tflops": round(flops / (ms / 1e3) / 1e12, 2),
+            f"mfma_frac_{dtype}_peak": round(flops / (ms / 1e3) / 1e12 / peak, 4), "note": note}
+
+
+BWD_NOTE_FP8 = "E4M3 Dgrad and Wgrad (1x128 / 128x128 scales, transposed operands quantised); f32 weight gradients"
+BWD_NOTE_BF16 = ("dx, dW_r, dW13, dW2 (f32); gate/up products recomputed; weight-transpose copies made once, "
+                 "outside the timed region")
+
+
+def layer_flops(c):
+    """Algorithmic flops of one forward: the router (2 T d N) plus a SwiGLU expert (6 d I) per
+    token for each of its top_k routed experts and the shared one."""
+    return 2 * c.T * c.d * c.n_experts + 6 * c.d * c.inter * c.T * (c.top_k + 1)
+
+
+def backward_flops(c):
+    """Algorithmic flops of one backward: twice the forward's (Dgrad and Wgrad) plus the gate/up
+    products recomputed."""
+    return 2 * layer_flops(c) + 4 * c.rows * c.d * c.inter
+
+
+def run_backward_only(torch, M, I, dev):
+    """The two backward workloads alone (bf16 at T = 4096, E4M3 at T = 16384)."""
+    out = []
+    for c, fp8 in ((I.V3_BF16, False), (I.V3_FP8, True)):
+        log(f"[bench] {c.name}_backward: weights ...")
+        W13, W2 = I.gen_all_weights(c, dev)
+        wr = I.gen_router(c).to(torch.bfloat16).to(dev)
+        layer = M.MoELayer(wr, W13, W2, I.gen_bias(c).to(dev), c.top_k, c.n_group, c.topk_group, fp8=fp8)
+        x = I.gen_x(c).to(dev)
+        d_out = I.gen_normal(c.seed + 900, (c.T, c.d), 1.0).to(dev)
+        ms = time_backward(torch, layer, x, d_out)
+        out.append(backward_record(c.name, "fp8" if fp8 else "bf16", c.T, ms, backward_flops(c),
+                                   FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS,
+                                   BWD_NOTE_FP8 if fp8 else BWD_NOTE_BF16))
+        log(f"[bench] {c.name}_backward: {ms:.3f} ms per backward")
+        del layer, W13, W2, x, d_out
+        torch.cuda.empty_cache()
+    return out
+
+
 def run_ceilings(torch, dev):
     """The chip's measured ceilings from libmoe_ceilings.so: each probe warmed up twice, then
     timed five times with HIP events on the stream it runs on (the best run is reported);
@@ -453,7 +517,6 @@ def main():
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload)
         return
     import sparse_moe_layer_sigmoid_amd as M
-    from oracle import moe_oracle as O
     from sparse_moe_layer_sigmoid_amd import inputs as I
 
     M.lib()
@@ -462,6 +525,9 @@ def main():
     if args.ceilings:
         print(json.dumps({"ceilings": run_ceilings(torch, dev), "device": torch.cuda.get_device_name(dev)}),
               flush=True)
+        return
+    if args.backward_only:
+        print(json.dumps({"backward": run_backward_only(torch, M, I, dev)}), flush=True)
         return
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -499,7 +565,7 @@ def main():
     fp8_main = cfg.dtype == "fp8"
     layer, xs_cpu, bias_cpu, counts0, ms, gu_ms, kf = measure(cfg, fp8_main, args.steps, args.warmup,
                                                               scales="e8m0" if main_e8m0 else "f32")
-    flops = O.layer_flops(cfg.T, cfg.d, cfg.n_experts, cfg.top_k, cfg.inter)
+    flops = layer_flops(cfg)
     tok_s = cfg.T / (ms / 1e3)
     gu_bytes = gate_up_bytes(cfg, counts0, fp8_main, 1 if main_e8m0 else 4)
     gu_flop = 4 * cfg.rows * cfg.d * cfg.inter
@@ -537,7 +603,7 @@ def main():
         sec = []
         c3 = I.V3_FP8
         l3, _, _, counts3, ms3, gu3, kf3 = measure(c3, True, max(5, args.steps // 2), 3)
-        f3 = O.layer_flops(c3.T, c3.d, c3.n_experts, c3.top_k, c3.inter)
+        f3 = layer_flops(c3)
         fl3 = 4 * c3.rows * c3.d * c3.inter
         sec.append({"workload": c3.name, "dtype": "fp8", "ms_per_step": round(ms3, 4),
                     "tokens_per_s": round(c3.T / (ms3 / 1e3), 1), "tflops": round(f3 / (ms3 / 1e3) / 1e12, 2),
@@ -547,28 +613,11 @@ def main():
         log(f"[bench] {c3.name}: {ms3:.3f} ms/step, gate/up {gu3:.3f} ms")
         # its backward on the FP8 path (E4M3 Dgrad and Wgrad)
         x3 = I.gen_x(c3).to(dev)
-        _, buf3 = l3.forward(x3, keep=True)
         d3 = I.gen_normal(c3.seed + 900, (c3.T, c3.d), 1.0).to(dev)
-        g3 = l3.backward(d3, buf3)  # warm-up; makes the transposed E4M3 weights once
-        keep3 = {"dw13": g3["dw13"], "dw2": g3["dw2"]}
-        del g3
-        torch.cuda.synchronize()
-        s3, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s3.record()
-        for _ in range(3):
-            g3 = l3.backward(d3, buf3, keep3)
-            del g3
-        e3.record()
-        torch.cuda.synchronize()
-        ms3b = s3.elapsed_time(e3) / 3
-        fb3 = 2 * f3 + 4 * c3.rows * c3.d * c3.inter
-        sec.append({"workload": c3.name + "_backward", "dtype": "fp8", "ms_per_step": round(ms3b, 4),
-                    "tokens_per_s": round(c3.T / (ms3b / 1e3), 1), "tflops": round(fb3 / (ms3b / 1e3) / 1e12, 2),
-                    "mfma_frac_fp8_peak": round(fb3 / (ms3b / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4),
-                    "note": "E4M3 Dgrad and Wgrad (1x128 / 128x128 scales, transposed operands quantised); f32 "
-                            "weight gradients"})
+        ms3b = time_backward(torch, l3, x3, d3)
+        sec.append(backward_record(c3.name, "fp8", c3.T, ms3b, backward_flops(c3), FP8_PEAK_TFLOPS, BWD_NOTE_FP8))
         log(f"[bench] {c3.name}_backward: {ms3b:.3f} ms per backward")
-        del l3, buf3, d3, keep3, x3
+        del l3, d3, x3
         torch.cuda.empty_cache()
         # the same layer with power-of-two (E8M0) tile scales applied by the matrix cores
         l3e, _, _, _, ms3e, gu3e, kf3e = measure(c3, True, max(5, args.steps // 2), 3, scales="e8m0")
@@ -584,33 +633,16 @@ def main():
         # expert's weights for a seeded d_out
         lb = M.MoELayer(wr, W13, W2, bias_cpu.to(dev), cfg.top_k, cfg.n_group, cfg.topk_group)
         xb = xs_cpu[0].to(dev)
-        _, bufb = lb.forward(xb, keep=True)
         d_out = I.gen_normal(cfg.seed + 900, (cfg.T, cfg.d), 1.0).to(dev)
-        gb = lb.backward(d_out, bufb)  # warm-up; makes the transposed weight copies once
-        keep_g = {"dw13": gb["dw13"], "dw2": gb["dw2"]}  # weight gradients reused across steps
-        del gb
-        torch.cuda.synchronize()
-        nb = 3
-        sb, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        sb.record()
-        for _ in range(nb):
-            gb = lb.backward(d_out, bufb, keep_g)
-            del gb
-        eb.record()
-        torch.cuda.synchronize()
-        msb = sb.elapsed_time(eb) / nb
-        fb = 2 * O.layer_flops(cfg.T, cfg.d, cfg.n_experts, cfg.top_k, cfg.inter) + 4 * cfg.rows * cfg.d * cfg.inter
-        sec.append({"workload": cfg.name + "_backward", "dtype": "bf16", "ms_per_step": round(msb, 4),
-                    "tokens_per_s": round(cfg.T / (msb / 1e3), 1), "tflops": round(fb / (msb / 1e3) / 1e12, 2),
-                    "mfma_frac_bf16_peak": round(fb / (msb / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                    "note": "dx, dW_r, dW13, dW2 (f32); gate/up products recomputed; weight-transpose copies made "
-                            "once, outside the timed region"})
+        msb = time_backward(torch, lb, xb, d_out)
+        sec.append(backward_record(cfg.name, "bf16", cfg.T, msb, backward_flops(cfg), BF16_PEAK_TFLOPS,
+                                   BWD_NOTE_BF16))
         log(f"[bench] {cfg.name}_backward: {msb:.3f} ms per backward")
-        del lb, bufb, d_out, keep_g
+        del lb, xb, d_out
         torch.cuda.empty_cache()
         c2 = I.V3_GROUP
         l2, _, _, _, ms2, _, kf2 = measure(c2, False, max(5, args.steps // 2), 3)
-        f2 = O.layer_flops(c2.T, c2.d, c2.n_experts, c2.top_k, c2.inter)
+        f2 = layer_flops(c2)
         sec.append({"workload": c2.name, "dtype": "bf16", "ms_per_step": round(ms2, 4),
                     "tokens_per_s": round(c2.T / (ms2 / 1e3), 1), "tflops": round(f2 / (ms2 / 1e3) / 1e12, 2),
                     "mfma_frac_bf16_peak": round(f2 / (ms2 / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4), "kernels": kf2})
