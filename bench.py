@@ -507,7 +507,7 @@ def run_ceilings(torch, dev):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1 "
+        print(json.dumps({"error": "this implementation runs on one GPU only: --gpus must be 1 "
                           "(the multi-GPU expert-parallel path is a design, not built)"}))
         sys.exit(2)
     import numpy as np

@@ -22,7 +22,7 @@ Sources (the pages this follows; cited by page title and section):
   for quantisation support in hardware), with [TR] "考察" (native tile / block quantisation
   in the matrix unit) -- the power-of-two scale variant below.
 
-Readings taken where the pages are silent (each is listed again in the design doc):
+Readings taken where the pages are silent:
 
 * affinity s = sigmoid(x . e_i) with e_i the i-th router row and no router bias vector;
 * selection on z = s + b, larger z first, equal z -> lower expert index;
