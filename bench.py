@@ -295,7 +295,19 @@ def cpu_baseline(cfg, wr_cpu, bias_cpu, W13_cpu, W2_cpu, budget_s=10.0, max_step
                        f"{cfg.T} tokens, permutation, the SwiGLU FFN of all {cfg.n_experts + 1} experts on their "
                        f"{cfg.T * (cfg.top_k + 1)} rows, combine and bias update per step; {timed:.1f} s of oracle "
                        f"compute"),
-            "seconds_measured": round(timed, 2)}
+            "seconds_measured": round(timed, 2), "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    """The host CPU's model name (first processor entry), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def decode_skew_sweep(torch, M, I, wr, W13, W2, dev, steps):
@@ -504,6 +516,51 @@ def run_ceilings(torch, dev):
     return out
 
 
+def measured_peaks(torch, dev):
+    """A short subset of the ceiling probes, for the bench line's secondary denominators: the
+    HBM read rate of direct-to-LDS DMA in the grouped GEMM's weight pattern (8 GiB) and the
+    bf16 / E4M3 matrix-core rates from registers."""
+    path = os.path.join(ROOT, "sparse_moe_layer_sigmoid_amd", "libmoe_ceilings.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    P, S, I32, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int64
+    lib.moe_ceil_dma_read.argtypes = [P, I64, I32, P, S, I32, P]
+    lib.moe_ceil_mfma.argtypes = [I32, I32, P, P, S, I32, P]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sp = torch.cuda.current_stream().cuda_stream
+    sink = torch.empty(cus * 512, dtype=torch.int32, device=dev)
+    cycles = torch.empty(cus, dtype=torch.int64, device=dev)
+
+    def best_ms(call, reps=5):
+        call()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            rc = call()
+            b.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"ceiling probe returned {rc}")
+            best = a.elapsed_time(b) if best is None else min(best, a.elapsed_time(b))
+        return best
+
+    row_bytes = 7168 * 2
+    rows = (8 << 30) // row_bytes // 256 * 256
+    buf = torch.empty(rows * row_bytes, dtype=torch.uint8, device=dev)
+    ms = best_ms(lambda: lib.moe_ceil_dma_read(buf.data_ptr(), rows, row_bytes, sink.data_ptr(), sink.numel(), cus, sp))
+    out = {"hbm_read_dma_GBs": round(rows * row_bytes / (ms / 1e3) / 1e9, 1)}
+    del buf
+    for kind, name, fl in ((0, "mfma_bf16_TFLOPs", 2 * 16 * 16 * 32), (1, "mfma_e4m3_TFLOPs", 2 * 16 * 16 * 128)):
+        iters = 2048
+        ms = best_ms(lambda: lib.moe_ceil_mfma(kind, iters, cycles.data_ptr(), sink.data_ptr(), sink.numel(), cus, sp))
+        out[name] = round(cus * 8 * iters * 8 * fl / (ms / 1e3) / 1e12, 1)
+    out["source"] = "bench.py measured_peaks (probes of sparse_moe_layer_sigmoid_amd/ceilings/ceilings.hip)"
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -689,6 +746,12 @@ def main():
         del l4, xs4, hist
         sec.append(decode_skew_sweep(torch, M, I, wr, W13, W2, dev, args.decode_sweep_steps))
         line["secondary"] = sec
+        # the chip's measured ceilings as a second denominator for the roofline
+        peaks = measured_peaks(torch, dev)
+        if peaks:
+            line["measured_peaks"] = peaks
+            ref = peaks["mfma_e4m3_TFLOPs"] if fp8_main else peaks["hbm_read_dma_GBs"]
+            line["roofline"]["frac_of_measured_peak"] = round(achieved / ref, 4)
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")

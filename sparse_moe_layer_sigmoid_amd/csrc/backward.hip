@@ -133,12 +133,12 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(const float* __res
                                               f32_to_bf16_rne(dc[2]) | (f32_to_bf16_rne(dc[3]) << 16)};
 }
 
-// A workgroup transposes 128 output columns (source rows) x 128 channels; wave w covers
-// channels 32w .. 32w + 31, lane (jb, ch) = (lane & 15, lane >> 4) the 8 output columns
-// 8 jb .. 8 jb + 7 and the 8 channels 32 w + 8 ch .. + 7: it loads 8 source rows of 16 bytes,
-// transposes the 8 x 8 block of bf16 in registers and stores 8 channel rows of 8 values.  A
-// load instruction of the wave covers 16 rows x 64 contiguous bytes, a store instruction 4
-// channel rows x 256 (bf16) or 128 (E4M3) contiguous bytes; no LDS.
+// A workgroup transposes 128 output columns (source rows) x 128 channels; wave w covers the
+// column half w & 1 and the channel half w >> 1 (64 x 64), lane (jb, ch) = (lane & 7, lane >> 3)
+// the 8 output columns 8 jb .. 8 jb + 7 and the 8 channels 8 ch .. 8 ch + 7 of it: it loads 8
+// source rows of 16 bytes, transposes the 8 x 8 block of bf16 in registers and stores 8 channel
+// rows of 8 values.  A load instruction of the wave covers 8 rows x 128 contiguous bytes, a store
+// instruction 8 channel rows x 128 (bf16) or 64 (E4M3) contiguous bytes; no LDS for the data.
 
 // Source row of output column j in segment block g (block start `start`), or -1 for a padding
 // column.
@@ -177,9 +177,9 @@ __global__ __launch_bounds__(256) void segment_transpose_kernel(const uint16_t* 
                                                                 int total, uint16_t* __restrict__ dst, int64_t ldd,
                                                                 int64_t seg_stride) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int jb = lane & 15, ch = lane >> 4;
-  const int j = blockIdx.x * 128 + jb * 8;
-  const int c = blockIdx.y * 128 + w * 32 + ch * 8;
+  const int jb = lane & 7, ch = lane >> 3;
+  const int j = blockIdx.x * 128 + (w & 1) * 64 + jb * 8;
+  const int c = blockIdx.y * 128 + (w >> 1) * 64 + ch * 8;
   if (j >= total) return;
   int lo = 0, hi = G;  // the segment block holding column j: the largest g with col[g] <= j
   while (hi - lo > 1) {
@@ -215,13 +215,15 @@ __global__ __launch_bounds__(256) void segment_transpose_fp8_kernel(const uint16
                                                                     const int32_t* __restrict__ gather,
                                                                     const int32_t* __restrict__ seg, int C, int width,
                                                                     uint8_t* __restrict__ q, float* __restrict__ scale) {
-  __shared__ float red[4];
+  // BLOCK: the four waves' maxima; else each channel row's maxima over the two column halves
+  __shared__ float red[BLOCK ? 4 : 2 * 128];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int jb = lane & 15, ch = lane >> 4;
+  const int jb = lane & 7, ch = lane >> 3, half = w & 1;
   const int tiles = width / 128;
   const int g = blockIdx.x / tiles, tile = blockIdx.x - g * tiles;
-  const int jl = tile * 128 + jb * 8;  // column within the block
-  const int c = blockIdx.y * 128 + w * 32 + ch * 8;
+  const int jl = tile * 128 + half * 64 + jb * 8;  // column within the block
+  const int cl = (w >> 1) * 64 + ch * 8;            // channel within the workgroup's 128
+  const int c = blockIdx.y * 128 + cl;
   int srow[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) srow[r] = column_source(jl + r, g, 0, seg, gather);
@@ -247,15 +249,24 @@ __global__ __launch_bounds__(256) void segment_transpose_fp8_kernel(const uint16
     for (int i = 0; i < 8; ++i) *(u32x2*)(qb + (int64_t)i * width) = encode8(f[i], s);
     if (threadIdx.x == 0) scale[((int64_t)g * (C / 128) + blockIdx.y) * tiles + tile] = s;
   } else {
+    float amax[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float amax = 0.f;
+      float m = 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(f[i][k]));
-      amax = max16(amax);  // the 16 lanes of this channel row hold its 128 columns
-      const float s = (amax == 0.f) ? 1.0f : amax / 448.0f;
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(f[i][k]));
+#pragma unroll
+      for (int o2 = 1; o2 < 8; o2 <<= 1) m = fmaxf(m, __shfl_xor(m, o2, kWave));  // the 8 lanes of the half row
+      amax[i] = m;
+      if (jb == 0) red[(cl + i) * 2 + half] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float m = fmaxf(amax[i], red[(cl + i) * 2 + (half ^ 1)]);  // with the other column half
+      const float s = (m == 0.f) ? 1.0f : m / 448.0f;
       *(u32x2*)(qb + (int64_t)i * width) = encode8(f[i], s);
-      if (jb == 0) scale[((int64_t)g * C + c + i) * tiles + tile] = s;
+      if (jb == 0 && half == 0) scale[((int64_t)g * C + c + i) * tiles + tile] = s;
     }
   }
 }
