@@ -328,14 +328,18 @@ moe_status moe_bias_update(float* bias, const int32_t* expert_counts, int n_expe
  *             T*top_k + t = d_out[t] (the down projection's input gradient, sorted rows)
  *   du        device f32 [T, top_k] out: router logit gradients of the selected experts
  *   du_row    device f32 [T*top_k] out: du by sorted row (du_row[pair_pos[t,k]] = du[t,k])
+ *   dy_q, dy_scale  NULL, or device u8 [T*(top_k+1), d] and f32 [T*(top_k+1), d/128] out: the
+ *             written dy rows also as E4M3 with 1x128 scales, the codes fp8_quant_1x128 gives on
+ *             them (the FP8 path's Dgrad operand, "FP8 混合精度訓練")
  * dg is accumulated in fp32 in a fixed order; the rest is fp32.  Limits: T >= 0;
- * 1 <= top_k <= min(32, n_experts); d >= 8, d % 8 == 0; routing and permutation as moe_route
- * and moe_permute produce them (valid, distinct experts).  With T == 0 nothing is done. */
+ * 1 <= top_k <= min(32, n_experts); d >= 8, d % 8 == 0 (d % 128 == 0 with dy_q); routing and
+ * permutation as moe_route and moe_permute produce them (valid, distinct experts).  With T == 0
+ * nothing is done. */
 moe_status moe_combine_backward(const uint16_t* d_out, const uint16_t* y_routed,
                                 const int32_t* topk_idx, const float* topk_gate,
                                 const float* scores, const int32_t* pair_pos, int T, int top_k,
                                 int d, int n_experts, uint16_t* dy, float* du, float* du_row,
-                                hipStream_t stream);
+                                uint8_t* dy_q, float* dy_scale, hipStream_t stream);
 
 /* moe_swiglu_backward -- through h = silu(a) c, elementwise over rows x inter:
  *   da = dh c sig(a) (1 + a (1 - sig(a))),  dc = dh a sig(a)   (fp32, stored RNE bf16)
@@ -343,9 +347,11 @@ moe_status moe_combine_backward(const uint16_t* d_out, const uint16_t* y_routed,
  *        (the gate/up GEMM without its SwiGLU epilogue)
  *   dh   device f32 [rows, inter]
  *   dac  device bf16 [rows, 2*inter] out: da | dc
- * Limits: rows >= 0; inter >= 4, inter % 4 == 0. */
+ *   dac_q, dac_scale  NULL, or device u8 [rows, 2*inter] and f32 [rows, 2*inter/128] out: dac
+ *        also as E4M3 with 1x128 scales, the codes fp8_quant_1x128 gives on it
+ * Limits: rows >= 0; inter >= 4, inter % 4 == 0 (inter % 128 == 0 with dac_q). */
 moe_status moe_swiglu_backward(const float* ac, const float* dh, int64_t rows, int inter,
-                               uint16_t* dac, hipStream_t stream);
+                               uint16_t* dac, uint8_t* dac_q, float* dac_scale, hipStream_t stream);
 
 /* moe_segment_transpose -- row segments of a bf16 matrix become zero-padded column blocks of
  * its transpose: for segment g (rows [seg_offsets[g], seg_offsets[g+1]) of the logical

@@ -98,9 +98,9 @@ def lib() -> ctypes.CDLL:
         L.moe_bias_update.restype = _i
         L.moe_bias_update.argtypes = [_p, _p, _i, _i64, _f, _p]
         L.moe_combine_backward.restype = _i
-        L.moe_combine_backward.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _p, _p]
+        L.moe_combine_backward.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p]
         L.moe_swiglu_backward.restype = _i
-        L.moe_swiglu_backward.argtypes = [_p, _p, _i64, _i, _p, _p]
+        L.moe_swiglu_backward.argtypes = [_p, _p, _i64, _i, _p, _p, _p, _p]
         L.moe_segment_transpose.restype = _i
         L.moe_segment_transpose.argtypes = [_p, _i64, _p, _p, _p, _i, _i, _i, _p, _i64, _i64, _p]
         L.moe_segment_transpose_fp8.restype = _i
@@ -351,8 +351,9 @@ def moe_bias_update(bias, expert_counts, total_assignments: int, gamma: float):
 # ----------------------------------------------------------------------------- backward
 
 
-def moe_combine_backward(d_out, y_routed, topk_idx, topk_gate, scores, pair_pos, out=None):
-    """-> (dy bf16 [T*(K+1), d], du f32 [T, K], du_row f32 [T*K])."""
+def moe_combine_backward(d_out, y_routed, topk_idx, topk_gate, scores, pair_pos, out=None, fp8: bool = False):
+    """-> (dy bf16 [T*(K+1), d], du f32 [T, K], du_row f32 [T*K]); with fp8=True also
+    (dy_q u8 [T*(K+1), d], dy_scale f32 [T*(K+1), d/128]), the 1x128 E4M3 form of dy."""
     _dev(d_out, torch.bfloat16, "d_out")
     _dev(y_routed, torch.bfloat16, "y_routed")
     _dev(scores, torch.float32, "scores")
@@ -365,23 +366,32 @@ def moe_combine_backward(d_out, y_routed, topk_idx, topk_gate, scores, pair_pos,
         dy = torch.empty((T * (K + 1), d), dtype=torch.bfloat16, device=dev)
     du = torch.empty((T, K), dtype=torch.float32, device=dev)
     du_row = torch.empty(T * K, dtype=torch.float32, device=dev)
+    dyq = dys = None
+    if fp8:
+        dyq = torch.empty((T * (K + 1), d), dtype=torch.uint8, device=dev)
+        dys = torch.empty((T * (K + 1), d // 128), dtype=torch.float32, device=dev)
     st = lib().moe_combine_backward(_ptr(d_out), _ptr(y_routed), _ptr(topk_idx), _ptr(topk_gate), _ptr(scores),
                                     _ptr(pair_pos), T, K, d, scores.shape[1], _ptr(dy), _ptr(du), _ptr(du_row),
-                                    _stream(d_out))
+                                    _ptr(dyq), _ptr(dys), _stream(d_out))
     _check("moe_combine_backward", st)
-    return dy, du, du_row
+    return (dy, du, du_row, dyq, dys) if fp8 else (dy, du, du_row)
 
 
-def moe_swiglu_backward(ac, dh, dac=None):
-    """ac f32 [rows, 2I] (a | c), dh f32 [rows, I] -> dac bf16 [rows, 2I] (da | dc)."""
+def moe_swiglu_backward(ac, dh, dac=None, fp8: bool = False):
+    """ac f32 [rows, 2I] (a | c), dh f32 [rows, I] -> dac bf16 [rows, 2I] (da | dc); with fp8=True
+    -> (dac, dac_q u8 [rows, 2I], dac_scale f32 [rows, 2I/128]), its 1x128 E4M3 form too."""
     _dev(ac, torch.float32, "ac")
     _dev(dh, torch.float32, "dh")
     rows, I = dh.shape
     if dac is None:
         dac = torch.empty((rows, 2 * I), dtype=torch.bfloat16, device=dh.device)
-    st = lib().moe_swiglu_backward(_ptr(ac), _ptr(dh), rows, I, _ptr(dac), _stream(dh))
+    dq = ds = None
+    if fp8:
+        dq = torch.empty((rows, 2 * I), dtype=torch.uint8, device=dh.device)
+        ds = torch.empty((rows, 2 * I // 128), dtype=torch.float32, device=dh.device)
+    st = lib().moe_swiglu_backward(_ptr(ac), _ptr(dh), rows, I, _ptr(dac), _ptr(dq), _ptr(ds), _stream(dh))
     _check("moe_swiglu_backward", st)
-    return dac
+    return (dac, dq, ds) if fp8 else dac
 
 
 def moe_segment_transpose(src, seg_offsets, dst_cols, total_cols: int, src_rows=None, dst=None, width: int = 0):

@@ -36,7 +36,8 @@ constexpr int kMaxBwdK = 32;
 __global__ __launch_bounds__(256) void combine_backward_kernel(
     const uint16_t* __restrict__ d_out, const uint16_t* __restrict__ y, const int32_t* __restrict__ idx,
     const float* __restrict__ gate, const float* __restrict__ scores, const int32_t* __restrict__ pair_pos, int T,
-    int K, int d, int N, uint16_t* __restrict__ dy, float* __restrict__ du, float* __restrict__ du_row) {
+    int K, int d, int N, uint16_t* __restrict__ dy, float* __restrict__ du, float* __restrict__ du_row,
+    uint8_t* __restrict__ dyq, float* __restrict__ dys) {
   __shared__ int s_p[kMaxBwdK];
   __shared__ float s_g[kMaxBwdK];
   __shared__ float s_part[kMaxBwdK][4];
@@ -52,9 +53,24 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
   for (int k = 0; k < kMaxBwdK; ++k) dot[k] = 0.f;
   const int nc = d / 8;
   const uint16_t* orow = d_out + (int64_t)t * d;
+  // with dyq: each dy row also as E4M3 with 1x128 scales, quantised from its bf16 values as
+  // fp8_quant_1x128 does; the 16 lanes of a 1x128 tile are 16 consecutive chunks (d % 128 == 0,
+  // so whole 16-lane groups share the loop's trip count)
+  auto quant_row = [&](int64_t row, int c, const u32x4& bits) {
+    float q[8];
+    unpack_bf16x8(bits, q);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(q[i]));
+    amax = max16(amax);
+    const float s = (amax == 0.f) ? 1.0f : amax / 448.0f;
+    *(u32x2*)(dyq + row * d + c * 8) = encode8(q, s);
+    if ((c & 15) == 0) dys[row * (d / 128) + c / 16] = s;
+  };
   for (int c = tid; c < nc; c += 256) {
     const u32x4 ov = *(const u32x4*)(orow + c * 8);
     *(u32x4*)(dy + ((int64_t)T * K + t) * d + c * 8) = ov;  // the shared expert's row: d_out itself
+    if (dyq) quant_row((int64_t)T * K + t, c, ov);
     float f[8];
     unpack_bf16x8(ov, f);
 #pragma unroll
@@ -72,6 +88,7 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16_rne(g * f[2 * i]) | (f32_to_bf16_rne(g * f[2 * i + 1]) << 16);
         *(u32x4*)(dy + p * d + c * 8) = o;
+        if (dyq) quant_row(p, c, o);
       }
     }
   }
@@ -111,7 +128,8 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
 
 __global__ __launch_bounds__(256) void swiglu_backward_kernel(const float* __restrict__ ac,
                                                               const float* __restrict__ dh, int64_t n4, int I,
-                                                              uint16_t* __restrict__ dac) {
+                                                              uint16_t* __restrict__ dac, uint8_t* __restrict__ dacq,
+                                                              float* __restrict__ dacs) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // quad of h elements
   if (q >= n4) return;
   const int qi = I / 4;
@@ -127,10 +145,37 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(const float* __res
     dc[e] = g[e] * (a[e] * sg);
     da[e] = g[e] * c[e] * (sg * (1.0f + a[e] * (1.0f - sg)));
   }
-  *(u32x2*)(dac + r * 2 * I + i) = u32x2{f32_to_bf16_rne(da[0]) | (f32_to_bf16_rne(da[1]) << 16),
-                                          f32_to_bf16_rne(da[2]) | (f32_to_bf16_rne(da[3]) << 16)};
-  *(u32x2*)(dac + r * 2 * I + I + i) = u32x2{f32_to_bf16_rne(dc[0]) | (f32_to_bf16_rne(dc[1]) << 16),
-                                              f32_to_bf16_rne(dc[2]) | (f32_to_bf16_rne(dc[3]) << 16)};
+  const u32x2 pa = u32x2{f32_to_bf16_rne(da[0]) | (f32_to_bf16_rne(da[1]) << 16),
+                         f32_to_bf16_rne(da[2]) | (f32_to_bf16_rne(da[3]) << 16)};
+  const u32x2 pc = u32x2{f32_to_bf16_rne(dc[0]) | (f32_to_bf16_rne(dc[1]) << 16),
+                         f32_to_bf16_rne(dc[2]) | (f32_to_bf16_rne(dc[3]) << 16)};
+  *(u32x2*)(dac + r * 2 * I + i) = pa;
+  *(u32x2*)(dac + r * 2 * I + I + i) = pc;
+  if (dacq) {
+    // the 1x128 E4M3 quantisation of the stored bf16 da | dc, as fp8_quant_1x128 does it: the 32
+    // lanes of a tile are 32 consecutive quads of one row (I % 128 == 0, so whole 32-lane groups
+    // share the early exit above)
+    const u32x2 pk[2] = {pa, pc};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        f[2 * e] = bf16_to_f32(pk[h][e] & 0xffffu);
+        f[2 * e + 1] = bf16_to_f32(pk[h][e] >> 16);
+      }
+      float amax = fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3])));
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+      const float s = (amax == 0.f) ? 1.0f : amax / 448.0f;
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w |= f32_to_e4m3(f[e] / s) << (8 * e);
+      const int col = h * I + i;
+      *(uint32_t*)(dacq + r * 2 * I + col) = w;
+      if ((i & 127) == 0) dacs[r * (2 * I / 128) + col / 128] = s;
+    }
+  }
 }
 
 // A workgroup transposes 128 output columns (source rows) x 128 channels; wave w covers the
@@ -301,36 +346,43 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const uint16_t* __res
 extern "C" moe_status moe_combine_backward(const uint16_t* d_out, const uint16_t* y_routed, const int32_t* topk_idx,
                                            const float* topk_gate, const float* scores, const int32_t* pair_pos,
                                            int T, int top_k, int d, int n_experts, uint16_t* dy, float* du,
-                                           float* du_row, hipStream_t stream) {
+                                           float* du_row, uint8_t* dy_q, float* dy_scale, hipStream_t stream) {
   using namespace moe;
   clear_error();
   MOE_REQUIRE(T == 0 || (d_out && y_routed && topk_idx && topk_gate && scores && pair_pos && dy && du && du_row),
               MOE_ERR_NULL, "moe_combine_backward: a required pointer is NULL");
-  MOE_REQUIRE(T >= 0 && top_k >= 1 && top_k <= kMaxBwdK && top_k <= n_experts && d >= 8 && d % 8 == 0, MOE_ERR_SHAPE,
-              "moe_combine_backward: T=%d top_k=%d (1..%d) d=%d (a multiple of 8) n_experts=%d", T, top_k, kMaxBwdK,
-              d, n_experts);
-  MOE_REQUIRE(aligned16(d_out) && aligned16(y_routed) && aligned16(dy), MOE_ERR_ALIGN,
-              "moe_combine_backward: d_out, y_routed and dy must be 16-byte aligned");
+  MOE_REQUIRE(!dy_q == !dy_scale, MOE_ERR_NULL, "moe_combine_backward: dy_q and dy_scale go together");
+  MOE_REQUIRE(T >= 0 && top_k >= 1 && top_k <= kMaxBwdK && top_k <= n_experts && d >= 8 && d % 8 == 0 &&
+                  (!dy_q || d % 128 == 0),
+              MOE_ERR_SHAPE,
+              "moe_combine_backward: T=%d top_k=%d (1..%d) d=%d (a multiple of 8; of 128 with dy_q) n_experts=%d", T,
+              top_k, kMaxBwdK, d, n_experts);
+  MOE_REQUIRE(aligned16(d_out) && aligned16(y_routed) && aligned16(dy) && ((uintptr_t)dy_q & 7u) == 0 &&
+                  ((uintptr_t)dy_scale & 3u) == 0,
+              MOE_ERR_ALIGN, "moe_combine_backward: d_out, y_routed and dy must be 16-byte, dy_q 8-byte aligned");
   if (T > 0)
     combine_backward_kernel<<<T, 256, 0, stream>>>(d_out, y_routed, topk_idx, topk_gate, scores, pair_pos, T, top_k, d,
-                                                   n_experts, dy, du, du_row);
+                                                   n_experts, dy, du, du_row, dy_q, dy_scale);
   return check_launch("moe_combine_backward");
 }
 
 extern "C" moe_status moe_swiglu_backward(const float* ac, const float* dh, int64_t rows, int inter, uint16_t* dac,
-                                          hipStream_t stream) {
+                                          uint8_t* dac_q, float* dac_scale, hipStream_t stream) {
   using namespace moe;
   clear_error();
   MOE_REQUIRE(rows == 0 || (ac && dh && dac), MOE_ERR_NULL, "moe_swiglu_backward: a required pointer is NULL");
-  MOE_REQUIRE(rows >= 0 && inter >= 4 && inter % 4 == 0, MOE_ERR_SHAPE,
-              "moe_swiglu_backward: rows=%lld inter=%d (a positive multiple of 4)", (long long)rows, inter);
-  MOE_REQUIRE(aligned16(ac) && aligned16(dh) && ((uintptr_t)dac & 7u) == 0, MOE_ERR_ALIGN,
-              "moe_swiglu_backward: ac and dh must be 16-byte, dac 8-byte aligned");
+  MOE_REQUIRE(!dac_q == !dac_scale, MOE_ERR_NULL, "moe_swiglu_backward: dac_q and dac_scale go together");
+  MOE_REQUIRE(rows >= 0 && inter >= 4 && inter % 4 == 0 && (!dac_q || inter % 128 == 0), MOE_ERR_SHAPE,
+              "moe_swiglu_backward: rows=%lld inter=%d (a positive multiple of 4; of 128 with dac_q)", (long long)rows,
+              inter);
+  MOE_REQUIRE(aligned16(ac) && aligned16(dh) && ((uintptr_t)dac & 7u) == 0 && ((uintptr_t)dac_q & 3u) == 0 &&
+                  ((uintptr_t)dac_scale & 3u) == 0,
+              MOE_ERR_ALIGN, "moe_swiglu_backward: ac and dh must be 16-byte, dac 8-byte, dac_q 4-byte aligned");
   const int64_t n4 = rows * (inter / 4);
   if (n4 > 0) {
     const int64_t grid = (n4 + 255) / 256;
     MOE_REQUIRE(grid < (int64_t)1 << 31, MOE_ERR_SHAPE, "moe_swiglu_backward: too many rows");
-    swiglu_backward_kernel<<<(unsigned)grid, 256, 0, stream>>>(ac, dh, n4, inter, dac);
+    swiglu_backward_kernel<<<(unsigned)grid, 256, 0, stream>>>(ac, dh, n4, inter, dac, dac_q, dac_scale);
   }
   return check_launch("moe_swiglu_backward");
 }

@@ -147,19 +147,19 @@ class MoELayer:
         offs_ready.synchronize()
         lens = offs_host[1:] - offs_host[:-1]
         d_out = d_out.to(torch.bfloat16).contiguous()
-        dy, du, du_row = L.moe_combine_backward(d_out, buf["y"], buf["topk_idx"], buf["topk_gate"], buf["scores"], pp)
+        cb = L.moe_combine_backward(d_out, buf["y"], buf["topk_idx"], buf["topk_gate"], buf["scores"], pp, fp8=fp8)
+        dy, du, du_row = cb[:3]
         extra = {}
         dh = torch.empty((rows, I), dtype=torch.float32, device=dev)
         ac = torch.empty((rows, 2 * I), dtype=torch.float32, device=dev)
         dxr = torch.empty((T * K, d), dtype=torch.bfloat16, device=dev)
         dxs = torch.empty((T, d), dtype=torch.float32, device=dev)
         if fp8:
-            dyq, dys = q1(dy)
+            dyq, dys = cb[3:]  # dy's 1x128 E4M3 form, written by the combine backward itself
             L.moe_grouped_gemm(dyq, W2T, offs, 0, G, rows, dh, a_scale=dys, w_scale=W2T_s)
             L.moe_grouped_gemm(buf["xq"], self.W13, offs, 0, G, rows, ac, a_scale=buf["xs"], a_rows=st_,
                                w_scale=self.W13_s)
-            dac = L.moe_swiglu_backward(ac, dh)
-            dacq, dacs = q1(dac)
+            dac, dacq, dacs = L.moe_swiglu_backward(ac, dh, fp8=True)
             L.moe_grouped_gemm(dacq, W13T, offs, 0, G, rows, dxr, a_scale=dacs, w_scale=W13T_s, out_tail=dxs,
                                tail_groups=1)
             extra.update(dyq=dyq, dys=dys, dacq=dacq, dacs=dacs)

@@ -30,7 +30,7 @@ def test_header_declares_exactly_the_exports():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.lib().moe_abi_version() == 5
+    assert L.lib().moe_abi_version() == 6
     assert L.status_str(0) == "MOE_OK" and L.status_str(5) == "MOE_ERR_WORKSPACE"
 
 
@@ -140,8 +140,10 @@ def test_backward_entry_points_reject():
     lib = L.lib()
     P = ctypes.c_void_p
     p = [P(16)] * 6
-    # moe_combine_backward(d_out, y, idx, gate, scores, pair_pos, T, K, d, N, dy, du, du_row, stream)
-    cb = lambda T=4, K=2, d=16, N=8, ptrs=None, dy=P(16): (*(ptrs or p), T, K, d, N, dy, P(16), P(16), None)
+    # moe_combine_backward(d_out, y, idx, gate, scores, pair_pos, T, K, d, N, dy, du, du_row, dy_q, dy_scale,
+    #                      stream)
+    cb = lambda T=4, K=2, d=16, N=8, ptrs=None, dy=P(16), dq=None, ds=None: (
+        *(ptrs or p), T, K, d, N, dy, P(16), P(16), dq, ds, None)
     _rejects(lib, "moe_combine_backward", cb(ptrs=[None] + p[1:]), 1)
     _rejects(lib, "moe_combine_backward", cb(T=-1), 2)
     _rejects(lib, "moe_combine_backward", cb(K=0), 2)
@@ -149,11 +151,17 @@ def test_backward_entry_points_reject():
     _rejects(lib, "moe_combine_backward", cb(K=9, N=8), 2)
     _rejects(lib, "moe_combine_backward", cb(d=12), 2)
     _rejects(lib, "moe_combine_backward", cb(dy=P(8)), 4)
-    # moe_swiglu_backward(ac, dh, rows, inter, dac, stream)
-    _rejects(lib, "moe_swiglu_backward", (None, P(16), 4, 8, P(16), None), 1)
-    _rejects(lib, "moe_swiglu_backward", (P(16), P(16), -1, 8, P(16), None), 2)
-    _rejects(lib, "moe_swiglu_backward", (P(16), P(16), 4, 6, P(16), None), 2)
-    _rejects(lib, "moe_swiglu_backward", (P(16), P(16), 4, 8, P(4), None), 4)
+    _rejects(lib, "moe_combine_backward", cb(dq=P(16)), 1)                 # dy_q without dy_scale
+    _rejects(lib, "moe_combine_backward", cb(d=64, dq=P(16), ds=P(16)), 2)  # E4M3 rows need d % 128 == 0
+    _rejects(lib, "moe_combine_backward", cb(d=128, dq=P(4), ds=P(16)), 4)
+    # moe_swiglu_backward(ac, dh, rows, inter, dac, dac_q, dac_scale, stream)
+    _rejects(lib, "moe_swiglu_backward", (None, P(16), 4, 8, P(16), None, None, None), 1)
+    _rejects(lib, "moe_swiglu_backward", (P(16), P(16), -1, 8, P(16), None, None, None), 2)
+    _rejects(lib, "moe_swiglu_backward", (P(16), P(16), 4, 6, P(16), None, None, None), 2)
+    _rejects(lib, "moe_swiglu_backward", (P(16), P(16), 4, 8, P(4), None, None, None), 4)
+    _rejects(lib, "moe_swiglu_backward", (P(16), P(16), 4, 8, P(16), None, P(16), None), 1)
+    _rejects(lib, "moe_swiglu_backward", (P(16), P(16), 4, 64, P(16), P(16), P(16), None), 2)
+    _rejects(lib, "moe_swiglu_backward", (P(16), P(16), 4, 128, P(16), P(2), P(16), None), 4)
     # moe_segment_transpose(src, ld_src, src_rows, seg_offsets, dst_cols, n_seg, cols, total_cols, dst, ld_dst,
     #                       seg_stride, stream)
     st = lambda src=P(16), ld_src=64, n=2, cols=64, total=128, dst=P(16), ld_dst=128, ss=0: (

@@ -152,6 +152,43 @@ def test_swiglu_backward():
     assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-6 * np.sqrt(np.mean(want ** 2)))
 
 
+def test_combine_and_swiglu_backward_fp8_outputs():
+    """The E4M3 forms the two kernels write alongside their bf16 outputs: the oracle's 1x128
+    quantiser applied to the device's own bf16 dy / [da | dc], bit for bit (including a skipped pair,
+    whose rows stay unwritten, an all-zero d_out row and an outlier)."""
+    T, K, N, d = 40, 4, 16, 384
+    idx = torch.from_numpy(np.stack([np.random.default_rng(t).choice(N, K, replace=False) for t in range(T)])
+                           .astype(np.int32))
+    idx[5, 2] = -1  # skipped by the permutation
+    offs, st_, pp = M()._lib.moe_permute(idx.to(DEV), N, 1)
+    ppn = pp.cpu().numpy()
+    y = I.gen_normal(95, (T * K, d), 1.0)
+    dn = I.gen_normal(96, (T, d), 1.0).float().numpy()
+    dn[7] = 0.0
+    dn[9, 100] = 500.0
+    d_out = torch.from_numpy(dn).to(torch.bfloat16)
+    scores = torch.rand((T, N), generator=torch.Generator().manual_seed(5)) * 0.8 + 0.1
+    gate = torch.rand((T, K), generator=torch.Generator().manual_seed(6))
+    dy, du, du_row, dyq, dys = M()._lib.moe_combine_backward(d_out.to(DEV), y.to(DEV), idx.to(DEV), gate.to(DEV),
+                                                             scores.to(DEV), pp, fp8=True)
+    rows = sorted(set(ppn[ppn >= 0].tolist()) | set(range(T * K, T * (K + 1))))
+    wq, ws = O.quant_1x128(dy[rows].float().cpu().numpy())
+    assert np.array_equal(dyq[rows].cpu().numpy(), wq)
+    assert np.array_equal(dys[rows].cpu().numpy(), ws)
+    # the bf16 outputs are those of the plain call
+    dy0, du0, _ = M()._lib.moe_combine_backward(d_out.to(DEV), y.to(DEV), idx.to(DEV), gate.to(DEV), scores.to(DEV), pp)
+    assert torch.equal(dy0[rows], dy[rows]) and torch.equal(du0, du)
+
+    r_, inter = 70, 256
+    ac = I.gen_normal(97, (r_, 2 * inter), 2.0, dtype=torch.float32)
+    dh = I.gen_normal(98, (r_, inter), 1.0, dtype=torch.float32)
+    dh[3] = 0.0
+    dac, dacq, dacs = M()._lib.moe_swiglu_backward(ac.to(DEV), dh.to(DEV), fp8=True)
+    wq, ws = O.quant_1x128(dac.float().cpu().numpy())
+    assert np.array_equal(dacq.cpu().numpy(), wq) and np.array_equal(dacs.cpu().numpy(), ws)
+    assert torch.equal(M()._lib.moe_swiglu_backward(ac.to(DEV), dh.to(DEV)), dac)
+
+
 def _layer(cfg):
     x = I.gen_x(cfg).to(torch.bfloat16)
     wr = I.gen_router(cfg).to(torch.bfloat16)
