@@ -250,6 +250,14 @@ typedef struct moe_gemm_desc {
   void* ws;                     /* device workspace of moe_grouped_gemm_workspace_size() bytes,
                                    16-byte aligned, zero-filled before its first use */
   size_t ws_bytes;
+  /* Optional ragged reduction (f32 output, epilogue NONE, f32 scales), for weight gradients
+   * whose reduction axis is each expert's own rows ("FP8 混合精度訓練": Wgrad): device i32,
+   * at least first_group + n_groups + 1 non-decreasing entries, or NULL.  Group g then sums only
+   * over K columns [0, k_g), k_g = len_g = k_offsets[g+1] - k_offsets[g] rounded up to the K
+   * step (64 bf16 / 128 FP8 elements), at least one step and at most K; columns [len_g, k_g) of
+   * A and W must hold zeros (the segment transposes write them) for the exact sum over len_g.
+   * Columns at and beyond k_g are not read. */
+  const int32_t* k_offsets;
 } moe_gemm_desc;
 /* Limits: K a positive multiple of 64 (bf16) or 128 (FP8); N a positive multiple of 128 (bf16)
  * or 256 (FP8) -- with SWIGLU that is N/2 a multiple of 64 or 128; FP8 input needs a_scale and

@@ -103,6 +103,7 @@ struct GemmArgs {
   uint8_t* out_tail;
   int64_t ldo_tail_b;   // bytes per tail output row
   unsigned int* sync;   // workspace: [8] round arrivals per XCD, [8] exit counter
+  const int32_t* k_offs;  // per-group reduction lengths (k_offs[g + 1] - k_offs[g]), or null
 };
 
 __device__ __forceinline__ float silu(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
@@ -122,12 +123,15 @@ __device__ __forceinline__ int load_offset(const int32_t* offs, int g) {
   return *(cint32*)(uintptr_t)(offs + __builtin_amdgcn_readfirstlane(g));
 }
 
-// Decode logical tile L (order: group, column block, row block) from the LDS prefix table.
+// Decode logical tile L (order: group, column block, row block; with band > 0, a group of more
+// than `band` row blocks goes in bands of `band` row blocks, column blocks inside a band) from
+// the LDS prefix table.
 // Every caller walks its tiles in increasing L, so the search for the group (the largest g with
 // tstart[g] <= L; then tstart[g + 1] > L, never an empty group) starts at the group of the
 // caller's previous tile (cur, updated): a few steps forward, else a binary search over the rest.
-template <int BM>
-__device__ __forceinline__ TileInfo decode_tile(int L, const int* tstart, int G, const int32_t* offs, int& cur) {
+template <int BM, bool BANDS>
+__device__ __forceinline__ TileInfo decode_tile(int L, const int* tstart, int G, const int32_t* offs, int& cur,
+                                                int band, int n_tiles) {
   int g = cur;
   for (int n = 0; n < 3 && g + 1 < G && __builtin_amdgcn_readfirstlane(tstart[g + 1]) <= L; ++n) ++g;
   if (g + 1 < G && __builtin_amdgcn_readfirstlane(tstart[g + 1]) <= L) {
@@ -147,7 +151,13 @@ __device__ __forceinline__ TileInfo decode_tile(int L, const int* tstart, int G,
   TileInfo t;
   t.g = g;
   t.nt = local / mt_g;
-  const int mt = local - t.nt * mt_g;
+  int mt = local - t.nt * mt_g;
+  if (BANDS && band > 0 && mt_g > band) {
+    const int b = local / (band * n_tiles), r = local - b * band * n_tiles;
+    const int rows_b = min(band, mt_g - b * band);  // the last band may be narrower
+    t.nt = r / rows_b;
+    mt = b * band + (r - t.nt * rows_b);
+  }
   t.row0 = m0 + mt * BM;
   t.nrows = min(BM, m1 - t.row0);
   return t;
@@ -250,7 +260,41 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   const int t_begin = (int)((int64_t)total * xcd / n_xcd), t_end = (int)((int64_t)total * (xcd + 1) / n_xcd);
   const int n_my = t_end - t_begin > slot ? (t_end - t_begin - slot + per_xcd - 1) / per_xcd : 0;
   const int ksteps = p.ksteps;
-  const int total_steps = n_my * ksteps;
+  // Ragged reduction (f32 outputs without SwiGLU, f32 scales): with k_offs set, the tiles of
+  // group g run only the K steps that cover its first k_offs[g + 1] - k_offs[g] elements (at
+  // least one step), so a weight gradient over zero-padded expert segments skips the padding
+  // beyond each expert's own length.  The walk over a workgroup's steps then keeps its own
+  // (tile, step) counters instead of dividing by a common step count.
+  constexpr bool kRag = OUT == OUT_F32 && !SWIGLU && !E8;
+  constexpr int kGran = FP8 ? 128 : 64;  // K elements per step
+  // Tile order of the E4M3 weight gradients (ragged launches with 16+ column blocks, i.e. the
+  // gate/up weights' gradient: 4096 rows x 28 column blocks per expert): bands of two row
+  // blocks, so that a round of an XCD's 32 workgroups covers 2 row blocks x 16 column blocks
+  // rather than 32 row blocks of one column block; measured 13.0 -> 10.6 ms at T = 16384.  The
+  // narrower down-projection gradient (8 column blocks) and the bf16 launches measured equal
+  // or slower with bands, so they keep the plain order.
+  constexpr bool kBands = kRag && FP8 == 1;
+  const int band = (kBands && p.k_offs && p.n_tiles >= 16) ? 2 : 0;
+  auto group_ksteps = [&](int g) {
+    if constexpr (kRag) {
+      if (p.k_offs) {
+        const int len = load_offset(p.k_offs, g + 1) - load_offset(p.k_offs, g);
+        return len <= 0 ? 1 : min(ksteps, (len - 1) / kGran + 1);
+      }
+    }
+    return ksteps;
+  };
+  int total_steps = n_my * ksteps;
+  if constexpr (kRag) {
+    if (p.k_offs) {
+      total_steps = 0;
+      int cur = 0;
+#pragma unroll 1
+      for (int q = 0; q < n_my; ++q)
+        total_steps +=
+            group_ksteps(decode_tile<BM, kBands>(t_begin + slot + q * per_xcd, s_tstart, G, p.offs, cur, band, p.n_tiles).g);
+    }
+  }
   // arrivals the XCD's counter holds once every workgroup with a round-r tile finished it,
   // summed over rounds r < q
   const int xr = t_end - t_begin;
@@ -330,7 +374,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   // tile q of this workgroup; the three walks over the tiles (weight rows of the batch being
   // loaded, gather rows one tile ahead, the tile being computed) keep their own search cursors
   int cur_b = 0, cur_r = 0, cur_c = 0;
-  auto tile_of = [&](int q, int& cur) { return decode_tile<BM>(t_begin + slot + q * per_xcd, s_tstart, G, p.offs, cur); };
+  auto tile_of = [&](int q, int& cur) {
+    return decode_tile<BM, kBands>(t_begin + slot + q * per_xcd, s_tstart, G, p.offs, cur, band, p.n_tiles);
+  };
   // gather sources of a tile's rows (global loads whose values are used one tile later)
   auto fetch_rows = [&](const TileInfo& t, int* dst, int* sdst) {
 #pragma unroll
@@ -383,14 +429,31 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   // so the number of batches in flight is constant) into ring slot SL
   int dma_kt = 0;            // K step of the batch being issued
   bool dma_scales = false;   // the batch starts a scale chunk
+  int ld_js = -1, ld_q = -1, ld_kt = 0, ld_ks = 0;  // ragged: step, tile, K step, tile's K steps
   // tile bookkeeping for the batch of global step js (clamped to the last step: every step
   // issues one batch, so the number of batches in flight is constant)
   auto issue_prep = [&](int js) __attribute__((always_inline)) {
     const bool past_end = js >= total_steps;
     js = min(js, total_steps - 1);
-    const int q = js / ksteps, kt = js - q * ksteps;
+    int q, kt;
+    if constexpr (kRag) {
+      if (js != ld_js) {  // the next step (the calls advance one step at a time)
+        ld_js = js;
+        if (++ld_kt >= ld_ks) {
+          ++ld_q;
+          ld_kt = 0;
+        }
+      }
+      q = ld_q;
+      kt = ld_kt;
+    } else {
+      q = js / ksteps;
+      kt = js - q * ksteps;
+    }
     if (q != lq) {  // entering a new tile: its rows were fetched one tile earlier
-      set_b(tile_of(q, cur_b));
+      const TileInfo tb = tile_of(q, cur_b);
+      set_b(tb);
+      if constexpr (kRag) ld_ks = group_ksteps(tb.g);
       if (q > 0) set_rows(a_nxt, s_nxt);
       if (q + 1 < n_my) fetch_rows(tile_of(q + 1, cur_r), a_nxt, s_nxt);
       lq = q;
@@ -486,6 +549,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
 #pragma unroll
     for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
   TileInfo ct = tile_of(0, cur_c);
+  int c_q = 0, c_kt = 0, c_ks = group_ksteps(ct.g);  // ragged: tile, K step, tile's K steps
   // operand reads: row & 7 = lr & 7 for every row a lane reads (tile offsets are multiples of
   // 16), so its two swizzled 16-byte chunks (lg and lg + 4) sit at fixed byte offsets lo / hi
   // from the row start and every read is one base register plus a constant
@@ -507,7 +571,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   // lanes' rows at distinct swizzled chunks and hits distinct banks.  The scales of the K
   // block: s_A of the lane's four rows (one 16-byte read) and the two weight-block scales
   // (one broadcast read), combined into s_A * s_W per row tile.
-  auto fp8_read = [&](const uint8_t* As, int kt, i32x8(&af)[TM], i32x8(&bfr)[TN], float(&s0)[TM],
+  auto fp8_read = [&](const uint8_t* As, int kt, int ks, i32x8(&af)[TM], i32x8(&bfr)[TN], float(&s0)[TM],
                       float(&s1)[TM]) __attribute__((always_inline)) {
     const uint8_t* Bs = As + A_BYTES;
 #pragma unroll
@@ -533,7 +597,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       s0[i] = sa[i] * sw0;
       s1[i] = SWIGLU ? sa[i] * sw1 : s0[i];
     }
-    if (kc == SC_CH - 1 || kt == ksteps - 1) sc_use = sc_use + 1 == SC_NB ? 0 : sc_use + 1;  // chunk done
+    if (kc == SC_CH - 1 || kt == ks - 1) sc_use = sc_use + 1 == SC_NB ? 0 : sc_use + 1;  // chunk done
   };
   // Products with W as the first operand: a lane's four results of tile (i, jj) are columns
   // lg * 4 .. lg * 4 + 3 of row lr, so one combined scale covers them.  Every tile's partial
@@ -561,8 +625,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   // ---- E8M0 K step: the same operand reads, the codes of the lane's four rows (one 16-byte
   // read, byte kc % 4 of each dword) and of the two weight blocks; every product goes straight
   // into its accumulator with the codes as the MFMA's block scales ----
-  auto e8_read = [&](const uint8_t* As, int kt, i32x8(&af)[TM], i32x8(&bfr)[TN], int(&sa)[TM], int& sw0, int& sw1)
-      __attribute__((always_inline)) {
+  auto e8_read = [&](const uint8_t* As, int kt, int ks, i32x8(&af)[TM], i32x8(&bfr)[TN], int(&sa)[TM], int& sw0,
+                     int& sw1) __attribute__((always_inline)) {
     const uint8_t* Bs = As + A_BYTES;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -587,7 +651,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     const uint32_t w0 = swp[0], w1 = swp[SC_CH / 4];
     sw0 = (int)(((SWIGLU || (wn * WN) / 128 == 0 ? w0 : w1) >> sh) & 255u);
     sw1 = (int)((w1 >> sh) & 255u);
-    if (kc == SC_CH - 1 || kt == ksteps - 1) sc_use = sc_use + 1 == SC_NB ? 0 : sc_use + 1;  // chunk done
+    if (kc == SC_CH - 1 || kt == ks - 1) sc_use = sc_use + 1 == SC_NB ? 0 : sc_use + 1;  // chunk done
   };
   auto e8_math = [&](auto slot_c, const i32x8(&af)[TM], const i32x8(&bfr)[TN], const int(&sa)[TM], int sw0, int sw1)
       __attribute__((always_inline)) {
@@ -726,7 +790,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     auto step = [&](auto slot_c, int j) __attribute__((always_inline)) {
       constexpr int SL = decltype(slot_c)::value;
       const uint8_t* As = SL == 0 ? slot0 : (SL == 1 ? slot1 : slot2);
-      const int kt = j % ksteps;
+      int kt, ks;
+      if constexpr (kRag) {
+        kt = c_kt;
+        ks = c_ks;
+      } else {
+        kt = j % ksteps;
+        ks = ksteps;
+      }
       if (kRoundSync && kt == 0 && j > 0) {  // a new round: arrive for the last one, wait for the XCD
         if (tid == 0) {
           const int q = j / ksteps;
@@ -745,7 +816,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       // spread over this step's MFMAs
       constexpr auto dslot = std::integral_constant<int, (SL + STAGES - 1) % STAGES>();
       issue_prep(j + STAGES - 1);
-      if constexpr (!FP8) dma_now = kt != ksteps - 1;
+      if constexpr (!FP8) dma_now = kt != ks - 1;
 
       if constexpr (!FP8) {
         const uint8_t* Bs = As + A_BYTES;
@@ -770,17 +841,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       } else if constexpr (E8) {
         i32x8 af[TM], bfr[TN];
         int sa[TM], sw0, sw1;
-        e8_read(As, kt, af, bfr, sa, sw0, sw1);
+        e8_read(As, kt, ks, af, bfr, sa, sw0, sw1);
         e8_math(dslot, af, bfr, sa, sw0, sw1);
       } else {
         i32x8 af[TM], bfr[TN];
         float s0[TM], s1[TM];
-        fp8_read(As, kt, af, bfr, s0, s1);
+        fp8_read(As, kt, ks, af, bfr, s0, s1);
         fp8_math(dslot, af, bfr, s0, s1);
       }
       issue_scales();
 
-      if (kt == ksteps - 1) {
+      if (kt == ks - 1) {
         float v[TM][TO][4];
         epi_values(v);
         if (OUT == OUT_FP8) {
@@ -789,10 +860,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
         }
         epi_store(v, ct);
         if (OUT == OUT_FP8) MOE_BARRIER();  // s_red is rewritten by the next tile
-        if (j + 1 < total_steps) ct = tile_of((j + 1) / ksteps, cur_c);
+        if (j + 1 < total_steps) ct = tile_of(kRag ? c_q + 1 : (j + 1) / ksteps, cur_c);
         if constexpr (!FP8) {
 #pragma unroll
           for (int k = 0; k < L_ISSUE; ++k) issue_one(dslot, k);
+        }
+      }
+      if constexpr (kRag) {
+        if (kt == ks - 1) {
+          ++c_q;
+          c_kt = 0;
+          c_ks = group_ksteps(ct.g);
+        } else {
+          ++c_kt;
         }
       }
     };
@@ -967,6 +1047,9 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
                 (long long)d->ldo_tail);
   }
 
+  MOE_REQUIRE(!d->k_offsets || (d->out_dtype == MOE_F32 && !swiglu && !e8), MOE_ERR_DTYPE,
+              "moe_grouped_gemm: k_offsets needs an f32 output, epilogue NONE and f32 scales");
+
   GemmArgs a;
   a.a = static_cast<const uint8_t*>(d->a);
   a.a_scale = d->a_scale;
@@ -991,6 +1074,7 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
   a.out_cols = out_cols;
   a.n_tiles = 0;  // set per tile shape at launch
   a.sync = static_cast<unsigned int*>(d->ws);
+  a.k_offs = d->k_offsets ? d->k_offsets + d->first_group : nullptr;
   const bool narrow = !fp8 && d->N % 256 != 0;
 
   // Tile shape by regime: many rows per expert -> 128-row blocks; few (decode) -> 64.

@@ -175,9 +175,10 @@ class MoELayer:
         dx = L.moe_combine(dxr, part, pp, torch.ones((T, K), dtype=torch.float32, device=dev), torch.float32)
         # Wgrad: each expert's rows are the reduction axis.  The routed experts' rows become
         # equal-width zero-padded blocks [N][C][kmax] (kmax = the largest routed segment,
-        # rounded up to 64), so one grouped GEMM covers all of them (an empty expert's blocks
-        # are zeros, so its gradient comes out zero); the shared expert (all T tokens) has
-        # its own launch.
+        # rounded up to the K step), so one grouped GEMM covers all of them; the GEMM's ragged
+        # reduction (k_offsets = the expert offsets) stops each expert at its own length
+        # rounded up to the K step, and an empty expert reduces one zero step to a zero
+        # gradient.  The shared expert (all T tokens) has its own launch.
         kq = 128 if fp8 else 64  # K granule of the GEMM
         kmax = max(kq, (int(lens[:N].max()) + kq - 1) // kq * kq)
         kp_s = (int(lens[N]) + kq - 1) // kq * kq
@@ -202,14 +203,15 @@ class MoELayer:
                 aq, as_ = L.moe_segment_transpose_fp8(a_src, seg, width)
                 bq, bs = L.moe_segment_transpose_fp8(b_src, seg, width, src_rows=rows_b, block_scales=True)
                 L.moe_grouped_gemm(aq.view(n_groups * C, width), bq, offsets, 0, n_groups, n_groups * C, out,
-                                   a_scale=as_.view(n_groups * C, width // 128), w_scale=bs)
+                                   a_scale=as_.view(n_groups * C, width // 128), w_scale=bs, k_offsets=seg)
                 if keep:
                     extra.setdefault("wgrad_operands", []).append((aq.view(n_groups * C, width), as_, bq, bs))
             else:
                 cols = torch.arange(0, (n_groups + 1) * width, width, dtype=torch.int32, device=dev)
                 at = L.moe_segment_transpose(a_src, seg, cols, n_groups * width, width=width)
                 bt = L.moe_segment_transpose(b_src, seg, cols, n_groups * width, src_rows=rows_b, width=width)
-                L.moe_grouped_gemm(at.view(n_groups * C, width), bt, offsets, 0, n_groups, n_groups * C, out)
+                L.moe_grouped_gemm(at.view(n_groups * C, width), bt, offsets, 0, n_groups, n_groups * C, out,
+                                   k_offsets=seg)
 
         wgrad(dy, h, seg_r, kmax, None, N, g_d, dw2[:N].view(N * d, I))
         wgrad(dac, x, seg_r, kmax, st_, N, g_2i, dw13[:N].view(N * 2 * I, d))

@@ -407,6 +407,82 @@ def test_gemm_fp8_exact(sizes, K):
         assert np.array_equal(got[offs[g]:offs[g + 1]], ref), g
 
 
+@pytest.mark.parametrize("fp8,N,m_sizes", [
+    (False, 256, [130, 0, 64, 200, 17, 129]),
+    (True, 256, [130, 0, 64, 200, 17, 129]),
+    (True, 4096, [640, 0, 385, 128, 1, 300]),  # 16+ column blocks: E4M3 tiles in bands of 2 row blocks
+], ids=["bf16", "fp8", "fp8_banded"])
+def test_gemm_ragged_k(fp8, N, m_sizes):
+    """Per-group reduction lengths (k_offsets, the weight gradient's layout): group g sums only
+    over its first len_g K columns rounded up to the K step (64 bf16 / 128 E4M3 elements, at
+    least one step).  The columns past that are NaN here, so a read of any of them would show;
+    the padding inside the last step is zero.  The result must equal the oracle's product over
+    the first len_g columns (exact for the E4M3 codes of small integers with power-of-two
+    scales, fp32 rounding for bf16) and, bit for bit, the same launch without k_offsets on the
+    NaN-free operands.  Groups: empty (0 rows), a zero-length reduction, one element, ragged
+    lengths, the full K, and enough rows for several row tiles.  With 16 or more column blocks
+    the E4M3 tiles run in bands of two row blocks (a group of 5 row blocks ends in a band of
+    one); the result does not depend on the order."""
+    gran = 128 if fp8 else 64
+    K = 640
+    m_sizes = np.array(m_sizes)
+    lens = np.array([300, 77, 0, 1, K, 129])
+    G = len(m_sizes)
+    offs = _offsets(m_sizes)
+    koffs = _offsets(lens)
+    rows = int(offs[-1])
+    kg = np.array([min(K, max(gran, -(-int(n) // gran) * gran)) for n in lens])
+    if fp8:
+        A = I.gen_e4m3_codes(61, (rows, K), small_int=True)
+        W = I.gen_e4m3_codes(63, (G, N, K), small_int=True)
+        As = torch.where(I.gen_scales(62, (rows, K // 128), pow2=True) <= 2.0 ** -6, 2.0 ** -4, 2.0 ** -3).float()
+        Ws = torch.where(I.gen_scales(64, (G, N // 128, K // 128), pow2=True) <= 2.0 ** -6, 2.0 ** -5, 2.0 ** -4).float()
+    else:
+        A = I.gen_normal(61, (rows, K), 1.0)
+        W = I.gen_normal(63, (G, N, K), 0.05)
+        As = Ws = None
+    # zeros in [len_g, k_g) and poison from k_g on (E4M3 NaN code 0x7F, bf16 NaN)
+    Az, Wz = A.clone(), W.clone()
+    Ap, Wp = A.clone(), W.clone()
+    nan = 0x7F if fp8 else float("nan")
+    Asp, Wsp = (As.clone(), Ws.clone()) if fp8 else (None, None)
+    for g in range(G):
+        lo, hi, n, k = offs[g], offs[g + 1], int(lens[g]), int(kg[g])
+        for t in (Az, Ap):
+            t[lo:hi, n:] = 0
+        for t in (Wz, Wp):
+            t[g, :, n:] = 0
+        Ap[lo:hi, k:] = nan
+        Wp[g, :, k:] = nan
+        if fp8:
+            Asp[lo:hi, k // 128:] = float("nan")
+            Wsp[g, :, k // 128:] = float("nan")
+    o = torch.from_numpy(offs).to(DEV)
+    ko = torch.from_numpy(koffs).to(DEV)
+    sc = lambda a_s, w_s: dict(a_scale=a_s.to(DEV), w_scale=w_s.to(DEV)) if fp8 else {}
+    rag = torch.empty((rows, N), dtype=torch.float32, device=DEV)
+    M().moe_grouped_gemm(Ap.to(DEV), Wp.to(DEV), o, 0, G, rows, rag, k_offsets=ko, **sc(Asp, Wsp))
+    pad = torch.empty_like(rag)
+    M().moe_grouped_gemm(Az.to(DEV), Wz.to(DEV), o, 0, G, rows, pad, **sc(As, Ws))
+    got = rag.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert torch.equal(rag, pad)
+    for g in range(G):
+        lo, hi, n = offs[g], offs[g + 1], int(lens[g])
+        if hi == lo:
+            continue
+        if fp8:
+            Ad = O.dequant_1x128(Az[lo:hi].numpy(), As[lo:hi].numpy())
+            Wd = O.dequant_128x128(Wz[g].numpy(), Ws[g].numpy())
+            assert np.array_equal(got[lo:hi], Ad @ Wd.T), g
+        else:
+            ref = np64(A[lo:hi, :n]) @ np64(W[g, :, :n]).T
+            assert np.max(np.abs(got[lo:hi] - ref)) <= 1e-5 * max(1.0, float(np.sqrt(np.mean(ref ** 2)))), g
+    if np.any(lens == 0):
+        g0 = int(np.argmax(lens == 0))
+        assert not np.any(got[offs[g0]:offs[g0 + 1]]), "a zero-length reduction gives zeros"
+
+
 # FP8_DOT_REL: the fp8 dot-product error bound (see tests/gpu_common.py).
 
 
