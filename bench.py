@@ -225,9 +225,10 @@ def ingest_pmc(fetch_dir, write_dir, workload):
     """HBM bytes per launch of the gate/up kernel from FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by the factor that maps the same counter on a 1 GiB device copy
     to 1 GiB."""
-    # template arguments <..., input kind (0 bf16, 1 E4M3 + f32 scales, 2 E4M3 + E8M0), SwiGLU, output>
+    # template arguments <..., input kind (0 bf16, 1 E4M3 + f32 scales, 2 E4M3 + E8M0), SwiGLU, output,
+    # pre-activation output (the inference forward: false)>
     kind = 2 if workload.endswith("_e8m0") else (1 if "fp8" in workload else 0)
-    want = f"{kind}, true, {2 if kind else 0}>"
+    want = f"{kind}, true, {2 if kind else 0}, false>"
     rec = {"workload": workload, "kernel_src_sha": kernel_src_sha(), "copy_bytes": COPY_BYTES}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _pmc_rows(d, counter)
@@ -352,8 +353,10 @@ def decode_skew_sweep(torch, M, I, wr, W13, W2, dev, steps):
 
 
 def time_backward(torch, layer, x, d_out, n=3):
-    """Mean time of n backward passes of `layer` for the forward of x (kept), after one warm-up
-    pass that also makes the transposed weight copies; the weight gradients are reused."""
+    """Mean times of n backward passes of `layer` for the forward of x (kept), after one warm-up
+    pass that also makes the transposed weight copies (the weight gradients are reused), and of
+    n training forwards (keep=True: the forward that also stores what the backward takes, the
+    gate/up products a | c among it)."""
     _, buf = layer.forward(x, keep=True)
     g = layer.backward(d_out, buf)
     keep = {"dw13": g["dw13"], "dw2": g["dw2"]}
@@ -366,18 +369,29 @@ def time_backward(torch, layer, x, d_out, n=3):
         del g
     e.record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / n
+    ms_bwd = s.elapsed_time(e) / n
+    del buf
+    s.record()
+    for _ in range(n):
+        _, buf = layer.forward(x, keep=True)
+        del buf
+    e.record()
+    torch.cuda.synchronize()
+    return ms_bwd, s.elapsed_time(e) / n
 
 
-def backward_record(name, dtype, T, ms, flops, peak, note):
+def backward_record(name, dtype, T, times, flops, peak, note):
+    ms, ms_fwd = times
     return {"workload": name + "_backward", "dtype": dtype, "ms_per_step": round(ms, 4),
             "tokens_per_s": round(T / (ms / 1e3), 1), "tflops": round(flops / (ms / 1e3) / 1e12, 2),
-            f"mfma_frac_{dtype}_peak": round(flops / (ms / 1e3) / 1e12 / peak, 4), "note": note}
+            f"mfma_frac_{dtype}_peak": round(flops / (ms / 1e3) / 1e12 / peak, 4),
+            "training_forward_ms": round(ms_fwd, 4), "note": note}
 
 
-BWD_NOTE_FP8 = "E4M3 Dgrad and Wgrad (1x128 / 128x128 scales, transposed operands quantised); f32 weight gradients"
-BWD_NOTE_BF16 = ("dx, dW_r, dW13, dW2 (f32); gate/up products recomputed; weight-transpose copies made once, "
-                 "outside the timed region")
+BWD_NOTE_FP8 = ("E4M3 Dgrad and Wgrad (1x128 / 128x128 scales, transposed operands quantised); f32 weight gradients; "
+                "gate/up products a | c stored by the training forward (training_forward_ms), not recomputed")
+BWD_NOTE_BF16 = ("dx, dW_r, dW13, dW2 (f32); gate/up products a | c stored by the training forward "
+                 "(training_forward_ms), not recomputed; weight-transpose copies made once, outside the timed region")
 
 
 def layer_flops(c):
@@ -387,9 +401,8 @@ def layer_flops(c):
 
 
 def backward_flops(c):
-    """Algorithmic flops of one backward: twice the forward's (Dgrad and Wgrad) plus the gate/up
-    products recomputed."""
-    return 2 * layer_flops(c) + 4 * c.rows * c.d * c.inter
+    """Algorithmic flops of one backward: twice the forward's (Dgrad and Wgrad)."""
+    return 2 * layer_flops(c)
 
 
 def run_backward_only(torch, M, I, dev):
@@ -406,7 +419,7 @@ def run_backward_only(torch, M, I, dev):
         out.append(backward_record(c.name, "fp8" if fp8 else "bf16", c.T, ms, backward_flops(c),
                                    FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS,
                                    BWD_NOTE_FP8 if fp8 else BWD_NOTE_BF16))
-        log(f"[bench] {c.name}_backward: {ms:.3f} ms per backward")
+        log(f"[bench] {c.name}_backward: {ms[0]:.3f} ms per backward, {ms[1]:.3f} ms per training forward")
         del layer, W13, W2, x, d_out
         torch.cuda.empty_cache()
     return out
@@ -673,7 +686,7 @@ def main():
         d3 = I.gen_normal(c3.seed + 900, (c3.T, c3.d), 1.0).to(dev)
         ms3b = time_backward(torch, l3, x3, d3)
         sec.append(backward_record(c3.name, "fp8", c3.T, ms3b, backward_flops(c3), FP8_PEAK_TFLOPS, BWD_NOTE_FP8))
-        log(f"[bench] {c3.name}_backward: {ms3b:.3f} ms per backward")
+        log(f"[bench] {c3.name}_backward: {ms3b[0]:.3f} ms per backward, {ms3b[1]:.3f} ms per training forward")
         del l3, d3, x3
         torch.cuda.empty_cache()
         # the same layer with power-of-two (E8M0) tile scales applied by the matrix cores
@@ -694,7 +707,7 @@ def main():
         msb = time_backward(torch, lb, xb, d_out)
         sec.append(backward_record(cfg.name, "bf16", cfg.T, msb, backward_flops(cfg), BF16_PEAK_TFLOPS,
                                    BWD_NOTE_BF16))
-        log(f"[bench] {cfg.name}_backward: {msb:.3f} ms per backward")
+        log(f"[bench] {cfg.name}_backward: {msb[0]:.3f} ms per backward, {msb[1]:.3f} ms per training forward")
         del lb, xb, d_out
         torch.cuda.empty_cache()
         c2 = I.V3_GROUP

@@ -258,6 +258,15 @@ typedef struct moe_gemm_desc {
    * A and W must hold zeros (the segment transposes write them) for the exact sum over len_g.
    * Columns at and beyond k_g are not read. */
   const int32_t* k_offsets;
+  /* Optional with SWIGLU: device f32 [rows, ldo_preact] out, or NULL: the gate and up products
+   * themselves (a = A W1^T in columns [0, N/2), c = A W3^T in [N/2, N), the fp32 values the
+   * epilogue takes, bit for bit those of the same launch without SwiGLU and with an f32
+   * output), for a training forward whose backward needs them (the SwiGLU backward takes a and
+   * c; "DeepSeek-V3 Technical Report", "FP8 混合精度訓練": activations cached for the backward).
+   * Row r lands in row r - group_offsets[first_group].  16-byte aligned, ldo_preact >= N and a
+   * multiple of 4. */
+  void* out_preact;
+  int64_t ldo_preact;
 } moe_gemm_desc;
 /* Limits: K a positive multiple of 64 (bf16) or 128 (FP8); N a positive multiple of 128 (bf16)
  * or 256 (FP8) -- with SWIGLU that is N/2 a multiple of 64 or 128; FP8 input needs a_scale and

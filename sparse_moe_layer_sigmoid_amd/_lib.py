@@ -42,7 +42,7 @@ class MoeGemmDesc(ctypes.Structure):
         ("n_groups", _i), ("m_total", _i64), ("N", _i), ("K", _i), ("epilogue", _i),
         ("out", _p), ("out_dtype", _i), ("ldo", _i64), ("out_scale", _p),
         ("tail_groups", _i), ("out_tail", _p), ("ldo_tail", _i64), ("scale_fmt", _i), ("ldw", _i64),
-        ("ws", _p), ("ws_bytes", _sz), ("k_offsets", _p),
+        ("ws", _p), ("ws_bytes", _sz), ("k_offsets", _p), ("out_preact", _p), ("ldo_preact", _i64),
     ]
 
 
@@ -277,7 +277,7 @@ def gemm_workspace(device, stream=None) -> torch.Tensor:
 
 def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_total: int, out,
                      a_scale=None, a_rows=None, w_scale=None, swiglu: bool = False, out_scale=None,
-                     out_tail=None, tail_groups: int = 0, ws=None, k_offsets=None):
+                     out_tail=None, tail_groups: int = 0, ws=None, k_offsets=None, out_preact=None):
     """out[r - off[first_group]] = epilogue(A[a_rows[r] or r] . W[g]^T) for each sorted row r
     of group g.  a: bf16 or uint8 (E4M3) [*, K]; w: same dtype [G, N, K]; out: bf16 / f32 /
     uint8 (E4M3, needs out_scale).  With tail_groups > 0 the last tail_groups groups write
@@ -285,7 +285,8 @@ def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_tot
     FP8 scales are f32, or E8M0 codes when they are uint8 tensors (all of them alike).
     ws: the launch's workspace (default: the current stream's, see gemm_workspace).
     k_offsets: int32 offsets whose differences give each group's reduction length (ragged K,
-    f32 output only; the K columns past a group's length rounded up to a K step are not read)."""
+    f32 output only; the K columns past a group's length rounded up to a K step are not read).
+    out_preact: with swiglu, an f32 [rows, N] tensor that also receives the gate | up products."""
     fp8 = a.dtype == torch.uint8
     scales = [s for s in (a_scale, w_scale, out_scale) if s is not None]
     e8 = fp8 and any(s.dtype == torch.uint8 for s in scales)
@@ -300,6 +301,10 @@ def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_tot
         _dev(k_offsets, torch.int32, "k_offsets")
         if k_offsets.numel() < first_group + n_groups + 1:
             raise ValueError("k_offsets needs first_group + n_groups + 1 entries")
+    if out_preact is not None:
+        _dev(out_preact, torch.float32, "out_preact", contiguous=False)
+        if out_preact.stride(-1) != 1:
+            raise ValueError("rows of out_preact must be contiguous")
     if tail_groups:
         _dev(out_tail, torch.float32, "out_tail", contiguous=False)
         if out_tail.stride(-1) != 1:
@@ -324,7 +329,9 @@ def moe_grouped_gemm(a, w, group_offsets, first_group: int, n_groups: int, m_tot
         ldo_tail=out_tail.stride(0) if tail_groups else 0,
         scale_fmt=MOE_SCALE_E8M0 if e8 else MOE_SCALE_F32, ldw=0 if ldw == K else ldw,
         ws=ws.data_ptr(), ws_bytes=ws.numel(),
-        k_offsets=k_offsets.data_ptr() if k_offsets is not None else None)
+        k_offsets=k_offsets.data_ptr() if k_offsets is not None else None,
+        out_preact=out_preact.data_ptr() if out_preact is not None else None,
+        ldo_preact=out_preact.stride(0) if out_preact is not None else 0)
     st = lib().moe_grouped_gemm(ctypes.byref(desc), _stream(a))
     _check("moe_grouped_gemm", st)
     return out

@@ -46,6 +46,6 @@ const char* moe_status_str(moe_status s) {
 
 const char* moe_last_error(void) { return moe::g_last_error.c_str(); }
 
-int moe_abi_version(void) { return 7; }
+int moe_abi_version(void) { return 8; }
 
 }  // extern "C"

@@ -104,6 +104,8 @@ struct GemmArgs {
   int64_t ldo_tail_b;   // bytes per tail output row
   unsigned int* sync;   // workspace: [8] round arrivals per XCD, [8] exit counter
   const int32_t* k_offs;  // per-group reduction lengths (k_offs[g + 1] - k_offs[g]), or null
+  uint8_t* out_pre;       // SwiGLU: f32 gate | up products before the epilogue, or null
+  int64_t ldo_pre_b;      // bytes per out_pre row
 };
 
 __device__ __forceinline__ float silu(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
@@ -165,7 +167,11 @@ __device__ __forceinline__ TileInfo decode_tile(int L, const int* tstart, int G,
 
 // FP8: 0 = bf16 inputs; 1 = E4M3 with f32 scales (promotion every K slice); 2 = E4M3 with
 // E8M0 scales (applied by the matrix core).
-template <int BM, int BN, int WGM, int WGN, int STAGES, int FP8, bool SWIGLU, int OUT>
+// PRE: the training forward's SwiGLU launch, which also stores the gate | up products
+// (out_pre); an instantiation of its own, so that the inference kernels carry none of its
+// registers (the pointer kept live through the loop cost the E4M3 gate/up 3% in spilled
+// scalar registers when it was a run-time option).
+template <int BM, int BN, int WGM, int WGN, int STAGES, int FP8, bool SWIGLU, int OUT, bool PRE>
 __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p) {
   constexpr bool E8 = FP8 == 2;
   constexpr int NW = WGM * WGN;
@@ -664,6 +670,45 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     }
   };
 
+  // ---- SwiGLU with out_pre: the gate and up products themselves (a | c, the epilogue's inputs)
+  // also stored, f32 rows of N columns (gate in [0, N/2), up in [N/2, N)), for a backward pass
+  // that would otherwise recompute them with a second gate/up GEMM ----
+  auto epi_preact = [&](const TileInfo& et) __attribute__((always_inline)) {
+    if constexpr (SWIGLU) {
+      const int64_t orow0 = (int64_t)(et.row0 - base_row);
+      const int half = p.N / 2;
+      if constexpr (FP8) {  // lane: row wm * WM + i * 16 + lr, columns c0 + jj * 16 + 0..3
+        const int c0 = et.nt * OC + wn * (WN / 2) + lg * 4;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int m = wm * WM + i * 16 + lr;
+          if (m >= et.nrows) continue;
+          float* prow = reinterpret_cast<float*>(p.out_pre + (orow0 + m) * p.ldo_pre_b);
+#pragma unroll
+          for (int jj = 0; jj < TO; ++jj) {
+            *reinterpret_cast<f32x4*>(prow + c0 + jj * 16) = acc[i][jj];
+            *reinterpret_cast<f32x4*>(prow + half + c0 + jj * 16) = acc[i][jj + TO];
+          }
+        }
+      } else {  // lane: rows wm * WM + i * 16 + lg * 4 + r, column c0 + jj * 16
+        const int c0 = et.nt * OC + wn * (WN / 2) + lr;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = wm * WM + i * 16 + lg * 4 + r;
+            if (m >= et.nrows) continue;
+            float* prow = reinterpret_cast<float*>(p.out_pre + (orow0 + m) * p.ldo_pre_b);
+#pragma unroll
+            for (int jj = 0; jj < TO; ++jj) {
+              prow[c0 + jj * 16] = acc[i][jj][r];
+              prow[half + c0 + jj * 16] = acc[i][jj + TO][r];
+            }
+          }
+      }
+    }
+  };
+
   // ---- epilogue of a tile: values (SwiGLU applied; the accumulators restart at zero), the
   // per-row amax of an E4M3 output into s_red, then the stores ----
   auto epi_values = [&](float(&v)[TM][TO][4]) __attribute__((always_inline)) {
@@ -852,6 +897,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       issue_scales();
 
       if (kt == ks - 1) {
+        if constexpr (SWIGLU && PRE) epi_preact(ct);
         float v[TM][TO][4];
         epi_values(v);
         if (OUT == OUT_FP8) {
@@ -907,13 +953,13 @@ int device_cus() {
 constexpr size_t kLdsBytes = 160 * 1024;
 
 // Static LDS of one kernel instantiation (queried once).
-template <int BM, int BN, int WGM, int WGN, int STAGES, int FP8, bool SWIGLU, int OUT>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int FP8, bool SWIGLU, int OUT, bool PRE>
 size_t static_lds() {
   static size_t bytes = 0;
   if (bytes == 0) {
     hipFuncAttributes attr;
-    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&grouped_gemm_kernel<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT>)) ==
-        hipSuccess)
+    const void* fn = reinterpret_cast<const void*>(&grouped_gemm_kernel<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT, PRE>);
+    if (hipFuncGetAttributes(&attr, fn) == hipSuccess)
       bytes = attr.sharedSizeBytes;
     else
       bytes = kLdsBytes;  // unknown: treat as full, so callers take a smaller configuration
@@ -921,12 +967,12 @@ size_t static_lds() {
   return bytes;
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, int FP8, bool SWIGLU, int OUT>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int FP8, bool SWIGLU, int OUT, bool PRE>
 bool fits(const GemmArgs& a) {
-  return static_lds<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT>() + (size_t)(a.n_groups + 1) * 4 <= kLdsBytes;
+  return static_lds<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT, PRE>() + (size_t)(a.n_groups + 1) * 4 <= kLdsBytes;
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, int FP8, bool SWIGLU, int OUT>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int FP8, bool SWIGLU, int OUT, bool PRE>
 void launch(GemmArgs a, int64_t m_total, hipStream_t stream) {
   a.n_tiles = a.out_cols / (SWIGLU ? BN / 2 : BN);
   const int64_t mtiles = (m_total + (int64_t)a.n_groups * (BM - 1)) / BM;
@@ -935,7 +981,7 @@ void launch(GemmArgs a, int64_t m_total, hipStream_t stream) {
   const int cus = device_cus();
   const int64_t grid = upper < cus ? ((upper + 7) / 8) * 8 : cus;
   const size_t dyn = (size_t)(a.n_groups + 1) * 4;  // the tile prefix table
-  grouped_gemm_kernel<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT><<<(unsigned)grid, WGM * WGN * 64, dyn, stream>>>(a);
+  grouped_gemm_kernel<BM, BN, WGM, WGN, STAGES, FP8, SWIGLU, OUT, PRE><<<(unsigned)grid, WGM * WGN * 64, dyn, stream>>>(a);
 }
 
 // Row-block height for bf16 groups of about mu rows (the group sizes live on the device, so
@@ -962,24 +1008,36 @@ bool prefer_tall_rows(int64_t m_total, int n_groups) {
 // where its LDS (147 KB of ring, the scale chunks and the tile table) fits, else two slots.
 // Decode-sized groups: 64-row blocks, 8 waves of 64x32.
 // Narrow bf16 outputs (N/2 or N not a multiple of 128 / 256): 128-column blocks, 4 waves.
-template <int FP8, bool SWIGLU, int OUT>
-void dispatch(const GemmArgs& a, int64_t m_total, bool small, bool narrow, hipStream_t stream) {
+template <int FP8, bool SWIGLU, int OUT, bool PRE>
+void dispatch_as(const GemmArgs& a, int64_t m_total, bool small, bool narrow, hipStream_t stream) {
   if constexpr (!FP8) {
     if (narrow) {
-      launch<64, 128, 1, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
+      launch<64, 128, 1, 4, 3, FP8, SWIGLU, OUT, PRE>(a, m_total, stream);
       return;
     }
   }
-  if (small) launch<64, 256, 1, 8, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
+  if (small) launch<64, 256, 1, 8, 3, FP8, SWIGLU, OUT, PRE>(a, m_total, stream);
   else if constexpr (!FP8) {
-    if (prefer_tall_rows(m_total, a.n_groups) && fits<160, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a))
-      launch<160, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
+    if (prefer_tall_rows(m_total, a.n_groups) && fits<160, 256, 2, 4, 3, FP8, SWIGLU, OUT, PRE>(a))
+      launch<160, 256, 2, 4, 3, FP8, SWIGLU, OUT, PRE>(a, m_total, stream);
     else
-      launch<128, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
+      launch<128, 256, 2, 4, 3, FP8, SWIGLU, OUT, PRE>(a, m_total, stream);
   } else {
-    if (fits<128, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a)) launch<128, 256, 2, 4, 3, FP8, SWIGLU, OUT>(a, m_total, stream);
-    else launch<128, 256, 2, 4, 2, FP8, SWIGLU, OUT>(a, m_total, stream);
+    if (fits<128, 256, 2, 4, 3, FP8, SWIGLU, OUT, PRE>(a)) launch<128, 256, 2, 4, 3, FP8, SWIGLU, OUT, PRE>(a, m_total, stream);
+    else launch<128, 256, 2, 4, 2, FP8, SWIGLU, OUT, PRE>(a, m_total, stream);
   }
+}
+
+// the preact kernels exist for the SwiGLU launches of bf16 and f32-scale E4M3 inputs
+template <int FP8, bool SWIGLU, int OUT>
+void dispatch(const GemmArgs& a, int64_t m_total, bool small, bool narrow, hipStream_t stream) {
+  if constexpr (SWIGLU && FP8 != 2) {
+    if (a.out_pre) {
+      dispatch_as<FP8, SWIGLU, OUT, true>(a, m_total, small, narrow, stream);
+      return;
+    }
+  }
+  dispatch_as<FP8, SWIGLU, OUT, false>(a, m_total, small, narrow, stream);
 }
 
 }  // namespace
@@ -1049,6 +1107,12 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
 
   MOE_REQUIRE(!d->k_offsets || (d->out_dtype == MOE_F32 && !swiglu && !e8), MOE_ERR_DTYPE,
               "moe_grouped_gemm: k_offsets needs an f32 output, epilogue NONE and f32 scales");
+  if (d->out_preact) {
+    MOE_REQUIRE(swiglu && !e8, MOE_ERR_DTYPE, "moe_grouped_gemm: out_preact needs the SwiGLU epilogue (bf16 or f32-scale FP8)");
+    MOE_REQUIRE(aligned16(d->out_preact) && d->ldo_preact >= d->N && (d->ldo_preact * 4) % 16 == 0, MOE_ERR_ALIGN,
+                "moe_grouped_gemm: out_preact must be 16-byte aligned with ldo_preact >= N (ldo_preact=%lld)",
+                (long long)d->ldo_preact);
+  }
 
   GemmArgs a;
   a.a = static_cast<const uint8_t*>(d->a);
@@ -1075,6 +1139,8 @@ extern "C" moe_status moe_grouped_gemm(const moe_gemm_desc* d, hipStream_t strea
   a.n_tiles = 0;  // set per tile shape at launch
   a.sync = static_cast<unsigned int*>(d->ws);
   a.k_offs = d->k_offsets ? d->k_offsets + d->first_group : nullptr;
+  a.out_pre = static_cast<uint8_t*>(d->out_preact);
+  a.ldo_pre_b = d->ldo_preact * 4;
   const bool narrow = !fp8 && d->N % 256 != 0;
 
   // Tile shape by regime: many rows per expert -> 128-row blocks; few (decode) -> 64.

@@ -50,7 +50,9 @@ class MoELayer:
 
     def forward(self, x, out_dtype=torch.bfloat16, update_bias: bool = False, gamma: float = 0.001,
                 keep: bool = False):
-        """x [T, d] bf16 -> out [T, d] (bf16 or f32).  With keep=True returns (out, buffers)."""
+        """x [T, d] bf16 -> out [T, d] (bf16 or f32).  With keep=True returns (out, buffers); the
+        buffers then also hold the gate/up products a | c (f32, written by the gate/up GEMM beside
+        h), which the backward takes instead of recomputing them."""
         T, d = x.shape
         N, K, I = self.N, self.top_k, self.I
         dev = x.device
@@ -63,16 +65,18 @@ class MoELayer:
             offs_ready = torch.cuda.Event()
             offs_ready.record()
         rows = T * (K + 1)
+        ac = torch.empty((rows, 2 * I), dtype=torch.float32, device=dev) if keep else None
         if self.fp8:
             xq, xs = (L.fp8_quant_1x128_e8m0 if self.e8m0 else L.fp8_quant_1x128)(x)
             h = torch.empty((rows, I), dtype=torch.uint8, device=dev)
             hs = torch.empty((rows, I // 128), dtype=xs.dtype, device=dev)
             L.moe_grouped_gemm(xq, self.W13, offs, 0, N + 1, rows, h, a_scale=xs, a_rows=sorted_token,
-                               w_scale=self.W13_s, swiglu=True, out_scale=hs)
+                               w_scale=self.W13_s, swiglu=True, out_scale=hs, out_preact=ac)
         else:
             xq = xs = hs = None
             h = torch.empty((rows, I), dtype=torch.bfloat16, device=dev)
-            L.moe_grouped_gemm(x, self.W13, offs, 0, N + 1, rows, h, a_rows=sorted_token, swiglu=True)
+            L.moe_grouped_gemm(x, self.W13, offs, 0, N + 1, rows, h, a_rows=sorted_token, swiglu=True,
+                               out_preact=ac)
         y = torch.empty((T * K, d), dtype=torch.bfloat16, device=dev)
         ysh = torch.empty((T, d), dtype=torch.float32, device=dev)
         # one launch for all N + 1 down projections: routed rows to y (bf16), the shared
@@ -86,7 +90,7 @@ class MoELayer:
             return out, {"x": x, "scores": scores, "topk_idx": idx, "topk_gate": gate, "expert_counts": counts,
                          "expert_offsets": offs, "expert_offsets_host": (offs_host, offs_ready),
                          "sorted_token": sorted_token, "pair_pos": pair_pos,
-                         "xq": xq, "xs": xs, "h": h, "hs": hs, "y": y, "y_shared": ysh}
+                         "xq": xq, "xs": xs, "h": h, "hs": hs, "ac": ac, "y": y, "y_shared": ysh}
         return out
 
     # ------------------------------------------------------------------ backward (bf16 path)
@@ -127,7 +131,8 @@ class MoELayer:
         the tokens and the transposed h (the stored E4M3 h, as bf16) and x in 128x128 blocks.
 
         Sequence: combine backward (dy, router logit gradients) -> Dgrad of the down projection
-        (dh = dy W2) -> gate/up recomputed without SwiGLU (a | c) -> SwiGLU backward -> Dgrad of
+        (dh = dy W2) -> [a | c from the forward, or the gate/up GEMM again without SwiGLU when the
+        buffers lack them] -> SwiGLU backward -> Dgrad of
         the gate/up projection (dx rows) -> two combines (router term + shared rows, then the
         routed rows) -> Wgrad per expert over transposed row segments -> router Wgrad."""
         W13T, W2T, W13T_s, W2T_s = self._transposed_weights()
@@ -151,21 +156,27 @@ class MoELayer:
         dy, du, du_row = cb[:3]
         extra = {}
         dh = torch.empty((rows, I), dtype=torch.float32, device=dev)
-        ac = torch.empty((rows, 2 * I), dtype=torch.float32, device=dev)
+        # a | c: cached by the forward's gate/up GEMM (the same fp32 values), else recomputed
+        ac = buf.get("ac")
+        recompute = ac is None
+        if recompute:
+            ac = torch.empty((rows, 2 * I), dtype=torch.float32, device=dev)
         dxr = torch.empty((T * K, d), dtype=torch.bfloat16, device=dev)
         dxs = torch.empty((T, d), dtype=torch.float32, device=dev)
         if fp8:
             dyq, dys = cb[3:]  # dy's 1x128 E4M3 form, written by the combine backward itself
             L.moe_grouped_gemm(dyq, W2T, offs, 0, G, rows, dh, a_scale=dys, w_scale=W2T_s)
-            L.moe_grouped_gemm(buf["xq"], self.W13, offs, 0, G, rows, ac, a_scale=buf["xs"], a_rows=st_,
-                               w_scale=self.W13_s)
+            if recompute:
+                L.moe_grouped_gemm(buf["xq"], self.W13, offs, 0, G, rows, ac, a_scale=buf["xs"], a_rows=st_,
+                                   w_scale=self.W13_s)
             dac, dacq, dacs = L.moe_swiglu_backward(ac, dh, fp8=True)
             L.moe_grouped_gemm(dacq, W13T, offs, 0, G, rows, dxr, a_scale=dacs, w_scale=W13T_s, out_tail=dxs,
                                tail_groups=1)
             extra.update(dyq=dyq, dys=dys, dacq=dacq, dacs=dacs)
         else:
             L.moe_grouped_gemm(dy, W2T, offs, 0, G, rows, dh)
-            L.moe_grouped_gemm(x, self.W13, offs, 0, G, rows, ac, a_rows=st_)
+            if recompute:
+                L.moe_grouped_gemm(x, self.W13, offs, 0, G, rows, ac, a_rows=st_)
             dac = L.moe_swiglu_backward(ac, dh)
             L.moe_grouped_gemm(dac, W13T, offs, 0, G, rows, dxr, out_tail=dxs, tail_groups=1)
         del ac, dh

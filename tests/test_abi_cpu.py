@@ -30,7 +30,7 @@ def test_header_declares_exactly_the_exports():
 
 def test_status_strings_and_version():
     L = _lib()
-    assert L.lib().moe_abi_version() == 7
+    assert L.lib().moe_abi_version() == 8
     assert L.status_str(0) == "MOE_OK" and L.status_str(5) == "MOE_ERR_WORKSPACE"
 
 
@@ -99,6 +99,12 @@ def _gemm(L, **kw):
     (dict(ws=None), 5), (dict(ws_bytes=255), 5), (dict(ws=8), 5),
     (dict(k_offsets=16, out_dtype=0), 3), (dict(k_offsets=16, epilogue=1, N=512, out_dtype=0, ldo=256), 3),
     (dict(k_offsets=16, in_dtype=2, a_scale=16, w_scale=16, scale_fmt=1, K=512, lda=512), 3),
+    (dict(out_preact=16, ldo_preact=256), 3),
+    (dict(out_preact=8, ldo_preact=512, epilogue=1, N=512, out_dtype=0), 4),
+    (dict(out_preact=16, ldo_preact=256, epilogue=1, N=512, out_dtype=0), 4),
+    (dict(out_preact=16, ldo_preact=514, epilogue=1, N=512, out_dtype=0), 4),
+    (dict(out_preact=16, ldo_preact=512, epilogue=1, N=512, out_dtype=2, in_dtype=2, a_scale=16, w_scale=16,
+          out_scale=16, scale_fmt=1, K=512, lda=512), 3),
 ])
 def test_gemm_rejects(kw, code):
     L = _lib()

@@ -439,3 +439,40 @@ def test_layer_backward_fp8(cfg):
         got = np64(g[name])
         e = np.sqrt(np.mean((got - ref[name]) ** 2)) / np.sqrt(np.mean(ref[name] ** 2))
         assert e <= 3e-2, (name, e)
+
+
+@pytest.mark.parametrize("cfg,fp8", [
+    (I.small(I.V3_BF16, name="bwd_cache_bf16", T=300, d=256, n_experts=16, top_k=4, inter=128, w_std=0.05,
+             router_std=0.05), False),
+    (I.small(I.V3_FP8, name="bwd_cache_fp8", T=300, d=512, n_experts=32, top_k=4, inter=256, w_std=0.04,
+             router_std=0.04), True),
+], ids=["bf16", "fp8"])
+def test_backward_cached_products_match_recompute(cfg, fp8):
+    """The training forward (keep=True) stores the gate/up products a | c beside h, and the
+    backward takes them instead of running the gate/up GEMM again; without them in the buffers
+    it recomputes them.  Both ways give the same gradients bit for bit, and the stored a | c
+    equal the recomputed ones."""
+    say(f"backward cached vs recomputed a | c {cfg.name}")
+    x, wr, bias, W13, W2 = _layer(cfg)
+    layer = M().MoELayer(wr.to(DEV), W13.to(DEV), W2.to(DEV), bias.to(DEV), cfg.top_k, fp8=fp8)
+    _, buf = layer.forward(x.to(DEV), out_dtype=torch.float32, keep=True)
+    assert buf["ac"] is not None and buf["ac"].shape == (cfg.T * (cfg.top_k + 1), 2 * cfg.inter)
+    d_out = I.gen_normal(cfg.seed + 900, (cfg.T, cfg.d), 1.0).to(DEV)
+    g1 = layer.backward(d_out, buf)
+    ac = buf["ac"].clone()
+    nobuf = dict(buf)
+    del nobuf["ac"]
+    g2 = layer.backward(d_out, nobuf)
+    torch.cuda.synchronize()
+    for k in ("dx", "dw_router", "dw13", "dw2"):
+        assert torch.equal(g1[k], g2[k]), k
+    # the recompute, as the backward runs it, against the stored products
+    rows = cfg.T * (cfg.top_k + 1)
+    again = torch.empty((rows, 2 * cfg.inter), dtype=torch.float32, device=DEV)
+    if fp8:
+        M().moe_grouped_gemm(buf["xq"], layer.W13, buf["expert_offsets"], 0, cfg.n_experts + 1, rows, again,
+                             a_scale=buf["xs"], a_rows=buf["sorted_token"], w_scale=layer.W13_s)
+    else:
+        M().moe_grouped_gemm(buf["x"], layer.W13, buf["expert_offsets"], 0, cfg.n_experts + 1, rows, again,
+                             a_rows=buf["sorted_token"])
+    assert torch.equal(again, ac)

@@ -411,7 +411,9 @@ def test_gemm_fp8_exact(sizes, K):
     (False, 256, [130, 0, 64, 200, 17, 129]),
     (True, 256, [130, 0, 64, 200, 17, 129]),
     (True, 4096, [640, 0, 385, 128, 1, 300]),  # 16+ column blocks: E4M3 tiles in bands of 2 row blocks
-], ids=["bf16", "fp8", "fp8_banded"])
+    (False, 128, [5, 30, 0, 17, 1, 60]),       # bf16 narrow output, 64-row tiles of 4 waves
+    (True, 256, [5, 30, 0, 17, 1, 60]),        # decode-sized groups: 64-row tiles
+], ids=["bf16", "fp8", "fp8_banded", "bf16_narrow_small", "fp8_small"])
 def test_gemm_ragged_k(fp8, N, m_sizes):
     """Per-group reduction lengths (k_offsets, the weight gradient's layout): group g sums only
     over its first len_g K columns rounded up to the K step (64 bf16 / 128 E4M3 elements, at
@@ -483,15 +485,65 @@ def test_gemm_ragged_k(fp8, N, m_sizes):
         assert not np.any(got[offs[g0]:offs[g0 + 1]]), "a zero-length reduction gives zeros"
 
 
+@pytest.mark.parametrize("fp8,out_kind,sizes,N", [
+    (False, "bf16", [150, 161, 0, 320, 97, 5, 170, 160], 512),   # 160-row blocks
+    (False, "bf16", [80, 0, 129, 40, 128, 97, 1], 512),           # 128-row blocks
+    (False, "bf16", [5, 30, 0, 17, 1, 60], 512),                  # decode-sized: 64-row blocks
+    (False, "bf16", [80, 0, 129, 40], 384),                       # narrow output: 64 x 128 tiles
+    (True, "fp8", [5, 130, 64, 300, 0, 129], 512),
+    (True, "bf16", [5, 130, 64, 300, 0, 129], 512),
+    (True, "fp8", [5, 30, 0, 17, 1, 60], 512),
+], ids=["bf16_rows160", "bf16_rows128", "bf16_small", "bf16_narrow", "fp8_h_fp8", "fp8_h_bf16", "fp8_small"])
+def test_gemm_swiglu_preact(fp8, out_kind, sizes, N):
+    """A SwiGLU launch with out_preact (the training forward) also stores the gate | up
+    products: they equal, bit for bit, the same launch without SwiGLU into an f32 output, and
+    the SwiGLU output (codes and scales) equals the launch without out_preact."""
+    K = 512
+    sizes = np.array(sizes)
+    G = len(sizes)
+    offs = _offsets(sizes)
+    rows = int(offs[-1])
+    T = 300
+    a_rows = torch.from_numpy(np.random.default_rng(31).integers(0, T, rows).astype(np.int32)).to(DEV)
+    A = I.gen_normal(32, (T, K), 1.0).to(DEV)
+    W = I.gen_normal(33, (G, N, K), 0.05).to(DEV)
+    o = torch.from_numpy(offs).to(DEV)
+    kw = {}
+    if fp8:
+        A, As = M().fp8_quant_1x128(A)
+        W, Ws = M().fp8_quant_128x128(W)
+        kw = dict(a_scale=As, w_scale=Ws)
+    hdt = torch.uint8 if out_kind == "fp8" else torch.bfloat16
+
+    def swiglu_out():
+        h = torch.full((rows, N // 2), 0x55 if out_kind == "fp8" else 7, dtype=hdt, device=DEV)
+        hs = torch.empty((rows, N // 256), dtype=torch.float32, device=DEV) if out_kind == "fp8" else None
+        return h, hs
+    h0, hs0 = swiglu_out()
+    M().moe_grouped_gemm(A, W, o, 0, G, rows, h0, a_rows=a_rows, swiglu=True, out_scale=hs0, **kw)
+    h1, hs1 = swiglu_out()
+    pre = torch.full((rows, N), float("nan"), dtype=torch.float32, device=DEV)
+    M().moe_grouped_gemm(A, W, o, 0, G, rows, h1, a_rows=a_rows, swiglu=True, out_scale=hs1, out_preact=pre, **kw)
+    ref = torch.full((rows, N), float("nan"), dtype=torch.float32, device=DEV)
+    M().moe_grouped_gemm(A, W, o, 0, G, rows, ref, a_rows=a_rows, **kw)
+    assert torch.equal(h0, h1)
+    if hs0 is not None:
+        assert torch.equal(hs0, hs1)
+    assert not torch.isnan(pre).any(), "every row and column written"
+    assert torch.equal(pre, ref)
+
+
 # FP8_DOT_REL: the fp8 dot-product error bound (see tests/gpu_common.py).
 
 
-@pytest.mark.parametrize("swiglu,G", [(True, 460), (False, 1000)], ids=["swiglu_fp8_out", "f32_out"])
-def test_gemm_fp8_two_slot_ring_matches_three(swiglu, G):
+@pytest.mark.parametrize("swiglu,G,ragged", [(True, 460, False), (False, 1000, False), (False, 1000, True)],
+                         ids=["swiglu_fp8_out", "f32_out", "f32_out_ragged_k"])
+def test_gemm_fp8_two_slot_ring_matches_three(swiglu, G, ragged):
     """An E4M3 launch whose tile table outgrows the three-slot ring's spare LDS takes the
     two-slot ring (SwiGLU with an E4M3 output: above 463 groups; f32 output: above 975); the
     same groups split over two launches take the three-slot ring.  The tile arithmetic does
-    not depend on the ring, so the outputs (codes and scales) agree bit for bit."""
+    not depend on the ring, so the outputs (codes and scales) agree bit for bit; also with a
+    ragged reduction (k_offsets: 1..256 columns per group)."""
     K, N = 256, 256
     sizes = np.random.default_rng(17).integers(60, 81, G)
     sizes[5] = 0
@@ -508,7 +560,12 @@ def test_gemm_fp8_two_slot_ring_matches_three(swiglu, G):
     else:
         one = torch.empty((rows, N), dtype=torch.float32, device=DEV)
         one_s = torch.empty((rows, 1), dtype=torch.float32, device=DEV)
-    kw = lambda s: dict(a_scale=As, w_scale=Ws, swiglu=True, out_scale=s) if swiglu else dict(a_scale=As, w_scale=Ws)
+    ko = None
+    if ragged:
+        lens = np.random.default_rng(18).integers(0, K + 1, G)
+        ko = torch.from_numpy(_offsets(lens)).to(DEV)
+    kw = lambda s: dict(a_scale=As, w_scale=Ws, swiglu=True, out_scale=s) if swiglu else dict(a_scale=As, w_scale=Ws,
+                                                                                             k_offsets=ko)
     M().moe_grouped_gemm(Aq, Wq, o, 0, G, rows, one, **kw(one_s))
     two = torch.empty_like(one)
     two_s = torch.empty_like(one_s)
