@@ -355,9 +355,9 @@ def decode_skew_sweep(torch, M, I, wr, W13, W2, dev, steps):
 def time_backward(torch, layer, x, d_out, n=3):
     """Mean times of n backward passes of `layer` for the forward of x (kept), after one warm-up
     pass that also makes the transposed weight copies (the weight gradients are reused), and of
-    n training forwards (keep=True: the forward that also stores what the backward takes, the
+    n training forwards (train=True: the forward that also stores what the backward takes, the
     gate/up products a | c among it)."""
-    _, buf = layer.forward(x, keep=True)
+    _, buf = layer.forward(x, train=True)
     g = layer.backward(d_out, buf)
     keep = {"dw13": g["dw13"], "dw2": g["dw2"]}
     del g
@@ -373,7 +373,7 @@ def time_backward(torch, layer, x, d_out, n=3):
     del buf
     s.record()
     for _ in range(n):
-        _, buf = layer.forward(x, keep=True)
+        _, buf = layer.forward(x, train=True)
         del buf
     e.record()
     torch.cuda.synchronize()

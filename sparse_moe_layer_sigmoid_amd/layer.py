@@ -49,10 +49,15 @@ class MoELayer:
             self.W2, self.W2_s = W2, None
 
     def forward(self, x, out_dtype=torch.bfloat16, update_bias: bool = False, gamma: float = 0.001,
-                keep: bool = False):
-        """x [T, d] bf16 -> out [T, d] (bf16 or f32).  With keep=True returns (out, buffers); the
-        buffers then also hold the gate/up products a | c (f32, written by the gate/up GEMM beside
-        h), which the backward takes instead of recomputing them."""
+                keep: bool = False, train: bool = False):
+        """x [T, d] bf16 -> out [T, d] (bf16 or f32).  With keep=True returns (out, buffers), which
+        the backward takes.  train=True (implies keep) is the training forward: the buffers then
+        also hold the gate/up products a | c (f32, written by the gate/up GEMM beside h), which
+        the backward takes instead of running the gate/up GEMM again."""
+        if train:
+            if self.e8m0:
+                raise NotImplementedError("the backward pass runs on the bf16 and the f32-scale FP8 paths")
+            keep = True
         T, d = x.shape
         N, K, I = self.N, self.top_k, self.I
         dev = x.device
@@ -65,7 +70,7 @@ class MoELayer:
             offs_ready = torch.cuda.Event()
             offs_ready.record()
         rows = T * (K + 1)
-        ac = torch.empty((rows, 2 * I), dtype=torch.float32, device=dev) if keep else None
+        ac = torch.empty((rows, 2 * I), dtype=torch.float32, device=dev) if train else None
         if self.fp8:
             xq, xs = (L.fp8_quant_1x128_e8m0 if self.e8m0 else L.fp8_quant_1x128)(x)
             h = torch.empty((rows, I), dtype=torch.uint8, device=dev)

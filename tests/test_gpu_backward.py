@@ -209,7 +209,7 @@ def test_layer_backward(cfg):
     say(f"layer backward {cfg.name}")
     x, wr, bias, W13, W2 = _layer(cfg)
     layer = M().MoELayer(wr.to(DEV), W13.to(DEV), W2.to(DEV), bias.to(DEV), cfg.top_k)
-    out, buf = layer.forward(x.to(DEV), out_dtype=torch.float32, keep=True)
+    out, buf = layer.forward(x.to(DEV), out_dtype=torch.float32, train=True)
     d_out = I.gen_normal(cfg.seed + 900, (cfg.T, cfg.d), 1.0)
     g = layer.backward(d_out.to(DEV), buf, keep=True)
     torch.cuda.synchronize()
@@ -333,7 +333,7 @@ def test_layer_backward_fp8(cfg):
     x, wr, bias, W13, W2 = _layer(cfg)
     W13d, W2d = W13.to(DEV), W2.to(DEV)
     layer = M().MoELayer(wr.to(DEV), W13d, W2d, bias.to(DEV), cfg.top_k, fp8=True)
-    out, buf = layer.forward(x.to(DEV), out_dtype=torch.float32, keep=True)
+    out, buf = layer.forward(x.to(DEV), out_dtype=torch.float32, train=True)
     d_out = I.gen_normal(cfg.seed + 900, (cfg.T, cfg.d), 1.0)
     g = layer.backward(d_out.to(DEV), buf, keep=True)
     torch.cuda.synchronize()
@@ -448,14 +448,14 @@ def test_layer_backward_fp8(cfg):
              router_std=0.04), True),
 ], ids=["bf16", "fp8"])
 def test_backward_cached_products_match_recompute(cfg, fp8):
-    """The training forward (keep=True) stores the gate/up products a | c beside h, and the
+    """The training forward (train=True) stores the gate/up products a | c beside h, and the
     backward takes them instead of running the gate/up GEMM again; without them in the buffers
-    it recomputes them.  Both ways give the same gradients bit for bit, and the stored a | c
+    (a forward with keep=True only) it recomputes them.  Both ways give the same gradients bit for bit, and the stored a | c
     equal the recomputed ones."""
     say(f"backward cached vs recomputed a | c {cfg.name}")
     x, wr, bias, W13, W2 = _layer(cfg)
     layer = M().MoELayer(wr.to(DEV), W13.to(DEV), W2.to(DEV), bias.to(DEV), cfg.top_k, fp8=fp8)
-    _, buf = layer.forward(x.to(DEV), out_dtype=torch.float32, keep=True)
+    _, buf = layer.forward(x.to(DEV), out_dtype=torch.float32, train=True)
     assert buf["ac"] is not None and buf["ac"].shape == (cfg.T * (cfg.top_k + 1), 2 * cfg.inter)
     d_out = I.gen_normal(cfg.seed + 900, (cfg.T, cfg.d), 1.0).to(DEV)
     g1 = layer.backward(d_out, buf)

@@ -240,7 +240,7 @@ def test_v3_bf16_T4096_backward(v3):
     x_cpu = I.gen_x(cfg)
     bias = I.gen_bias(cfg)
     layer = M().MoELayer(v3.wr, v3.W13, v3.W2, bias.to(DEV), cfg.top_k)
-    out, buf = layer.forward(x_cpu.to(DEV), out_dtype=torch.float32, keep=True)
+    out, buf = layer.forward(x_cpu.to(DEV), out_dtype=torch.float32, train=True)
     d_out = I.gen_normal(cfg.seed + 900, (cfg.T, cfg.d), 1.0)
     t0 = time.time()
     g = layer.backward(d_out.to(DEV), buf, keep=True)
@@ -305,7 +305,7 @@ def test_v3_fp8_T16384_backward(v3):
     x_cpu = I.gen_x(cfg)
     bias = I.gen_bias(cfg)
     layer = fp8_layer(v3, bias, cfg)
-    out, buf = layer.forward(x_cpu.to(DEV), out_dtype=torch.float32, keep=True)
+    out, buf = layer.forward(x_cpu.to(DEV), out_dtype=torch.float32, train=True)
     d_out = I.gen_normal(cfg.seed + 900, (cfg.T, cfg.d), 1.0)
     t0 = time.time()
     g = layer.backward(d_out.to(DEV), buf, keep=True)
