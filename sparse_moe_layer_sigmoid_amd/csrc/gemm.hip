@@ -577,7 +577,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   // lanes' rows at distinct swizzled chunks and hits distinct banks.  The scales of the K
   // block: s_A of the lane's four rows (one 16-byte read) and the two weight-block scales
   // (one broadcast read), combined into s_A * s_W per row tile.
-  auto fp8_read = [&](const uint8_t* As, int kt, int ks, i32x8(&af)[TM], i32x8(&bfr)[TN], float(&s0)[TM],
+  auto fp8_read = [&](const uint8_t* As, int kt, int tks, i32x8(&af)[TM], i32x8(&bfr)[TN], float(&s0)[TM],
                       float(&s1)[TM]) __attribute__((always_inline)) {
     const uint8_t* Bs = As + A_BYTES;
 #pragma unroll
@@ -603,7 +603,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       s0[i] = sa[i] * sw0;
       s1[i] = SWIGLU ? sa[i] * sw1 : s0[i];
     }
-    if (kc == SC_CH - 1 || kt == ks - 1) sc_use = sc_use + 1 == SC_NB ? 0 : sc_use + 1;  // chunk done
+    if (kc == SC_CH - 1 || kt == tks - 1) sc_use = sc_use + 1 == SC_NB ? 0 : sc_use + 1;  // chunk done
   };
   // Products with W as the first operand: a lane's four results of tile (i, jj) are columns
   // lg * 4 .. lg * 4 + 3 of row lr, so one combined scale covers them.  Every tile's partial
@@ -631,7 +631,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
   // ---- E8M0 K step: the same operand reads, the codes of the lane's four rows (one 16-byte
   // read, byte kc % 4 of each dword) and of the two weight blocks; every product goes straight
   // into its accumulator with the codes as the MFMA's block scales ----
-  auto e8_read = [&](const uint8_t* As, int kt, int ks, i32x8(&af)[TM], i32x8(&bfr)[TN], int(&sa)[TM], int& sw0,
+  auto e8_read = [&](const uint8_t* As, int kt, int tks, i32x8(&af)[TM], i32x8(&bfr)[TN], int(&sa)[TM], int& sw0,
                      int& sw1) __attribute__((always_inline)) {
     const uint8_t* Bs = As + A_BYTES;
 #pragma unroll
@@ -657,7 +657,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     const uint32_t w0 = swp[0], w1 = swp[SC_CH / 4];
     sw0 = (int)(((SWIGLU || (wn * WN) / 128 == 0 ? w0 : w1) >> sh) & 255u);
     sw1 = (int)((w1 >> sh) & 255u);
-    if (kc == SC_CH - 1 || kt == ks - 1) sc_use = sc_use + 1 == SC_NB ? 0 : sc_use + 1;  // chunk done
+    if (kc == SC_CH - 1 || kt == tks - 1) sc_use = sc_use + 1 == SC_NB ? 0 : sc_use + 1;  // chunk done
   };
   auto e8_math = [&](auto slot_c, const i32x8(&af)[TM], const i32x8(&bfr)[TN], const int(&sa)[TM], int sw0, int sw1)
       __attribute__((always_inline)) {
@@ -835,13 +835,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
     auto step = [&](auto slot_c, int j) __attribute__((always_inline)) {
       constexpr int SL = decltype(slot_c)::value;
       const uint8_t* As = SL == 0 ? slot0 : (SL == 1 ? slot1 : slot2);
-      int kt, ks;
+      int kt, tks;  // K step within the tile, the tile's K steps
       if constexpr (kRag) {
         kt = c_kt;
-        ks = c_ks;
+        tks = c_ks;
       } else {
         kt = j % ksteps;
-        ks = ksteps;
+        tks = ksteps;
       }
       if (kRoundSync && kt == 0 && j > 0) {  // a new round: arrive for the last one, wait for the XCD
         if (tid == 0) {
@@ -861,7 +861,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       // spread over this step's MFMAs
       constexpr auto dslot = std::integral_constant<int, (SL + STAGES - 1) % STAGES>();
       issue_prep(j + STAGES - 1);
-      if constexpr (!FP8) dma_now = kt != ks - 1;
+      if constexpr (!FP8) dma_now = kt != tks - 1;
 
       if constexpr (!FP8) {
         const uint8_t* Bs = As + A_BYTES;
@@ -886,17 +886,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
       } else if constexpr (E8) {
         i32x8 af[TM], bfr[TN];
         int sa[TM], sw0, sw1;
-        e8_read(As, kt, ks, af, bfr, sa, sw0, sw1);
+        e8_read(As, kt, tks, af, bfr, sa, sw0, sw1);
         e8_math(dslot, af, bfr, sa, sw0, sw1);
       } else {
         i32x8 af[TM], bfr[TN];
         float s0[TM], s1[TM];
-        fp8_read(As, kt, ks, af, bfr, s0, s1);
+        fp8_read(As, kt, tks, af, bfr, s0, s1);
         fp8_math(dslot, af, bfr, s0, s1);
       }
       issue_scales();
 
-      if (kt == ks - 1) {
+      if (kt == tks - 1) {
         if constexpr (SWIGLU && PRE) epi_preact(ct);
         float v[TM][TO][4];
         epi_values(v);
@@ -913,7 +913,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void grouped_gemm_kernel(GemmArgs p
         }
       }
       if constexpr (kRag) {
-        if (kt == ks - 1) {
+        if (kt == tks - 1) {
           ++c_q;
           c_kt = 0;
           c_ks = group_ksteps(ct.g);
