@@ -4,6 +4,7 @@
                     [--no-cpu-baseline]
     python bench.py --ceilings     (the chip's measured ceilings; no layer)
     python bench.py --backward-only   (the two backward workloads alone)
+    python bench.py --t-sweep         (the layer at T = 256 .. 32768, bf16 and E4M3)
 
 One step = one training-mode forward of one DeepSeekMoE layer over one batch of synthetic
 tokens: route -> permute -> [fp8 quantisation of x] -> gate/up grouped GEMM + SwiGLU ->
@@ -53,6 +54,9 @@ def parse():
                    help="first copy 1 GiB device-to-device twice (the reference dispatch for HBM counters)")
     p.add_argument("--backward-only", action="store_true",
                    help="time only the two backward workloads (bf16 T = 4096, E4M3 T = 16384) and print one JSON line")
+    p.add_argument("--t-sweep", action="store_true",
+                   help="time the V3-shaped layer (bf16 and E4M3, bias update on) at T = 256 .. 32768 and print "
+                        "one JSON line")
     p.add_argument("--ceilings", action="store_true",
                    help="run the ceiling micro-benchmarks (HBM read, DMA read in the GEMM's pattern, copy, "
                         "LDS read, matrix cores, fp32 FMA) instead of the layer and print one JSON line")
@@ -425,6 +429,44 @@ def run_backward_only(torch, M, I, dev):
     return out
 
 
+def run_t_sweep(torch, M, I, dev, steps=10, warmup=3):
+    """The V3-shaped layer against the batch size: for each T the same seeded x every step,
+    `warmup` untimed and `steps` timed forwards with the bias update (events on the stream),
+    the bias restored between sizes."""
+    c = I.V3_BF16
+    W13, W2 = I.gen_all_weights(c, dev)
+    wr = I.gen_router(c).to(torch.bfloat16).to(dev)
+    out = []
+    for fp8 in (False, True):
+        layer = M.MoELayer(wr, W13, W2, I.gen_bias(c).to(dev), c.top_k, fp8=fp8)
+        b0 = layer.bias.clone()
+        for T in (256, 1024, 2048, 4096, 8192, 16384, 32768):
+            cfg = I.small(c, T=T, name=f"v3_T{T}")
+            x = I.gen_x(cfg).to(dev)
+            for _ in range(warmup):
+                layer.forward(x, update_bias=True, gamma=c.gamma)
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(steps):
+                layer.forward(x, update_bias=True, gamma=c.gamma)
+            e.record()
+            torch.cuda.synchronize()
+            ms = s.elapsed_time(e) / steps
+            layer.bias.copy_(b0)
+            fl = layer_flops(cfg)
+            peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
+            out.append({"dtype": "fp8" if fp8 else "bf16", "T": T, "ms_per_step": round(ms, 4),
+                        "tokens_per_s": round(T / (ms / 1e3), 1), "tflops": round(fl / (ms / 1e3) / 1e12, 1),
+                        "mfma_frac": round(fl / (ms / 1e3) / 1e12 / peak, 4)})
+            log(f"[bench] t-sweep {out[-1]}")
+            del x
+            torch.cuda.empty_cache()
+        del layer
+        torch.cuda.empty_cache()
+    return out
+
+
 def run_ceilings(torch, dev):
     """The chip's measured ceilings from libmoe_ceilings.so: each probe warmed up twice, then
     timed five times with HIP events on the stream it runs on (the best run is reported);
@@ -598,6 +640,9 @@ def main():
         return
     if args.backward_only:
         print(json.dumps({"backward": run_backward_only(torch, M, I, dev)}), flush=True)
+        return
+    if args.t_sweep:
+        print(json.dumps({"t_sweep": run_t_sweep(torch, M, I, dev)}), flush=True)
         return
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
