@@ -207,3 +207,16 @@ def test_layer_fp8_e8m0(cfg):
         f"(tol {FP8_TOL}); end to end vs the oracle's fp8_e8m0 pipeline {err:.2e}")
     if cfg.inter >= 2048:   # end to end at the layer's width; the staged check carries reduced widths
         fp8_end_to_end_bar(err, cfg.name)
+
+
+def test_training_forward_refused_with_e8m0_scales():
+    """The backward runs on the bf16 and f32-scale FP8 paths only, so the training forward of
+    an E8M0 layer refuses before launching anything (a kept forward still runs)."""
+    cfg = I.small(I.V3_FP8, name="e8m0_train", T=32, d=512, n_experts=8, top_k=2, inter=512, w_std=0.05,
+                  router_std=0.05)
+    x, wr, bias, W13, W2 = _layer_case(cfg)
+    layer = M().MoELayer(wr.to(DEV), W13.to(DEV), W2.to(DEV), bias.to(DEV), cfg.top_k, fp8=True, fp8_scales="e8m0")
+    with pytest.raises(NotImplementedError):
+        layer.forward(x.to(DEV), train=True)
+    _, buf = layer.forward(x.to(DEV), keep=True)
+    assert buf["ac"] is None
