@@ -1,0 +1,115 @@
+"""Randomised shapes for moe_grouped_gemm: 24 seeded draws of dtype (bf16 / E4M3), mode (f32
+output, bf16 output with an f32 tail split, SwiGLU, ragged reduction), group count and sizes
+(empty groups included), K, N, gathered or plain rows and a sub-range of the groups, each against
+a float64 product of the same operands.  E4M3 operands are codes of small integers with
+power-of-two scales, so their sums are exact in fp32 and those outputs must match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from sparse_moe_layer_sigmoid_amd import inputs as I
+from tests.gpu_common import np64, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def M():
+    import sparse_moe_layer_sigmoid_amd as m
+    return m
+
+
+def _draw(seed):
+    r = np.random.default_rng(7000 + seed)
+    fp8 = bool(r.random() < 0.5)
+    mode = ["f32", "tail", "swiglu", "ragged"][seed % 4]
+    G = int(r.integers(1, 41))
+    sizes = r.integers(0, 301, G)
+    sizes[r.random(G) < 0.15] = 0
+    gran = 128 if fp8 else 64
+    K = gran * int(r.integers(1, 9))
+    N = (256 if fp8 else 128) * int(r.integers(1, 3 if fp8 else 5))
+    gather = bool(r.random() < 0.5)
+    first = int(r.integers(0, G)) if r.random() < 0.3 else 0
+    n_groups = G - first
+    tail = int(r.integers(1, min(2, n_groups) + 1)) if mode == "tail" else 0
+    return r, fp8, mode, G, sizes, gran, K, N, gather, first, n_groups, tail
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_gemm_random_shapes(seed):
+    r, fp8, mode, G, sizes, gran, K, N, gather, first, n_groups, tail = _draw(seed)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows_all = int(offs[-1])
+    base = int(offs[first])
+    m_total = int(offs[first + n_groups]) - base
+    say(f"random gemm seed {seed}: {'E4M3' if fp8 else 'bf16'} {mode} G={G} first={first} K={K} N={N} "
+        f"rows={m_total} gather={gather}")
+    T = int(r.integers(1, 400)) if gather else max(rows_all, 1)
+    a_rows = r.integers(0, T, max(rows_all, 1)).astype(np.int32) if gather else None
+    if fp8:
+        A = I.gen_e4m3_codes(100 + seed, (T, K), small_int=True)
+        W = I.gen_e4m3_codes(200 + seed, (G, N, K), small_int=True)
+        As = torch.where(I.gen_scales(300 + seed, (T, K // 128), pow2=True) <= 2.0 ** -6, 2.0 ** -4, 2.0 ** -3).float()
+        Ws = torch.where(I.gen_scales(400 + seed, (G, N // 128, K // 128), pow2=True) <= 2.0 ** -6, 2.0 ** -5,
+                         2.0 ** -4).float()
+        Ad = O.dequant_1x128(A.numpy(), As.numpy())
+        Wd = np.stack([O.dequant_128x128(W[g].numpy(), Ws[g].numpy()) for g in range(G)])
+        kw = dict(a_scale=As.to(DEV), w_scale=Ws.to(DEV))
+    else:
+        A = I.gen_normal(100 + seed, (T, K), 1.0)
+        W = I.gen_normal(200 + seed, (G, N, K), 0.05)
+        Ad, Wd = np64(A), np64(W)
+        kw = {}
+    o = torch.from_numpy(offs).to(DEV)
+    if gather:
+        kw["a_rows"] = torch.from_numpy(a_rows).to(DEV)
+    kg = None
+    if mode == "ragged":
+        lens = r.integers(0, K + 1, G)
+        kw["k_offsets"] = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(DEV)
+        kg = np.minimum(K, np.maximum(gran, -(-lens // gran) * gran))
+    swiglu = mode == "swiglu"
+    oc = N // 2 if swiglu else N
+    if mode in ("f32", "ragged"):
+        out = torch.full((max(m_total, 1), oc), float("nan"), dtype=torch.float32, device=DEV)
+    else:
+        out = torch.full((max(m_total, 1), oc), float("nan"), dtype=torch.bfloat16, device=DEV)
+    if tail:
+        t_first = first + n_groups - tail
+        t_rows = int(offs[first + n_groups]) - int(offs[t_first])
+        out_tail = torch.full((max(t_rows, 1), N), float("nan"), dtype=torch.float32, device=DEV)
+        kw.update(out_tail=out_tail, tail_groups=tail)
+    M().moe_grouped_gemm(A.to(DEV), W.to(DEV), o, first, n_groups, m_total, out[:m_total], swiglu=swiglu, **kw)
+    got = np64(out)
+    got_tail = np64(out_tail) if tail else None
+    for g in range(first, first + n_groups):
+        lo, hi = int(offs[g]), int(offs[g + 1])
+        if hi == lo:
+            continue
+        src = a_rows[lo:hi] if gather else np.arange(lo, hi)
+        k = int(kg[g]) if kg is not None else K
+        a, w = Ad[src, :k], Wd[g, :, :k]
+        if swiglu:
+            ref = O.swiglu_hidden(a, Wd[g])
+        else:
+            ref = a @ w.T
+        in_tail = tail and g >= first + n_groups - tail
+        if in_tail:
+            dst = got_tail[lo - int(offs[first + n_groups - tail]):hi - int(offs[first + n_groups - tail])]
+        else:
+            dst = got[lo - base:hi - base]
+        rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+        if mode in ("f32", "ragged") or in_tail:
+            if fp8:
+                assert np.array_equal(dst, ref), (seed, g)
+            else:
+                assert np.max(np.abs(dst - ref)) <= 1e-5 * max(rms, 1e-30), (seed, g)
+        elif swiglu:  # silu in fp32 on the matrix cores' sums, then one bf16 rounding
+            assert np.all(np.abs(dst - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-5 * rms), (seed, g)
+        else:  # bf16 output: one rounding of the fp32 sum (exact for E4M3 operands)
+            if fp8:
+                assert np.array_equal(dst, O.bf16_round(ref.astype(np.float32)).astype(np.float64)), (seed, g)
+            else:
+                assert np.all(np.abs(dst - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6 * rms), (seed, g)
