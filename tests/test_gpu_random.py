@@ -1,15 +1,22 @@
-"""Randomised shapes for moe_grouped_gemm: 24 seeded draws of dtype (bf16 / E4M3), mode (f32
-output, bf16 output with an f32 tail split, SwiGLU, ragged reduction), group count and sizes
-(empty groups included), K, N, gathered or plain rows and a sub-range of the groups, each against
-a float64 product of the same operands.  E4M3 operands are codes of small integers with
-power-of-two scales, so their sums are exact in fp32 and those outputs must match bit for bit."""
+"""Randomised shapes, seeded, against the oracle or float64.
+
+moe_grouped_gemm: 24 draws of dtype (bf16 / E4M3), mode (f32 output, bf16 output with an f32
+tail split, SwiGLU, ragged reduction), group count and sizes (empty groups included), K, N,
+gathered or plain rows and a sub-range of the groups, each against a float64 product of the same
+operands.  E4M3 operands are codes of small integers with power-of-two scales, so their sums are
+exact in fp32 and those outputs must match bit for bit.
+
+moe_route + moe_permute + moe_combine: 16 draws of T, d, the expert count, top-K and the group
+limit: routing against the oracle's (sets exact outside the tie window, gates within 1e-6), the
+permutation of the device's own routing bit-exact against the oracle's counting sort, and the
+combine of random rows within the fp32 accumulation of the oracle's float64 sum."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import moe_oracle as O
 from sparse_moe_layer_sigmoid_amd import inputs as I
-from tests.gpu_common import np64, say
+from tests.gpu_common import check_route, np64, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -113,3 +120,47 @@ def test_gemm_random_shapes(seed):
                 assert np.array_equal(dst, O.bf16_round(ref.astype(np.float32)).astype(np.float64)), (seed, g)
             else:
                 assert np.all(np.abs(dst - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6 * rms), (seed, g)
+
+
+def _route_draw(seed):
+    r = np.random.default_rng(9000 + seed)
+    N = int(r.choice([8, 16, 32, 64, 128, 256]))
+    ng, tg = 1, 1
+    if r.random() < 0.5:
+        cands = [g for g in (2, 4, 8, 16, 32, 64) if N % g == 0 and N // g >= 4]
+        if cands:
+            ng = int(r.choice(cands))
+            tg = int(r.integers(1, ng + 1))
+    K = int(r.integers(1, min(N, tg * (N // ng), 16) + 1))
+    T = int(r.integers(0, 3000))
+    d = 64 * int(r.integers(1, 17))
+    return r, T, d, N, K, ng, tg
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_route_permute_combine_random(seed):
+    r, T, d, N, K, ng, tg = _route_draw(seed)
+    say(f"random route seed {seed}: T={T} d={d} N={N} K={K} groups={ng}/{tg}")
+    x = I.gen_normal(500 + seed, (T, d), 1.0)
+    wr = I.gen_normal(600 + seed, (N, d), 0.5 / np.sqrt(d))
+    bias = torch.from_numpy(r.uniform(-0.02, 0.02, N).astype(np.float32))
+    idx, gate, counts, scores = M().moe_route(x.to(DEV), wr.to(DEV), bias.to(DEV), K, ng, tg, want_scores=True)
+    ro = O.route(np64(x), np64(wr), bias.numpy(), K, ng, tg)
+    if T > 0:
+        check_route(idx, gate, counts, scores, ro, N, K)
+    else:
+        assert not counts.cpu().numpy().any()
+    # the permutation of the device's own routing, bit-exact
+    offs, st, pp = M().moe_permute(idx, N, 1)
+    want_offs, want_st, want_pp = O.permute(idx.cpu().numpy(), N, 1)
+    assert np.array_equal(offs.cpu().numpy(), want_offs)
+    assert np.array_equal(st.cpu().numpy(), want_st)
+    assert np.array_equal(pp.cpu().numpy(), want_pp)
+    # the combine of random routed rows (bf16) and shared rows (f32) with the device's gates
+    if T > 0:
+        y = I.gen_normal(700 + seed, (T * K, d), 1.0)
+        ysh = I.gen_normal(800 + seed, (T, d), 1.0, dtype=torch.float32)
+        out = M().moe_combine(y.to(DEV), ysh.to(DEV), pp, gate, torch.float32)
+        ref = O.combine(np64(y), np64(ysh), pp.cpu().numpy(), gate.cpu().numpy().astype(np.float64))
+        bound = (K + 1) * 2.0 ** -23 * (np.abs(np64(ysh)) + np.abs(np64(y))[pp.cpu().numpy()].sum(axis=1)) + 1e-30
+        assert np.all(np.abs(np64(out) - ref) <= bound)
