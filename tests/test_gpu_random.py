@@ -9,7 +9,10 @@ exact in fp32 and those outputs must match bit for bit.
 moe_route + moe_permute + moe_combine: 16 draws of T, d, the expert count, top-K and the group
 limit: routing against the oracle's (sets exact outside the tie window, gates within 1e-6), the
 permutation of the device's own routing bit-exact against the oracle's counting sort, and the
-combine of random rows within the fp32 accumulation of the oracle's float64 sum."""
+combine of random rows within the fp32 accumulation of the oracle's float64 sum.
+
+moe_segment_transpose / moe_segment_transpose_fp8: 12 draws of segment counts and lengths, block
+width, channel count and gathered rows."""
 import numpy as np
 import pytest
 import torch
@@ -164,3 +167,54 @@ def test_route_permute_combine_random(seed):
         ref = O.combine(np64(y), np64(ysh), pp.cpu().numpy(), gate.cpu().numpy().astype(np.float64))
         bound = (K + 1) * 2.0 ** -23 * (np.abs(np64(ysh)) + np.abs(np64(y))[pp.cpu().numpy()].sum(axis=1)) + 1e-30
         assert np.all(np.abs(np64(out) - ref) <= bound)
+
+
+def _transpose_draw(seed):
+    r = np.random.default_rng(11000 + seed)
+    fp8 = bool(seed % 2)
+    n_seg = int(r.integers(1, 21))
+    lens = r.integers(0, 301, n_seg)
+    lens[r.random(n_seg) < 0.15] = 0
+    gran = 128 if fp8 else 64
+    width = gran * int(r.integers(max(1, -(-int(lens.max()) // gran)), max(1, -(-int(lens.max()) // gran)) + 3))
+    C = (128 if fp8 else 8) * int(r.integers(1, 5 if fp8 else 65))
+    gather = bool(r.random() < 0.5)
+    return r, fp8, lens, width, C, gather
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_segment_transpose_random(seed):
+    """Random segments into equal-width blocks [n][C][width] (bf16: exact copies with zero padding;
+    E4M3: the oracle's 1x128 or 128x128 quantisers applied to those padded bf16 blocks)."""
+    r, fp8, lens, width, C, gather = _transpose_draw(seed)
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    n_seg, rows = len(lens), int(offs[-1])
+    n_src = int(r.integers(1, 600)) if gather else max(rows, 1)
+    say(f"random transpose seed {seed}: {'E4M3' if fp8 else 'bf16'} segments={n_seg} rows={rows} C={C} "
+        f"width={width} gather={gather}")
+    src = I.gen_normal(900 + seed, (n_src, C), 1.0)
+    g_rows = r.integers(0, n_src, max(rows, 1)).astype(np.int32) if gather else None
+    s_ = src.float().numpy()
+    blocks = np.zeros((n_seg, C, width), dtype=np.float32)
+    for g in range(n_seg):
+        sel = g_rows[offs[g]:offs[g + 1]] if gather else np.arange(offs[g], offs[g + 1])
+        blocks[g, :, :lens[g]] = s_[sel].T
+    o = torch.from_numpy(offs).to(DEV)
+    kw = dict(src_rows=torch.from_numpy(g_rows).to(DEV)) if gather else {}
+    if fp8:
+        block = bool(r.random() < 0.5)
+        q, sc = M()._lib.moe_segment_transpose_fp8(src.to(DEV), o, width, block_scales=block, **kw)
+        if block:
+            for g in range(n_seg):
+                wq, ws = O.quant_128x128(blocks[g])
+                assert np.array_equal(q[g].cpu().numpy(), wq), g
+                assert np.array_equal(sc[g].cpu().numpy(), ws), g
+        else:
+            wq, ws = O.quant_1x128(blocks.reshape(n_seg * C, width))
+            assert np.array_equal(q.cpu().numpy().reshape(n_seg * C, width), wq)
+            assert np.array_equal(sc.cpu().numpy(), ws)
+    else:
+        cols = np.arange(0, (n_seg + 1) * width, width).astype(np.int32)
+        out = M()._lib.moe_segment_transpose(src.to(DEV), o, torch.from_numpy(cols).to(DEV), n_seg * width,
+                                             width=width, **kw)
+        assert np.array_equal(out.float().cpu().numpy(), blocks)
