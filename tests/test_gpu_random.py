@@ -218,3 +218,74 @@ def test_segment_transpose_random(seed):
         out = M()._lib.moe_segment_transpose(src.to(DEV), o, torch.from_numpy(cols).to(DEV), n_seg * width,
                                              width=width, **kw)
         assert np.array_equal(out.float().cpu().numpy(), blocks)
+
+
+def _layer_draw(seed):
+    r = np.random.default_rng(13000 + seed)
+    N = int(r.choice([8, 16, 32, 64]))
+    ng, tg = 1, 1
+    if r.random() < 0.4:
+        cands = [g for g in (2, 4, 8) if N % g == 0 and N // g >= 4]
+        if cands:
+            ng = int(r.choice(cands))
+            tg = int(r.integers(1, ng + 1))
+    K = int(r.integers(1, min(8, tg * (N // ng)) + 1))
+    T = int(r.integers(1, 401))
+    d = 128 * int(r.integers(1, 5))
+    inter = 64 * int(r.integers(1, 5))
+    return I.small(I.V3_BF16, name=f"rand_layer_{seed}", T=T, d=d, n_experts=N, top_k=K, inter=inter, n_group=ng,
+                   topk_group=tg, w_std=0.05, router_std=0.05, seed=14000 + seed)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_layer_bf16_random(seed):
+    """Whole bf16 layers of random shape (T, d, expert count, top-K down to 1, group limit,
+    width), stage by stage against float64 recomputed from the device's own upstream values:
+    the routing against the oracle's; h = silu(a) c within one bf16 rounding of the float64 SwiGLU
+    of x and W13; each routed row within one bf16 rounding, and the shared rows within fp32
+    accumulation, of the float64 product of the device's h and W2; the output within the fp32
+    accumulation of the combine of the device's rows.  The error against the oracle's bf16 model
+    end to end is reported (with one expert per token a single bf16 rounding of a row near a
+    midpoint can move an output element by 2^-7 of that row, beyond the 1e-2 bar of the K = 8
+    layer)."""
+    from tests.gpu_common import rel_err
+    cfg = _layer_draw(seed)
+    say(f"random layer seed {seed}: T={cfg.T} d={cfg.d} N={cfg.n_experts} K={cfg.top_k} I={cfg.inter} "
+        f"groups={cfg.n_group}/{cfg.topk_group}")
+    x = I.gen_x(cfg).to(torch.bfloat16)
+    wr = I.gen_router(cfg).to(torch.bfloat16)
+    bias = I.gen_bias(cfg)
+    ex = [I.gen_expert(cfg, e) for e in range(cfg.groups)]
+    W13 = torch.stack([a for a, _ in ex]).to(torch.bfloat16)
+    W2 = torch.stack([b for _, b in ex]).to(torch.bfloat16)
+    layer = M().MoELayer(wr.to(DEV), W13.to(DEV), W2.to(DEV), bias.to(DEV), cfg.top_k, cfg.n_group, cfg.topk_group)
+    out32, buf = layer.forward(x.to(DEV), out_dtype=torch.float32, keep=True)
+    x64 = np64(x)
+    r = O.route(x64, np64(wr), bias.numpy(), cfg.top_k, cfg.n_group, cfg.topk_group)
+    tie = check_route(buf["topk_idx"], buf["topk_gate"], buf["expert_counts"], None, r, cfg.n_experts, cfg.top_k)
+    W13n, W2n = np64(W13), np64(W2)
+    offs = buf["expert_offsets"].cpu().numpy()
+    st = buf["sorted_token"].cpu().numpy()
+    hd, yd, ysd = np64(buf["h"]), np64(buf["y"]), np64(buf["y_shared"])
+    N, T = cfg.n_experts, cfg.T
+    for e in range(N + 1):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        if hi == lo:
+            continue
+        h64 = O.swiglu_hidden(x64[st[lo:hi]], W13n[e])
+        hr = float(np.sqrt(np.mean(h64 ** 2)))
+        assert np.all(np.abs(hd[lo:hi] - h64) <= np.abs(h64) * 2.0 ** -8 + 1e-5 * hr), (seed, e, "h")
+        y64 = hd[lo:hi] @ W2n[e].T
+        yrms = float(np.sqrt(np.mean(y64 ** 2)))
+        if e < N:
+            assert np.all(np.abs(yd[lo:hi] - y64) <= np.abs(y64) * 2.0 ** -8 + 1e-6 * yrms), (seed, e, "y")
+        else:
+            assert np.max(np.abs(ysd - y64)) <= 1e-5 * yrms, (seed, "shared y")
+    pp = buf["pair_pos"].cpu().numpy()
+    gate = buf["topk_gate"].cpu().numpy().astype(np.float64)
+    comb = ysd + np.einsum("tk,tkd->td", gate, yd[pp])
+    terms = np.abs(ysd) + np.einsum("tk,tkd->td", np.abs(gate), np.abs(yd[pp]))
+    assert np.all(np.abs(np64(out32) - comb) <= (cfg.top_k + 1) * 2.0 ** -23 * terms + 1e-30), (seed, "combine")
+    ref, _ = O.forward_sparse(x64, r["idx"], r["gate"], N, lambda e: (W13n[e], W2n[e]), "bf16")
+    keep = ~tie
+    say(f"  max|err|/rms vs the oracle's bf16 model {rel_err(np64(out32)[keep], ref[keep]):.2e}")
