@@ -11,9 +11,10 @@
 // Five kernels:
 //  1. logits: a split-K MFMA GEMM.  A workgroup (8 waves of 64 tokens x 64 experts) owns 128
 //     tokens x all experts x one K slice; x and router rows are staged through LDS in 128-byte
-//     K steps (double buffered, XOR-swizzled); every 256 elements of K the 16x16x32 bf16 MFMA
-//     partial sum is added into an fp32 accumulator (the matrix cores truncate inside their
-//     adder, so long chains are avoided).  Partial logits of each slice go to the workspace.
+//     K steps (double buffered, XOR-swizzled, global loads issued two steps ahead); every 256
+//     elements of K the 16x16x32 bf16 MFMA partial sum is added into an fp32 accumulator (the
+//     matrix cores truncate inside their adder, so long chains are avoided).  Partial logits of
+//     each slice go to the workspace.
 //  2. select: one wave per token (lane l holds experts 4l..4l+3) sums the slices in a fixed
 //     order, forms s and z, picks the top-K by wave-wide argmax rounds (ties to the lower
 //     index) and measures the decision margin: the gap between the K-th and (K+1)-th z, and
@@ -234,15 +235,19 @@ __global__ __launch_bounds__(kLogitsThreads) void route_logits_kernel(const uint
     }
     dst[i] = r * 128 + ((cch ^ (r & 7)) << 4);
   }
-  u32x4 reg[kChunks];
-  auto gload = [&](int ks) {
+  // two register sets: the global loads of step ks + 2 are issued while step ks computes and
+  // step ks + 1's data, loaded a step earlier, moves to LDS, so each load has two steps to land
+  u32x4 rA[kChunks], rB[kChunks];
+  // (the loads are unconditional -- rows past T or N read a clamped valid row -- and the dead
+  // rows are zeroed as they go to LDS, so no branch hides the loads' counts from the waits)
+  auto gload = [&](u32x4 (&reg)[kChunks], int ks) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) reg[i] = *(const u32x4*)(src[i] + (int64_t)ks * 128);
+  };
+  auto sstore = [&](const u32x4 (&reg)[kChunks], int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i)
-      reg[i] = live[i] ? *(const u32x4*)(src[i] + (int64_t)ks * 128) : u32x4{0u, 0u, 0u, 0u};
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) *(u32x4*)(smem + buf * STAGE + dst[i]) = reg[i];
+      *(u32x4*)(smem + buf * STAGE + dst[i]) = live[i] ? reg[i] : u32x4{0u, 0u, 0u, 0u};
   };
   f32x4 acc[4][4], prt[4][4];
 #pragma unroll
@@ -250,15 +255,18 @@ __global__ __launch_bounds__(kLogitsThreads) void route_logits_kernel(const uint
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = prt[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int lr = lane & 15, lg = lane >> 4;
+  // (every step issues its loads, the last steps re-reading step ks1 - 1, so the number of
+  // loads in flight is the same on every path and the waits can leave the newer ones pending)
   if (ks0 < ks1) {
-    gload(ks0);
-    sstore(0);
+    gload(rA, ks0);
+    sstore(rA, 0);
+    gload(rB, min(ks0 + 1, ks1 - 1));
   }
   __syncthreads();
-  for (int ks = ks0; ks < ks1; ++ks) {
+  // step ks: LDS buffer (ks - ks0) & 1 holds its data, `nxt` holds step ks + 1's, `fre` is free
+  auto step = [&](int ks, u32x4 (&nxt)[kChunks], u32x4 (&fre)[kChunks]) __attribute__((always_inline)) {
     const int cur = (ks - ks0) & 1;
-    const bool more = ks + 1 < ks1;
-    if (more) gload(ks + 1);
+    gload(fre, min(ks + 2, ks1 - 1));
     const uint8_t* S = smem + cur * STAGE;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -279,6 +287,7 @@ __global__ __launch_bounds__(kLogitsThreads) void route_logits_kernel(const uint
 #pragma unroll
         for (int j = 0; j < 4; ++j) prt[i][j] = mfma_bf16(af[i], bf[j], prt[i][j]);
     }
+    const bool more = ks + 1 < ks1;
     if (((ks + 1) & 3) == 0 || !more) {  // promote every 256 elements of K
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -288,9 +297,15 @@ __global__ __launch_bounds__(kLogitsThreads) void route_logits_kernel(const uint
           prt[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    if (more) sstore(cur ^ 1);
+    if (more) sstore(nxt, cur ^ 1);
     __syncthreads();
+  };
+  int ks = ks0;
+  for (; ks + 1 < ks1; ks += 2) {
+    step(ks, rB, rA);
+    step(ks + 1, rA, rB);
   }
+  if (ks < ks1) step(ks, rB, rA);
   float* out = part + (int64_t)split * T * 256;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -328,12 +343,15 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
 
 // ---- kernel 3a: fp64 logits of the flagged (near-tie) tokens ----
 // Workgroup (x, y) takes listed tokens x, x + gridDim.x, ... and experts 16y .. 16y + 15: wave
-// w computes experts 16y + w, 16y + w + 4, ...; its lanes split K into 16-byte chunks and keep
-// eight independent fp64 partial sums (one per element of a chunk), so the fp64 adds
-// pipeline.  Spreading a token over N / 16 workgroups keeps the router-row reads (the whole
-// W_r per token) off one CU: a handful of listed tokens used to take ~110 us.  Each logit
+// w computes experts 16y + w + 4j (j < 4) side by side; its lanes split K into 16-byte chunks
+// (lane l takes chunks l, l + 64, ...) and keep eight independent fp64 partial sums per expert
+// (one per element of a chunk), so the fp64 adds pipeline, and each pass loads kRefineU chunks
+// of the token and of the four expert rows before using any, so that the pass waits for one
+// memory latency rather than one per chunk and expert.  Spreading a token over N / 16
+// workgroups keeps the router-row reads (the whole W_r per token) off one CU.  Each logit
 // depends on its token and expert alone, so the list's order does not matter.
 constexpr int kRefineChunk = 16;  // experts per workgroup
+constexpr int kRefineU = 3;       // chunks per lane per pass
 __global__ __launch_bounds__(256) void route_refine_logits_kernel(const uint16_t* __restrict__ x,
                                                                   const uint16_t* __restrict__ wr, int d, int N,
                                                                   const int32_t* __restrict__ n_flagged,
@@ -342,26 +360,50 @@ __global__ __launch_bounds__(256) void route_refine_logits_kernel(const uint16_t
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nf = *n_flagged;
   const int nd = d / 8;  // 16-byte chunks per row
-  const int e0 = blockIdx.y * kRefineChunk, e1 = min(N, e0 + kRefineChunk);
+  const uint16_t* er[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) er[j] = wr + (int64_t)min(blockIdx.y * kRefineChunk + wave + 4 * j, N - 1) * d;
   for (int i = blockIdx.x; i < nf; i += gridDim.x) {
     const int64_t t = flagged[i];
     const uint16_t* xr = x + t * d;
-    for (int e = e0 + wave; e < e1; e += 4) {
-      const uint16_t* er = wr + (int64_t)e * d;
-      double a[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-      for (int c = lane; c < nd; c += 64) {
-        const u32x4 xv = *(const u32x4*)(xr + c * 8);
-        const u32x4 ev = *(const u32x4*)(er + c * 8);
-        float xf[8], ef[8];
-        unpack_bf16x8(xv, xf);
-        unpack_bf16x8(ev, ef);
+    double a[4][8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) a[q] += (double)(xf[q] * ef[q]);  // bf16 products are exact in fp32
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) a[j][q] = 0.0;
+    for (int c0 = lane; c0 < nd; c0 += 64 * kRefineU) {
+      u32x4 xv[kRefineU], ev[kRefineU][4];
+#pragma unroll
+      for (int u = 0; u < kRefineU; ++u) {  // chunks past the row re-read its last one, unused
+        const int c = min(c0 + 64 * u, nd - 1);
+        xv[u] = *(const u32x4*)(xr + c * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ev[u][j] = *(const u32x4*)(er[j] + c * 8);
       }
-      double sum = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+      __builtin_amdgcn_sched_barrier(0);  // keep the pass's loads together, ahead of their uses
+#pragma unroll
+      for (int u = 0; u < kRefineU; ++u) {
+        // a chunk past the row adds +0 (no branch, so the loads above stay batched; the sums
+        // start at +0 and never become -0, so adding +0 leaves them unchanged)
+        if (c0 + 64 * u >= nd) xv[u] = u32x4{0u, 0u, 0u, 0u};
+        float xf[8];
+        unpack_bf16x8(xv[u], xf);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float ef[8];
+          unpack_bf16x8(ev[u][j], ef);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) a[j][q] += (double)(xf[q] * ef[q]);  // bf16 products are exact in fp32
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      double sum = ((a[j][0] + a[j][1]) + (a[j][2] + a[j][3])) + ((a[j][4] + a[j][5]) + (a[j][6] + a[j][7]));
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
-      if (lane == 0) l64[(int64_t)i * 256 + e] = sum;
+      const int e = blockIdx.y * kRefineChunk + wave + 4 * j;
+      if (lane == 0 && e < N) l64[(int64_t)i * 256 + e] = sum;
     }
   }
 }
