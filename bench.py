@@ -478,6 +478,7 @@ def run_ceilings(torch, dev):
     P, S, I32, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int64
     lib.moe_ceil_hbm_read.argtypes = [P, S, P, S, I32, P]
     lib.moe_ceil_dma_read.argtypes = [P, I64, I32, P, S, I32, P]
+    lib.moe_ceil_dma_resident.argtypes = [I32, P, I32, I32, I32, P, P, S, I32, P]
     lib.moe_ceil_lds_read.argtypes = [I32, I32, P, P, S, I32, P]
     lib.moe_ceil_mfma.argtypes = [I32, I32, P, P, S, I32, P]
     lib.moe_ceil_valu.argtypes = [I32, P, P, S, I32, P]
@@ -519,6 +520,19 @@ def run_ceilings(torch, dev):
     ms = timed(lambda: lib.moe_ceil_dma_read(buf.data_ptr(), rows, row_bytes, sk, skn, cus, sp))
     out["hbm_read_dma_gemm_pattern_GBs"] = {"rows": rows, "row_bytes": row_bytes, "grid": cus,
                                             "GBs": round(rows * row_bytes / (ms / 1e3) / 1e9, 1)}
+    # the same step pattern over working sets held by one cache level: 8 row blocks of 256 rows x
+    # 2 KB read by every CU (4 MB: in each XCD's L2), and one 256-row x 1 KB block per CU (8 MB
+    # per XCD, past its 4 MB L2; 64 MB in all, inside the Infinity Cache), by direct-to-LDS DMA
+    # and by vector loads into registers
+    res = {}
+    for label, n_blocks, rbytes, steps in (("l2", 8, 2048, 1800), ("infinity_cache", cus, 1024, 240)):
+        for mode, how in ((0, "dma"), (1, "vector_loads")):
+            ms = timed(lambda: lib.moe_ceil_dma_resident(mode, buf.data_ptr(), n_blocks, rbytes, steps, cy, sk, skn,
+                                                         cus, sp))
+            per_cu = steps * 256 * 128
+            res[f"{label}_{how}"] = {"B_per_clk_per_CU": round(per_cu / med_cycles(), 1),
+                                     "TBs_chip": round(per_cu * cus / (ms / 1e3) / 1e12, 2)}
+    out["resident_read_gemm_pattern"] = res
     half = buf.numel() // 2
     src, dst = buf[:half], buf[half:]
     ms = timed(lambda: (dst.copy_(src), 0)[1])

@@ -7,6 +7,15 @@
 //                      grouped GEMM's weight pattern: blocks of 256 rows x 128 bytes, each wave
 //                      instruction 8 rows x 128 bytes, a three-slot LDS ring, one vmcnt wait
 //                      and one barrier per step, one workgroup per CU walking its row blocks
+//   moe_ceil_dma_resident  the same step pattern (256 rows x 128 bytes per step, 8 rows x 128 B
+//                      per wave instruction, three-slot ring) over a working set chosen to sit in
+//                      one cache level: workgroup b reads row block b % n_blocks over and over,
+//                      `steps` K steps of its rows (wrapping around the row length); mode 0
+//                      moves the data with direct-to-LDS DMA, mode 1 with 16-byte vector loads
+//                      into registers.  A few row blocks shared by every workgroup stay in the
+//                      L2; one row block per workgroup of a size the XCD's L2 cannot hold, but
+//                      the Infinity Cache can, is served from there.  Per-CU rate from the
+//                      workgroups' s_memtime cycles, chip rate from the launch time.
 //   moe_ceil_lds_read  LDS read bandwidth with ds_read_b128 (width 16) or ds_read_b64 (8),
 //                      one 8-wave workgroup per CU, conflict-free addresses; iters reads per
 //                      lane (a multiple of 16)
@@ -78,6 +87,65 @@ __global__ __launch_bounds__(512) void dma_read_kernel(const uint8_t* __restrict
     if (g + 2 < n) issue(g + 2);
   }
   sink[(size_t)blockIdx.x * 512 + threadIdx.x] = (uint32_t)n;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512) void dma_resident_kernel(const uint8_t* __restrict__ buf, int n_blocks, int row_bytes,
+                                                           int steps, uint64_t* cycles, uint32_t* sink) {
+  __shared__ __attribute__((aligned(1024))) uint8_t slot[3][kStep];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int steps_per_row = row_bytes / 128;
+  const uint8_t* base = buf + (int64_t)(blockIdx.x % n_blocks) * kRowsPerBlock * row_bytes + (lane & 7) * 16;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  u32x4 r[3][4];
+  // instruction j of wave w at step g: rows 8q .. 8q + 7 (q = 4w + j), the step's 128-byte slice
+  auto issue = [&](int g, auto slot_c) {
+    constexpr int s = decltype(slot_c)::value;
+    const int k = g % steps_per_row;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = wave * 4 + j;
+      const uint8_t* src = base + (int64_t)(q * 8 + (lane >> 3)) * row_bytes + k * 128;
+      if (MODE == 0)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(&slot[s][q * 1024]), 16, 0, 0);
+      else
+        r[s][j] = *(const u32x4*)src;
+    }
+  };
+  auto step = [&](int g, auto slot_c) {
+    constexpr int s = decltype(slot_c)::value;
+    CEIL_WAIT_VM(4);  // step g has landed (the 4 instructions of step g + 1 may still be in flight)
+    if (MODE == 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc ^= r[s][j];
+    }
+    __builtin_amdgcn_s_barrier();  // every wave is past step g - 1: its slot takes step g + 2
+    issue(g + 2, std::integral_constant<int, (s + 2) % 3>());
+  };
+  __syncthreads();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  issue(0, std::integral_constant<int, 0>());
+  issue(1, std::integral_constant<int, 1>());
+  for (int g = 0; g < steps; g += 3) {
+    step(g, std::integral_constant<int, 0>());
+    step(g + 1, std::integral_constant<int, 1>());
+    step(g + 2, std::integral_constant<int, 2>());
+  }
+  CEIL_WAIT_VM(0);  // the two batches issued past the last step
+  __syncthreads();
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  if (MODE == 1) {
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc ^= r[s][j];
+  } else {
+    acc[0] ^= slot[0][threadIdx.x];
+  }
+  sink[(size_t)blockIdx.x * 512 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (threadIdx.x == 0) cycles[blockIdx.x] = t1 - t0;
 }
 
 template <int WIDTH>
@@ -215,6 +283,19 @@ int moe_ceil_dma_read(const void* buf, int64_t rows, int row_bytes, uint32_t* si
     return -1;
   dma_read_kernel<<<grid, 512, 0, stream>>>(static_cast<const uint8_t*>(buf), (int)(rows / kRowsPerBlock),
                                             row_bytes, sink);
+  return launched();
+}
+
+// buf holds n_blocks x 256 rows x row_bytes bytes; row_bytes % 128 == 0; steps a positive
+// multiple of 3; cycles[grid] (u64) receives each workgroup's cycle count.
+int moe_ceil_dma_resident(int mode, const void* buf, int n_blocks, int row_bytes, int steps, uint64_t* cycles,
+                          uint32_t* sink, size_t sink_words, int grid, hipStream_t stream) {
+  if ((mode != 0 && mode != 1) || !buf || !cycles || !sink || n_blocks < 1 || row_bytes < 128 || row_bytes % 128 ||
+      steps < 3 || steps % 3 || ((uintptr_t)buf & 15) || grid < 1 || sink_words < (size_t)grid * 512)
+    return -1;
+  const uint8_t* b = static_cast<const uint8_t*>(buf);
+  if (mode == 0) dma_resident_kernel<0><<<grid, 512, 0, stream>>>(b, n_blocks, row_bytes, steps, cycles, sink);
+  else dma_resident_kernel<1><<<grid, 512, 0, stream>>>(b, n_blocks, row_bytes, steps, cycles, sink);
   return launched();
 }
 
