@@ -1,17 +1,17 @@
 """Randomised shapes, seeded, against the oracle or float64.
 
-moe_grouped_gemm: 24 draws of dtype (bf16 / E4M3), mode (f32 output, bf16 output with an f32
+moe_grouped_gemm: 64 draws of dtype (bf16 / E4M3), mode (f32 output, bf16 output with an f32
 tail split, SwiGLU, ragged reduction), group count and sizes (empty groups included), K, N,
 gathered or plain rows and a sub-range of the groups, each against a float64 product of the same
 operands.  E4M3 operands are codes of small integers with power-of-two scales, so their sums are
 exact in fp32 and those outputs must match bit for bit.
 
-moe_route + moe_permute + moe_combine: 16 draws of T, d, the expert count, top-K and the group
+moe_route + moe_permute + moe_combine: 40 draws of T, d, the expert count, top-K and the group
 limit: routing against the oracle's (sets exact outside the tie window, gates within 1e-6), the
 permutation of the device's own routing bit-exact against the oracle's counting sort, and the
 combine of random rows within the fp32 accumulation of the oracle's float64 sum.
 
-moe_segment_transpose / moe_segment_transpose_fp8: 12 draws of segment counts and lengths, block
+moe_segment_transpose / moe_segment_transpose_fp8: 30 draws of segment counts and lengths, block
 width, channel count and gathered rows."""
 import numpy as np
 import pytest
@@ -47,7 +47,7 @@ def _draw(seed):
     return r, fp8, mode, G, sizes, gran, K, N, gather, first, n_groups, tail
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(64))
 def test_gemm_random_shapes(seed):
     r, fp8, mode, G, sizes, gran, K, N, gather, first, n_groups, tail = _draw(seed)
     offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
@@ -140,7 +140,7 @@ def _route_draw(seed):
     return r, T, d, N, K, ng, tg
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(40))
 def test_route_permute_combine_random(seed):
     r, T, d, N, K, ng, tg = _route_draw(seed)
     say(f"random route seed {seed}: T={T} d={d} N={N} K={K} groups={ng}/{tg}")
@@ -182,7 +182,7 @@ def _transpose_draw(seed):
     return r, fp8, lens, width, C, gather
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(30))
 def test_segment_transpose_random(seed):
     """Random segments into equal-width blocks [n][C][width] (bf16: exact copies with zero padding;
     E4M3: the oracle's 1x128 or 128x128 quantisers applied to those padded bf16 blocks)."""
@@ -237,7 +237,7 @@ def _layer_draw(seed):
                    topk_group=tg, w_std=0.05, router_std=0.05, seed=14000 + seed)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(10))
 def test_layer_bf16_random(seed):
     """Whole bf16 layers of random shape (T, d, expert count, top-K down to 1, group limit,
     width), stage by stage against float64 recomputed from the device's own upstream values:
