@@ -795,6 +795,61 @@ def pin_block_quantisation_idempotent():
     assert np.array_equal(full, pre)
 
 
+def pin_fp32_round_closed_forms():
+    """IEEE binary32 round-to-nearest-even at points worked out from the format: [1, 2) has
+    spacing 2^-23, so 1 + 2^-24 is a tie that goes to the even neighbour 1, 1 + 3 * 2^-25 lies
+    above the midpoint and goes to 1 + 2^-23, and (1 + 2^-23) + 2^-24 is a tie whose even
+    neighbour is 1 + 2^-22; [2^24, 2^25) has spacing 2, so 2^24 + 1 ties to 2^24 and 2^24 + 3 to
+    2^24 + 4.  The same with the sign flipped."""
+    cases = [(1 + 2.0 ** -24, 1.0), (1 + 2.0 ** -25, 1.0), (1 + 3 * 2.0 ** -25, 1 + 2.0 ** -23),
+             (1 + 2.0 ** -23 + 2.0 ** -24, 1 + 2.0 ** -22), (2.0 ** 24 + 1, 2.0 ** 24), (2.0 ** 24 + 3, 2.0 ** 24 + 4),
+             (0.1, 13421773 * 2.0 ** -27)]
+    for v, want in cases:
+        assert O.fp32_round(v) == want and O.fp32_round(-v) == -want, (v, want)
+
+
+def pin_quant_negative_extreme():
+    """A tile or block whose largest magnitude is a negative value: the scale comes from |x|.
+    Tile [-3.5, 1.75, 0.4375, 0, ...]: amax 3.5 -> s = 3.5 / 448 = 2^-7 (power-of-two rule: the
+    same 2^-7), the values scale to -448, 224, 56, all E4M3 numbers, so the negative extreme
+    is stored as code 0xFE and every value comes back exactly.  The same values in one
+    128x128 weight block."""
+    x = np.zeros((1, 128))
+    x[0, :3] = [-3.5, 1.75, 0.4375]
+    q, s = O.quant_1x128(x)
+    assert s[0, 0] == np.float32(2.0 ** -7) and q[0, 0] == 0xFE
+    assert np.array_equal(O.dequant_1x128(q, s), x)
+    q8, c8 = O.quant_1x128_e8m0(x)
+    assert c8[0, 0] == 127 - 7 and q8[0, 0] == 0xFE
+    w = np.zeros((128, 128))
+    w[5, 9], w[0, 0], w[127, 127] = -3.5, 1.75, 0.4375
+    qw, sw = O.quant_128x128(w)
+    assert sw[0, 0] == np.float32(2.0 ** -7) and qw[5, 9] == 0xFE
+    assert np.array_equal(O.dequant_128x128(qw, sw), w)
+    qw8, cw8 = O.quant_128x128_e8m0(w)
+    assert cw8[0, 0] == 127 - 7 and qw8[5, 9] == 0xFE
+
+
+def pin_forward_h_quantised_from_fp32():
+    """The fp8 paths quantise h as the float32 value the kernels form.  Hand-built expert
+    (d = I = 128, weights given as already quantised): x = e_0, W1 column 0 = [64, 64, 0, ...],
+    W3 column 0 = [7, (1.0625 + 2^-30) / 64, 0, ...]; silu(64) = 64 in float64, so h = [448,
+    1.0625 + 2^-30, 0, ...], whose tile (amax 448) has scale 1 under both scale rules.  In
+    float32 h_1 is 1.0625, the midpoint between the E4M3 neighbours 1 and 1.125, and rounds to
+    the even one, 1; the float64 value lies above the midpoint and would give 1.125."""
+    d = inter = 128
+    rows = np.zeros((1, d))
+    rows[0, 0] = 1.0
+    w13 = np.zeros((2 * inter, d))
+    w2 = np.zeros((d, inter))
+    w13[0, 0] = w13[1, 0] = 64.0
+    w13[inter, 0] = 7.0
+    w13[inter + 1, 0] = (1.0625 + 2.0 ** -30) / 64
+    for prec in ("fp8", "fp8_e8m0"):
+        _, h = O.expert_rows(rows, w13, w2, prec, return_h=True, weights_quantised=True)
+        assert h[0, 0] == 448.0 and h[0, 1] == 1.0 and not np.any(h[0, 2:]), prec
+
+
 def pin_layer_flops():
     # DeepSeek-V3 shape: 9 of 257 experts per token; 2*7168*256 + 6*7168*2048*9 per token
     assert O.layer_flops(1, 7168, 256, 8, 2048) == 796_393_472

@@ -361,6 +361,109 @@ def _mut_bwd_fp8_x_unquantised(mp):
     _patch_source(mp, "backward", "x_in = dequant_1x128(*quant_1x128(x)) if fp8 else x", "x_in = x")
 
 
+def _mut_fp32_round_toward_zero(mp):
+    def trunc32(a):
+        a = np.asarray(a, dtype=np.float64)
+        f = a.astype(np.float32)
+        over = np.abs(f.astype(np.float64)) > np.abs(a)
+        f = np.where(over, np.nextafter(f, np.float32(0)), f)
+        return f.astype(np.float64)
+    mp.setattr(O, "fp32_round", trunc32)
+
+
+def _mut_quant_amax_signed(mp):
+    _patch_source(mp, "quant_1x128", "amax = np.max(np.abs(t), axis=2)", "amax = np.max(t, axis=2)")
+
+
+def _mut_quant128_amax_signed(mp):
+    _patch_source(mp, "quant_128x128", "amax = np.max(np.abs(b), axis=(1, 3))", "amax = np.max(b, axis=(1, 3))")
+
+
+def _mut_tile_scale_zero_tile(mp):
+    _patch_source(mp, "_tile_scale", "return np.where(amax32 == 0, np.float32(1.0), s).astype(np.float32)",
+                  "return s.astype(np.float32)")
+
+
+def _mut_dequant_divides(mp):
+    _patch_source(mp, "dequant_1x128", "* s.astype(np.float64)[:, :, None]", "/ s.astype(np.float64)[:, :, None]")
+
+
+def _mut_e4m3_overflow_to_nan(mp):
+    _patch_source(mp, "e4m3_encode", "code = np.where((a >= E4M3_MAX) | (code > 126), 126, code)",
+                  "code = np.where((a > E4M3_MAX) | (code > 126), 127, code)")
+
+
+def _mut_e4m3_subnormal_boundary(mp):
+    _patch_source(mp, "e4m3_encode", "e = np.where(a < 2.0 ** -6, -6, e - 1)", "e = np.where(a < 2.0 ** -7, -7, e - 1)")
+
+
+def _mut_e8m0_decode_off_by_one(mp):
+    _patch_source(mp, "e8m0_decode", "np.exp2((c - E8M0_BIAS).astype(np.float64))",
+                  "np.exp2((c - E8M0_BIAS + 1).astype(np.float64))")
+
+
+def _mut_sigmoid_of_minus(mp):
+    _patch_source(mp, "sigmoid", "return 1.0 / (1.0 + np.exp(-u))", "return 1.0 / (1.0 + np.exp(u))")
+
+
+def _mut_counts_top1_only(mp):
+    _patch_source(mp, "expert_counts", "for e in np.asarray(idx).reshape(-1):", "for e in np.asarray(idx)[:, 0]:")
+
+
+def _mut_combine_gates_reversed(mp):
+    _patch_source(mp, "combine", "out += gate[:, k:k + 1] * y_routed[pair_pos[:, k]]",
+                  "out += gate[:, K - 1 - k:K - k] * y_routed[pair_pos[:, k]]")
+
+
+def _mut_bias_average_expert_moves(mp):
+    _patch_source(mp, "bias_update", "return np.where(diff == 0, bias32, moved).astype(np.float32)",
+                  "return moved.astype(np.float32)")
+
+
+def _mut_route_one_group_too_many(mp):
+    _patch_source(mp, "route", "kept = sorted(gorder[:topk_group])", "kept = sorted(gorder[:topk_group + 1])")
+
+
+def _mut_group_score_top3(mp):
+    _patch_source(mp, "route", "gscore[g] = zz[0] + zz[1]", "gscore[g] = zz[0] + zz[1] + zz[2]")
+
+
+def _mut_swiglu_no_silu(mp):
+    _patch_source(mp, "swiglu_hidden", "return silu(a) * c", "return a * c")
+
+
+def _mut_permute_shared_reversed(mp):
+    _patch_source(mp, "permute", "sorted_token[base:base + T] = np.arange(T)", "sorted_token[base:base + T] = np.arange(T)[::-1]")
+
+
+def _mut_fwd_shared_uses_expert0(mp):
+    _patch_source(mp, "forward_sparse", "we13, we2 = expert_weights(e)",
+                  "we13, we2 = expert_weights(e if e < n_experts else 0)")
+
+
+def _mut_fwd_fp8_weights_unquantised(mp):
+    _patch_source(mp, "expert_rows", "w13d = np.asarray(w13, np.float64) if weights_quantised else dequant_128x128(*qw(w13))",
+                  "w13d = np.asarray(w13, np.float64)")
+
+
+def _mut_fwd_fp8_w2_unquantised(mp):
+    _patch_source(mp, "expert_rows", "w2d = np.asarray(w2, np.float64) if weights_quantised else dequant_128x128(*qw(w2))",
+                  "w2d = np.asarray(w2, np.float64)")
+
+
+def _mut_fwd_fp8_h_quantised_from_fp64(mp):
+    _patch_source(mp, "expert_rows", "hq, hs = qa(fp32_round(h))", "hq, hs = qa(h)")
+
+
+def _mut_fwd_fp8_e8m0_uses_fp32_scales(mp):
+    _patch_source(mp, "_quantisers", 'if precision == "fp8":', 'if precision in ("fp8", "fp8_e8m0"):')
+
+
+def _mut_layer_flops_no_shared(mp):
+    real = O.layer_flops
+    mp.setattr(O, "layer_flops", lambda T, d, n, k, i, n_shared=1: real(T, d, n, k, i, 0))
+
+
 MUTATIONS = [
     _mut_gate_from_z, _mut_ascending, _mut_tie_higher_index, _mut_silu_sign, _mut_swap_w1_w3,
     _mut_bias_sign, _mut_bias_mean_off, _mut_e4m3_ties_odd, _mut_fnuz_scale,
@@ -375,6 +478,12 @@ MUTATIONS = [
     _mut_bwd_routed_dx_unrounded, _mut_bwd_fp8_dgrad_dy_unquantised, _mut_bwd_fp8_dgrad_dac_unquantised,
     _mut_bwd_fp8_wgrad_dy_unquantised, _mut_bwd_fp8_wgrad_h_unquantised, _mut_bwd_fp8_wgrad_x_unquantised,
     _mut_bwd_fp8_wgrad_dac_unquantised, _mut_bwd_fp8_wgrad_dy_wrong_axis, _mut_bwd_fp8_x_unquantised,
+    _mut_fp32_round_toward_zero, _mut_quant_amax_signed, _mut_quant128_amax_signed, _mut_tile_scale_zero_tile,
+    _mut_dequant_divides, _mut_e4m3_overflow_to_nan, _mut_e4m3_subnormal_boundary, _mut_e8m0_decode_off_by_one,
+    _mut_sigmoid_of_minus, _mut_counts_top1_only, _mut_combine_gates_reversed, _mut_bias_average_expert_moves,
+    _mut_route_one_group_too_many, _mut_group_score_top3, _mut_swiglu_no_silu, _mut_permute_shared_reversed,
+    _mut_fwd_shared_uses_expert0, _mut_fwd_fp8_weights_unquantised, _mut_fwd_fp8_w2_unquantised,
+    _mut_fwd_fp8_h_quantised_from_fp64, _mut_fwd_fp8_e8m0_uses_fp32_scales, _mut_layer_flops_no_shared,
 ]
 
 
