@@ -479,6 +479,7 @@ def run_ceilings(torch, dev):
     lib.moe_ceil_hbm_read.argtypes = [P, S, P, S, I32, P]
     lib.moe_ceil_dma_read.argtypes = [P, I64, I32, P, S, I32, P]
     lib.moe_ceil_dma_resident.argtypes = [I32, P, I32, I32, I32, P, P, S, I32, P]
+    lib.moe_ceil_dma_read_ring.argtypes = [I32, P, I64, I32, P, S, I32, P]
     lib.moe_ceil_lds_read.argtypes = [I32, I32, P, P, S, I32, P]
     lib.moe_ceil_mfma.argtypes = [I32, I32, P, P, S, I32, P]
     lib.moe_ceil_valu.argtypes = [I32, P, P, S, I32, P]
@@ -520,6 +521,11 @@ def run_ceilings(torch, dev):
     ms = timed(lambda: lib.moe_ceil_dma_read(buf.data_ptr(), rows, row_bytes, sk, skn, cus, sp))
     out["hbm_read_dma_gemm_pattern_GBs"] = {"rows": rows, "row_bytes": row_bytes, "grid": cus,
                                             "GBs": round(rows * row_bytes / (ms / 1e3) / 1e9, 1)}
+    ring = {}
+    for slots in (2, 3, 4, 5):  # slots - 1 steps of 32 KB in flight per CU
+        ms = timed(lambda: lib.moe_ceil_dma_read_ring(slots, buf.data_ptr(), rows, row_bytes, sk, skn, cus, sp))
+        ring[f"slots_{slots}"] = round(rows * row_bytes / (ms / 1e3) / 1e9, 1)
+    out["hbm_read_dma_by_ring_depth_GBs"] = ring
     # the same step pattern over working sets held by one cache level: 8 row blocks of 256 rows x
     # 2 KB read by every CU (4 MB: in each XCD's L2), and one 256-row x 1 KB block per CU (8 MB
     # per XCD, past its 4 MB L2; 64 MB in all, inside the Infinity Cache), by direct-to-LDS DMA

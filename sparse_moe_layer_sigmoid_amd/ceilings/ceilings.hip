@@ -7,6 +7,8 @@
 //                      grouped GEMM's weight pattern: blocks of 256 rows x 128 bytes, each wave
 //                      instruction 8 rows x 128 bytes, a three-slot LDS ring, one vmcnt wait
 //                      and one barrier per step, one workgroup per CU walking its row blocks
+//   moe_ceil_dma_read_ring  the same streaming read with a ring of `slots` (2..5) 32 KB slots, so
+//                      slots - 1 steps are in flight per CU (how deep a ring HBM streaming needs)
 //   moe_ceil_dma_resident  the same step pattern (256 rows x 128 bytes per step, 8 rows x 128 B
 //                      per wave instruction, three-slot ring) over a working set chosen to sit in
 //                      one cache level: workgroup b reads row block b % n_blocks over and over,
@@ -85,6 +87,44 @@ __global__ __launch_bounds__(512) void dma_read_kernel(const uint8_t* __restrict
     if (g + 1 < n) CEIL_WAIT_VM(4); else CEIL_WAIT_VM(0);  // step g has landed
     __builtin_amdgcn_s_barrier();                          // ... for every wave: slot (g+2)%3 is free
     if (g + 2 < n) issue(g + 2);
+  }
+  sink[(size_t)blockIdx.x * 512 + threadIdx.x] = (uint32_t)n;
+}
+
+// dma_read_kernel's walk with an NS-slot ring: NS - 1 steps in flight, one wait and one barrier
+// per step (a slot is refilled one step after it was waited for, once every wave is past it)
+template <int NS>
+__global__ __launch_bounds__(512) void dma_ring_kernel(const uint8_t* __restrict__ buf, int n_rb, int row_bytes,
+                                                       uint32_t* sink) {
+  __shared__ __attribute__((aligned(1024))) uint8_t slot[NS][kStep];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int steps_per_rb = row_bytes / 128;
+  const int n_my = blockIdx.x < n_rb ? (n_rb - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  const int64_t n = (int64_t)n_my * steps_per_rb;
+  auto issue = [&](int64_t g) {
+    const int64_t rb = blockIdx.x + (g / steps_per_rb) * gridDim.x;
+    const int k = (int)(g % steps_per_rb);
+    uint8_t* st = slot[g % NS];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = wave * 4 + j;
+      const int64_t row = rb * kRowsPerBlock + q * 8 + (lane >> 3);
+      const uint8_t* src = buf + row * row_bytes + k * 128 + (lane & 7) * 16;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(st + q * 1024), 16, 0, 0);
+    }
+  };
+  for (int64_t g = 0; g < NS - 1 && g < n; ++g) issue(g);
+  for (int64_t g = 0; g < n; ++g) {
+    // step g has landed: the batches of the min(NS - 2, n - 1 - g) later steps may still be in flight
+    const int64_t later = n - 1 - g < NS - 2 ? n - 1 - g : NS - 2;
+    if (later >= 3) CEIL_WAIT_VM(12);
+    else if (later == 2) CEIL_WAIT_VM(8);
+    else if (later == 1) CEIL_WAIT_VM(4);
+    else CEIL_WAIT_VM(0);
+    __builtin_amdgcn_s_barrier();  // every wave is past step g - 1: its slot takes step g + NS - 1
+    if (g + NS - 1 < n) issue(g + NS - 1);
   }
   sink[(size_t)blockIdx.x * 512 + threadIdx.x] = (uint32_t)n;
 }
@@ -283,6 +323,22 @@ int moe_ceil_dma_read(const void* buf, int64_t rows, int row_bytes, uint32_t* si
     return -1;
   dma_read_kernel<<<grid, 512, 0, stream>>>(static_cast<const uint8_t*>(buf), (int)(rows / kRowsPerBlock),
                                             row_bytes, sink);
+  return launched();
+}
+
+// as moe_ceil_dma_read, with `slots` (2..5) ring slots
+int moe_ceil_dma_read_ring(int slots, const void* buf, int64_t rows, int row_bytes, uint32_t* sink, size_t sink_words,
+                           int grid, hipStream_t stream) {
+  if (slots < 2 || slots > 5 || !buf || !sink || rows < kRowsPerBlock || rows % kRowsPerBlock || row_bytes < 128 ||
+      row_bytes % 128 || ((uintptr_t)buf & 15) || grid < 1 || rows / kRowsPerBlock > INT32_MAX ||
+      sink_words < (size_t)grid * 512)
+    return -1;
+  const uint8_t* b = static_cast<const uint8_t*>(buf);
+  const int n_rb = (int)(rows / kRowsPerBlock);
+  if (slots == 2) dma_ring_kernel<2><<<grid, 512, 0, stream>>>(b, n_rb, row_bytes, sink);
+  else if (slots == 3) dma_ring_kernel<3><<<grid, 512, 0, stream>>>(b, n_rb, row_bytes, sink);
+  else if (slots == 4) dma_ring_kernel<4><<<grid, 512, 0, stream>>>(b, n_rb, row_bytes, sink);
+  else dma_ring_kernel<5><<<grid, 512, 0, stream>>>(b, n_rb, row_bytes, sink);
   return launched();
 }
 

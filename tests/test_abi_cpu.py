@@ -253,6 +253,7 @@ def test_ceilings_library_exports_and_rejects():
     lib.moe_ceil_hbm_read.argtypes = [P, S, P, S, I32, P]
     lib.moe_ceil_dma_read.argtypes = [P, I64, I32, P, S, I32, P]
     lib.moe_ceil_dma_resident.argtypes = [I32, P, I32, I32, I32, P, P, S, I32, P]
+    lib.moe_ceil_dma_read_ring.argtypes = [I32, P, I64, I32, P, S, I32, P]
     lib.moe_ceil_lds_read.argtypes = [I32, I32, P, P, S, I32, P]
     lib.moe_ceil_mfma.argtypes = [I32, I32, P, P, S, I32, P]
     lib.moe_ceil_valu.argtypes = [I32, P, P, S, I32, P]
@@ -261,6 +262,9 @@ def test_ceilings_library_exports_and_rejects():
     assert lib.moe_ceil_hbm_read(16, 1024, 16, 100, 4, None) == -1  # sink too small
     assert lib.moe_ceil_dma_read(16, 300, 128, 16, big, 4, None) == -1  # rows not a multiple of 256
     assert lib.moe_ceil_dma_read(16, 256, 100, 16, big, 4, None) == -1  # row bytes not a multiple of 128
+    assert lib.moe_ceil_dma_read_ring(6, 16, 256, 128, 16, big, 4, None) == -1  # slots
+    assert lib.moe_ceil_dma_read_ring(1, 16, 256, 128, 16, big, 4, None) == -1  # slots
+    assert lib.moe_ceil_dma_read_ring(3, 16, 300, 128, 16, big, 4, None) == -1  # rows not a multiple of 256
     assert lib.moe_ceil_dma_resident(2, 16, 1, 128, 3, 16, 16, big, 4, None) == -1  # mode
     assert lib.moe_ceil_dma_resident(0, 16, 1, 100, 3, 16, 16, big, 4, None) == -1  # row bytes not a multiple of 128
     assert lib.moe_ceil_dma_resident(0, 16, 1, 128, 4, 16, 16, big, 4, None) == -1  # steps not a multiple of 3
