@@ -186,6 +186,25 @@ def step_bytes(cfg, counts_np, fp8: bool):
     return w + cfg.n_experts * cfg.d * 2 + 2 * cfg.T * cfg.d * 2
 
 
+def gate_up_roofline(flop, nbytes, ms, fp8: bool):
+    """Roofline object of the gate/up launch: against the matrix-core peak of its dtype when its
+    arithmetic intensity (algorithmic flop per algorithmic byte) lies above that peak's ridge
+    point (peak flop/s over the 8 TB/s HBM peak: 312 flop/B for bf16, 625 for E4M3), else
+    against the HBM peak."""
+    peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
+    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    name = "grouped_gemm gate/up + SwiGLU" + (" (E4M3)" if fp8 else "")
+    common = {"traffic": None, "avg_launch_ms": round(ms, 4), "algorithmic_flop_per_launch": int(flop),
+              "algorithmic_bytes_per_launch": int(nbytes)}
+    if flop / nbytes > ridge:
+        achieved = flop / (ms / 1e3) / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), **common}
+    achieved = nbytes / (ms / 1e3) / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), **common}
+
+
 def kernel_src_sha():
     h = hashlib.sha256()
     for f in ("gemm.hip", "device_common.h"):
@@ -705,18 +724,8 @@ def main():
     gu_bytes = gate_up_bytes(cfg, counts0, fp8_main, 1 if main_e8m0 else 4)
     gu_flop = 4 * cfg.rows * cfg.d * cfg.inter
     tag = f"gate_up_{args.workload}"
-    if fp8_main:  # compute-bound: the E4M3 gate/up against the matrix-core peak
-        achieved = gu_flop / (gu_ms / 1e3) / 1e12
-        roofline = {"kernel": "grouped_gemm gate/up + SwiGLU (E4M3)", "bound": "mfma", "achieved": round(achieved, 1),
-                    "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                    "traffic": measured_traffic(tag), "avg_launch_ms": round(gu_ms, 4),
-                    "algorithmic_flop_per_launch": int(gu_flop), "algorithmic_bytes_per_launch": int(gu_bytes)}
-    else:
-        achieved = gu_bytes / (gu_ms / 1e3) / 1e9
-        roofline = {"kernel": "grouped_gemm gate/up + SwiGLU", "bound": "hbm", "achieved": round(achieved, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(tag), "avg_launch_ms": round(gu_ms, 4),
-                    "algorithmic_bytes_per_launch": int(gu_bytes)}
+    roofline = gate_up_roofline(gu_flop, gu_bytes, gu_ms, fp8_main)
+    roofline["traffic"] = measured_traffic(tag)
     line = {
         "metric": "MoE-layer tokens/s + % MFMA peak (T=4096 bf16, T=16384 fp8); decode GB/s",
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -730,7 +739,7 @@ def main():
         "roofline": roofline,
         "kernels": kf,
     }
-    log(f"[bench] {args.workload}: {ms:.3f} ms/step, {tok_s:,.0f} tok/s, gate/up {gu_ms:.3f} ms ({achieved:.0f} "
+    log(f"[bench] {args.workload}: {ms:.3f} ms/step, {tok_s:,.0f} tok/s, gate/up {gu_ms:.3f} ms ({roofline['achieved']:.0f} "
         f"{roofline['unit']}), down {kf['down']['ms']:.3f} ms, combine {kf['combine']['ms']:.3f} ms")
 
     # ---------------------------------------------------------------- secondary workloads
@@ -828,8 +837,11 @@ def main():
         peaks = measured_peaks(torch, dev)
         if peaks:
             line["measured_peaks"] = peaks
-            ref = peaks["mfma_e4m3_TFLOPs"] if fp8_main else peaks["hbm_read_dma_GBs"]
-            line["roofline"]["frac_of_measured_peak"] = round(achieved / ref, 4)
+            if roofline["bound"] == "mfma":
+                ref = peaks["mfma_e4m3_TFLOPs"] if fp8_main else peaks["mfma_bf16_TFLOPs"]
+            else:
+                ref = peaks["hbm_read_dma_GBs"]
+            line["roofline"]["frac_of_measured_peak"] = round(roofline["achieved"] / ref, 4)
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")

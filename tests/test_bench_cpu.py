@@ -59,6 +59,24 @@ def test_layer_and_backward_flops():
     assert bench.backward_flops(c) == 2 * f
 
 
+def test_roofline_bound_from_arithmetic_intensity():
+    """The gate/up roofline is taken against the matrix cores only above the ridge point of its
+    dtype's peak (bf16 2.5 PFLOP/s / 8 TB/s = 312.5 flop/B, E4M3 625): the bf16 T = 4096
+    headline (141 flop/B) and the E4M3 decode step are HBM-bound, the E4M3 T = 16384 layer
+    (1085 flop/B) is matrix-core-bound; the fractions divide by the matching peak."""
+    for cfg, fp8, bound in ((I.V3_BF16, False, "hbm"), (I.V3_FP8, True, "mfma"), (I.V3_DECODE, True, "hbm")):
+        flop = 4 * cfg.rows * cfg.d * cfg.inter
+        nbytes = bench.gate_up_bytes(cfg, np.ones(256, dtype=np.int64), fp8)
+        r = bench.gate_up_roofline(flop, nbytes, 2.0, fp8)
+        assert r["bound"] == bound, cfg.name
+        if bound == "hbm":
+            assert r["unit"] == "GB/s" and abs(r["frac"] - nbytes / 2e-3 / 8e12) < 1e-4
+        else:
+            assert r["unit"] == "TFLOP/s" and abs(r["frac"] - flop / 2e-3 / 5e15) < 1e-4
+    assert bench.gate_up_roofline(312.6e9, 1e9, 1.0, False)["bound"] == "mfma"
+    assert bench.gate_up_roofline(312.4e9, 1e9, 1.0, False)["bound"] == "hbm"
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
