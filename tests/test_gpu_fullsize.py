@@ -196,6 +196,34 @@ def test_v3_fp8_T16384(v3):
     fp8_end_to_end_bar(err, cfg.name)
 
 
+def test_v3_bf16_T32768(v3):
+    """The largest batch the benchmark's T sweep times (294,912 expert rows): every token's
+    routing, loads and permutation; the output of every 32nd token (1024 tokens reaching all
+    experts) against the oracle's bf16 model."""
+    cfg = I.small(I.V3_BF16, T=32768, name="v3_bf16_T32768")
+    x_cpu, bias, r, tie, out32, buf = _route_and_layer(v3, cfg, False)
+    sub = np.arange(0, cfg.T, 32)
+    err, pick, experts = _all_token_output_check(cfg, x_cpu, r, tie, out32, "bf16", BF16_TOL, tokens=sub)
+    assert len(pick) >= len(sub) - 8 and len(experts) == cfg.n_experts
+    assert err <= BF16_TOL
+
+
+def test_v3_fp8_T32768(v3):
+    """The E4M3 layer at T = 32768 (x with the 0.1% x100 outliers): every token's routing, the x
+    quantisation bit-exact, every 16th token (2048 tokens, all experts) end to end against the
+    oracle's fp8 pipeline (recorded against the bar) and stage by stage."""
+    cfg = I.small(I.V3_FP8, T=32768, name="v3_fp8_T32768")
+    x_cpu, bias, r, tie, out32, buf = _route_and_layer(v3, cfg, True)
+    xq, xs = O.quant_1x128(x_cpu.float().numpy())
+    assert np.array_equal(buf["xq"].cpu().numpy(), xq) and np.array_equal(buf["xs"].cpu().numpy(), xs)
+    del xq, xs
+    sub = np.arange(0, cfg.T, 16)
+    err, pick, experts = _all_token_output_check(cfg, x_cpu, r, tie, out32, "fp8", FP8_TOL, tokens=sub)
+    assert len(pick) >= len(sub) - 8 and len(experts) == cfg.n_experts
+    assert len(_fp8_staged(cfg, x_cpu, r, tie, out32, buf, "fp8", every=16)) == cfg.n_experts
+    fp8_end_to_end_bar(err, cfg.name)
+
+
 def test_v3_fp8_e8m0_T16384(v3):
     """The T = 16384 E4M3 workload with power-of-two (E8M0) tile scales."""
     cfg = I.V3_FP8
